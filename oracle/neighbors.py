@@ -19,29 +19,37 @@ GPU builder must reproduce bit for bit:
 import numpy as np
 
 
-def neighbors_bruteforce(pos, cutoff, box=None, mol_id=None):
-    """Return (row_ptr int32 [N+1], col int32 [E])."""
+def neighbors_bruteforce(pos, cutoff, box=None, mol_id=None, rows=None):
+    """Return (row_ptr int32 [N+1], col int32 [E]); with `rows`, return the
+    sorted neighbour arrays of just those atoms (for sampled checks)."""
     p = np.asarray(pos, dtype=np.float32).astype(np.float64)
     n = p.shape[0]
     rc = np.float64(np.float32(cutoff))
     rc2 = rc * rc
     b = None if box is None else np.asarray(box, dtype=np.float32).astype(np.float64)
     mol = None if mol_id is None else np.asarray(mol_id)
+    idx = np.arange(n)
+    if rows is not None:
+        return [_row(p, i, idx, rc2, b, mol) for i in rows]
     counts = np.zeros(n, dtype=np.int64)
     cols = []
-    idx = np.arange(n)
     for i in range(n):
-        d = [p[:, a] - p[i, a] for a in range(3)]
-        if b is not None:
-            d = [d[a] - b[a] * np.rint(d[a] / b[a]) for a in range(3)]
-        s = (d[0] * d[0] + d[1] * d[1]) + d[2] * d[2]
-        keep = (s < rc2) & (idx != i)
-        if mol is not None:
-            keep &= mol == mol[i]
-        js = idx[keep]  # ascending by construction
+        js = _row(p, i, idx, rc2, b, mol)
         counts[i] = js.size
         cols.append(js)
     row_ptr = np.zeros(n + 1, dtype=np.int64)
     np.cumsum(counts, out=row_ptr[1:])
     col = np.concatenate(cols) if cols else np.zeros(0, dtype=np.int64)
     return row_ptr.astype(np.int32), col.astype(np.int32)
+
+
+def _row(p, i, idx, rc2, b, mol):
+    """Sorted neighbours of atom i (the test of the module docstring)."""
+    d = [p[:, a] - p[i, a] for a in range(3)]
+    if b is not None:
+        d = [d[a] - b[a] * np.rint(d[a] / b[a]) for a in range(3)]
+    s = (d[0] * d[0] + d[1] * d[1]) + d[2] * d[2]
+    keep = (s < rc2) & (idx != i)
+    if mol is not None:
+        keep &= mol == mol[i]
+    return idx[keep].astype(np.int32)  # ascending by construction

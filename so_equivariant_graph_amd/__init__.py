@@ -1,0 +1,289 @@
+"""MI355X (gfx950) on-the-fly SO(2) equivariant graph attention forward.
+
+Thin Python binding over the C ABI in include/so2attn.h (libso2attn.so,
+built in-tree by ``so_equivariant_graph_amd.build``).  This module only
+marshals arguments: it allocates outputs and workspace with PyTorch, passes
+raw device pointers and the current stream, and raises on a non-OK status.
+Every step of the computation runs in the HIP library; there is no other
+implementation behind these calls, and loading fails loudly when the
+library is missing.
+
+    row_ptr, col = build_neighbors(pos, cutoff, box=None, mol_id=None)
+    y = so2_attention_fwd(pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2,
+                          l_max=4, heads=8, cutoff=6.0)
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libso2attn.so")
+
+SO2_OK = 0
+SO2_ERR_INVALID_ARGUMENT = 1
+SO2_ERR_UNSUPPORTED = 2
+SO2_ERR_CAPACITY = 3
+SO2_ERR_BOX = 4
+SO2_ERR_DEVICE = 5
+SO2_ERR_WORKSPACE = 6
+
+SO2_FP32 = 0
+SO2_BF16 = 1
+
+FLAG_RBF_ENVELOPE = 1
+FLAG_NO_RADIAL = 2
+
+KERNEL_NONE, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
+
+EXPORTED_SYMBOLS = (
+    "so2_status_string",
+    "so2_last_device_error",
+    "so2_neighbors_workspace_bytes",
+    "build_neighbors",
+    "so2_weight_count",
+    "so2_attention_workspace_bytes",
+    "so2_attention_kernel_kind",
+    "so2_attention_fwd",
+    "so2_edge_frame_host",
+)
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_atoms", ctypes.c_int32),
+        ("n_targets", ctypes.c_int32),
+        ("n_edges", ctypes.c_int64),
+        ("l_max", ctypes.c_int32),
+        ("channels", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("n_rbf", ctypes.c_int32),
+        ("envelope_p", ctypes.c_int32),
+        ("cutoff", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class SO2Error(RuntimeError):
+    def __init__(self, status, where, detail=""):
+        self.status = status
+        msg = f"{where}: {status_string(status)}"
+        if detail:
+            msg += f" ({detail})"
+        super().__init__(msg)
+
+
+_lib_handle = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libso2attn.so; raises if it has not been built."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m so_equivariant_graph_amd.build` "
+            "(the SO(2) attention path has no other implementation)"
+        )
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.so2_status_string.argtypes = [ctypes.c_int]
+    lib.so2_status_string.restype = ctypes.c_char_p
+    lib.so2_last_device_error.argtypes = []
+    lib.so2_last_device_error.restype = ctypes.c_char_p
+    lib.so2_neighbors_workspace_bytes.argtypes = [i32]
+    lib.so2_neighbors_workspace_bytes.restype = sz
+    lib.build_neighbors.argtypes = [vp, i32, vp, vp, f32, vp, vp, i64, ctypes.POINTER(i64), vp, sz, vp]
+    lib.build_neighbors.restype = ctypes.c_int
+    lib.so2_weight_count.argtypes = [i32, i32]
+    lib.so2_weight_count.restype = i64
+    lib.so2_attention_workspace_bytes.argtypes = [ctypes.POINTER(AttnDesc)]
+    lib.so2_attention_workspace_bytes.restype = sz
+    lib.so2_attention_kernel_kind.argtypes = [ctypes.POINTER(AttnDesc)]
+    lib.so2_attention_kernel_kind.restype = i32
+    lib.so2_attention_fwd.argtypes = [ctypes.POINTER(AttnDesc)] + [vp] * 11 + [sz, vp]
+    lib.so2_attention_fwd.restype = ctypes.c_int
+    lib.so2_edge_frame_host.argtypes = [i32, vp, vp, vp]
+    lib.so2_edge_frame_host.restype = ctypes.c_int
+    _lib_handle = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().so2_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != SO2_OK:
+        detail = ""
+        if status == SO2_ERR_DEVICE:
+            detail = load_library().so2_last_device_error().decode()
+        raise SO2Error(status, where, detail)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream_handle(device):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _host_box(box):
+    if box is None:
+        return None, ctypes.c_void_p(0)
+    arr = (ctypes.c_float * 3)(*[float(v) for v in np.asarray(box, dtype=np.float32).reshape(3)])
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def weight_count(l_max: int, channels: int) -> int:
+    return int(load_library().so2_weight_count(l_max, channels))
+
+
+def neighbors_workspace_bytes(n_atoms: int) -> int:
+    return int(load_library().so2_neighbors_workspace_bytes(n_atoms))
+
+
+def make_desc(*, n_atoms, n_targets, n_edges, l_max, channels, heads, n_rbf, envelope_p, cutoff,
+              flags, dtype) -> AttnDesc:
+    return AttnDesc(
+        int(n_atoms), int(n_targets), int(n_edges), int(l_max), int(channels), int(heads),
+        int(n_rbf), int(envelope_p), float(np.float32(cutoff)), int(flags), int(dtype),
+    )
+
+
+def attention_workspace_bytes(desc: AttnDesc) -> int:
+    return int(load_library().so2_attention_workspace_bytes(ctypes.byref(desc)))
+
+
+def attention_kernel_kind(desc: AttnDesc) -> int:
+    return int(load_library().so2_attention_kernel_kind(ctypes.byref(desc)))
+
+
+def build_neighbors(pos, cutoff, box=None, mol_id=None, capacity=None, workspace=None):
+    """Radius graph on the device.  pos: [N,3] float32 CUDA tensor.
+    Returns (row_ptr int32 [N+1], col int32 [E]) on pos.device."""
+    import torch
+
+    lib = load_library()
+    if pos.dtype != torch.float32 or pos.dim() != 2 or pos.shape[1] != 3 or not pos.is_cuda:
+        raise ValueError("pos must be a [N,3] float32 CUDA tensor")
+    pos = pos.contiguous()
+    n = pos.shape[0]
+    dev = pos.device
+    if mol_id is not None:
+        mol_id = mol_id.to(device=dev, dtype=torch.int32).contiguous()
+    ws_bytes = lib.so2_neighbors_workspace_bytes(n)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    row_ptr = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    cap = int(capacity) if capacity is not None else 96 * n
+    keep, box_p = _host_box(box)
+    stream = _stream_handle(dev)
+    for _ in range(2):
+        col = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+        n_edges = ctypes.c_int64(0)
+        st = lib.build_neighbors(
+            _ptr(pos), n, _ptr(mol_id), box_p, ctypes.c_float(float(cutoff)), _ptr(row_ptr),
+            _ptr(col), cap, ctypes.byref(n_edges), _ptr(workspace), ws_bytes, stream,
+        )
+        if st == SO2_ERR_CAPACITY:
+            cap = int(n_edges.value)
+            continue
+        _check(st, "build_neighbors")
+        return row_ptr, col[: n_edges.value]
+    raise SO2Error(SO2_ERR_CAPACITY, "build_neighbors")
+
+
+_DTYPES = {}
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.float32:
+        return SO2_FP32
+    if t.dtype == torch.bfloat16:
+        return SO2_BF16
+    raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def so2_attention_fwd(pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, *, l_max, heads, cutoff,
+                      envelope_p=5, box=None, flags=0, n_targets=None, out=None, workspace=None):
+    """Fused SO(2) attention forward.  x: [N,(L+1)^2,C] (float32 or bfloat16);
+    the weights share x's dtype.  Returns y [n_targets,(L+1)^2,C] float32."""
+    import torch
+
+    lib = load_library()
+    dt = _dtype_code(x)
+    for name, t in (("w_q", w_q), ("w_k", w_k), ("w_rad", w_rad), ("w_so2", w_so2)):
+        if t.dtype != x.dtype:
+            raise ValueError(f"{name} must have x's dtype {x.dtype}")
+    n, nc, C = x.shape
+    if nc != (l_max + 1) ** 2:
+        raise ValueError("x has the wrong number of irreps components")
+    if w_so2.numel() != lib.so2_weight_count(l_max, C):
+        raise ValueError("w_so2 has the wrong number of entries")
+    if w_rad.dim() != 2 or w_rad.shape[1] != C:
+        raise ValueError("w_rad must be [K, C]")
+    nt = n if n_targets is None else int(n_targets)
+    tensors = [t.contiguous() for t in (pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2)]
+    pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2 = tensors
+    desc = make_desc(
+        n_atoms=n, n_targets=nt, n_edges=col.numel(), l_max=l_max, channels=C, heads=heads,
+        n_rbf=w_rad.shape[0], envelope_p=envelope_p, cutoff=cutoff, flags=flags, dtype=dt,
+    )
+    ws_bytes = lib.so2_attention_workspace_bytes(ctypes.byref(desc))
+    if ws_bytes == 0:
+        st = lib.so2_attention_fwd(ctypes.byref(desc), *([ctypes.c_void_p(0)] * 11), 0, ctypes.c_void_p(0))
+        _check(st if st != SO2_OK else SO2_ERR_INVALID_ARGUMENT, "so2_attention_fwd")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    y = out if out is not None else torch.empty((nt, nc, C), dtype=torch.float32, device=x.device)
+    keep, box_p = _host_box(box)
+    col_arg = col if col.numel() > 0 else row_ptr  # any valid device pointer when E = 0
+    st = lib.so2_attention_fwd(
+        ctypes.byref(desc), _ptr(pos), box_p, _ptr(row_ptr), _ptr(col_arg), _ptr(x), _ptr(w_q),
+        _ptr(w_k), _ptr(w_rad), _ptr(w_so2), _ptr(y), _ptr(workspace), ws_bytes,
+        _stream_handle(x.device),
+    )
+    _check(st, "so2_attention_fwd")
+    return y
+
+
+def edge_frame_host(l_max: int, rhat):
+    """CPU evaluation of the kernels' edge frame and Wigner-D code (fp32).
+    Returns (R [3,3], [D^0..D^L])."""
+    lib = load_library()
+    r = np.ascontiguousarray(np.asarray(rhat, dtype=np.float32).reshape(3))
+    R = np.zeros(9, dtype=np.float32)
+    total = sum((2 * l + 1) ** 2 for l in range(l_max + 1))
+    D = np.zeros(total, dtype=np.float32)
+    st = lib.so2_edge_frame_host(l_max, r.ctypes.data, R.ctypes.data, D.ctypes.data)
+    _check(st, "so2_edge_frame_host")
+    blocks, off = [], 0
+    for l in range(l_max + 1):
+        n = 2 * l + 1
+        blocks.append(D[off : off + n * n].reshape(n, n).astype(np.float64))
+        off += n * n
+    return R.reshape(3, 3).astype(np.float64), blocks
+
+
+__all__ = [
+    "build_neighbors",
+    "so2_attention_fwd",
+    "edge_frame_host",
+    "weight_count",
+    "neighbors_workspace_bytes",
+    "attention_workspace_bytes",
+    "attention_kernel_kind",
+    "make_desc",
+    "load_library",
+    "SO2Error",
+    "AttnDesc",
+]

@@ -1,0 +1,171 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/so2attn.h declares, its host-side edge frame / Wigner-D code agrees
+with the oracle, and argument errors come back as status codes before
+anything is launched (device pointers are never touched on these paths)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import so_equivariant_graph_amd as sea
+from oracle import real_sh, so2_weight_count, wigner_d_blocks
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "so2attn.h")
+FAKE = ctypes.c_void_p(1 << 30)  # never dereferenced: every call below fails validation first
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_0-9]+)\s*\(", text)
+    skip = {"if", "sizeof", "defined"}
+    return sorted({n for n in names if n not in skip and (n.startswith("so2_") or n == "build_neighbors")})
+
+
+def test_library_exports_every_declared_function():
+    lib = sea.load_library()
+    declared = _declared_functions()
+    assert "build_neighbors" in declared and "so2_attention_fwd" in declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(sea.EXPORTED_SYMBOLS)
+
+
+@pytest.mark.parametrize("L", [0, 1, 2, 4, 6])
+@pytest.mark.parametrize("C", [1, 16, 128])
+def test_weight_count_matches_oracle(L, C):
+    assert sea.weight_count(L, C) == so2_weight_count(L, C)
+
+
+def test_status_strings():
+    lib = sea.load_library()
+    for code in range(7):
+        assert lib.so2_status_string(code).decode().startswith("SO2_")
+
+
+@pytest.mark.parametrize(
+    "rhat",
+    [(0.3, -0.2, 0.9), (0.0, 0.0, 1.0), (0.0, 0.0, -1.0), (1e-6, 0.0, -1.0), (-1.0, 0.0, 0.0), (0.0, 1.0, 0.0)],
+)
+def test_host_edge_frame_and_wigner_match_oracle(rhat):
+    L = 6
+    R, D = sea.edge_frame_host(L, rhat)
+    r = np.asarray(rhat, dtype=np.float64)
+    r /= np.linalg.norm(r)
+    np.testing.assert_allclose(R @ R.T, np.eye(3), atol=2e-7)
+    np.testing.assert_allclose(R @ r, [0, 0, 1], atol=2e-7)
+    assert abs(np.linalg.det(R) - 1) < 1e-6
+    ref = wigner_d_blocks(L, R)
+    for l in range(L + 1):
+        np.testing.assert_allclose(D[l], ref[l], atol=2e-6)
+    # Lemma 4.1 of the E2Former-V2 summary: in the aligned frame only m = 0 survives
+    Y = real_sh(L, r[None])[0]
+    for l in range(L + 1):
+        v = D[l] @ Y[l * l : (l + 1) ** 2]
+        v[l] -= np.sqrt((2 * l + 1) / (4 * np.pi))
+        assert np.abs(v).max() < 3e-6
+
+
+def test_host_edge_frame_random_directions():
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        r = rng.standard_normal(3)
+        R, D = sea.edge_frame_host(4, r)
+        ref = wigner_d_blocks(4, R)
+        for l in range(5):
+            np.testing.assert_allclose(D[l], ref[l], atol=2e-6)
+
+
+def test_edge_frame_rejects_bad_input():
+    lib = sea.load_library()
+    z = np.zeros(3, dtype=np.float32)
+    out = np.zeros(500, dtype=np.float32)
+    assert lib.so2_edge_frame_host(4, z.ctypes.data, out.ctypes.data, out.ctypes.data) == sea.SO2_ERR_INVALID_ARGUMENT
+    r = np.ones(3, dtype=np.float32)
+    assert lib.so2_edge_frame_host(7, r.ctypes.data, out.ctypes.data, out.ctypes.data) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert lib.so2_edge_frame_host(2, None, out.ctypes.data, out.ctypes.data) == sea.SO2_ERR_INVALID_ARGUMENT
+
+
+def _desc(**kw):
+    base = dict(n_atoms=10, n_targets=10, n_edges=40, l_max=2, channels=16, heads=2, n_rbf=8,
+                envelope_p=5, cutoff=5.0, flags=0, dtype=sea.SO2_FP32)
+    base.update(kw)
+    return sea.make_desc(**base)
+
+
+def _fwd(desc, box=None, ws_bytes=None, null=()):
+    lib = sea.load_library()
+    names = ["pos", "box", "row_ptr", "col", "x", "w_q", "w_k", "w_rad", "w_so2", "y", "ws"]
+    keep, box_p = sea._host_box(box)
+    args = []
+    for name in names:
+        if name == "box":
+            args.append(box_p)
+        elif name in null:
+            args.append(ctypes.c_void_p(0))
+        else:
+            args.append(FAKE)
+    wsb = 0 if ws_bytes is None else ws_bytes
+    return lib.so2_attention_fwd(ctypes.byref(desc), *args, wsb, ctypes.c_void_p(0))
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(channels=15), sea.SO2_ERR_INVALID_ARGUMENT),  # C % H != 0
+        (dict(l_max=7), sea.SO2_ERR_UNSUPPORTED),
+        (dict(l_max=-1), sea.SO2_ERR_INVALID_ARGUMENT),
+        (dict(n_rbf=1), sea.SO2_ERR_INVALID_ARGUMENT),
+        (dict(cutoff=0.0), sea.SO2_ERR_INVALID_ARGUMENT),
+        (dict(cutoff=float("nan")), sea.SO2_ERR_INVALID_ARGUMENT),
+        (dict(n_targets=11), sea.SO2_ERR_INVALID_ARGUMENT),
+        (dict(n_atoms=0, n_targets=0), sea.SO2_ERR_INVALID_ARGUMENT),
+        (dict(flags=8), sea.SO2_ERR_INVALID_ARGUMENT),
+        (dict(dtype=7), sea.SO2_ERR_INVALID_ARGUMENT),
+        (dict(envelope_p=0), sea.SO2_ERR_INVALID_ARGUMENT),
+        (dict(channels=512, heads=8), sea.SO2_ERR_UNSUPPORTED),
+    ],
+)
+def test_attention_desc_errors(kw, status):
+    d = _desc(**kw)
+    assert _fwd(d, ws_bytes=1 << 40) == status
+    assert sea.attention_workspace_bytes(d) == 0
+
+
+def test_attention_pointer_box_and_workspace_errors():
+    d = _desc()
+    need = sea.attention_workspace_bytes(d)
+    assert need > 0
+    assert _fwd(d, ws_bytes=need, null=("x",)) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert _fwd(d, ws_bytes=need, null=("y",)) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert _fwd(d, ws_bytes=need, box=[10.0, 10.0, 10.0]) == sea.SO2_ERR_BOX  # 10 <= 2 * 5
+    assert _fwd(d, ws_bytes=need - 1) == sea.SO2_ERR_WORKSPACE
+    lib = sea.load_library()
+    misaligned = ctypes.c_void_p((1 << 30) + 4)
+    args = [FAKE, ctypes.c_void_p(0)] + [FAKE] * 8 + [misaligned]
+    assert lib.so2_attention_fwd(ctypes.byref(d), *args, need, ctypes.c_void_p(0)) == sea.SO2_ERR_WORKSPACE
+
+
+def test_kernel_kind_selection():
+    assert sea.attention_kernel_kind(_desc()) == sea.KERNEL_VALU
+    assert sea.attention_kernel_kind(_desc(l_max=7)) == sea.KERNEL_NONE
+
+
+def test_neighbor_errors_before_launch():
+    lib = sea.load_library()
+    n_e = ctypes.c_int64(0)
+    ws = sea.neighbors_workspace_bytes(100)
+    assert ws > 0
+    call = lambda pos, n, box, rc, rp, col, cap, wsp, wsb: lib.build_neighbors(
+        pos, n, None, box, ctypes.c_float(rc), rp, col, cap, ctypes.byref(n_e), wsp, wsb, None
+    )
+    keep, box_small = sea._host_box([9.0, 20.0, 20.0])
+    assert call(None, 100, None, 4.5, FAKE, FAKE, 10, FAKE, ws) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(FAKE, 0, None, 4.5, FAKE, FAKE, 10, FAKE, ws) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(FAKE, 100, None, -1.0, FAKE, FAKE, 10, FAKE, ws) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(FAKE, 100, box_small, 4.5, FAKE, FAKE, 10, FAKE, ws) == sea.SO2_ERR_BOX
+    assert call(FAKE, 100, None, 4.5, FAKE, FAKE, 10, FAKE, ws - 1) == sea.SO2_ERR_WORKSPACE
+    assert call(FAKE, 100, None, 4.5, FAKE, None, 10, FAKE, ws) == sea.SO2_ERR_INVALID_ARGUMENT

@@ -1,0 +1,199 @@
+"""Forward parity on the GPU: so2_attention_fwd (through the C ABI) against
+the fp64 oracle, element by element.
+
+* tiny_fp32: every atom, max relative error (normalised per atom) <= 1e-4;
+* bf16 workloads: a small batch of the same kind (several kernel tiles and a
+  ragged tail) on every atom, and the full-size workloads on seeded sampled
+  targets, at <= 2e-2 (the oracle gets the same bf16-rounded inputs);
+* edge cases: empty neighbourhoods, n_targets < n_atoms, L = 0 and L = 6,
+  odd channel counts, both flags;
+* GPU-side invariants: softmax weights summing to one, rotation
+  equivariance, bitwise determinism of repeated calls."""
+
+import numpy as np
+import pytest
+
+from helpers import TOL, csr_to_device, device_inputs, gpu_attention, oracle_attention, say
+from oracle import max_rel_error, neighbors_bruteforce, so2_weight_count, wigner_d_blocks
+from synth import make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_pair(w, targets=None, use_gpu_graph=False, **kw):
+    import torch
+
+    import so_equivariant_graph_amd as sea
+
+    d = device_inputs(w)
+    rp, col = neighbors_bruteforce(w.pos, w.cutoff, w.box, w.mol_id)
+    if use_gpu_graph:
+        rp_d, col_d = sea.build_neighbors(d["pos"], w.cutoff, box=w.box, mol_id=d["mol"])
+    else:
+        rp_d, col_d = csr_to_device(rp, col)
+    y = gpu_attention(w, d, rp_d, col_d, **kw)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    t = np.arange(w.n_atoms) if targets is None else np.asarray(targets)
+    y_ref = oracle_attention(w, rp, col, targets=t, **kw)
+    return y[t], y_ref
+
+
+def test_tiny_fp32_every_atom():
+    say("attention tiny_fp32 full")
+    w = make_workload("tiny_fp32")
+    y, y_ref = _run_pair(w, use_gpu_graph=True)
+    err = max_rel_error(y, y_ref)
+    say("max rel err", err)
+    assert err <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("flags", [1, 2])
+def test_tiny_fp32_flags(flags):
+    say("attention tiny flags", flags)
+    w = make_workload("tiny_fp32")
+    y, y_ref = _run_pair(w, flags=flags)
+    assert max_rel_error(y, y_ref) <= TOL["fp32"]
+
+
+def test_small_molecules_batch_every_atom_bf16():
+    say("attention small_molecules batch of 4")
+    w = make_workload("small_molecules", geometry=dict(n_molecules=4))
+    y, y_ref = _run_pair(w, use_gpu_graph=True)
+    err = max_rel_error(y, y_ref)
+    say("max rel err", err)
+    assert err <= TOL["bf16"]
+
+
+def _sampled(name, n_samples, seed=0):
+    import torch
+
+    import so_equivariant_graph_amd as sea
+
+    say("attention full-size sampled", name)
+    w = make_workload(name)
+    d = device_inputs(w)
+    rp_d, col_d = sea.build_neighbors(d["pos"], w.cutoff, box=w.box, mol_id=d["mol"])
+    y = gpu_attention(w, d, rp_d, col_d)
+    torch.cuda.synchronize()
+    rp, col = rp_d.cpu().numpy(), col_d.cpu().numpy()
+    # the oracle's own rows for the sampled targets decide the neighbour set
+    t = np.sort(np.random.default_rng(seed).choice(w.n_atoms, size=n_samples, replace=False))
+    t = np.unique(np.concatenate([t, [0, w.n_atoms - 1]]))
+    ref_rows = neighbors_bruteforce(w.pos, w.cutoff, w.box, w.mol_id, rows=t)
+    for i, r in zip(t, ref_rows):
+        assert np.array_equal(col[rp[i] : rp[i + 1]], r)
+    y_ref = oracle_attention(w, rp, col, targets=t)
+    err = max_rel_error(y[t].cpu().numpy(), y_ref)
+    say("max rel err", err, "targets", len(t))
+    assert np.all(np.isfinite(y.cpu().numpy()))
+    return err
+
+
+@pytest.mark.parametrize(
+    "name,n", [("small_molecules", 24), ("water_l6", 10), ("solvated_protein", 16), ("water_100k", 16)]
+)
+def test_full_size_sampled_targets_bf16(name, n):
+    assert _sampled(name, n) <= TOL["bf16"]
+
+
+def test_empty_neighbourhood_and_partial_targets():
+    say("attention empty rows, n_targets < n_atoms")
+    w = make_workload("tiny_fp32")
+    w.pos[5] = [500.0, 500.0, 500.0]  # isolated atom
+    y, y_ref = _run_pair(w)
+    assert np.all(y[5] == 0.0)
+    assert max_rel_error(y, y_ref) <= TOL["fp32"]
+    import torch
+
+    d = device_inputs(w)
+    rp, col = neighbors_bruteforce(w.pos, w.cutoff)
+    rp_d, col_d = csr_to_device(rp, col)
+    y_part = gpu_attention(w, d, rp_d, col_d, n_targets=17)
+    torch.cuda.synchronize()
+    assert y_part.shape[0] == 17
+    assert max_rel_error(y_part.cpu().numpy(), y_ref[:17]) <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("L,C,H,dtype", [(0, 8, 2, "fp32"), (6, 8, 1, "fp32"), (3, 3, 3, "fp32"), (2, 16, 4, "bf16")])
+def test_shapes(L, C, H, dtype):
+    say("attention shape", L, C, H, dtype)
+    w = make_workload("tiny_fp32", l_max=L, channels=C, heads=H, dtype=dtype)
+    y, y_ref = _run_pair(w)
+    assert max_rel_error(y, y_ref) <= TOL[dtype]
+
+
+def test_softmax_weights_sum_to_one_on_gpu():
+    say("attention softmax sum trick")
+    import torch
+
+    w = make_workload("small_molecules", geometry=dict(n_molecules=3), dtype="bf16")
+    L, C = w.l_max, w.channels
+    w.x[:] = 0.0
+    w.x[:, 0, :] = 1.0
+    blocks = [np.eye((L + 1) * C).ravel()]
+    for m in range(1, L + 1):
+        km = (L + 1 - m) * C
+        blocks += [np.eye(km).ravel(), np.zeros(km * km)]
+    w.w_so2 = np.concatenate(blocks).astype(np.float32)
+    assert w.w_so2.size == so2_weight_count(L, C)
+    d = device_inputs(w)
+    rp, col = neighbors_bruteforce(w.pos, w.cutoff, w.box, w.mol_id)
+    rp_d, col_d = csr_to_device(rp, col)
+    y = gpu_attention(w, d, rp_d, col_d, flags=2)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    has = np.diff(rp) > 0
+    np.testing.assert_allclose(y[has, 0, :], 1.0, atol=2e-2)
+    assert np.abs(y[has, 1:, :]).max() < 2e-2
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_rotation_equivariance_on_gpu(dtype):
+    say("attention equivariance", dtype)
+    import torch
+    from scipy.spatial.transform import Rotation
+
+    from synth import to_bf16_exact
+
+    w = make_workload("tiny_fp32", l_max=3, channels=16, heads=2, dtype=dtype)
+    R = Rotation.random(random_state=11).as_matrix()
+    D = wigner_d_blocks(w.l_max, R)
+
+    def rot(feat):
+        out = np.empty_like(feat)
+        for l in range(w.l_max + 1):
+            sl = slice(l * l, (l + 1) ** 2)
+            out[:, sl, :] = np.einsum("ab,nbc->nac", D[l], feat[:, sl, :])
+        return out
+
+    def run(pos, x):
+        w2 = make_workload("tiny_fp32", l_max=3, channels=16, heads=2, dtype=dtype)
+        w2.pos, w2.x = pos.astype(np.float32), x.astype(np.float32)
+        d = device_inputs(w2)
+        rp, col = neighbors_bruteforce(w2.pos, w2.cutoff)
+        y = gpu_attention(w2, d, *csr_to_device(rp, col))
+        torch.cuda.synchronize()
+        return y.cpu().numpy().astype(np.float64)
+
+    c = w.pos.mean(0)
+    x_r = rot(w.x)
+    if dtype == "bf16":
+        x_r = to_bf16_exact(x_r.astype(np.float32))
+    y = run(w.pos, w.x)
+    y_r = run((w.pos - c) @ R.T + c, x_r)
+    assert max_rel_error(y_r, rot(y)) <= TOL[dtype]
+
+
+def test_repeated_calls_are_bitwise_identical():
+    say("attention determinism")
+    import torch
+
+    w = make_workload("small_molecules", geometry=dict(n_molecules=3))
+    d = device_inputs(w)
+    rp, col = neighbors_bruteforce(w.pos, w.cutoff, w.box, w.mol_id)
+    rp_d, col_d = csr_to_device(rp, col)
+    a = gpu_attention(w, d, rp_d, col_d).clone()
+    b = gpu_attention(w, d, rp_d, col_d)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
