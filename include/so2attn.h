@@ -161,6 +161,13 @@ so2_status so2_attention_fwd(const so2_attn_desc* desc, const float* pos,
                              float* y, void* workspace, size_t workspace_bytes,
                              so2_stream_t stream);
 
+/* Benchmark hook: when both are non-NULL, every later so2_attention_fwd
+ * call from this thread records `start` on its stream just before the fused
+ * attention kernel and `stop` just after it (hipEvent_t handles created and
+ * owned by the caller), so the kernel alone can be timed on the stream it
+ * runs on.  so2_set_kernel_timing_events(NULL, NULL) switches it off. */
+void so2_set_kernel_timing_events(void* start, void* stop);
+
 /* ------------------------------------------------------------------------
  * Host-side diagnostics (no device work): evaluate, on the CPU, the same
  * edge-frame and Wigner-D code the kernels run in fp32, for tests.

@@ -47,6 +47,7 @@ EXPORTED_SYMBOLS = (
     "so2_attention_kernel_kind",
     "so2_attention_fwd",
     "so2_edge_frame_host",
+    "so2_set_kernel_timing_events",
 )
 
 
@@ -88,6 +89,10 @@ def load_library(path: str = LIB_PATH):
             f"{path} is missing: build it with `python -m so_equivariant_graph_amd.build` "
             "(the SO(2) attention path has no other implementation)"
         )
+    try:  # bind to the HIP runtime torch already uses, so there is only one
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.so2_status_string.argtypes = [ctypes.c_int]
@@ -108,6 +113,8 @@ def load_library(path: str = LIB_PATH):
     lib.so2_attention_fwd.restype = ctypes.c_int
     lib.so2_edge_frame_host.argtypes = [i32, vp, vp, vp]
     lib.so2_edge_frame_host.restype = ctypes.c_int
+    lib.so2_set_kernel_timing_events.argtypes = [vp, vp]
+    lib.so2_set_kernel_timing_events.restype = None
     _lib_handle = lib
     return lib
 
@@ -254,6 +261,62 @@ def so2_attention_fwd(pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, *, l_max, he
     )
     _check(st, "so2_attention_fwd")
     return y
+
+
+def hip_runtime():
+    """The libamdhip64 already loaded in this process (torch's), via ctypes."""
+    import re
+
+    load_library()
+    with open("/proc/self/maps") as f:
+        paths = sorted(set(re.findall(r"\S*libamdhip64\.so\S*", f.read())))
+    if not paths:
+        raise RuntimeError("no HIP runtime loaded")
+    hip = ctypes.CDLL(paths[0])
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+class KernelTimer:
+    """Times the fused attention kernel alone with HIP events recorded by the
+    library on the kernel's own stream (one event pair per call)."""
+
+    def __init__(self, n_calls: int):
+        self.hip = hip_runtime()
+        self.pairs = []
+        for _ in range(n_calls):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(a)) == 0
+            assert self.hip.hipEventCreate(ctypes.byref(b)) == 0
+            self.pairs.append((a, b))
+        self.k = 0
+
+    def arm(self):
+        a, b = self.pairs[self.k]
+        load_library().so2_set_kernel_timing_events(a, b)
+        self.k += 1
+
+    def disarm(self):
+        load_library().so2_set_kernel_timing_events(None, None)
+
+    def elapsed_ms(self):
+        out = []
+        for a, b in self.pairs[: self.k]:
+            self.hip.hipEventSynchronize(b)
+            ms = ctypes.c_float(0.0)
+            assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        self.disarm()
+        for a, b in self.pairs:
+            self.hip.hipEventDestroy(a)
+            self.hip.hipEventDestroy(b)
+        self.pairs = []
 
 
 def edge_frame_host(l_max: int, rhat):

@@ -11,6 +11,8 @@
 namespace so2 {
 
 static thread_local char g_last_error[256] = "";
+static thread_local hipEvent_t g_timing_start = nullptr;
+static thread_local hipEvent_t g_timing_stop = nullptr;
 
 so2_status device_error(hipError_t err) {
   snprintf(g_last_error, sizeof(g_last_error), "%s: %s", hipGetErrorName(err),
@@ -56,7 +58,7 @@ AttnLayout attn_layout(const so2_attn_desc* d, Kind kind) {
   L.k = off;
   off += align256(sizeof(float) * (size_t)d->n_atoms * d->channels);
   L.scratch = off;
-  L.scratch_bytes = kind == kMfma ? mfma_scratch_bytes(d->n_atoms, d->l_max, d->channels)
+  L.scratch_bytes = kind == kMfma ? mfma_scratch_bytes(d->n_targets, d->heads)
                                   : valu_scratch_bytes(d->l_max, d->channels);
   off += align256(L.scratch_bytes);
   L.total = off;
@@ -179,10 +181,25 @@ so2_status so2_attention_fwd(const so2_attn_desc* desc, const float* pos, const 
   a.periodic = box_host != nullptr;
   for (int d = 0; d < 3; ++d) a.box[d] = box_host ? box_host[d] : 0.0f;
 
+  if (kind == kMfma && !mfma_aligned(a)) return SO2_ERR_INVALID_ARGUMENT;
+
   hipStream_t s = (hipStream_t)stream;
   st = launch_qk_proj(a, s);
   if (st != SO2_OK) return st;
-  return kind == kMfma ? launch_attention_mfma(a, s) : launch_attention_valu(a, s);
+  if (kind == kMfma) {
+    st = launch_attention_mfma_prep(a, s);
+    if (st != SO2_OK) return st;
+  }
+  if (g_timing_start && g_timing_stop) SO2_CHECK(hipEventRecord(g_timing_start, s));
+  st = kind == kMfma ? launch_attention_mfma(a, s) : launch_attention_valu(a, s);
+  if (st != SO2_OK) return st;
+  if (g_timing_start && g_timing_stop) SO2_CHECK(hipEventRecord(g_timing_stop, s));
+  return SO2_OK;
+}
+
+void so2_set_kernel_timing_events(void* start, void* stop) {
+  g_timing_start = (hipEvent_t)start;
+  g_timing_stop = (hipEvent_t)stop;
 }
 
 so2_status so2_edge_frame_host(int32_t l_max, const float* rhat, float* R_out, float* D_out) {

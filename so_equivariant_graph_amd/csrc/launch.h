@@ -58,9 +58,13 @@ bool valu_supported(int L, int C, int H);
 size_t valu_scratch_bytes(int L, int C);
 so2_status launch_attention_valu(const AttnArgs& a, hipStream_t stream);
 
-// bf16 MFMA kernel (attention_mfma.hip).
+// bf16 MFMA kernel (attention_mfma.hip): C = 128, 1 <= L <= 4, H <= 16.
+// x, w_rad and w_so2 must be 16-byte aligned.
 bool mfma_supported(int L, int C, int H);
-size_t mfma_scratch_bytes(int n_atoms, int L, int C);
+bool mfma_aligned(const AttnArgs& a);
+size_t mfma_scratch_bytes(int n_targets, int H);
+// softmax statistics pass, then the fused kernel
+so2_status launch_attention_mfma_prep(const AttnArgs& a, hipStream_t stream);
 so2_status launch_attention_mfma(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace so2

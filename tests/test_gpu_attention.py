@@ -197,3 +197,83 @@ def test_repeated_calls_are_bitwise_identical():
     b = gpu_attention(w, d, rp_d, col_d)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- bf16 MFMA kernel
+
+
+def _kind(w, n_edges=1000):
+    import so_equivariant_graph_amd as sea
+
+    d = sea.make_desc(n_atoms=w.n_atoms, n_targets=w.n_atoms, n_edges=n_edges, l_max=w.l_max,
+                      channels=w.channels, heads=w.heads, n_rbf=w.n_rbf, envelope_p=w.envelope_p,
+                      cutoff=w.cutoff, flags=0, dtype=sea.SO2_BF16 if w.dtype == "bf16" else sea.SO2_FP32)
+    return sea.attention_kernel_kind(d)
+
+
+@pytest.mark.parametrize("name", ["small_molecules", "solvated_protein", "water_100k"])
+def test_l4_workloads_run_on_the_mfma_kernel(name):
+    import so_equivariant_graph_amd as sea
+
+    w = make_workload(name, with_features=False)
+    assert _kind(w) == sea.KERNEL_MFMA
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 4])
+def test_mfma_every_degree(L):
+    say("mfma L", L)
+    import so_equivariant_graph_amd as sea
+
+    w = make_workload("tiny_fp32", l_max=L, channels=128, heads=8, n_rbf=16, dtype="bf16")
+    assert _kind(w) == sea.KERNEL_MFMA
+    y, y_ref = _run_pair(w)
+    err = max_rel_error(y, y_ref)
+    say("max rel err", err)
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("heads", [1, 4, 16])
+def test_mfma_head_counts(heads):
+    say("mfma heads", heads)
+    w = make_workload("tiny_fp32", l_max=2, channels=128, heads=heads, n_rbf=8, dtype="bf16")
+    y, y_ref = _run_pair(w)
+    assert max_rel_error(y, y_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("flags", [1, 2])
+def test_mfma_flags(flags):
+    say("mfma flags", flags)
+    w = make_workload("small_molecules", geometry=dict(n_molecules=2))
+    y, y_ref = _run_pair(w, flags=flags)
+    assert max_rel_error(y, y_ref) <= TOL["bf16"]
+
+
+def test_mfma_ragged_degrees_and_split_targets():
+    """Degrees 0, 1, 2 and > 64 (one target spanning several 64-edge chunks),
+    a target count that is not a multiple of the 16-target group, and
+    n_targets < n_atoms."""
+    say("mfma ragged degrees")
+    import torch
+
+    rng = np.random.default_rng(7)
+    dense = rng.uniform(0, 4.0, size=(90, 3))  # about 90 neighbours each within rc = 5
+    sparse = np.array([[50, 0, 0], [53, 0, 0], [50, 4, 0], [80, 0, 0], [90, 0, 0], [93.5, 0, 0], [150, 0, 0]], float)
+    pos = np.vstack([dense, sparse, rng.uniform(200, 210, size=(40, 3))])
+    w = make_workload("tiny_fp32", l_max=4, channels=128, heads=8, n_rbf=16, dtype="bf16")
+    from synth import to_bf16_exact
+
+    n = pos.shape[0]
+    w.pos = pos.astype(np.float32)
+    w.x = to_bf16_exact(rng.standard_normal((n, 25, 128)).astype(np.float32))
+    rp, col = neighbors_bruteforce(w.pos, w.cutoff)
+    deg = np.diff(rp)
+    assert deg.max() > 64 and (deg == 0).any() and (deg == 1).any()
+    y, y_ref = _run_pair(w)
+    err = max_rel_error(y, y_ref)
+    say("max rel err", err, "max deg", deg.max())
+    assert err <= TOL["bf16"]
+    assert np.all(y[deg == 0] == 0.0)
+    d = device_inputs(w)
+    y_part = gpu_attention(w, d, *csr_to_device(rp, col), n_targets=101)
+    torch.cuda.synchronize()
+    assert max_rel_error(y_part.cpu().numpy(), y_ref[:101]) <= TOL["bf16"]
