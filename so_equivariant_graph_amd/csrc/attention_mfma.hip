@@ -65,6 +65,8 @@ constexpr int kTargetsPerGroup = 16;  // targets per workgroup
 constexpr int kKC = 64;               // channels per K chunk (2 MFMA K steps)
 constexpr int kApad = kKC + 8;        // LDS row pitch of the A chunk, bf16
 constexpr int kMaxHeads = 16;
+constexpr int kGpad = kC + 8;         // LDS row pitch of the radial gate, bf16
+constexpr int kMaxDeg = 2;            // output degrees per pass for m >= 1
 
 struct MfmaParams {
   const float* pos;
@@ -78,6 +80,8 @@ struct MfmaParams {
   float* stat_max;  // [n_targets][H]
   float* stat_inv;  // [n_targets][H]
   float* y;
+  uint32_t x_bytes;  // extent of x for its buffer descriptor (< 4 GiB)
+  uint32_t w_bytes;  // extent of w_so2
   int32_t n_targets, H, K, p;
   float cutoff;
   uint32_t flags;
@@ -88,14 +92,28 @@ struct MfmaParams {
 __device__ inline float bf_lo(unsigned int u) { return __uint_as_float(u << 16); }
 __device__ inline float bf_hi(unsigned int u) { return __uint_as_float(u & 0xffff0000u); }
 
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+// Two floats to packed bf16 (round to nearest even): one v_cvt_pk_bf16_f32.
 __device__ inline unsigned int pack_bf16x2(float a, float b) {
-  return (unsigned int)float_to_bf16(a) | ((unsigned int)float_to_bf16(b) << 16);
+  return __builtin_bit_cast(unsigned int, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ inline f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Raw buffer descriptor (gfx9 family: dword3 = 0x00020000).  Loads through
+// it take one 32-bit VGPR offset and return 0 past num_records bytes.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
 __device__ inline void edge_vec(const MfmaParams& P, int i, int j, float* r) {
@@ -165,16 +183,14 @@ struct Smem {
   int flush_t[kSlots];  // target written out from each slot after this chunk, or -1
   int row_j[kM];
   int row_slot[kM];
-  float row_rho[kM];
-  float row_u[kM];
 };
 
 template <int L>
 struct Lds {
   static constexpr size_t kHdr = (sizeof(Smem) + 15) & ~(size_t)15;
   static constexpr size_t kD = kHdr;                                    // float [kM][WT]
-  static constexpr size_t kG = kD + sizeof(float) * kM * Cfg<L>::WT;    // bf16 [kM][kC]
-  static constexpr size_t kW = kG + sizeof(uint16_t) * kM * kC;         // float [kM][kMaxHeads]
+  static constexpr size_t kG = kD + sizeof(float) * kM * Cfg<L>::WT;    // bf16 [kM][kGpad]
+  static constexpr size_t kW = kG + sizeof(uint16_t) * kM * kGpad;      // float [kM][kMaxHeads]
   static constexpr size_t kA = kW + sizeof(float) * kM * kMaxHeads;     // bf16 [2][2][kM][kApad]
   static constexpr size_t kAbuf = sizeof(uint16_t) * 2 * kM * kApad;    // one buffer, both signs
   static constexpr size_t kT = kA + 2 * kAbuf;                          // f32x4 [TT][kWaves][64]
@@ -187,43 +203,75 @@ __device__ inline f32x4* tacc_tile(char* smem, int ot, int wave) {
   return (f32x4*)(smem + Lds<L>::kT) + (ot * kWaves + wave) * 64;
 }
 
+// Edge er of the chunk: its target t (one of the slots' targets), source j
+// and minimum-image vector r_ij = p_j - p_t.
+__device__ inline void row_edge(const MfmaParams& P, const Smem& S, int er, int t_first, int& t, int& j,
+                                float* rv) {
+  int s = 0;
+  while (s + 1 < kSlots && S.rp[s + 1] <= er) ++s;
+  t = t_first + s;
+  j = P.col[er];
+  edge_vec(P, t, j, rv);
+}
+
 // ---------------------------------------------------------------- A operand
 
 // Build one A chunk: rows of 64 edges, 64 channels [cbase, cbase+64) of
 // degree lp, for +m and (m > 0) -m:  a[r][c] = g_r[c] sum_b D^lp_r[+-m][b] x_j[(lp,b)][c].
-template <int L>
-__device__ inline void gen_chunk(const MfmaParams& P, char* smem, int m, int lp, int cbase,
+// Lane (r = tid / 8, 8 channels at cbase + 8 (tid % 8)).  gen_load issues the
+// 2lp+1 gathers of x_j back to back (one 16-byte load each); gen_store
+// combines them with the edge's Wigner-D rows and the radial gate.
+constexpr int kMaxComp = 2 * 4 + 1;  // 2 L + 1 for L <= 4
+
+__device__ inline void gen_load(__amdgpu_buffer_rsrc_t xrs, const Smem& S, int NC, int lp, int cbase,
+                                u32x4 (&xr)[kMaxComp]) {
+  const int tid = threadIdx.x;
+  const int r = tid >> 3;
+  const int c = cbase + 8 * (tid & 7);
+  const int j = S.row_j[r];
+  const int n = 2 * lp + 1;
+  const uint32_t voff = (((uint32_t)(j < 0 ? 0 : j) * NC + lp * lp) * kC + c) * 2u;
+#pragma unroll
+  for (int b = 0; b < kMaxComp; ++b)
+    if (b < n && j >= 0) xr[b] = buffer_load16(xrs, voff + b * kC * 2, 0);
+}
+
+template <int L, int NS>
+__device__ inline void gen_store(char* smem, int m, int lp, int cbase, const u32x4 (&xr)[kMaxComp],
                                  uint16_t* abuf) {
   const Smem& S = *(const Smem*)smem;
   const float* sD = (const float*)(smem + Lds<L>::kD);
   const uint16_t* sG = (const uint16_t*)(smem + Lds<L>::kG);
   const int tid = threadIdx.x;
-  const int r = tid >> 3;  // edge row
-  const int cg = tid & 7;  // 8-channel group
+  const int r = tid >> 3;
+  const int cg = tid & 7;
   const int c = cbase + 8 * cg;
   const int j = S.row_j[r];
+  const int n = 2 * lp + 1;
   float ap[8], am[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) ap[q] = am[q] = 0.0f;
   if (j >= 0) {
-    const int n = 2 * lp + 1;
     const float* Dl = sD + r * Cfg<L>::WT + wig_offset(lp);
     const float* dp = Dl + (lp + m) * n;
     const float* dm = Dl + (lp - m) * n;
-    const uint16_t* xr = P.x + ((int64_t)j * Cfg<L>::NC + lp * lp) * kC + c;
-    for (int b = 0; b < n; ++b) {
-      const u32x4 v = *(const u32x4*)(xr + b * kC);
-      const float xv[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
-                           bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
-      const float wp = dp[b];
-      const float wm = dm[b];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        ap[q] += wp * xv[q];
-        am[q] += wm * xv[q];
+    for (int b = 0; b < kMaxComp; ++b) {
+      if (b < n) {
+        const u32x4 v = xr[b];
+        const float xv[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
+                             bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
+        const float wp = dp[b];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ap[q] += wp * xv[q];
+        if (NS > 1) {
+          const float wm = dm[b];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) am[q] += wm * xv[q];
+        }
       }
     }
-    const u32x4 gv = *(const u32x4*)(sG + r * kC + c);
+    const u32x4 gv = *(const u32x4*)(sG + r * kGpad + c);
     const float g[8] = {bf_lo(gv.x), bf_hi(gv.x), bf_lo(gv.y), bf_hi(gv.y),
                         bf_lo(gv.z), bf_hi(gv.z), bf_lo(gv.w), bf_hi(gv.w)};
 #pragma unroll
@@ -238,7 +286,7 @@ __device__ inline void gen_chunk(const MfmaParams& P, char* smem, int m, int lp,
   op.z = pack_bf16x2(ap[4], ap[5]);
   op.w = pack_bf16x2(ap[6], ap[7]);
   *(u32x4*)(abuf + r * kApad + 8 * cg) = op;
-  if (m > 0) {
+  if (NS > 1) {
     u32x4 om;
     om.x = pack_bf16x2(am[0], am[1]);
     om.y = pack_bf16x2(am[2], am[3]);
@@ -255,66 +303,86 @@ __device__ inline void gen_chunk(const MfmaParams& P, char* smem, int m, int lp,
 //   m = 0:  acc[d][0] += xt_0 W0^T
 //   m > 0:  acc[d][0] += xt_+ W1^T - xt_- W2^T,  acc[d][1] += xt_+ W2^T + xt_- W1^T
 // for output degrees lo .. lo+nd-1 (nd <= ND) of this wave's 16 channels.
+// The K steps (32 inputs each, two per A chunk) run as one flat loop; the B
+// fragments of step s+1 are loaded before the MFMAs of step s.
+template <int L, int ND, int NS>
+__device__ inline void load_b(__amdgpu_buffer_rsrc_t wrs, uint32_t w1_byte, uint32_t w2_byte, int KM,
+                              int m, int lo, int nd, int s, u32x4 (&b1)[ND], u32x4 (&b2)[ND]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int q = s >> 1;
+  const int kin = (q / (kC / kKC)) * kC + kKC * (q % (kC / kKC)) + 32 * (s & 1) + 8 * (lane >> 4);
+#pragma unroll
+  for (int di = 0; di < ND; ++di) {
+    if (di < nd) {
+      const int row = (lo + di - m) * kC + 16 * wave + (lane & 15);
+      const uint32_t voff = (uint32_t)(row * KM + kin) * 2u;
+      b1[di] = buffer_load16(wrs, voff, w1_byte);
+      if (NS > 1) b2[di] = buffer_load16(wrs, voff, w2_byte);
+    }
+  }
+}
+
 template <int L, int ND, int NS>
 __device__ inline void main_gemm(const MfmaParams& P, char* smem, int m, int lo, int nd,
                                  f32x4 (&acc)[ND][NS][kRT]) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
   uint16_t* abase = (uint16_t*)(smem + Lds<L>::kA);
   const int KM = (L + 1 - m) * kC;
   const int NQ = (L + 1 - m) * (kC / kKC);
-  const uint16_t* W1 = P.w_so2 + (m == 0 ? 0 : so2_w1_offset(L, kC, m));
-  const uint16_t* W2 = W1 + (int64_t)KM * KM;
+  const uint32_t w1_byte = (uint32_t)(m == 0 ? 0 : so2_w1_offset(L, kC, m)) * 2u;
+  const uint32_t w2_byte = w1_byte + (uint32_t)(KM * KM) * 2u;
+  const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(P.w_so2, P.w_bytes);
+  const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(P.x, P.x_bytes);
 
-  gen_chunk<L>(P, smem, m, m, 0, abase);
+  const Smem& S = *(const Smem*)smem;
+  constexpr int NC = Cfg<L>::NC;
+  u32x4 b1[ND], b2[ND], n1[ND], n2[ND];
+  u32x4 xr[kMaxComp];
+  load_b<L, ND, NS>(wrs, w1_byte, w2_byte, KM, m, lo, nd, 0, b1, b2);
+  gen_load(xrs, S, NC, m, 0, xr);
+  gen_store<L, NS>(smem, m, m, 0, xr, abase);
   __syncthreads();
-  for (int q = 0; q < NQ; ++q) {
-    const int lp = m + q / (kC / kKC);
-    const int cb = kKC * (q % (kC / kKC));
+  for (int s = 0; s < 2 * NQ; ++s) {
+    const int q = s >> 1;
+    const int ks = s & 1;
     const uint16_t* abuf = abase + (q & 1) * (2 * kM * kApad);
-    if (q + 1 < NQ) {
-      const int lq = m + (q + 1) / (kC / kKC);
-      const int cq = kKC * ((q + 1) % (kC / kKC));
-      gen_chunk<L>(P, smem, m, lq, cq, abase + ((q + 1) & 1) * (2 * kM * kApad));
-    }
+    const int lq = m + (q + 1) / (kC / kKC);      // next A chunk
+    const int cq = kKC * ((q + 1) % (kC / kKC));
+    // gathers for the next A chunk go out first; they land during this chunk's MFMAs
+    if (ks == 0 && q + 1 < NQ) gen_load(xrs, S, NC, lq, cq, xr);
+    if (s + 1 < 2 * NQ) load_b<L, ND, NS>(wrs, w1_byte, w2_byte, KM, m, lo, nd, s + 1, n1, n2);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 b1[ND], b2[ND];
-      const int kin = (lp - m) * kC + cb + 32 * ks + 8 * g4;
+    for (int rt = 0; rt < kRT; ++rt) {
+      const int off = (16 * rt + l16) * kApad + 32 * ks + 8 * g4;
+      const u32x4 ap = *(const u32x4*)(abuf + off);
+      if (NS == 1) {
 #pragma unroll
-      for (int di = 0; di < ND; ++di) {
-        if (di < nd) {
-          const int row = (lo + di - m) * kC + 16 * wave + l16;
-          b1[di] = *(const u32x4*)(W1 + (int64_t)row * KM + kin);
-          if (NS > 1) b2[di] = *(const u32x4*)(W2 + (int64_t)row * KM + kin);
-        }
-      }
+        for (int di = 0; di < ND; ++di)
+          acc[di][0][rt] = mfma(as_bf16x8(ap), as_bf16x8(b1[di]), acc[di][0][rt]);
+      } else {
+        const u32x4 am = *(const u32x4*)(abuf + kM * kApad + off);
+        const u32x4 amn = am ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
 #pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) {
-        const int off = (16 * rt + l16) * kApad + 32 * ks + 8 * g4;
-        const u32x4 ap = *(const u32x4*)(abuf + off);
-        if (NS == 1) {
-#pragma unroll
-          for (int di = 0; di < ND; ++di)
+        for (int di = 0; di < ND; ++di) {
+          if (di < nd) {
             acc[di][0][rt] = mfma(as_bf16x8(ap), as_bf16x8(b1[di]), acc[di][0][rt]);
-        } else {
-          const u32x4 am = *(const u32x4*)(abuf + kM * kApad + off);
-          const u32x4 amn = am ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-#pragma unroll
-          for (int di = 0; di < ND; ++di) {
-            if (di < nd) {
-              acc[di][0][rt] = mfma(as_bf16x8(ap), as_bf16x8(b1[di]), acc[di][0][rt]);
-              acc[di][0][rt] = mfma(as_bf16x8(amn), as_bf16x8(b2[di]), acc[di][0][rt]);
-              acc[di][NS - 1][rt] = mfma(as_bf16x8(ap), as_bf16x8(b2[di]), acc[di][NS - 1][rt]);
-              acc[di][NS - 1][rt] = mfma(as_bf16x8(am), as_bf16x8(b1[di]), acc[di][NS - 1][rt]);
-            }
+            acc[di][0][rt] = mfma(as_bf16x8(amn), as_bf16x8(b2[di]), acc[di][0][rt]);
+            acc[di][NS - 1][rt] = mfma(as_bf16x8(ap), as_bf16x8(b2[di]), acc[di][NS - 1][rt]);
+            acc[di][NS - 1][rt] = mfma(as_bf16x8(am), as_bf16x8(b1[di]), acc[di][NS - 1][rt]);
           }
         }
       }
     }
-    __syncthreads();
+    if (ks == 1 && q + 1 < NQ) gen_store<L, NS>(smem, m, lq, cq, xr, abase + ((q + 1) & 1) * (2 * kM * kApad));
+#pragma unroll
+    for (int di = 0; di < ND; ++di) {
+      b1[di] = n1[di];
+      b2[di] = n2[di];
+    }
+    if (ks == 1) __syncthreads();
   }
 }
 
@@ -330,17 +398,69 @@ __device__ inline void main_gemm(const MfmaParams& P, char* smem, int m, int lo,
 //   m = 0:  edge 16 (2 st + jj / 4) + 4 g + (jj & 3);
 // A' row R of the accumulator (R = kSlots l^2 + slot (2l+1) + m' + l) holds
 // D^l_e[l +- m][m' + l] in the same K order when edge e belongs to that
-// slot's target, 0 otherwise (and 0 on rows of other degrees).
-template <int L, int NS>
-__device__ inline void rot_back(char* smem, const f32x4 (&yt)[NS][kRT], int m, int l, int head) {
+// slot's target, 0 otherwise (and 0 on rows of other degrees).  A' does not
+// depend on the output channels, so the whole workgroup builds it once per
+// pass into LDS (aprime_build) and every wave reads it from there.
+
+__device__ inline int deg_tiles(int l) {
+  return (kSlots * (l + 1) * (l + 1) - 1) / 16 - (kSlots * l * l) / 16 + 1;
+}
+
+// A' fragments of a pass (degrees lo .. lo+nd-1), in the order
+// (degree, tile, K step), 64 lanes x 16 bytes each, written to frag.
+template <int L>
+__device__ inline void aprime_build(char* smem, int m, int lo, int nd, u32x4* frag) {
   const Smem& S = *(const Smem*)smem;
   const float* sD = (const float*)(smem + Lds<L>::kD);
+  const int steps = m == 0 ? kRT / 2 : kRT;
+  int total = 0;
+  for (int di = 0; di < nd; ++di) total += deg_tiles(lo + di) * steps;
+  for (int idx = threadIdx.x; idx < total * 64; idx += kThreads) {
+    int f = idx >> 6;
+    const int lane = idx & 63;
+    int l = lo;
+    while (f >= deg_tiles(l) * steps) {
+      f -= deg_tiles(l) * steps;
+      ++l;
+    }
+    const int ot = (kSlots * l * l) / 16 + f / steps;
+    const int st = f % steps;
+    const int n = 2 * l + 1;
+    const int r0 = kSlots * l * l, r1 = kSlots * (l + 1) * (l + 1);
+    const int R = 16 * ot + (lane & 15);
+    const bool mine = R >= r0 && R < r1;
+    const int oslot = mine ? (R - r0) / n : -1;
+    const int omp = mine ? (R - r0) - oslot * n : 0;
+    const int g4 = lane >> 4;
+    float av[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      int r, srow;
+      if (m > 0) {
+        r = 16 * st + 4 * g4 + (jj & 3);
+        srow = (jj < 4) ? (l + m) : (l - m);
+      } else {
+        r = 16 * (2 * st + (jj >> 2)) + 4 * g4 + (jj & 3);
+        srow = l;
+      }
+      av[jj] = S.row_slot[r] == oslot ? sD[r * Cfg<L>::WT + wig_offset(l) + srow * n + omp] : 0.0f;
+    }
+    u32x4 a;
+    a.x = pack_bf16x2(av[0], av[1]);
+    a.y = pack_bf16x2(av[2], av[3]);
+    a.z = pack_bf16x2(av[4], av[5]);
+    a.w = pack_bf16x2(av[6], av[7]);
+    frag[idx] = a;
+  }
+}
+
+template <int L, int NS>
+__device__ inline void rot_back(char* smem, const f32x4 (&yt)[NS][kRT], int l, int head,
+                                const u32x4* frag) {
   const float* sW = (const float*)(smem + Lds<L>::kW);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int l16 = lane & 15;
   const int g4 = lane >> 4;
-  const int n = 2 * l + 1;
   constexpr bool M0 = NS == 1;
   u32x4 bq[kRT];
 #pragma unroll
@@ -368,36 +488,14 @@ __device__ inline void rot_back(char* smem, const f32x4 (&yt)[NS][kRT], int m, i
     }
   }
   constexpr int kSteps = M0 ? kRT / 2 : kRT;
-  const int r0 = kSlots * l * l;              // first accumulator row of degree l
-  const int r1 = kSlots * (l + 1) * (l + 1);  // one past the last
-  for (int ot = r0 / 16; ot <= (r1 - 1) / 16; ++ot) {
-    const int R = 16 * ot + l16;  // this lane's A' row
-    const bool mine = R >= r0 && R < r1;
-    const int oslot = mine ? (R - r0) / n : -1;
-    const int omp = mine ? (R - r0) - oslot * n : 0;
-    f32x4* tile = tacc_tile<L>(smem, ot, wave);
+  const int ot0 = (kSlots * l * l) / 16;
+  const int nt = deg_tiles(l);
+  for (int q = 0; q < nt; ++q) {
+    f32x4* tile = tacc_tile<L>(smem, ot0 + q, wave);
     f32x4 tv = tile[lane];
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
-      float av[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        int r, srow;
-        if (!M0) {
-          r = 16 * st + 4 * g4 + (jj & 3);
-          srow = (jj < 4) ? (l + m) : (l - m);
-        } else {
-          r = 16 * (2 * st + (jj >> 2)) + 4 * g4 + (jj & 3);
-          srow = l;
-        }
-        const bool hit = S.row_slot[r] == oslot;
-        av[jj] = hit ? sD[r * Cfg<L>::WT + wig_offset(l) + srow * n + omp] : 0.0f;
-      }
-      u32x4 a;
-      a.x = pack_bf16x2(av[0], av[1]);
-      a.y = pack_bf16x2(av[2], av[3]);
-      a.z = pack_bf16x2(av[4], av[5]);
-      a.w = pack_bf16x2(av[6], av[7]);
+      const u32x4 a = frag[(q * kSteps + st) * 64 + lane];
       tv = mfma(as_bf16x8(a), as_bf16x8(bq[M0 ? 2 * st : st]), tv);
     }
     tile[lane] = tv;
@@ -406,30 +504,31 @@ __device__ inline void rot_back(char* smem, const f32x4 (&yt)[NS][kRT], int m, i
 
 // ---------------------------------------------------------------- passes
 
-// Block m = 0, all output degrees 0..L in one pass.
-template <int L>
-__device__ inline void pass_m0(const MfmaParams& P, char* smem, int head) {
-  f32x4 acc[L + 1][1][kRT];
+// One pass: block m, output degrees lo .. lo+nd-1 (nd <= ND): main GEMM,
+// then the A' fragments, then the rotate-back GEMM of each degree.
+template <int L, int ND, int NS>
+__device__ inline void pass(const MfmaParams& P, char* smem, int m, int lo, int nd, int head) {
+  f32x4 acc[ND][NS][kRT];
 #pragma unroll
-  for (int a = 0; a <= L; ++a)
+  for (int a = 0; a < ND; ++a)
 #pragma unroll
-    for (int c = 0; c < kRT; ++c) acc[a][0][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  main_gemm<L, L + 1, 1>(P, smem, 0, 0, L + 1, acc);
+    for (int b = 0; b < NS; ++b)
 #pragma unroll
-  for (int l = 0; l <= L; ++l) rot_back<L, 1>(smem, acc[l], 0, l, head);
-}
-
-// Block m >= 1, output degrees lo .. lo+nd-1 (nd <= 2).
-template <int L>
-__device__ inline void pass_m(const MfmaParams& P, char* smem, int m, int lo, int nd, int head) {
-  f32x4 acc[2][2][kRT];
+      for (int c = 0; c < kRT; ++c) acc[a][b][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  main_gemm<L, ND, NS>(P, smem, m, lo, nd, acc);  // ends with a barrier
+  u32x4* frag = (u32x4*)(smem + Lds<L>::kA);       // the A chunks are dead now
+  aprime_build<L>(smem, m, lo, nd, frag);
+  __syncthreads();
+  const int steps = NS == 1 ? kRT / 2 : kRT;
+  int fbase = 0;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int c = 0; c < kRT; ++c) acc[a][0][c] = acc[a][1][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  main_gemm<L, 2, 2>(P, smem, m, lo, nd, acc);
-  rot_back<L, 2>(smem, acc[0], m, lo, head);
-  if (nd > 1) rot_back<L, 2>(smem, acc[1], m, lo + 1, head);
+  for (int di = 0; di < ND; ++di) {
+    if (di < nd) {
+      rot_back<L, NS>(smem, acc[di], lo + di, head, frag + fbase * 64);
+      fbase += deg_tiles(lo + di) * steps;
+    }
+  }
+  __syncthreads();  // the next pass overwrites the fragments
 }
 
 // ---------------------------------------------------------------- flush
@@ -512,111 +611,104 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(MfmaParams P, int n
       const int t = t_first + ((tid - t_first % kSlots + kSlots) % kSlots);
       S.flush_t[tid] = (t <= t_first + sl && S.rp[t - t_first + 1] <= e_stop) ? t : -1;
     }
-    for (int pr = tid; pr < kM * kMaxHeads; pr += kThreads) {
-      const int r = pr / kMaxHeads, h = pr % kMaxHeads;
-      float wv = 0.0f;
-      if (r < nrows && h < H) {
-        const int er = e + r;
-        int s = 0;
-        while (s + 1 < kSlots && S.rp[s + 1] <= er) ++s;
-        const int t = t_first + s;
-        const int j = P.col[er];
+    if (tid < kM) {
+      // wave 0: one edge per lane: metadata, frame and all Wigner-D blocks
+      const int r = tid;
+      if (r < nrows) {
+        int t, j;
         float rv[3];
-        edge_vec(P, t, j, rv);
+        row_edge(P, S, e + r, t_first, t, j, rv);
         const float rho = sqrtf(rv[0] * rv[0] + rv[1] * rv[1] + rv[2] * rv[2]);
-        const float u = envelope_u(rho / rc, P.p);
-        float z = 0.0f;
-        for (int c = h * dh; c < (h + 1) * dh; ++c) z += P.q[(int64_t)t * kC + c] * P.k[(int64_t)j * kC + c];
-        z *= inv_sqrt_d;
-        wv = u * expf(z - P.stat_max[(int64_t)t * H + h]) * P.stat_inv[(int64_t)t * H + h];
-        if (h == 0) {
-          S.row_j[r] = j;
-          S.row_slot[r] = t % kSlots;
-          S.row_rho[r] = rho;
-          S.row_u[r] = u;
-          const float inv = rho > 0.0f ? 1.0f / rho : 0.0f;
-          float R[9];
-          edge_frame(rv[0] * inv, rv[1] * inv, rv[2] * inv, R);
-          float* Dr = sD + r * Cfg<L>::WT;
-          Dr[0] = 1.0f;
-          wigner_l1(R, Dr + 1);
-        }
-      } else if (r >= nrows && h == 0) {
+        S.row_j[r] = j;
+        S.row_slot[r] = t % kSlots;
+        const float inv = rho > 0.0f ? 1.0f / rho : 0.0f;
+        float R[9];
+        edge_frame(rv[0] * inv, rv[1] * inv, rv[2] * inv, R);
+        wigner_blocks_unrolled<L>(R, sD + r * Cfg<L>::WT);
+      } else {
         S.row_j[r] = -1;
         S.row_slot[r] = -2;  // matches no slot
-        S.row_rho[r] = 0.0f;
-        S.row_u[r] = 0.0f;
       }
-      sW[r * kMaxHeads + h] = wv;
-    }
-    __syncthreads();
-    // radial gate g[r][c] (bf16) and Wigner-D degrees 2..L
-    for (int pr = tid; pr < kM * (kC / 16); pr += kThreads) {
-      const int r = pr / (kC / 16), c0 = 16 * (pr % (kC / 16));
-      float gv[16];
+    } else {
+      // waves 1..7: radial gates (64 rows x 8 groups of 16 channels), then
+      // the softmax weights (64 rows x kMaxHeads)
+      for (int it = tid - kM; it < kM * (kC / 16) + kM * kMaxHeads; it += kThreads - kM) {
+        if (it < kM * (kC / 16)) {
+          const int r = it / (kC / 16), c0 = 16 * (it % (kC / 16));
+          float gv[16];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) gv[q] = 0.0f;
-      if (r < nrows) {
-        if (P.flags & SO2_FLAG_NO_RADIAL) {
+          for (int q = 0; q < 16; ++q) gv[q] = 0.0f;
+          if (r < nrows) {
+            if (P.flags & SO2_FLAG_NO_RADIAL) {
 #pragma unroll
-          for (int q = 0; q < 16; ++q) gv[q] = 1.0f;
+              for (int q = 0; q < 16; ++q) gv[q] = 1.0f;
+            } else {
+              int t, j;
+              float rv[3];
+              row_edge(P, S, e + r, t_first, t, j, rv);
+              const float rho = sqrtf(rv[0] * rv[0] + rv[1] * rv[1] + rv[2] * rv[2]);
+              const float step = rc / (float)(P.K - 1);
+              const float inv2s2 = 1.0f / (2.0f * step * step);
+              for (int kk = 0; kk < P.K; ++kk) {
+                const float dr = rho - step * (float)kk;
+                const float phi = expf(-dr * dr * inv2s2);
+                const uint16_t* wr = P.w_rad + (int64_t)kk * kC + c0;
+                const u32x4 v0 = *(const u32x4*)wr;
+                const u32x4 v1 = *(const u32x4*)(wr + 8);
+                const float wv[16] = {bf_lo(v0.x), bf_hi(v0.x), bf_lo(v0.y), bf_hi(v0.y),
+                                      bf_lo(v0.z), bf_hi(v0.z), bf_lo(v0.w), bf_hi(v0.w),
+                                      bf_lo(v1.x), bf_hi(v1.x), bf_lo(v1.y), bf_hi(v1.y),
+                                      bf_lo(v1.z), bf_hi(v1.z), bf_lo(v1.w), bf_hi(v1.w)};
+#pragma unroll
+                for (int q = 0; q < 16; ++q) gv[q] += phi * wv[q];
+              }
+              if (P.flags & SO2_FLAG_RBF_ENVELOPE) {
+                const float u = envelope_u(rho / rc, P.p);
+#pragma unroll
+                for (int q = 0; q < 16; ++q) gv[q] *= u;
+              }
+            }
+          }
+          u32x4 g0, g1;
+          g0.x = pack_bf16x2(gv[0], gv[1]);
+          g0.y = pack_bf16x2(gv[2], gv[3]);
+          g0.z = pack_bf16x2(gv[4], gv[5]);
+          g0.w = pack_bf16x2(gv[6], gv[7]);
+          g1.x = pack_bf16x2(gv[8], gv[9]);
+          g1.y = pack_bf16x2(gv[10], gv[11]);
+          g1.z = pack_bf16x2(gv[12], gv[13]);
+          g1.w = pack_bf16x2(gv[14], gv[15]);
+          *(u32x4*)(sG + r * kGpad + c0) = g0;
+          *(u32x4*)(sG + r * kGpad + c0 + 8) = g1;
         } else {
-          const float rho = S.row_rho[r];
-          const float step = rc / (float)(P.K - 1);
-          const float inv2s2 = 1.0f / (2.0f * step * step);
-          for (int kk = 0; kk < P.K; ++kk) {
-            const float dr = rho - step * (float)kk;
-            const float phi = expf(-dr * dr * inv2s2);
-            const uint16_t* wr = P.w_rad + (int64_t)kk * kC + c0;
-            const u32x4 v0 = *(const u32x4*)wr;
-            const u32x4 v1 = *(const u32x4*)(wr + 8);
-            const float wv[16] = {bf_lo(v0.x), bf_hi(v0.x), bf_lo(v0.y), bf_hi(v0.y),
-                                  bf_lo(v0.z), bf_hi(v0.z), bf_lo(v0.w), bf_hi(v0.w),
-                                  bf_lo(v1.x), bf_hi(v1.x), bf_lo(v1.y), bf_hi(v1.y),
-                                  bf_lo(v1.z), bf_hi(v1.z), bf_lo(v1.w), bf_hi(v1.w)};
-#pragma unroll
-            for (int q = 0; q < 16; ++q) gv[q] += phi * wv[q];
+          const int pr = it - kM * (kC / 16);
+          const int r = pr / kMaxHeads, h = pr % kMaxHeads;
+          float wv = 0.0f;
+          if (r < nrows && h < H) {
+            int t, j;
+            float rv[3];
+            row_edge(P, S, e + r, t_first, t, j, rv);
+            const float rho = sqrtf(rv[0] * rv[0] + rv[1] * rv[1] + rv[2] * rv[2]);
+            const float u = envelope_u(rho / rc, P.p);
+            float z = 0.0f;
+            for (int c = h * dh; c < (h + 1) * dh; ++c) z += P.q[(int64_t)t * kC + c] * P.k[(int64_t)j * kC + c];
+            z *= inv_sqrt_d;
+            wv = u * expf(z - P.stat_max[(int64_t)t * H + h]) * P.stat_inv[(int64_t)t * H + h];
           }
-          if (P.flags & SO2_FLAG_RBF_ENVELOPE) {
-            const float u = S.row_u[r];
-#pragma unroll
-            for (int q = 0; q < 16; ++q) gv[q] *= u;
-          }
+          sW[r * kMaxHeads + h] = wv;
         }
       }
-      u32x4 g0, g1;
-      g0.x = pack_bf16x2(gv[0], gv[1]);
-      g0.y = pack_bf16x2(gv[2], gv[3]);
-      g0.z = pack_bf16x2(gv[4], gv[5]);
-      g0.w = pack_bf16x2(gv[6], gv[7]);
-      g1.x = pack_bf16x2(gv[8], gv[9]);
-      g1.y = pack_bf16x2(gv[10], gv[11]);
-      g1.z = pack_bf16x2(gv[12], gv[13]);
-      g1.w = pack_bf16x2(gv[14], gv[15]);
-      *(u32x4*)(sG + r * kC + c0) = g0;
-      *(u32x4*)(sG + r * kC + c0 + 8) = g1;
-    }
-    for (int l = 2; l <= L; ++l) {
-      const int n = 2 * l + 1;
-      for (int pr = tid; pr < kM * n * n; pr += kThreads) {
-        const int r = pr / (n * n), q = pr % (n * n);
-        if (r < nrows) {
-          float* Dr = sD + r * Cfg<L>::WT;
-          Dr[wig_offset(l) + q] = wigner_entry(l, q / n - l, q % n - l, Dr + 1, Dr + wig_offset(l - 1));
-        }
-      }
-      __syncthreads();
     }
     __syncthreads();
 
     // ---- phase B: per-m GEMMs and the rotate-back GEMMs
-    pass_m0<L>(P, smem, head);
+#pragma nounroll
+    for (int lo = 0; lo <= L; lo += 3) pass<L, 3, 1>(P, smem, 0, lo, min(3, L + 1 - lo), head);
 #pragma nounroll
     for (int m = 1; m <= L; ++m) {
 #pragma nounroll
-      for (int lo = m; lo <= L; lo += 2) pass_m<L>(P, smem, m, lo, min(2, L + 1 - lo), head);
+      for (int lo = m; lo <= L; lo += kMaxDeg) pass<L, kMaxDeg, 2>(P, smem, m, lo, min(kMaxDeg, L + 1 - lo), head);
     }
-    __syncthreads();
 
     // ---- phase D: write out targets whose last edge is in this chunk
     flush_slots<L>(smem, P.y);
@@ -651,6 +743,8 @@ MfmaParams make_params(const AttnArgs& a) {
   P.stat_max = stats;
   P.stat_inv = stats + (size_t)a.n_targets * a.H;
   P.y = a.y;
+  P.x_bytes = (uint32_t)((uint64_t)a.n_atoms * (a.L + 1) * (a.L + 1) * kC * 2);
+  P.w_bytes = (uint32_t)(so2_w1_offset(a.L, kC, a.L + 1) * 2);
   P.n_targets = a.n_targets;
   P.H = a.H;
   P.K = a.K;
@@ -664,8 +758,11 @@ MfmaParams make_params(const AttnArgs& a) {
 
 }  // namespace
 
-bool mfma_supported(int L, int C, int H) {
-  return C == kC && L >= 1 && L <= 4 && H >= 1 && H <= kMaxHeads && C % H == 0;
+bool mfma_supported(int L, int C, int H, int n_atoms) {
+  // x is addressed through a 32-bit buffer descriptor
+  const uint64_t x_bytes = (uint64_t)n_atoms * (L + 1) * (L + 1) * C * 2;
+  return C == kC && L >= 1 && L <= 4 && H >= 1 && H <= kMaxHeads && C % H == 0 &&
+         x_bytes < 0xffffffffull;
 }
 
 bool mfma_aligned(const AttnArgs& a) {

@@ -60,7 +60,7 @@ so2_status launch_attention_valu(const AttnArgs& a, hipStream_t stream);
 
 // bf16 MFMA kernel (attention_mfma.hip): C = 128, 1 <= L <= 4, H <= 16.
 // x, w_rad and w_so2 must be 16-byte aligned.
-bool mfma_supported(int L, int C, int H);
+bool mfma_supported(int L, int C, int H, int n_atoms);
 bool mfma_aligned(const AttnArgs& a);
 size_t mfma_scratch_bytes(int n_targets, int H);
 // softmax statistics pass, then the fused kernel

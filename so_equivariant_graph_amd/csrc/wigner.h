@@ -58,8 +58,9 @@ __host__ __device__ inline void wigner_l1(const float* R, float* D1) {
 
 // One entry D^l[m][mp] (l >= 2) from D^1 (3x3, m-ordered) and D^{l-1}
 // ((2l-1)^2 row-major, m-ordered).
-__host__ __device__ inline float wigner_entry(int l, int m, int mp, const float* D1,
-                                              const float* Dp) {
+__host__ __device__ __attribute__((always_inline)) inline float wigner_entry(int l, int m, int mp,
+                                                                           const float* D1,
+                                                                           const float* Dp) {
   const int lp = l - 1;
   const int np = 2 * lp + 1;
   auto r1 = [&](int i, int j) { return D1[(i + 1) * 3 + (j + 1)]; };
@@ -111,6 +112,63 @@ __host__ __device__ inline void wigner_blocks_serial(int L, const float* R, floa
     const int n = 2 * l + 1;
     for (int a = 0; a < n; ++a)
       for (int b = 0; b < n; ++b) Dl[a * n + b] = wigner_entry(l, a - l, b - l, D1, Dp);
+  }
+}
+
+// D^l (l >= 2) from D^1 and D^{l-1}, all in registers: with l a template
+// parameter every index, coefficient and branch of wigner_entry folds to a
+// constant, leaving a few multiply-adds per entry.
+template <int l>
+__device__ __attribute__((always_inline)) inline void wigner_step(const float (&D1)[9],
+                                                                  const float (&Dp)[(2 * l - 1) * (2 * l - 1)],
+                                                                  float (&Dl)[(2 * l + 1) * (2 * l + 1)]) {
+  constexpr int n = 2 * l + 1;
+#pragma unroll
+  for (int a = 0; a < n; ++a)
+#pragma unroll
+    for (int b = 0; b < n; ++b) Dl[a * n + b] = wigner_entry(l, a - l, b - l, D1, Dp);
+}
+
+// All blocks D^0..D^L of one rotation written to out[wig_total(L)], by one
+// thread, in registers.
+template <int L>
+__device__ inline void wigner_blocks_unrolled(const float* R, float* out) {
+  float D1[9];
+  wigner_l1(R, D1);
+  out[0] = 1.0f;
+  if constexpr (L >= 1) {
+#pragma unroll
+    for (int q = 0; q < 9; ++q) out[wig_offset(1) + q] = D1[q];
+  }
+  if constexpr (L >= 2) {
+    float D2[25];
+    wigner_step<2>(D1, D1, D2);
+#pragma unroll
+    for (int q = 0; q < 25; ++q) out[wig_offset(2) + q] = D2[q];
+    if constexpr (L >= 3) {
+      float D3[49];
+      wigner_step<3>(D1, D2, D3);
+#pragma unroll
+      for (int q = 0; q < 49; ++q) out[wig_offset(3) + q] = D3[q];
+      if constexpr (L >= 4) {
+        float D4[81];
+        wigner_step<4>(D1, D3, D4);
+#pragma unroll
+        for (int q = 0; q < 81; ++q) out[wig_offset(4) + q] = D4[q];
+        if constexpr (L >= 5) {
+          float D5[121];
+          wigner_step<5>(D1, D4, D5);
+#pragma unroll
+          for (int q = 0; q < 121; ++q) out[wig_offset(5) + q] = D5[q];
+          if constexpr (L >= 6) {
+            float D6[169];
+            wigner_step<6>(D1, D5, D6);
+#pragma unroll
+            for (int q = 0; q < 169; ++q) out[wig_offset(6) + q] = D6[q];
+          }
+        }
+      }
+    }
   }
 }
 
