@@ -170,6 +170,7 @@ so2_status so2_attention_fwd(const so2_attn_desc* desc, const float* pos, const 
   a.scratch_bytes = lay.scratch_bytes;
   a.n_atoms = desc->n_atoms;
   a.n_targets = desc->n_targets;
+  a.n_edges = desc->n_edges;
   a.L = desc->l_max;
   a.C = desc->channels;
   a.H = desc->heads;

@@ -32,7 +32,8 @@
 // The target accumulators live in LDS in the MFMA C layout.
 //
 // Workgroup: 8 waves (512 lanes), wave w owns output channels
-// [16w, 16w+16).  Each workgroup takes 16 consecutive target atoms; its
+// [16w, 16w+16).  Each workgroup takes a run of consecutive target atoms
+// holding about the same number of edges as every other workgroup; its
 // edges are processed in chunks of at most 64 edges whose targets span at
 // most 4 consecutive indices (4 accumulator slots, slot = target mod 4); a
 // target whose edges continue into the next chunk keeps its slot, a target
@@ -43,6 +44,8 @@
 // sum_j u_ij exp(z_ij - max), accumulated online over the neighbours, so the
 // fused kernel applies final weights and never rescales its accumulators.
 #include <math.h>
+
+#include <algorithm>
 
 #include "common.h"
 #include "launch.h"
@@ -61,7 +64,7 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kM = 64;                // edges per chunk
 constexpr int kRT = kM / 16;          // row tiles
 constexpr int kSlots = 4;             // targets live in one chunk
-constexpr int kTargetsPerGroup = 16;  // targets per workgroup
+constexpr int kEdgesPerGroup = 384;   // edges per workgroup (about six chunks)
 constexpr int kKC = 64;               // channels per K chunk (2 MFMA K steps)
 constexpr int kApad = kKC + 8;        // LDS row pitch of the A chunk, bf16
 constexpr int kMaxHeads = 16;
@@ -558,6 +561,23 @@ __device__ inline void flush_slots(char* smem, float* y) {
 
 // ---------------------------------------------------------------- kernel
 
+// First target of group g: the smallest t with row_ptr[t] - row_ptr[0] >=
+// g E / n_groups (E = edges of all targets); group n_groups starts at
+// n_targets.  Binary search, uniform across the workgroup.
+__device__ inline int group_start(const MfmaParams& P, int g, int n_groups) {
+  if (g >= n_groups) return P.n_targets;
+  const int e0 = P.row_ptr[0];
+  const int64_t E = (int64_t)P.row_ptr[P.n_targets] - e0;
+  const int64_t goal = e0 + (E * g) / n_groups;
+  int lo = 0, hi = P.n_targets;  // answer in [lo, hi]
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)P.row_ptr[mid] >= goal) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
 template <int L>
 __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(MfmaParams P, int n_groups) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -569,14 +589,16 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(MfmaParams P, int n
   const int wave = tid >> 6;
   constexpr int NC = Cfg<L>::NC;
 
-  // Workgroup -> target group, contiguous per XCD (workgroups are dispatched
-  // to the 8 XCDs round robin; neighbouring groups share neighbours in L2).
+  // Workgroup -> group of consecutive targets holding about E / n_groups
+  // edges (group g starts at the first target whose edges start at or after
+  // g E / n_groups), contiguous per XCD: workgroups are dispatched to the 8
+  // XCDs round robin, and neighbouring groups share neighbours in L2.
   const int b = blockIdx.x;
   const int per = n_groups / 8, rem = n_groups % 8;
   const int xcd = b % 8, idx = b / 8;
   const int grp = xcd * per + min(xcd, rem) + idx;
-  const int t_begin = grp * kTargetsPerGroup;
-  const int t_end = min(t_begin + kTargetsPerGroup, P.n_targets);
+  const int t_begin = group_start(P, grp, n_groups);
+  const int t_end = group_start(P, grp + 1, n_groups);
 
   // targets without neighbours: y = 0
   for (int a = tid; a < (t_end - t_begin) * NC * kC; a += kThreads) {
@@ -717,9 +739,16 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(MfmaParams P, int n
   }
 }
 
+// Workgroups: about kEdgesPerGroup edges each, rounded up to a whole number
+// of waves of workgroups over the device's compute units (one per CU).
 template <int L>
-so2_status launch_L(const MfmaParams& P, hipStream_t stream) {
-  const int n_groups = (P.n_targets + kTargetsPerGroup - 1) / kTargetsPerGroup;
+so2_status launch_L(const MfmaParams& P, int64_t n_edges, hipStream_t stream) {
+  int dev = 0, n_cu = 256;
+  SO2_CHECK(hipGetDevice(&dev));
+  SO2_CHECK(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+  int64_t want = (n_edges + kEdgesPerGroup - 1) / kEdgesPerGroup;
+  want = ((want + n_cu - 1) / n_cu) * n_cu;
+  const int n_groups = (int)std::max<int64_t>(1, std::min<int64_t>(want, P.n_targets));
   const size_t smem = Lds<L>::kTotal;
   static_assert(Lds<L>::kTotal <= 160 * 1024, "LDS budget");
   SO2_CHECK(hipFuncSetAttribute((const void*)attn_mfma_kernel<L>,
@@ -784,13 +813,13 @@ so2_status launch_attention_mfma(const AttnArgs& a, hipStream_t stream) {
   const MfmaParams P = make_params(a);
   switch (a.L) {
     case 1:
-      return launch_L<1>(P, stream);
+      return launch_L<1>(P, a.n_edges, stream);
     case 2:
-      return launch_L<2>(P, stream);
+      return launch_L<2>(P, a.n_edges, stream);
     case 3:
-      return launch_L<3>(P, stream);
+      return launch_L<3>(P, a.n_edges, stream);
     case 4:
-      return launch_L<4>(P, stream);
+      return launch_L<4>(P, a.n_edges, stream);
   }
   return SO2_ERR_UNSUPPORTED;
 }

@@ -43,6 +43,7 @@ struct AttnArgs {
   void* scratch;  // kernel-specific workspace area
   size_t scratch_bytes;
   int32_t n_atoms, n_targets, L, C, H, K, p;
+  int64_t n_edges;  // edges of the target rows (from the descriptor)
   float cutoff;
   uint32_t flags;
   int32_t dtype;
