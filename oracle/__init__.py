@@ -16,9 +16,11 @@ What it follows (page titles as printed on the source pages):
   block-wise linear maps) and section 2.2 (node-centric attention: query and
   key are SO(3)-invariant scalar projections, geometry enters only through
   the values, a softmax over the neighbours N(i) within the cutoff).
-* "EquiformerV3: ...", technical summary, section 2.B.3 (smooth radius
+* "EquiformerV3: Scaling Efficient, Expressive, and General
+  SE(3)-Equivariant Graph Attention Transformers", technical summary, section 2.B.3 (smooth radius
   cutoff: the envelope sits inside attention, denominator included).
-* "DPA4 ...", technical summary, section 2.1 A3 (envelope-gated attention,
+* "DPA4: Pushing the Accuracy-Cost Frontier of Interatomic
+  Potentials with EMFA SO(2) Convolution", technical summary, section 2.1 A3 (envelope-gated attention,
   weights from the invariant l = 0 section).
 
 The pages print no equations, so every formula here is a stated reading;

@@ -13,10 +13,12 @@ reading, listed with its evidence in the design doc):
   - section 2.2: query and key are SO(3)-invariant scalar projections (its
     "Eq. 6"), geometry enters only through the value path, a softmax runs
     over the neighbours j in N(i), value updates are accumulated per atom.
-* "EquiformerV3: ...", technical summary, section 2.B.3: the envelope of the
+* "EquiformerV3: Scaling Efficient, Expressive, and General
+  SE(3)-Equivariant Graph Attention Transformers", technical summary, section 2.B.3: the envelope of the
   smooth radius cutoff multiplies the attention terms in the numerator and in
   the softmax denominator.
-* "DPA4 ...", technical summary, section 2.1 A3: envelope-gated attention
+* "DPA4: Pushing the Accuracy-Cost Frontier of Interatomic
+  Potentials with EMFA SO(2) Convolution", technical summary, section 2.1 A3: envelope-gated attention
   with weights from the invariant l = 0 section (corroborates the above).
 
 The softmax here is two-pass (max, then normalised sum); the streaming GPU
