@@ -5,7 +5,8 @@
  * The operation (stated in prose, without equations, by "E2Former-V2:
  * On-the-Fly Equivariant Attention with Linear Activation Memory",
  * technical summary, sections 2.1 and 2.2; envelope placement from
- * "EquiformerV3", technical summary, section 2.B.3):
+ * "EquiformerV3: Scaling Efficient, Expressive, and General SE(3)-Equivariant
+ * Graph Attention Transformers", technical summary, section 2.B.3):
  *
  *   For every target atom i, stream its neighbours j within the cutoff.
  *   For each edge, rotate the neighbour's irreps features x_j into the frame
@@ -115,8 +116,7 @@ so2_status build_neighbors(const float* pos, int32_t n_atoms, const int32_t* mol
  * so2_attention_fwd - the fused forward pass described at the top.
  * Follows the E2Former-V2 summary (technical sections 2.1, 2.2): query and
  * key are projections of the invariant l = 0 slice, the softmax over N(i)
- * is gated by the envelope in numerator and denominator (EquiformerV3
- * summary, technical section 2.B.3), y_i = 0 when N(i) is empty.
+ * is gated by the envelope in numerator and denominator ("EquiformerV3: ...", technical summary, section 2.B.3), y_i = 0 when N(i) is empty.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t n_atoms;    /* rows of x and pos                                    */

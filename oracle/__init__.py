@@ -17,14 +17,15 @@ What it follows (page titles as printed on the source pages):
   key are SO(3)-invariant scalar projections, geometry enters only through
   the values, a softmax over the neighbours N(i) within the cutoff).
 * "EquiformerV3: Scaling Efficient, Expressive, and General
-  SE(3)-Equivariant Graph Attention Transformers", technical summary, section 2.B.3 (smooth radius
-  cutoff: the envelope sits inside attention, denominator included).
-* "DPA4: Pushing the Accuracy-Cost Frontier of Interatomic
-  Potentials with EMFA SO(2) Convolution", technical summary, section 2.1 A3 (envelope-gated attention,
-  weights from the invariant l = 0 section).
+  SE(3)-Equivariant Graph Attention Transformers", technical summary,
+  section 2.B.3 (smooth radius cutoff: the envelope sits inside attention,
+  denominator included).
+* "DPA4: Pushing the Accuracy-Cost Frontier of Interatomic Potentials with
+  EMFA SO(2) Convolution", technical summary, section 2.1 A3
+  (envelope-gated attention, weights from the invariant l = 0 section).
 
-The pages print no equations, so every formula here is a stated reading;
-the readings are listed in DESIGN.md ("Readings").  Parity status of every
+The pages print no equations, so every formula here is a stated reading
+(each module says which, and why).  Parity status of every
 function is pinned by ``tests/test_oracle_*.py`` against closed forms,
 invariants and brute force; the absolute output values of the layer are not
 printed on the pages (no worked example exists), so the layer as a whole is

@@ -2,7 +2,7 @@
 per-edge loop in fp64.  Test infrastructure (see oracle/__init__).
 
 Sources (page titles; the pages print no equations, so each step below is a
-reading, listed with its evidence in the design doc):
+reading of their prose):
 
 * "E2Former-V2: On-the-Fly Equivariant Attention with Linear Activation
   Memory", technical summary
@@ -14,12 +14,13 @@ reading, listed with its evidence in the design doc):
     "Eq. 6"), geometry enters only through the value path, a softmax runs
     over the neighbours j in N(i), value updates are accumulated per atom.
 * "EquiformerV3: Scaling Efficient, Expressive, and General
-  SE(3)-Equivariant Graph Attention Transformers", technical summary, section 2.B.3: the envelope of the
-  smooth radius cutoff multiplies the attention terms in the numerator and in
-  the softmax denominator.
-* "DPA4: Pushing the Accuracy-Cost Frontier of Interatomic
-  Potentials with EMFA SO(2) Convolution", technical summary, section 2.1 A3: envelope-gated attention
-  with weights from the invariant l = 0 section (corroborates the above).
+  SE(3)-Equivariant Graph Attention Transformers", technical summary,
+  section 2.B.3: the envelope of the smooth radius cutoff multiplies the
+  attention terms in the numerator and in the softmax denominator.
+* "DPA4: Pushing the Accuracy-Cost Frontier of Interatomic Potentials with
+  EMFA SO(2) Convolution", technical summary, section 2.1 A3:
+  envelope-gated attention with weights from the invariant l = 0 section
+  (corroborates the above).
 
 The softmax here is two-pass (max, then normalised sum); the streaming GPU
 kernel reaches the same numbers by a different schedule.

@@ -3,7 +3,8 @@
 //
 // The method ("E2Former-V2: On-the-Fly Equivariant Attention with Linear
 // Activation Memory", technical summary, sections 2.1 and 2.2; envelope in
-// numerator and denominator from "EquiformerV3", technical summary, section
+// numerator and denominator from "EquiformerV3: Scaling Efficient, Expressive, and General SE(3)-Equivariant
+// Graph Attention Transformers", technical summary, section
 // 2.B.3): for every target atom stream its neighbours, rotate each
 // neighbour's irreps into the edge frame, gate per channel, apply one linear
 // map per |m|, rotate back, weight with the envelope-gated softmax and sum.

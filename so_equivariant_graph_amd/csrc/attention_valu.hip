@@ -7,7 +7,8 @@
 //
 // Method ("E2Former-V2: On-the-Fly Equivariant Attention with Linear
 // Activation Memory", technical summary, sections 2.1 and 2.2; envelope
-// from "EquiformerV3", technical summary, section 2.B.3):
+// from "EquiformerV3: Scaling Efficient, Expressive, and General SE(3)-Equivariant
+// Graph Attention Transformers", technical summary, section 2.B.3):
 //   sweep 1 (online softmax statistics): for each head a running maximum
 //     of the logits and a running normaliser sum_j u_ij exp(z_ij - max),
 //     rescaled whenever the maximum grows; lanes combine their partial

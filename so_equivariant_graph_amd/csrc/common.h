@@ -67,7 +67,9 @@ __device__ inline float load_as_float<uint16_t>(const uint16_t* p, int64_t i) {
 }
 
 // Envelope u(s) = 1 - (p+1)(p+2)/2 s^p + p(p+2) s^(p+1) - p(p+1)/2 s^(p+2)
-// for s < 1, else 0 (smooth radius cutoff inside attention: "EquiformerV3",
+// for s < 1, else 0 (smooth radius cutoff inside attention: "EquiformerV3:
+// Scaling Efficient, Expressive, and General SE(3)-Equivariant Graph Attention
+// Transformers",
 // technical summary, section 2.B.3).
 __device__ inline float envelope_u(float s, int p) {
   if (!(s < 1.0f)) return 0.0f;
