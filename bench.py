@@ -20,6 +20,7 @@ cpu_baseline   the fp64 oracle (never tuned) on a bounded sample of the same
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -33,10 +34,60 @@ METRIC = "neighbor-pair messages/sec, fused SO(2) attention fwd; % bf16 MFMA pea
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (vendor figure, no sparsity)
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes moved by one launch of the fused kernel, from two rocprofv3 --pmc
+# passes over this benchmark (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+# each multiplied by the factor that maps the same counter's reading for a plain
+# device copy of known size (--copy-probe) onto that size.  A figure holds only
+# for the kernel sources it was taken on: their digest is stored with it and a
+# mismatch reports null.
+MEASURED_TRAFFIC = {
+    # FETCH_SIZE 440293 KiB x 2.00 (a 1 GiB copy reads as 524303 KiB), WRITE_SIZE
+    # 129800 KiB x 1.00 (the copy writes read exactly 1048576 KiB); mean of 7 launches.
+    "small_molecules": {
+        "sources_sha256": "c9f7e8a85c4520778124c1a990420f884ab4f91bc4aff5ae8a1d0b3f4fdf2eb2",
+        "fetch_bytes": 901695839,
+        "write_bytes": 132915200,
+    },
+}
+KERNEL_SOURCES = ("attention_mfma.hip", "wigner.h", "common.h", "launch.h")
+
 
 def flops_per_edge(L, C):
     """2 C^2 [(L+1)^2 + 2/3 L (L+1)(2L+1)]: the per-m map, 4 real products per m >= 1."""
     return 2 * C * C * ((L + 1) ** 2 + (2 * L * (L + 1) * (2 * L + 1)) // 3)
+
+
+def kernel_digest():
+    """sha256 over the fused kernel's source files, in a fixed order."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "so_equivariant_graph_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    rec = MEASURED_TRAFFIC.get(workload)
+    if rec is None or rec["sources_sha256"] != kernel_digest():
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
+
+
+def copy_probe(mib):
+    """A plain device-to-device copy of `mib` MiB, three times: the reference
+    reading for FETCH_SIZE / WRITE_SIZE (each copy reads and writes mib MiB)."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    ok = bool(torch.equal(a[:: 1 << 16], b[:: 1 << 16]))
+    print(json.dumps({"copy_probe_bytes": n * 4, "copies": 3, "ok": ok}), flush=True)
 
 
 # ------------------------------------------------------------------ CPU leg
@@ -191,6 +242,8 @@ def main():
     ap.add_argument("--workload", default="small_molecules")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, metavar="MIB", default=0,
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(
@@ -199,6 +252,9 @@ def main():
             file=sys.stderr,
         )
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     from synth import make_workload
 
@@ -213,6 +269,7 @@ def main():
     kern = sorted(g["kern_ms"])
     kern_mean = sum(kern) / len(kern)
     achieved = E * F / (kern_mean * 1e-3) / 1e12
+    traffic = measured_traffic(w.name) if g["kind"] == 2 else None
     line = {
         "metric": METRIC,
         "value": E * args.steps / g["total_s"],
@@ -244,7 +301,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": traffic,
         },
         "cpu_baseline": cpu,
         "detail": {
@@ -256,6 +313,9 @@ def main():
             "attention_messages_per_s": E / (kern_mean * 1e-3),
             "neighbors_plus_overhead_ms": ms_step - kern_mean,
             "flop_per_edge": F,
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "traffic_GBps": None if traffic is None else traffic / (kern_mean * 1e-3) / 1e9,
+            "kernel_sources_sha256": kernel_digest(),
             "peak_device_bytes": g["peak_bytes"],
             "peak_device_bytes_per_atom": g["peak_bytes"] / w.n_atoms,
             "outputs_finite": g["finite"],
