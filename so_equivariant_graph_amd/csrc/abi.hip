@@ -58,7 +58,7 @@ AttnLayout attn_layout(const so2_attn_desc* d, Kind kind) {
   L.k = off;
   off += align256(sizeof(float) * (size_t)d->n_atoms * d->channels);
   L.scratch = off;
-  L.scratch_bytes = kind == kMfma ? mfma_scratch_bytes(d->n_targets, d->heads)
+  L.scratch_bytes = kind == kMfma ? mfma_scratch_bytes(d->n_atoms, d->n_targets, d->l_max, d->heads, d->n_rbf)
                                   : valu_scratch_bytes(d->l_max, d->channels);
   off += align256(L.scratch_bytes);
   L.total = off;

@@ -3,12 +3,12 @@
 //
 // The method ("E2Former-V2: On-the-Fly Equivariant Attention with Linear
 // Activation Memory", technical summary, sections 2.1 and 2.2; envelope in
-// numerator and denominator from "EquiformerV3: Scaling Efficient, Expressive, and General SE(3)-Equivariant
-// Graph Attention Transformers", technical summary, section
-// 2.B.3): for every target atom stream its neighbours, rotate each
-// neighbour's irreps into the edge frame, gate per channel, apply one linear
-// map per |m|, rotate back, weight with the envelope-gated softmax and sum.
-// No per-edge tensor leaves the workgroup.
+// numerator and denominator from "EquiformerV3: Scaling Efficient,
+// Expressive, and General SE(3)-Equivariant Graph Attention Transformers",
+// technical summary, section 2.B.3): for every target atom stream its
+// neighbours, rotate each neighbour's irreps into the edge frame, gate per
+// channel, apply one linear map per |m|, rotate back, weight with the
+// envelope-gated softmax and sum.  No per-edge tensor leaves the workgroup.
 //
 // The per-m map is a dense contraction over channels and degrees shared by
 // every edge, so it runs as GEMMs on the matrix cores
@@ -17,12 +17,19 @@
 //   edges are the M dimension: a chunk holds up to 64 consecutive edges of
 //   the CSR (4 row tiles of 16), crossing target boundaries;
 //   for block m the A operand is the rotated, gated input rows (l', +-m) of
-//   those edges, built on the vector ALUs from x_j and the edge's Wigner-D
-//   rows and staged through LDS in bf16; the B operand is W0 (m = 0) or
-//   W1_m / W2_m read straight from the caller's row-major [out][in] weights
-//   (8 consecutive bf16 of one row per lane, one 16-byte load);
+//   those edges, built on the vector ALUs and staged through LDS in bf16,
+//   one degree l' (128 channels, 4 K steps of 32) per A chunk;
+//   the B operand is W0 (m = 0) or W1_m / W2_m read straight from the
+//   caller's row-major [out][in] weights (8 consecutive bf16 of one row per
+//   lane, one 16-byte load);
 //   m >= 1 is the complex product (W1 + i W2)(xt_+ + i xt_-): four real MFMAs
-//   per tile pair, the minus sign carried by negating the xt_- operand.
+//   per tile pair, the minus sign carried by the W2 fragment.
+//
+// The rotation into the edge frame, xt[(l', m)][c] = sum_b D^l'[m][b]
+// x_j[(l', b)][c], runs on v_dot2_f32_bf16: a prologue kernel repacks x so
+// that one dword holds the components b = 2p and 2p+1 of one channel
+// (zero for the odd one out), and the Wigner-D rows are kept in LDS as the
+// matching bf16 pairs, so each dot2 is two multiply-adds with no unpacking.
 //
 // Rotating back and summing over neighbours is a second, small GEMM: for
 // output degree l the target accumulator rows are (l, target slot, m'), its
@@ -30,15 +37,25 @@
 // belongs to that target (0 elsewhere); its B operand is the weighted output
 // of the first GEMM, which is already in the right lane layout (the K order
 // follows the accumulator layout), so it is only scaled and rounded to bf16.
-// The target accumulators live in LDS in the MFMA C layout.
+// The target accumulators stay in registers in the MFMA C layout.
 //
-// Workgroup: 8 waves (512 lanes), wave w owns output channels
-// [16w, 16w+16).  Each workgroup takes a run of consecutive target atoms
-// holding about the same number of edges as every other workgroup; its
-// edges are processed in chunks of at most 64 edges whose targets span at
-// most 4 consecutive indices (4 accumulator slots, slot = target mod 4); a
-// target whose edges continue into the next chunk keeps its slot, a target
-// whose last edge is in the chunk is written out and its slot cleared.
+// Workgroup: 8 waves (512 lanes), two per SIMD so that one wave's memory
+// waits are covered by the other's MFMAs; wave w owns output channels
+// [16w, 16w+16).  Each
+// workgroup takes a run of consecutive target atoms holding about the same
+// number of edges as every other workgroup; its edges are processed in
+// chunks of at most 64 edges whose targets span at most 4 consecutive
+// indices (4 accumulator slots, slot = target mod 4); a target whose edges
+// continue into the next chunk keeps its slot, a target whose last edge is
+// in the chunk is written out and its slot cleared.
+//
+// Software pipeline: while the MFMAs consume A chunk q from one LDS buffer,
+// every lane generates one quarter of the next A chunk per K step into the
+// other buffer (its gathers issued before the step's MFMAs) and the B
+// fragments of the next K step load; one barrier per A chunk.  Every pass
+// (block m, a group of output degrees) is a compile-time instance, so its
+// loop bounds, weight offsets and register tiles are constants, and it
+// generates the first A chunk of the pass after it.
 //
 // Softmax weights come from a statistics pass (attn_stats_kernel): for every
 // target and head the running maximum and the normaliser
@@ -56,48 +73,60 @@ namespace so2 {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr int kC = 128;               // channels
-constexpr int kWaves = kC / 16;       // 8 waves, 16 output channels each
+constexpr int kWaves = 8;             // two waves per SIMD
 constexpr int kThreads = kWaves * 64;
+constexpr int kNT = kC / (16 * kWaves);  // 16-column tiles per wave: wave w owns channels 16 kNT w ..
+constexpr int kGR = 64 * 8 / kThreads;   // generator rows per lane (8 lanes per row and K step)
+constexpr int kGStride = kThreads / 8;   // distance between a lane's generator rows
 constexpr int kM = 64;                // edges per chunk
 constexpr int kRT = kM / 16;          // row tiles
 constexpr int kSlots = 4;             // targets live in one chunk
 constexpr int kEdgesPerGroup = 384;   // edges per workgroup (about six chunks)
-constexpr int kKC = 64;               // channels per K chunk (2 MFMA K steps)
-constexpr int kApad = kKC + 8;        // LDS row pitch of the A chunk, bf16
+constexpr int kKC = 128;              // channels per A chunk (one degree, 4 MFMA K steps)
+constexpr int kAplane = kM * kKC;     // one sign plane of an A chunk, bf16
+constexpr int kAbuf = 2 * kAplane;    // one A buffer (both signs), bf16
 constexpr int kMaxHeads = 16;
-constexpr int kGpad = kC + 8;         // LDS row pitch of the radial gate, bf16
-constexpr int kMaxDeg = 2;            // output degrees per pass for m >= 1
+constexpr int kMaxPairs = 5;          // component pairs of one degree, L <= 4
+
+// Component pairs: degree l has l + 1 pairs (2p, 2p+1), the last one padded
+// with zero.  pair_off(l) = pairs of the degrees below l.
+__host__ __device__ constexpr int pair_off(int l) { return l * (l + 1) / 2; }
+// Wigner-D pair dwords of the degrees below l: sum_{k<l} (2k+1)(k+1).
+__host__ __device__ constexpr int dpair_off(int l) {
+  return l * (l - 1) * (2 * l - 1) / 3 + 3 * l * (l - 1) / 2 + l;
+}
+__host__ __device__ constexpr int64_t w1_offset(int L, int m) {
+  int64_t off = (int64_t)(L + 1) * kC * (L + 1) * kC;
+  for (int mu = 1; mu < m; ++mu) off += 2 * (int64_t)(L + 1 - mu) * kC * (L + 1 - mu) * kC;
+  return off;
+}
 
 struct MfmaParams {
   const float* pos;
   const int32_t* row_ptr;
   const int32_t* col;
-  const uint16_t* x;
-  const uint16_t* w_rad;
-  const uint16_t* w_so2;
+  const uint32_t* xp;     // x repacked as component pairs [n_atoms][pair_off(L+1)][C]
+  const float* wrad;      // w_rad in fp32 [K][C]
+  const uint16_t* wf;     // w_so2 in MFMA fragment order
   const float* q;
   const float* k;
   float* stat_max;  // [n_targets][H]
   float* stat_inv;  // [n_targets][H]
   float* y;
-  uint32_t x_bytes;  // extent of x for its buffer descriptor (< 4 GiB)
-  uint32_t w_bytes;  // extent of w_so2
+  uint32_t xp_bytes;  // extent of xp for its buffer descriptor
+  uint32_t w_bytes;   // extent of w_so2
   int32_t n_targets, H, K, p;
   float cutoff;
   uint32_t flags;
   int32_t periodic;
   float box[3];
 };
-
-__device__ inline float bf_lo(unsigned int u) { return __uint_as_float(u << 16); }
-__device__ inline float bf_hi(unsigned int u) { return __uint_as_float(u & 0xffff0000u); }
-
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(2))) float f32x2;
 
 // Two floats to packed bf16 (round to nearest even): one v_cvt_pk_bf16_f32.
 __device__ inline unsigned int pack_bf16x2(float a, float b) {
@@ -110,8 +139,15 @@ __device__ inline f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// a.lo * b.lo + a.hi * b.hi + c (bf16 pairs, fp32 accumulate).
+__device__ inline float dot2(unsigned int a, unsigned int b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
+                                         false);
+}
+
 // Raw buffer descriptor (gfx9 family: dword3 = 0x00020000).  Loads through
-// it take one 32-bit VGPR offset and return 0 past num_records bytes.
+// it take one 32-bit VGPR offset plus a scalar offset and return 0 past
+// num_records bytes.
 __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
@@ -126,6 +162,71 @@ __device__ inline void edge_vec(const MfmaParams& P, int i, int j, float* r) {
     float v = P.pos[3 * (int64_t)j + d] - P.pos[3 * (int64_t)i + d];
     if (P.periodic) v = v - P.box[d] * rintf(v / P.box[d]);
     r[d] = v;
+  }
+}
+
+// ---------------------------------------------------------------- prologue
+
+// x [n][(L+1)^2][C] bf16 -> xp [n][pair_off(L+1)][C] dwords, dword (l, p, c)
+// = x[l^2 + 2p][c] | x[l^2 + 2p + 1][c] << 16 (upper half 0 for p = l),
+// four channels per thread;
+// w_rad bf16 -> fp32;
+// w_so2 -> fragment order: each matrix (W0, then W1_m, W2_m for m = 1..L,
+// at the same offsets) is cut into 16-row x 32-column blocks, block (row
+// tile R, K step s) at (R (KM / 32) + s) KB, and lane (row % 16) + 16
+// ((col % 32) / 8) of a block holds its 8 consecutive columns, so one
+// 16-byte load per lane reads a whole MFMA B fragment from 1 KB of memory.
+template <int L>
+__global__ void __launch_bounds__(256) attn_pack_kernel(const uint16_t* __restrict__ x, uint32_t* __restrict__ xp,
+                                                        int n_atoms, const uint16_t* __restrict__ w_rad,
+                                                        float* __restrict__ wrad, int n_rbf,
+                                                        const uint16_t* __restrict__ w_so2,
+                                                        uint16_t* __restrict__ wf) {
+  constexpr int NC = (L + 1) * (L + 1);
+  constexpr int NP = pair_off(L + 1);
+  const int64_t n_x = (int64_t)n_atoms * NP * (kC / 4);
+  const int64_t n_w = (int64_t)n_rbf * kC;
+  const int64_t n_f = w1_offset(L, L + 1) / 8;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_x + n_w + n_f; i += stride) {
+    if (i < n_x) {
+      const int c4 = (int)(i % (kC / 4));
+      const int pi = (int)((i / (kC / 4)) % NP);
+      const int64_t a = i / ((kC / 4) * NP);
+      int l = 0;
+      while (pair_off(l + 1) <= pi) ++l;
+      const int pp = pi - pair_off(l);
+      const int comp = l * l + 2 * pp;
+      typedef __attribute__((ext_vector_type(4))) unsigned short u16x4;
+      const u16x4 lo = *(const u16x4*)(x + (a * NC + comp) * kC + 4 * c4);
+      u16x4 hi = {0, 0, 0, 0};
+      if (pp < l) hi = *(const u16x4*)(x + (a * NC + comp + 1) * kC + 4 * c4);
+      u32x4 o;
+      o.x = (uint32_t)lo.x | ((uint32_t)hi.x << 16);
+      o.y = (uint32_t)lo.y | ((uint32_t)hi.y << 16);
+      o.z = (uint32_t)lo.z | ((uint32_t)hi.z << 16);
+      o.w = (uint32_t)lo.w | ((uint32_t)hi.w << 16);
+      *(u32x4*)(xp + ((a * NP + pi) * kC + 4 * c4)) = o;
+    } else if (i < n_x + n_w) {
+      const int64_t w = i - n_x;
+      wrad[w] = bf16_to_float(w_rad[w]);
+    } else {
+      const int64_t g = 8 * (i - n_x - n_w);  // first element of this lane's 16 bytes in wf
+      int64_t base = 0;
+      int mi = 0, KM = (L + 1) * kC;
+      while (g >= base + (int64_t)KM * KM) {
+        base += (int64_t)KM * KM;
+        ++mi;
+        KM = (L + 1 - (mi + 1) / 2) * kC;
+      }
+      const int64_t lg = (g - base) / 8;
+      const int lane = (int)(lg % 64);
+      const int64_t f = lg / 64;
+      const int ks = (int)(f % (KM / 32));
+      const int64_t row = 16 * (f / (KM / 32)) + (lane & 15);
+      const int col = 32 * ks + 8 * (lane >> 4);
+      *(u32x4*)(wf + g) = *(const u32x4*)(w_so2 + base + row * KM + col);
+    }
   }
 }
 
@@ -176,7 +277,8 @@ __global__ void __launch_bounds__(256) attn_stats_kernel(MfmaParams P, int C) {
 template <int L>
 struct Cfg {
   static constexpr int NC = (L + 1) * (L + 1);
-  static constexpr int WT = wig_total(L);
+  static constexpr int NP = pair_off(L + 1);   // x pairs per channel
+  static constexpr int DPW = dpair_off(L + 1); // Wigner-D pair dwords per edge
   // target accumulator rows (l, slot, m') packed: kSlots l^2 + slot (2l+1) + m' + l
   static constexpr int TROWS = kSlots * NC;
   static constexpr int TT = (TROWS + 15) / 16;  // 16-row MFMA tiles
@@ -187,25 +289,77 @@ struct Smem {
   int flush_t[kSlots];  // target written out from each slot after this chunk, or -1
   int row_j[kM];
   int row_slot[kM];
+  uint16_t rowinfo[112];  // accumulator row R -> slot << 8 | component, 0xffff past the rows
 };
+
+// Passes in execution order: blocks m = 1..L, each in groups of at most two
+// output degrees, then m = 0 in groups of at most three.  Every pass
+// generates, during its last A chunk, the first A chunk of the pass after
+// it; ending on m = 0 means a pass never has to produce more sign planes
+// than it has itself (an m >= 1 pass writes both planes, m = 0 reads one).
+struct PassInfo {
+  int M, LO, ND;
+};
+
+__host__ __device__ constexpr PassInfo pass_info(int L, int idx) {
+  int i = 0;
+  for (int mm = 1; mm <= L + 1; ++mm) {
+    const int M = mm == L + 1 ? 0 : mm;
+    const int nd = M == 0 ? 3 : 2;
+    for (int lo = M; lo <= L; lo += nd) {
+      if (i == idx) return PassInfo{M, lo, (L + 1 - lo) < nd ? (L + 1 - lo) : nd};
+      ++i;
+    }
+  }
+  return PassInfo{-1, -1, 0};
+}
+
+__host__ __device__ constexpr int deg_tiles(int l) {
+  return (kSlots * (l + 1) * (l + 1) - 1) / 16 - (kSlots * l * l) / 16 + 1;
+}
+
+// A' fragments of pass idx: (degree, tile, K step) for its output degrees.
+__host__ __device__ constexpr int frag_count(int L, int idx) {
+  const PassInfo pi = pass_info(L, idx);
+  const int steps = pi.M == 0 ? kRT / 2 : kRT;
+  int t = 0;
+  for (int di = 0; di < pi.ND; ++di) t += deg_tiles(pi.LO + di) * steps;
+  return t;
+}
+
+__host__ __device__ constexpr int max_frags(int L) {
+  int m = 0;
+  for (int i = 0; pass_info(L, i).M >= 0; ++i) m = frag_count(L, i) > m ? frag_count(L, i) : m;
+  return m;
+}
+
+// A chunks (one degree of one block, 128 channels) of the passes before idx.
+__host__ __device__ constexpr int chunks_before(int L, int idx) {
+  int c = 0;
+  for (int i = 0; i < idx; ++i) c += L + 1 - pass_info(L, i).M;
+  return c;
+}
 
 template <int L>
 struct Lds {
   static constexpr size_t kHdr = (sizeof(Smem) + 15) & ~(size_t)15;
-  static constexpr size_t kD = kHdr;                                    // float [kM][WT]
-  static constexpr size_t kG = kD + sizeof(float) * kM * Cfg<L>::WT;    // bf16 [kM][kGpad]
-  static constexpr size_t kW = kG + sizeof(uint16_t) * kM * kGpad;      // float [kM][kMaxHeads]
-  static constexpr size_t kA = kW + sizeof(float) * kM * kMaxHeads;     // bf16 [2][2][kM][kApad]
-  static constexpr size_t kAbuf = sizeof(uint16_t) * 2 * kM * kApad;    // one buffer, both signs
-  static constexpr size_t kT = kA + 2 * kAbuf;                          // f32x4 [TT][kWaves][64]
-  static constexpr size_t kTotal = kT + sizeof(f32x4) * Cfg<L>::TT * kWaves * 64;
+  static constexpr size_t kD = kHdr;                                             // u32 [kM][DPW]
+  static constexpr size_t kG = (kD + 4 * kM * Cfg<L>::DPW + 15) & ~(size_t)15;  // f32 [kM][kC], swizzled
+  static constexpr size_t kW = kG + sizeof(float) * kM * kC;                     // f32 [kM][kMaxHeads]
+  static constexpr size_t kA = kW + sizeof(float) * kM * kMaxHeads;              // bf16 [2][2][kM][kKC], swizzled
+  static constexpr size_t kF = kA + sizeof(uint16_t) * 2 * kAbuf;                // A' fragments u32x4 [][64]
+  static constexpr size_t kTotal = kF + sizeof(u32x4) * 64 * max_frags(L);
 };
 
-// Target accumulator tile ot of wave w, in the MFMA C layout (lane, 4 rows).
-template <int L>
-__device__ inline f32x4* tacc_tile(char* smem, int ot, int wave) {
-  return (f32x4*)(smem + Lds<L>::kT) + (ot * kWaves + wave) * 64;
-}
+// 16-byte column groups are XOR-swizzled by row so that both the MFMA
+// operand reads (16 rows, one group) and the generator's writes (4 rows x 4
+// groups) touch 16 distinct bank groups.
+__device__ inline int a_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ inline int a_off(int row, int group) { return row * kKC + 8 * (group ^ a_swz(row)); }
+// gate rows: 32 groups of 4 floats; the generator reads groups 8 k .. 8 k + 7
+// of 2 consecutive rows
+__device__ inline int g_swz(int row) { return ((row & 1) << 3) | ((row >> 1) & 1); }
+__device__ inline int g_off(int row, int group) { return row * kC + 4 * (group ^ g_swz(row)); }
 
 // Edge er of the chunk: its target t (one of the slots' targets), source j
 // and minimum-image vector r_ij = p_j - p_t.
@@ -218,175 +372,303 @@ __device__ inline void row_edge(const MfmaParams& P, const Smem& S, int er, int 
   edge_vec(P, t, j, rv);
 }
 
-// ---------------------------------------------------------------- A operand
-
-// Build one A chunk: rows of 64 edges, 64 channels [cbase, cbase+64) of
-// degree lp, for +m and (m > 0) -m:  a[r][c] = g_r[c] sum_b D^lp_r[+-m][b] x_j[(lp,b)][c].
-// Lane (r = tid / 8, 8 channels at cbase + 8 (tid % 8)).  gen_load issues the
-// 2lp+1 gathers of x_j back to back (one 16-byte load each); gen_store
-// combines them with the edge's Wigner-D rows and the radial gate.
-constexpr int kMaxComp = 2 * 4 + 1;  // 2 L + 1 for L <= 4
-
-__device__ inline void gen_load(__amdgpu_buffer_rsrc_t xrs, const Smem& S, int NC, int lp, int cbase,
-                                u32x4 (&xr)[kMaxComp]) {
-  const int tid = threadIdx.x;
-  const int r = tid >> 3;
-  const int c = cbase + 8 * (tid & 7);
-  const int j = S.row_j[r];
-  const int n = 2 * lp + 1;
-  const uint32_t voff = (((uint32_t)(j < 0 ? 0 : j) * NC + lp * lp) * kC + c) * 2u;
+// D^l rows of one edge as bf16 pairs: dword (l, a, p) at dpair_off(l) +
+// a (l+1) + p holds D^l[a][2p] | D^l[a][2p+1] << 16 (upper half 0 for p = l).
+template <int l>
+__device__ inline void store_dpairs(const float* D, uint32_t* out) {
+  constexpr int n = 2 * l + 1;
 #pragma unroll
-  for (int b = 0; b < kMaxComp; ++b)
-    if (b < n && j >= 0) xr[b] = buffer_load16(xrs, voff + b * kC * 2, 0);
+  for (int a = 0; a < n; ++a)
+#pragma unroll
+    for (int p = 0; p <= l; ++p)
+      out[dpair_off(l) + a * (l + 1) + p] = pack_bf16x2(D[a * n + 2 * p], 2 * p + 1 < n ? D[a * n + 2 * p + 1] : 0.0f);
 }
 
-template <int L, int NS>
-__device__ inline void gen_store(char* smem, int m, int lp, int cbase, const u32x4 (&xr)[kMaxComp],
-                                 uint16_t* abuf) {
-  const Smem& S = *(const Smem*)smem;
-  const float* sD = (const float*)(smem + Lds<L>::kD);
-  const uint16_t* sG = (const uint16_t*)(smem + Lds<L>::kG);
-  const int tid = threadIdx.x;
-  const int r = tid >> 3;
-  const int cg = tid & 7;
-  const int c = cbase + 8 * cg;
-  const int j = S.row_j[r];
-  const int n = 2 * lp + 1;
-  float ap[8], am[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) ap[q] = am[q] = 0.0f;
-  if (j >= 0) {
-    const float* Dl = sD + r * Cfg<L>::WT + wig_offset(lp);
-    const float* dp = Dl + (lp + m) * n;
-    const float* dm = Dl + (lp - m) * n;
-#pragma unroll
-    for (int b = 0; b < kMaxComp; ++b) {
-      if (b < n) {
-        const u32x4 v = xr[b];
-        const float xv[8] = {bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y),
-                             bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w)};
-        const float wp = dp[b];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) ap[q] += wp * xv[q];
-        if (NS > 1) {
-          const float wm = dm[b];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) am[q] += wm * xv[q];
-        }
+template <int L>
+__device__ inline void wigner_pairs(const float* R, uint32_t* out) {
+  float D1[9];
+  wigner_l1(R, D1);
+  out[0] = pack_bf16x2(1.0f, 0.0f);
+  if constexpr (L >= 1) store_dpairs<1>(D1, out);
+  if constexpr (L >= 2) {
+    float D2[25];
+    wigner_step<2>(D1, D1, D2);
+    store_dpairs<2>(D2, out);
+    if constexpr (L >= 3) {
+      float D3[49];
+      wigner_step<3>(D1, D2, D3);
+      store_dpairs<3>(D3, out);
+      if constexpr (L >= 4) {
+        float D4[81];
+        wigner_step<4>(D1, D3, D4);
+        store_dpairs<4>(D4, out);
       }
     }
-    const u32x4 gv = *(const u32x4*)(sG + r * kGpad + c);
-    const float g[8] = {bf_lo(gv.x), bf_hi(gv.x), bf_lo(gv.y), bf_hi(gv.y),
-                        bf_lo(gv.z), bf_hi(gv.z), bf_lo(gv.w), bf_hi(gv.w)};
+  }
+}
+
+// ---------------------------------------------------------------- A operand
+
+// Per-lane state for one edge chunk.  Generator lane: rows r0 = tid / 8
+// (+ kGStride u, u < kGR) and, in K step k of an A chunk, the 4 channels
+// 32 k + 4 (tid % 8): the 8 lanes of a row read one 128-byte line of x
+// pairs per load.
+struct Ctx {
+  uint32_t xoff[kGR];  // byte offset of (j, pair 0, channel 4 (tid % 8)) in xp per row; xp_bytes if no edge
+  int r0, c8;
+  int head[kNT];       // head of each of this lane's output column tiles
+};
+
+// Gathers of generator unit k of an A chunk of degree glp: for every pair
+// p <= L and every generator row one 16-byte load (p > glp reads past the
+// buffer: zeros, no memory traffic, so the code has no branch on glp).
+__device__ inline void gen_issue(__amdgpu_buffer_rsrc_t xrs, const Ctx& c, uint32_t oob, int glp, int k,
+                                 u32x4 (&xr)[kGR * kMaxPairs]) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      ap[q] *= g[q];
-      am[q] *= g[q];
+  for (int p = 0; p < kMaxPairs; ++p) {
+    const uint32_t soff = (uint32_t)((pair_off(glp) + p) * kC + 32 * k) * 4u;
+#pragma unroll
+    for (int u = 0; u < kGR; ++u) xr[kGR * p + u] = buffer_load16(xrs, p <= glp ? c.xoff[u] : oob, soff);
+  }
+}
+
+// D pairs of both generator rows for an A chunk (gm, glp): rows glp + gm and
+// glp - gm of D^glp, pairs 0..L (past glp they hold other entries of the
+// same edge, which meet zero gathers).
+__device__ inline void gen_dpairs(const uint32_t* sD, int DPW, const Ctx& c, int gm, int glp,
+                                  uint32_t (&dp)[kGR][kMaxPairs], uint32_t (&dm)[kGR][kMaxPairs]) {
+#pragma unroll
+  for (int u = 0; u < kGR; ++u) {
+    const uint32_t* d = sD + (c.r0 + kGStride * u) * DPW + dpair_off(glp);
+#pragma unroll
+    for (int p = 0; p < kMaxPairs; ++p) {
+      dp[u][p] = d[(glp + gm) * (glp + 1) + p];
+      dm[u][p] = d[(glp - gm) * (glp + 1) + p];
     }
   }
-  u32x4 op;
-  op.x = pack_bf16x2(ap[0], ap[1]);
-  op.y = pack_bf16x2(ap[2], ap[3]);
-  op.z = pack_bf16x2(ap[4], ap[5]);
-  op.w = pack_bf16x2(ap[6], ap[7]);
-  *(u32x4*)(abuf + r * kApad + 8 * cg) = op;
-  if (NS > 1) {
-    u32x4 om;
-    om.x = pack_bf16x2(am[0], am[1]);
-    om.y = pack_bf16x2(am[2], am[3]);
-    om.z = pack_bf16x2(am[4], am[5]);
-    om.w = pack_bf16x2(am[6], am[7]);
-    *(u32x4*)(abuf + (kM + r) * kApad + 8 * cg) = om;
+}
+
+// Generator unit k: a[r][c] = g_r[c] sum_p dot2(D pair, x pair) for the
+// + row and (NS = 2) the - row, rounded to bf16 into K step k of abuf.
+template <int NS>
+__device__ inline void gen_finish(const float* sG, const Ctx& c, int k, const u32x4 (&xr)[kGR * kMaxPairs],
+                                  const uint32_t (&dp)[kGR][kMaxPairs], const uint32_t (&dm)[kGR][kMaxPairs],
+                                  uint16_t* abuf) {
+#pragma unroll
+  for (int u = 0; u < kGR; ++u) {
+    const int r = c.r0 + kGStride * u;
+    float ap[4], am[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ap[q] = am[q] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kMaxPairs; ++p) {
+      const u32x4 v = xr[kGR * p + u];
+      const uint32_t xv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ap[q] = dot2(dp[u][p], xv[q], ap[q]);
+      if constexpr (NS > 1) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) am[q] = dot2(dm[u][p], xv[q], am[q]);
+      }
+    }
+    const f32x4 g = *(const f32x4*)(sG + g_off(r, 8 * k + c.c8));
+    const int ao = a_off(r, 4 * k + (c.c8 >> 1)) + 4 * (c.c8 & 1);
+    typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+    *(u32x2*)(abuf + ao) = u32x2{pack_bf16x2(ap[0] * g.x, ap[1] * g.y), pack_bf16x2(ap[2] * g.z, ap[3] * g.w)};
+    if constexpr (NS > 1)
+      *(u32x2*)(abuf + kAplane + ao) =
+          u32x2{pack_bf16x2(am[0] * g.x, am[1] * g.y), pack_bf16x2(am[2] * g.z, am[3] * g.w)};
   }
 }
 
 // ---------------------------------------------------------------- main GEMM
 
-// K loop of one pass: stream A chunks (degree lp, 64 channels, +m and for
-// m > 0 also -m) through double-buffered LDS and accumulate
-//   m = 0:  acc[d][0] += xt_0 W0^T
-//   m > 0:  acc[d][0] += xt_+ W1^T - xt_- W2^T,  acc[d][1] += xt_+ W2^T + xt_- W1^T
-// for output degrees lo .. lo+nd-1 (nd <= ND) of this wave's 16 channels.
-// The K steps (32 inputs each, two per A chunk) run as one flat loop; the B
-// fragments of step s+1 are loaded before the MFMAs of step s.
-template <int L, int ND, int NS>
-__device__ inline void load_b(__amdgpu_buffer_rsrc_t wrs, uint32_t w1_byte, uint32_t w2_byte, int KM,
-                              int m, int lo, int nd, int s, u32x4 (&b1)[ND], u32x4 (&b2)[ND]) {
+// B fragments of one K step of pass (M, LO, ND): for output degree LO + di,
+// matrix s (W0 / W1, then W2), column tile nt of this wave: the 1 KB block
+// (row tile, K step) of the fragment-ordered weights.  The lane and tile
+// part of the address is fixed for the pass; the step part (1 KB per step)
+// is the scalar offset.
+template <int L, int M, int LO, int ND>
+__device__ inline void load_b(__amdgpu_buffer_rsrc_t wrs, const uint32_t (&boff)[ND][kNT], int step,
+                              u32x4 (&b)[ND][M ? 2 : 1][kNT]) {
+  constexpr int KM = (L + 1 - M) * kC;
+  constexpr uint32_t w1_byte = (uint32_t)(M == 0 ? 0 : w1_offset(L, M)) * 2u;
+  constexpr uint32_t w2_byte = w1_byte + (uint32_t)(KM * KM) * 2u;
+  const uint32_t sb = 1024u * (uint32_t)step;
+#pragma unroll
+  for (int di = 0; di < ND; ++di)
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      b[di][0][nt] = buffer_load16(wrs, boff[di][nt], w1_byte + sb);
+      if constexpr (M > 0) b[di][1][nt] = buffer_load16(wrs, boff[di][nt], w2_byte + sb);
+    }
+}
+
+template <int L, int M, int LO, int ND>
+__device__ inline void b_offsets(uint32_t (&boff)[ND][kNT]) {
+  constexpr int KM = (L + 1 - M) * kC;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int q = s >> 1;
-  const int kin = (q / (kC / kKC)) * kC + kKC * (q % (kC / kKC)) + 32 * (s & 1) + 8 * (lane >> 4);
 #pragma unroll
-  for (int di = 0; di < ND; ++di) {
-    if (di < nd) {
-      const int row = (lo + di - m) * kC + 16 * wave + (lane & 15);
-      const uint32_t voff = (uint32_t)(row * KM + kin) * 2u;
-      b1[di] = buffer_load16(wrs, voff, w1_byte);
-      if (NS > 1) b2[di] = buffer_load16(wrs, voff, w2_byte);
-    }
+  for (int di = 0; di < ND; ++di)
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt)
+      boff[di][nt] = 16u * lane + (uint32_t)(((LO + di - M) * 8 + kNT * wave + nt) * (KM / 32)) * 1024u;
+}
+
+// One K step with its generator unit interleaved.  MFMA i of the step is
+// followed by the generator's dot products [i D / F, (i+1) D / F) (D dot
+// products, F MFMAs) and a scheduling fence, so that the matrix core and
+// the vector ALU of the SIMD work at the same time; the unit's gate,
+// rounding and LDS store follow the last MFMA.
+template <int ND, int NS>
+struct StepState {
+  const u32x4* ap;                      // [kRT] + plane fragments
+  const u32x4* am;                      // [kRT] - plane fragments
+  const u32x4 (&b)[ND][NS][kNT];
+  const u32x4 (&nb2)[ND][kNT];
+  f32x4 (&acc)[ND][NS][kNT][kRT];
+  const u32x4 (&xr)[kGR * kMaxPairs];
+  const uint32_t (&dp)[kGR][kMaxPairs];
+  const uint32_t (&dm)[kGR][kMaxPairs];
+  float (&vp)[kGR][4];
+  float (&vm)[kGR][4];
+  // loads for the next K step, spread over the MFMAs of this one
+  u32x4 (&bn)[ND][NS][kNT];             // B fragments of the next step
+  __amdgpu_buffer_rsrc_t wrs;
+  const uint32_t (&boff)[ND][kNT];
+  uint32_t wsoff[2];                    // scalar offsets of the next step's W0/W1 and W2 blocks
+  u32x4 (&xn)[kGR * kMaxPairs];         // gathers of the next generator unit
+  __amdgpu_buffer_rsrc_t xrs;
+  uint32_t xoff[kGR];                   // per row; past the end for pairs beyond the unit's degree
+  uint32_t xsoff;                       // scalar offset of the unit's pair 0
+  int glp;                              // degree of the next unit's chunk
+  uint32_t oob;
+};
+
+// Load j of the next-step loads: first the B fragments, then the gathers.
+template <int ND, int NS, int J>
+__device__ __attribute__((always_inline)) inline void step_load(StepState<ND, NS>& st) {
+  constexpr int NB = ND * NS * kNT;
+  if constexpr (J < NB) {
+    constexpr int di = J / (NS * kNT), sm = (J / kNT) % NS, nt = J % kNT;
+    st.bn[di][sm][nt] = buffer_load16(st.wrs, st.boff[di][nt], st.wsoff[sm]);
+  } else {
+    constexpr int g = J - NB, p = g / kGR, u = g % kGR;
+    st.xn[g] = buffer_load16(st.xrs, p <= st.glp ? st.xoff[u] : st.oob, st.xsoff + (uint32_t)p * (kC * 4));
   }
 }
 
-template <int L, int ND, int NS>
-__device__ inline void main_gemm(const MfmaParams& P, char* smem, int m, int lo, int nd,
-                                 f32x4 (&acc)[ND][NS][kRT]) {
+template <int ND, int NS, int I>
+__device__ __attribute__((always_inline)) inline void step_mfma(StepState<ND, NS>& st) {
+  constexpr int PR = ND * kNT * NS * NS;  // MFMAs per row tile
+  constexpr int rt = I / PR, j = I % PR;
+  if constexpr (NS == 1) {
+    constexpr int di = j / kNT, nt = j % kNT;
+    st.acc[di][0][nt][rt] = mfma(as_bf16x8(st.ap[rt]), as_bf16x8(st.b[di][0][nt]), st.acc[di][0][nt][rt]);
+  } else {
+    constexpr int ph = j / (2 * ND * kNT), jj = j % (2 * ND * kNT);
+    constexpr int di = jj / (2 * kNT), nt = (jj / 2) % kNT, mt = jj % 2;
+    if constexpr (ph == 0)
+      st.acc[di][mt][nt][rt] = mfma(as_bf16x8(st.ap[rt]), as_bf16x8(st.b[di][mt][nt]), st.acc[di][mt][nt][rt]);
+    else if constexpr (mt == 0)
+      st.acc[di][0][nt][rt] = mfma(as_bf16x8(st.am[rt]), as_bf16x8(st.nb2[di][nt]), st.acc[di][0][nt][rt]);
+    else
+      st.acc[di][1][nt][rt] = mfma(as_bf16x8(st.am[rt]), as_bf16x8(st.b[di][0][nt]), st.acc[di][1][nt][rt]);
+  }
+}
+
+template <int ND, int NS, int D0, int D1>
+__device__ __attribute__((always_inline)) inline void step_dots(StepState<ND, NS>& st) {
+  if constexpr (D0 < D1) {
+    constexpr int p = D0 / (4 * kGR * NS), r = D0 % (4 * kGR * NS);
+    constexpr int u = r / (4 * NS), q = (r / NS) % 4, sg = r % NS;
+    const u32x4 v = st.xr[kGR * p + u];
+    const uint32_t xv = q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+    if constexpr (sg == 0) st.vp[u][q] = dot2(st.dp[u][p], xv, st.vp[u][q]);
+    else st.vm[u][q] = dot2(st.dm[u][p], xv, st.vm[u][q]);
+    step_dots<ND, NS, D0 + 1, D1>(st);
+  }
+}
+
+template <int ND, int NS, int I>
+__device__ __attribute__((always_inline)) inline void step_seq(StepState<ND, NS>& st) {
+  constexpr int F = ND * kNT * NS * NS * kRT;
+  constexpr int D = kMaxPairs * kGR * 4 * NS;
+  constexpr int NL = ND * NS * kNT + kGR * kMaxPairs;  // loads of the next step
+  constexpr int SP = (2 * F / 3) / NL > 0 ? (2 * F / 3) / NL : 1;
+  if constexpr (I < F) {
+    step_mfma<ND, NS, I>(st);
+    if constexpr (I % SP == 0 && I / SP < NL) step_load<ND, NS, I / SP>(st);
+    step_dots<ND, NS, I * D / F, (I + 1) * D / F>(st);
+    __builtin_amdgcn_sched_barrier(0);
+    step_seq<ND, NS, I + 1>(st);
+  } else if constexpr (I / SP < NL) {
+    // more loads than MFMA slots: issue the rest
+    step_load<ND, NS, I / SP>(st);
+    step_seq<ND, NS, I + SP>(st);
+  }
+}
+
+// K step k of an A chunk: MFMAs on the current chunk (abuf) with B
+// fragments b, interleaved with generator unit k of the next chunk from the
+// gathers xr (written into anext) and with the loads of the next K step:
+// its B fragments (step nstep) into bn and the gathers of the next
+// generator unit (slice nk of a chunk of degree nglp) into xn.
+template <int L, int M, int LO, int ND>
+__device__ inline void fused_step(const uint16_t* abuf, int k, const u32x4 (&b)[ND][M ? 2 : 1][kNT],
+                                  f32x4 (&acc)[ND][M ? 2 : 1][kNT][kRT], const float* sG, const Ctx& c,
+                                  const u32x4 (&xr)[kGR * kMaxPairs], const uint32_t (&dp)[kGR][kMaxPairs],
+                                  const uint32_t (&dm)[kGR][kMaxPairs], uint16_t* anext,
+                                  u32x4 (&bn)[ND][M ? 2 : 1][kNT], __amdgpu_buffer_rsrc_t wrs,
+                                  const uint32_t (&boff)[ND][kNT], int nstep, u32x4 (&xn)[kGR * kMaxPairs],
+                                  __amdgpu_buffer_rsrc_t xrs, int nglp, int nk, uint32_t oob) {
+  constexpr int NS = M ? 2 : 1;
+  constexpr int KM = (L + 1 - M) * kC;
+  constexpr uint32_t w1_byte = (uint32_t)(M == 0 ? 0 : w1_offset(L, M)) * 2u;
+  constexpr uint32_t w2_byte = w1_byte + (uint32_t)(KM * KM) * 2u;
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15;
-  const int g4 = lane >> 4;
-  uint16_t* abase = (uint16_t*)(smem + Lds<L>::kA);
-  const int KM = (L + 1 - m) * kC;
-  const int NQ = (L + 1 - m) * (kC / kKC);
-  const uint32_t w1_byte = (uint32_t)(m == 0 ? 0 : so2_w1_offset(L, kC, m)) * 2u;
-  const uint32_t w2_byte = w1_byte + (uint32_t)(KM * KM) * 2u;
-  const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(P.w_so2, P.w_bytes);
-  const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(P.x, P.x_bytes);
-
-  const Smem& S = *(const Smem*)smem;
-  constexpr int NC = Cfg<L>::NC;
-  u32x4 b1[ND], b2[ND], n1[ND], n2[ND];
-  u32x4 xr[kMaxComp];
-  load_b<L, ND, NS>(wrs, w1_byte, w2_byte, KM, m, lo, nd, 0, b1, b2);
-  gen_load(xrs, S, NC, m, 0, xr);
-  gen_store<L, NS>(smem, m, m, 0, xr, abase);
-  __syncthreads();
-  for (int s = 0; s < 2 * NQ; ++s) {
-    const int q = s >> 1;
-    const int ks = s & 1;
-    const uint16_t* abuf = abase + (q & 1) * (2 * kM * kApad);
-    const int lq = m + (q + 1) / (kC / kKC);      // next A chunk
-    const int cq = kKC * ((q + 1) % (kC / kKC));
-    // gathers for the next A chunk go out first; they land during this chunk's MFMAs
-    if (ks == 0 && q + 1 < NQ) gen_load(xrs, S, NC, lq, cq, xr);
-    if (s + 1 < 2 * NQ) load_b<L, ND, NS>(wrs, w1_byte, w2_byte, KM, m, lo, nd, s + 1, n1, n2);
+  const int grp = 4 * k + (lane >> 4);
+  u32x4 ap[kRT], am[kRT];
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) {
-      const int off = (16 * rt + l16) * kApad + 32 * ks + 8 * g4;
-      const u32x4 ap = *(const u32x4*)(abuf + off);
-      if (NS == 1) {
+  for (int rt = 0; rt < kRT; ++rt) {
+    const int o = a_off(16 * rt + l16, grp);
+    ap[rt] = *(const u32x4*)(abuf + o);
+    if constexpr (NS > 1) am[rt] = *(const u32x4*)(abuf + kAplane + o);
+  }
+  u32x4 nb2[ND][kNT];
 #pragma unroll
-        for (int di = 0; di < ND; ++di)
-          acc[di][0][rt] = mfma(as_bf16x8(ap), as_bf16x8(b1[di]), acc[di][0][rt]);
-      } else {
-        const u32x4 am = *(const u32x4*)(abuf + kM * kApad + off);
-        const u32x4 amn = am ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  for (int di = 0; di < ND; ++di)
 #pragma unroll
-        for (int di = 0; di < ND; ++di) {
-          if (di < nd) {
-            acc[di][0][rt] = mfma(as_bf16x8(ap), as_bf16x8(b1[di]), acc[di][0][rt]);
-            acc[di][0][rt] = mfma(as_bf16x8(amn), as_bf16x8(b2[di]), acc[di][0][rt]);
-            acc[di][NS - 1][rt] = mfma(as_bf16x8(ap), as_bf16x8(b2[di]), acc[di][NS - 1][rt]);
-            acc[di][NS - 1][rt] = mfma(as_bf16x8(am), as_bf16x8(b1[di]), acc[di][NS - 1][rt]);
-          }
-        }
-      }
-    }
-    if (ks == 1 && q + 1 < NQ) gen_store<L, NS>(smem, m, lq, cq, xr, abase + ((q + 1) & 1) * (2 * kM * kApad));
+    for (int nt = 0; nt < kNT; ++nt)
+      nb2[di][nt] = NS > 1 ? b[di][NS - 1][nt] ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}
+                           : b[di][0][nt];
+  float vp[kGR][4], vm[kGR][4];
 #pragma unroll
-    for (int di = 0; di < ND; ++di) {
-      b1[di] = n1[di];
-      b2[di] = n2[di];
-    }
-    if (ks == 1) __syncthreads();
+  for (int u = 0; u < kGR; ++u)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) vp[u][q] = vm[u][q] = 0.0f;
+  const uint32_t sb = 1024u * (uint32_t)nstep;
+  uint32_t xo[kGR];
+#pragma unroll
+  for (int u = 0; u < kGR; ++u) xo[u] = c.xoff[u];
+  StepState<ND, NS> st{ap, am, b, nb2, acc, xr, dp, dm, vp, vm,
+                       bn, wrs, boff, {w1_byte + sb, w2_byte + sb},
+                       xn, xrs, {}, (uint32_t)(pair_off(nglp) * kC + 32 * nk) * 4u, nglp, oob};
+#pragma unroll
+  for (int u = 0; u < kGR; ++u) st.xoff[u] = xo[u];
+  step_seq<ND, NS, 0>(st);
+#pragma unroll
+  for (int u = 0; u < kGR; ++u) {
+    const int r = c.r0 + kGStride * u;
+    const f32x4 g = *(const f32x4*)(sG + g_off(r, 8 * k + c.c8));
+    const int ao = a_off(r, 4 * k + (c.c8 >> 1)) + 4 * (c.c8 & 1);
+    typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+    *(u32x2*)(anext + ao) = u32x2{pack_bf16x2(vp[u][0] * g.x, vp[u][1] * g.y), pack_bf16x2(vp[u][2] * g.z, vp[u][3] * g.w)};
+    if constexpr (NS > 1)
+      *(u32x2*)(anext + kAplane + ao) =
+          u32x2{pack_bf16x2(vm[u][0] * g.x, vm[u][1] * g.y), pack_bf16x2(vm[u][2] * g.z, vm[u][3] * g.w)};
   }
 }
 
@@ -394,170 +676,280 @@ __device__ inline void main_gemm(const MfmaParams& P, char* smem, int m, int lo,
 
 // Rotate back and sum over neighbours for output degree l of block m:
 //   T[l] += A'(D, slots) x B'(w * yt).
-// yt[s][rt] is the main GEMM accumulator of this degree (s = 0: +m or m = 0,
-// s = 1: -m), lane rows 4 (lane/16) + i of row tile rt, column lane % 16.
-// B' is yt scaled by the lane's head weight and rounded to bf16, packed so
-// that K index 8 g + jj of lane group g is
+// yt[s][nt][rt] is the main GEMM accumulator of this degree (s = 0: +m or
+// m = 0, s = 1: -m), lane rows 4 (lane/16) + i of row tile rt, column lane %
+// 16 of column tile nt.  B' is yt scaled by the lane's head weight and
+// rounded to bf16, packed so that K index 8 g + jj of lane group g is
 //   m > 0:  edge 16 st + 4 g + (jj & 3), sign + for jj < 4, - otherwise
 //   m = 0:  edge 16 (2 st + jj / 4) + 4 g + (jj & 3);
 // A' row R of the accumulator (R = kSlots l^2 + slot (2l+1) + m' + l) holds
 // D^l_e[l +- m][m' + l] in the same K order when edge e belongs to that
 // slot's target, 0 otherwise (and 0 on rows of other degrees).  A' does not
-// depend on the output channels, so the whole workgroup builds it once per
-// pass into LDS (aprime_build) and every wave reads it from there.
+// depend on the output channels, so the workgroup builds it once per pass
+// into LDS (aprime_build) and every wave reads it from there.  The target
+// accumulators T stay in registers, in the MFMA C layout.
 
-__device__ inline int deg_tiles(int l) {
-  return (kSlots * (l + 1) * (l + 1) - 1) / 16 - (kSlots * l * l) / 16 + 1;
-}
-
-// A' fragments of a pass (degrees lo .. lo+nd-1), in the order
-// (degree, tile, K step), 64 lanes x 16 bytes each, written to frag.
-template <int L>
-__device__ inline void aprime_build(char* smem, int m, int lo, int nd, u32x4* frag) {
+// A' fragments of pass PI, in the order (degree, tile, K step), 64 lanes x
+// 16 bytes each.  Wave w builds fragments w, w + 4, ...; the fragment decode
+// is wave-uniform.
+template <int L, int PI>
+__device__ inline void aprime_build(char* smem, u32x4* frag) {
+  constexpr PassInfo pi = pass_info(L, PI);
+  constexpr int M = pi.M, LO = pi.LO;
+  constexpr int STEPS = M == 0 ? kRT / 2 : kRT;
+  constexpr int TOTAL = frag_count(L, PI);
   const Smem& S = *(const Smem*)smem;
-  const float* sD = (const float*)(smem + Lds<L>::kD);
-  const int steps = m == 0 ? kRT / 2 : kRT;
-  int total = 0;
-  for (int di = 0; di < nd; ++di) total += deg_tiles(lo + di) * steps;
-  for (int idx = threadIdx.x; idx < total * 64; idx += kThreads) {
-    int f = idx >> 6;
-    const int lane = idx & 63;
-    int l = lo;
-    while (f >= deg_tiles(l) * steps) {
-      f -= deg_tiles(l) * steps;
+  const uint32_t* sD = (const uint32_t*)(smem + Lds<L>::kD);
+  const int lane = threadIdx.x & 63;
+  const int g4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int f = wave; f < TOTAL; f += kWaves) {
+    int ff = f, l = LO;
+    while (ff >= deg_tiles(l) * STEPS) {
+      ff -= deg_tiles(l) * STEPS;
       ++l;
     }
-    const int ot = (kSlots * l * l) / 16 + f / steps;
-    const int st = f % steps;
+    const int ot = (kSlots * l * l) / 16 + ff / STEPS;
+    const int st = ff % STEPS;
     const int n = 2 * l + 1;
-    const int r0 = kSlots * l * l, r1 = kSlots * (l + 1) * (l + 1);
-    const int R = 16 * ot + (lane & 15);
-    const bool mine = R >= r0 && R < r1;
-    const int oslot = mine ? (R - r0) / n : -1;
-    const int omp = mine ? (R - r0) - oslot * n : 0;
-    const int g4 = lane >> 4;
-    float av[8];
+    const int rr = 16 * ot + (lane & 15) - kSlots * l * l;
+    const bool mine = rr >= 0 && rr < kSlots * n;
+    const int oslot = mine ? (int)(((float)rr + 0.5f) * (1.0f / (float)n)) : -1;
+    const int omp = mine ? rr - oslot * n : 0;
+    const uint32_t* dl = sD + dpair_off(l) + (omp >> 1);
+    const int sh = (omp & 1) * 16;
+    unsigned int hv[8];
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
       int r, srow;
-      if (m > 0) {
+      if constexpr (M > 0) {
         r = 16 * st + 4 * g4 + (jj & 3);
-        srow = (jj < 4) ? (l + m) : (l - m);
+        srow = (jj < 4) ? (l + M) : (l - M);
       } else {
         r = 16 * (2 * st + (jj >> 2)) + 4 * g4 + (jj & 3);
         srow = l;
       }
-      av[jj] = S.row_slot[r] == oslot ? sD[r * Cfg<L>::WT + wig_offset(l) + srow * n + omp] : 0.0f;
+      const uint32_t w = dl[r * Cfg<L>::DPW + srow * (l + 1)];
+      hv[jj] = S.row_slot[r] == oslot ? (w >> sh) & 0xffffu : 0u;
     }
     u32x4 a;
-    a.x = pack_bf16x2(av[0], av[1]);
-    a.y = pack_bf16x2(av[2], av[3]);
-    a.z = pack_bf16x2(av[4], av[5]);
-    a.w = pack_bf16x2(av[6], av[7]);
-    frag[idx] = a;
+    a.x = hv[0] | (hv[1] << 16);
+    a.y = hv[2] | (hv[3] << 16);
+    a.z = hv[4] | (hv[5] << 16);
+    a.w = hv[6] | (hv[7] << 16);
+    frag[f * 64 + lane] = a;
   }
 }
 
-template <int L, int NS>
-__device__ inline void rot_back(char* smem, const f32x4 (&yt)[NS][kRT], int l, int head,
-                                const u32x4* frag) {
+template <int L, int NS, int l>
+__device__ inline void rot_back(char* smem, const Ctx& c, const f32x4 (&yt)[NS][kNT][kRT], const u32x4* frag,
+                                f32x4 (&T)[Cfg<L>::TT][kNT]) {
   const float* sW = (const float*)(smem + Lds<L>::kW);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int g4 = lane >> 4;
   constexpr bool M0 = NS == 1;
-  u32x4 bq[kRT];
+  constexpr int kSteps = M0 ? kRT / 2 : kRT;
+  constexpr int ot0 = (kSlots * l * l) / 16;
+  u32x4 bq[kNT][kRT];
 #pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) {
-    float w4[4];
+  for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w4[i] = sW[(16 * rt + 4 * g4 + i) * kMaxHeads + head];
-    if (!M0) {
-      const f32x4 yp = yt[0][rt], ym = yt[NS - 1][rt];
-      bq[rt].x = pack_bf16x2(yp[0] * w4[0], yp[1] * w4[1]);
-      bq[rt].y = pack_bf16x2(yp[2] * w4[2], yp[3] * w4[3]);
-      bq[rt].z = pack_bf16x2(ym[0] * w4[0], ym[1] * w4[1]);
-      bq[rt].w = pack_bf16x2(ym[2] * w4[2], ym[3] * w4[3]);
-    } else {
-      const f32x4 y0 = yt[0][rt];
-      const unsigned int lo01 = pack_bf16x2(y0[0] * w4[0], y0[1] * w4[1]);
-      const unsigned int lo23 = pack_bf16x2(y0[2] * w4[2], y0[3] * w4[3]);
-      if ((rt & 1) == 0) {
-        bq[rt].x = lo01;
-        bq[rt].y = lo23;
+    for (int rt = 0; rt < kRT; ++rt) {
+      float w4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w4[i] = sW[(16 * rt + 4 * g4 + i) * kMaxHeads + c.head[nt]];
+      if constexpr (!M0) {
+        const f32x4 yp = yt[0][nt][rt], ym = yt[NS - 1][nt][rt];
+        bq[nt][rt].x = pack_bf16x2(yp[0] * w4[0], yp[1] * w4[1]);
+        bq[nt][rt].y = pack_bf16x2(yp[2] * w4[2], yp[3] * w4[3]);
+        bq[nt][rt].z = pack_bf16x2(ym[0] * w4[0], ym[1] * w4[1]);
+        bq[nt][rt].w = pack_bf16x2(ym[2] * w4[2], ym[3] * w4[3]);
       } else {
-        bq[rt - 1].z = lo01;
-        bq[rt - 1].w = lo23;
+        const f32x4 y0 = yt[0][nt][rt];
+        const unsigned int lo01 = pack_bf16x2(y0[0] * w4[0], y0[1] * w4[1]);
+        const unsigned int lo23 = pack_bf16x2(y0[2] * w4[2], y0[3] * w4[3]);
+        if ((rt & 1) == 0) {
+          bq[nt][rt].x = lo01;
+          bq[nt][rt].y = lo23;
+        } else {
+          bq[nt][rt - 1].z = lo01;
+          bq[nt][rt - 1].w = lo23;
+        }
       }
     }
-  }
-  constexpr int kSteps = M0 ? kRT / 2 : kRT;
-  const int ot0 = (kSlots * l * l) / 16;
-  const int nt = deg_tiles(l);
-  for (int q = 0; q < nt; ++q) {
-    f32x4* tile = tacc_tile<L>(smem, ot0 + q, wave);
-    f32x4 tv = tile[lane];
+#pragma unroll
+  for (int q = 0; q < deg_tiles(l); ++q)
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
       const u32x4 a = frag[(q * kSteps + st) * 64 + lane];
-      tv = mfma(as_bf16x8(a), as_bf16x8(bq[M0 ? 2 * st : st]), tv);
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+        T[ot0 + q][nt] = mfma(as_bf16x8(a), as_bf16x8(bq[nt][M0 ? 2 * st : st]), T[ot0 + q][nt]);
     }
-    tile[lane] = tv;
-  }
+}
+
+template <int L, int M, int LO, int DI, int ND>
+__device__ inline void rot_back_all(char* smem, const Ctx& c, const f32x4 (&acc)[ND][M ? 2 : 1][kNT][kRT],
+                                    const u32x4* frag, f32x4 (&T)[Cfg<L>::TT][kNT]) {
+  constexpr int STEPS = M == 0 ? kRT / 2 : kRT;
+  rot_back<L, M ? 2 : 1, LO + DI>(smem, c, acc[DI], frag, T);
+  if constexpr (DI + 1 < ND)
+    rot_back_all<L, M, LO, DI + 1, ND>(smem, c, acc, frag + deg_tiles(LO + DI) * STEPS * 64, T);
 }
 
 // ---------------------------------------------------------------- passes
 
-// One pass: block m, output degrees lo .. lo+nd-1 (nd <= ND): main GEMM,
-// then the A' fragments, then the rotate-back GEMM of each degree.
-template <int L, int ND, int NS>
-__device__ inline void pass(const MfmaParams& P, char* smem, int m, int lo, int nd, int head) {
-  f32x4 acc[ND][NS][kRT];
+// Generation target of A chunk q of pass PI (the chunk written while chunk
+// q is multiplied): the next degree of the same block, else the first
+// chunk of the next pass; after the last pass a dummy (degree 0 of m = 0)
+// whose result nobody reads.
+template <int L, int PI>
+__device__ inline void gen_target(int q, int& gm, int& glp) {
+  constexpr PassInfo pi = pass_info(L, PI), pn = pass_info(L, PI + 1);
+  constexpr int NCH = L + 1 - pi.M;
+  if (q + 1 < NCH) {
+    gm = pi.M;
+    glp = pi.M + q + 1;
+  } else {
+    gm = pn.M >= 0 ? pn.M : 0;
+    glp = pn.M >= 0 ? pn.M : 0;
+  }
+}
+
+// One pass: block M, output degrees LO .. LO+ND-1.  On entry the B fragments
+// of K step 0 are in flight in ring[0] and the gathers of generator unit 0
+// of chunk 0's target in xa; A chunk 0 is in LDS buffer chunks_before(PI) & 1
+// once every wave has reached the first barrier.
+//
+// K step s = 4 q + k multiplies A chunk q (degree M + q, channels 32 k ..
+// 32 k + 31) with ring[s & 1] while the B fragments of step s + 1 load into
+// ring[(s + 1) & 1]; its VALU work, generator unit k of the chunk after q
+// (slice k of the other buffer), uses gathers issued one step earlier and is
+// interleaved with the MFMAs.  The loop body is two K steps; one barrier
+// per A chunk.
+template <int L, int PI>
+__device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams& P, char* smem, const Ctx& c,
+                                                               f32x4 (&T)[Cfg<L>::TT][kNT],
+                                                               u32x4 (&ring)[2][pass_info(L, PI).ND]
+                                                                            [pass_info(L, PI).M ? 2 : 1][kNT],
+                                                               u32x4 (&xa)[kGR * kMaxPairs], u32x4 (&xb)[kGR * kMaxPairs]) {
+  constexpr PassInfo pi = pass_info(L, PI), pn = pass_info(L, PI + 1);
+  constexpr int M = pi.M, LO = pi.LO, ND = pi.ND, NS = M ? 2 : 1;
+  constexpr int NCH = L + 1 - M, NSTEP = 4 * NCH;
+  constexpr int PAR = chunks_before(L, PI) & 1;
+  const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(P.wf, P.w_bytes);
+  const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(P.xp, P.xp_bytes);
+  const uint32_t* sD = (const uint32_t*)(smem + Lds<L>::kD);
+  const float* sG = (const float*)(smem + Lds<L>::kG);
+  uint16_t* abase = (uint16_t*)(smem + Lds<L>::kA);
+  u32x4* frag = (u32x4*)(smem + Lds<L>::kF);
+  const uint32_t oob = P.xp_bytes;
+
+  uint32_t boff[ND][kNT];
+  b_offsets<L, M, LO, ND>(boff);
+
+  __syncthreads();  // chunk 0 written; every wave is done with the previous A'
+  aprime_build<L, PI>(smem, frag);
+
+  f32x4 acc[ND][NS][kNT][kRT];
 #pragma unroll
   for (int a = 0; a < ND; ++a)
 #pragma unroll
     for (int b = 0; b < NS; ++b)
 #pragma unroll
-      for (int c = 0; c < kRT; ++c) acc[a][b][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  main_gemm<L, ND, NS>(P, smem, m, lo, nd, acc);  // ends with a barrier
-  u32x4* frag = (u32x4*)(smem + Lds<L>::kA);       // the A chunks are dead now
-  aprime_build<L>(smem, m, lo, nd, frag);
-  __syncthreads();
-  const int steps = NS == 1 ? kRT / 2 : kRT;
-  int fbase = 0;
+      for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-  for (int di = 0; di < ND; ++di) {
-    if (di < nd) {
-      rot_back<L, NS>(smem, acc[di], lo + di, head, frag + fbase * 64);
-      fbase += deg_tiles(lo + di) * steps;
+        for (int rt = 0; rt < kRT; ++rt) acc[a][b][nt][rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  uint32_t dp[kGR][kMaxPairs], dm[kGR][kMaxPairs];
+  int glp = 0;
+#pragma nounroll
+  for (int s = 0; s < NSTEP; s += 2) {
+    const int q = s >> 2;
+    const int k = s & 3;  // 0 or 2
+    if (k == 0) {
+      int gm;
+      gen_target<L, PI>(q, gm, glp);
+      gen_dpairs(sD, Cfg<L>::DPW, c, gm, glp, dp, dm);
     }
+    // degree of the chunk whose generator unit 0 is gathered in step s + 1
+    int glp2 = glp;
+    if (k == 2) {
+      int gm2;
+      gen_target<L, PI>(q + 1 < NCH ? q + 1 : q, gm2, glp2);
+    }
+    const uint16_t* acur = abase + ((PAR + q) & 1) * kAbuf;
+    uint16_t* anext = abase + ((PAR + q + 1) & 1) * kAbuf;
+    // K step s: unit k from xa; loads B of step s + 1 and the gathers of unit k + 1
+    fused_step<L, M, LO, ND>(acur, k, ring[0], acc, sG, c, xa, dp, dm, anext, ring[1], wrs, boff, s + 1, xb, xrs,
+                             glp, k + 1, oob);
+    // K step s + 1: unit k + 1 from xb; loads B of step s + 2 and the gathers of the next unit
+    fused_step<L, M, LO, ND>(acur, k + 1, ring[1], acc, sG, c, xb, dp, dm, anext, ring[0], wrs, boff,
+                             min(s + 2, NSTEP - 1), xa, xrs, glp2, (k + 2) & 3, oob);
+    if (k == 2) __syncthreads();  // chunk q + 1 written, chunk q read by every wave
   }
-  __syncthreads();  // the next pass overwrites the fragments
+
+  if constexpr (pn.M >= 0) {
+    constexpr int NDn = pn.ND, NSn = pn.M ? 2 : 1;
+    u32x4 nring[2][NDn][NSn][kNT];
+    uint32_t nboff[NDn][kNT];
+    b_offsets<L, pn.M, pn.LO, NDn>(nboff);
+    load_b<L, pn.M, pn.LO, NDn>(wrs, nboff, 0, nring[0]);
+    // gathers of generator unit 0 for the next pass's chunk 0 target
+    int gm, glp0;
+    gen_target<L, PI + 1>(0, gm, glp0);
+    gen_issue(xrs, c, oob, glp0, 0, xa);
+    rot_back_all<L, M, LO, 0, ND>(smem, c, acc, frag, T);
+    run_pass<L, PI + 1>(P, smem, c, T, nring, xa, xb);
+  } else {
+    rot_back_all<L, M, LO, 0, ND>(smem, c, acc, frag, T);
+  }
 }
 
 // ---------------------------------------------------------------- flush
 
-// Write every slot whose target finished in this chunk to y (whole 512-byte
-// rows) and clear it.  Accumulator element (slot, comp, c) sits in tile
-// R / 16 (R = kSlots l^2 + slot (2l+1) + comp - l^2) of wave c / 16, lane
-// 16 ((R % 16) / 4) + c % 16, entry R % 4.
+// Accumulator row R = kSlots l^2 + slot (2l+1) + comp - l^2 as slot << 8 |
+// comp (0xffff for the padding rows of the last tile).
+__device__ inline uint16_t row_info(int R, int TROWS) {
+  if (R >= TROWS) return 0xffff;
+  int l = 0;
+  while (kSlots * (l + 1) * (l + 1) <= R) ++l;
+  const int rr = R - kSlots * l * l, n = 2 * l + 1;
+  return (uint16_t)(((rr / n) << 8) | (l * l + rr % n));
+}
+
+// Write every slot whose target finished in this chunk to y and clear it.
+// T[ot][nt] entry i of lane (g, l16) is accumulator row R = 16 ot + 4 g + i,
+// column 32 wave + 16 nt + l16.  Straight-line code: each entry looks its
+// row up in the row table and its slot's target in flush_t, and lanes with
+// nothing to write store past the end of a buffer descriptor that covers
+// the chunk's (at most kSlots) target rows of y.
 template <int L>
-__device__ inline void flush_slots(char* smem, float* y) {
+__device__ inline void flush_slots(const MfmaParams& P, const Smem& S, int t_first, f32x4 (&T)[Cfg<L>::TT][kNT]) {
   constexpr int NC = Cfg<L>::NC;
-  const Smem& S = *(const Smem*)smem;
-  float* T = (float*)(smem + Lds<L>::kT);
-  for (int s = 0; s < kSlots; ++s) {
-    const int t = S.flush_t[s];
-    if (t < 0) continue;
-    for (int a = threadIdx.x; a < NC * kC; a += kThreads) {
-      const int comp = a / kC, c = a % kC;
-      const int l = (int)sqrtf((float)comp + 0.5f);
-      const int R = kSlots * l * l + s * (2 * l + 1) + (comp - l * l);
-      const int idx = (((R >> 4) * kWaves + (c >> 4)) * 64 + 16 * ((R & 15) >> 2) + (c & 15)) * 4 + (R & 3);
-      y[(int64_t)t * NC * kC + a] = T[idx];
-      T[idx] = 0.0f;
+  constexpr uint32_t kRow = NC * kC * 4;  // bytes of one target row of y
+  if (S.flush_t[0] < 0 && S.flush_t[1] < 0 && S.flush_t[2] < 0 && S.flush_t[3] < 0) return;
+  const int lane = threadIdx.x & 63;
+  const int g4 = lane >> 4;
+  const uint32_t colb = 4u * (uint32_t)(16 * kNT * (threadIdx.x >> 6) + (lane & 15));
+  const int nt_rows = min(kSlots, P.n_targets - t_first);
+  const __amdgpu_buffer_rsrc_t yrs = buffer_rsrc(P.y + (int64_t)t_first * NC * kC, (uint32_t)nt_rows * kRow);
+  const uint32_t oob = (uint32_t)kSlots * kRow;
+#pragma unroll
+  for (int ot = 0; ot < Cfg<L>::TT; ++ot)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int info = S.rowinfo[16 * ot + 4 * g4 + i];
+      const int t = S.flush_t[(info >> 8) & (kSlots - 1)];
+      const bool out = info != 0xffff && t >= 0;
+      const uint32_t off = out ? (uint32_t)(t - t_first) * kRow + (uint32_t)(info & 0xff) * (kC * 4) + colb : oob;
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        const float v = T[ot][nt][i];
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), yrs, (int)(off + 64u * nt), 0, 0);
+        T[ot][nt][i] = out ? 0.0f : v;
+      }
     }
-  }
 }
 
 // ---------------------------------------------------------------- kernel
@@ -580,15 +972,19 @@ __device__ inline int group_start(const MfmaParams& P, int g, int n_groups) {
 }
 
 template <int L>
-__global__ void __launch_bounds__(kThreads) attn_mfma_kernel(MfmaParams P, int n_groups) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
+attn_mfma_kernel(MfmaParams P, int n_groups) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   Smem& S = *(Smem*)smem;
-  float* sD = (float*)(smem + Lds<L>::kD);
-  uint16_t* sG = (uint16_t*)(smem + Lds<L>::kG);
+  uint32_t* sD = (uint32_t*)(smem + Lds<L>::kD);
+  float* sG = (float*)(smem + Lds<L>::kG);
   float* sW = (float*)(smem + Lds<L>::kW);
+  uint16_t* abase = (uint16_t*)(smem + Lds<L>::kA);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   constexpr int NC = Cfg<L>::NC;
+  constexpr PassInfo p0 = pass_info(L, 0);
+  constexpr int NS0 = p0.M ? 2 : 1;
 
   // Workgroup -> group of consecutive targets holding about E / n_groups
   // edges (group g starts at the first target whose edges start at or after
@@ -606,17 +1002,31 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(MfmaParams P, int n
     const int t = t_begin + a / (NC * kC);
     if (P.row_ptr[t] == P.row_ptr[t + 1]) P.y[(int64_t)t * NC * kC + a % (NC * kC)] = 0.0f;
   }
-  for (int a = tid; a < Cfg<L>::TT * kWaves * 64; a += kThreads)
-    ((f32x4*)(smem + Lds<L>::kT))[a] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  static_assert(16 * Cfg<L>::TT <= 112, "row table");
+  if (tid < 16 * Cfg<L>::TT) S.rowinfo[tid] = row_info(tid, Cfg<L>::TROWS);
+
+  f32x4 T[Cfg<L>::TT][kNT];
+#pragma unroll
+  for (int ot = 0; ot < Cfg<L>::TT; ++ot)
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) T[ot][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int e_end = P.row_ptr[t_end];
   int e = P.row_ptr[t_begin];
   int t_cur = t_begin;
   const int H = P.H;
   const int dh = kC / H;
-  const int head = (16 * wave + (tid & 15)) / dh;
   const float inv_sqrt_d = 1.0f / sqrtf((float)dh);
   const float rc = P.cutoff;
+  const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(P.wf, P.w_bytes);
+  const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(P.xp, P.xp_bytes);
+
+  Ctx c;
+  c.r0 = tid >> 3;
+  c.c8 = tid & 7;
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) c.head[nt] = (16 * kNT * wave + 16 * nt + (tid & 15)) / dh;
 
   while (e < e_end) {
     while (P.row_ptr[t_cur + 1] <= e) ++t_cur;  // target of edge e
@@ -624,6 +1034,14 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(MfmaParams P, int n
     const int t_lim = min(t_first + kSlots, t_end);
     const int e_stop = min(min(e + kM, e_end), P.row_ptr[t_lim]);
     const int nrows = e_stop - e;
+
+    // B fragments of the first pass's first K step go out before the setup
+    u32x4 ring[2][p0.ND][NS0][kNT];
+    {
+      uint32_t boff[p0.ND][kNT];
+      b_offsets<L, p0.M, p0.LO, p0.ND>(boff);
+      load_b<L, p0.M, p0.LO, p0.ND>(wrs, boff, 0, ring[0]);
+    }
 
     // ---- phase A: per-edge setup
     if (tid <= kSlots) S.rp[tid] = P.row_ptr[min(t_first + tid, t_end)];
@@ -635,8 +1053,9 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(MfmaParams P, int n
       S.flush_t[tid] = (t <= t_first + sl && S.rp[t - t_first + 1] <= e_stop) ? t : -1;
     }
     if (tid < kM) {
-      // wave 0: one edge per lane: metadata, frame and all Wigner-D blocks
+      // wave 0: one edge per lane: metadata, frame and the Wigner-D pairs
       const int r = tid;
+      uint32_t* dr = sD + r * Cfg<L>::DPW;
       if (r < nrows) {
         int t, j;
         float rv[3];
@@ -647,13 +1066,14 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(MfmaParams P, int n
         const float inv = rho > 0.0f ? 1.0f / rho : 0.0f;
         float R[9];
         edge_frame(rv[0] * inv, rv[1] * inv, rv[2] * inv, R);
-        wigner_blocks_unrolled<L>(R, sD + r * Cfg<L>::WT);
+        wigner_pairs<L>(R, dr);
       } else {
         S.row_j[r] = -1;
         S.row_slot[r] = -2;  // matches no slot
+        for (int q = 0; q < Cfg<L>::DPW; ++q) dr[q] = 0u;
       }
     } else {
-      // waves 1..7: radial gates (64 rows x 8 groups of 16 channels), then
+      // waves 1..3: radial gates (64 rows x 8 groups of 16 channels), then
       // the softmax weights (64 rows x kMaxHeads)
       for (int it = tid - kM; it < kM * (kC / 16) + kM * kMaxHeads; it += kThreads - kM) {
         if (it < kM * (kC / 16)) {
@@ -675,15 +1095,15 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(MfmaParams P, int n
               for (int kk = 0; kk < P.K; ++kk) {
                 const float dr = rho - step * (float)kk;
                 const float phi = expf(-dr * dr * inv2s2);
-                const uint16_t* wr = P.w_rad + (int64_t)kk * kC + c0;
-                const u32x4 v0 = *(const u32x4*)wr;
-                const u32x4 v1 = *(const u32x4*)(wr + 8);
-                const float wv[16] = {bf_lo(v0.x), bf_hi(v0.x), bf_lo(v0.y), bf_hi(v0.y),
-                                      bf_lo(v0.z), bf_hi(v0.z), bf_lo(v0.w), bf_hi(v0.w),
-                                      bf_lo(v1.x), bf_hi(v1.x), bf_lo(v1.y), bf_hi(v1.y),
-                                      bf_lo(v1.z), bf_hi(v1.z), bf_lo(v1.w), bf_hi(v1.w)};
+                const f32x4* wr = (const f32x4*)(P.wrad + (int64_t)kk * kC + c0);
 #pragma unroll
-                for (int q = 0; q < 16; ++q) gv[q] += phi * wv[q];
+                for (int v = 0; v < 4; ++v) {
+                  const f32x4 w4 = wr[v];
+                  gv[4 * v + 0] += phi * w4.x;
+                  gv[4 * v + 1] += phi * w4.y;
+                  gv[4 * v + 2] += phi * w4.z;
+                  gv[4 * v + 3] += phi * w4.w;
+                }
               }
               if (P.flags & SO2_FLAG_RBF_ENVELOPE) {
                 const float u = envelope_u(rho / rc, P.p);
@@ -692,17 +1112,9 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(MfmaParams P, int n
               }
             }
           }
-          u32x4 g0, g1;
-          g0.x = pack_bf16x2(gv[0], gv[1]);
-          g0.y = pack_bf16x2(gv[2], gv[3]);
-          g0.z = pack_bf16x2(gv[4], gv[5]);
-          g0.w = pack_bf16x2(gv[6], gv[7]);
-          g1.x = pack_bf16x2(gv[8], gv[9]);
-          g1.y = pack_bf16x2(gv[10], gv[11]);
-          g1.z = pack_bf16x2(gv[12], gv[13]);
-          g1.w = pack_bf16x2(gv[14], gv[15]);
-          *(u32x4*)(sG + r * kGpad + c0) = g0;
-          *(u32x4*)(sG + r * kGpad + c0 + 8) = g1;
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            *(f32x4*)(sG + g_off(r, c0 / 4 + v)) = f32x4{gv[4 * v], gv[4 * v + 1], gv[4 * v + 2], gv[4 * v + 3]};
         } else {
           const int pr = it - kM * (kC / 16);
           const int r = pr / kMaxHeads, h = pr % kMaxHeads;
@@ -713,8 +1125,13 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(MfmaParams P, int n
             row_edge(P, S, e + r, t_first, t, j, rv);
             const float rho = sqrtf(rv[0] * rv[0] + rv[1] * rv[1] + rv[2] * rv[2]);
             const float u = envelope_u(rho / rc, P.p);
+            const f32x4* qv = (const f32x4*)(P.q + (int64_t)t * kC + h * dh);
+            const f32x4* kv = (const f32x4*)(P.k + (int64_t)j * kC + h * dh);
             float z = 0.0f;
-            for (int c = h * dh; c < (h + 1) * dh; ++c) z += P.q[(int64_t)t * kC + c] * P.k[(int64_t)j * kC + c];
+            for (int cc = 0; cc < dh / 4; ++cc) {
+              const f32x4 a = qv[cc], bb = kv[cc];
+              z += a.x * bb.x + a.y * bb.y + a.z * bb.z + a.w * bb.w;
+            }
             z *= inv_sqrt_d;
             wv = u * expf(z - P.stat_max[(int64_t)t * H + h]) * P.stat_inv[(int64_t)t * H + h];
           }
@@ -724,19 +1141,36 @@ __global__ void __launch_bounds__(kThreads) attn_mfma_kernel(MfmaParams P, int n
     }
     __syncthreads();
 
-    // ---- phase B: per-m GEMMs and the rotate-back GEMMs
-#pragma nounroll
-    for (int lo = 0; lo <= L; lo += 3) pass<L, 3, 1>(P, smem, 0, lo, min(3, L + 1 - lo), head);
-#pragma nounroll
-    for (int m = 1; m <= L; ++m) {
-#pragma nounroll
-      for (int lo = m; lo <= L; lo += kMaxDeg) pass<L, kMaxDeg, 2>(P, smem, m, lo, min(kMaxDeg, L + 1 - lo), head);
+    // ---- first A chunk (block p0.M, degree p0.M): all four generator units
+    {
+#pragma unroll
+      for (int u = 0; u < kGR; ++u) {
+        const int j = S.row_j[c.r0 + kGStride * u];
+        c.xoff[u] = j >= 0 ? ((uint32_t)j * Cfg<L>::NP * kC + 4 * c.c8) * 4u : P.xp_bytes;
+      }
+      uint32_t dp[kGR][kMaxPairs], dm[kGR][kMaxPairs];
+      gen_dpairs(sD, Cfg<L>::DPW, c, p0.M, p0.M, dp, dm);
+      u32x4 xa[kGR * kMaxPairs], xb[kGR * kMaxPairs];
+      gen_issue(xrs, c, P.xp_bytes, p0.M, 0, xa);
+      gen_issue(xrs, c, P.xp_bytes, p0.M, 1, xb);
+      gen_finish<NS0>(sG, c, 0, xa, dp, dm, abase);  // chunks_before(L, 0) = 0
+      gen_issue(xrs, c, P.xp_bytes, p0.M, 2, xa);
+      gen_finish<NS0>(sG, c, 1, xb, dp, dm, abase);
+      gen_issue(xrs, c, P.xp_bytes, p0.M, 3, xb);
+      gen_finish<NS0>(sG, c, 2, xa, dp, dm, abase);
+      // gathers of generator unit 0 for chunk 0's target
+      int gm, glp;
+      gen_target<L, 0>(0, gm, glp);
+      gen_issue(xrs, c, P.xp_bytes, glp, 0, xa);
+      gen_finish<NS0>(sG, c, 3, xb, dp, dm, abase);
+
+      // ---- phase B: every pass, each ending in its rotate-back GEMMs
+      run_pass<L, 0>(P, smem, c, T, ring, xa, xb);
     }
 
     // ---- phase D: write out targets whose last edge is in this chunk
-    flush_slots<L>(smem, P.y);
+    flush_slots<L>(P, S, t_first, T);
     e = e_stop;
-    __syncthreads();
   }
 }
 
@@ -759,22 +1193,42 @@ so2_status launch_L(const MfmaParams& P, int64_t n_edges, hipStream_t stream) {
   return SO2_OK;
 }
 
+// Workspace of the MFMA path: softmax statistics, the x pairs, w_rad in
+// fp32 and w_so2 in fragment order.
+struct ScratchLayout {
+  size_t stats, xp, wrad, wf, total;
+};
+
+size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+ScratchLayout scratch_layout(int n_atoms, int n_targets, int L, int H, int K) {
+  ScratchLayout s{};
+  s.stats = 0;
+  s.xp = up256(sizeof(float) * 2 * (size_t)n_targets * H);
+  s.wrad = s.xp + up256(sizeof(uint32_t) * (size_t)n_atoms * pair_off(L + 1) * kC);
+  s.wf = s.wrad + up256(sizeof(float) * (size_t)K * kC);
+  s.total = s.wf + up256(sizeof(uint16_t) * (size_t)w1_offset(L, L + 1));
+  return s;
+}
+
 MfmaParams make_params(const AttnArgs& a) {
   MfmaParams P{};
+  const ScratchLayout s = scratch_layout(a.n_atoms, a.n_targets, a.L, a.H, a.K);
+  char* base = (char*)a.scratch;
   P.pos = a.pos;
   P.row_ptr = a.row_ptr;
   P.col = a.col;
-  P.x = (const uint16_t*)a.x;
-  P.w_rad = (const uint16_t*)a.w_rad;
-  P.w_so2 = (const uint16_t*)a.w_so2;
+  P.xp = (const uint32_t*)(base + s.xp);
+  P.wrad = (const float*)(base + s.wrad);
+  P.wf = (const uint16_t*)(base + s.wf);
   P.q = a.q;
   P.k = a.k;
-  float* stats = (float*)a.scratch;
+  float* stats = (float*)(base + s.stats);
   P.stat_max = stats;
   P.stat_inv = stats + (size_t)a.n_targets * a.H;
   P.y = a.y;
-  P.x_bytes = (uint32_t)((uint64_t)a.n_atoms * (a.L + 1) * (a.L + 1) * kC * 2);
-  P.w_bytes = (uint32_t)(so2_w1_offset(a.L, kC, a.L + 1) * 2);
+  P.xp_bytes = (uint32_t)((uint64_t)a.n_atoms * pair_off(a.L + 1) * kC * 4);
+  P.w_bytes = (uint32_t)(w1_offset(a.L, a.L + 1) * 2);
   P.n_targets = a.n_targets;
   P.H = a.H;
   P.K = a.K;
@@ -786,24 +1240,55 @@ MfmaParams make_params(const AttnArgs& a) {
   return P;
 }
 
+template <int L>
+so2_status launch_pack_L(const AttnArgs& a, const MfmaParams& P, hipStream_t stream) {
+  const int64_t work = (int64_t)a.n_atoms * pair_off(L + 1) * (kC / 4) + (int64_t)a.K * kC + w1_offset(L, L + 1) / 8;
+  const int64_t blocks = std::min<int64_t>((work + 255) / 256, 8192);
+  hipLaunchKernelGGL(attn_pack_kernel<L>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (const uint16_t*)a.x, const_cast<uint32_t*>(P.xp), a.n_atoms, (const uint16_t*)a.w_rad,
+                     const_cast<float*>(P.wrad), a.K, (const uint16_t*)a.w_so2, const_cast<uint16_t*>(P.wf));
+  SO2_CHECK_LAUNCH();
+  return SO2_OK;
+}
+
 }  // namespace
 
 bool mfma_supported(int L, int C, int H, int n_atoms) {
-  // x is addressed through a 32-bit buffer descriptor
-  const uint64_t x_bytes = (uint64_t)n_atoms * (L + 1) * (L + 1) * C * 2;
+  // the x pairs are addressed through a 32-bit buffer descriptor, with room
+  // past the end for the zero reads of rows without an edge
+  const uint64_t xp_bytes = (uint64_t)n_atoms * pair_off(L + 1) * C * 4;
   return C == kC && L >= 1 && L <= 4 && H >= 1 && H <= kMaxHeads && C % H == 0 &&
-         x_bytes < 0xffffffffull;
+         xp_bytes < 0xffff0000ull;
 }
 
 bool mfma_aligned(const AttnArgs& a) {
   return !(((uintptr_t)a.x & 15) || ((uintptr_t)a.w_so2 & 15) || ((uintptr_t)a.w_rad & 15));
 }
 
-size_t mfma_scratch_bytes(int n_targets, int H) { return sizeof(float) * 2 * (size_t)n_targets * H + 256; }
+size_t mfma_scratch_bytes(int n_atoms, int n_targets, int L, int H, int K) {
+  return scratch_layout(n_atoms, n_targets, L, H, K).total;
+}
 
 so2_status launch_attention_mfma_prep(const AttnArgs& a, hipStream_t stream) {
-  if (a.n_targets == 0) return SO2_OK;
   const MfmaParams P = make_params(a);
+  so2_status st = SO2_OK;
+  switch (a.L) {
+    case 1:
+      st = launch_pack_L<1>(a, P, stream);
+      break;
+    case 2:
+      st = launch_pack_L<2>(a, P, stream);
+      break;
+    case 3:
+      st = launch_pack_L<3>(a, P, stream);
+      break;
+    case 4:
+      st = launch_pack_L<4>(a, P, stream);
+      break;
+    default:
+      return SO2_ERR_UNSUPPORTED;
+  }
+  if (st != SO2_OK || a.n_targets == 0) return st;
   hipLaunchKernelGGL(attn_stats_kernel, dim3((a.n_targets + 3) / 4), dim3(256), 0, stream, P, kC);
   SO2_CHECK_LAUNCH();
   return SO2_OK;

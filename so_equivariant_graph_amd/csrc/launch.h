@@ -63,8 +63,9 @@ so2_status launch_attention_valu(const AttnArgs& a, hipStream_t stream);
 // x, w_rad and w_so2 must be 16-byte aligned.
 bool mfma_supported(int L, int C, int H, int n_atoms);
 bool mfma_aligned(const AttnArgs& a);
-size_t mfma_scratch_bytes(int n_targets, int H);
-// softmax statistics pass, then the fused kernel
+size_t mfma_scratch_bytes(int n_atoms, int n_targets, int L, int H, int K);
+// prologue (x repacked as component pairs, w_rad in fp32) and softmax
+// statistics pass, then the fused kernel
 so2_status launch_attention_mfma_prep(const AttnArgs& a, hipStream_t stream);
 so2_status launch_attention_mfma(const AttnArgs& a, hipStream_t stream);
 
