@@ -41,7 +41,7 @@ so2_status check_desc(const so2_attn_desc* d) {
 }
 
 Kind pick_kind(const so2_attn_desc* d) {
-  if (d->dtype == SO2_BF16 && mfma_supported(d->l_max, d->channels, d->heads, d->n_atoms)) return kMfma;
+  if (d->dtype == SO2_BF16 && mfma_supported(d->l_max, d->channels, d->heads, d->n_rbf, d->n_atoms)) return kMfma;
   if (valu_supported(d->l_max, d->channels, d->heads)) return kValu;
   return kNone;
 }

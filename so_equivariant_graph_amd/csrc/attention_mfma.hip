@@ -84,6 +84,7 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kNT = kC / (16 * kWaves);  // 16-column tiles per wave: wave w owns channels 16 kNT w ..
 constexpr int kGR = 64 * 8 / kThreads;   // generator rows per lane (8 lanes per row and K step)
 constexpr int kGStride = kThreads / 8;   // distance between a lane's generator rows
+static_assert(kThreads == 8 * 64, "phase A maps 8 lanes to each of the 64 edge rows");
 constexpr int kM = 64;                // edges per chunk
 constexpr int kRT = kM / 16;          // row tiles
 constexpr int kSlots = 4;             // targets live in one chunk
@@ -93,6 +94,7 @@ constexpr int kAplane = kM * kKC;     // one sign plane of an A chunk, bf16
 constexpr int kAbuf = 2 * kAplane;    // one A buffer (both signs), bf16
 constexpr int kMaxHeads = 16;
 constexpr int kMaxPairs = 5;          // component pairs of one degree, L <= 4
+constexpr int kMaxRbf = 32;           // radial basis functions kept per edge in LDS
 
 // Component pairs: degree l has l + 1 pairs (2p, 2p+1), the last one padded
 // with zero.  pair_off(l) = pairs of the degrees below l.
@@ -290,6 +292,8 @@ struct Smem {
   int row_j[kM];
   int row_slot[kM];
   uint16_t rowinfo[112];  // accumulator row R -> slot << 8 | component, 0xffff past the rows
+  int row_t[kM];          // target of each edge row
+  f32x4 row_rv[kM];       // minimum-image edge vector and its length
 };
 
 // Passes in execution order: blocks m = 1..L, each in groups of at most two
@@ -348,7 +352,8 @@ struct Lds {
   static constexpr size_t kW = kG + sizeof(float) * kM * kC;                     // f32 [kM][kMaxHeads]
   static constexpr size_t kA = kW + sizeof(float) * kM * kMaxHeads;              // bf16 [2][2][kM][kKC], swizzled
   static constexpr size_t kF = kA + sizeof(uint16_t) * 2 * kAbuf;                // A' fragments u32x4 [][64]
-  static constexpr size_t kTotal = kF + sizeof(u32x4) * 64 * max_frags(L);
+  static constexpr size_t kPhi = kF + sizeof(u32x4) * 64 * max_frags(L);         // f32 [kM][kMaxRbf]
+  static constexpr size_t kTotal = kPhi + sizeof(float) * kM * kMaxRbf;
 };
 
 // 16-byte column groups are XOR-swizzled by row so that both the MFMA
@@ -432,9 +437,10 @@ __device__ inline void gen_issue(__amdgpu_buffer_rsrc_t xrs, const Ctx& c, uint3
   }
 }
 
-// D pairs of both generator rows for an A chunk (gm, glp): rows glp + gm and
-// glp - gm of D^glp, pairs 0..L (past glp they hold other entries of the
-// same edge, which meet zero gathers).
+// D pairs of the generator rows for an A chunk (gm, glp): rows glp + gm and
+// glp - gm of D^glp, pairs 0..glp; the pairs past glp are zero (their
+// gathers read zeros too) and are not read, since past the last row of a
+// degree lie the next edge's pairs or, after the last edge, other LDS data.
 __device__ inline void gen_dpairs(const uint32_t* sD, int DPW, const Ctx& c, int gm, int glp,
                                   uint32_t (&dp)[kGR][kMaxPairs], uint32_t (&dm)[kGR][kMaxPairs]) {
 #pragma unroll
@@ -442,8 +448,11 @@ __device__ inline void gen_dpairs(const uint32_t* sD, int DPW, const Ctx& c, int
     const uint32_t* d = sD + (c.r0 + kGStride * u) * DPW + dpair_off(glp);
 #pragma unroll
     for (int p = 0; p < kMaxPairs; ++p) {
-      dp[u][p] = d[(glp + gm) * (glp + 1) + p];
-      dm[u][p] = d[(glp - gm) * (glp + 1) + p];
+      const int pc = p <= glp ? p : glp;
+      const uint32_t vp = d[(glp + gm) * (glp + 1) + pc];
+      const uint32_t vm = d[(glp - gm) * (glp + 1) + pc];
+      dp[u][p] = p <= glp ? vp : 0u;
+      dm[u][p] = p <= glp ? vm : 0u;
     }
   }
 }
@@ -516,11 +525,12 @@ __device__ inline void b_offsets(uint32_t (&boff)[ND][kNT]) {
       boff[di][nt] = 16u * lane + (uint32_t)(((LO + di - M) * 8 + kNT * wave + nt) * (KM / 32)) * 1024u;
 }
 
-// One K step with its generator unit interleaved.  MFMA i of the step is
-// followed by the generator's dot products [i D / F, (i+1) D / F) (D dot
-// products, F MFMAs) and a scheduling fence, so that the matrix core and
-// the vector ALU of the SIMD work at the same time; the unit's gate,
-// rounding and LDS store follow the last MFMA.
+// One K step with its generator unit interleaved.  In source order MFMA i
+// of the step is followed by the generator's dot products [i D / F, (i+1)
+// D / F) (D dot products, F MFMAs) and the loads of the next step are
+// spread over the first two thirds of the MFMAs; the compiler schedules
+// the block from there (with two waves per SIMD a strict order measured
+// slower).  The unit's gate, rounding and LDS store follow the last MFMA.
 template <int ND, int NS>
 struct StepState {
   const u32x4* ap;                      // [kRT] + plane fragments
@@ -601,7 +611,6 @@ __device__ __attribute__((always_inline)) inline void step_seq(StepState<ND, NS>
     step_mfma<ND, NS, I>(st);
     if constexpr (I % SP == 0 && I / SP < NL) step_load<ND, NS, I / SP>(st);
     step_dots<ND, NS, I * D / F, (I + 1) * D / F>(st);
-    __builtin_amdgcn_sched_barrier(0);
     step_seq<ND, NS, I + 1>(st);
   } else if constexpr (I / SP < NL) {
     // more loads than MFMA slots: issue the rest
@@ -979,6 +988,7 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
   uint32_t* sD = (uint32_t*)(smem + Lds<L>::kD);
   float* sG = (float*)(smem + Lds<L>::kG);
   float* sW = (float*)(smem + Lds<L>::kW);
+  float* sPhi = (float*)(smem + Lds<L>::kPhi);
   uint16_t* abase = (uint16_t*)(smem + Lds<L>::kA);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -1043,7 +1053,7 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
       load_b<L, p0.M, p0.LO, p0.ND>(wrs, boff, 0, ring[0]);
     }
 
-    // ---- phase A: per-edge setup
+    // ---- phase A1: per-edge metadata, radial basis and softmax weights
     if (tid <= kSlots) S.rp[tid] = P.row_ptr[min(t_first + tid, t_end)];
     __syncthreads();
     if (tid < kSlots) {
@@ -1052,90 +1062,120 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
       const int t = t_first + ((tid - t_first % kSlots + kSlots) % kSlots);
       S.flush_t[tid] = (t <= t_first + sl && S.rp[t - t_first + 1] <= e_stop) ? t : -1;
     }
-    if (tid < kM) {
-      // wave 0: one edge per lane: metadata, frame and the Wigner-D pairs
-      const int r = tid;
-      uint32_t* dr = sD + r * Cfg<L>::DPW;
+    {
+      // 8 lanes per edge row: lane hs of row r computes the row's geometry,
+      // the radial basis functions hs, hs + 8, ... and the softmax weights
+      // of heads hs, hs + 8; lane 0 of the row stores the row metadata
+      const int r = tid >> 3, hs = tid & 7;
+      int jr = -1;  // source atom of row r
       if (r < nrows) {
         int t, j;
         float rv[3];
         row_edge(P, S, e + r, t_first, t, j, rv);
+        jr = j;
         const float rho = sqrtf(rv[0] * rv[0] + rv[1] * rv[1] + rv[2] * rv[2]);
-        S.row_j[r] = j;
-        S.row_slot[r] = t % kSlots;
-        const float inv = rho > 0.0f ? 1.0f / rho : 0.0f;
+        if (hs == 0) {
+          S.row_j[r] = j;
+          S.row_slot[r] = t % kSlots;
+          S.row_t[r] = t;
+          S.row_rv[r] = f32x4{rv[0], rv[1], rv[2], rho};
+        }
+        // Gaussian radial basis of this edge (centres k rc/(K-1), width rc/(K-1))
+        const float step = rc / (float)(P.K - 1);
+        const float inv2s2 = 1.0f / (2.0f * step * step);
+        for (int kk = hs; kk < ((P.K + 7) & ~7); kk += 8) {
+          const float dr = rho - step * (float)kk;
+          sPhi[r * kMaxRbf + kk] = kk < P.K ? expf(-dr * dr * inv2s2) : 0.0f;
+        }
+        const float u = envelope_u(rho / rc, P.p);
+        for (int h = hs; h < H; h += 8) {
+          const f32x4* qv = (const f32x4*)(P.q + (int64_t)t * kC + h * dh);
+          const f32x4* kv = (const f32x4*)(P.k + (int64_t)j * kC + h * dh);
+          float z = 0.0f;
+          for (int cc = 0; cc < dh / 4; ++cc) {
+            const f32x4 qa = qv[cc], kb = kv[cc];
+            z += qa.x * kb.x + qa.y * kb.y + qa.z * kb.z + qa.w * kb.w;
+          }
+          z *= inv_sqrt_d;
+          sW[r * kMaxHeads + h] = u * expf(z - P.stat_max[(int64_t)t * H + h]) * P.stat_inv[(int64_t)t * H + h];
+        }
+      } else {
+        if (hs == 0) {
+          S.row_j[r] = -1;
+          S.row_slot[r] = -2;  // matches no slot
+          S.row_t[r] = t_first;
+          S.row_rv[r] = f32x4{0.0f, 0.0f, 1.0f, 0.0f};
+        }
+        for (int kk = hs; kk < ((P.K + 7) & ~7); kk += 8) sPhi[r * kMaxRbf + kk] = 0.0f;
+        for (int h = hs; h < H; h += 8) sW[r * kMaxHeads + h] = 0.0f;
+      }
+      // the generator row of this lane is r (kGR = 1)
+      static_assert(kGR == 1 && kGStride == kM, "one generator row per lane, the phase A1 row");
+      c.xoff[0] = jr >= 0 ? ((uint32_t)jr * Cfg<L>::NP * kC + 4 * c.c8) * 4u : P.xp_bytes;
+    }
+    __syncthreads();
+
+    // gathers of the first A chunk's generator units 0 and 1, which land
+    // during phase A2
+    u32x4 xa[kGR * kMaxPairs], xb[kGR * kMaxPairs];
+    gen_issue(xrs, c, P.xp_bytes, p0.M, 0, xa);
+    gen_issue(xrs, c, P.xp_bytes, p0.M, 1, xb);
+
+    // ---- phase A2: wave 0 the Wigner-D pairs of its edge row; waves 1..7
+    // the radial gates: lane (channel quad cq, row phase rg) owns rows rg,
+    // rg + NRG, ...; the w_rad columns of its 4 channels stream through
+    // registers 8 basis functions at a time and meet every owned row
+    if (tid < kM) {
+      const int r = tid;
+      uint32_t* dr = sD + r * Cfg<L>::DPW;
+      if (r < nrows) {
+        const f32x4 v = S.row_rv[r];
+        const float inv = v.w > 0.0f ? 1.0f / v.w : 0.0f;
         float R[9];
-        edge_frame(rv[0] * inv, rv[1] * inv, rv[2] * inv, R);
+        edge_frame(v.x * inv, v.y * inv, v.z * inv, R);
         wigner_pairs<L>(R, dr);
       } else {
-        S.row_j[r] = -1;
-        S.row_slot[r] = -2;  // matches no slot
         for (int q = 0; q < Cfg<L>::DPW; ++q) dr[q] = 0u;
       }
     } else {
-      // waves 1..3: radial gates (64 rows x 8 groups of 16 channels), then
-      // the softmax weights (64 rows x kMaxHeads)
-      for (int it = tid - kM; it < kM * (kC / 16) + kM * kMaxHeads; it += kThreads - kM) {
-        if (it < kM * (kC / 16)) {
-          const int r = it / (kC / 16), c0 = 16 * (it % (kC / 16));
-          float gv[16];
+      const int tw = tid - kM;  // 0 .. kThreads - kM - 1
+      constexpr int NRG = (kThreads - kM) / (kC / 4);
+      constexpr int kGRows = (kM + NRG - 1) / NRG;
+      const int cq = tw % (kC / 4), rg = tw / (kC / 4);
+      if (rg < NRG) {
+        f32x4 g[kGRows];
 #pragma unroll
-          for (int q = 0; q < 16; ++q) gv[q] = 0.0f;
-          if (r < nrows) {
-            if (P.flags & SO2_FLAG_NO_RADIAL) {
+        for (int i = 0; i < kGRows; ++i) g[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (!(P.flags & SO2_FLAG_NO_RADIAL)) {
+          for (int k0 = 0; k0 < P.K; k0 += 8) {
+            f32x4 w4[8];
 #pragma unroll
-              for (int q = 0; q < 16; ++q) gv[q] = 1.0f;
-            } else {
-              int t, j;
-              float rv[3];
-              row_edge(P, S, e + r, t_first, t, j, rv);
-              const float rho = sqrtf(rv[0] * rv[0] + rv[1] * rv[1] + rv[2] * rv[2]);
-              const float step = rc / (float)(P.K - 1);
-              const float inv2s2 = 1.0f / (2.0f * step * step);
-              for (int kk = 0; kk < P.K; ++kk) {
-                const float dr = rho - step * (float)kk;
-                const float phi = expf(-dr * dr * inv2s2);
-                const f32x4* wr = (const f32x4*)(P.wrad + (int64_t)kk * kC + c0);
+            for (int kk = 0; kk < 8; ++kk)
+              w4[kk] = k0 + kk < P.K ? *(const f32x4*)(P.wrad + (int64_t)(k0 + kk) * kC + 4 * cq)
+                                     : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                  const f32x4 w4 = wr[v];
-                  gv[4 * v + 0] += phi * w4.x;
-                  gv[4 * v + 1] += phi * w4.y;
-                  gv[4 * v + 2] += phi * w4.z;
-                  gv[4 * v + 3] += phi * w4.w;
-                }
-              }
-              if (P.flags & SO2_FLAG_RBF_ENVELOPE) {
-                const float u = envelope_u(rho / rc, P.p);
-#pragma unroll
-                for (int q = 0; q < 16; ++q) gv[q] *= u;
+            for (int i = 0; i < kGRows; ++i) {
+              const int r = rg + NRG * i;
+              if (r < kM) {
+                const f32x4 f0 = *(const f32x4*)(sPhi + r * kMaxRbf + k0);
+                const f32x4 f1 = *(const f32x4*)(sPhi + r * kMaxRbf + k0 + 4);
+                g[i] += f0.x * w4[0] + f0.y * w4[1] + f0.z * w4[2] + f0.w * w4[3] +
+                        f1.x * w4[4] + f1.y * w4[5] + f1.z * w4[6] + f1.w * w4[7];
               }
             }
           }
+        }
+        const bool env = (P.flags & SO2_FLAG_RBF_ENVELOPE) != 0;
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            *(f32x4*)(sG + g_off(r, c0 / 4 + v)) = f32x4{gv[4 * v], gv[4 * v + 1], gv[4 * v + 2], gv[4 * v + 3]};
-        } else {
-          const int pr = it - kM * (kC / 16);
-          const int r = pr / kMaxHeads, h = pr % kMaxHeads;
-          float wv = 0.0f;
-          if (r < nrows && h < H) {
-            int t, j;
-            float rv[3];
-            row_edge(P, S, e + r, t_first, t, j, rv);
-            const float rho = sqrtf(rv[0] * rv[0] + rv[1] * rv[1] + rv[2] * rv[2]);
-            const float u = envelope_u(rho / rc, P.p);
-            const f32x4* qv = (const f32x4*)(P.q + (int64_t)t * kC + h * dh);
-            const f32x4* kv = (const f32x4*)(P.k + (int64_t)j * kC + h * dh);
-            float z = 0.0f;
-            for (int cc = 0; cc < dh / 4; ++cc) {
-              const f32x4 a = qv[cc], bb = kv[cc];
-              z += a.x * bb.x + a.y * bb.y + a.z * bb.z + a.w * bb.w;
-            }
-            z *= inv_sqrt_d;
-            wv = u * expf(z - P.stat_max[(int64_t)t * H + h]) * P.stat_inv[(int64_t)t * H + h];
+        for (int i = 0; i < kGRows; ++i) {
+          const int r = rg + NRG * i;
+          if (r < kM) {
+            f32x4 gi = g[i];
+            if (r >= nrows) gi = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            else if (P.flags & SO2_FLAG_NO_RADIAL) gi = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+            else if (env) gi = gi * envelope_u(S.row_rv[r].w / rc, P.p);
+            *(f32x4*)(sG + g_off(r, cq)) = gi;
           }
-          sW[r * kMaxHeads + h] = wv;
         }
       }
     }
@@ -1143,16 +1183,8 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
 
     // ---- first A chunk (block p0.M, degree p0.M): all four generator units
     {
-#pragma unroll
-      for (int u = 0; u < kGR; ++u) {
-        const int j = S.row_j[c.r0 + kGStride * u];
-        c.xoff[u] = j >= 0 ? ((uint32_t)j * Cfg<L>::NP * kC + 4 * c.c8) * 4u : P.xp_bytes;
-      }
       uint32_t dp[kGR][kMaxPairs], dm[kGR][kMaxPairs];
       gen_dpairs(sD, Cfg<L>::DPW, c, p0.M, p0.M, dp, dm);
-      u32x4 xa[kGR * kMaxPairs], xb[kGR * kMaxPairs];
-      gen_issue(xrs, c, P.xp_bytes, p0.M, 0, xa);
-      gen_issue(xrs, c, P.xp_bytes, p0.M, 1, xb);
       gen_finish<NS0>(sG, c, 0, xa, dp, dm, abase);  // chunks_before(L, 0) = 0
       gen_issue(xrs, c, P.xp_bytes, p0.M, 2, xa);
       gen_finish<NS0>(sG, c, 1, xb, dp, dm, abase);
@@ -1253,11 +1285,11 @@ so2_status launch_pack_L(const AttnArgs& a, const MfmaParams& P, hipStream_t str
 
 }  // namespace
 
-bool mfma_supported(int L, int C, int H, int n_atoms) {
+bool mfma_supported(int L, int C, int H, int K, int n_atoms) {
   // the x pairs are addressed through a 32-bit buffer descriptor, with room
   // past the end for the zero reads of rows without an edge
   const uint64_t xp_bytes = (uint64_t)n_atoms * pair_off(L + 1) * C * 4;
-  return C == kC && L >= 1 && L <= 4 && H >= 1 && H <= kMaxHeads && C % H == 0 &&
+  return C == kC && L >= 1 && L <= 4 && H >= 1 && H <= kMaxHeads && C % H == 0 && K <= kMaxRbf &&
          xp_bytes < 0xffff0000ull;
 }
 

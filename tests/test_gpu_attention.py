@@ -232,6 +232,20 @@ def test_mfma_every_degree(L):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("L,K", [(1, 8), (2, 8), (2, 12), (2, 24), (3, 8), (3, 20)])
+def test_mfma_degree_and_rbf_counts(L, K):
+    """Degrees below 4 leave some of the five component-pair slots of a lane
+    unused and basis counts other than 16 change the gate and rotation data
+    next to the Wigner-D rows: every output must stay finite and match."""
+    say("mfma L", L, "n_rbf", K)
+    w = make_workload("tiny_fp32", l_max=L, channels=128, heads=8, n_rbf=K, dtype="bf16")
+    y, y_ref = _run_pair(w)
+    assert np.isfinite(y).all()
+    err = max_rel_error(y, y_ref)
+    say("max rel err", err)
+    assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("heads", [1, 4, 16])
 def test_mfma_head_counts(heads):
     say("mfma heads", heads)
