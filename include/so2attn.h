@@ -59,7 +59,7 @@ typedef struct ihipStream_t* so2_stream_t; /* same object as hipStream_t */
 typedef enum {
   SO2_OK = 0,
   SO2_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, non-finite position */
-  SO2_ERR_UNSUPPORTED = 2,      /* legal shape with no kernel (e.g. L > 6)     */
+  SO2_ERR_UNSUPPORTED = 2,      /* legal shape with no kernel (e.g. C > 256)   */
   SO2_ERR_CAPACITY = 3,         /* col[] too small; *n_edges_host = required E */
   SO2_ERR_BOX = 4,              /* a box side <= 2 * cutoff                    */
   SO2_ERR_DEVICE = 5,           /* a HIP call failed                            */
@@ -150,8 +150,10 @@ int32_t so2_attention_kernel_kind(const so2_attn_desc* desc);
  *   w_q, w_k  [C][C], w_rad [K][C], w_so2 [so2_weight_count]   dtype
  *   y         [n_targets][(L+1)^2][C] fp32, written
  *   workspace >= so2_attention_workspace_bytes(desc) bytes
- * Errors: INVALID_ARGUMENT, UNSUPPORTED (fp32 needs C <= 256; bf16 needs
- * C in {64, 128} and L <= 6), BOX, WORKSPACE, DEVICE.  Asynchronous on
+ * Kernels: bf16 with C = 128, 1 <= L <= 4, H <= 16, K <= 32 runs on the
+ * MFMA kernel; every other shape (fp32 or bf16) on the VALU kernel.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (L > 6 or C > 256: no kernel), BOX,
+ * WORKSPACE, DEVICE.  Asynchronous on
  * `stream`.  Device memory beyond the caller's buffers: none; activation
  * memory is O(n_atoms) (workspace), never O(E). */
 so2_status so2_attention_fwd(const so2_attn_desc* desc, const float* pos,
