@@ -108,11 +108,24 @@ __host__ __device__ constexpr int64_t w1_offset(int L, int m) {
   for (int mu = 1; mu < m; ++mu) off += 2 * (int64_t)(L + 1 - mu) * kC * (L + 1 - mu) * kC;
   return off;
 }
+// The fragment-ordered weights hold, after W0 and (W1_m, W2_m), a copy of
+// every -W2_m (m = 1..L), so that the complex product needs no sign flips
+// in the main loop.  wneg_offset(L, m): first entry of -W2_m;
+// wneg_offset(L, L + 1): entries in all.
+__host__ __device__ constexpr int64_t wneg_offset(int L, int m) {
+  int64_t off = w1_offset(L, L + 1);
+  for (int mu = 1; mu < m; ++mu) off += (int64_t)(L + 1 - mu) * kC * (L + 1 - mu) * kC;
+  return off;
+}
+// B matrices of block m: W0 (m = 0), or W1_m, W2_m and -W2_m.
+__host__ __device__ constexpr int n_bmat(int m) { return m ? 3 : 1; }
 
 struct MfmaParams {
   const float* pos;
   const int32_t* row_ptr;
   const int32_t* col;
+  const int32_t* gs;      // first target of every group, gs[n_groups] = n_targets
+  const int32_t* order;   // groups of each XCD's range, most chunks first
   const uint32_t* xp;     // x repacked as component pairs [n_atoms][pair_off(L+1)][C]
   const float* wrad;      // w_rad in fp32 [K][C]
   const uint16_t* wf;     // w_so2 in MFMA fragment order
@@ -145,6 +158,15 @@ __device__ inline f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ inline float dot2(unsigned int a, unsigned int b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
                                          false);
+}
+
+// a.lo * b.lo + a.hi * b.hi in one instruction: the three-operand encoding
+// with the constant 0 as accumulator (the builtin with c = 0 becomes a move
+// of 0 plus the two-operand accumulating form).
+__device__ inline float dot2_0(unsigned int a, unsigned int b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 // Raw buffer descriptor (gfx9 family: dword3 = 0x00020000).  Loads through
@@ -188,7 +210,7 @@ __global__ void __launch_bounds__(256) attn_pack_kernel(const uint16_t* __restri
   constexpr int NP = pair_off(L + 1);
   const int64_t n_x = (int64_t)n_atoms * NP * (kC / 4);
   const int64_t n_w = (int64_t)n_rbf * kC;
-  const int64_t n_f = w1_offset(L, L + 1) / 8;
+  const int64_t n_f = wneg_offset(L, L + 1) / 8;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_x + n_w + n_f; i += stride) {
     if (i < n_x) {
@@ -214,12 +236,28 @@ __global__ void __launch_bounds__(256) attn_pack_kernel(const uint16_t* __restri
       wrad[w] = bf16_to_float(w_rad[w]);
     } else {
       const int64_t g = 8 * (i - n_x - n_w);  // first element of this lane's 16 bytes in wf
-      int64_t base = 0;
-      int mi = 0, KM = (L + 1) * kC;
-      while (g >= base + (int64_t)KM * KM) {
-        base += (int64_t)KM * KM;
-        ++mi;
-        KM = (L + 1 - (mi + 1) / 2) * kC;
+      int64_t base = 0, src = 0;  // first entry of the matrix in wf and in w_so2
+      uint32_t neg = 0;
+      int KM = (L + 1) * kC;
+      if (g < w1_offset(L, L + 1)) {
+        int mi = 0;
+        while (g >= base + (int64_t)KM * KM) {
+          base += (int64_t)KM * KM;
+          ++mi;
+          KM = (L + 1 - (mi + 1) / 2) * kC;
+        }
+        src = base;
+      } else {
+        int m = 1;
+        KM = L * kC;
+        base = wneg_offset(L, 1);
+        while (g >= base + (int64_t)KM * KM) {
+          base += (int64_t)KM * KM;
+          ++m;
+          KM = (L + 1 - m) * kC;
+        }
+        src = w1_offset(L, m) + (int64_t)KM * KM;  // W2_m
+        neg = 0x80008000u;
       }
       const int64_t lg = (g - base) / 8;
       const int lane = (int)(lg % 64);
@@ -227,7 +265,7 @@ __global__ void __launch_bounds__(256) attn_pack_kernel(const uint16_t* __restri
       const int ks = (int)(f % (KM / 32));
       const int64_t row = 16 * (f / (KM / 32)) + (lane & 15);
       const int col = 32 * ks + 8 * (lane >> 4);
-      *(u32x4*)(wf + g) = *(const u32x4*)(w_so2 + base + row * KM + col);
+      *(u32x4*)(wf + g) = *(const u32x4*)(w_so2 + src + row * KM + col) ^ u32x4{neg, neg, neg, neg};
     }
   }
 }
@@ -497,20 +535,23 @@ __device__ inline void gen_finish(const float* sG, const Ctx& c, int k, const u3
 // (row tile, K step) of the fragment-ordered weights.  The lane and tile
 // part of the address is fixed for the pass; the step part (1 KB per step)
 // is the scalar offset.
-template <int L, int M, int LO, int ND>
-__device__ inline void load_b(__amdgpu_buffer_rsrc_t wrs, const uint32_t (&boff)[ND][kNT], int step,
-                              u32x4 (&b)[ND][M ? 2 : 1][kNT]) {
+template <int L, int M>
+__device__ constexpr uint32_t bmat_byte(int s) {
   constexpr int KM = (L + 1 - M) * kC;
   constexpr uint32_t w1_byte = (uint32_t)(M == 0 ? 0 : w1_offset(L, M)) * 2u;
-  constexpr uint32_t w2_byte = w1_byte + (uint32_t)(KM * KM) * 2u;
+  return s == 0 ? w1_byte : s == 1 ? w1_byte + (uint32_t)(KM * KM) * 2u : (uint32_t)wneg_offset(L, M) * 2u;
+}
+
+template <int L, int M, int LO, int ND>
+__device__ inline void load_b(__amdgpu_buffer_rsrc_t wrs, const uint32_t (&boff)[ND][kNT], int step,
+                              u32x4 (&b)[ND][n_bmat(M)][kNT]) {
   const uint32_t sb = 1024u * (uint32_t)step;
 #pragma unroll
   for (int di = 0; di < ND; ++di)
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-      b[di][0][nt] = buffer_load16(wrs, boff[di][nt], w1_byte + sb);
-      if constexpr (M > 0) b[di][1][nt] = buffer_load16(wrs, boff[di][nt], w2_byte + sb);
-    }
+    for (int sm = 0; sm < n_bmat(M); ++sm)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) b[di][sm][nt] = buffer_load16(wrs, boff[di][nt], bmat_byte<L, M>(sm) + sb);
 }
 
 template <int L, int M, int LO, int ND>
@@ -535,8 +576,7 @@ template <int ND, int NS>
 struct StepState {
   const u32x4* ap;                      // [kRT] + plane fragments
   const u32x4* am;                      // [kRT] - plane fragments
-  const u32x4 (&b)[ND][NS][kNT];
-  const u32x4 (&nb2)[ND][kNT];
+  const u32x4 (&b)[ND][NS == 2 ? 3 : 1][kNT];  // W0, or W1, W2, -W2
   f32x4 (&acc)[ND][NS][kNT][kRT];
   const u32x4 (&xr)[kGR * kMaxPairs];
   const uint32_t (&dp)[kGR][kMaxPairs];
@@ -544,10 +584,10 @@ struct StepState {
   float (&vp)[kGR][4];
   float (&vm)[kGR][4];
   // loads for the next K step, spread over the MFMAs of this one
-  u32x4 (&bn)[ND][NS][kNT];             // B fragments of the next step
+  u32x4 (&bn)[ND][NS == 2 ? 3 : 1][kNT];  // B fragments of the next step
   __amdgpu_buffer_rsrc_t wrs;
   const uint32_t (&boff)[ND][kNT];
-  uint32_t wsoff[2];                    // scalar offsets of the next step's W0/W1 and W2 blocks
+  uint32_t wsoff[3];                    // scalar offsets of the next step's W0 / W1, W2, -W2 blocks
   u32x4 (&xn)[kGR * kMaxPairs];         // gathers of the next generator unit
   __amdgpu_buffer_rsrc_t xrs;
   uint32_t xoff[kGR];                   // per row; past the end for pairs beyond the unit's degree
@@ -559,9 +599,10 @@ struct StepState {
 // Load j of the next-step loads: first the B fragments, then the gathers.
 template <int ND, int NS, int J>
 __device__ __attribute__((always_inline)) inline void step_load(StepState<ND, NS>& st) {
-  constexpr int NB = ND * NS * kNT;
+  constexpr int NBM = NS == 2 ? 3 : 1;
+  constexpr int NB = ND * NBM * kNT;
   if constexpr (J < NB) {
-    constexpr int di = J / (NS * kNT), sm = (J / kNT) % NS, nt = J % kNT;
+    constexpr int di = J / (NBM * kNT), sm = (J / kNT) % NBM, nt = J % kNT;
     st.bn[di][sm][nt] = buffer_load16(st.wrs, st.boff[di][nt], st.wsoff[sm]);
   } else {
     constexpr int g = J - NB, p = g / kGR, u = g % kGR;
@@ -582,7 +623,7 @@ __device__ __attribute__((always_inline)) inline void step_mfma(StepState<ND, NS
     if constexpr (ph == 0)
       st.acc[di][mt][nt][rt] = mfma(as_bf16x8(st.ap[rt]), as_bf16x8(st.b[di][mt][nt]), st.acc[di][mt][nt][rt]);
     else if constexpr (mt == 0)
-      st.acc[di][0][nt][rt] = mfma(as_bf16x8(st.am[rt]), as_bf16x8(st.nb2[di][nt]), st.acc[di][0][nt][rt]);
+      st.acc[di][0][nt][rt] = mfma(as_bf16x8(st.am[rt]), as_bf16x8(st.b[di][2][nt]), st.acc[di][0][nt][rt]);
     else
       st.acc[di][1][nt][rt] = mfma(as_bf16x8(st.am[rt]), as_bf16x8(st.b[di][0][nt]), st.acc[di][1][nt][rt]);
   }
@@ -595,7 +636,10 @@ __device__ __attribute__((always_inline)) inline void step_dots(StepState<ND, NS
     constexpr int u = r / (4 * NS), q = (r / NS) % 4, sg = r % NS;
     const u32x4 v = st.xr[kGR * p + u];
     const uint32_t xv = q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
-    if constexpr (sg == 0) st.vp[u][q] = dot2(st.dp[u][p], xv, st.vp[u][q]);
+    // pair 0 starts the sum: its accumulator input is the constant 0
+    if constexpr (p == 0 && sg == 0) st.vp[u][q] = dot2_0(st.dp[u][p], xv);
+    else if constexpr (p == 0) st.vm[u][q] = dot2_0(st.dm[u][p], xv);
+    else if constexpr (sg == 0) st.vp[u][q] = dot2(st.dp[u][p], xv, st.vp[u][q]);
     else st.vm[u][q] = dot2(st.dm[u][p], xv, st.vm[u][q]);
     step_dots<ND, NS, D0 + 1, D1>(st);
   }
@@ -605,7 +649,7 @@ template <int ND, int NS, int I>
 __device__ __attribute__((always_inline)) inline void step_seq(StepState<ND, NS>& st) {
   constexpr int F = ND * kNT * NS * NS * kRT;
   constexpr int D = kMaxPairs * kGR * 4 * NS;
-  constexpr int NL = ND * NS * kNT + kGR * kMaxPairs;  // loads of the next step
+  constexpr int NL = ND * (NS == 2 ? 3 : 1) * kNT + kGR * kMaxPairs;  // loads of the next step
   constexpr int SP = (2 * F / 3) / NL > 0 ? (2 * F / 3) / NL : 1;
   if constexpr (I < F) {
     step_mfma<ND, NS, I>(st);
@@ -625,17 +669,14 @@ __device__ __attribute__((always_inline)) inline void step_seq(StepState<ND, NS>
 // its B fragments (step nstep) into bn and the gathers of the next
 // generator unit (slice nk of a chunk of degree nglp) into xn.
 template <int L, int M, int LO, int ND>
-__device__ inline void fused_step(const uint16_t* abuf, int k, const u32x4 (&b)[ND][M ? 2 : 1][kNT],
+__device__ inline void fused_step(const uint16_t* abuf, int k, const u32x4 (&b)[ND][n_bmat(M)][kNT],
                                   f32x4 (&acc)[ND][M ? 2 : 1][kNT][kRT], const float* sG, const Ctx& c,
                                   const u32x4 (&xr)[kGR * kMaxPairs], const uint32_t (&dp)[kGR][kMaxPairs],
                                   const uint32_t (&dm)[kGR][kMaxPairs], uint16_t* anext,
-                                  u32x4 (&bn)[ND][M ? 2 : 1][kNT], __amdgpu_buffer_rsrc_t wrs,
+                                  u32x4 (&bn)[ND][n_bmat(M)][kNT], __amdgpu_buffer_rsrc_t wrs,
                                   const uint32_t (&boff)[ND][kNT], int nstep, u32x4 (&xn)[kGR * kMaxPairs],
                                   __amdgpu_buffer_rsrc_t xrs, int nglp, int nk, uint32_t oob) {
   constexpr int NS = M ? 2 : 1;
-  constexpr int KM = (L + 1 - M) * kC;
-  constexpr uint32_t w1_byte = (uint32_t)(M == 0 ? 0 : w1_offset(L, M)) * 2u;
-  constexpr uint32_t w2_byte = w1_byte + (uint32_t)(KM * KM) * 2u;
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15;
   const int grp = 4 * k + (lane >> 4);
@@ -646,24 +687,18 @@ __device__ inline void fused_step(const uint16_t* abuf, int k, const u32x4 (&b)[
     ap[rt] = *(const u32x4*)(abuf + o);
     if constexpr (NS > 1) am[rt] = *(const u32x4*)(abuf + kAplane + o);
   }
-  u32x4 nb2[ND][kNT];
+  float vp[kGR][4], vm[kGR][4];  // every entry is first written by its pair-0 dot product
+  // gates of the unit's rows and channels, read before the MFMAs so that the
+  // LDS latency is hidden behind them
+  f32x4 gate[kGR];
 #pragma unroll
-  for (int di = 0; di < ND; ++di)
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
-      nb2[di][nt] = NS > 1 ? b[di][NS - 1][nt] ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}
-                           : b[di][0][nt];
-  float vp[kGR][4], vm[kGR][4];
-#pragma unroll
-  for (int u = 0; u < kGR; ++u)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) vp[u][q] = vm[u][q] = 0.0f;
+  for (int u = 0; u < kGR; ++u) gate[u] = *(const f32x4*)(sG + g_off(c.r0 + kGStride * u, 8 * k + c.c8));
   const uint32_t sb = 1024u * (uint32_t)nstep;
   uint32_t xo[kGR];
 #pragma unroll
   for (int u = 0; u < kGR; ++u) xo[u] = c.xoff[u];
-  StepState<ND, NS> st{ap, am, b, nb2, acc, xr, dp, dm, vp, vm,
-                       bn, wrs, boff, {w1_byte + sb, w2_byte + sb},
+  StepState<ND, NS> st{ap, am, b, acc, xr, dp, dm, vp, vm,
+                       bn, wrs, boff, {bmat_byte<L, M>(0) + sb, bmat_byte<L, M>(1) + sb, bmat_byte<L, M>(2) + sb},
                        xn, xrs, {}, (uint32_t)(pair_off(nglp) * kC + 32 * nk) * 4u, nglp, oob};
 #pragma unroll
   for (int u = 0; u < kGR; ++u) st.xoff[u] = xo[u];
@@ -671,7 +706,7 @@ __device__ inline void fused_step(const uint16_t* abuf, int k, const u32x4 (&b)[
 #pragma unroll
   for (int u = 0; u < kGR; ++u) {
     const int r = c.r0 + kGStride * u;
-    const f32x4 g = *(const f32x4*)(sG + g_off(r, 8 * k + c.c8));
+    const f32x4 g = gate[u];
     const int ao = a_off(r, 4 * k + (c.c8 >> 1)) + 4 * (c.c8 & 1);
     typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
     *(u32x2*)(anext + ao) = u32x2{pack_bf16x2(vp[u][0] * g.x, vp[u][1] * g.y), pack_bf16x2(vp[u][2] * g.z, vp[u][3] * g.w)};
@@ -840,7 +875,7 @@ template <int L, int PI>
 __device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams& P, char* smem, const Ctx& c,
                                                                f32x4 (&T)[Cfg<L>::TT][kNT],
                                                                u32x4 (&ring)[2][pass_info(L, PI).ND]
-                                                                            [pass_info(L, PI).M ? 2 : 1][kNT],
+                                                                            [n_bmat(pass_info(L, PI).M)][kNT],
                                                                u32x4 (&xa)[kGR * kMaxPairs], u32x4 (&xb)[kGR * kMaxPairs]) {
   constexpr PassInfo pi = pass_info(L, PI), pn = pass_info(L, PI + 1);
   constexpr int M = pi.M, LO = pi.LO, ND = pi.ND, NS = M ? 2 : 1;
@@ -899,8 +934,8 @@ __device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams&
   }
 
   if constexpr (pn.M >= 0) {
-    constexpr int NDn = pn.ND, NSn = pn.M ? 2 : 1;
-    u32x4 nring[2][NDn][NSn][kNT];
+    constexpr int NDn = pn.ND;
+    u32x4 nring[2][NDn][n_bmat(pn.M)][kNT];
     uint32_t nboff[NDn][kNT];
     b_offsets<L, pn.M, pn.LO, NDn>(nboff);
     load_b<L, pn.M, pn.LO, NDn>(wrs, nboff, 0, nring[0]);
@@ -965,19 +1000,89 @@ __device__ inline void flush_slots(const MfmaParams& P, const Smem& S, int t_fir
 
 // First target of group g: the smallest t with row_ptr[t] - row_ptr[0] >=
 // g E / n_groups (E = edges of all targets); group n_groups starts at
-// n_targets.  Binary search, uniform across the workgroup.
-__device__ inline int group_start(const MfmaParams& P, int g, int n_groups) {
-  if (g >= n_groups) return P.n_targets;
-  const int e0 = P.row_ptr[0];
-  const int64_t E = (int64_t)P.row_ptr[P.n_targets] - e0;
+// n_targets.  Binary search.
+__device__ inline int group_start(const int32_t* row_ptr, int n_targets, int g, int n_groups) {
+  if (g >= n_groups) return n_targets;
+  const int e0 = row_ptr[0];
+  const int64_t E = (int64_t)row_ptr[n_targets] - e0;
   const int64_t goal = e0 + (E * g) / n_groups;
-  int lo = 0, hi = P.n_targets;  // answer in [lo, hi]
+  int lo = 0, hi = n_targets;  // answer in [lo, hi]
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
-    if ((int64_t)P.row_ptr[mid] >= goal) hi = mid;
+    if ((int64_t)row_ptr[mid] >= goal) hi = mid;
     else lo = mid + 1;
   }
   return lo;
+}
+
+// Groups of XCD x: the contiguous range [xcd_first(x), xcd_first(x + 1)).
+__host__ __device__ inline int xcd_first(int x, int n_groups) {
+  const int per = n_groups / 8, rem = n_groups % 8;
+  return x * per + (x < rem ? x : rem);
+}
+
+// Schedule of the fused kernel, one block per XCD range of groups: the
+// group starts, then the range's groups ordered by their number of edge
+// chunks, most first (stable), so that the hardware, which hands the
+// workgroups of an XCD to its compute units in launch order, starts the
+// long groups first and the makespan stays close to the mean.  The chunk
+// count repeats the fused kernel's chunking: at most kM edges and kSlots
+// consecutive targets per chunk.
+constexpr int kOrderBuckets = 32;  // chunk counts above 31 share the top bucket
+__global__ void __launch_bounds__(256) attn_order_kernel(const int32_t* __restrict__ row_ptr, int n_targets,
+                                                         int n_groups, int32_t* __restrict__ gs,
+                                                         int32_t* __restrict__ bucket,
+                                                         int32_t* __restrict__ order) {
+  __shared__ int hist[kOrderBuckets][257];  // [bucket][thread]: counts, then scatter positions
+  __shared__ int base[kOrderBuckets];       // first position of every bucket
+  const int t = threadIdx.x;
+  const int r0 = xcd_first(blockIdx.x, n_groups), r1 = xcd_first(blockIdx.x + 1, n_groups);
+  // thread t owns the contiguous groups [a, b) of the range
+  const int n = r1 - r0;
+  const int a = r0 + (int)(((int64_t)n * t) / 256), b = r0 + (int)(((int64_t)n * (t + 1)) / 256);
+  for (int k = 0; k < kOrderBuckets; ++k) hist[k][t] = 0;
+  for (int g = a; g < b; ++g) {
+    const int t_begin = group_start(row_ptr, n_targets, g, n_groups);
+    const int t_end = group_start(row_ptr, n_targets, g + 1, n_groups);
+    gs[g] = t_begin;
+    if (g + 1 == n_groups) gs[n_groups] = n_targets;
+    const int e_end = row_ptr[t_end];
+    int e = row_ptr[t_begin], tc = t_begin, chunks = 0;
+    while (e < e_end) {
+      while (row_ptr[tc + 1] <= e) ++tc;
+      const int t_lim = min(tc + kSlots, t_end);
+      e = min(min(e + kM, e_end), row_ptr[t_lim]);
+      ++chunks;
+    }
+    const int bk = kOrderBuckets - 1 - min(chunks, kOrderBuckets - 1);  // bucket 0: most chunks
+    bucket[g] = bk;
+    ++hist[bk][t];
+  }
+  __syncthreads();
+  // exclusive prefix in (bucket, thread) order
+  if (t < kOrderBuckets) {
+    int sum = 0;
+    for (int u = 0; u < 256; ++u) {
+      const int v = hist[t][u];
+      hist[t][u] = sum;
+      sum += v;
+    }
+    base[t] = sum;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int k = 0; k < kOrderBuckets; ++k) {
+      const int v = base[k];
+      base[k] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  for (int g = a; g < b; ++g) {
+    const int bk = bucket[g];
+    order[r0 + base[bk] + hist[bk][t]++] = g;
+  }
 }
 
 template <int L>
@@ -998,20 +1103,18 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
 
   // Workgroup -> group of consecutive targets holding about E / n_groups
   // edges (group g starts at the first target whose edges start at or after
-  // g E / n_groups), contiguous per XCD: workgroups are dispatched to the 8
-  // XCDs round robin, and neighbouring groups share neighbours in L2.
+  // g E / n_groups).  Workgroups are dispatched to the 8 XCDs round robin;
+  // XCD x takes a contiguous range of groups, since neighbouring groups
+  // share neighbours in L2, in the order attn_order_kernel chose.
   const int b = blockIdx.x;
-  const int per = n_groups / 8, rem = n_groups % 8;
-  const int xcd = b % 8, idx = b / 8;
-  const int grp = xcd * per + min(xcd, rem) + idx;
-  const int t_begin = group_start(P, grp, n_groups);
-  const int t_end = group_start(P, grp + 1, n_groups);
+  const int grp = P.order[xcd_first(b % 8, n_groups) + b / 8];
+  const int t_begin = P.gs[grp];
+  const int t_end = P.gs[grp + 1];
 
-  // targets without neighbours: y = 0
-  for (int a = tid; a < (t_end - t_begin) * NC * kC; a += kThreads) {
-    const int t = t_begin + a / (NC * kC);
-    if (P.row_ptr[t] == P.row_ptr[t + 1]) P.y[(int64_t)t * NC * kC + a % (NC * kC)] = 0.0f;
-  }
+  // targets without neighbours: y = 0, one wave per target
+  for (int t = t_begin + wave; t < t_end; t += kWaves)
+    if (P.row_ptr[t] == P.row_ptr[t + 1])
+      for (int a = tid & 63; a < NC * kC; a += 64) P.y[(int64_t)t * NC * kC + a] = 0.0f;
 
   static_assert(16 * Cfg<L>::TT <= 112, "row table");
   if (tid < 16 * Cfg<L>::TT) S.rowinfo[tid] = row_info(tid, Cfg<L>::TROWS);
@@ -1046,7 +1149,7 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
     const int nrows = e_stop - e;
 
     // B fragments of the first pass's first K step go out before the setup
-    u32x4 ring[2][p0.ND][NS0][kNT];
+    u32x4 ring[2][p0.ND][n_bmat(p0.M)][kNT];
     {
       uint32_t boff[p0.ND][kNT];
       b_offsets<L, p0.M, p0.LO, p0.ND>(boff);
@@ -1209,13 +1312,16 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
 // Workgroups: about kEdgesPerGroup edges each, rounded up to a whole number
 // of waves of workgroups over the device's compute units (one per CU).
 template <int L>
-so2_status launch_L(const MfmaParams& P, int64_t n_edges, hipStream_t stream) {
+so2_status launch_L(const MfmaParams& P, int32_t* bucket, int64_t n_edges, hipStream_t stream) {
   int dev = 0, n_cu = 256;
   SO2_CHECK(hipGetDevice(&dev));
   SO2_CHECK(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
   int64_t want = (n_edges + kEdgesPerGroup - 1) / kEdgesPerGroup;
   want = ((want + n_cu - 1) / n_cu) * n_cu;
   const int n_groups = (int)std::max<int64_t>(1, std::min<int64_t>(want, P.n_targets));
+  hipLaunchKernelGGL(attn_order_kernel, dim3(8), dim3(256), 0, stream, P.row_ptr, P.n_targets, n_groups,
+                     const_cast<int32_t*>(P.gs), bucket, const_cast<int32_t*>(P.order));
+  SO2_CHECK_LAUNCH();
   const size_t smem = Lds<L>::kTotal;
   static_assert(Lds<L>::kTotal <= 160 * 1024, "LDS budget");
   SO2_CHECK(hipFuncSetAttribute((const void*)attn_mfma_kernel<L>,
@@ -1228,7 +1334,7 @@ so2_status launch_L(const MfmaParams& P, int64_t n_edges, hipStream_t stream) {
 // Workspace of the MFMA path: softmax statistics, the x pairs, w_rad in
 // fp32 and w_so2 in fragment order.
 struct ScratchLayout {
-  size_t stats, xp, wrad, wf, total;
+  size_t stats, xp, wrad, wf, gs, bucket, order, total;
 };
 
 size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -1239,7 +1345,11 @@ ScratchLayout scratch_layout(int n_atoms, int n_targets, int L, int H, int K) {
   s.xp = up256(sizeof(float) * 2 * (size_t)n_targets * H);
   s.wrad = s.xp + up256(sizeof(uint32_t) * (size_t)n_atoms * pair_off(L + 1) * kC);
   s.wf = s.wrad + up256(sizeof(float) * (size_t)K * kC);
-  s.total = s.wf + up256(sizeof(uint16_t) * (size_t)w1_offset(L, L + 1));
+  s.gs = s.wf + up256(sizeof(uint16_t) * (size_t)wneg_offset(L, L + 1));
+  // at most n_targets groups
+  s.bucket = s.gs + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
+  s.order = s.bucket + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
+  s.total = s.order + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
   return s;
 }
 
@@ -1253,6 +1363,8 @@ MfmaParams make_params(const AttnArgs& a) {
   P.xp = (const uint32_t*)(base + s.xp);
   P.wrad = (const float*)(base + s.wrad);
   P.wf = (const uint16_t*)(base + s.wf);
+  P.gs = (const int32_t*)(base + s.gs);
+  P.order = (const int32_t*)(base + s.order);
   P.q = a.q;
   P.k = a.k;
   float* stats = (float*)(base + s.stats);
@@ -1260,7 +1372,7 @@ MfmaParams make_params(const AttnArgs& a) {
   P.stat_inv = stats + (size_t)a.n_targets * a.H;
   P.y = a.y;
   P.xp_bytes = (uint32_t)((uint64_t)a.n_atoms * pair_off(a.L + 1) * kC * 4);
-  P.w_bytes = (uint32_t)(w1_offset(a.L, a.L + 1) * 2);
+  P.w_bytes = (uint32_t)(wneg_offset(a.L, a.L + 1) * 2);
   P.n_targets = a.n_targets;
   P.H = a.H;
   P.K = a.K;
@@ -1274,7 +1386,7 @@ MfmaParams make_params(const AttnArgs& a) {
 
 template <int L>
 so2_status launch_pack_L(const AttnArgs& a, const MfmaParams& P, hipStream_t stream) {
-  const int64_t work = (int64_t)a.n_atoms * pair_off(L + 1) * (kC / 4) + (int64_t)a.K * kC + w1_offset(L, L + 1) / 8;
+  const int64_t work = (int64_t)a.n_atoms * pair_off(L + 1) * (kC / 4) + (int64_t)a.K * kC + wneg_offset(L, L + 1) / 8;
   const int64_t blocks = std::min<int64_t>((work + 255) / 256, 8192);
   hipLaunchKernelGGL(attn_pack_kernel<L>, dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const uint16_t*)a.x, const_cast<uint32_t*>(P.xp), a.n_atoms, (const uint16_t*)a.w_rad,
@@ -1329,15 +1441,16 @@ so2_status launch_attention_mfma_prep(const AttnArgs& a, hipStream_t stream) {
 so2_status launch_attention_mfma(const AttnArgs& a, hipStream_t stream) {
   if (a.n_targets == 0) return SO2_OK;
   const MfmaParams P = make_params(a);
+  int32_t* bucket = (int32_t*)((char*)a.scratch + scratch_layout(a.n_atoms, a.n_targets, a.L, a.H, a.K).bucket);
   switch (a.L) {
     case 1:
-      return launch_L<1>(P, a.n_edges, stream);
+      return launch_L<1>(P, bucket, a.n_edges, stream);
     case 2:
-      return launch_L<2>(P, a.n_edges, stream);
+      return launch_L<2>(P, bucket, a.n_edges, stream);
     case 3:
-      return launch_L<3>(P, a.n_edges, stream);
+      return launch_L<3>(P, bucket, a.n_edges, stream);
     case 4:
-      return launch_L<4>(P, a.n_edges, stream);
+      return launch_L<4>(P, bucket, a.n_edges, stream);
   }
   return SO2_ERR_UNSUPPORTED;
 }
