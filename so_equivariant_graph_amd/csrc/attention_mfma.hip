@@ -566,12 +566,10 @@ __device__ inline void b_offsets(uint32_t (&boff)[ND][kNT]) {
       boff[di][nt] = 16u * lane + (uint32_t)(((LO + di - M) * 8 + kNT * wave + nt) * (KM / 32)) * 1024u;
 }
 
-// One K step with its generator unit interleaved.  In source order MFMA i
-// of the step is followed by the generator's dot products [i D / F, (i+1)
-// D / F) (D dot products, F MFMAs) and the loads of the next step are
-// spread over the first two thirds of the MFMAs; the compiler schedules
-// the block from there (with two waves per SIMD a strict order measured
-// slower).  The unit's gate, rounding and LDS store follow the last MFMA.
+// One K step with its generator unit.  The loads of the next step are
+// spread over the first two thirds of the step's F MFMAs; the generator's D
+// dot products follow the last MFMA as one block, then the unit's gate,
+// rounding and LDS store.
 template <int ND, int NS>
 struct StepState {
   const u32x4* ap;                      // [kRT] + plane fragments
@@ -654,7 +652,13 @@ __device__ __attribute__((always_inline)) inline void step_seq(StepState<ND, NS>
   if constexpr (I < F) {
     step_mfma<ND, NS, I>(st);
     if constexpr (I % SP == 0 && I / SP < NL) step_load<ND, NS, I / SP>(st);
-    step_dots<ND, NS, I * D / F, (I + 1) * D / F>(st);
+    if constexpr (I == F - 1) {
+      // the dot products go after the step's last MFMA, as one block: on
+      // gfx950 v_dot2_f32_bf16 does not overlap with MFMAs, and interleaving
+      // the two measured about 10 % slower than issuing them in sequence
+      __builtin_amdgcn_sched_barrier(0);
+      step_dots<ND, NS, 0, D>(st);
+    }
     step_seq<ND, NS, I + 1>(st);
   } else if constexpr (I / SP < NL) {
     // more loads than MFMA slots: issue the rest
