@@ -335,7 +335,8 @@ struct Smem {
 };
 
 // Passes in execution order: blocks m = 1..L, each in groups of at most two
-// output degrees, then m = 0 in groups of at most three.  Every pass
+// output degrees (the limit of the register budget with two sign planes),
+// then m = 0 in one pass over all its L + 1 output degrees.  Every pass
 // generates, during its last A chunk, the first A chunk of the pass after
 // it; ending on m = 0 means a pass never has to produce more sign planes
 // than it has itself (an m >= 1 pass writes both planes, m = 0 reads one).
@@ -347,7 +348,7 @@ __host__ __device__ constexpr PassInfo pass_info(int L, int idx) {
   int i = 0;
   for (int mm = 1; mm <= L + 1; ++mm) {
     const int M = mm == L + 1 ? 0 : mm;
-    const int nd = M == 0 ? 3 : 2;
+    const int nd = M == 0 ? L + 1 : 2;
     for (int lo = M; lo <= L; lo += nd) {
       if (i == idx) return PassInfo{M, lo, (L + 1 - lo) < nd ? (L + 1 - lo) : nd};
       ++i;
