@@ -388,7 +388,7 @@ struct Lds {
   static constexpr size_t kHdr = (sizeof(Smem) + 15) & ~(size_t)15;
   static constexpr size_t kD = kHdr;                                             // u32 [kM][DPW]
   static constexpr size_t kG = (kD + 4 * kM * Cfg<L>::DPW + 15) & ~(size_t)15;  // f32 [kM][kC], swizzled
-  static constexpr size_t kW = kG + sizeof(float) * kM * kC;                     // f32 [kM][kMaxHeads]
+  static constexpr size_t kW = kG + sizeof(float) * kM * kC;                     // f32 [kMaxHeads][kM]
   static constexpr size_t kA = kW + sizeof(float) * kM * kMaxHeads;              // bf16 [2][2][kM][kKC], swizzled
   static constexpr size_t kF = kA + sizeof(uint16_t) * 2 * kAbuf;                // A' fragments u32x4 [][64]
   static constexpr size_t kPhi = kF + sizeof(u32x4) * 64 * max_frags(L);         // f32 [kM][kMaxRbf]
@@ -808,9 +808,9 @@ __device__ inline void rot_back(char* smem, const Ctx& c, const f32x4 (&yt)[NS][
   for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
-      float w4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w4[i] = sW[(16 * rt + 4 * g4 + i) * kMaxHeads + c.head[nt]];
+      // weights of this lane's 4 edge rows for the head of column tile nt
+      const f32x4 wv = *(const f32x4*)(sW + c.head[nt] * kM + 16 * rt + 4 * g4);
+      const float w4[4] = {wv.x, wv.y, wv.z, wv.w};
       if constexpr (!M0) {
         const f32x4 yp = yt[0][nt][rt], ym = yt[NS - 1][nt][rt];
         bq[nt][rt].x = pack_bf16x2(yp[0] * w4[0], yp[1] * w4[1]);
@@ -1209,7 +1209,7 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
             z += qa.x * kb.x + qa.y * kb.y + qa.z * kb.z + qa.w * kb.w;
           }
           z *= inv_sqrt_d;
-          sW[r * kMaxHeads + h] = u * expf(z - P.stat_max[(int64_t)t * H + h]) * P.stat_inv[(int64_t)t * H + h];
+          sW[h * kM + r] = u * expf(z - P.stat_max[(int64_t)t * H + h]) * P.stat_inv[(int64_t)t * H + h];
         }
       } else {
         if (hs == 0) {
@@ -1219,7 +1219,7 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
           S.row_rv[r] = f32x4{0.0f, 0.0f, 1.0f, 0.0f};
         }
         for (int kk = hs; kk < ((P.K + 7) & ~7); kk += 8) sPhi[r * kMaxRbf + kk] = 0.0f;
-        for (int h = hs; h < H; h += 8) sW[r * kMaxHeads + h] = 0.0f;
+        for (int h = hs; h < H; h += 8) sW[h * kM + r] = 0.0f;
       }
       // the generator row of this lane is r (kGR = 1)
       static_assert(kGR == 1 && kGStride == kM, "one generator row per lane, the phase A1 row");
