@@ -118,7 +118,12 @@ __host__ __device__ constexpr int64_t wneg_offset(int L, int m) {
   return off;
 }
 // B matrices of block m: W0 (m = 0), or W1_m, W2_m and -W2_m.
-__host__ __device__ constexpr int n_bmat(int m) { return m ? 3 : 1; }
+constexpr bool kNegCopies = false;  // load -W2 fragments (true) or flip W2's sign bits per step (false)
+__host__ __device__ constexpr int n_bmat(int m) { return m ? (kNegCopies ? 3 : 2) : 1; }
+// entries of the fragment-ordered weights
+__host__ __device__ constexpr int64_t wf_entries(int L) {
+  return kNegCopies ? wneg_offset(L, L + 1) : w1_offset(L, L + 1);
+}
 
 struct MfmaParams {
   const float* pos;
@@ -210,7 +215,7 @@ __global__ void __launch_bounds__(256) attn_pack_kernel(const uint16_t* __restri
   constexpr int NP = pair_off(L + 1);
   const int64_t n_x = (int64_t)n_atoms * NP * (kC / 4);
   const int64_t n_w = (int64_t)n_rbf * kC;
-  const int64_t n_f = wneg_offset(L, L + 1) / 8;
+  const int64_t n_f = wf_entries(L) / 8;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_x + n_w + n_f; i += stride) {
     if (i < n_x) {
@@ -575,7 +580,7 @@ template <int ND, int NS>
 struct StepState {
   const u32x4* ap;                      // [kRT] + plane fragments
   const u32x4* am;                      // [kRT] - plane fragments
-  const u32x4 (&b)[ND][NS == 2 ? 3 : 1][kNT];  // W0, or W1, W2, -W2
+  const u32x4 (&b)[ND][n_bmat(NS - 1)][kNT];  // W0, or W1, W2 (and -W2)
   f32x4 (&acc)[ND][NS][kNT][kRT];
   const u32x4 (&xr)[kGR * kMaxPairs];
   const uint32_t (&dp)[kGR][kMaxPairs];
@@ -583,7 +588,7 @@ struct StepState {
   float (&vp)[kGR][4];
   float (&vm)[kGR][4];
   // loads for the next K step, spread over the MFMAs of this one
-  u32x4 (&bn)[ND][NS == 2 ? 3 : 1][kNT];  // B fragments of the next step
+  u32x4 (&bn)[ND][n_bmat(NS - 1)][kNT];  // B fragments of the next step
   __amdgpu_buffer_rsrc_t wrs;
   const uint32_t (&boff)[ND][kNT];
   uint32_t wsoff[3];                    // scalar offsets of the next step's W0 / W1, W2, -W2 blocks
@@ -598,7 +603,7 @@ struct StepState {
 // Load j of the next-step loads: first the B fragments, then the gathers.
 template <int ND, int NS, int J>
 __device__ __attribute__((always_inline)) inline void step_load(StepState<ND, NS>& st) {
-  constexpr int NBM = NS == 2 ? 3 : 1;
+  constexpr int NBM = n_bmat(NS - 1);
   constexpr int NB = ND * NBM * kNT;
   if constexpr (J < NB) {
     constexpr int di = J / (NBM * kNT), sm = (J / kNT) % NBM, nt = J % kNT;
@@ -622,7 +627,11 @@ __device__ __attribute__((always_inline)) inline void step_mfma(StepState<ND, NS
     if constexpr (ph == 0)
       st.acc[di][mt][nt][rt] = mfma(as_bf16x8(st.ap[rt]), as_bf16x8(st.b[di][mt][nt]), st.acc[di][mt][nt][rt]);
     else if constexpr (mt == 0)
-      st.acc[di][0][nt][rt] = mfma(as_bf16x8(st.am[rt]), as_bf16x8(st.b[di][2][nt]), st.acc[di][0][nt][rt]);
+      st.acc[di][0][nt][rt] =
+          mfma(as_bf16x8(st.am[rt]),
+               as_bf16x8(kNegCopies ? st.b[di][n_bmat(1) - 1][nt]
+                                    : st.b[di][1][nt] ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}),
+               st.acc[di][0][nt][rt]);
     else
       st.acc[di][1][nt][rt] = mfma(as_bf16x8(st.am[rt]), as_bf16x8(st.b[di][0][nt]), st.acc[di][1][nt][rt]);
   }
@@ -648,7 +657,7 @@ template <int ND, int NS, int I>
 __device__ __attribute__((always_inline)) inline void step_seq(StepState<ND, NS>& st) {
   constexpr int F = ND * kNT * NS * NS * kRT;
   constexpr int D = kMaxPairs * kGR * 4 * NS;
-  constexpr int NL = ND * (NS == 2 ? 3 : 1) * kNT + kGR * kMaxPairs;  // loads of the next step
+  constexpr int NL = ND * n_bmat(NS - 1) * kNT + kGR * kMaxPairs;  // loads of the next step
   constexpr int SP = (2 * F / 3) / NL > 0 ? (2 * F / 3) / NL : 1;
   if constexpr (I < F) {
     step_mfma<ND, NS, I>(st);
@@ -1354,7 +1363,7 @@ ScratchLayout scratch_layout(int n_atoms, int n_targets, int L, int H, int K) {
   s.xp = up256(sizeof(float) * 2 * (size_t)n_targets * H);
   s.wrad = s.xp + up256(sizeof(uint32_t) * (size_t)n_atoms * pair_off(L + 1) * kC);
   s.wf = s.wrad + up256(sizeof(float) * (size_t)K * kC);
-  s.gs = s.wf + up256(sizeof(uint16_t) * (size_t)wneg_offset(L, L + 1));
+  s.gs = s.wf + up256(sizeof(uint16_t) * (size_t)wf_entries(L));
   // at most n_targets groups
   s.bucket = s.gs + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
   s.order = s.bucket + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
@@ -1381,7 +1390,7 @@ MfmaParams make_params(const AttnArgs& a) {
   P.stat_inv = stats + (size_t)a.n_targets * a.H;
   P.y = a.y;
   P.xp_bytes = (uint32_t)((uint64_t)a.n_atoms * pair_off(a.L + 1) * kC * 4);
-  P.w_bytes = (uint32_t)(wneg_offset(a.L, a.L + 1) * 2);
+  P.w_bytes = (uint32_t)(wf_entries(a.L) * 2);
   P.n_targets = a.n_targets;
   P.H = a.H;
   P.K = a.K;
@@ -1395,7 +1404,7 @@ MfmaParams make_params(const AttnArgs& a) {
 
 template <int L>
 so2_status launch_pack_L(const AttnArgs& a, const MfmaParams& P, hipStream_t stream) {
-  const int64_t work = (int64_t)a.n_atoms * pair_off(L + 1) * (kC / 4) + (int64_t)a.K * kC + wneg_offset(L, L + 1) / 8;
+  const int64_t work = (int64_t)a.n_atoms * pair_off(L + 1) * (kC / 4) + (int64_t)a.K * kC + wf_entries(L) / 8;
   const int64_t blocks = std::min<int64_t>((work + 255) / 256, 8192);
   hipLaunchKernelGGL(attn_pack_kernel<L>, dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const uint16_t*)a.x, const_cast<uint32_t*>(P.xp), a.n_atoms, (const uint16_t*)a.w_rad,
