@@ -277,42 +277,68 @@ __global__ void __launch_bounds__(256) attn_pack_kernel(const uint16_t* __restri
 
 // ---------------------------------------------------------------- statistics
 
-// One wave per target: lanes walk the neighbours, each keeps an online
-// (max, normaliser) pair per head; the wave then combines the pairs.
+// One wave per target (4 per block); lane i takes the target's neighbours
+// i, i + 64, ...  For each neighbour the lane computes the edge geometry and
+// envelope once and the logits of every head from the whole k_j row (16-byte
+// loads) and q_t (staged in LDS per wave, read as broadcasts), and keeps an
+// online (max, normaliser) pair per head; the wave then combines the pairs.
 __global__ void __launch_bounds__(256) attn_stats_kernel(MfmaParams P, int C) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= P.n_targets) return;
+  __shared__ __attribute__((aligned(16))) float qs[4][kC];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + w;
+  const bool live = t < P.n_targets;
+  if (live)
+    for (int c = lane; c < kC; c += 64) qs[w][c] = P.q[(int64_t)t * kC + c];
+  __syncthreads();
+  if (!live) return;
   const int e0 = P.row_ptr[t], e1 = P.row_ptr[t + 1];
-  const int H = P.H, d = C / H;
+  const int H = P.H, d = kC / H;
   const float inv_sqrt_d = 1.0f / sqrtf((float)d);
-  for (int h = 0; h < H; ++h) {
-    float m = -INFINITY, s = 0.0f;
-    for (int e = e0 + lane; e < e1; e += 64) {
-      const int j = P.col[e];
-      float r[3];
-      edge_vec(P, t, j, r);
-      const float rho = sqrtf(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
-      const float u = envelope_u(rho / P.cutoff, P.p);
-      float z = 0.0f;
-      for (int c = h * d; c < (h + 1) * d; ++c) z += P.q[(int64_t)t * C + c] * P.k[(int64_t)j * C + c];
-      z *= inv_sqrt_d;
-      if (z > m) {
-        s = s * expf(m - z) + u;
-        m = z;
-      } else {
-        s += u * expf(z - m);
+  float m[kMaxHeads], s[kMaxHeads];
+#pragma unroll
+  for (int h = 0; h < kMaxHeads; ++h) {
+    m[h] = -INFINITY;
+    s[h] = 0.0f;
+  }
+  for (int e = e0 + lane; e < e1; e += 64) {
+    const int j = P.col[e];
+    float r[3];
+    edge_vec(P, t, j, r);
+    const float rho = sqrtf(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
+    const float u = envelope_u(rho / P.cutoff, P.p);
+    const f32x4* kr = (const f32x4*)(P.k + (int64_t)j * kC);
+    const f32x4* qr = (const f32x4*)qs[w];
+#pragma unroll
+    for (int h = 0; h < kMaxHeads; ++h) {
+      if (h < H) {
+        float z = 0.0f;
+        for (int i = h * d / 4; i < (h + 1) * d / 4; ++i) {
+          const f32x4 kv = kr[i], qv = qr[i];
+          z += qv.x * kv.x + qv.y * kv.y + qv.z * kv.z + qv.w * kv.w;
+        }
+        z *= inv_sqrt_d;
+        if (z > m[h]) {
+          s[h] = s[h] * expf(m[h] - z) + u;
+          m[h] = z;
+        } else {
+          s[h] += u * expf(z - m[h]);
+        }
       }
     }
-    float M = m;
+  }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    float part = (m == -INFINITY) ? 0.0f : s * expf(m - M);
+  for (int h = 0; h < kMaxHeads; ++h) {
+    if (h < H) {
+      float M = m[h];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
-    if (lane == 0) {
-      P.stat_max[(int64_t)t * H + h] = M;
-      P.stat_inv[(int64_t)t * H + h] = part > 0.0f ? 1.0f / part : 0.0f;
+      for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+      float part = (m[h] == -INFINITY) ? 0.0f : s[h] * expf(m[h] - M);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+      if (lane == 0) {
+        P.stat_max[(int64_t)t * H + h] = M;
+        P.stat_inv[(int64_t)t * H + h] = part > 0.0f ? 1.0f / part : 0.0f;
+      }
     }
   }
 }
