@@ -11,7 +11,7 @@
 //   assign    cell of every atom, cell occupancy (atomics)
 //   scan      occupancy -> cell start (one workgroup)
 //   scatter   atoms grouped by cell, with their positions and molecule ids
-//   count     one thread per atom: up to 27 cells, exact fp64 test
+//   count     16 lanes per atom: up to 27 cells, exact fp64 test
 //   scan      counts -> row_ptr, E as int64 -> host (sync 2)
 //   fill      same loop, writes col (order within a row is arbitrary)
 //   sort      ascending j inside each row: one 64-lane workgroup per row up
@@ -190,46 +190,62 @@ __device__ inline bool within_cutoff(double pix, double piy, double piz, double 
   return s < rc2;
 }
 
+// Count (kFill = false) or fill (kFill = true) the neighbours of atom i with
+// kGroup lanes per atom: the group walks the up to 27 cells together, its
+// lanes taking the cell's members kGroup apart, and counts its hits with a
+// ballot; in the fill pass every hit goes to row_ptr[i] + (hits so far) +
+// (hits of lower lanes of the group in this round).
+constexpr int kGroup = 16;
 template <bool kFill>
-__global__ void nb_pairs_kernel(const float* __restrict__ pos, const int* __restrict__ mol, int n,
-                                GridParams g, double rc2, const int* __restrict__ cell_start,
-                                const int* __restrict__ sorted_idx,
-                                const float* __restrict__ sorted_pos,
-                                const int* __restrict__ sorted_mol, int* __restrict__ counts,
-                                const int* __restrict__ row_ptr, int* __restrict__ col,
-                                int* __restrict__ long_rows, int* __restrict__ n_long,
-                                int* __restrict__ n_over) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  double pix = (double)pos[3 * (int64_t)i + 0];
-  double piy = (double)pos[3 * (int64_t)i + 1];
-  double piz = (double)pos[3 * (int64_t)i + 2];
-  int mi = mol ? mol[i] : 0;
+__global__ void __launch_bounds__(256) nb_pairs_kernel(const float* __restrict__ pos, const int* __restrict__ mol,
+                                                       int n, GridParams g, double rc2,
+                                                       const int* __restrict__ cell_start,
+                                                       const int* __restrict__ sorted_idx,
+                                                       const float* __restrict__ sorted_pos,
+                                                       const int* __restrict__ sorted_mol, int* __restrict__ counts,
+                                                       const int* __restrict__ row_ptr, int* __restrict__ col,
+                                                       int* __restrict__ long_rows, int* __restrict__ n_long,
+                                                       int* __restrict__ n_over) {
+  const int gid = blockIdx.x * (blockDim.x / kGroup) + threadIdx.x / kGroup;
+  const int li = threadIdx.x % kGroup;                // lane within the group
+  const int gshift = (threadIdx.x & 63) & ~(kGroup - 1);  // first lane of the group in the wave
+  if (gid >= n) return;  // whole groups leave together
+  const int i = gid;
+  const double pix = (double)pos[3 * (int64_t)i + 0];
+  const double piy = (double)pos[3 * (int64_t)i + 1];
+  const double piz = (double)pos[3 * (int64_t)i + 2];
+  const int mi = mol ? mol[i] : 0;
   int cx[3], cy[3], cz[3];
-  int nx = axis_cells(cell_coord(pix, 0, g), 0, g, cx);
-  int ny = axis_cells(cell_coord(piy, 1, g), 1, g, cy);
-  int nz = axis_cells(cell_coord(piz, 2, g), 2, g, cz);
-  int cnt = 0;
-  int base = kFill ? row_ptr[i] : 0;
+  const int nx = axis_cells(cell_coord(pix, 0, g), 0, g, cx);
+  const int ny = axis_cells(cell_coord(piy, 1, g), 1, g, cy);
+  const int nz = axis_cells(cell_coord(piz, 2, g), 2, g, cz);
+  int cnt = 0;  // hits of the whole group so far (same in every lane)
+  const int base = kFill ? row_ptr[i] : 0;
   for (int a = 0; a < nz; ++a)
     for (int b = 0; b < ny; ++b)
       for (int c = 0; c < nx; ++c) {
-        int cell = (cz[a] * g.n[1] + cy[b]) * g.n[0] + cx[c];
-        int k0 = cell_start[cell], k1 = cell_start[cell + 1];
-        for (int k = k0; k < k1; ++k) {
-          int j = sorted_idx[k];
-          if (j == i) continue;
-          if (sorted_mol[k] != mi) continue;
-          double pjx = (double)sorted_pos[3 * (int64_t)k + 0];
-          double pjy = (double)sorted_pos[3 * (int64_t)k + 1];
-          double pjz = (double)sorted_pos[3 * (int64_t)k + 2];
-          if (within_cutoff(pix, piy, piz, pjx, pjy, pjz, g, rc2)) {
-            if (kFill) col[base + cnt] = j;
-            ++cnt;
+        const int cell = (cz[a] * g.n[1] + cy[b]) * g.n[0] + cx[c];
+        const int k0 = cell_start[cell], k1 = cell_start[cell + 1];
+        for (int kb = k0; kb < k1; kb += kGroup) {
+          const int k = kb + li;
+          bool hit = false;
+          int j = -1;
+          if (k < k1) {
+            j = sorted_idx[k];
+            if (j != i && sorted_mol[k] == mi) {
+              const double pjx = (double)sorted_pos[3 * (int64_t)k + 0];
+              const double pjy = (double)sorted_pos[3 * (int64_t)k + 1];
+              const double pjz = (double)sorted_pos[3 * (int64_t)k + 2];
+              hit = within_cutoff(pix, piy, piz, pjx, pjy, pjz, g, rc2);
+            }
           }
+          const unsigned long long bal = __ballot(hit);
+          const unsigned int gm = (unsigned int)(bal >> gshift) & ((1u << kGroup) - 1u);
+          if (kFill && hit) col[base + cnt + __popc(gm & ((1u << li) - 1u))] = j;
+          cnt += __popc(gm);
         }
       }
-  if (!kFill) {
+  if (!kFill && li == 0) {
     counts[i] = cnt;
     if (cnt > kLongRow) {
       atomicAdd(n_over, 1);
@@ -422,7 +438,8 @@ so2_status neighbors_build(const float* pos, int32_t n, const int32_t* mol_id,
 
   // 4. count, scan, read E
   const double rc2 = rc * rc;
-  hipLaunchKernelGGL(nb_pairs_kernel<false>, dim3(nblk), dim3(tb), 0, stream, pos, mol_id, n, g,
+  const int nblk_pairs = (n + tb / kGroup - 1) / (tb / kGroup);
+  hipLaunchKernelGGL(nb_pairs_kernel<false>, dim3(nblk_pairs), dim3(tb), 0, stream, pos, mol_id, n, g,
                      rc2, cell_start, sorted_idx, sorted_pos, sorted_mol, counts,
                      (const int*)nullptr, (int*)nullptr, long_rows, n_long, n_over);
   hipLaunchKernelGGL(nb_scan_kernel, dim3(1), dim3(1024), 0, stream, counts, n, row_ptr,
@@ -440,7 +457,7 @@ so2_status neighbors_build(const float* pos, int32_t n, const int32_t* mol_id,
   if (E > capacity) return SO2_ERR_CAPACITY;
 
   // 5. fill and sort rows
-  hipLaunchKernelGGL(nb_pairs_kernel<true>, dim3(nblk), dim3(tb), 0, stream, pos, mol_id, n, g,
+  hipLaunchKernelGGL(nb_pairs_kernel<true>, dim3(nblk_pairs), dim3(tb), 0, stream, pos, mol_id, n, g,
                      rc2, cell_start, sorted_idx, sorted_pos, sorted_mol, (int*)nullptr, row_ptr,
                      col, (int*)nullptr, (int*)nullptr, (int*)nullptr);
   hipLaunchKernelGGL(nb_sort_short_kernel, dim3(n), dim3(64), 0, stream, row_ptr, col, n);
