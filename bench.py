@@ -8,6 +8,7 @@ fused kernel, a2-a11).  Inputs are resident in device memory before the
 timed region starts.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload small_molecules]
+    python bench.py --memory-sweep [--steps 5 --warmup 2]   (peak bytes against N)
 
 value          messages (edges) per second of the whole step
 roofline       the fused attention kernel against the dense bf16 MFMA peak:
@@ -234,6 +235,46 @@ def run_gpu(w, steps, warmup):
     )
 
 
+SWEEP_ATOMS = (12_500, 25_000, 50_000, 100_000, 200_000)
+
+
+def memory_sweep(steps, warmup):
+    """Peak device bytes and throughput of the whole step against atom count:
+    the periodic water box at 0.1 atoms/A^3 with a 5 A cutoff (the 100k-atom
+    workload's recipe) at every size in SWEEP_ATOMS.  Prints one JSON line
+    per size, then a least-squares line bytes = a + b N with its largest
+    relative residual.  Every buffer of the step is a torch allocation (the
+    library allocates nothing), so torch's peak counter covers them all."""
+    import numpy as np
+    import torch
+
+    from synth import make_workload
+
+    pts = []
+    for n in SWEEP_ATOMS:
+        w = make_workload("water_100k", geometry={"n_atoms": n})
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        g = run_gpu(w, steps, warmup)
+        kern = sum(g["kern_ms"]) / len(g["kern_ms"])
+        rec = {
+            "n_atoms": n, "n_edges": g["E"], "peak_device_bytes": g["peak_bytes"],
+            "peak_bytes_per_atom": g["peak_bytes"] / n, "ms_per_step": g["total_s"] / steps * 1e3,
+            "messages_per_s": g["E"] * steps / g["total_s"], "attention_kernel_ms_mean": kern,
+            "attention_tflops": g["E"] * flops_per_edge(w.l_max, w.channels) / (kern * 1e-3) / 1e12,
+            "outputs_finite": g["finite"],
+        }
+        pts.append(rec)
+        print(json.dumps(rec), flush=True)
+        del w, g
+    n = np.array([p["n_atoms"] for p in pts], dtype=np.float64)
+    b = np.array([p["peak_device_bytes"] for p in pts], dtype=np.float64)
+    slope, icpt = np.polyfit(n, b, 1)
+    resid = np.abs(b - (icpt + slope * n)) / b
+    print(json.dumps({"fit": "peak_device_bytes = a + b * n_atoms", "a_bytes": icpt, "b_bytes_per_atom": slope,
+                      "max_relative_residual": float(resid.max())}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +285,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, metavar="MIB", default=0,
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--memory-sweep", action="store_true",
+                    help="only run the water box at 12.5k-200k atoms: peak device bytes against N")
     args = ap.parse_args()
     if args.gpus != 1:
         print(
@@ -254,6 +297,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.memory_sweep:
+        memory_sweep(args.steps, args.warmup)
         return
 
     from synth import make_workload

@@ -108,22 +108,11 @@ __host__ __device__ constexpr int64_t w1_offset(int L, int m) {
   for (int mu = 1; mu < m; ++mu) off += 2 * (int64_t)(L + 1 - mu) * kC * (L + 1 - mu) * kC;
   return off;
 }
-// The fragment-ordered weights hold, after W0 and (W1_m, W2_m), a copy of
-// every -W2_m (m = 1..L), so that the complex product needs no sign flips
-// in the main loop.  wneg_offset(L, m): first entry of -W2_m;
-// wneg_offset(L, L + 1): entries in all.
-__host__ __device__ constexpr int64_t wneg_offset(int L, int m) {
-  int64_t off = w1_offset(L, L + 1);
-  for (int mu = 1; mu < m; ++mu) off += (int64_t)(L + 1 - mu) * kC * (L + 1 - mu) * kC;
-  return off;
-}
-// B matrices of block m: W0 (m = 0), or W1_m, W2_m and -W2_m.
-constexpr bool kNegCopies = false;  // load -W2 fragments (true) or flip W2's sign bits per step (false)
-__host__ __device__ constexpr int n_bmat(int m) { return m ? (kNegCopies ? 3 : 2) : 1; }
-// entries of the fragment-ordered weights
-__host__ __device__ constexpr int64_t wf_entries(int L) {
-  return kNegCopies ? wneg_offset(L, L + 1) : w1_offset(L, L + 1);
-}
+// B matrices of block m: W0 (m = 0), or W1_m and W2_m; the minus sign of the
+// complex product is applied by flipping W2's sign bits in registers.
+__host__ __device__ constexpr int n_bmat(int m) { return m ? 2 : 1; }
+// entries of the fragment-ordered weights (the same count as w_so2)
+__host__ __device__ constexpr int64_t wf_entries(int L) { return w1_offset(L, L + 1); }
 
 struct MfmaParams {
   const float* pos;
@@ -241,28 +230,12 @@ __global__ void __launch_bounds__(256) attn_pack_kernel(const uint16_t* __restri
       wrad[w] = bf16_to_float(w_rad[w]);
     } else {
       const int64_t g = 8 * (i - n_x - n_w);  // first element of this lane's 16 bytes in wf
-      int64_t base = 0, src = 0;  // first entry of the matrix in wf and in w_so2
-      uint32_t neg = 0;
-      int KM = (L + 1) * kC;
-      if (g < w1_offset(L, L + 1)) {
-        int mi = 0;
-        while (g >= base + (int64_t)KM * KM) {
-          base += (int64_t)KM * KM;
-          ++mi;
-          KM = (L + 1 - (mi + 1) / 2) * kC;
-        }
-        src = base;
-      } else {
-        int m = 1;
-        KM = L * kC;
-        base = wneg_offset(L, 1);
-        while (g >= base + (int64_t)KM * KM) {
-          base += (int64_t)KM * KM;
-          ++m;
-          KM = (L + 1 - m) * kC;
-        }
-        src = w1_offset(L, m) + (int64_t)KM * KM;  // W2_m
-        neg = 0x80008000u;
+      int64_t base = 0;  // first entry of the matrix (the same in wf and in w_so2)
+      int mi = 0, KM = (L + 1) * kC;
+      while (g >= base + (int64_t)KM * KM) {
+        base += (int64_t)KM * KM;
+        ++mi;
+        KM = (L + 1 - (mi + 1) / 2) * kC;
       }
       const int64_t lg = (g - base) / 8;
       const int lane = (int)(lg % 64);
@@ -270,7 +243,7 @@ __global__ void __launch_bounds__(256) attn_pack_kernel(const uint16_t* __restri
       const int ks = (int)(f % (KM / 32));
       const int64_t row = 16 * (f / (KM / 32)) + (lane & 15);
       const int col = 32 * ks + 8 * (lane >> 4);
-      *(u32x4*)(wf + g) = *(const u32x4*)(w_so2 + src + row * KM + col) ^ u32x4{neg, neg, neg, neg};
+      *(u32x4*)(wf + g) = *(const u32x4*)(w_so2 + base + row * KM + col);
     }
   }
 }
@@ -571,7 +544,7 @@ template <int L, int M>
 __device__ constexpr uint32_t bmat_byte(int s) {
   constexpr int KM = (L + 1 - M) * kC;
   constexpr uint32_t w1_byte = (uint32_t)(M == 0 ? 0 : w1_offset(L, M)) * 2u;
-  return s == 0 ? w1_byte : s == 1 ? w1_byte + (uint32_t)(KM * KM) * 2u : (uint32_t)wneg_offset(L, M) * 2u;
+  return s == 0 ? w1_byte : w1_byte + (uint32_t)(KM * KM) * 2u;
 }
 
 template <int L, int M, int LO, int ND>
@@ -606,7 +579,7 @@ template <int ND, int NS>
 struct StepState {
   const u32x4* ap;                      // [kRT] + plane fragments
   const u32x4* am;                      // [kRT] - plane fragments
-  const u32x4 (&b)[ND][n_bmat(NS - 1)][kNT];  // W0, or W1, W2 (and -W2)
+  const u32x4 (&b)[ND][n_bmat(NS - 1)][kNT];  // W0, or W1 and W2
   f32x4 (&acc)[ND][NS][kNT][kRT];
   const u32x4 (&xr)[kGR * kMaxPairs];
   const uint32_t (&dp)[kGR][kMaxPairs];
@@ -617,7 +590,7 @@ struct StepState {
   u32x4 (&bn)[ND][n_bmat(NS - 1)][kNT];  // B fragments of the next step
   __amdgpu_buffer_rsrc_t wrs;
   const uint32_t (&boff)[ND][kNT];
-  uint32_t wsoff[3];                    // scalar offsets of the next step's W0 / W1, W2, -W2 blocks
+  uint32_t wsoff[2];                    // scalar offsets of the next step's W0 / W1 and W2 blocks
   u32x4 (&xn)[kGR * kMaxPairs];         // gathers of the next generator unit
   __amdgpu_buffer_rsrc_t xrs;
   uint32_t xoff[kGR];                   // per row; past the end for pairs beyond the unit's degree
@@ -655,8 +628,7 @@ __device__ __attribute__((always_inline)) inline void step_mfma(StepState<ND, NS
     else if constexpr (mt == 0)
       st.acc[di][0][nt][rt] =
           mfma(as_bf16x8(st.am[rt]),
-               as_bf16x8(kNegCopies ? st.b[di][n_bmat(1) - 1][nt]
-                                    : st.b[di][1][nt] ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}),
+               as_bf16x8(st.b[di][1][nt] ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u}),
                st.acc[di][0][nt][rt]);
     else
       st.acc[di][1][nt][rt] = mfma(as_bf16x8(st.am[rt]), as_bf16x8(st.b[di][0][nt]), st.acc[di][1][nt][rt]);
@@ -739,7 +711,7 @@ __device__ inline void fused_step(const uint16_t* abuf, int k, const u32x4 (&b)[
 #pragma unroll
   for (int u = 0; u < kGR; ++u) xo[u] = c.xoff[u];
   StepState<ND, NS> st{ap, am, b, acc, xr, dp, dm, vp, vm,
-                       bn, wrs, boff, {bmat_byte<L, M>(0) + sb, bmat_byte<L, M>(1) + sb, bmat_byte<L, M>(2) + sb},
+                       bn, wrs, boff, {bmat_byte<L, M>(0) + sb, bmat_byte<L, M>(1) + sb},
                        xn, xrs, {}, (uint32_t)(pair_off(nglp) * kC + 32 * nk) * 4u, nglp, oob};
 #pragma unroll
   for (int u = 0; u < kGR; ++u) st.xoff[u] = xo[u];
