@@ -150,7 +150,7 @@ int32_t so2_attention_kernel_kind(const so2_attn_desc* desc);
  *   w_q, w_k  [C][C], w_rad [K][C], w_so2 [so2_weight_count]   dtype
  *   y         [n_targets][(L+1)^2][C] fp32, written
  *   workspace >= so2_attention_workspace_bytes(desc) bytes
- * Kernels: bf16 with C = 128, 1 <= L <= 4, H <= 16, K <= 32 runs on the
+ * Kernels: bf16 with C = 128, 1 <= L <= 6, H <= 16, K <= 32 runs on the
  * MFMA kernel; every other shape (fp32 or bf16) on the VALU kernel.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (L > 6 or C > 256: no kernel), BOX,
  * WORKSPACE, DEVICE.  Asynchronous on

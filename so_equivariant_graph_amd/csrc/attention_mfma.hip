@@ -77,24 +77,51 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
 constexpr int kC = 128;               // channels
 constexpr int kWaves = 8;             // two waves per SIMD
 constexpr int kThreads = kWaves * 64;
 constexpr int kNT = kC / (16 * kWaves);  // 16-column tiles per wave: wave w owns channels 16 kNT w ..
-constexpr int kGR = 64 * 8 / kThreads;   // generator rows per lane (8 lanes per row and K step)
-constexpr int kGStride = kThreads / 8;   // distance between a lane's generator rows
-static_assert(kThreads == 8 * 64, "phase A maps 8 lanes to each of the 64 edge rows");
-constexpr int kM = 64;                // edges per chunk
-constexpr int kRT = kM / 16;          // row tiles
+constexpr int kGR = 1;                // generator rows per lane and K step
+constexpr int kMaxM = 64;             // largest chunk
 constexpr int kSlots = 4;             // targets live in one chunk
-constexpr int kEdgesPerGroup = 384;   // edges per workgroup (about six chunks)
+constexpr int kEdgesPerGroup = 384;   // edges per workgroup (about six 64-edge chunks)
 constexpr int kKC = 128;              // channels per A chunk (one degree, 4 MFMA K steps)
-constexpr int kAplane = kM * kKC;     // one sign plane of an A chunk, bf16
-constexpr int kAbuf = 2 * kAplane;    // one A buffer (both signs), bf16
 constexpr int kMaxHeads = 16;
-constexpr int kMaxPairs = 5;          // component pairs of one degree, L <= 4
 constexpr int kMaxRbf = 32;           // radial basis functions kept per edge in LDS
+
+// Edges per chunk: 64 up to L = 4; 32 for L = 5, 6, where the Wigner-D
+// rows, the A' fragments and the accumulators of 64 edges would not fit the
+// 160 KB of LDS and the register file.
+__host__ __device__ constexpr int chunk_edges(int L) { return L <= 4 ? 64 : 32; }
+
+// Chunk geometry of degree L.  In every K step each lane generates GCH
+// channels of one edge row of the next A chunk: GL lanes per row, so the
+// GL lanes of a row read one contiguous 32-channel slice of x pairs.
+template <int L>
+struct Geo {
+  static constexpr int M = chunk_edges(L);       // edges per chunk
+  static constexpr int RT = M / 16;              // MFMA row tiles
+  static constexpr int GL = kThreads / M;        // generator lanes per edge row
+  static constexpr int GCH = 32 / GL;            // channels per generator lane and K step
+  static constexpr int MP = L + 1 > 5 ? L + 1 : 5;  // component pairs per generator unit
+  static constexpr int APLANE = M * kKC;         // one sign plane of an A chunk, bf16
+  static constexpr int ABUF = 2 * APLANE;        // one A buffer (both signs), bf16
+};
+static_assert(kThreads == 8 * 64, "phase A maps the 512 lanes onto the edge rows of a chunk");
+
+// Gather vector of a generator lane: its GCH channels of one x pair.
+template <int G>
+struct XVec;
+template <>
+struct XVec<4> {
+  typedef u32x4 type;
+};
+template <>
+struct XVec<2> {
+  typedef u32x2 type;
+};
 
 // Component pairs: degree l has l + 1 pairs (2p, 2p+1), the last one padded
 // with zero.  pair_off(l) = pairs of the degrees below l.
@@ -172,6 +199,17 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t 
 
 __device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+__device__ inline u32x2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
+
+// One gather vector (16 or 8 bytes).
+template <int G>
+__device__ inline typename XVec<G>::type buffer_load_x(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (G == 4) return buffer_load16(r, voff, soff);
+  else return buffer_load8(r, voff, soff);
 }
 
 __device__ inline void edge_vec(const MfmaParams& P, int i, int j, float* r) {
@@ -328,19 +366,24 @@ struct Cfg {
   static constexpr int TT = (TROWS + 15) / 16;  // 16-row MFMA tiles
 };
 
-struct Smem {
+template <int NRI>
+struct SmemT {
   int rp[kSlots + 2];   // row_ptr[t_first .. t_first + kSlots]
   int flush_t[kSlots];  // target written out from each slot after this chunk, or -1
-  int row_j[kM];
-  int row_slot[kM];
-  uint16_t rowinfo[112];  // accumulator row R -> slot << 8 | component, 0xffff past the rows
-  int row_t[kM];          // target of each edge row
-  f32x4 row_rv[kM];       // minimum-image edge vector and its length
+  int row_j[kMaxM];
+  int row_slot[kMaxM];
+  uint16_t rowinfo[NRI];  // accumulator row R -> slot << 8 | component, 0xffff past the rows
+  int row_t[kMaxM];       // target of each edge row
+  f32x4 row_rv[kMaxM];    // minimum-image edge vector and its length
 };
+// the row table covers the accumulator tiles (at least 112 entries)
+template <int L>
+using Smem = SmemT<(16 * Cfg<L>::TT > 112 ? 16 * Cfg<L>::TT : 112)>;
 
 // Passes in execution order: blocks m = 1..L, each in groups of at most two
 // output degrees (the limit of the register budget with two sign planes),
-// then m = 0 in one pass over all its L + 1 output degrees.  Every pass
+// then m = 0 in one pass over all its L + 1 output degrees (two passes for
+// L >= 5).  Every pass
 // generates, during its last A chunk, the first A chunk of the pass after
 // it; ending on m = 0 means a pass never has to produce more sign planes
 // than it has itself (an m >= 1 pass writes both planes, m = 0 reads one).
@@ -352,7 +395,7 @@ __host__ __device__ constexpr PassInfo pass_info(int L, int idx) {
   int i = 0;
   for (int mm = 1; mm <= L + 1; ++mm) {
     const int M = mm == L + 1 ? 0 : mm;
-    const int nd = M == 0 ? L + 1 : 2;
+    const int nd = M == 0 ? (L <= 4 ? L + 1 : (L + 2) / 2) : 2;
     for (int lo = M; lo <= L; lo += nd) {
       if (i == idx) return PassInfo{M, lo, (L + 1 - lo) < nd ? (L + 1 - lo) : nd};
       ++i;
@@ -368,7 +411,8 @@ __host__ __device__ constexpr int deg_tiles(int l) {
 // A' fragments of pass idx: (degree, tile, K step) for its output degrees.
 __host__ __device__ constexpr int frag_count(int L, int idx) {
   const PassInfo pi = pass_info(L, idx);
-  const int steps = pi.M == 0 ? kRT / 2 : kRT;
+  const int rt = chunk_edges(L) / 16;
+  const int steps = pi.M == 0 ? rt / 2 : rt;
   int t = 0;
   for (int di = 0; di < pi.ND; ++di) t += deg_tiles(pi.LO + di) * steps;
   return t;
@@ -389,14 +433,21 @@ __host__ __device__ constexpr int chunks_before(int L, int idx) {
 
 template <int L>
 struct Lds {
-  static constexpr size_t kHdr = (sizeof(Smem) + 15) & ~(size_t)15;
-  static constexpr size_t kD = kHdr;                                             // u32 [kM][DPW]
-  static constexpr size_t kG = (kD + 4 * kM * Cfg<L>::DPW + 15) & ~(size_t)15;  // f32 [kM][kC], swizzled
-  static constexpr size_t kW = kG + sizeof(float) * kM * kC;                     // f32 [kMaxHeads][kM]
-  static constexpr size_t kA = kW + sizeof(float) * kM * kMaxHeads;              // bf16 [2][2][kM][kKC], swizzled
-  static constexpr size_t kF = kA + sizeof(uint16_t) * 2 * kAbuf;                // A' fragments u32x4 [][64]
-  static constexpr size_t kPhi = kF + sizeof(u32x4) * 64 * max_frags(L);         // f32 [kM][kMaxRbf]
-  static constexpr size_t kTotal = kPhi + sizeof(float) * kM * kMaxRbf;
+  static constexpr int M = Geo<L>::M;
+  static constexpr size_t kHdr = (sizeof(Smem<L>) + 15) & ~(size_t)15;
+  static constexpr size_t kD = kHdr;                                            // u32 [M][DPW]
+  static constexpr size_t kG = (kD + 4 * M * Cfg<L>::DPW + 15) & ~(size_t)15;  // f32 [M][kC], swizzled
+  static constexpr size_t kW = kG + sizeof(float) * M * kC;                     // f32 [kMaxHeads][M]
+  static constexpr size_t kA = kW + sizeof(float) * M * kMaxHeads;              // bf16 [2][2][M][kKC], swizzled
+  static constexpr size_t kF = kA + sizeof(uint16_t) * 2 * Geo<L>::ABUF;        // A' fragments u32x4 [][64]
+  static constexpr size_t kPhi = kF + sizeof(u32x4) * 64 * max_frags(L);        // f32 [M][kMaxRbf]
+  static constexpr size_t kTotal = kPhi + sizeof(float) * M * kMaxRbf;
+  // L >= 5, phase A only: D^1, D^4 and D^5 of every edge in fp32, in the
+  // A buffers (free until the first A chunk is generated)
+  static constexpr size_t kS1 = kA;
+  static constexpr size_t kS4 = kS1 + sizeof(float) * M * 9;
+  static constexpr size_t kS5 = kS4 + sizeof(float) * M * 81;
+  static_assert(L <= 4 || kS5 + sizeof(float) * M * 121 <= kF, "Wigner-D staging fits the A buffers");
 };
 
 // 16-byte column groups are XOR-swizzled by row so that both the MFMA
@@ -411,7 +462,8 @@ __device__ inline int g_off(int row, int group) { return row * kC + 4 * (group ^
 
 // Edge er of the chunk: its target t (one of the slots' targets), source j
 // and minimum-image vector r_ij = p_j - p_t.
-__device__ inline void row_edge(const MfmaParams& P, const Smem& S, int er, int t_first, int& t, int& j,
+template <class SM>
+__device__ inline void row_edge(const MfmaParams& P, const SM& S, int er, int t_first, int& t, int& j,
                                 float* rv) {
   int s = 0;
   while (s + 1 < kSlots && S.rp[s + 1] <= er) ++s;
@@ -432,12 +484,19 @@ __device__ inline void store_dpairs(const float* D, uint32_t* out) {
       out[dpair_off(l) + a * (l + 1) + p] = pack_bf16x2(D[a * n + 2 * p], 2 * p + 1 < n ? D[a * n + 2 * p + 1] : 0.0f);
 }
 
+// D^0 .. D^min(L, 4) of one edge as pairs, in registers; for L >= 5 also
+// D^1 and D^4 in fp32 (s1, s4), from which the higher degrees follow row by
+// row (wigner_row).
 template <int L>
-__device__ inline void wigner_pairs(const float* R, uint32_t* out) {
+__device__ inline void wigner_pairs(const float* R, uint32_t* out, float* s1, float* s4) {
   float D1[9];
   wigner_l1(R, D1);
   out[0] = pack_bf16x2(1.0f, 0.0f);
   if constexpr (L >= 1) store_dpairs<1>(D1, out);
+  if constexpr (L >= 5) {
+#pragma unroll
+    for (int q = 0; q < 9; ++q) s1[q] = D1[q];
+  }
   if constexpr (L >= 2) {
     float D2[25];
     wigner_step<2>(D1, D1, D2);
@@ -450,33 +509,64 @@ __device__ inline void wigner_pairs(const float* R, uint32_t* out) {
         float D4[81];
         wigner_step<4>(D1, D3, D4);
         store_dpairs<4>(D4, out);
+        if constexpr (L >= 5) {
+#pragma unroll
+          for (int q = 0; q < 81; ++q) s4[q] = D4[q];
+        }
       }
     }
   }
 }
 
+// Row a of D^l (l >= 5) of one edge by the same recursion, from D^1 and
+// D^{l-1} in fp32: its pairs into the edge's pair block out and, if kNext,
+// the row in fp32 into next (D^l, for degree l + 1).
+template <int l, int a, bool kNext>
+__device__ inline void wigner_row(const float (&D1)[9], const float* Dp, uint32_t* out, float* next) {
+  constexpr int n = 2 * l + 1;
+  float v[n];
+#pragma unroll
+  for (int b = 0; b < n; ++b) v[b] = wigner_entry(l, a - l, b - l, D1, Dp);
+  if constexpr (kNext) {
+#pragma unroll
+    for (int b = 0; b < n; ++b) next[a * n + b] = v[b];
+  }
+#pragma unroll
+  for (int p = 0; p <= l; ++p)
+    out[dpair_off(l) + a * (l + 1) + p] = pack_bf16x2(v[2 * p], 2 * p + 1 < n ? v[2 * p + 1] : 0.0f);
+}
+
+// wigner_row for a row index known only at run time.
+template <int l, int A, bool kNext>
+__device__ inline void wigner_row_any(int a, const float (&D1)[9], const float* Dp, uint32_t* out, float* next) {
+  if constexpr (A < 2 * l + 1) {
+    if (a == A) wigner_row<l, A, kNext>(D1, Dp, out, next);
+    else wigner_row_any<l, A + 1, kNext>(a, D1, Dp, out, next);
+  }
+}
+
 // ---------------------------------------------------------------- A operand
 
-// Per-lane state for one edge chunk.  Generator lane: rows r0 = tid / 8
-// (+ kGStride u, u < kGR) and, in K step k of an A chunk, the 4 channels
-// 32 k + 4 (tid % 8): the 8 lanes of a row read one 128-byte line of x
-// pairs per load.
+// Per-lane state for one edge chunk.  Generator lane: row r0 = tid / GL
+// and, in K step k of an A chunk, the GCH channels 32 k + GCH (tid % GL):
+// the GL lanes of a row read one 128-byte line of x pairs per load.
 struct Ctx {
-  uint32_t xoff[kGR];  // byte offset of (j, pair 0, channel 4 (tid % 8)) in xp per row; xp_bytes if no edge
+  uint32_t xoff[kGR];  // byte offset of (j, pair 0, channel GCH (tid % GL)) in xp per row; xp_bytes if no edge
   int r0, c8;
   int head[kNT];       // head of each of this lane's output column tiles
 };
 
 // Gathers of generator unit k of an A chunk of degree glp: for every pair
-// p <= L and every generator row one 16-byte load (p > glp reads past the
-// buffer: zeros, no memory traffic, so the code has no branch on glp).
+// p < MP and every generator row one 16- or 8-byte load (p > glp reads past
+// the buffer: zeros, no memory traffic, so the code has no branch on glp).
+template <int L>
 __device__ inline void gen_issue(__amdgpu_buffer_rsrc_t xrs, const Ctx& c, uint32_t oob, int glp, int k,
-                                 u32x4 (&xr)[kGR * kMaxPairs]) {
+                                 typename XVec<Geo<L>::GCH>::type (&xr)[kGR * Geo<L>::MP]) {
 #pragma unroll
-  for (int p = 0; p < kMaxPairs; ++p) {
+  for (int p = 0; p < Geo<L>::MP; ++p) {
     const uint32_t soff = (uint32_t)((pair_off(glp) + p) * kC + 32 * k) * 4u;
 #pragma unroll
-    for (int u = 0; u < kGR; ++u) xr[kGR * p + u] = buffer_load16(xrs, p <= glp ? c.xoff[u] : oob, soff);
+    for (int u = 0; u < kGR; ++u) xr[kGR * p + u] = buffer_load_x<Geo<L>::GCH>(xrs, p <= glp ? c.xoff[u] : oob, soff);
   }
 }
 
@@ -484,13 +574,15 @@ __device__ inline void gen_issue(__amdgpu_buffer_rsrc_t xrs, const Ctx& c, uint3
 // glp - gm of D^glp, pairs 0..glp; the pairs past glp are zero (their
 // gathers read zeros too) and are not read, since past the last row of a
 // degree lie the next edge's pairs or, after the last edge, other LDS data.
-__device__ inline void gen_dpairs(const uint32_t* sD, int DPW, const Ctx& c, int gm, int glp,
-                                  uint32_t (&dp)[kGR][kMaxPairs], uint32_t (&dm)[kGR][kMaxPairs]) {
+template <int L>
+__device__ inline void gen_dpairs(const uint32_t* sD, const Ctx& c, int gm, int glp,
+                                  uint32_t (&dp)[kGR][Geo<L>::MP], uint32_t (&dm)[kGR][Geo<L>::MP]) {
+  constexpr int DPW = Cfg<L>::DPW;
 #pragma unroll
   for (int u = 0; u < kGR; ++u) {
-    const uint32_t* d = sD + (c.r0 + kGStride * u) * DPW + dpair_off(glp);
+    const uint32_t* d = sD + (c.r0 + Geo<L>::M * u) * DPW + dpair_off(glp);
 #pragma unroll
-    for (int p = 0; p < kMaxPairs; ++p) {
+    for (int p = 0; p < Geo<L>::MP; ++p) {
       const int pc = p <= glp ? p : glp;
       const uint32_t vp = d[(glp + gm) * (glp + 1) + pc];
       const uint32_t vm = d[(glp - gm) * (glp + 1) + pc];
@@ -500,36 +592,62 @@ __device__ inline void gen_dpairs(const uint32_t* sD, int DPW, const Ctx& c, int
   }
 }
 
+// Gates of a generator lane's GCH channels of row r in K step k.
+template <int G>
+__device__ inline void load_gate(const float* sG, int r, int k, int c8, float (&g)[G]) {
+  if constexpr (G == 4) {
+    const f32x4 v = *(const f32x4*)(sG + g_off(r, 8 * k + c8));
+    g[0] = v.x;
+    g[1] = v.y;
+    g[2] = v.z;
+    g[3] = v.w;
+  } else {
+    const f32x2 v = *(const f32x2*)(sG + g_off(r, 8 * k + (c8 >> 1)) + 2 * (c8 & 1));
+    g[0] = v.x;
+    g[1] = v.y;
+  }
+}
+
+// Round g * v to bf16 and store the lane's GCH channels of row r, K step k.
+template <int G>
+__device__ inline void store_a(uint16_t* plane, int r, int k, int c8, const float (&v)[G], const float (&g)[G]) {
+  if constexpr (G == 4) {
+    const int ao = a_off(r, 4 * k + (c8 >> 1)) + 4 * (c8 & 1);
+    *(u32x2*)(plane + ao) = u32x2{pack_bf16x2(v[0] * g[0], v[1] * g[1]), pack_bf16x2(v[2] * g[2], v[3] * g[3])};
+  } else {
+    const int ao = a_off(r, 4 * k + (c8 >> 2)) + 2 * (c8 & 3);
+    *(uint32_t*)(plane + ao) = pack_bf16x2(v[0] * g[0], v[1] * g[1]);
+  }
+}
+
 // Generator unit k: a[r][c] = g_r[c] sum_p dot2(D pair, x pair) for the
 // + row and (NS = 2) the - row, rounded to bf16 into K step k of abuf.
-template <int NS>
-__device__ inline void gen_finish(const float* sG, const Ctx& c, int k, const u32x4 (&xr)[kGR * kMaxPairs],
-                                  const uint32_t (&dp)[kGR][kMaxPairs], const uint32_t (&dm)[kGR][kMaxPairs],
+template <int L, int NS>
+__device__ inline void gen_finish(const float* sG, const Ctx& c, int k,
+                                  const typename XVec<Geo<L>::GCH>::type (&xr)[kGR * Geo<L>::MP],
+                                  const uint32_t (&dp)[kGR][Geo<L>::MP], const uint32_t (&dm)[kGR][Geo<L>::MP],
                                   uint16_t* abuf) {
+  constexpr int G = Geo<L>::GCH;
 #pragma unroll
   for (int u = 0; u < kGR; ++u) {
-    const int r = c.r0 + kGStride * u;
-    float ap[4], am[4];
+    const int r = c.r0 + Geo<L>::M * u;
+    float ap[G], am[G];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ap[q] = am[q] = 0.0f;
+    for (int q = 0; q < G; ++q) ap[q] = am[q] = 0.0f;
 #pragma unroll
-    for (int p = 0; p < kMaxPairs; ++p) {
-      const u32x4 v = xr[kGR * p + u];
-      const uint32_t xv[4] = {v.x, v.y, v.z, v.w};
+    for (int p = 0; p < Geo<L>::MP; ++p) {
+      const typename XVec<G>::type v = xr[kGR * p + u];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) ap[q] = dot2(dp[u][p], xv[q], ap[q]);
+      for (int q = 0; q < G; ++q) ap[q] = dot2(dp[u][p], v[q], ap[q]);
       if constexpr (NS > 1) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) am[q] = dot2(dm[u][p], xv[q], am[q]);
+        for (int q = 0; q < G; ++q) am[q] = dot2(dm[u][p], v[q], am[q]);
       }
     }
-    const f32x4 g = *(const f32x4*)(sG + g_off(r, 8 * k + c.c8));
-    const int ao = a_off(r, 4 * k + (c.c8 >> 1)) + 4 * (c.c8 & 1);
-    typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
-    *(u32x2*)(abuf + ao) = u32x2{pack_bf16x2(ap[0] * g.x, ap[1] * g.y), pack_bf16x2(ap[2] * g.z, ap[3] * g.w)};
-    if constexpr (NS > 1)
-      *(u32x2*)(abuf + kAplane + ao) =
-          u32x2{pack_bf16x2(am[0] * g.x, am[1] * g.y), pack_bf16x2(am[2] * g.z, am[3] * g.w)};
+    float g[G];
+    load_gate<G>(sG, r, k, c.c8, g);
+    store_a<G>(abuf, r, k, c.c8, ap, g);
+    if constexpr (NS > 1) store_a<G>(abuf + Geo<L>::APLANE, r, k, c.c8, am, g);
   }
 }
 
@@ -575,23 +693,25 @@ __device__ inline void b_offsets(uint32_t (&boff)[ND][kNT]) {
 // spread over the first two thirds of the step's F MFMAs; the generator's D
 // dot products follow the last MFMA as one block, then the unit's gate,
 // rounding and LDS store.
-template <int ND, int NS>
+template <int L, int ND, int NS>
 struct StepState {
-  const u32x4* ap;                      // [kRT] + plane fragments
-  const u32x4* am;                      // [kRT] - plane fragments
+  typedef typename XVec<Geo<L>::GCH>::type XV;
+  static constexpr int RT = Geo<L>::RT, MP = Geo<L>::MP, G = Geo<L>::GCH;
+  const u32x4* ap;                      // [RT] + plane fragments
+  const u32x4* am;                      // [RT] - plane fragments
   const u32x4 (&b)[ND][n_bmat(NS - 1)][kNT];  // W0, or W1 and W2
-  f32x4 (&acc)[ND][NS][kNT][kRT];
-  const u32x4 (&xr)[kGR * kMaxPairs];
-  const uint32_t (&dp)[kGR][kMaxPairs];
-  const uint32_t (&dm)[kGR][kMaxPairs];
-  float (&vp)[kGR][4];
-  float (&vm)[kGR][4];
+  f32x4 (&acc)[ND][NS][kNT][RT];
+  const XV (&xr)[kGR * MP];
+  const uint32_t (&dp)[kGR][MP];
+  const uint32_t (&dm)[kGR][MP];
+  float (&vp)[kGR][G];
+  float (&vm)[kGR][G];
   // loads for the next K step, spread over the MFMAs of this one
   u32x4 (&bn)[ND][n_bmat(NS - 1)][kNT];  // B fragments of the next step
   __amdgpu_buffer_rsrc_t wrs;
   const uint32_t (&boff)[ND][kNT];
   uint32_t wsoff[2];                    // scalar offsets of the next step's W0 / W1 and W2 blocks
-  u32x4 (&xn)[kGR * kMaxPairs];         // gathers of the next generator unit
+  XV (&xn)[kGR * MP];                   // gathers of the next generator unit
   __amdgpu_buffer_rsrc_t xrs;
   uint32_t xoff[kGR];                   // per row; past the end for pairs beyond the unit's degree
   uint32_t xsoff;                       // scalar offset of the unit's pair 0
@@ -600,8 +720,8 @@ struct StepState {
 };
 
 // Load j of the next-step loads: first the B fragments, then the gathers.
-template <int ND, int NS, int J>
-__device__ __attribute__((always_inline)) inline void step_load(StepState<ND, NS>& st) {
+template <int L, int ND, int NS, int J>
+__device__ __attribute__((always_inline)) inline void step_load(StepState<L, ND, NS>& st) {
   constexpr int NBM = n_bmat(NS - 1);
   constexpr int NB = ND * NBM * kNT;
   if constexpr (J < NB) {
@@ -609,12 +729,13 @@ __device__ __attribute__((always_inline)) inline void step_load(StepState<ND, NS
     st.bn[di][sm][nt] = buffer_load16(st.wrs, st.boff[di][nt], st.wsoff[sm]);
   } else {
     constexpr int g = J - NB, p = g / kGR, u = g % kGR;
-    st.xn[g] = buffer_load16(st.xrs, p <= st.glp ? st.xoff[u] : st.oob, st.xsoff + (uint32_t)p * (kC * 4));
+    st.xn[g] = buffer_load_x<Geo<L>::GCH>(st.xrs, p <= st.glp ? st.xoff[u] : st.oob,
+                                          st.xsoff + (uint32_t)p * (kC * 4));
   }
 }
 
-template <int ND, int NS, int I>
-__device__ __attribute__((always_inline)) inline void step_mfma(StepState<ND, NS>& st) {
+template <int L, int ND, int NS, int I>
+__device__ __attribute__((always_inline)) inline void step_mfma(StepState<L, ND, NS>& st) {
   constexpr int PR = ND * kNT * NS * NS;  // MFMAs per row tile
   constexpr int rt = I / PR, j = I % PR;
   if constexpr (NS == 1) {
@@ -635,44 +756,45 @@ __device__ __attribute__((always_inline)) inline void step_mfma(StepState<ND, NS
   }
 }
 
-template <int ND, int NS, int D0, int D1>
-__device__ __attribute__((always_inline)) inline void step_dots(StepState<ND, NS>& st) {
+template <int L, int ND, int NS, int D0, int D1>
+__device__ __attribute__((always_inline)) inline void step_dots(StepState<L, ND, NS>& st) {
+  constexpr int G = Geo<L>::GCH;
   if constexpr (D0 < D1) {
-    constexpr int p = D0 / (4 * kGR * NS), r = D0 % (4 * kGR * NS);
-    constexpr int u = r / (4 * NS), q = (r / NS) % 4, sg = r % NS;
-    const u32x4 v = st.xr[kGR * p + u];
-    const uint32_t xv = q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+    constexpr int p = D0 / (G * kGR * NS), r = D0 % (G * kGR * NS);
+    constexpr int u = r / (G * NS), q = (r / NS) % G, sg = r % NS;
+    const typename XVec<G>::type v = st.xr[kGR * p + u];
+    const uint32_t xv = v[q];
     // pair 0 starts the sum: its accumulator input is the constant 0
     if constexpr (p == 0 && sg == 0) st.vp[u][q] = dot2_0(st.dp[u][p], xv);
     else if constexpr (p == 0) st.vm[u][q] = dot2_0(st.dm[u][p], xv);
     else if constexpr (sg == 0) st.vp[u][q] = dot2(st.dp[u][p], xv, st.vp[u][q]);
     else st.vm[u][q] = dot2(st.dm[u][p], xv, st.vm[u][q]);
-    step_dots<ND, NS, D0 + 1, D1>(st);
+    step_dots<L, ND, NS, D0 + 1, D1>(st);
   }
 }
 
-template <int ND, int NS, int I>
-__device__ __attribute__((always_inline)) inline void step_seq(StepState<ND, NS>& st) {
-  constexpr int F = ND * kNT * NS * NS * kRT;
-  constexpr int D = kMaxPairs * kGR * 4 * NS;
-  constexpr int NL = ND * n_bmat(NS - 1) * kNT + kGR * kMaxPairs;  // loads of the next step
+template <int L, int ND, int NS, int I>
+__device__ __attribute__((always_inline)) inline void step_seq(StepState<L, ND, NS>& st) {
+  constexpr int F = ND * kNT * NS * NS * Geo<L>::RT;
+  constexpr int D = Geo<L>::MP * kGR * Geo<L>::GCH * NS;
+  constexpr int NL = ND * n_bmat(NS - 1) * kNT + kGR * Geo<L>::MP;  // loads of the next step
   constexpr int SP = (2 * F / 3) / NL > 0 ? (2 * F / 3) / NL : 1;
   if constexpr (I < F) {
-    step_mfma<ND, NS, I>(st);
-    if constexpr (I % SP == 0 && I / SP < NL) step_load<ND, NS, I / SP>(st);
+    step_mfma<L, ND, NS, I>(st);
+    if constexpr (I % SP == 0 && I / SP < NL) step_load<L, ND, NS, I / SP>(st);
     if constexpr (I == F - 1) {
       // the dot products go after the step's last MFMA, as one block: on
       // gfx950 v_dot2_f32_bf16 does not overlap with MFMAs, and interleaving
       // the two measured about 10 % slower than issuing them in sequence
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(0);
-      step_dots<ND, NS, 0, D>(st);
+      step_dots<L, ND, NS, 0, D>(st);
     }
-    step_seq<ND, NS, I + 1>(st);
+    step_seq<L, ND, NS, I + 1>(st);
   } else if constexpr (I / SP < NL) {
     // more loads than MFMA slots: issue the rest
-    step_load<ND, NS, I / SP>(st);
-    step_seq<ND, NS, I + SP>(st);
+    step_load<L, ND, NS, I / SP>(st);
+    step_seq<L, ND, NS, I + SP>(st);
   }
 }
 
@@ -683,52 +805,49 @@ __device__ __attribute__((always_inline)) inline void step_seq(StepState<ND, NS>
 // generator unit (slice nk of a chunk of degree nglp) into xn.
 template <int L, int M, int LO, int ND>
 __device__ inline void fused_step(const uint16_t* abuf, int k, const u32x4 (&b)[ND][n_bmat(M)][kNT],
-                                  f32x4 (&acc)[ND][M ? 2 : 1][kNT][kRT], const float* sG, const Ctx& c,
-                                  const u32x4 (&xr)[kGR * kMaxPairs], const uint32_t (&dp)[kGR][kMaxPairs],
-                                  const uint32_t (&dm)[kGR][kMaxPairs], uint16_t* anext,
-                                  u32x4 (&bn)[ND][n_bmat(M)][kNT], __amdgpu_buffer_rsrc_t wrs,
-                                  const uint32_t (&boff)[ND][kNT], int nstep, u32x4 (&xn)[kGR * kMaxPairs],
+                                  f32x4 (&acc)[ND][M ? 2 : 1][kNT][Geo<L>::RT], const float* sG, const Ctx& c,
+                                  const typename XVec<Geo<L>::GCH>::type (&xr)[kGR * Geo<L>::MP],
+                                  const uint32_t (&dp)[kGR][Geo<L>::MP], const uint32_t (&dm)[kGR][Geo<L>::MP],
+                                  uint16_t* anext, u32x4 (&bn)[ND][n_bmat(M)][kNT], __amdgpu_buffer_rsrc_t wrs,
+                                  const uint32_t (&boff)[ND][kNT], int nstep,
+                                  typename XVec<Geo<L>::GCH>::type (&xn)[kGR * Geo<L>::MP],
                                   __amdgpu_buffer_rsrc_t xrs, int nglp, int nk, uint32_t oob) {
   constexpr int NS = M ? 2 : 1;
+  constexpr int RT = Geo<L>::RT, G = Geo<L>::GCH;
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15;
   const int grp = 4 * k + (lane >> 4);
-  u32x4 ap[kRT], am[kRT];
+  u32x4 ap[RT], am[RT];
 #pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     const int o = a_off(16 * rt + l16, grp);
     ap[rt] = *(const u32x4*)(abuf + o);
-    if constexpr (NS > 1) am[rt] = *(const u32x4*)(abuf + kAplane + o);
+    if constexpr (NS > 1) am[rt] = *(const u32x4*)(abuf + Geo<L>::APLANE + o);
   }
-  float vp[kGR][4], vm[kGR][4];  // every entry is first written by its pair-0 dot product
+  float vp[kGR][G], vm[kGR][G];  // every entry is first written by its pair-0 dot product
   // gates of the unit's rows and channels, read before the MFMAs so that the
   // LDS latency is hidden behind them
-  f32x4 gate[kGR];
+  float gate[kGR][G];
 #pragma unroll
-  for (int u = 0; u < kGR; ++u) gate[u] = *(const f32x4*)(sG + g_off(c.r0 + kGStride * u, 8 * k + c.c8));
+  for (int u = 0; u < kGR; ++u) load_gate<G>(sG, c.r0 + Geo<L>::M * u, k, c.c8, gate[u]);
   const uint32_t sb = 1024u * (uint32_t)nstep;
   uint32_t xo[kGR];
 #pragma unroll
   for (int u = 0; u < kGR; ++u) xo[u] = c.xoff[u];
-  StepState<ND, NS> st{ap, am, b, acc, xr, dp, dm, vp, vm,
-                       bn, wrs, boff, {bmat_byte<L, M>(0) + sb, bmat_byte<L, M>(1) + sb},
-                       xn, xrs, {}, (uint32_t)(pair_off(nglp) * kC + 32 * nk) * 4u, nglp, oob};
+  StepState<L, ND, NS> st{ap, am, b, acc, xr, dp, dm, vp, vm,
+                          bn, wrs, boff, {bmat_byte<L, M>(0) + sb, bmat_byte<L, M>(1) + sb},
+                          xn, xrs, {}, (uint32_t)(pair_off(nglp) * kC + 32 * nk) * 4u, nglp, oob};
 #pragma unroll
   for (int u = 0; u < kGR; ++u) st.xoff[u] = xo[u];
   // the MFMA part of the step runs at raised wave priority, the dot products
   // and LDS stores after it at normal priority (measured about 2 % faster)
   __builtin_amdgcn_s_setprio(1);
-  step_seq<ND, NS, 0>(st);
+  step_seq<L, ND, NS, 0>(st);
 #pragma unroll
   for (int u = 0; u < kGR; ++u) {
-    const int r = c.r0 + kGStride * u;
-    const f32x4 g = gate[u];
-    const int ao = a_off(r, 4 * k + (c.c8 >> 1)) + 4 * (c.c8 & 1);
-    typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
-    *(u32x2*)(anext + ao) = u32x2{pack_bf16x2(vp[u][0] * g.x, vp[u][1] * g.y), pack_bf16x2(vp[u][2] * g.z, vp[u][3] * g.w)};
-    if constexpr (NS > 1)
-      *(u32x2*)(anext + kAplane + ao) =
-          u32x2{pack_bf16x2(vm[u][0] * g.x, vm[u][1] * g.y), pack_bf16x2(vm[u][2] * g.z, vm[u][3] * g.w)};
+    const int r = c.r0 + Geo<L>::M * u;
+    store_a<G>(anext, r, k, c.c8, vp[u], gate[u]);
+    if constexpr (NS > 1) store_a<G>(anext + Geo<L>::APLANE, r, k, c.c8, vm[u], gate[u]);
   }
 }
 
@@ -756,9 +875,9 @@ template <int L, int PI>
 __device__ inline void aprime_build(char* smem, u32x4* frag) {
   constexpr PassInfo pi = pass_info(L, PI);
   constexpr int M = pi.M, LO = pi.LO;
-  constexpr int STEPS = M == 0 ? kRT / 2 : kRT;
+  constexpr int STEPS = M == 0 ? Geo<L>::RT / 2 : Geo<L>::RT;
   constexpr int TOTAL = frag_count(L, PI);
-  const Smem& S = *(const Smem*)smem;
+  const Smem<L>& S = *(const Smem<L>*)smem;
   const uint32_t* sD = (const uint32_t*)(smem + Lds<L>::kD);
   const int lane = threadIdx.x & 63;
   const int g4 = lane >> 4;
@@ -802,21 +921,22 @@ __device__ inline void aprime_build(char* smem, u32x4* frag) {
 }
 
 template <int L, int NS, int l>
-__device__ inline void rot_back(char* smem, const Ctx& c, const f32x4 (&yt)[NS][kNT][kRT], const u32x4* frag,
+__device__ inline void rot_back(char* smem, const Ctx& c, const f32x4 (&yt)[NS][kNT][Geo<L>::RT], const u32x4* frag,
                                 f32x4 (&T)[Cfg<L>::TT][kNT]) {
+  constexpr int RT = Geo<L>::RT;
   const float* sW = (const float*)(smem + Lds<L>::kW);
   const int lane = threadIdx.x & 63;
   const int g4 = lane >> 4;
   constexpr bool M0 = NS == 1;
-  constexpr int kSteps = M0 ? kRT / 2 : kRT;
+  constexpr int kSteps = M0 ? RT / 2 : RT;
   constexpr int ot0 = (kSlots * l * l) / 16;
-  u32x4 bq[kNT][kRT];
+  u32x4 bq[kNT][RT];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
       // weights of this lane's 4 edge rows for the head of column tile nt
-      const f32x4 wv = *(const f32x4*)(sW + c.head[nt] * kM + 16 * rt + 4 * g4);
+      const f32x4 wv = *(const f32x4*)(sW + c.head[nt] * Geo<L>::M + 16 * rt + 4 * g4);
       const float w4[4] = {wv.x, wv.y, wv.z, wv.w};
       if constexpr (!M0) {
         const f32x4 yp = yt[0][nt][rt], ym = yt[NS - 1][nt][rt];
@@ -849,9 +969,9 @@ __device__ inline void rot_back(char* smem, const Ctx& c, const f32x4 (&yt)[NS][
 }
 
 template <int L, int M, int LO, int DI, int ND>
-__device__ inline void rot_back_all(char* smem, const Ctx& c, const f32x4 (&acc)[ND][M ? 2 : 1][kNT][kRT],
+__device__ inline void rot_back_all(char* smem, const Ctx& c, const f32x4 (&acc)[ND][M ? 2 : 1][kNT][Geo<L>::RT],
                                     const u32x4* frag, f32x4 (&T)[Cfg<L>::TT][kNT]) {
-  constexpr int STEPS = M == 0 ? kRT / 2 : kRT;
+  constexpr int STEPS = M == 0 ? Geo<L>::RT / 2 : Geo<L>::RT;
   rot_back<L, M ? 2 : 1, LO + DI>(smem, c, acc[DI], frag, T);
   if constexpr (DI + 1 < ND)
     rot_back_all<L, M, LO, DI + 1, ND>(smem, c, acc, frag + deg_tiles(LO + DI) * STEPS * 64, T);
@@ -892,9 +1012,11 @@ __device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams&
                                                                f32x4 (&T)[Cfg<L>::TT][kNT],
                                                                u32x4 (&ring)[2][pass_info(L, PI).ND]
                                                                             [n_bmat(pass_info(L, PI).M)][kNT],
-                                                               u32x4 (&xa)[kGR * kMaxPairs], u32x4 (&xb)[kGR * kMaxPairs]) {
+                                                               typename XVec<Geo<L>::GCH>::type (&xa)[kGR * Geo<L>::MP],
+                                                               typename XVec<Geo<L>::GCH>::type (&xb)[kGR * Geo<L>::MP]) {
   constexpr PassInfo pi = pass_info(L, PI), pn = pass_info(L, PI + 1);
   constexpr int M = pi.M, LO = pi.LO, ND = pi.ND, NS = M ? 2 : 1;
+  constexpr int RT = Geo<L>::RT, MP = Geo<L>::MP;
   constexpr int NCH = L + 1 - M, NSTEP = 4 * NCH;
   constexpr int PAR = chunks_before(L, PI) & 1;
   const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(P.wf, P.w_bytes);
@@ -911,7 +1033,7 @@ __device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams&
   __syncthreads();  // chunk 0 written; every wave is done with the previous A'
   aprime_build<L, PI>(smem, frag);
 
-  f32x4 acc[ND][NS][kNT][kRT];
+  f32x4 acc[ND][NS][kNT][RT];
 #pragma unroll
   for (int a = 0; a < ND; ++a)
 #pragma unroll
@@ -919,9 +1041,9 @@ __device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams&
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) acc[a][b][nt][rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int rt = 0; rt < RT; ++rt) acc[a][b][nt][rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  uint32_t dp[kGR][kMaxPairs], dm[kGR][kMaxPairs];
+  uint32_t dp[kGR][MP], dm[kGR][MP];
   int glp = 0;
 #pragma nounroll
   for (int s = 0; s < NSTEP; s += 2) {
@@ -930,7 +1052,7 @@ __device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams&
     if (k == 0) {
       int gm;
       gen_target<L, PI>(q, gm, glp);
-      gen_dpairs(sD, Cfg<L>::DPW, c, gm, glp, dp, dm);
+      gen_dpairs<L>(sD, c, gm, glp, dp, dm);
     }
     // degree of the chunk whose generator unit 0 is gathered in step s + 1
     int glp2 = glp;
@@ -938,8 +1060,8 @@ __device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams&
       int gm2;
       gen_target<L, PI>(q + 1 < NCH ? q + 1 : q, gm2, glp2);
     }
-    const uint16_t* acur = abase + ((PAR + q) & 1) * kAbuf;
-    uint16_t* anext = abase + ((PAR + q + 1) & 1) * kAbuf;
+    const uint16_t* acur = abase + ((PAR + q) & 1) * Geo<L>::ABUF;
+    uint16_t* anext = abase + ((PAR + q + 1) & 1) * Geo<L>::ABUF;
     // K step s: unit k from xa; loads B of step s + 1 and the gathers of unit k + 1
     fused_step<L, M, LO, ND>(acur, k, ring[0], acc, sG, c, xa, dp, dm, anext, ring[1], wrs, boff, s + 1, xb, xrs,
                              glp, k + 1, oob);
@@ -958,7 +1080,7 @@ __device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams&
     // gathers of generator unit 0 for the next pass's chunk 0 target
     int gm, glp0;
     gen_target<L, PI + 1>(0, gm, glp0);
-    gen_issue(xrs, c, oob, glp0, 0, xa);
+    gen_issue<L>(xrs, c, oob, glp0, 0, xa);
     rot_back_all<L, M, LO, 0, ND>(smem, c, acc, frag, T);
     run_pass<L, PI + 1>(P, smem, c, T, nring, xa, xb);
   } else {
@@ -985,7 +1107,7 @@ __device__ inline uint16_t row_info(int R, int TROWS) {
 // nothing to write store past the end of a buffer descriptor that covers
 // the chunk's (at most kSlots) target rows of y.
 template <int L>
-__device__ inline void flush_slots(const MfmaParams& P, const Smem& S, int t_first, f32x4 (&T)[Cfg<L>::TT][kNT]) {
+__device__ inline void flush_slots(const MfmaParams& P, const Smem<L>& S, int t_first, f32x4 (&T)[Cfg<L>::TT][kNT]) {
   constexpr int NC = Cfg<L>::NC;
   constexpr uint32_t kRow = NC * kC * 4;  // bytes of one target row of y
   if (S.flush_t[0] < 0 && S.flush_t[1] < 0 && S.flush_t[2] < 0 && S.flush_t[3] < 0) return;
@@ -1042,11 +1164,11 @@ __host__ __device__ inline int xcd_first(int x, int n_groups) {
 // chunks, most first (stable), so that the hardware, which hands the
 // workgroups of an XCD to its compute units in launch order, starts the
 // long groups first and the makespan stays close to the mean.  The chunk
-// count repeats the fused kernel's chunking: at most kM edges and kSlots
-// consecutive targets per chunk.
+// count repeats the fused kernel's chunking: at most chunk_m edges and
+// kSlots consecutive targets per chunk.
 constexpr int kOrderBuckets = 32;  // chunk counts above 31 share the top bucket
 __global__ void __launch_bounds__(256) attn_order_kernel(const int32_t* __restrict__ row_ptr, int n_targets,
-                                                         int n_groups, int32_t* __restrict__ gs,
+                                                         int n_groups, int chunk_m, int32_t* __restrict__ gs,
                                                          int32_t* __restrict__ bucket,
                                                          int32_t* __restrict__ order) {
   __shared__ int hist[kOrderBuckets][257];  // [bucket][thread]: counts, then scatter positions
@@ -1067,7 +1189,7 @@ __global__ void __launch_bounds__(256) attn_order_kernel(const int32_t* __restri
     while (e < e_end) {
       while (row_ptr[tc + 1] <= e) ++tc;
       const int t_lim = min(tc + kSlots, t_end);
-      e = min(min(e + kM, e_end), row_ptr[t_lim]);
+      e = min(min(e + chunk_m, e_end), row_ptr[t_lim]);
       ++chunks;
     }
     const int bk = kOrderBuckets - 1 - min(chunks, kOrderBuckets - 1);  // bucket 0: most chunks
@@ -1105,7 +1227,7 @@ template <int L>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 attn_mfma_kernel(MfmaParams P, int n_groups) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  Smem& S = *(Smem*)smem;
+  Smem<L>& S = *(Smem<L>*)smem;
   uint32_t* sD = (uint32_t*)(smem + Lds<L>::kD);
   float* sG = (float*)(smem + Lds<L>::kG);
   float* sW = (float*)(smem + Lds<L>::kW);
@@ -1116,6 +1238,8 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
   constexpr int NC = Cfg<L>::NC;
   constexpr PassInfo p0 = pass_info(L, 0);
   constexpr int NS0 = p0.M ? 2 : 1;
+  constexpr int CM = Geo<L>::M, GL = Geo<L>::GL, MP = Geo<L>::MP;
+  typedef typename XVec<Geo<L>::GCH>::type XV;
 
   // Workgroup -> group of consecutive targets holding about E / n_groups
   // edges (group g starts at the first target whose edges start at or after
@@ -1132,7 +1256,7 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
     if (P.row_ptr[t] == P.row_ptr[t + 1])
       for (int a = tid & 63; a < NC * kC; a += 64) P.y[(int64_t)t * NC * kC + a] = 0.0f;
 
-  static_assert(16 * Cfg<L>::TT <= 112, "row table");
+  static_assert(16 * Cfg<L>::TT <= (int)(sizeof(S.rowinfo) / sizeof(S.rowinfo[0])), "row table");
   if (tid < 16 * Cfg<L>::TT) S.rowinfo[tid] = row_info(tid, Cfg<L>::TROWS);
 
   f32x4 T[Cfg<L>::TT][kNT];
@@ -1152,8 +1276,8 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
   const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(P.xp, P.xp_bytes);
 
   Ctx c;
-  c.r0 = tid >> 3;
-  c.c8 = tid & 7;
+  c.r0 = tid / GL;
+  c.c8 = tid % GL;
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) c.head[nt] = (16 * kNT * wave + 16 * nt + (tid & 15)) / dh;
 
@@ -1161,7 +1285,7 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
     while (P.row_ptr[t_cur + 1] <= e) ++t_cur;  // target of edge e
     const int t_first = t_cur;
     const int t_lim = min(t_first + kSlots, t_end);
-    const int e_stop = min(min(e + kM, e_end), P.row_ptr[t_lim]);
+    const int e_stop = min(min(e + CM, e_end), P.row_ptr[t_lim]);
     const int nrows = e_stop - e;
 
     // B fragments of the first pass's first K step go out before the setup
@@ -1182,10 +1306,10 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
       S.flush_t[tid] = (t <= t_first + sl && S.rp[t - t_first + 1] <= e_stop) ? t : -1;
     }
     {
-      // 8 lanes per edge row: lane hs of row r computes the row's geometry,
-      // the radial basis functions hs, hs + 8, ... and the softmax weights
-      // of heads hs, hs + 8; lane 0 of the row stores the row metadata
-      const int r = tid >> 3, hs = tid & 7;
+      // GL lanes per edge row: lane hs of row r computes the row's geometry,
+      // the radial basis functions hs, hs + GL, ... and the softmax weights
+      // of heads hs, hs + GL; lane 0 of the row stores the row metadata
+      const int r = tid / GL, hs = tid % GL;
       int jr = -1;  // source atom of row r
       if (r < nrows) {
         int t, j;
@@ -1202,12 +1326,12 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
         // Gaussian radial basis of this edge (centres k rc/(K-1), width rc/(K-1))
         const float step = rc / (float)(P.K - 1);
         const float inv2s2 = 1.0f / (2.0f * step * step);
-        for (int kk = hs; kk < ((P.K + 7) & ~7); kk += 8) {
+        for (int kk = hs; kk < ((P.K + 7) & ~7); kk += GL) {
           const float dr = rho - step * (float)kk;
           sPhi[r * kMaxRbf + kk] = kk < P.K ? expf(-dr * dr * inv2s2) : 0.0f;
         }
         const float u = envelope_u(rho / rc, P.p);
-        for (int h = hs; h < H; h += 8) {
+        for (int h = hs; h < H; h += GL) {
           const f32x4* qv = (const f32x4*)(P.q + (int64_t)t * kC + h * dh);
           const f32x4* kv = (const f32x4*)(P.k + (int64_t)j * kC + h * dh);
           float z = 0.0f;
@@ -1216,7 +1340,7 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
             z += qa.x * kb.x + qa.y * kb.y + qa.z * kb.z + qa.w * kb.w;
           }
           z *= inv_sqrt_d;
-          sW[h * kM + r] = u * expf(z - P.stat_max[(int64_t)t * H + h]) * P.stat_inv[(int64_t)t * H + h];
+          sW[h * CM + r] = u * expf(z - P.stat_max[(int64_t)t * H + h]) * P.stat_inv[(int64_t)t * H + h];
         }
       } else {
         if (hs == 0) {
@@ -1225,41 +1349,46 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
           S.row_t[r] = t_first;
           S.row_rv[r] = f32x4{0.0f, 0.0f, 1.0f, 0.0f};
         }
-        for (int kk = hs; kk < ((P.K + 7) & ~7); kk += 8) sPhi[r * kMaxRbf + kk] = 0.0f;
-        for (int h = hs; h < H; h += 8) sW[h * kM + r] = 0.0f;
+        for (int kk = hs; kk < ((P.K + 7) & ~7); kk += GL) sPhi[r * kMaxRbf + kk] = 0.0f;
+        for (int h = hs; h < H; h += GL) sW[h * CM + r] = 0.0f;
       }
       // the generator row of this lane is r (kGR = 1)
-      static_assert(kGR == 1 && kGStride == kM, "one generator row per lane, the phase A1 row");
-      c.xoff[0] = jr >= 0 ? ((uint32_t)jr * Cfg<L>::NP * kC + 4 * c.c8) * 4u : P.xp_bytes;
+      static_assert(kGR == 1, "one generator row per lane, the phase A1 row");
+      c.xoff[0] = jr >= 0 ? ((uint32_t)jr * Cfg<L>::NP * kC + Geo<L>::GCH * c.c8) * 4u : P.xp_bytes;
     }
     __syncthreads();
 
     // gathers of the first A chunk's generator units 0 and 1, which land
     // during phase A2
-    u32x4 xa[kGR * kMaxPairs], xb[kGR * kMaxPairs];
-    gen_issue(xrs, c, P.xp_bytes, p0.M, 0, xa);
-    gen_issue(xrs, c, P.xp_bytes, p0.M, 1, xb);
+    XV xa[kGR * MP], xb[kGR * MP];
+    gen_issue<L>(xrs, c, P.xp_bytes, p0.M, 0, xa);
+    gen_issue<L>(xrs, c, P.xp_bytes, p0.M, 1, xb);
 
     // ---- phase A2: wave 0 the Wigner-D pairs of its edge row; waves 1..7
     // the radial gates: lane (channel quad cq, row phase rg) owns rows rg,
     // rg + NRG, ...; the w_rad columns of its 4 channels stream through
     // registers 8 basis functions at a time and meet every owned row
-    if (tid < kM) {
+    float* s1 = (float*)(smem + Lds<L>::kS1);
+    float* s4 = (float*)(smem + Lds<L>::kS4);
+    float* s5 = (float*)(smem + Lds<L>::kS5);
+    if (tid < 64) {
       const int r = tid;
-      uint32_t* dr = sD + r * Cfg<L>::DPW;
-      if (r < nrows) {
-        const f32x4 v = S.row_rv[r];
-        const float inv = v.w > 0.0f ? 1.0f / v.w : 0.0f;
-        float R[9];
-        edge_frame(v.x * inv, v.y * inv, v.z * inv, R);
-        wigner_pairs<L>(R, dr);
-      } else {
-        for (int q = 0; q < Cfg<L>::DPW; ++q) dr[q] = 0u;
+      if (r < CM) {
+        uint32_t* dr = sD + r * Cfg<L>::DPW;
+        if (r < nrows) {
+          const f32x4 v = S.row_rv[r];
+          const float inv = v.w > 0.0f ? 1.0f / v.w : 0.0f;
+          float R[9];
+          edge_frame(v.x * inv, v.y * inv, v.z * inv, R);
+          wigner_pairs<L>(R, dr, s1 + 9 * r, s4 + 81 * r);
+        } else {
+          for (int q = 0; q < Cfg<L>::DPW; ++q) dr[q] = 0u;
+        }
       }
     } else {
-      const int tw = tid - kM;  // 0 .. kThreads - kM - 1
-      constexpr int NRG = (kThreads - kM) / (kC / 4);
-      constexpr int kGRows = (kM + NRG - 1) / NRG;
+      const int tw = tid - 64;  // 0 .. kThreads - 65
+      constexpr int NRG = (kThreads - 64) / (kC / 4);
+      constexpr int kGRows = (CM + NRG - 1) / NRG;
       const int cq = tw % (kC / 4), rg = tw / (kC / 4);
       if (rg < NRG) {
         f32x4 g[kGRows];
@@ -1275,7 +1404,7 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
 #pragma unroll
             for (int i = 0; i < kGRows; ++i) {
               const int r = rg + NRG * i;
-              if (r < kM) {
+              if (r < CM) {
                 const f32x4 f0 = *(const f32x4*)(sPhi + r * kMaxRbf + k0);
                 const f32x4 f1 = *(const f32x4*)(sPhi + r * kMaxRbf + k0 + 4);
                 g[i] += f0.x * w4[0] + f0.y * w4[1] + f0.z * w4[2] + f0.w * w4[3] +
@@ -1288,7 +1417,7 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
 #pragma unroll
         for (int i = 0; i < kGRows; ++i) {
           const int r = rg + NRG * i;
-          if (r < kM) {
+          if (r < CM) {
             f32x4 gi = g[i];
             if (r >= nrows) gi = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             else if (P.flags & SO2_FLAG_NO_RADIAL) gi = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
@@ -1300,20 +1429,38 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
     }
     __syncthreads();
 
+    if constexpr (L >= 5) {
+      // ---- phase A3 (L >= 5): D^5 and D^6 row by row, lane (row a, edge
+      // er) of all waves, from the fp32 D^1, D^4 (and D^5) staged in the
+      // idle A buffers; rows past the chunk's edges stay zero
+      const int er = tid % CM, a = tid / CM;
+      float D1[9];
+      if (er < nrows) {
+#pragma unroll
+        for (int q = 0; q < 9; ++q) D1[q] = s1[9 * er + q];
+        wigner_row_any<5, 0, (L >= 6)>(a, D1, s4 + 81 * er, sD + er * Cfg<L>::DPW, s5 + 121 * er);
+      }
+      __syncthreads();
+      if constexpr (L >= 6) {
+        if (er < nrows) wigner_row_any<6, 0, false>(a, D1, s5 + 121 * er, sD + er * Cfg<L>::DPW, nullptr);
+        __syncthreads();
+      }
+    }
+
     // ---- first A chunk (block p0.M, degree p0.M): all four generator units
     {
-      uint32_t dp[kGR][kMaxPairs], dm[kGR][kMaxPairs];
-      gen_dpairs(sD, Cfg<L>::DPW, c, p0.M, p0.M, dp, dm);
-      gen_finish<NS0>(sG, c, 0, xa, dp, dm, abase);  // chunks_before(L, 0) = 0
-      gen_issue(xrs, c, P.xp_bytes, p0.M, 2, xa);
-      gen_finish<NS0>(sG, c, 1, xb, dp, dm, abase);
-      gen_issue(xrs, c, P.xp_bytes, p0.M, 3, xb);
-      gen_finish<NS0>(sG, c, 2, xa, dp, dm, abase);
+      uint32_t dp[kGR][MP], dm[kGR][MP];
+      gen_dpairs<L>(sD, c, p0.M, p0.M, dp, dm);
+      gen_finish<L, NS0>(sG, c, 0, xa, dp, dm, abase);  // chunks_before(L, 0) = 0
+      gen_issue<L>(xrs, c, P.xp_bytes, p0.M, 2, xa);
+      gen_finish<L, NS0>(sG, c, 1, xb, dp, dm, abase);
+      gen_issue<L>(xrs, c, P.xp_bytes, p0.M, 3, xb);
+      gen_finish<L, NS0>(sG, c, 2, xa, dp, dm, abase);
       // gathers of generator unit 0 for chunk 0's target
       int gm, glp;
       gen_target<L, 0>(0, gm, glp);
-      gen_issue(xrs, c, P.xp_bytes, glp, 0, xa);
-      gen_finish<NS0>(sG, c, 3, xb, dp, dm, abase);
+      gen_issue<L>(xrs, c, P.xp_bytes, glp, 0, xa);
+      gen_finish<L, NS0>(sG, c, 3, xb, dp, dm, abase);
 
       // ---- phase B: every pass, each ending in its rotate-back GEMMs
       run_pass<L, 0>(P, smem, c, T, ring, xa, xb);
@@ -1336,7 +1483,7 @@ so2_status launch_L(const MfmaParams& P, int32_t* bucket, int64_t n_edges, hipSt
   want = ((want + n_cu - 1) / n_cu) * n_cu;
   const int n_groups = (int)std::max<int64_t>(1, std::min<int64_t>(want, P.n_targets));
   hipLaunchKernelGGL(attn_order_kernel, dim3(8), dim3(256), 0, stream, P.row_ptr, P.n_targets, n_groups,
-                     const_cast<int32_t*>(P.gs), bucket, const_cast<int32_t*>(P.order));
+                     Geo<L>::M, const_cast<int32_t*>(P.gs), bucket, const_cast<int32_t*>(P.order));
   SO2_CHECK_LAUNCH();
   const size_t smem = Lds<L>::kTotal;
   static_assert(Lds<L>::kTotal <= 160 * 1024, "LDS budget");
@@ -1417,7 +1564,7 @@ bool mfma_supported(int L, int C, int H, int K, int n_atoms) {
   // the x pairs are addressed through a 32-bit buffer descriptor, with room
   // past the end for the zero reads of rows without an edge
   const uint64_t xp_bytes = (uint64_t)n_atoms * pair_off(L + 1) * C * 4;
-  return C == kC && L >= 1 && L <= 4 && H >= 1 && H <= kMaxHeads && C % H == 0 && K <= kMaxRbf &&
+  return C == kC && L >= 1 && L <= 6 && H >= 1 && H <= kMaxHeads && C % H == 0 && K <= kMaxRbf &&
          xp_bytes < 0xffff0000ull;
 }
 
@@ -1445,6 +1592,12 @@ so2_status launch_attention_mfma_prep(const AttnArgs& a, hipStream_t stream) {
     case 4:
       st = launch_pack_L<4>(a, P, stream);
       break;
+    case 5:
+      st = launch_pack_L<5>(a, P, stream);
+      break;
+    case 6:
+      st = launch_pack_L<6>(a, P, stream);
+      break;
     default:
       return SO2_ERR_UNSUPPORTED;
   }
@@ -1467,6 +1620,10 @@ so2_status launch_attention_mfma(const AttnArgs& a, hipStream_t stream) {
       return launch_L<3>(P, bucket, a.n_edges, stream);
     case 4:
       return launch_L<4>(P, bucket, a.n_edges, stream);
+    case 5:
+      return launch_L<5>(P, bucket, a.n_edges, stream);
+    case 6:
+      return launch_L<6>(P, bucket, a.n_edges, stream);
   }
   return SO2_ERR_UNSUPPORTED;
 }

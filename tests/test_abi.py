@@ -152,6 +152,11 @@ def test_attention_pointer_box_and_workspace_errors():
 def test_kernel_kind_selection():
     assert sea.attention_kernel_kind(_desc()) == sea.KERNEL_VALU
     assert sea.attention_kernel_kind(_desc(l_max=7)) == sea.KERNEL_NONE
+    for L in range(1, 7):
+        d = _desc(l_max=L, channels=128, heads=8, n_rbf=16, dtype=sea.SO2_BF16)
+        assert sea.attention_kernel_kind(d) == sea.KERNEL_MFMA
+    assert sea.attention_kernel_kind(_desc(l_max=0, channels=128, heads=8, dtype=sea.SO2_BF16)) == sea.KERNEL_VALU
+    assert sea.attention_kernel_kind(_desc(l_max=6, channels=128, heads=8, dtype=sea.SO2_FP32)) == sea.KERNEL_VALU
 
 
 def test_neighbor_errors_before_launch():

@@ -211,15 +211,15 @@ def _kind(w, n_edges=1000):
     return sea.attention_kernel_kind(d)
 
 
-@pytest.mark.parametrize("name", ["small_molecules", "solvated_protein", "water_100k"])
-def test_l4_workloads_run_on_the_mfma_kernel(name):
+@pytest.mark.parametrize("name", ["small_molecules", "water_l6", "solvated_protein", "water_100k"])
+def test_bf16_workloads_run_on_the_mfma_kernel(name):
     import so_equivariant_graph_amd as sea
 
     w = make_workload(name, with_features=False)
     assert _kind(w) == sea.KERNEL_MFMA
 
 
-@pytest.mark.parametrize("L", [1, 2, 3, 4])
+@pytest.mark.parametrize("L", [1, 2, 3, 4, 5, 6])
 def test_mfma_every_degree(L):
     say("mfma L", L)
     import so_equivariant_graph_amd as sea
@@ -232,11 +232,12 @@ def test_mfma_every_degree(L):
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("L,K", [(1, 8), (2, 8), (2, 12), (2, 24), (3, 8), (3, 20)])
+@pytest.mark.parametrize("L,K", [(1, 8), (2, 8), (2, 12), (2, 24), (3, 8), (3, 20), (5, 8), (6, 24)])
 def test_mfma_degree_and_rbf_counts(L, K):
     """Degrees below 4 leave some of the five component-pair slots of a lane
     unused and basis counts other than 16 change the gate and rotation data
-    next to the Wigner-D rows: every output must stay finite and match."""
+    next to the Wigner-D rows (32-edge chunks for L = 5, 6): every output
+    must stay finite and match."""
     say("mfma L", L, "n_rbf", K)
     w = make_workload("tiny_fp32", l_max=L, channels=128, heads=8, n_rbf=K, dtype="bf16")
     y, y_ref = _run_pair(w)
@@ -262,32 +263,37 @@ def test_mfma_flags(flags):
     assert max_rel_error(y, y_ref) <= TOL["bf16"]
 
 
-def test_mfma_ragged_degrees_and_split_targets():
-    """Degrees 0, 1, 2 and > 64 (one target spanning several 64-edge chunks),
-    a target count that is not a multiple of the 16-target group, and
-    n_targets < n_atoms."""
-    say("mfma ragged degrees")
+@pytest.mark.parametrize("L", [4, 6])
+def test_mfma_ragged_degrees_and_split_targets(L):
+    """Degrees 0, 1, 2 and > 64 (one target spanning several 64- or 32-edge
+    chunks), a target count that is not a multiple of the 16-target group,
+    and n_targets < n_atoms."""
+    say("mfma ragged degrees, L", L)
     import torch
 
     rng = np.random.default_rng(7)
-    dense = rng.uniform(0, 4.0, size=(90, 3))  # about 90 neighbours each within rc = 5
+    chunk = 64 if L <= 4 else 32
+    # a dense cluster: neighbours within rc = 5 well above one chunk per target
+    dense = rng.uniform(0, 4.0, size=(90 if L <= 4 else 50, 3))
     sparse = np.array([[50, 0, 0], [53, 0, 0], [50, 4, 0], [80, 0, 0], [90, 0, 0], [93.5, 0, 0], [150, 0, 0]], float)
     pos = np.vstack([dense, sparse, rng.uniform(200, 210, size=(40, 3))])
-    w = make_workload("tiny_fp32", l_max=4, channels=128, heads=8, n_rbf=16, dtype="bf16")
+    w = make_workload("tiny_fp32", l_max=L, channels=128, heads=8, n_rbf=16, dtype="bf16")
     from synth import to_bf16_exact
 
     n = pos.shape[0]
     w.pos = pos.astype(np.float32)
-    w.x = to_bf16_exact(rng.standard_normal((n, 25, 128)).astype(np.float32))
+    w.x = to_bf16_exact(rng.standard_normal((n, (L + 1) ** 2, 128)).astype(np.float32))
     rp, col = neighbors_bruteforce(w.pos, w.cutoff)
     deg = np.diff(rp)
-    assert deg.max() > 64 and (deg == 0).any() and (deg == 1).any()
+    assert deg.max() > chunk and (deg == 0).any() and (deg == 1).any()
     y, y_ref = _run_pair(w)
     err = max_rel_error(y, y_ref)
     say("max rel err", err, "max deg", deg.max())
     assert err <= TOL["bf16"]
     assert np.all(y[deg == 0] == 0.0)
     d = device_inputs(w)
-    y_part = gpu_attention(w, d, *csr_to_device(rp, col), n_targets=101)
+    nt = n - 36  # 101 (L = 4) or 61 (L = 6) targets, not a multiple of 16
+    y_part = gpu_attention(w, d, *csr_to_device(rp, col), n_targets=nt)
     torch.cuda.synchronize()
-    assert max_rel_error(y_part.cpu().numpy(), y_ref[:101]) <= TOL["bf16"]
+    assert y_part.shape[0] == nt
+    assert max_rel_error(y_part.cpu().numpy(), y_ref[:nt]) <= TOL["bf16"]
