@@ -15,7 +15,8 @@
 // (v_mfma_f32_16x16x32_bf16):
 //
 //   edges are the M dimension: a chunk holds up to 64 consecutive edges of
-//   the CSR (4 row tiles of 16), crossing target boundaries;
+//   the CSR (4 row tiles of 16; 32 edges and 2 row tiles for L = 5, 6),
+//   crossing target boundaries;
 //   for block m the A operand is the rotated, gated input rows (l', +-m) of
 //   those edges, built on the vector ALUs and staged through LDS in bf16,
 //   one degree l' (128 channels, 4 K steps of 32) per A chunk;
@@ -44,7 +45,7 @@
 // [16w, 16w+16).  Each
 // workgroup takes a run of consecutive target atoms holding about the same
 // number of edges as every other workgroup; its edges are processed in
-// chunks of at most 64 edges whose targets span at most 4 consecutive
+// chunks of at most 64 (32) edges whose targets span at most 4 consecutive
 // indices (4 accumulator slots, slot = target mod 4); a target whose edges
 // continue into the next chunk keeps its slot, a target whose last edge is
 // in the chunk is written out and its slot cleared.
