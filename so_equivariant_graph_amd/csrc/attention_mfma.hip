@@ -182,14 +182,12 @@ __device__ inline float dot2(unsigned int a, unsigned int b, float c) {
                                          false);
 }
 
-// a.lo * b.lo + a.hi * b.hi in one instruction: the three-operand encoding
-// with the constant 0 as accumulator (the builtin with c = 0 becomes a move
-// of 0 plus the two-operand accumulating form).
-__device__ inline float dot2_0(unsigned int a, unsigned int b) {
-  float r;
-  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
+// a.lo * b.lo + a.hi * b.hi.  Written with the builtin (a move of 0 plus
+// the accumulating form), not as inline asm: the compiler cannot see the
+// registers an asm statement writes when it inserts the wait states that
+// keep a VALU write off the operands and result registers of an MFMA still
+// in flight.
+__device__ inline float dot2_0(unsigned int a, unsigned int b) { return dot2(a, b, 0.0f); }
 
 // Raw buffer descriptor (gfx9 family: dword3 = 0x00020000).  Loads through
 // it take one 32-bit VGPR offset plus a scalar offset and return 0 past
@@ -718,6 +716,7 @@ struct StepState {
   uint32_t xsoff;                       // scalar offset of the unit's pair 0
   int glp;                              // degree of the next unit's chunk
   uint32_t oob;
+  int dglp;                             // degree of this step's unit: pairs 0..dglp are nonzero
 };
 
 // Load j of the next-step loads: first the B fragments, then the gathers.
@@ -774,10 +773,23 @@ __device__ __attribute__((always_inline)) inline void step_dots(StepState<L, ND,
   }
 }
 
+// The dot products of pairs P, P + 1, ... up to the unit's degree: the pairs
+// past it hold zeros on both sides, so they are skipped (a wave-uniform
+// branch per pair; the unit's degree is the same for every lane).
+template <int L, int ND, int NS, int P>
+__device__ __attribute__((always_inline)) inline void step_dots_pairs(StepState<L, ND, NS>& st) {
+  constexpr int PD = Geo<L>::GCH * kGR * NS;  // dot products per pair
+  if constexpr (P < Geo<L>::MP) {
+    if (P == 0 || P <= st.dglp) {
+      step_dots<L, ND, NS, P * PD, (P + 1) * PD>(st);
+      step_dots_pairs<L, ND, NS, P + 1>(st);
+    }
+  }
+}
+
 template <int L, int ND, int NS, int I>
 __device__ __attribute__((always_inline)) inline void step_seq(StepState<L, ND, NS>& st) {
   constexpr int F = ND * kNT * NS * NS * Geo<L>::RT;
-  constexpr int D = Geo<L>::MP * kGR * Geo<L>::GCH * NS;
   constexpr int NL = ND * n_bmat(NS - 1) * kNT + kGR * Geo<L>::MP;  // loads of the next step
   constexpr int SP = (2 * F / 3) / NL > 0 ? (2 * F / 3) / NL : 1;
   if constexpr (I < F) {
@@ -789,7 +801,7 @@ __device__ __attribute__((always_inline)) inline void step_seq(StepState<L, ND, 
       // the two measured about 10 % slower than issuing them in sequence
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(0);
-      step_dots<L, ND, NS, 0, D>(st);
+      step_dots_pairs<L, ND, NS, 0>(st);
     }
     step_seq<L, ND, NS, I + 1>(st);
   } else if constexpr (I / SP < NL) {
@@ -805,7 +817,7 @@ __device__ __attribute__((always_inline)) inline void step_seq(StepState<L, ND, 
 // its B fragments (step nstep) into bn and the gathers of the next
 // generator unit (slice nk of a chunk of degree nglp) into xn.
 template <int L, int M, int LO, int ND>
-__device__ inline void fused_step(const uint16_t* abuf, int k, const u32x4 (&b)[ND][n_bmat(M)][kNT],
+__device__ inline void fused_step(const uint16_t* abuf, int k, int dglp, const u32x4 (&b)[ND][n_bmat(M)][kNT],
                                   f32x4 (&acc)[ND][M ? 2 : 1][kNT][Geo<L>::RT], const float* sG, const Ctx& c,
                                   const typename XVec<Geo<L>::GCH>::type (&xr)[kGR * Geo<L>::MP],
                                   const uint32_t (&dp)[kGR][Geo<L>::MP], const uint32_t (&dm)[kGR][Geo<L>::MP],
@@ -837,7 +849,7 @@ __device__ inline void fused_step(const uint16_t* abuf, int k, const u32x4 (&b)[
   for (int u = 0; u < kGR; ++u) xo[u] = c.xoff[u];
   StepState<L, ND, NS> st{ap, am, b, acc, xr, dp, dm, vp, vm,
                           bn, wrs, boff, {bmat_byte<L, M>(0) + sb, bmat_byte<L, M>(1) + sb},
-                          xn, xrs, {}, (uint32_t)(pair_off(nglp) * kC + 32 * nk) * 4u, nglp, oob};
+                          xn, xrs, {}, (uint32_t)(pair_off(nglp) * kC + 32 * nk) * 4u, nglp, oob, dglp};
 #pragma unroll
   for (int u = 0; u < kGR; ++u) st.xoff[u] = xo[u];
   // the MFMA part of the step runs at raised wave priority, the dot products
@@ -1064,10 +1076,10 @@ __device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams&
     const uint16_t* acur = abase + ((PAR + q) & 1) * Geo<L>::ABUF;
     uint16_t* anext = abase + ((PAR + q + 1) & 1) * Geo<L>::ABUF;
     // K step s: unit k from xa; loads B of step s + 1 and the gathers of unit k + 1
-    fused_step<L, M, LO, ND>(acur, k, ring[0], acc, sG, c, xa, dp, dm, anext, ring[1], wrs, boff, s + 1, xb, xrs,
+    fused_step<L, M, LO, ND>(acur, k, glp, ring[0], acc, sG, c, xa, dp, dm, anext, ring[1], wrs, boff, s + 1, xb, xrs,
                              glp, k + 1, oob);
     // K step s + 1: unit k + 1 from xb; loads B of step s + 2 and the gathers of the next unit
-    fused_step<L, M, LO, ND>(acur, k + 1, ring[1], acc, sG, c, xb, dp, dm, anext, ring[0], wrs, boff,
+    fused_step<L, M, LO, ND>(acur, k + 1, glp, ring[1], acc, sG, c, xb, dp, dm, anext, ring[0], wrs, boff,
                              min(s + 2, NSTEP - 1), xa, xrs, glp2, (k + 2) & 3, oob);
     if (k == 2) __syncthreads();  // chunk q + 1 written, chunk q read by every wave
   }
