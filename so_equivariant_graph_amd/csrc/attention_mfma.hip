@@ -287,69 +287,79 @@ __global__ void __launch_bounds__(256) attn_pack_kernel(const uint16_t* __restri
 
 // ---------------------------------------------------------------- statistics
 
-// One wave per target (4 per block); lane i takes the target's neighbours
-// i, i + 64, ...  For each neighbour the lane computes the edge geometry and
-// envelope once and the logits of every head from the whole k_j row (16-byte
-// loads) and q_t (staged in LDS per wave, read as broadcasts), and keeps an
-// online (max, normaliser) pair per head; the wave then combines the pairs.
+// One wave per target (4 per block); the neighbours go in batches of 64.
+// First each lane takes one neighbour of the batch: its source j and
+// envelope u (geometry once per edge).  Then each half-wave takes one
+// neighbour at a time (the halves take alternate ones, kStatUnroll in
+// flight), with j and u shuffled from the lane that owns the edge: lane c4
+// of a half holds channels 4 c4 .. 4 c4 + 3 of q_t and reads the same
+// channels of k_j, so one neighbour's k row is one coalesced 512-byte load.
+// The d / 4 lanes of a head sum their partial products by xor shuffles
+// (d = C / H, a power of two for H <= 16) and keep the head's online
+// (max, normaliser) pair over their half's neighbours; the halves are
+// combined at the end.
+constexpr int kStatUnroll = 4;
 __global__ void __launch_bounds__(256) attn_stats_kernel(MfmaParams P, int C) {
-  __shared__ __attribute__((aligned(16))) float qs[4][kC];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + w;
-  const bool live = t < P.n_targets;
-  if (live)
-    for (int c = lane; c < kC; c += 64) qs[w][c] = P.q[(int64_t)t * kC + c];
-  __syncthreads();
-  if (!live) return;
-  const int e0 = P.row_ptr[t], e1 = P.row_ptr[t + 1];
-  const int H = P.H, d = kC / H;
+  if (t >= P.n_targets) return;
+  const int half = lane >> 5, c4 = lane & 31;
+  const int H = P.H, d = kC / H, gl = d / 4;  // lanes per head
+  const int h = c4 / gl;
   const float inv_sqrt_d = 1.0f / sqrtf((float)d);
-  float m[kMaxHeads], s[kMaxHeads];
+  const f32x4 qv = *(const f32x4*)(P.q + (int64_t)t * kC + 4 * c4);
+  const int e0 = P.row_ptr[t], e1 = P.row_ptr[t + 1];
+  float m = -INFINITY, ssum = 0.0f;
+  for (int b0 = e0; b0 < e1; b0 += 64) {
+    const int nb = min(64, e1 - b0);
+    // one edge per lane: source and envelope
+    int jl = t;
+    float ul = 0.0f;
+    if (lane < nb) {
+      jl = P.col[b0 + lane];
+      float r[3];
+      edge_vec(P, t, jl, r);
+      const float rho = sqrtf(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
+      ul = envelope_u(rho / P.cutoff, P.p);
+    }
+    // one edge per half-wave: logits per head and the online softmax (both
+    // halves run every iteration, so that the shuffles see all 64 lanes)
+    for (int i0 = 0; i0 < nb; i0 += 2 * kStatUnroll) {
+      const int i = i0 + half;
+      int j[kStatUnroll];
+      float u[kStatUnroll];
+      f32x4 kv[kStatUnroll];
 #pragma unroll
-  for (int h = 0; h < kMaxHeads; ++h) {
-    m[h] = -INFINITY;
-    s[h] = 0.0f;
-  }
-  for (int e = e0 + lane; e < e1; e += 64) {
-    const int j = P.col[e];
-    float r[3];
-    edge_vec(P, t, j, r);
-    const float rho = sqrtf(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
-    const float u = envelope_u(rho / P.cutoff, P.p);
-    const f32x4* kr = (const f32x4*)(P.k + (int64_t)j * kC);
-    const f32x4* qr = (const f32x4*)qs[w];
+      for (int v = 0; v < kStatUnroll; ++v) {
+        const int src = min(i + 2 * v, 63);
+        j[v] = __shfl(jl, src, 64);
+        u[v] = __shfl(ul, src, 64);
+      }
 #pragma unroll
-    for (int h = 0; h < kMaxHeads; ++h) {
-      if (h < H) {
-        float z = 0.0f;
-        for (int i = h * d / 4; i < (h + 1) * d / 4; ++i) {
-          const f32x4 kv = kr[i], qv = qr[i];
-          z += qv.x * kv.x + qv.y * kv.y + qv.z * kv.z + qv.w * kv.w;
-        }
-        z *= inv_sqrt_d;
-        if (z > m[h]) {
-          s[h] = s[h] * expf(m[h] - z) + u;
-          m[h] = z;
-        } else {
-          s[h] += u * expf(z - m[h]);
+      for (int v = 0; v < kStatUnroll; ++v) kv[v] = *(const f32x4*)(P.k + (int64_t)j[v] * kC + 4 * c4);
+#pragma unroll
+      for (int v = 0; v < kStatUnroll; ++v) {
+        float z = qv.x * kv[v].x + qv.y * kv[v].y + qv.z * kv[v].z + qv.w * kv[v].w;
+        for (int off = 1; off < gl; off <<= 1) z += __shfl_xor(z, off, 64);
+        if (i + 2 * v < nb) {
+          z *= inv_sqrt_d;
+          if (z > m) {
+            ssum = ssum * expf(m - z) + u[v];
+            m = z;
+          } else {
+            ssum += u[v] * expf(z - m);
+          }
         }
       }
     }
   }
-#pragma unroll
-  for (int h = 0; h < kMaxHeads; ++h) {
-    if (h < H) {
-      float M = m[h];
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-      float part = (m[h] == -INFINITY) ? 0.0f : s[h] * expf(m[h] - M);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
-      if (lane == 0) {
-        P.stat_max[(int64_t)t * H + h] = M;
-        P.stat_inv[(int64_t)t * H + h] = part > 0.0f ? 1.0f / part : 0.0f;
-      }
-    }
+  // combine the two halves (lanes c4 and c4 + 32 hold the same head)
+  const float mo = __shfl_xor(m, 32, 64), so = __shfl_xor(ssum, 32, 64);
+  const float M = fmaxf(m, mo);
+  const float S = (m == -INFINITY ? 0.0f : ssum * expf(m - M)) + (mo == -INFINITY ? 0.0f : so * expf(mo - M));
+  if (half == 0 && c4 % gl == 0) {
+    P.stat_max[(int64_t)t * H + h] = M;
+    P.stat_inv[(int64_t)t * H + h] = S > 0.0f ? 1.0f / S : 0.0f;
   }
 }
 
