@@ -42,12 +42,12 @@ PEAK_HBM_GBS = 8000.0
 # for the kernel sources it was taken on: their digest is stored with it and a
 # mismatch reports null.
 MEASURED_TRAFFIC = {
-    # FETCH_SIZE 1167638 KiB x 2.00 (a 1 GiB copy reads as 524302 KiB), WRITE_SIZE
-    # 260728 KiB x 1.00 (the copy writes read exactly 1048576 KiB); mean of 7 launches.
+    # FETCH_SIZE 1083138 KiB x 2.00 (a 1 GiB copy reads as 524302 KiB), WRITE_SIZE
+    # 185096 KiB x 1.00 (the copy writes read exactly 1048576 KiB); mean of 7 launches.
     "small_molecules": {
-        "sources_sha256": "3314dc2aae8e41fc625f67a3116b9724af1a4b05876f68095b44d43e9276e51d",
-        "fetch_bytes": 2391257594,
-        "write_bytes": 266985472,
+        "sources_sha256": "e2412d8d5eb0f75ace3cb212f9a7ace43c506e56a669866c97c537e0f8e27155",
+        "fetch_bytes": 2218206122,
+        "write_bytes": 189538304,
     },
 }
 KERNEL_SOURCES = ("attention_mfma.hip", "wigner.h", "common.h", "launch.h")
