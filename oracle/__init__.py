@@ -38,6 +38,8 @@ wigner     Wigner-D blocks by exact quadrature, edge-frame rotation
 neighbors  brute-force O(N^2) radius graph in fp64, CSR output
 attention  the per-edge loop: rotate, gate, SO(2) map, rotate back,
            two-pass softmax with the envelope, aggregate
+norm       the merged RMS layer norm of the node features ("EquiformerV3"
+           technical summary, section 2.B.1)
 """
 
 from .sh import real_sh, n_comp
@@ -51,6 +53,7 @@ from .attention import (
     so2_weight_count,
     max_rel_error,
 )
+from .norm import merged_rms_norm_ref
 
 __all__ = [
     "real_sh",
@@ -60,6 +63,7 @@ __all__ = [
     "rot_z",
     "neighbors_bruteforce",
     "so2_attention_ref",
+    "merged_rms_norm_ref",
     "envelope",
     "radial_gaussians",
     "unpack_so2",
