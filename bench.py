@@ -9,6 +9,7 @@ timed region starts.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload small_molecules]
     python bench.py --memory-sweep [--steps 5 --warmup 2]   (peak bytes against N)
+    python bench.py --norm                                  (merged RMS layer norm, HBM roofline)
 
 value          messages (edges) per second of the whole step
 roofline       the fused attention kernel against the dense bf16 MFMA peak:
@@ -235,6 +236,69 @@ def run_gpu(w, steps, warmup):
     )
 
 
+NORM_TRAFFIC = {
+    # HBM bytes of one launch of merged_rms_norm_reg_kernel<bf16, 8> on the 100k-atom water
+    # box's features: FETCH_SIZE 312574 KiB x 2.00, WRITE_SIZE 625000 KiB x 1.00 (the same
+    # copy calibration as the fused kernel's figure); mean of 4 launches.
+    "water_100k": {
+        "sources_sha256": "ee2c3c264342728eb32bd5a439502a95e163eaa5e494cfbb147df873fe5dfbac",
+        "fetch_bytes": 640134813,
+        "write_bytes": 640000000,
+    },
+}
+NORM_SOURCES = ("norm.hip", "common.h")
+
+
+def norm_bench(steps, warmup):
+    """The merged RMS layer norm of the 100k-atom water box's node features
+    (bf16, L = 4, C = 128): nodes/s and the HBM roofline.  Algorithmic bytes
+    per node: read x once and write y once, 2 (L+1)^2 C x 2 B, plus the
+    gains (read once per launch).  Kernel time from torch events on the
+    stream the library launches on (torch's current stream)."""
+    import numpy as np
+    import torch
+
+    import so_equivariant_graph_amd as sea
+    from synth import make_workload
+
+    w = make_workload("water_100k")
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(w.x).to(device=dev, dtype=torch.bfloat16)
+    del w.x
+    gamma = torch.from_numpy(np.random.default_rng(0).uniform(0.5, 2.0, size=(w.l_max + 1, w.channels))
+                             .astype(np.float32)).to(dev)
+    y = torch.empty_like(x)
+    for _ in range(warmup):
+        sea.merged_rms_norm(x, gamma, out=y)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        sea.merged_rms_norm(x, gamma, out=y)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    mean = sum(ms) / len(ms)
+    n, nc, C = x.shape
+    algo = 2 * n * nc * C * 2 + gamma.numel() * 4
+    h = hashlib.sha256()
+    for f in NORM_SOURCES:
+        h.update(open(os.path.join(ROOT, "so_equivariant_graph_amd", "csrc", f), "rb").read())
+    rec = NORM_TRAFFIC.get("water_100k")
+    traffic = rec["fetch_bytes"] + rec["write_bytes"] if rec and rec["sources_sha256"] == h.hexdigest() else None
+    print(json.dumps({
+        "metric": "merged RMS layer norm nodes/s", "value": n / (mean * 1e-3), "unit": "nodes/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": mean, "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "water_100k node features", "n_atoms": n, "l_max": int(round(nc ** 0.5)) - 1,
+                   "channels": C},
+        "roofline": {"bound": "hbm", "achieved": algo / (mean * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": algo / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": traffic},
+        "detail": {"algorithmic_bytes": algo, "ms_min": ms[0], "ms_median": ms[len(ms) // 2],
+                   "kernel_sources_sha256": h.hexdigest()},
+    }), flush=True)
+
+
 SWEEP_ATOMS = (12_500, 25_000, 50_000, 100_000, 200_000)
 
 
@@ -285,6 +349,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, metavar="MIB", default=0,
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--norm", action="store_true",
+                    help="only time the merged RMS layer norm on the 100k-atom water box's features")
     ap.add_argument("--memory-sweep", action="store_true",
                     help="only run the water box at 12.5k-200k atoms: peak device bytes against N")
     args = ap.parse_args()
@@ -300,6 +366,9 @@ def main():
         return
     if args.memory_sweep:
         memory_sweep(args.steps, args.warmup)
+        return
+    if args.norm:
+        norm_bench(args.steps, args.warmup)
         return
 
     from synth import make_workload

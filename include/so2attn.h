@@ -171,6 +171,24 @@ so2_status so2_attention_fwd(const so2_attn_desc* desc, const float* pos,
 void so2_set_kernel_timing_events(void* start, void* stop);
 
 /* ------------------------------------------------------------------------
+ * so2_merged_rms_norm - equivariant merged RMS layer norm of node features
+ * ("EquiformerV3: Scaling Efficient, Expressive, and General SE(3)-Equivariant
+ * Graph Attention Transformers", technical summary, section 2.B.1: one RMS
+ * statistic shared by all degrees of a node):
+ *   y[i][(l,m)][c] = gamma[l][c] x[i][(l,m)][c] / sqrt(mean_{l,m,c} x[i]^2 + eps)
+ *   x        [n_atoms][(l_max+1)^2][channels] dtype (device)
+ *   gamma    [l_max+1][channels] fp32 (device): gain per degree and channel
+ *   y        same shape and dtype as x (device); may be x itself (in place)
+ *   eps      >= 0, finite
+ * Statistics in fp32; bf16 outputs are rounded to nearest even.
+ * Errors: INVALID_ARGUMENT (nulls with n_atoms > 0, n_atoms < 0, l_max < 0,
+ * channels < 1, bad eps or dtype), UNSUPPORTED (l_max > 6), DEVICE.
+ * Asynchronous on `stream`; no workspace, no device allocation.
+ * ---------------------------------------------------------------------- */
+so2_status so2_merged_rms_norm(const void* x, const float* gamma, void* y, int32_t n_atoms, int32_t l_max,
+                               int32_t channels, float eps, int32_t dtype, so2_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Host-side diagnostics (no device work): evaluate, on the CPU, the same
  * edge-frame and Wigner-D code the kernels run in fp32, for tests.
  *   rhat   float[3] edge direction (need not be normalised)

@@ -48,6 +48,7 @@ EXPORTED_SYMBOLS = (
     "so2_attention_fwd",
     "so2_edge_frame_host",
     "so2_set_kernel_timing_events",
+    "so2_merged_rms_norm",
 )
 
 
@@ -115,6 +116,8 @@ def load_library(path: str = LIB_PATH):
     lib.so2_edge_frame_host.restype = ctypes.c_int
     lib.so2_set_kernel_timing_events.argtypes = [vp, vp]
     lib.so2_set_kernel_timing_events.restype = None
+    lib.so2_merged_rms_norm.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, vp]
+    lib.so2_merged_rms_norm.restype = ctypes.c_int
     _lib_handle = lib
     return lib
 
@@ -260,6 +263,28 @@ def so2_attention_fwd(pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, *, l_max, he
         _stream_handle(x.device),
     )
     _check(st, "so2_attention_fwd")
+    return y
+
+
+def merged_rms_norm(x, gamma, *, eps=1e-5, out=None):
+    """Merged RMS layer norm: one RMS statistic per node over every degree,
+    gain gamma [L+1, C] (float32) per degree and channel.  x: [N,(L+1)^2,C]
+    float32 or bfloat16; returns y of x's shape and dtype (out may be x)."""
+    import torch
+
+    lib = load_library()
+    dt = _dtype_code(x)
+    n, nc, C = x.shape
+    L = int(round(nc ** 0.5)) - 1
+    if (L + 1) ** 2 != nc:
+        raise ValueError("x has the wrong number of irreps components")
+    if gamma.dtype != torch.float32 or tuple(gamma.shape) != (L + 1, C):
+        raise ValueError("gamma must be float32 [L+1, C]")
+    x, gamma = x.contiguous(), gamma.contiguous()
+    y = out if out is not None else torch.empty_like(x)
+    st = lib.so2_merged_rms_norm(_ptr(x), _ptr(gamma), _ptr(y), n, L, C, ctypes.c_float(eps), dt,
+                                 _stream_handle(x.device))
+    _check(st, "so2_merged_rms_norm")
     return y
 
 

@@ -24,6 +24,7 @@ SOURCES = [
     "abi.hip",
     "neighbors.hip",
     "attention_prep.hip",
+    "norm.hip",
     "attention_valu.hip",
     "attention_mfma.hip",
 ]

@@ -203,6 +203,15 @@ void so2_set_kernel_timing_events(void* start, void* stop) {
   g_timing_stop = (hipEvent_t)stop;
 }
 
+so2_status so2_merged_rms_norm(const void* x, const float* gamma, void* y, int32_t n_atoms, int32_t l_max,
+                               int32_t channels, float eps, int32_t dtype, so2_stream_t stream) {
+  if (n_atoms < 0 || l_max < 0 || channels < 1 || !(eps >= 0.0f) || !isfinite(eps)) return SO2_ERR_INVALID_ARGUMENT;
+  if (dtype != SO2_FP32 && dtype != SO2_BF16) return SO2_ERR_INVALID_ARGUMENT;
+  if (n_atoms > 0 && (!x || !gamma || !y)) return SO2_ERR_INVALID_ARGUMENT;
+  if (l_max > kMaxL) return SO2_ERR_UNSUPPORTED;
+  return launch_merged_rms_norm(x, gamma, y, n_atoms, l_max, channels, eps, dtype, (hipStream_t)stream);
+}
+
 so2_status so2_edge_frame_host(int32_t l_max, const float* rhat, float* R_out, float* D_out) {
   if (!rhat || !R_out || !D_out || l_max < 0 || l_max > kMaxL) return SO2_ERR_INVALID_ARGUMENT;
   float n = sqrtf(rhat[0] * rhat[0] + rhat[1] * rhat[1] + rhat[2] * rhat[2]);

@@ -159,6 +159,22 @@ def test_kernel_kind_selection():
     assert sea.attention_kernel_kind(_desc(l_max=6, channels=128, heads=8, dtype=sea.SO2_FP32)) == sea.KERNEL_VALU
 
 
+def test_norm_errors_before_launch():
+    lib = sea.load_library()
+    call = lambda x, g, y, n, L, C, eps, dt: lib.so2_merged_rms_norm(x, g, y, n, L, C, ctypes.c_float(eps), dt, None)
+    assert call(None, FAKE, FAKE, 4, 2, 8, 1e-5, sea.SO2_BF16) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(FAKE, None, FAKE, 4, 2, 8, 1e-5, sea.SO2_BF16) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(FAKE, FAKE, None, 4, 2, 8, 1e-5, sea.SO2_BF16) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(FAKE, FAKE, FAKE, -1, 2, 8, 1e-5, sea.SO2_BF16) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(FAKE, FAKE, FAKE, 4, -1, 8, 1e-5, sea.SO2_BF16) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(FAKE, FAKE, FAKE, 4, 2, 0, 1e-5, sea.SO2_BF16) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(FAKE, FAKE, FAKE, 4, 2, 8, -1.0, sea.SO2_BF16) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(FAKE, FAKE, FAKE, 4, 2, 8, float("nan"), sea.SO2_BF16) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(FAKE, FAKE, FAKE, 4, 2, 8, 1e-5, 7) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(FAKE, FAKE, FAKE, 4, 7, 8, 1e-5, sea.SO2_BF16) == sea.SO2_ERR_UNSUPPORTED
+    assert call(None, None, None, 0, 2, 8, 1e-5, sea.SO2_FP32) == sea.SO2_OK  # nothing to do
+
+
 def test_neighbor_errors_before_launch():
     lib = sea.load_library()
     n_e = ctypes.c_int64(0)
