@@ -241,12 +241,12 @@ NORM_TRAFFIC = {
     # box's features: FETCH_SIZE 312574 KiB x 2.00, WRITE_SIZE 625000 KiB x 1.00 (the same
     # copy calibration as the fused kernel's figure); mean of 4 launches.
     "water_100k": {
-        "sources_sha256": "ee2c3c264342728eb32bd5a439502a95e163eaa5e494cfbb147df873fe5dfbac",
+        "sources_sha256": "728e522721c4a27c254123d554044f5e4e350bd439a9f0ebdf0e151b5f144e76",
         "fetch_bytes": 640134813,
         "write_bytes": 640000000,
     },
 }
-NORM_SOURCES = ("norm.hip", "common.h")
+NORM_SOURCES = ("norm.hip", "norm.h", "common.h")
 
 
 def norm_bench(steps, warmup):

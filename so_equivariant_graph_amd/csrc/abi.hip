@@ -6,6 +6,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "norm.h"
 #include "wigner.h"
 
 namespace so2 {

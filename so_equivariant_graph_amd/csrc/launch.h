@@ -51,10 +51,6 @@ struct AttnArgs {
   float box[3];
 };
 
-// Merged RMS layer norm of node features (norm.hip).
-so2_status launch_merged_rms_norm(const void* x, const float* gamma, void* y, int n_atoms, int L, int C,
-                                  float eps, int dtype, hipStream_t stream);
-
 // q/k projection of the l = 0 slice (attention_prep.hip).
 so2_status launch_qk_proj(const AttnArgs& a, hipStream_t stream);
 

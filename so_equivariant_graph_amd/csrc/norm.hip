@@ -14,7 +14,8 @@
 // summed in fp32 and reduced across the wave; then gamma x / rms is written,
 // rounded to bf16 when the input is bf16.  Larger nodes read x twice.  Every
 // element is read before the same lane writes it, so y may alias x.
-#include "common.h"
+#include "norm.h"
+
 #include "launch.h"
 
 namespace so2 {
