@@ -392,8 +392,7 @@ using Smem = SmemT<(16 * Cfg<L>::TT > 112 ? 16 * Cfg<L>::TT : 112)>;
 // Passes in execution order: blocks m = 1..L, each in groups of at most two
 // output degrees (the limit of the register and LDS budgets with two sign
 // planes and 64-edge chunks; three with the 32-edge chunks of L >= 5), then
-// m = 0 in one pass over all its L + 1 output degrees (two passes for
-// L >= 5).  Every pass
+// m = 0 in one pass over all its L + 1 output degrees.  Every pass
 // generates, during its last A chunk, the first A chunk of the pass after
 // it; ending on m = 0 means a pass never has to produce more sign planes
 // than it has itself (an m >= 1 pass writes both planes, m = 0 reads one).
@@ -405,7 +404,7 @@ __host__ __device__ constexpr PassInfo pass_info(int L, int idx) {
   int i = 0;
   for (int mm = 1; mm <= L + 1; ++mm) {
     const int M = mm == L + 1 ? 0 : mm;
-    const int nd = M == 0 ? (L <= 4 ? L + 1 : (L + 2) / 2) : (L <= 4 ? 2 : 3);
+    const int nd = M == 0 ? L + 1 : (L <= 4 ? 2 : 3);
     for (int lo = M; lo <= L; lo += nd) {
       if (i == idx) return PassInfo{M, lo, (L + 1 - lo) < nd ? (L + 1 - lo) : nd};
       ++i;
