@@ -20,11 +20,12 @@
 //   for block m the A operand is the rotated, gated input rows (l', +-m) of
 //   those edges, built on the vector ALUs and staged through LDS in bf16,
 //   one degree l' (128 channels, 4 K steps of 32) per A chunk;
-//   the B operand is W0 (m = 0) or W1_m / W2_m read straight from the
-//   caller's row-major [out][in] weights (8 consecutive bf16 of one row per
-//   lane, one 16-byte load);
+//   the B operand is W0 (m = 0) or W1_m / W2_m, copied by the prologue from
+//   the caller's row-major [out][in] weights into MFMA fragment order, so
+//   that one 16-byte load per lane is a whole fragment;
 //   m >= 1 is the complex product (W1 + i W2)(xt_+ + i xt_-): four real MFMAs
-//   per tile pair, the minus sign carried by the W2 fragment.
+//   per tile pair, the minus sign applied by flipping W2's sign bits in
+//   registers.
 //
 // The rotation into the edge frame, xt[(l', m)][c] = sum_b D^l'[m][b]
 // x_j[(l', b)][c], runs on v_dot2_f32_bf16: a prologue kernel repacks x so
@@ -42,9 +43,9 @@
 //
 // Workgroup: 8 waves (512 lanes), two per SIMD so that one wave's memory
 // waits are covered by the other's MFMAs; wave w owns output channels
-// [16w, 16w+16).  Each
-// workgroup takes a run of consecutive target atoms holding about the same
-// number of edges as every other workgroup; its edges are processed in
+// [16w, 16w+16).  Each workgroup takes a run of consecutive target atoms
+// holding about the same number of edges as every other workgroup (a
+// scheduling kernel orders the runs longest first); its edges are processed in
 // chunks of at most 64 (32) edges whose targets span at most 4 consecutive
 // indices (4 accumulator slots, slot = target mod 4); a target whose edges
 // continue into the next chunk keeps its slot, a target whose last edge is
@@ -52,8 +53,9 @@
 //
 // Software pipeline: while the MFMAs consume A chunk q from one LDS buffer,
 // every lane generates one quarter of the next A chunk per K step into the
-// other buffer (its gathers issued before the step's MFMAs) and the B
-// fragments of the next K step load; one barrier per A chunk.  Every pass
+// other buffer (its gathers issued one step ahead, its dot products after
+// the step's MFMAs) and the B fragments of the next K step load; one
+// barrier per A chunk.  Every pass
 // (block m, a group of output degrees) is a compile-time instance, so its
 // loop bounds, weight offsets and register tiles are constants, and it
 // generates the first A chunk of the pass after it.
@@ -460,12 +462,12 @@ struct Lds {
 };
 
 // 16-byte column groups are XOR-swizzled by row so that both the MFMA
-// operand reads (16 rows, one group) and the generator's writes (4 rows x 4
-// groups) touch 16 distinct bank groups.
+// operand reads (16 rows, one group) and the generator's writes (8 or 4 rows
+// x 4 groups per wave) spread over distinct bank groups.
 __device__ inline int a_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 __device__ inline int a_off(int row, int group) { return row * kKC + 8 * (group ^ a_swz(row)); }
-// gate rows: 32 groups of 4 floats; the generator reads groups 8 k .. 8 k + 7
-// of 2 consecutive rows
+// gate rows: 32 groups of 4 floats, swizzled by row; in K step k the
+// generator reads groups 8 k .. 8 k + 7 of each of its rows
 __device__ inline int g_swz(int row) { return ((row & 1) << 3) | ((row >> 1) & 1); }
 __device__ inline int g_off(int row, int group) { return row * kC + 4 * (group ^ g_swz(row)); }
 
