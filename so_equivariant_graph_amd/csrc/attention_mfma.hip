@@ -741,8 +741,17 @@ __device__ __attribute__((always_inline)) inline void step_load(StepState<L, ND,
     st.bn[di][sm][nt] = buffer_load16(st.wrs, st.boff[di][nt], st.wsoff[sm]);
   } else {
     constexpr int g = J - NB, p = g / kGR, u = g % kGR;
-    st.xn[g] = buffer_load_x<Geo<L>::GCH>(st.xrs, p <= st.glp ? st.xoff[u] : st.oob,
-                                          st.xsoff + (uint32_t)p * (kC * 4));
+    if constexpr (L >= 5) {
+      // pairs past the next unit's degree are not loaded (their dot products
+      // are skipped, so the registers may keep stale values); measured faster
+      // at L = 6, while at L <= 4 the branches cost more registers than the
+      // loads they save
+      if (p == 0 || p <= st.glp)
+        st.xn[g] = buffer_load_x<Geo<L>::GCH>(st.xrs, st.xoff[u], st.xsoff + (uint32_t)p * (kC * 4));
+    } else {
+      st.xn[g] = buffer_load_x<Geo<L>::GCH>(st.xrs, p <= st.glp ? st.xoff[u] : st.oob,
+                                            st.xsoff + (uint32_t)p * (kC * 4));
+    }
   }
 }
 
