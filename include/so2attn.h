@@ -101,9 +101,10 @@ const char* so2_last_device_error(void);
  * Errors: INVALID_ARGUMENT (nulls, n_atoms < 1, cutoff <= 0 or not finite,
  * non-finite positions, E > INT32_MAX), BOX (side <= 2*cutoff), CAPACITY,
  * WORKSPACE, DEVICE.
- * Synchronisation: the call waits for `stream` twice (bounding box, then E)
- * and returns once E is known; the fill and the row sort are left queued on
- * `stream`.  Cost O(N) memory, O(N k) work.
+ * Synchronisation: the call waits for `stream` once, for E (the bounding box
+ * and the cell grid are computed on the device), and returns once E is
+ * known; the fill and the row sort are left queued on `stream`.  Non-finite
+ * positions are reported at that point, before the fill.  Cost O(N) memory, O(N k) work.
  * ---------------------------------------------------------------------- */
 size_t so2_neighbors_workspace_bytes(int32_t n_atoms);
 

@@ -40,9 +40,46 @@ struct GridParams {
   int periodic;
 };
 
+// Cells at least rc wide (widened by 1e-6 so that rounding of the cell
+// coordinate can never split a pair closer than rc by two cells), at most
+// max_cells of them: the longest axis is halved until the grid fits.
+__device__ inline void make_grid(const float* bb, double rc, int periodic, const double* box, int64_t max_cells,
+                                 GridParams& g) {
+  const double cs = rc * (1.0 + 1e-6);
+  g.periodic = periodic;
+  for (int d = 0; d < 3; ++d) {
+    if (periodic) {
+      g.box[d] = box[d];
+      g.origin[d] = 0.0;
+      g.n[d] = (int)fmax(1.0, floor(box[d] / cs));
+    } else {
+      const double ext = (double)bb[3 + d] - (double)bb[d];
+      g.box[d] = 0.0;
+      g.origin[d] = (double)bb[d];
+      g.n[d] = (int)fmax(1.0, fmin(floor(ext / cs), 1e9));
+    }
+  }
+  while ((int64_t)g.n[0] * g.n[1] * g.n[2] > max_cells) {
+    const int d = (g.n[0] >= g.n[1] && g.n[0] >= g.n[2]) ? 0 : (g.n[1] >= g.n[2] ? 1 : 2);
+    g.n[d] = (g.n[d] + 1) / 2;
+  }
+  for (int d = 0; d < 3; ++d) {
+    const double cell = periodic ? g.box[d] / g.n[d] : fmax(cs, ((double)bb[3 + d] - (double)bb[d]) / g.n[d]);
+    g.inv_cell[d] = 1.0 / cell;
+  }
+}
+
+// Bounding box of the finite coordinates, a flag for non-finite ones, and
+// the cell grid built from them (or from the box), all written to device
+// memory: no host round trip before the binning.  Non-finite coordinates
+// still land in clamped cells (NaN converts to 0, +-inf saturates), so every
+// later kernel stays in bounds; the call reports them once E is read back.
 __global__ void __launch_bounds__(1024) nb_bbox_kernel(const float* __restrict__ pos, int n,
                                                       float* __restrict__ out_f,
-                                                      int* __restrict__ out_i) {
+                                                      int* __restrict__ out_i, double rc, int periodic,
+                                                      double bx, double by, double bz, long long max_cells,
+                                                      GridParams* __restrict__ out_g,
+                                                      int* __restrict__ out_ncell) {
   __shared__ float s_mn[3][1024];
   __shared__ float s_mx[3][1024];
   __shared__ int s_bad[1024];
@@ -78,6 +115,16 @@ __global__ void __launch_bounds__(1024) nb_bbox_kernel(const float* __restrict__
     __syncthreads();
   }
   if (t == 0) {
+    float bb[6];
+    for (int d = 0; d < 3; ++d) {
+      bb[d] = s_mn[d][0];
+      bb[3 + d] = s_mx[d][0];
+    }
+    const double box[3] = {bx, by, bz};
+    GridParams g;
+    make_grid(bb, rc, periodic, box, max_cells, g);
+    *out_g = g;
+    *out_ncell = g.n[0] * g.n[1] * g.n[2];
     for (int d = 0; d < 3; ++d) {
       out_f[d] = s_mn[d][0];
       out_f[3 + d] = s_mx[d][0];
@@ -99,10 +146,11 @@ __device__ inline int cell_coord(double p, int d, const GridParams& g) {
   return c;
 }
 
-__global__ void nb_assign_kernel(const float* __restrict__ pos, int n, GridParams g,
+__global__ void nb_assign_kernel(const float* __restrict__ pos, int n, const GridParams* __restrict__ gp,
                                  int* __restrict__ cell_of, int* __restrict__ cell_count) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
+  const GridParams g = *gp;
   int cx = cell_coord((double)pos[3 * (int64_t)i + 0], 0, g);
   int cy = cell_coord((double)pos[3 * (int64_t)i + 1], 1, g);
   int cz = cell_coord((double)pos[3 * (int64_t)i + 2], 2, g);
@@ -111,13 +159,15 @@ __global__ void nb_assign_kernel(const float* __restrict__ pos, int n, GridParam
   atomicAdd(&cell_count[c], 1);
 }
 
-// Exclusive scan of in[0..n) into out[0..n], out[n] = total (int32), total
-// also stored as int64 in *total64.  One workgroup of 1024 threads.
+// Exclusive scan of in[0..n) into out[0..n] (and out2[0..n) if given),
+// out[n] = total (int32), total also stored as int64 in *total64; n is read
+// from n_dev when that is given.  One workgroup of 1024 threads.
 __global__ void __launch_bounds__(1024) nb_scan_kernel(const int* __restrict__ in, int n,
-                                                      int* __restrict__ out,
-                                                      long long* __restrict__ total64) {
+                                                      const int* __restrict__ n_dev, int* __restrict__ out,
+                                                      int* __restrict__ out2, long long* __restrict__ total64) {
   __shared__ long long s[1024];
   int t = threadIdx.x;
+  if (n_dev) n = *n_dev;
   int per = (n + blockDim.x - 1) / blockDim.x;
   int a = t * per;
   int b = min(n, a + per);
@@ -135,6 +185,7 @@ __global__ void __launch_bounds__(1024) nb_scan_kernel(const int* __restrict__ i
   long long run = s[t] - sum;
   for (int i = a; i < b; ++i) {
     out[i] = (int)run;
+    if (out2) out2[i] = (int)run;
     run += in[i];
   }
   if (t == blockDim.x - 1) {
@@ -198,7 +249,7 @@ __device__ inline bool within_cutoff(double pix, double piy, double piz, double 
 constexpr int kGroup = 16;
 template <bool kFill>
 __global__ void __launch_bounds__(256) nb_pairs_kernel(const float* __restrict__ pos, const int* __restrict__ mol,
-                                                       int n, GridParams g, double rc2,
+                                                       int n, const GridParams* __restrict__ gp, double rc2,
                                                        const int* __restrict__ cell_start,
                                                        const int* __restrict__ sorted_idx,
                                                        const float* __restrict__ sorted_pos,
@@ -210,6 +261,7 @@ __global__ void __launch_bounds__(256) nb_pairs_kernel(const float* __restrict__
   const int li = threadIdx.x % kGroup;                // lane within the group
   const int gshift = (threadIdx.x & 63) & ~(kGroup - 1);  // first lane of the group in the wave
   if (gid >= n) return;  // whole groups leave together
+  const GridParams g = *gp;
   const int i = gid;
   const double pix = (double)pos[3 * (int64_t)i + 0];
   const double piy = (double)pos[3 * (int64_t)i + 1];
@@ -315,7 +367,7 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 int64_t max_cells(int32_t n_atoms) { return 2 * (int64_t)n_atoms + 1024; }
 
 struct NbLayout {
-  size_t bbox, cell_of, cell_count, cell_start, cursor, sorted_idx, sorted_pos, sorted_mol,
+  size_t bbox, grid, cell_of, cell_count, cell_start, cursor, sorted_idx, sorted_pos, sorted_mol,
       counts, long_rows, scalars, total;
 };
 
@@ -329,6 +381,7 @@ NbLayout nb_layout(int32_t n) {
   };
   int64_t nc = max_cells(n);
   L.bbox = take(64);
+  L.grid = take(sizeof(GridParams) + 16);
   L.cell_of = take(sizeof(int) * (size_t)n);
   L.cell_count = take(sizeof(int) * (size_t)(nc + 1));
   L.cell_start = take(sizeof(int) * (size_t)(nc + 1));
@@ -338,7 +391,7 @@ NbLayout nb_layout(int32_t n) {
   L.sorted_mol = take(sizeof(int) * (size_t)n);
   L.counts = take(sizeof(int) * (size_t)n);
   L.long_rows = take(sizeof(int) * (size_t)n);
-  L.scalars = take(64);  // [0] E (int64), [8] n_long, [12] n_over
+  L.scalars = take(64);  // [0] E (int64), [8] n_long, [12] n_over, [16] non-finite flag
   L.total = off;
   return L;
 }
@@ -363,7 +416,6 @@ so2_status neighbors_build(const float* pos, int32_t n, const int32_t* mol_id,
   if (workspace_bytes < L.total || ((uintptr_t)workspace & 255)) return SO2_ERR_WORKSPACE;
   char* ws = (char*)workspace;
   float* bbox_f = (float*)(ws + L.bbox);
-  int* bbox_i = (int*)(ws + L.bbox + 32);
   int* cell_of = (int*)(ws + L.cell_of);
   int* cell_count = (int*)(ws + L.cell_count);
   int* cell_start = (int*)(ws + L.cell_start);
@@ -377,61 +429,30 @@ so2_status neighbors_build(const float* pos, int32_t n, const int32_t* mol_id,
   int* n_long = (int*)(ws + L.scalars + 8);
   int* n_over = (int*)(ws + L.scalars + 12);
 
-  // 1. bounding box and finiteness
-  hipLaunchKernelGGL(nb_bbox_kernel, dim3(1), dim3(1024), 0, stream, pos, n, bbox_f, bbox_i);
+  GridParams* grid = (GridParams*)(ws + L.grid);
+  int* ncell_dev = (int*)(ws + L.grid + sizeof(GridParams));
+  int* bad_dev = (int*)(ws + L.scalars + 16);
+  const int64_t ncell_max = max_cells(n);
+
+  // 1. bounding box, finiteness flag and cell grid, on the device
+  hipLaunchKernelGGL(nb_zero_kernel, dim3(1), dim3(64), 0, stream, (int*)(ws + L.scalars), 16);
+  const int periodic = box_host != nullptr;
+  hipLaunchKernelGGL(nb_bbox_kernel, dim3(1), dim3(1024), 0, stream, pos, n, bbox_f, bad_dev, (double)cutoff,
+                     periodic, periodic ? (double)box_host[0] : 0.0, periodic ? (double)box_host[1] : 0.0,
+                     periodic ? (double)box_host[2] : 0.0, (long long)ncell_max, grid, ncell_dev);
   SO2_CHECK_LAUNCH();
-  float hb[8];
-  int hbad = 0;
-  SO2_CHECK(hipMemcpyAsync(hb, bbox_f, 6 * sizeof(float), hipMemcpyDeviceToHost, stream));
-  SO2_CHECK(hipMemcpyAsync(&hbad, bbox_i, sizeof(int), hipMemcpyDeviceToHost, stream));
-  SO2_CHECK(hipStreamSynchronize(stream));
-  if (hbad) return SO2_ERR_INVALID_ARGUMENT;
-
-  // 2. cell grid: cells at least rc wide (widened by 1e-6 so that rounding of
-  //    the cell coordinate can never split a pair closer than rc by two cells)
-  GridParams g{};
   const double rc = (double)cutoff;
-  const double cs = rc * (1.0 + 1e-6);
-  g.periodic = box_host != nullptr;
-  for (int d = 0; d < 3; ++d) {
-    if (g.periodic) {
-      double b = (double)box_host[d];
-      g.box[d] = b;
-      g.n[d] = (int)fmax(1.0, floor(b / cs));
-    } else {
-      double ext = (double)hb[3 + d] - (double)hb[d];
-      g.origin[d] = (double)hb[d];
-      g.n[d] = (int)fmax(1.0, fmin(floor(ext / cs), 1e9));
-    }
-  }
-  while ((int64_t)g.n[0] * g.n[1] * g.n[2] > max_cells(n)) {
-    int d = (g.n[0] >= g.n[1] && g.n[0] >= g.n[2]) ? 0 : (g.n[1] >= g.n[2] ? 1 : 2);
-    g.n[d] = (g.n[d] + 1) / 2;
-  }
-  for (int d = 0; d < 3; ++d) {
-    double cell;
-    if (g.periodic) {
-      cell = g.box[d] / g.n[d];
-    } else {
-      double ext = (double)hb[3 + d] - (double)hb[d];
-      cell = fmax(cs, ext / g.n[d]);
-    }
-    g.inv_cell[d] = 1.0 / cell;
-  }
-  const int ncell = g.n[0] * g.n[1] * g.n[2];
 
-  // 3. bin atoms by cell
+  // 2.-3. bin atoms by cell (launch sizes from the cell bound; the kernels
+  // read the grid and its cell count from device memory)
   const int tb = 256;
   const int nblk = (n + tb - 1) / tb;
-  hipLaunchKernelGGL(nb_zero_kernel, dim3((ncell + 1 + 255) / 256), dim3(256), 0, stream,
-                     cell_count, (int64_t)ncell + 1);
-  hipLaunchKernelGGL(nb_zero_kernel, dim3(1), dim3(64), 0, stream, (int*)(ws + L.scalars), 16);
-  hipLaunchKernelGGL(nb_assign_kernel, dim3(nblk), dim3(tb), 0, stream, pos, n, g, cell_of,
+  hipLaunchKernelGGL(nb_zero_kernel, dim3((unsigned)((ncell_max + 1 + 255) / 256)), dim3(256), 0, stream,
+                     cell_count, (int64_t)ncell_max + 1);
+  hipLaunchKernelGGL(nb_assign_kernel, dim3(nblk), dim3(tb), 0, stream, pos, n, (const GridParams*)grid, cell_of,
                      cell_count);
-  hipLaunchKernelGGL(nb_scan_kernel, dim3(1), dim3(1024), 0, stream, cell_count, ncell,
-                     cell_start, (long long*)nullptr);
-  SO2_CHECK(hipMemcpyAsync(cursor, cell_start, sizeof(int) * (size_t)ncell,
-                           hipMemcpyDeviceToDevice, stream));
+  hipLaunchKernelGGL(nb_scan_kernel, dim3(1), dim3(1024), 0, stream, cell_count, 0, (const int*)ncell_dev,
+                     cell_start, cursor, (long long*)nullptr);
   hipLaunchKernelGGL(nb_scatter_kernel, dim3(nblk), dim3(tb), 0, stream, pos, mol_id, n, cell_of,
                      cursor, sorted_idx, sorted_pos, sorted_mol);
   SO2_CHECK_LAUNCH();
@@ -439,15 +460,16 @@ so2_status neighbors_build(const float* pos, int32_t n, const int32_t* mol_id,
   // 4. count, scan, read E
   const double rc2 = rc * rc;
   const int nblk_pairs = (n + tb / kGroup - 1) / (tb / kGroup);
-  hipLaunchKernelGGL(nb_pairs_kernel<false>, dim3(nblk_pairs), dim3(tb), 0, stream, pos, mol_id, n, g,
-                     rc2, cell_start, sorted_idx, sorted_pos, sorted_mol, counts,
+  hipLaunchKernelGGL(nb_pairs_kernel<false>, dim3(nblk_pairs), dim3(tb), 0, stream, pos, mol_id, n,
+                     (const GridParams*)grid, rc2, cell_start, sorted_idx, sorted_pos, sorted_mol, counts,
                      (const int*)nullptr, (int*)nullptr, long_rows, n_long, n_over);
-  hipLaunchKernelGGL(nb_scan_kernel, dim3(1), dim3(1024), 0, stream, counts, n, row_ptr,
-                     e_total);
+  hipLaunchKernelGGL(nb_scan_kernel, dim3(1), dim3(1024), 0, stream, counts, n, (const int*)nullptr, row_ptr,
+                     (int*)nullptr, e_total);
   SO2_CHECK_LAUNCH();
-  long long hs[2] = {0, 0};
-  SO2_CHECK(hipMemcpyAsync(hs, e_total, 16, hipMemcpyDeviceToHost, stream));
+  long long hs[3] = {0, 0, 0};
+  SO2_CHECK(hipMemcpyAsync(hs, e_total, 24, hipMemcpyDeviceToHost, stream));
   SO2_CHECK(hipStreamSynchronize(stream));
+  if (hs[2] & 0xffffffffLL) return SO2_ERR_INVALID_ARGUMENT;  // non-finite positions
   const long long E = hs[0];
   const int h_long = (int)(hs[1] & 0xffffffffLL);
   const int h_over = (int)((unsigned long long)hs[1] >> 32);
@@ -457,8 +479,8 @@ so2_status neighbors_build(const float* pos, int32_t n, const int32_t* mol_id,
   if (E > capacity) return SO2_ERR_CAPACITY;
 
   // 5. fill and sort rows
-  hipLaunchKernelGGL(nb_pairs_kernel<true>, dim3(nblk_pairs), dim3(tb), 0, stream, pos, mol_id, n, g,
-                     rc2, cell_start, sorted_idx, sorted_pos, sorted_mol, (int*)nullptr, row_ptr,
+  hipLaunchKernelGGL(nb_pairs_kernel<true>, dim3(nblk_pairs), dim3(tb), 0, stream, pos, mol_id, n,
+                     (const GridParams*)grid, rc2, cell_start, sorted_idx, sorted_pos, sorted_mol, (int*)nullptr, row_ptr,
                      col, (int*)nullptr, (int*)nullptr, (int*)nullptr);
   hipLaunchKernelGGL(nb_sort_short_kernel, dim3(n), dim3(64), 0, stream, row_ptr, col, n);
   if (h_long > 0)
