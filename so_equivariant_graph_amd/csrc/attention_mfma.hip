@@ -89,7 +89,7 @@ constexpr int kNT = kC / (16 * kWaves);  // 16-column tiles per wave: wave w own
 constexpr int kGR = 1;                // generator rows per lane and K step
 constexpr int kMaxM = 64;             // largest chunk
 constexpr int kSlots = 4;             // targets live in one chunk
-constexpr int kEdgesPerGroup = 384;   // edges per workgroup (about six 64-edge chunks)
+constexpr int kEdgesPerGroup = 384;   // edges per workgroup for L = 5, 6 (twelve 32-edge chunks)
 constexpr int kKC = 128;              // channels per A chunk (one degree, 4 MFMA K steps)
 constexpr int kMaxHeads = 16;
 constexpr int kMaxRbf = 32;           // radial basis functions kept per edge in LDS
@@ -1257,6 +1257,75 @@ __global__ void __launch_bounds__(256) attn_order_kernel(const int32_t* __restri
   }
 }
 
+// Work of target t in 1/64 of a chunk, an additive estimate of the fused
+// kernel's greedy chunking (at most chunk_m edges and kSlots targets per
+// chunk): a target takes d / chunk_m chunks, and at least 1 / kSlots of one.
+__device__ inline int64_t target_work(int d, int chunk_m) {
+  const int64_t w = (int64_t)d * (64 / chunk_m);
+  return w > 64 / kSlots ? w : 64 / kSlots;
+}
+
+// Schedule of the fused kernel for L <= 4, one workgroup of 1024 threads:
+// the prefix sums wsum[t] of target_work over targets 0..t-1 (a block scan
+// per 1024 targets), then the group starts: group g starts at the first
+// target with wsum >= g W / n_groups (W = total work), group n_groups at
+// n_targets, and the identity order.  With one group per compute unit the
+// groups hold equal estimated work and all run at once, so the makespan is
+// that of the largest group; at the small-molecule workload this beat
+// equal-edge groups dispatched longest first (attn_order_kernel), which the
+// 32-edge chunks of L = 5, 6 keep, since there whole targets (about three
+// chunks each) are too coarse a unit for one group per compute unit.
+constexpr int kSchedThreads = 1024;
+__global__ void __launch_bounds__(kSchedThreads) attn_groups_kernel(const int32_t* __restrict__ row_ptr,
+                                                                    int n_targets, int n_groups, int chunk_m,
+                                                                    int64_t* __restrict__ wsum,
+                                                                    int32_t* __restrict__ gs,
+                                                                    int32_t* __restrict__ order) {
+  __shared__ int64_t part[kSchedThreads / 64];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  int64_t carry = 0;
+  if (t == 0) wsum[0] = 0;
+  for (int base = 0; base < n_targets; base += kSchedThreads) {
+    const int i = base + t;
+    int64_t v = i < n_targets ? target_work(row_ptr[i + 1] - row_ptr[i], chunk_m) : 0;
+    // inclusive scan within the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t o = __shfl_up(v, off, 64);
+      if (lane >= off) v += o;
+    }
+    if (lane == 63) part[wv] = v;
+    __syncthreads();
+    int64_t before = carry, total = 0;
+#pragma unroll
+    for (int k = 0; k < kSchedThreads / 64; ++k) {
+      if (k < wv) before += part[k];
+      total += part[k];
+    }
+    if (i < n_targets) wsum[i + 1] = before + v;
+    carry += total;
+    __syncthreads();  // part is rewritten by the next block of targets
+  }
+  __threadfence();
+  __syncthreads();
+  const int64_t W = carry;
+  for (int g = t; g <= n_groups; g += kSchedThreads) {
+    int res = n_targets;
+    if (g < n_groups) {
+      const int64_t goal = (W * g) / n_groups;
+      int lo = 0, hi = n_targets;  // smallest t in [0, n_targets] with wsum[t] >= goal
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (wsum[mid] >= goal) hi = mid;
+        else lo = mid + 1;
+      }
+      res = lo;
+    }
+    gs[g] = res;
+    if (g < n_groups) order[g] = g;  // one group per compute unit: no ordering
+  }
+}
+
 template <int L>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 attn_mfma_kernel(MfmaParams P, int n_groups) {
@@ -1275,11 +1344,10 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
   constexpr int CM = Geo<L>::M, GL = Geo<L>::GL, MP = Geo<L>::MP;
   typedef typename XVec<Geo<L>::GCH>::type XV;
 
-  // Workgroup -> group of consecutive targets holding about E / n_groups
-  // edges (group g starts at the first target whose edges start at or after
-  // g E / n_groups).  Workgroups are dispatched to the 8 XCDs round robin;
-  // XCD x takes a contiguous range of groups, since neighbouring groups
-  // share neighbours in L2, in the order attn_order_kernel chose.
+  // Workgroup -> group of consecutive targets (attn_groups_kernel or
+  // attn_order_kernel chose the group starts).  Workgroups are dispatched to
+  // the 8 XCDs round robin; XCD x takes a contiguous range of groups, since
+  // neighbouring groups share neighbours in L2, in the order P.order holds.
   const int b = blockIdx.x;
   const int grp = P.order[xcd_first(b % 8, n_groups) + b / 8];
   const int t_begin = P.gs[grp];
@@ -1506,18 +1574,26 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
   }
 }
 
-// Workgroups: about kEdgesPerGroup edges each, rounded up to a whole number
-// of waves of workgroups over the device's compute units (one per CU).
+// Workgroups: for L <= 4 one per compute unit, each with an equal share of
+// the estimated work; for L = 5, 6 about kEdgesPerGroup edges each, rounded
+// up to a whole number of waves of workgroups over the compute units.
 template <int L>
-so2_status launch_L(const MfmaParams& P, int32_t* bucket, int64_t n_edges, hipStream_t stream) {
+so2_status launch_L(const MfmaParams& P, int32_t* bucket, int64_t* wsum, int64_t n_edges, hipStream_t stream) {
   int dev = 0, n_cu = 256;
   SO2_CHECK(hipGetDevice(&dev));
   SO2_CHECK(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
-  int64_t want = (n_edges + kEdgesPerGroup - 1) / kEdgesPerGroup;
-  want = ((want + n_cu - 1) / n_cu) * n_cu;
-  const int n_groups = (int)std::max<int64_t>(1, std::min<int64_t>(want, P.n_targets));
-  hipLaunchKernelGGL(attn_order_kernel, dim3(8), dim3(256), 0, stream, P.row_ptr, P.n_targets, n_groups,
-                     Geo<L>::M, const_cast<int32_t*>(P.gs), bucket, const_cast<int32_t*>(P.order));
+  int n_groups;
+  if constexpr (L <= 4) {
+    n_groups = std::max(1, std::min(n_cu, P.n_targets));
+    hipLaunchKernelGGL(attn_groups_kernel, dim3(1), dim3(kSchedThreads), 0, stream, P.row_ptr, P.n_targets,
+                       n_groups, Geo<L>::M, wsum, const_cast<int32_t*>(P.gs), const_cast<int32_t*>(P.order));
+  } else {
+    int64_t want = (n_edges + kEdgesPerGroup - 1) / kEdgesPerGroup;
+    want = ((want + n_cu - 1) / n_cu) * n_cu;
+    n_groups = (int)std::max<int64_t>(1, std::min<int64_t>(want, P.n_targets));
+    hipLaunchKernelGGL(attn_order_kernel, dim3(8), dim3(256), 0, stream, P.row_ptr, P.n_targets, n_groups,
+                       Geo<L>::M, const_cast<int32_t*>(P.gs), bucket, const_cast<int32_t*>(P.order));
+  }
   SO2_CHECK_LAUNCH();
   const size_t smem = Lds<L>::kTotal;
   static_assert(Lds<L>::kTotal <= 160 * 1024, "LDS budget");
@@ -1531,7 +1607,7 @@ so2_status launch_L(const MfmaParams& P, int32_t* bucket, int64_t n_edges, hipSt
 // Workspace of the MFMA path: softmax statistics, the x pairs, w_rad in
 // fp32 and w_so2 in fragment order.
 struct ScratchLayout {
-  size_t stats, xp, wrad, wf, gs, bucket, order, total;
+  size_t stats, xp, wrad, wf, gs, bucket, order, wsum, total;
 };
 
 size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -1546,7 +1622,8 @@ ScratchLayout scratch_layout(int n_atoms, int n_targets, int L, int H, int K) {
   // at most n_targets groups
   s.bucket = s.gs + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
   s.order = s.bucket + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
-  s.total = s.order + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
+  s.wsum = s.order + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
+  s.total = s.wsum + up256(sizeof(int64_t) * ((size_t)n_targets + 1));
   return s;
 }
 
@@ -1644,20 +1721,22 @@ so2_status launch_attention_mfma_prep(const AttnArgs& a, hipStream_t stream) {
 so2_status launch_attention_mfma(const AttnArgs& a, hipStream_t stream) {
   if (a.n_targets == 0) return SO2_OK;
   const MfmaParams P = make_params(a);
-  int32_t* bucket = (int32_t*)((char*)a.scratch + scratch_layout(a.n_atoms, a.n_targets, a.L, a.H, a.K).bucket);
+  const ScratchLayout s = scratch_layout(a.n_atoms, a.n_targets, a.L, a.H, a.K);
+  int32_t* bucket = (int32_t*)((char*)a.scratch + s.bucket);
+  int64_t* wsum = (int64_t*)((char*)a.scratch + s.wsum);
   switch (a.L) {
     case 1:
-      return launch_L<1>(P, bucket, a.n_edges, stream);
+      return launch_L<1>(P, bucket, wsum, a.n_edges, stream);
     case 2:
-      return launch_L<2>(P, bucket, a.n_edges, stream);
+      return launch_L<2>(P, bucket, wsum, a.n_edges, stream);
     case 3:
-      return launch_L<3>(P, bucket, a.n_edges, stream);
+      return launch_L<3>(P, bucket, wsum, a.n_edges, stream);
     case 4:
-      return launch_L<4>(P, bucket, a.n_edges, stream);
+      return launch_L<4>(P, bucket, wsum, a.n_edges, stream);
     case 5:
-      return launch_L<5>(P, bucket, a.n_edges, stream);
+      return launch_L<5>(P, bucket, wsum, a.n_edges, stream);
     case 6:
-      return launch_L<6>(P, bucket, a.n_edges, stream);
+      return launch_L<6>(P, bucket, wsum, a.n_edges, stream);
   }
   return SO2_ERR_UNSUPPORTED;
 }

@@ -75,8 +75,7 @@ __device__ inline int comp_degree(int comp) {
 constexpr int kMaxVec = 16;
 template <typename T, int MV>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MV <= 8 ? 4 : 2)))
-merged_rms_norm_reg_kernel(const T* x, const float* __restrict__ gamma, T* y,
-                                                                  int n_atoms, int nc, int C, float eps) {
+merged_rms_norm_reg_kernel(const T* x, const float* __restrict__ gamma, T* y, int n_atoms, int nc, int C, float eps) {
   constexpr int N = NormVec<T>::N;
   const int lane = threadIdx.x & 63;
   const int node = blockIdx.x * 4 + (threadIdx.x >> 6);
