@@ -1265,30 +1265,90 @@ __device__ inline int64_t target_work(int d, int chunk_m) {
   return w > 64 / kSlots ? w : 64 / kSlots;
 }
 
-// Schedule of the fused kernel for L <= 4, one workgroup of 1024 threads:
-// the prefix sums wsum[t] of target_work over targets 0..t-1 (a block scan
-// per 1024 targets), then the group starts: group g starts at the first
-// target with wsum >= g W / n_groups (W = total work), group n_groups at
-// n_targets, and the identity order.  With one group per compute unit the
-// groups hold equal estimated work and all run at once, so the makespan is
-// that of the largest group; at the small-molecule workload this beat
-// equal-edge groups dispatched longest first (attn_order_kernel), which the
-// 32-edge chunks of L = 5, 6 keep, since there whole targets (about three
-// chunks each) are too coarse a unit for one group per compute unit.
+// Schedule of the fused kernel for L <= 4, one workgroup of 1024 threads.
+// With W the total work and wsum[t] the work of targets 0..t-1, run g of
+// n_groups starts at the first target t with wsum[t] >= goal_g =
+// floor(g W / n_groups), and run n_groups at n_targets.  Runs are written
+// from the prefix sums without a search: the number of runs whose goal is
+// at most X is runs_upto(X) = min(n_groups, ceil((X + 1) n_groups / W)), so
+// target i, with wsum[i] = a and wsum[i + 1] = b, starts runs
+// [runs_upto(a), runs_upto(b)) at i + 1, and run 0 starts at 0.  The first
+// pass sums W; the second scans the targets kSchedItems per thread and
+// walks the run index along them.  With
+// one run per compute unit the runs hold equal estimated work and all run
+// at once, so the makespan is that of the largest; at the small-molecule
+// workload this beat equal-edge groups dispatched longest first
+// (attn_order_kernel), which the 32-edge chunks of L = 5, 6 keep, since
+// there whole targets (about three chunks each) are too coarse a unit for
+// one run per compute unit.
 constexpr int kSchedThreads = 1024;
+constexpr int kSchedItems = 8;
+
+__device__ inline int runs_upto(int64_t X, int64_t W, int n_groups) {
+  const int64_t r = ((X + 1) * n_groups + W - 1) / W;
+  return r < n_groups ? (int)r : n_groups;
+}
+
 __global__ void __launch_bounds__(kSchedThreads) attn_groups_kernel(const int32_t* __restrict__ row_ptr,
                                                                     int n_targets, int n_groups, int chunk_m,
-                                                                    int64_t* __restrict__ wsum,
                                                                     int32_t* __restrict__ gs,
                                                                     int32_t* __restrict__ order) {
+  constexpr int kSpan = kSchedThreads * kSchedItems;
   __shared__ int64_t part[kSchedThreads / 64];
+  __shared__ int wbuf[kSpan + kSpan / 32];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+
+  // pass 1: W
+  int64_t s = 0;
+  for (int base = 0; base < n_targets; base += kSpan) {
+    int d[kSchedItems];  // clamped, unpredicated loads: all in flight at once
+#pragma unroll
+    for (int j = 0; j < kSchedItems; ++j) {
+      const int i = min(base + j * kSchedThreads + t, n_targets - 1);
+      d[j] = row_ptr[i + 1] - row_ptr[i];
+    }
+#pragma unroll
+    for (int j = 0; j < kSchedItems; ++j)
+      if (base + j * kSchedThreads + t < n_targets) s += target_work(d[j], chunk_m);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+  if (lane == 0) part[wv] = s;
+  __syncthreads();
+  int64_t W = 0;
+#pragma unroll
+  for (int k = 0; k < kSchedThreads / 64; ++k) W += part[k];
+  __syncthreads();  // part is reused below
+
+  if (t == 0) {
+    gs[0] = 0;
+    gs[n_groups] = n_targets;
+  }
+  if (t < n_groups) order[t] = t;  // one run per compute unit: no ordering
+
+  // pass 2: targets i0 .. i0 + kSchedItems - 1 of each thread, their work
+  // staged through LDS so that the row_ptr loads stay coalesced (the LDS
+  // index is padded by one word per 32 to spread the reads over the banks)
   int64_t carry = 0;
-  if (t == 0) wsum[0] = 0;
-  for (int base = 0; base < n_targets; base += kSchedThreads) {
-    const int i = base + t;
-    int64_t v = i < n_targets ? target_work(row_ptr[i + 1] - row_ptr[i], chunk_m) : 0;
-    // inclusive scan within the wave
+  for (int base = 0; base < n_targets; base += kSpan) {
+#pragma unroll
+    for (int j = 0; j < kSchedItems; ++j) {
+      const int i = min(base + j * kSchedThreads + t, n_targets - 1);
+      const int dj = row_ptr[i + 1] - row_ptr[i];
+      const int k = j * kSchedThreads + t;
+      wbuf[k + (k >> 5)] = base + k < n_targets ? (int)target_work(dj, chunk_m) : 0;
+    }
+    __syncthreads();
+    const int i0 = base + t * kSchedItems;
+    int64_t w[kSchedItems];
+    int64_t v = 0;
+#pragma unroll
+    for (int j = 0; j < kSchedItems; ++j) {
+      const int k = t * kSchedItems + j;
+      w[j] = wbuf[k + (k >> 5)];
+      v += w[j];
+    }
+    // inclusive scan of the thread sums within the wave, then across waves
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int64_t o = __shfl_up(v, off, 64);
@@ -1296,33 +1356,24 @@ __global__ void __launch_bounds__(kSchedThreads) attn_groups_kernel(const int32_
     }
     if (lane == 63) part[wv] = v;
     __syncthreads();
-    int64_t before = carry, total = 0;
+    int64_t a = carry, total = 0;
 #pragma unroll
     for (int k = 0; k < kSchedThreads / 64; ++k) {
-      if (k < wv) before += part[k];
+      if (k < wv) a += part[k];
       total += part[k];
     }
-    if (i < n_targets) wsum[i + 1] = before + v;
-    carry += total;
-    __syncthreads();  // part is rewritten by the next block of targets
-  }
-  __threadfence();
-  __syncthreads();
-  const int64_t W = carry;
-  for (int g = t; g <= n_groups; g += kSchedThreads) {
-    int res = n_targets;
-    if (g < n_groups) {
-      const int64_t goal = (W * g) / n_groups;
-      int lo = 0, hi = n_targets;  // smallest t in [0, n_targets] with wsum[t] >= goal
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (wsum[mid] >= goal) hi = mid;
-        else lo = mid + 1;
-      }
-      res = lo;
+    a += __shfl_up(v, 1, 64) * (lane > 0);  // exclusive prefix of this thread
+    // goal_g <= X  <=>  g W < (X + 1) n_groups: one division per thread
+    int g = runs_upto(a, W, n_groups);
+#pragma unroll
+    for (int j = 0; j < kSchedItems; ++j) {
+      const int i = i0 + j;
+      a += w[j];
+      if (i < n_targets)
+        for (; g < n_groups && (int64_t)g * W < (a + 1) * n_groups; ++g) gs[g] = i + 1;
     }
-    gs[g] = res;
-    if (g < n_groups) order[g] = g;  // one group per compute unit: no ordering
+    carry += total;
+    __syncthreads();  // part is rewritten by the next span
   }
 }
 
@@ -1578,7 +1629,7 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
 // the estimated work; for L = 5, 6 about kEdgesPerGroup edges each, rounded
 // up to a whole number of waves of workgroups over the compute units.
 template <int L>
-so2_status launch_L(const MfmaParams& P, int32_t* bucket, int64_t* wsum, int64_t n_edges, hipStream_t stream) {
+so2_status launch_L(const MfmaParams& P, int32_t* bucket, int64_t n_edges, hipStream_t stream) {
   int dev = 0, n_cu = 256;
   SO2_CHECK(hipGetDevice(&dev));
   SO2_CHECK(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
@@ -1586,7 +1637,7 @@ so2_status launch_L(const MfmaParams& P, int32_t* bucket, int64_t* wsum, int64_t
   if constexpr (L <= 4) {
     n_groups = std::max(1, std::min(n_cu, P.n_targets));
     hipLaunchKernelGGL(attn_groups_kernel, dim3(1), dim3(kSchedThreads), 0, stream, P.row_ptr, P.n_targets,
-                       n_groups, Geo<L>::M, wsum, const_cast<int32_t*>(P.gs), const_cast<int32_t*>(P.order));
+                       n_groups, Geo<L>::M, const_cast<int32_t*>(P.gs), const_cast<int32_t*>(P.order));
   } else {
     int64_t want = (n_edges + kEdgesPerGroup - 1) / kEdgesPerGroup;
     want = ((want + n_cu - 1) / n_cu) * n_cu;
@@ -1607,7 +1658,7 @@ so2_status launch_L(const MfmaParams& P, int32_t* bucket, int64_t* wsum, int64_t
 // Workspace of the MFMA path: softmax statistics, the x pairs, w_rad in
 // fp32 and w_so2 in fragment order.
 struct ScratchLayout {
-  size_t stats, xp, wrad, wf, gs, bucket, order, wsum, total;
+  size_t stats, xp, wrad, wf, gs, bucket, order, total;
 };
 
 size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -1622,8 +1673,7 @@ ScratchLayout scratch_layout(int n_atoms, int n_targets, int L, int H, int K) {
   // at most n_targets groups
   s.bucket = s.gs + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
   s.order = s.bucket + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
-  s.wsum = s.order + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
-  s.total = s.wsum + up256(sizeof(int64_t) * ((size_t)n_targets + 1));
+  s.total = s.order + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
   return s;
 }
 
@@ -1721,22 +1771,20 @@ so2_status launch_attention_mfma_prep(const AttnArgs& a, hipStream_t stream) {
 so2_status launch_attention_mfma(const AttnArgs& a, hipStream_t stream) {
   if (a.n_targets == 0) return SO2_OK;
   const MfmaParams P = make_params(a);
-  const ScratchLayout s = scratch_layout(a.n_atoms, a.n_targets, a.L, a.H, a.K);
-  int32_t* bucket = (int32_t*)((char*)a.scratch + s.bucket);
-  int64_t* wsum = (int64_t*)((char*)a.scratch + s.wsum);
+  int32_t* bucket = (int32_t*)((char*)a.scratch + scratch_layout(a.n_atoms, a.n_targets, a.L, a.H, a.K).bucket);
   switch (a.L) {
     case 1:
-      return launch_L<1>(P, bucket, wsum, a.n_edges, stream);
+      return launch_L<1>(P, bucket, a.n_edges, stream);
     case 2:
-      return launch_L<2>(P, bucket, wsum, a.n_edges, stream);
+      return launch_L<2>(P, bucket, a.n_edges, stream);
     case 3:
-      return launch_L<3>(P, bucket, wsum, a.n_edges, stream);
+      return launch_L<3>(P, bucket, a.n_edges, stream);
     case 4:
-      return launch_L<4>(P, bucket, wsum, a.n_edges, stream);
+      return launch_L<4>(P, bucket, a.n_edges, stream);
     case 5:
-      return launch_L<5>(P, bucket, wsum, a.n_edges, stream);
+      return launch_L<5>(P, bucket, a.n_edges, stream);
     case 6:
-      return launch_L<6>(P, bucket, wsum, a.n_edges, stream);
+      return launch_L<6>(P, bucket, a.n_edges, stream);
   }
   return SO2_ERR_UNSUPPORTED;
 }

@@ -161,36 +161,76 @@ __global__ void nb_assign_kernel(const float* __restrict__ pos, int n, const Gri
 
 // Exclusive scan of in[0..n) into out[0..n] (and out2[0..n) if given),
 // out[n] = total (int32), total also stored as int64 in *total64; n is read
-// from n_dev when that is given.  One workgroup of 1024 threads.
-__global__ void __launch_bounds__(1024) nb_scan_kernel(const int* __restrict__ in, int n,
-                                                      const int* __restrict__ n_dev, int* __restrict__ out,
-                                                      int* __restrict__ out2, long long* __restrict__ total64) {
-  __shared__ long long s[1024];
-  int t = threadIdx.x;
+// from n_dev when that is given.  One workgroup of 1024 threads walks the
+// input in spans of 8192 values.  A span is loaded with coalesced loads into
+// LDS; each thread then takes 8 consecutive values, the thread sums are
+// scanned with wave shuffles and across the 16 waves, the results go back
+// through LDS and out with coalesced stores; a running carry links the
+// spans.  The LDS index is padded by one word per 32 so that the
+// consecutive-value reads of a wave spread over the banks.
+constexpr int kScanThreads = 1024;
+constexpr int kScanItems = 8;
+constexpr int kScanSpan = kScanThreads * kScanItems;
+__device__ inline int scan_pad(int i) { return i + (i >> 5); }
+
+__global__ void __launch_bounds__(kScanThreads) nb_scan_kernel(const int* __restrict__ in, int n,
+                                                               const int* __restrict__ n_dev, int* __restrict__ out,
+                                                               int* __restrict__ out2, long long* __restrict__ total64) {
+  __shared__ long long part[kScanThreads / 64];
+  __shared__ int buf[kScanSpan + kScanSpan / 32];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   if (n_dev) n = *n_dev;
-  int per = (n + blockDim.x - 1) / blockDim.x;
-  int a = t * per;
-  int b = min(n, a + per);
-  long long sum = 0;
-  for (int i = a; i < b; ++i) sum += in[i];
-  s[t] = sum;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 partial sums.
-  for (int off = 1; off < 1024; off <<= 1) {
-    long long v = (t >= off) ? s[t - off] : 0;
+  long long carry = 0;
+  for (int base = 0; base < n; base += kScanSpan) {
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) {
+      const int i = base + j * kScanThreads + t;
+      const int x = in[min(i, n - 1)];
+      buf[scan_pad(j * kScanThreads + t)] = i < n ? x : 0;
+    }
     __syncthreads();
-    s[t] += v;
+    int v[kScanItems];
+    long long sum = 0;
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) {
+      v[j] = buf[scan_pad(t * kScanItems + j)];
+      sum += v[j];
+    }
+    long long incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) part[wv] = incl;
     __syncthreads();
+    long long run = carry + incl - sum, total = 0;
+#pragma unroll
+    for (int k = 0; k < kScanThreads / 64; ++k) {
+      if (k < wv) run += part[k];
+      total += part[k];
+    }
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) {
+      buf[scan_pad(t * kScanItems + j)] = (int)run;
+      run += v[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) {
+      const int i = base + j * kScanThreads + t;
+      if (i < n) {
+        const int r = buf[scan_pad(j * kScanThreads + t)];
+        out[i] = r;
+        if (out2) out2[i] = r;
+      }
+    }
+    carry += total;
+    __syncthreads();  // part and buf are rewritten by the next span
   }
-  long long run = s[t] - sum;
-  for (int i = a; i < b; ++i) {
-    out[i] = (int)run;
-    if (out2) out2[i] = (int)run;
-    run += in[i];
-  }
-  if (t == blockDim.x - 1) {
-    out[n] = (int)s[t];
-    if (total64) *total64 = s[t];
+  if (t == 0) {
+    out[n] = (int)carry;
+    if (total64) *total64 = carry;
   }
 }
 
@@ -451,7 +491,7 @@ so2_status neighbors_build(const float* pos, int32_t n, const int32_t* mol_id,
                      cell_count, (int64_t)ncell_max + 1);
   hipLaunchKernelGGL(nb_assign_kernel, dim3(nblk), dim3(tb), 0, stream, pos, n, (const GridParams*)grid, cell_of,
                      cell_count);
-  hipLaunchKernelGGL(nb_scan_kernel, dim3(1), dim3(1024), 0, stream, cell_count, 0, (const int*)ncell_dev,
+  hipLaunchKernelGGL(nb_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, cell_count, 0, (const int*)ncell_dev,
                      cell_start, cursor, (long long*)nullptr);
   hipLaunchKernelGGL(nb_scatter_kernel, dim3(nblk), dim3(tb), 0, stream, pos, mol_id, n, cell_of,
                      cursor, sorted_idx, sorted_pos, sorted_mol);
@@ -463,7 +503,7 @@ so2_status neighbors_build(const float* pos, int32_t n, const int32_t* mol_id,
   hipLaunchKernelGGL(nb_pairs_kernel<false>, dim3(nblk_pairs), dim3(tb), 0, stream, pos, mol_id, n,
                      (const GridParams*)grid, rc2, cell_start, sorted_idx, sorted_pos, sorted_mol, counts,
                      (const int*)nullptr, (int*)nullptr, long_rows, n_long, n_over);
-  hipLaunchKernelGGL(nb_scan_kernel, dim3(1), dim3(1024), 0, stream, counts, n, (const int*)nullptr, row_ptr,
+  hipLaunchKernelGGL(nb_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts, n, (const int*)nullptr, row_ptr,
                      (int*)nullptr, e_total);
   SO2_CHECK_LAUNCH();
   long long hs[3] = {0, 0, 0};
