@@ -1258,10 +1258,11 @@ __global__ void __launch_bounds__(256) attn_order_kernel(const int32_t* __restri
 }
 
 // Work of target t in 1/64 of a chunk, an additive estimate of the fused
-// kernel's greedy chunking (at most chunk_m edges and kSlots targets per
-// chunk): a target takes d / chunk_m chunks, and at least 1 / kSlots of one.
-__device__ inline int64_t target_work(int d, int chunk_m) {
-  const int64_t w = (int64_t)d * (64 / chunk_m);
+// kernel's greedy chunking (at most CM edges and kSlots targets per
+// chunk): a target takes d / CM chunks, and at least 1 / kSlots of one.
+template <int CM>
+__device__ inline int64_t target_work(int d) {
+  const int64_t w = (int64_t)d * (64 / CM);
   return w > 64 / kSlots ? w : 64 / kSlots;
 }
 
@@ -1289,66 +1290,108 @@ __device__ inline int runs_upto(int64_t X, int64_t W, int n_groups) {
   return r < n_groups ? (int)r : n_groups;
 }
 
+// One chunk of the fused kernel's greedy chunking (at most CM edges
+// and kSlots targets per chunk) in a run that ends at target x (e_x =
+// rp(x)): from edge e of target t (rp(t) <= e < rp(t + 1)) the chunk ends at
+// min(e + CM, e_x, rp(min(t + kSlots, x))); t moves to the last target
+// that starts at or before that end.  The kSlots row offsets are read at
+// once; only targets without edges right at the end need the slow loop.
+template <int CM, typename RP>
+__device__ inline int chunk_end(const RP& rp, int& t, int e, int x, int e_x) {
+  int r[kSlots];
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) r[j] = rp(min(t + 1 + j, x));
+  const int e2 = min(min(e + CM, e_x), r[kSlots - 1]);
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) c += r[j] <= e2;
+  t += c;
+  if (c == kSlots)
+    while (t < x && rp(t + 1) <= e2) ++t;
+  return e2;
+}
+
+// Chunks of run [s, x).
+template <int CM, typename RP>
+__device__ inline int run_chunks(const RP& rp, int s, int x) {
+  int e = rp(s), t = s, c = 0;
+  const int e_x = rp(x);
+  if (e < e_x)
+    while (rp(t + 1) <= e) ++t;
+  while (e < e_x) {
+    e = chunk_end<CM>(rp, t, e, x, e_x);
+    ++c;
+  }
+  return c;
+}
+
+// Exact refinement for graphs of at most kExactTargets targets and
+// kExactRuns runs.  The fused kernel's time per run is close to
+// proportional to the run's chunk count, so the makespan is set by the
+// largest count M of the estimated runs; the whole-number rounding of
+// about 18 chunks per run costs up to a chunk there.  Since greedy maximal
+// chunks are the fewest for any range of targets, the chunk count of a
+// range grows with the range, and the greedy partition under a cap of K
+// chunks per run (each run as long as the cap allows) uses the fewest
+// runs.  attn_groups_kernel counts the chunks of every estimated run (row
+// offsets staged in LDS) and, when M exceeds the mean, sets K = M - 1;
+// attn_runs_next_kernel finds, for every start s, the end next[s] of a
+// greedy run of at most K chunks; attn_runs_chain_kernel follows the chain
+// 0, next[0], next[next[0]], ... by pointer doubling and takes it as the
+// run starts when n_groups runs reach n_targets, else keeps the estimate.
+constexpr int kExactTargets = 12288;
+constexpr int kExactRuns = 256;
+constexpr int kExactItems = (kExactTargets + kSchedThreads) / kSchedThreads;  // row offsets per thread
+
+// dst[i] = src[i] for i = 0..n1-1 (n1 <= kExactTargets + 1) by one workgroup
+// of kSchedThreads, all loads in flight at once.
+__device__ inline void stage_rows(const int32_t* __restrict__ src, int* dst, int n1) {
+  int v[kExactItems];
+#pragma unroll
+  for (int k = 0; k < kExactItems; ++k) v[k] = src[min((int)threadIdx.x + k * kSchedThreads, n1 - 1)];
+#pragma unroll
+  for (int k = 0; k < kExactItems; ++k) {
+    const int i = threadIdx.x + k * kSchedThreads;
+    if (i < n1) dst[i] = v[k];
+  }
+}
+
+template <bool EXACT, int CM>
 __global__ void __launch_bounds__(kSchedThreads) attn_groups_kernel(const int32_t* __restrict__ row_ptr,
-                                                                    int n_targets, int n_groups, int chunk_m,
+                                                                    int n_targets, int n_groups,
                                                                     int32_t* __restrict__ gs,
-                                                                    int32_t* __restrict__ order) {
+                                                                    int32_t* __restrict__ order,
+                                                                    int32_t* __restrict__ sched) {
   constexpr int kSpan = kSchedThreads * kSchedItems;
   __shared__ int64_t part[kSchedThreads / 64];
   __shared__ int wbuf[kSpan + kSpan / 32];
+  __shared__ int gsl[kExactRuns + 1];  // run starts, exact refinement only
+  __shared__ int red[2][kSchedThreads / 64];
+  extern __shared__ int rps[];         // row_ptr, exact refinement only
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-
-  // pass 1: W
-  int64_t s = 0;
-  for (int base = 0; base < n_targets; base += kSpan) {
-    int d[kSchedItems];  // clamped, unpredicated loads: all in flight at once
-#pragma unroll
-    for (int j = 0; j < kSchedItems; ++j) {
-      const int i = min(base + j * kSchedThreads + t, n_targets - 1);
-      d[j] = row_ptr[i + 1] - row_ptr[i];
-    }
-#pragma unroll
-    for (int j = 0; j < kSchedItems; ++j)
-      if (base + j * kSchedThreads + t < n_targets) s += target_work(d[j], chunk_m);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-  if (lane == 0) part[wv] = s;
-  __syncthreads();
-  int64_t W = 0;
-#pragma unroll
-  for (int k = 0; k < kSchedThreads / 64; ++k) W += part[k];
-  __syncthreads();  // part is reused below
-
-  if (t == 0) {
-    gs[0] = 0;
-    gs[n_groups] = n_targets;
-  }
-  if (t < n_groups) order[t] = t;  // one run per compute unit: no ordering
-
-  // pass 2: targets i0 .. i0 + kSchedItems - 1 of each thread, their work
-  // staged through LDS so that the row_ptr loads stay coalesced (the LDS
-  // index is padded by one word per 32 to spread the reads over the banks)
-  int64_t carry = 0;
-  for (int base = 0; base < n_targets; base += kSpan) {
-#pragma unroll
-    for (int j = 0; j < kSchedItems; ++j) {
-      const int i = min(base + j * kSchedThreads + t, n_targets - 1);
-      const int dj = row_ptr[i + 1] - row_ptr[i];
-      const int k = j * kSchedThreads + t;
-      wbuf[k + (k >> 5)] = base + k < n_targets ? (int)target_work(dj, chunk_m) : 0;
-    }
+  if constexpr (EXACT) {
+    stage_rows(row_ptr, rps, n_targets + 1);
     __syncthreads();
-    const int i0 = base + t * kSchedItems;
-    int64_t w[kSchedItems];
+  }
+  // row offsets from LDS in the exact mode, else from memory
+  auto rp = [&](int i) {
+    if constexpr (EXACT) return rps[i];
+    else return row_ptr[i];
+  };
+  if constexpr (EXACT) {
+    // all targets in one span: thread t takes targets kExactItems t ..
+    // kExactItems t + kExactItems - 1, the block scan of the thread sums
+    // gives both the prefixes and W
+    const int i0 = t * kExactItems;
+    int w[kExactItems];
     int64_t v = 0;
 #pragma unroll
-    for (int j = 0; j < kSchedItems; ++j) {
-      const int k = t * kSchedItems + j;
-      w[j] = wbuf[k + (k >> 5)];
+    for (int j = 0; j < kExactItems; ++j) {
+      const int i = min(i0 + j, n_targets - 1);
+      w[j] = i0 + j < n_targets ? (int)target_work<CM>(rp(i + 1) - rp(i)) : 0;
       v += w[j];
     }
-    // inclusive scan of the thread sums within the wave, then across waves
+    const int64_t own = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int64_t o = __shfl_up(v, off, 64);
@@ -1356,25 +1399,206 @@ __global__ void __launch_bounds__(kSchedThreads) attn_groups_kernel(const int32_
     }
     if (lane == 63) part[wv] = v;
     __syncthreads();
-    int64_t a = carry, total = 0;
+    int64_t a = v - own, W = 0;
 #pragma unroll
     for (int k = 0; k < kSchedThreads / 64; ++k) {
       if (k < wv) a += part[k];
-      total += part[k];
+      W += part[k];
     }
-    a += __shfl_up(v, 1, 64) * (lane > 0);  // exclusive prefix of this thread
-    // goal_g <= X  <=>  g W < (X + 1) n_groups: one division per thread
+    if (t == 0) {
+      gs[0] = gsl[0] = 0;
+      gs[n_groups] = gsl[n_groups] = n_targets;
+    }
+    if (t < n_groups) order[t] = t;  // one run per compute unit: no ordering
     int g = runs_upto(a, W, n_groups);
 #pragma unroll
-    for (int j = 0; j < kSchedItems; ++j) {
-      const int i = i0 + j;
+    for (int j = 0; j < kExactItems; ++j) {
       a += w[j];
-      if (i < n_targets)
-        for (; g < n_groups && (int64_t)g * W < (a + 1) * n_groups; ++g) gs[g] = i + 1;
+      if (i0 + j < n_targets)
+        for (; g < n_groups && (int64_t)g * W < (a + 1) * n_groups; ++g) gs[g] = gsl[g] = i0 + j + 1;
     }
-    carry += total;
-    __syncthreads();  // part is rewritten by the next span
+    __syncthreads();
+  } else {
+    // pass 1: W
+    int64_t s = 0;
+    for (int base = 0; base < n_targets; base += kSpan) {
+      int d[kSchedItems];  // clamped, unpredicated loads: all in flight at once
+#pragma unroll
+      for (int j = 0; j < kSchedItems; ++j) {
+        const int i = min(base + j * kSchedThreads + t, n_targets - 1);
+        d[j] = rp(i + 1) - rp(i);
+      }
+#pragma unroll
+      for (int j = 0; j < kSchedItems; ++j)
+        if (base + j * kSchedThreads + t < n_targets) s += target_work<CM>(d[j]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (lane == 0) part[wv] = s;
+    __syncthreads();
+    int64_t W = 0;
+#pragma unroll
+    for (int k = 0; k < kSchedThreads / 64; ++k) W += part[k];
+    __syncthreads();  // part is reused below
+
+    if (t == 0) {
+      gs[0] = 0;
+      gs[n_groups] = n_targets;
+    }
+    if (t < n_groups) order[t] = t;  // one run per compute unit: no ordering
+
+    // pass 2: targets i0 .. i0 + kSchedItems - 1 of each thread, their work
+    // staged through LDS so that the row_ptr loads stay coalesced (the LDS
+    // index is padded by one word per 32 to spread the reads over the banks)
+    int64_t carry = 0;
+    for (int base = 0; base < n_targets; base += kSpan) {
+#pragma unroll
+      for (int j = 0; j < kSchedItems; ++j) {
+        const int i = min(base + j * kSchedThreads + t, n_targets - 1);
+        const int dj = rp(i + 1) - rp(i);
+        const int k = j * kSchedThreads + t;
+        wbuf[k + (k >> 5)] = base + k < n_targets ? (int)target_work<CM>(dj) : 0;
+      }
+      __syncthreads();
+      const int i0 = base + t * kSchedItems;
+      int64_t w[kSchedItems];
+      int64_t v = 0;
+#pragma unroll
+      for (int j = 0; j < kSchedItems; ++j) {
+        const int k = t * kSchedItems + j;
+        w[j] = wbuf[k + (k >> 5)];
+        v += w[j];
+      }
+      // inclusive scan of the thread sums within the wave, then across waves
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int64_t o = __shfl_up(v, off, 64);
+        if (lane >= off) v += o;
+      }
+      if (lane == 63) part[wv] = v;
+      __syncthreads();
+      int64_t a = carry, total = 0;
+#pragma unroll
+      for (int k = 0; k < kSchedThreads / 64; ++k) {
+        if (k < wv) a += part[k];
+        total += part[k];
+      }
+      a += __shfl_up(v, 1, 64) * (lane > 0);  // exclusive prefix of this thread
+      // goal_g <= X  <=>  g W < (X + 1) n_groups: one division per thread
+      int g = runs_upto(a, W, n_groups);
+#pragma unroll
+      for (int j = 0; j < kSchedItems; ++j) {
+        const int i = i0 + j;
+        a += w[j];
+        if (i < n_targets)
+          for (; g < n_groups && (int64_t)g * W < (a + 1) * n_groups; ++g) gs[g] = i + 1;
+      }
+      carry += total;
+      __syncthreads();  // part is rewritten by the next span
+    }
   }
+  if constexpr (!EXACT) return;
+
+  // chunk counts of the estimated runs: their maximum and sum set K
+  int mx = t < n_groups ? run_chunks<CM>(rp, gsl[t], gsl[t + 1]) : 0;
+  int sm = mx;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    mx = max(mx, __shfl_xor(mx, off, 64));
+    sm += __shfl_xor(sm, off, 64);
+  }
+  if (lane == 0) {
+    red[0][wv] = mx;
+    red[1][wv] = sm;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int M = 0, S = 0;
+    for (int k = 0; k < kSchedThreads / 64; ++k) {
+      M = max(M, red[0][k]);
+      S += red[1][k];
+    }
+    sched[0] = M > (S + n_groups - 1) / n_groups ? M - 1 : 0;
+  }
+}
+
+// next[s] for s = 0..n_targets: the end of the greedy run from target s
+// with at most K = sched[0] chunks (the first target that K chunks from
+// row_ptr[s] do not finish), next[n_targets] = n_targets.  One thread per
+// start; every workgroup stages all of row_ptr (at most kExactTargets + 1
+// offsets) in LDS.
+template <int CM>
+__global__ void __launch_bounds__(kSchedThreads) attn_runs_next_kernel(const int32_t* __restrict__ row_ptr,
+                                                                       int n_targets,
+                                                                       const int32_t* __restrict__ sched,
+                                                                       int32_t* __restrict__ next) {
+  const int K = sched[0];
+  if (K == 0) return;
+  extern __shared__ int rpn[];  // n_targets + 1
+  stage_rows(row_ptr, rpn, n_targets + 1);
+  __syncthreads();
+  auto rp = [&](int i) { return rpn[i]; };
+  const int s = blockIdx.x * kSchedThreads + threadIdx.x;
+  if (s > n_targets) return;
+  const int e_end = rp(n_targets);
+  int e = rp(s), t = s;
+  if (e < e_end)
+    while (rp(t + 1) <= e) ++t;
+  for (int c = 0; c < K && e < e_end; ++c) e = chunk_end<CM>(rp, t, e, n_targets, e_end);
+  next[s] = e < e_end ? t : n_targets;  // t holds edge e
+}
+
+// Run starts from next[]: next^2, next^4, next^8 and next^16 by squaring in
+// LDS, the starts of runs 0, 16, 32, ... by one thread along next^16, the
+// rest by one thread per 16 runs along next.  Written to gs only when run
+// n_groups starts at n_targets (the cap K is feasible).
+__global__ void __launch_bounds__(kSchedThreads) attn_runs_chain_kernel(const int32_t* __restrict__ next,
+                                                                        int n_targets, int n_groups,
+                                                                        const int32_t* __restrict__ sched,
+                                                                        int32_t* __restrict__ gs) {
+  if (sched[0] == 0) return;
+  extern __shared__ int lds[];  // 3 (n_targets + 1)
+  __shared__ int pos[kExactRuns + 1];
+  const int t = threadIdx.x, n1 = n_targets + 1;
+  int* A = lds;
+  int* B = lds + n1;
+  int* C = lds + 2 * n1;
+  stage_rows(next, A, n1);
+  __syncthreads();
+  // Y = X o X, all gathers of a thread in flight at once
+  auto square = [&](const int* X, int* Y) {
+    int v[kExactItems];
+#pragma unroll
+    for (int k = 0; k < kExactItems; ++k) v[k] = X[min(t + k * kSchedThreads, n1 - 1)];
+#pragma unroll
+    for (int k = 0; k < kExactItems; ++k) v[k] = X[v[k]];
+#pragma unroll
+    for (int k = 0; k < kExactItems; ++k)
+      if (t + k * kSchedThreads < n1) Y[t + k * kSchedThreads] = v[k];
+    __syncthreads();
+  };
+  square(A, B);
+  square(B, C);
+  square(C, B);
+  square(B, C);
+  if (t == 0) {
+    int x = 0;
+    for (int j = 0; 16 * j <= n_groups; ++j) {
+      pos[16 * j] = x;
+      x = C[x];
+    }
+  }
+  __syncthreads();
+  if (16 * t < n_groups) {
+    int x = pos[16 * t];
+    for (int r = 1; r < 16 && 16 * t + r <= n_groups; ++r) {
+      x = A[x];
+      pos[16 * t + r] = x;
+    }
+  }
+  __syncthreads();
+  if (pos[n_groups] == n_targets)
+    for (int g = t; g < n_groups; g += kSchedThreads) gs[g] = pos[g];
 }
 
 template <int L>
@@ -1629,15 +1853,37 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
 // the estimated work; for L = 5, 6 about kEdgesPerGroup edges each, rounded
 // up to a whole number of waves of workgroups over the compute units.
 template <int L>
-so2_status launch_L(const MfmaParams& P, int32_t* bucket, int64_t n_edges, hipStream_t stream) {
+so2_status launch_L(const MfmaParams& P, int32_t* bucket, int32_t* sched, int64_t n_edges, hipStream_t stream) {
   int dev = 0, n_cu = 256;
   SO2_CHECK(hipGetDevice(&dev));
   SO2_CHECK(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
   int n_groups;
   if constexpr (L <= 4) {
     n_groups = std::max(1, std::min(n_cu, P.n_targets));
-    hipLaunchKernelGGL(attn_groups_kernel, dim3(1), dim3(kSchedThreads), 0, stream, P.row_ptr, P.n_targets,
-                       n_groups, Geo<L>::M, const_cast<int32_t*>(P.gs), const_cast<int32_t*>(P.order));
+    const bool exact = P.n_targets <= kExactTargets && n_groups <= kExactRuns;
+    if (exact) {
+      constexpr int CM = Geo<L>::M;
+      const size_t lds1 = sizeof(int) * ((size_t)P.n_targets + 1);
+      SO2_CHECK(hipFuncSetAttribute((const void*)(attn_groups_kernel<true, CM>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)(sizeof(int) * (kExactTargets + 1))));
+      hipLaunchKernelGGL((attn_groups_kernel<true, CM>), dim3(1), dim3(kSchedThreads), lds1, stream, P.row_ptr,
+                         P.n_targets, n_groups, const_cast<int32_t*>(P.gs), const_cast<int32_t*>(P.order), sched);
+      SO2_CHECK_LAUNCH();
+      hipLaunchKernelGGL(attn_runs_next_kernel<CM>, dim3((P.n_targets + kSchedThreads) / kSchedThreads),
+                         dim3(kSchedThreads), lds1, stream, P.row_ptr, P.n_targets, (const int32_t*)sched, bucket);
+      SO2_CHECK_LAUNCH();
+      SO2_CHECK(hipFuncSetAttribute((const void*)attn_runs_chain_kernel,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)(3 * sizeof(int) * (kExactTargets + 1))));
+      hipLaunchKernelGGL(attn_runs_chain_kernel, dim3(1), dim3(kSchedThreads), 3 * lds1, stream,
+                         (const int32_t*)bucket, P.n_targets, n_groups, (const int32_t*)sched,
+                         const_cast<int32_t*>(P.gs));
+    } else {
+      hipLaunchKernelGGL((attn_groups_kernel<false, Geo<L>::M>), dim3(1), dim3(kSchedThreads), 0, stream,
+                         P.row_ptr, P.n_targets, n_groups, const_cast<int32_t*>(P.gs),
+                         const_cast<int32_t*>(P.order), sched);
+    }
   } else {
     int64_t want = (n_edges + kEdgesPerGroup - 1) / kEdgesPerGroup;
     want = ((want + n_cu - 1) / n_cu) * n_cu;
@@ -1658,7 +1904,7 @@ so2_status launch_L(const MfmaParams& P, int32_t* bucket, int64_t n_edges, hipSt
 // Workspace of the MFMA path: softmax statistics, the x pairs, w_rad in
 // fp32 and w_so2 in fragment order.
 struct ScratchLayout {
-  size_t stats, xp, wrad, wf, gs, bucket, order, total;
+  size_t stats, xp, wrad, wf, gs, bucket, order, sched, total;
 };
 
 size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -1673,7 +1919,8 @@ ScratchLayout scratch_layout(int n_atoms, int n_targets, int L, int H, int K) {
   // at most n_targets groups
   s.bucket = s.gs + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
   s.order = s.bucket + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
-  s.total = s.order + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
+  s.sched = s.order + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
+  s.total = s.sched + 256;
   return s;
 }
 
@@ -1771,20 +2018,22 @@ so2_status launch_attention_mfma_prep(const AttnArgs& a, hipStream_t stream) {
 so2_status launch_attention_mfma(const AttnArgs& a, hipStream_t stream) {
   if (a.n_targets == 0) return SO2_OK;
   const MfmaParams P = make_params(a);
-  int32_t* bucket = (int32_t*)((char*)a.scratch + scratch_layout(a.n_atoms, a.n_targets, a.L, a.H, a.K).bucket);
+  const ScratchLayout s = scratch_layout(a.n_atoms, a.n_targets, a.L, a.H, a.K);
+  int32_t* bucket = (int32_t*)((char*)a.scratch + s.bucket);
+  int32_t* sched = (int32_t*)((char*)a.scratch + s.sched);
   switch (a.L) {
     case 1:
-      return launch_L<1>(P, bucket, a.n_edges, stream);
+      return launch_L<1>(P, bucket, sched, a.n_edges, stream);
     case 2:
-      return launch_L<2>(P, bucket, a.n_edges, stream);
+      return launch_L<2>(P, bucket, sched, a.n_edges, stream);
     case 3:
-      return launch_L<3>(P, bucket, a.n_edges, stream);
+      return launch_L<3>(P, bucket, sched, a.n_edges, stream);
     case 4:
-      return launch_L<4>(P, bucket, a.n_edges, stream);
+      return launch_L<4>(P, bucket, sched, a.n_edges, stream);
     case 5:
-      return launch_L<5>(P, bucket, a.n_edges, stream);
+      return launch_L<5>(P, bucket, sched, a.n_edges, stream);
     case 6:
-      return launch_L<6>(P, bucket, a.n_edges, stream);
+      return launch_L<6>(P, bucket, sched, a.n_edges, stream);
   }
   return SO2_ERR_UNSUPPORTED;
 }

@@ -297,3 +297,57 @@ def test_mfma_ragged_degrees_and_split_targets(L):
     torch.cuda.synchronize()
     assert y_part.shape[0] == nt
     assert max_rel_error(y_part.cpu().numpy(), y_ref[:nt]) <= TOL["bf16"]
+
+
+def test_mfma_every_target_row_written_small_molecules():
+    """At the full small-molecule size the runs of targets come from the
+    exact chunk-count refinement (a chunk cap one below the estimate's
+    largest run): every target row must still be written (rows start as NaN)."""
+    say("mfma run schedule covers every target, small_molecules")
+    import torch
+
+    import so_equivariant_graph_amd as sea
+
+    w = make_workload("small_molecules")
+    d = device_inputs(w)
+    rp_d, col_d = sea.build_neighbors(d["pos"], w.cutoff, box=w.box, mol_id=d["mol"])
+    y = torch.full((w.n_atoms, (w.l_max + 1) ** 2, w.x.shape[2]), float("nan"), device="cuda")
+    gpu_attention(w, d, rp_d, col_d, out=y)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    deg = torch.diff(rp_d).cpu().numpy()
+    assert np.all(y[torch.from_numpy(deg == 0).cuda()].cpu().numpy() == 0.0)
+
+
+def test_mfma_hub_target_keeps_estimated_runs():
+    """One target with 250 neighbours (4 chunks of 64 edges) among
+    300 targets of degree 19: the chunk cap one below the largest estimated
+    run cannot hold the hub, so the estimated runs stay; every target is
+    checked against the oracle."""
+    say("mfma hub target")
+    from synth import to_bf16_exact
+
+    rng = np.random.default_rng(11)
+    g = np.arange(-4, 5) * 1.2
+    lat = np.array(np.meshgrid(g, g, g, indexing="ij")).reshape(3, -1).T
+    shell = lat[(np.linalg.norm(lat, axis=1) > 0) & (np.linalg.norm(lat, axis=1) < 4.8)]
+    cube = np.array(np.meshgrid(*(np.arange(3) * 1.2,) * 3, indexing="ij")).reshape(3, -1).T[:20]
+    groups = [cube + [100.0 + 30.0 * k, 0.0, 0.0] for k in range(15)]
+    pos = np.vstack([[[0.0, 0.0, 0.0]], *groups, shell])
+    nt = 1 + 15 * 20
+    n = pos.shape[0]
+    w = make_workload("tiny_fp32", l_max=2, channels=128, heads=8, n_rbf=16, dtype="bf16")
+    w.pos = pos.astype(np.float32)
+    w.x = to_bf16_exact(rng.standard_normal((n, 9, 128)).astype(np.float32))
+    rp, col = neighbors_bruteforce(w.pos, w.cutoff)
+    deg = np.diff(rp)
+    assert deg[0] > 3 * 64 and np.all(deg[1:nt] == 19)
+    import torch
+
+    d = device_inputs(w)
+    y = gpu_attention(w, d, *csr_to_device(rp, col), n_targets=nt)
+    torch.cuda.synchronize()
+    y_ref = oracle_attention(w, rp, col, targets=np.arange(nt))
+    err = max_rel_error(y.cpu().numpy(), y_ref)
+    say("max rel err", err, "hub degree", deg[0])
+    assert err <= TOL["bf16"]
