@@ -1853,13 +1853,32 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
 // the estimated work; for L = 5, 6 about kEdgesPerGroup edges each, rounded
 // up to a whole number of waves of workgroups over the compute units.
 template <int L>
-so2_status launch_L(const MfmaParams& P, int32_t* bucket, int32_t* sched, int64_t n_edges, hipStream_t stream) {
-  int dev = 0, n_cu = 256;
-  SO2_CHECK(hipGetDevice(&dev));
-  SO2_CHECK(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
-  int n_groups;
+int group_count(int n_targets, int64_t n_edges, int n_cu) {
   if constexpr (L <= 4) {
-    n_groups = std::max(1, std::min(n_cu, P.n_targets));
+    return std::max(1, std::min(n_cu, n_targets));
+  } else {
+    int64_t want = (n_edges + kEdgesPerGroup - 1) / kEdgesPerGroup;
+    want = ((want + n_cu - 1) / n_cu) * n_cu;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(want, n_targets));
+  }
+}
+
+so2_status device_cu_count(int* n_cu) {
+  int dev = 0;
+  *n_cu = 256;
+  SO2_CHECK(hipGetDevice(&dev));
+  SO2_CHECK(hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+  return SO2_OK;
+}
+
+// The run starts (and the order of the groups) for the fused kernel.
+template <int L>
+so2_status schedule_L(const MfmaParams& P, int32_t* bucket, int32_t* sched, int64_t n_edges, hipStream_t stream) {
+  int n_cu = 256;
+  const so2_status st = device_cu_count(&n_cu);
+  if (st != SO2_OK) return st;
+  const int n_groups = group_count<L>(P.n_targets, n_edges, n_cu);
+  if constexpr (L <= 4) {
     const bool exact = P.n_targets <= kExactTargets && n_groups <= kExactRuns;
     if (exact) {
       constexpr int CM = Geo<L>::M;
@@ -1885,13 +1904,19 @@ so2_status launch_L(const MfmaParams& P, int32_t* bucket, int32_t* sched, int64_
                          const_cast<int32_t*>(P.order), sched);
     }
   } else {
-    int64_t want = (n_edges + kEdgesPerGroup - 1) / kEdgesPerGroup;
-    want = ((want + n_cu - 1) / n_cu) * n_cu;
-    n_groups = (int)std::max<int64_t>(1, std::min<int64_t>(want, P.n_targets));
     hipLaunchKernelGGL(attn_order_kernel, dim3(8), dim3(256), 0, stream, P.row_ptr, P.n_targets, n_groups,
                        Geo<L>::M, const_cast<int32_t*>(P.gs), bucket, const_cast<int32_t*>(P.order));
   }
   SO2_CHECK_LAUNCH();
+  return SO2_OK;
+}
+
+template <int L>
+so2_status launch_L(const MfmaParams& P, int64_t n_edges, hipStream_t stream) {
+  int n_cu = 256;
+  const so2_status st = device_cu_count(&n_cu);
+  if (st != SO2_OK) return st;
+  const int n_groups = group_count<L>(P.n_targets, n_edges, n_cu);
   const size_t smem = Lds<L>::kTotal;
   static_assert(Lds<L>::kTotal <= 160 * 1024, "LDS budget");
   SO2_CHECK(hipFuncSetAttribute((const void*)attn_mfma_kernel<L>,
@@ -2012,28 +2037,42 @@ so2_status launch_attention_mfma_prep(const AttnArgs& a, hipStream_t stream) {
   if (st != SO2_OK || a.n_targets == 0) return st;
   hipLaunchKernelGGL(attn_stats_kernel, dim3((a.n_targets + 3) / 4), dim3(256), 0, stream, P, kC);
   SO2_CHECK_LAUNCH();
-  return SO2_OK;
-}
-
-so2_status launch_attention_mfma(const AttnArgs& a, hipStream_t stream) {
-  if (a.n_targets == 0) return SO2_OK;
-  const MfmaParams P = make_params(a);
   const ScratchLayout s = scratch_layout(a.n_atoms, a.n_targets, a.L, a.H, a.K);
   int32_t* bucket = (int32_t*)((char*)a.scratch + s.bucket);
   int32_t* sched = (int32_t*)((char*)a.scratch + s.sched);
   switch (a.L) {
     case 1:
-      return launch_L<1>(P, bucket, sched, a.n_edges, stream);
+      return schedule_L<1>(P, bucket, sched, a.n_edges, stream);
     case 2:
-      return launch_L<2>(P, bucket, sched, a.n_edges, stream);
+      return schedule_L<2>(P, bucket, sched, a.n_edges, stream);
     case 3:
-      return launch_L<3>(P, bucket, sched, a.n_edges, stream);
+      return schedule_L<3>(P, bucket, sched, a.n_edges, stream);
     case 4:
-      return launch_L<4>(P, bucket, sched, a.n_edges, stream);
+      return schedule_L<4>(P, bucket, sched, a.n_edges, stream);
     case 5:
-      return launch_L<5>(P, bucket, sched, a.n_edges, stream);
+      return schedule_L<5>(P, bucket, sched, a.n_edges, stream);
     case 6:
-      return launch_L<6>(P, bucket, sched, a.n_edges, stream);
+      return schedule_L<6>(P, bucket, sched, a.n_edges, stream);
+  }
+  return SO2_ERR_UNSUPPORTED;
+}
+
+so2_status launch_attention_mfma(const AttnArgs& a, hipStream_t stream) {
+  if (a.n_targets == 0) return SO2_OK;
+  const MfmaParams P = make_params(a);
+  switch (a.L) {
+    case 1:
+      return launch_L<1>(P, a.n_edges, stream);
+    case 2:
+      return launch_L<2>(P, a.n_edges, stream);
+    case 3:
+      return launch_L<3>(P, a.n_edges, stream);
+    case 4:
+      return launch_L<4>(P, a.n_edges, stream);
+    case 5:
+      return launch_L<5>(P, a.n_edges, stream);
+    case 6:
+      return launch_L<6>(P, a.n_edges, stream);
   }
   return SO2_ERR_UNSUPPORTED;
 }

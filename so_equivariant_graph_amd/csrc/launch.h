@@ -59,13 +59,14 @@ bool valu_supported(int L, int C, int H);
 size_t valu_scratch_bytes(int L, int C);
 so2_status launch_attention_valu(const AttnArgs& a, hipStream_t stream);
 
-// bf16 MFMA kernel (attention_mfma.hip): C = 128, 1 <= L <= 4, H <= 16, K <= 32.
+// bf16 MFMA kernel (attention_mfma.hip): C = 128, 1 <= L <= 6, H <= 16, K <= 32.
 // x, w_rad and w_so2 must be 16-byte aligned.
 bool mfma_supported(int L, int C, int H, int K, int n_atoms);
 bool mfma_aligned(const AttnArgs& a);
 size_t mfma_scratch_bytes(int n_atoms, int n_targets, int L, int H, int K);
-// prologue (x repacked as component pairs, w_rad in fp32) and softmax
-// statistics pass, then the fused kernel
+// prologue (x repacked as component pairs, w_rad in fp32, w_so2 in fragment
+// order), softmax statistics and the run schedule; then the fused kernel
+// alone
 so2_status launch_attention_mfma_prep(const AttnArgs& a, hipStream_t stream);
 so2_status launch_attention_mfma(const AttnArgs& a, hipStream_t stream);
 
