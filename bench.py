@@ -43,12 +43,12 @@ PEAK_HBM_GBS = 8000.0
 # for the kernel sources it was taken on: their digest is stored with it and a
 # mismatch reports null.
 MEASURED_TRAFFIC = {
-    # FETCH_SIZE 1084808 KiB x 2.00 (a 1 GiB copy reads as 524303 KiB), WRITE_SIZE
-    # 185096 KiB x 1.00 (the copy writes read exactly 1048576 KiB); mean of 7 launches.
+    # FETCH_SIZE 2588172 KiB x 2.00 (a 1 GiB copy reads as 524303 KiB), WRITE_SIZE
+    # 147800 KiB x 1.00 (the copy writes read exactly 1048576 KiB); mean of 7 launches.
     "small_molecules": {
-        "sources_sha256": "d0c2e1bdb791d1f1bdea1414f15b547a52b82f1f637dcc7693ca1d1fdd07e4ac",
-        "fetch_bytes": 2221621223,
-        "write_bytes": 189538304,
+        "sources_sha256": "de05f65cb7ec75498353659ce5d030731b4afab6088ed7dc6f4f12313a7e7134",
+        "fetch_bytes": 5300428630,
+        "write_bytes": 151347200,
     },
 }
 KERNEL_SOURCES = ("attention_mfma.hip", "wigner.h", "common.h", "launch.h")
@@ -241,8 +241,8 @@ NORM_TRAFFIC = {
     # box's features: FETCH_SIZE 312574 KiB x 2.00, WRITE_SIZE 625000 KiB x 1.00 (the same
     # copy calibration as the fused kernel's figure); mean of 4 launches.
     "water_100k": {
-        "sources_sha256": "728e522721c4a27c254123d554044f5e4e350bd439a9f0ebdf0e151b5f144e76",
-        "fetch_bytes": 640134813,
+        "sources_sha256": "84afa7d832182174e207bd85e5d226f8156f28722616c3d8f53e7018826b4a74",
+        "fetch_bytes": 640132977,
         "write_bytes": 640000000,
     },
 }
