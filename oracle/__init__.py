@@ -40,6 +40,8 @@ attention  the per-edge loop: rotate, gate, SO(2) map, rotate back,
            two-pass softmax with the envelope, aggregate
 norm       the merged RMS layer norm of the node features ("EquiformerV3"
            technical summary, section 2.B.1)
+swiglu     the SwiGLU-S2 activation of the node features ("EquiformerV3"
+           technical summary, section 2.C)
 """
 
 from .sh import real_sh, n_comp
@@ -54,6 +56,7 @@ from .attention import (
     max_rel_error,
 )
 from .norm import merged_rms_norm_ref
+from .swiglu import s2_grid, swiglu_s2_ref
 
 __all__ = [
     "real_sh",
@@ -64,6 +67,8 @@ __all__ = [
     "neighbors_bruteforce",
     "so2_attention_ref",
     "merged_rms_norm_ref",
+    "swiglu_s2_ref",
+    "s2_grid",
     "envelope",
     "radial_gaussians",
     "unpack_so2",
