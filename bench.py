@@ -10,6 +10,7 @@ timed region starts.  Prints ONE JSON line.
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload small_molecules]
     python bench.py --memory-sweep [--steps 5 --warmup 2]   (peak bytes against N)
     python bench.py --norm                                  (merged RMS layer norm, HBM roofline)
+    python bench.py --swiglu                                (SwiGLU-S2 activation, vector-unit roofline)
 
 value          messages (edges) per second of the whole step
 roofline       the fused attention kernel against the dense bf16 MFMA peak:
@@ -299,6 +300,78 @@ def norm_bench(steps, warmup):
     }), flush=True)
 
 
+PEAK_FP32_VALU_TFLOPS = 157.3  # published vector fp32 (with packed FMA; single-issue FMA is half)
+
+
+def swiglu_flops(L, C):
+    """Algorithmic flops per node of the SwiGLU-S2 activation: the three
+    per-degree maps and the gate map on the matrix cores, 2 C^2 (3 (L+1)^2 + 1),
+    and the separable grid step on the vector units per channel, 2 x
+    [3 n_t ((L+1)^2 + n_f (2L+1))] multiply-adds plus the n_t n_f products."""
+    nc, nt, nf, nm = (L + 1) ** 2, (3 * L + 2) // 2, 3 * L + 1, 2 * L + 1
+    mfma = 2 * C * C * (3 * nc + 1)
+    grid = C * (2 * 3 * nt * (nc + nf * nm) + nt * nf)
+    return mfma, grid
+
+
+def swiglu_bench(steps, warmup):
+    """The SwiGLU-S2 activation of the 100k-atom water box's node features
+    (bf16, L = 4, C = 128) with seeded weights: nodes/s, and the vector-unit
+    roofline of the grid kernel (the largest of the step's kernels), timed by
+    the library's HIP events on its stream; the whole call by torch events."""
+    import numpy as np
+    import torch
+
+    import so_equivariant_graph_amd as sea
+    from synth import make_workload
+
+    w = make_workload("water_100k")
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(w.x).to(device=dev, dtype=torch.bfloat16)
+    del w.x
+    n, nc, C = x.shape
+    L = int(round(nc ** 0.5)) - 1
+    rng = np.random.default_rng(5)
+    s = 1.0 / np.sqrt(C)
+    mk = lambda *shape: torch.from_numpy((rng.standard_normal(shape) * s).astype(np.float32)).to(dev, torch.bfloat16)
+    A, B, O, G = mk(L + 1, C, C), mk(L + 1, C, C), mk(L + 1, C, C), mk(C, C)
+    y = torch.empty((n, nc, C), dtype=torch.float32, device=dev)
+    ws = torch.empty(sea.load_library().so2_swiglu_s2_workspace_bytes(n, L, C, sea.SO2_BF16), dtype=torch.uint8,
+                     device=dev)
+    for _ in range(warmup):
+        sea.swiglu_s2(x, A, B, G, O, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    timer = sea.KernelTimer(steps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        timer.arm()
+        a.record()
+        sea.swiglu_s2(x, A, B, G, O, out=y, workspace=ws)
+        b.record()
+    torch.cuda.synchronize()
+    timer.disarm()
+    grid_ms = timer.elapsed_ms()
+    timer.close()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    mean = sum(ms) / len(ms)
+    gmean = sum(grid_ms) / len(grid_ms)
+    f_mfma, f_grid = swiglu_flops(L, C)
+    achieved = n * f_grid / (gmean * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "SwiGLU-S2 activation nodes/s", "value": n / (mean * 1e-3), "unit": "nodes/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": mean, "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "water_100k node features", "n_atoms": n, "l_max": L, "channels": C},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP32_VALU_TFLOPS, "traffic": None},
+        "detail": {"grid_kernel_ms_mean": gmean, "grid_flop_per_node": f_grid, "mfma_flop_per_node": f_mfma,
+                   "maps_ms": mean - gmean,
+                   "maps_tflops": n * f_mfma / ((mean - gmean) * 1e-3) / 1e12 if mean > gmean else None,
+                   "ms_min": ms[0], "ms_median": ms[len(ms) // 2],
+                   "outputs_finite": bool(torch.isfinite(y).all())},
+    }), flush=True)
+
+
 SWEEP_ATOMS = (12_500, 25_000, 50_000, 100_000, 200_000)
 
 
@@ -349,6 +422,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, metavar="MIB", default=0,
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--swiglu", action="store_true",
+                    help="the SwiGLU-S2 activation of the 100k-atom water box's features instead of the attention step")
     ap.add_argument("--norm", action="store_true",
                     help="only time the merged RMS layer norm on the 100k-atom water box's features")
     ap.add_argument("--memory-sweep", action="store_true",
@@ -369,6 +444,9 @@ def main():
         return
     if args.norm:
         norm_bench(args.steps, args.warmup)
+        return
+    if args.swiglu:
+        swiglu_bench(args.steps, args.warmup)
         return
 
     from synth import make_workload

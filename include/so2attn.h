@@ -166,7 +166,8 @@ so2_status so2_attention_fwd(const so2_attn_desc* desc, const float* pos,
 
 /* Benchmark hook: when both are non-NULL, every later so2_attention_fwd
  * call from this thread records `start` on its stream just before the fused
- * attention kernel and `stop` just after it (hipEvent_t handles created and
+ * attention kernel and `stop` just after it, and every later so2_swiglu_s2
+ * call does the same around its grid kernel (hipEvent_t handles created and
  * owned by the caller), so the kernel alone can be timed on the stream it
  * runs on.  so2_set_kernel_timing_events(NULL, NULL) switches it off. */
 void so2_set_kernel_timing_events(void* start, void* stop);
@@ -188,6 +189,38 @@ void so2_set_kernel_timing_events(void* start, void* stop);
  * ---------------------------------------------------------------------- */
 so2_status so2_merged_rms_norm(const void* x, const float* gamma, void* y, int32_t n_atoms, int32_t l_max,
                                int32_t channels, float eps, int32_t dtype, so2_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * so2_swiglu_s2 - SwiGLU-S2 activation of node features ("EquiformerV3:
+ * Scaling Efficient, Expressive, and General SE(3)-Equivariant Graph
+ * Attention Transformers", technical summary, section 2.C: features on a
+ * sphere grid, the nonlinear gate on the scalar channels only, a bilinear
+ * product of grid features).  Per node, with Y the real harmonics:
+ *   u = x A_l, v = x B_l            (per degree l, row vectors of C channels)
+ *   g = x[(0,0)] G
+ *   h[(l,m)] = sum_p w_p Y_lm(r_p) u(r_p) v(r_p)    for l <= l_max
+ *   y[(l,m)] = (SiLU(g) * h[(l,m)]) O_l
+ * on the product grid of ceil((3 l_max + 1) / 2) Gauss-Legendre nodes in
+ * cos(theta) times 3 l_max + 1 equally spaced phi (exact for the degree
+ * <= 3 l_max integrands, so the map is equivariant).
+ *   x              [n_atoms][(l_max+1)^2][channels] dtype (device)
+ *   w_a, w_b, w_o  [l_max+1][channels][channels] dtype, [l][in][out] (device)
+ *   w_g            [channels][channels] dtype, [in][out] (device)
+ *   y              [n_atoms][(l_max+1)^2][channels] fp32, written (device)
+ *   workspace      >= so2_swiglu_s2_workspace_bytes(...) bytes, 16-byte
+ *                  aligned (device): u, v, g and the gated product
+ * bf16 with channels = 128 and 16-byte aligned x and weights runs the maps on
+ * the matrix cores (bf16 operands, fp32 sums) and keeps u, v and the gated
+ * product in bf16; every other shape runs in fp32 arithmetic.
+ * Errors: INVALID_ARGUMENT (nulls with n_atoms > 0, n_atoms < 0, l_max < 0,
+ * channels < 1, bad dtype), UNSUPPORTED (l_max > 6), WORKSPACE, DEVICE.
+ * Asynchronous on `stream`; no device allocation.  The workspace query
+ * returns 0 for arguments the call rejects.
+ * ---------------------------------------------------------------------- */
+size_t so2_swiglu_s2_workspace_bytes(int32_t n_atoms, int32_t l_max, int32_t channels, int32_t dtype);
+so2_status so2_swiglu_s2(const void* x, const void* w_a, const void* w_b, const void* w_g, const void* w_o, float* y,
+                         int32_t n_atoms, int32_t l_max, int32_t channels, int32_t dtype, void* workspace,
+                         size_t workspace_bytes, so2_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Host-side diagnostics (no device work): evaluate, on the CPU, the same

@@ -49,6 +49,8 @@ EXPORTED_SYMBOLS = (
     "so2_edge_frame_host",
     "so2_set_kernel_timing_events",
     "so2_merged_rms_norm",
+    "so2_swiglu_s2_workspace_bytes",
+    "so2_swiglu_s2",
 )
 
 
@@ -118,6 +120,10 @@ def load_library(path: str = LIB_PATH):
     lib.so2_set_kernel_timing_events.restype = None
     lib.so2_merged_rms_norm.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, vp]
     lib.so2_merged_rms_norm.restype = ctypes.c_int
+    lib.so2_swiglu_s2_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.so2_swiglu_s2_workspace_bytes.restype = ctypes.c_size_t
+    lib.so2_swiglu_s2.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.so2_swiglu_s2.restype = ctypes.c_int
     _lib_handle = lib
     return lib
 
@@ -306,8 +312,9 @@ def hip_runtime():
 
 
 class KernelTimer:
-    """Times the fused attention kernel alone with HIP events recorded by the
-    library on the kernel's own stream (one event pair per call)."""
+    """Times the fused attention kernel (so2_attention_fwd) or the grid kernel
+    (so2_swiglu_s2) alone with HIP events recorded by the library on the
+    kernel's own stream (one event pair per call)."""
 
     def __init__(self, n_calls: int):
         self.hip = hip_runtime()
@@ -375,3 +382,34 @@ __all__ = [
     "SO2Error",
     "AttnDesc",
 ]
+
+
+def swiglu_s2(x, w_a, w_b, w_g, w_o, *, out=None, workspace=None):
+    """SwiGLU-S2 activation of node features.  x: [N,(L+1)^2,C] float32 or
+    bfloat16; w_a, w_b, w_o: [L+1,C,C] ([l][in][out]) and w_g: [C,C] in x's
+    dtype.  Returns y [N,(L+1)^2,C] float32."""
+    import torch
+
+    lib = load_library()
+    dt = _dtype_code(x)
+    n, nc, C = x.shape
+    L = int(round(nc ** 0.5)) - 1
+    if (L + 1) ** 2 != nc:
+        raise ValueError("x must be [N,(L+1)^2,C]")
+    for name, t, shape in (("w_a", w_a, (L + 1, C, C)), ("w_b", w_b, (L + 1, C, C)), ("w_o", w_o, (L + 1, C, C)),
+                           ("w_g", w_g, (C, C))):
+        if t.dtype != x.dtype:
+            raise ValueError(f"{name} must have x's dtype {x.dtype}")
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {list(shape)}")
+    x, w_a, w_b, w_g, w_o = (t.contiguous() for t in (x, w_a, w_b, w_g, w_o))
+    ws_bytes = lib.so2_swiglu_s2_workspace_bytes(n, L, C, dt)
+    if ws_bytes == 0 and n > 0:
+        _check(SO2_ERR_UNSUPPORTED if L > 6 else SO2_ERR_INVALID_ARGUMENT, "so2_swiglu_s2")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    y = out if out is not None else torch.empty((n, nc, C), dtype=torch.float32, device=x.device)
+    st = lib.so2_swiglu_s2(_ptr(x), _ptr(w_a), _ptr(w_b), _ptr(w_g), _ptr(w_o), _ptr(y), n, L, C, dt,
+                           _ptr(workspace), ws_bytes, _stream_handle(x.device))
+    _check(st, "so2_swiglu_s2")
+    return y

@@ -25,6 +25,7 @@ SOURCES = [
     "neighbors.hip",
     "attention_prep.hip",
     "norm.hip",
+    "swiglu.hip",
     "attention_valu.hip",
     "attention_mfma.hip",
 ]

@@ -7,6 +7,7 @@
 #include "common.h"
 #include "launch.h"
 #include "norm.h"
+#include "swiglu.h"
 #include "wigner.h"
 
 namespace so2 {
@@ -211,6 +212,23 @@ so2_status so2_merged_rms_norm(const void* x, const float* gamma, void* y, int32
   if (n_atoms > 0 && (!x || !gamma || !y)) return SO2_ERR_INVALID_ARGUMENT;
   if (l_max > kMaxL) return SO2_ERR_UNSUPPORTED;
   return launch_merged_rms_norm(x, gamma, y, n_atoms, l_max, channels, eps, dtype, (hipStream_t)stream);
+}
+
+size_t so2_swiglu_s2_workspace_bytes(int32_t n_atoms, int32_t l_max, int32_t channels, int32_t dtype) {
+  if (n_atoms < 0 || l_max < 0 || l_max > kMaxL || channels < 1) return 0;
+  if (dtype != SO2_FP32 && dtype != SO2_BF16) return 0;
+  return swiglu_s2_workspace_bytes(n_atoms, l_max, channels, dtype);
+}
+
+so2_status so2_swiglu_s2(const void* x, const void* w_a, const void* w_b, const void* w_g, const void* w_o, float* y,
+                         int32_t n_atoms, int32_t l_max, int32_t channels, int32_t dtype, void* workspace,
+                         size_t workspace_bytes, so2_stream_t stream) {
+  if (n_atoms < 0 || l_max < 0 || channels < 1) return SO2_ERR_INVALID_ARGUMENT;
+  if (dtype != SO2_FP32 && dtype != SO2_BF16) return SO2_ERR_INVALID_ARGUMENT;
+  if (n_atoms > 0 && (!x || !w_a || !w_b || !w_g || !w_o || !y)) return SO2_ERR_INVALID_ARGUMENT;
+  if (l_max > kMaxL) return SO2_ERR_UNSUPPORTED;
+  return launch_swiglu_s2(x, w_a, w_b, w_g, w_o, y, n_atoms, l_max, channels, dtype, workspace, workspace_bytes,
+                          (hipStream_t)stream, g_timing_start, g_timing_stop);
 }
 
 so2_status so2_edge_frame_host(int32_t l_max, const float* rhat, float* R_out, float* D_out) {

@@ -1,0 +1,18 @@
+// SwiGLU-S2 activation of node features (swiglu.hip), host launcher.
+#pragma once
+
+#include "common.h"
+
+namespace so2 {
+
+// Workspace bytes of launch_swiglu_s2 for n_atoms nodes of degree <= L and C
+// channels: u, v, the gate and the gated grid product s, sized for fp32.
+size_t swiglu_s2_workspace_bytes(int n_atoms, int L, int C, int dtype);
+
+// ev_start / ev_stop (or null): recorded on `stream` just before and after the
+// grid kernel.
+so2_status launch_swiglu_s2(const void* x, const void* w_a, const void* w_b, const void* w_g, const void* w_o,
+                            float* y, int n_atoms, int L, int C, int dtype, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop);
+
+}  // namespace so2

@@ -175,6 +175,30 @@ def test_norm_errors_before_launch():
     assert call(None, None, None, 0, 2, 8, 1e-5, sea.SO2_FP32) == sea.SO2_OK  # nothing to do
 
 
+def test_swiglu_errors_before_launch():
+    lib = sea.load_library()
+
+    def call(n, L, C, dt, ptrs=(FAKE,) * 6, ws=None, ws_bytes=0):
+        return lib.so2_swiglu_s2(*ptrs, n, L, C, dt, ws, ws_bytes, None)
+
+    for i in range(6):  # x, w_a, w_b, w_g, w_o, y
+        ptrs = [FAKE] * 6
+        ptrs[i] = None
+        assert call(4, 2, 8, sea.SO2_BF16, ptrs) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(-1, 2, 8, sea.SO2_BF16) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(4, -1, 8, sea.SO2_BF16) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(4, 2, 0, sea.SO2_BF16) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(4, 2, 8, 7) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(4, 7, 8, sea.SO2_BF16) == sea.SO2_ERR_UNSUPPORTED
+    assert call(4, 2, 8, sea.SO2_FP32) == sea.SO2_ERR_WORKSPACE  # no workspace
+    need = lib.so2_swiglu_s2_workspace_bytes(4, 2, 8, sea.SO2_FP32)
+    assert need >= 3 * 4 * 9 * 8 * 4 + 4 * 8 * 4  # u, v, s and the gate in fp32
+    assert call(4, 2, 8, sea.SO2_FP32, ws=FAKE, ws_bytes=need - 1) == sea.SO2_ERR_WORKSPACE
+    assert lib.so2_swiglu_s2_workspace_bytes(4, 7, 8, sea.SO2_FP32) == 0
+    assert lib.so2_swiglu_s2_workspace_bytes(-1, 2, 8, sea.SO2_FP32) == 0
+    assert call(0, 2, 8, sea.SO2_FP32, (None,) * 6) == sea.SO2_OK  # nothing to do
+
+
 def test_neighbor_errors_before_launch():
     lib = sea.load_library()
     n_e = ctypes.c_int64(0)
