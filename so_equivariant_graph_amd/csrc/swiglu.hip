@@ -268,12 +268,21 @@ __global__ void __launch_bounds__(256) lin_mfma_kernel(const uint16_t* __restric
   if (row0 >= n_atoms) return;
   const int ar = row0 + (lane & 15);
   const int g = lane >> 4;
-  for (int k = l * l; k < (l + 1) * (l + 1); ++k) {
-    sw_u32x4 af[4];
+  // A fragments of component k + 1 load while component k runs
+  auto load_a = [&](int k, sw_u32x4 (&af)[4]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       af[ks] = ar < n_atoms ? *(const sw_u32x4*)(in + (int64_t)ar * in_stride + (int64_t)k * C + 32 * ks + 8 * g)
                             : sw_u32x4{0u, 0u, 0u, 0u};
+  };
+  const int k_end = (l + 1) * (l + 1);
+  sw_u32x4 an[4];
+  load_a(l * l, an);
+  for (int k = l * l; k < k_end; ++k) {
+    sw_u32x4 af[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) af[ks] = an[ks];
+    if (k + 1 < k_end) load_a(k + 1, an);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       TO* out = m == 0 ? out0 : out1;
