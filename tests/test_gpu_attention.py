@@ -351,3 +351,44 @@ def test_mfma_hub_target_keeps_estimated_runs():
     err = max_rel_error(y.cpu().numpy(), y_ref)
     say("max rel err", err, "hub degree", deg[0])
     assert err <= TOL["bf16"]
+
+
+def test_mfma_exact_schedule_with_isolated_targets():
+    """96 small molecules with 1923 isolated atoms mixed into the index order
+    (5769 targets, a third without neighbours): the run schedule takes the
+    exact refinement (a cap of 8 chunks, 229 runs), with runs that start and
+    end next to targets without neighbours.  Every row is compared with the
+    fp32 VALU kernel on the same bf16-exact inputs (one workgroup per target,
+    no run schedule), and 40 seeded targets with the oracle."""
+    import copy
+
+    import torch
+
+    from synth import to_bf16_exact
+
+    say("mfma exact schedule, isolated targets mixed in")
+    w = make_workload("small_molecules", geometry=dict(n_molecules=96))
+    rng = np.random.default_rng(3)
+    n0 = w.n_atoms
+    n_iso = n0 // 2
+    iso = np.stack([np.full(n_iso, -500.0), np.arange(n_iso) * 20.0, np.zeros(n_iso)], 1)
+    perm = rng.permutation(n0 + n_iso)
+    w.pos = np.vstack([w.pos, iso])[perm].astype(np.float32)
+    w.mol_id = np.concatenate([w.mol_id, 100000 + np.arange(n_iso)])[perm].astype(np.int32)
+    x_iso = to_bf16_exact(rng.standard_normal((n_iso,) + w.x.shape[1:]).astype(np.float32))
+    w.x = np.concatenate([w.x, x_iso])[perm]
+    rp, col = neighbors_bruteforce(w.pos, w.cutoff, w.box, w.mol_id)
+    deg = np.diff(rp)
+    assert (deg == 0).sum() > w.n_atoms // 4
+    y = gpu_attention(w, device_inputs(w), *csr_to_device(rp, col))
+    w32 = copy.copy(w)
+    w32.dtype = "fp32"
+    y32 = gpu_attention(w32, device_inputs(w32), *csr_to_device(rp, col))
+    torch.cuda.synchronize()
+    y, y32 = y.cpu().numpy(), y32.cpu().numpy()
+    assert np.all(np.isfinite(y)) and np.all(y[deg == 0] == 0.0)
+    err_all = max_rel_error(y, y32)
+    t = np.sort(rng.choice(w.n_atoms, size=40, replace=False))
+    err_ref = max_rel_error(y[t], oracle_attention(w, rp, col, targets=t))
+    say("vs fp32 kernel", err_all, "vs oracle", err_ref)
+    assert err_all <= TOL["bf16"] and err_ref <= TOL["bf16"]
