@@ -304,13 +304,19 @@ PEAK_FP32_VALU_TFLOPS = 157.3  # published vector fp32 (with packed FMA; single-
 
 
 def swiglu_flops(L, C):
-    """Algorithmic flops per node of the SwiGLU-S2 activation: the three
-    per-degree maps and the gate map on the matrix cores, 2 C^2 (3 (L+1)^2 + 1),
-    and the separable grid step on the vector units per channel, 2 x
-    [3 n_t ((L+1)^2 + n_f (2L+1))] multiply-adds plus the n_t n_f products."""
-    nc, nt, nf, nm = (L + 1) ** 2, (3 * L + 2) // 2, 3 * L + 1, 2 * L + 1
+    """Algorithmic flops per node of the SwiGLU-S2 activation.  Matrix cores:
+    the three per-degree maps and the gate map, 2 C^2 (3 (L+1)^2 + 1).  Vector
+    units, per channel, the grid step as the kernel runs it (rings paired at
+    +-cos(theta), meridians paired at +-phi): the even/odd harmonic sums of u
+    and v, 2 (L+1)^2 multiply-adds per ring pair or middle ring (R of them);
+    per ring, 6L multiply-adds for each of the Q = (n_f - 1) // 2 meridian
+    pairs and 3 (L + 1) for phi = pi when n_f is even; (L+1)^2 per ring pair
+    for the projection back; plus one product per grid point."""
+    nc, nt, nf = (L + 1) ** 2, (3 * L + 2) // 2, 3 * L + 1
     mfma = 2 * C * C * (3 * nc + 1)
-    grid = C * (2 * 3 * nt * (nc + nf * nm) + nt * nf)
+    r, q, e = (nt + 1) // 2, (nf - 1) // 2, 1 if nf % 2 == 0 else 0
+    fma = r * 2 * nc + nt * (q * 6 * L + e * 3 * (L + 1)) + r * nc
+    grid = C * (2 * fma + nt * nf)
     return mfma, grid
 
 

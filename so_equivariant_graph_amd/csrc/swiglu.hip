@@ -24,9 +24,9 @@
 //   grid factorises, Y_lm(theta_i, phi_j) = Pn_lm(theta_i) T_m(phi_j) with
 //   T_0 = 1, T_m = cos(m phi), T_-m = sin(m phi), so u on ring i is
 //   sum_m F_m T_m(phi_j) with F_m = sum_l Pn_lm(theta_i) u_lm, and the
-//   projection runs the same two sums in reverse: about
-//   n_t (L+1)^2 + n_t n_f (2L+1) multiply-adds per field and channel instead
-//   of n_t n_f (L+1)^2.  The tables Pn and T are built in LDS by each block.
+//   projection runs the same two sums in reverse.  Both factors have a mirror
+//   symmetry (rings at +-cos(theta), meridians at +-phi) that halves each
+//   sum again.  The tables Pn and T are built in LDS by each block.
 #include "swiglu.h"
 
 #include <math.h>
@@ -137,7 +137,7 @@ __device__ inline void store_value<uint16_t>(uint16_t* p, float v) {
 // node (grid-stride over nodes), lanes over channels.
 constexpr int kS2Threads = 256;
 template <int L, typename TU, typename TS>
-__global__ void __launch_bounds__(kS2Threads) s2_kernel(const TU* __restrict__ u, const TU* __restrict__ v,
+__global__ void __launch_bounds__(kS2Threads) __attribute__((amdgpu_waves_per_eu(L <= 3 ? 3 : 1))) s2_kernel(const TU* __restrict__ u, const TU* __restrict__ v,
                                                         const float* __restrict__ gate, TS* __restrict__ s,
                                                         int n_atoms, int C, GridArgs grid) {
   constexpr int NC = (L + 1) * (L + 1), NM = 2 * L + 1, NT = (3 * L + 2) / 2, NF = 3 * L + 1;
@@ -155,6 +155,56 @@ __global__ void __launch_bounds__(kS2Threads) s2_kernel(const TU* __restrict__ u
   if (threadIdx.x < NT) wq[threadIdx.x] = (float)grid.wt[threadIdx.x];
   __syncthreads();
 
+  // One ring: the product of u and v at its NF meridians, projected onto the
+  // T_m, added to g.  phi_0 = 0 (T_m = 1 for m >= 0, 0 for m < 0) stands
+  // alone; phi_j and phi_{NF-j} share the cosines and have opposite sines,
+  // so each pair costs one cosine sum and one sine sum per field; for even
+  // NF, phi = pi stands alone too.
+  auto ring_phi = [&](const float (&fu)[NM], const float (&fv)[NM], float (&g)[NM]) {
+    {
+      float a = 0.0f, b = 0.0f;
+#pragma unroll
+      for (int q = L; q < NM; ++q) {
+        a += fu[q];
+        b += fv[q];
+      }
+      const float hp = a * b;
+#pragma unroll
+      for (int q = L; q < NM; ++q) g[q] += hp;
+    }
+    for (int j = 1; 2 * j < NF; ++j) {
+      float cu = fu[L], cv = fv[L], su = 0.0f, sv = 0.0f;
+#pragma unroll
+      for (int m = 1; m <= L; ++m) {
+        const float c = tf[j][L + m], sn = tf[j][L - m];
+        cu += c * fu[L + m];
+        cv += c * fv[L + m];
+        su += sn * fu[L - m];
+        sv += sn * fv[L - m];
+      }
+      const float h1 = (cu + su) * (cv + sv), h2 = (cu - su) * (cv - sv);
+      const float hs = h1 + h2, hd = h1 - h2;
+      g[L] += hs;
+#pragma unroll
+      for (int m = 1; m <= L; ++m) {
+        g[L + m] += tf[j][L + m] * hs;
+        g[L - m] += tf[j][L - m] * hd;
+      }
+    }
+    if constexpr (NF % 2 == 0) {
+      constexpr int j = NF / 2;
+      float a = 0.0f, b = 0.0f;
+#pragma unroll
+      for (int q = L; q < NM; ++q) {
+        a += tf[j][q] * fu[q];
+        b += tf[j][q] * fv[q];
+      }
+      const float hp = a * b;
+#pragma unroll
+      for (int q = L; q < NM; ++q) g[q] += tf[j][q] * hp;
+    }
+  };
+
   const int lane = threadIdx.x & 63;
   const int n_waves = gridDim.x * (kS2Threads / 64);
   for (int node = blockIdx.x * (kS2Threads / 64) + (threadIdx.x >> 6); node < n_atoms; node += n_waves) {
@@ -169,34 +219,52 @@ __global__ void __launch_bounds__(kS2Threads) s2_kernel(const TU* __restrict__ u
       }
       const float z = gate[(int64_t)node * C + c];
       const float sg = z / (1.0f + expf(-z));
-      for (int i = 0; i < NT; ++i) {
-        float fu[NM], fv[NM], gm[NM];
+      // Ring pairs: rings i and NT - 1 - i have opposite cos(theta), and
+      // Pn_lm(-x) = (-1)^(l+m) Pn_lm(x), so one sum over the even l + m terms
+      // and one over the odd ones serve both (F = E + O on ring i, E - O on
+      // its mirror); the projection back takes ga + gb or ga - gb by parity.
+      for (int i = 0; i < (NT + 1) / 2; ++i) {
+        const bool pair = 2 * i + 1 != NT;
+        float eu[NM], ou[NM], ev[NM], ov[NM];
 #pragma unroll
-        for (int q = 0; q < NM; ++q) fu[q] = fv[q] = gm[q] = 0.0f;
+        for (int q = 0; q < NM; ++q) eu[q] = ou[q] = ev[q] = ov[q] = 0.0f;
 #pragma unroll
         for (int l = 0; l <= L; ++l)
 #pragma unroll
           for (int m = -l; m <= l; ++m) {
             const float p = pn[i][l * l + l + m];
-            fu[m + L] += p * uu[l * l + l + m];
-            fv[m + L] += p * vv[l * l + l + m];
+            if (((l + m) & 1) == 0) {
+              eu[m + L] += p * uu[l * l + l + m];
+              ev[m + L] += p * vv[l * l + l + m];
+            } else {
+              ou[m + L] += p * uu[l * l + l + m];
+              ov[m + L] += p * vv[l * l + l + m];
+            }
           }
-        for (int j = 0; j < NF; ++j) {
-          float a = 0.0f, b = 0.0f;
+        float fu[NM], fv[NM], ga[NM], gb[NM];
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+          fu[q] = eu[q] + ou[q];
+          fv[q] = ev[q] + ov[q];
+          ga[q] = gb[q] = 0.0f;
+        }
+        ring_phi(fu, fv, ga);
+        if (pair) {
 #pragma unroll
           for (int q = 0; q < NM; ++q) {
-            a += tf[j][q] * fu[q];
-            b += tf[j][q] * fv[q];
+            fu[q] = eu[q] - ou[q];
+            fv[q] = ev[q] - ov[q];
           }
-          const float hp = a * b;
-#pragma unroll
-          for (int q = 0; q < NM; ++q) gm[q] += tf[j][q] * hp;
+          ring_phi(fu, fv, gb);
         }
         const float w = wq[i];
 #pragma unroll
         for (int l = 0; l <= L; ++l)
 #pragma unroll
-          for (int m = -l; m <= l; ++m) hh[l * l + l + m] += pn[i][l * l + l + m] * (w * gm[m + L]);
+          for (int m = -l; m <= l; ++m) {
+            const float gq = ((l + m) & 1) == 0 ? ga[m + L] + gb[m + L] : ga[m + L] - gb[m + L];
+            hh[l * l + l + m] += pn[i][l * l + l + m] * (w * gq);
+          }
       }
 #pragma unroll
       for (int k = 0; k < NC; ++k) store_value(s + base + (int64_t)k * C, sg * hh[k]);
