@@ -1852,9 +1852,16 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
 // Workgroups: for L <= 4 one per compute unit, each with an equal share of
 // the estimated work; for L = 5, 6 about kEdgesPerGroup edges each, rounded
 // up to a whole number of waves of workgroups over the compute units.
+// One run per compute unit from the run estimate (and its exact refinement)
+// for L <= 4, and for L = 5, 6 when the refinement applies.
+template <int L>
+bool one_run_per_cu(int n_targets) {
+  return L <= 4 || n_targets <= kExactTargets;
+}
+
 template <int L>
 int group_count(int n_targets, int64_t n_edges, int n_cu) {
-  if constexpr (L <= 4) {
+  if (one_run_per_cu<L>(n_targets)) {
     return std::max(1, std::min(n_cu, n_targets));
   } else {
     int64_t want = (n_edges + kEdgesPerGroup - 1) / kEdgesPerGroup;
@@ -1878,7 +1885,7 @@ so2_status schedule_L(const MfmaParams& P, int32_t* bucket, int32_t* sched, int6
   const so2_status st = device_cu_count(&n_cu);
   if (st != SO2_OK) return st;
   const int n_groups = group_count<L>(P.n_targets, n_edges, n_cu);
-  if constexpr (L <= 4) {
+  if (one_run_per_cu<L>(P.n_targets)) {
     const bool exact = P.n_targets <= kExactTargets && n_groups <= kExactRuns;
     if (exact) {
       constexpr int CM = Geo<L>::M;
