@@ -347,6 +347,11 @@ __global__ void __launch_bounds__(256) lin_mfma_kernel(const uint16_t* __restric
   sw_u32x4 an[4];
   load_a(l * l, an);
   for (int k = l * l; k < k_end; ++k) {
+    // NM = 2: a compiler-only barrier, so that the B fragments are re-read
+    // from LDS for every component instead of being held in 256 registers
+    // (one wave per SIMD): 720 -> 640 us at 100k nodes.  The single-matrix
+    // maps were slower that way and keep their fragments in registers.
+    if constexpr (NM == 2) asm volatile("" ::: "memory");
     sw_u32x4 af[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) af[ks] = an[ks];
