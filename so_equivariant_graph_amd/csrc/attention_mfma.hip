@@ -2016,8 +2016,75 @@ size_t mfma_scratch_bytes(int n_atoms, int n_targets, int L, int H, int K) {
   return scratch_layout(n_atoms, n_targets, L, H, K).total;
 }
 
+namespace {
+
+so2_status launch_schedule(const AttnArgs& a, const MfmaParams& P, hipStream_t stream) {
+  const ScratchLayout s = scratch_layout(a.n_atoms, a.n_targets, a.L, a.H, a.K);
+  int32_t* bucket = (int32_t*)((char*)a.scratch + s.bucket);
+  int32_t* sched = (int32_t*)((char*)a.scratch + s.sched);
+  switch (a.L) {
+    case 1:
+      return schedule_L<1>(P, bucket, sched, a.n_edges, stream);
+    case 2:
+      return schedule_L<2>(P, bucket, sched, a.n_edges, stream);
+    case 3:
+      return schedule_L<3>(P, bucket, sched, a.n_edges, stream);
+    case 4:
+      return schedule_L<4>(P, bucket, sched, a.n_edges, stream);
+    case 5:
+      return schedule_L<5>(P, bucket, sched, a.n_edges, stream);
+    case 6:
+      return schedule_L<6>(P, bucket, sched, a.n_edges, stream);
+  }
+  return SO2_ERR_UNSUPPORTED;
+}
+
+// A second stream (default priority, non-blocking) and a fork and a join
+// event, per host thread and device, created on first use and kept until the
+// process ends.  Per thread, so that calls from different host threads never
+// share an event.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+
+so2_status side_stream(SideStream** out) {
+  static thread_local SideStream per_device[kMaxDevices];
+  int dev = 0;
+  SO2_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return SO2_ERR_UNSUPPORTED;
+  SideStream& ss = per_device[dev];
+  if (!ss.join) {
+    if (!ss.stream) SO2_CHECK(hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking));
+    if (!ss.fork) SO2_CHECK(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming));
+    SO2_CHECK(hipEventCreateWithFlags(&ss.join, hipEventDisableTiming));
+  }
+  *out = &ss;
+  return SO2_OK;
+}
+
+}  // namespace
+
+// The run schedule reads only row_ptr, so it runs on a side stream beside the
+// repack and the statistics (which fill the device, while the schedule
+// kernels use one or a few workgroups); the caller's stream waits for it
+// before the fused kernel.  Without a side stream it runs in line.
 so2_status launch_attention_mfma_prep(const AttnArgs& a, hipStream_t stream) {
   const MfmaParams P = make_params(a);
+  SideStream* side = nullptr;
+  if (a.n_targets > 0) {
+    if (side_stream(&side) == SO2_OK) {
+      SO2_CHECK(hipEventRecord(side->fork, stream));
+      SO2_CHECK(hipStreamWaitEvent(side->stream, side->fork, 0));
+      const so2_status st = launch_schedule(a, P, side->stream);
+      if (st != SO2_OK) return st;
+      SO2_CHECK(hipEventRecord(side->join, side->stream));
+    } else {
+      const so2_status st = launch_schedule(a, P, stream);
+      if (st != SO2_OK) return st;
+    }
+  }
   so2_status st = SO2_OK;
   switch (a.L) {
     case 1:
@@ -2039,29 +2106,14 @@ so2_status launch_attention_mfma_prep(const AttnArgs& a, hipStream_t stream) {
       st = launch_pack_L<6>(a, P, stream);
       break;
     default:
-      return SO2_ERR_UNSUPPORTED;
+      st = SO2_ERR_UNSUPPORTED;
   }
-  if (st != SO2_OK || a.n_targets == 0) return st;
-  hipLaunchKernelGGL(attn_stats_kernel, dim3((a.n_targets + 3) / 4), dim3(256), 0, stream, P, kC);
-  SO2_CHECK_LAUNCH();
-  const ScratchLayout s = scratch_layout(a.n_atoms, a.n_targets, a.L, a.H, a.K);
-  int32_t* bucket = (int32_t*)((char*)a.scratch + s.bucket);
-  int32_t* sched = (int32_t*)((char*)a.scratch + s.sched);
-  switch (a.L) {
-    case 1:
-      return schedule_L<1>(P, bucket, sched, a.n_edges, stream);
-    case 2:
-      return schedule_L<2>(P, bucket, sched, a.n_edges, stream);
-    case 3:
-      return schedule_L<3>(P, bucket, sched, a.n_edges, stream);
-    case 4:
-      return schedule_L<4>(P, bucket, sched, a.n_edges, stream);
-    case 5:
-      return schedule_L<5>(P, bucket, sched, a.n_edges, stream);
-    case 6:
-      return schedule_L<6>(P, bucket, sched, a.n_edges, stream);
+  if (st == SO2_OK && a.n_targets > 0) {
+    hipLaunchKernelGGL(attn_stats_kernel, dim3((a.n_targets + 3) / 4), dim3(256), 0, stream, P, kC);
+    SO2_CHECK_LAUNCH();
   }
-  return SO2_ERR_UNSUPPORTED;
+  if (side) SO2_CHECK(hipStreamWaitEvent(stream, side->join, 0));
+  return st;
 }
 
 so2_status launch_attention_mfma(const AttnArgs& a, hipStream_t stream) {
