@@ -1266,22 +1266,24 @@ __device__ inline int64_t target_work(int d) {
   return w > 64 / kSlots ? w : 64 / kSlots;
 }
 
-// Schedule of the fused kernel for L <= 4, one workgroup of 1024 threads.
-// With W the total work and wsum[t] the work of targets 0..t-1, run g of
-// n_groups starts at the first target t with wsum[t] >= goal_g =
-// floor(g W / n_groups), and run n_groups at n_targets.  Runs are written
-// from the prefix sums without a search: the number of runs whose goal is
-// at most X is runs_upto(X) = min(n_groups, ceil((X + 1) n_groups / W)), so
-// target i, with wsum[i] = a and wsum[i + 1] = b, starts runs
-// [runs_upto(a), runs_upto(b)) at i + 1, and run 0 starts at 0.  The first
-// pass sums W; the second scans the targets kSchedItems per thread and
-// walks the run index along them.  With
-// one run per compute unit the runs hold equal estimated work and all run
-// at once, so the makespan is that of the largest; at the small-molecule
-// workload this beat equal-edge groups dispatched longest first
-// (attn_order_kernel), which the 32-edge chunks of L = 5, 6 keep, since
-// there whole targets (about three chunks each) are too coarse a unit for
-// one run per compute unit.
+// Run estimate of the fused kernel's schedule (one run of consecutive
+// targets per compute unit), one workgroup of 1024 threads; used for L <= 4,
+// and for L = 5, 6 on graphs of at most kExactTargets targets.  With W the
+// total work and wsum[t] the work of targets 0..t-1, run g of n_groups
+// starts at the first target t with wsum[t] >= goal_g = floor(g W /
+// n_groups), and run n_groups at n_targets.  Runs are written from the
+// prefix sums without a search: the number of runs whose goal is at most X
+// is runs_upto(X) = min(n_groups, ceil((X + 1) n_groups / W)), so target i,
+// with wsum[i] = a and wsum[i + 1] = b, starts runs [runs_upto(a),
+// runs_upto(b)) at i + 1, and run 0 starts at 0.  In the exact mode the row
+// offsets are staged in LDS and all targets form one span (kExactItems per
+// thread); otherwise a first pass sums W and a second scans the targets in
+// spans of kSchedItems per thread, walking the run index along them.  With
+// one run per compute unit all runs run at once and the makespan is that of
+// the largest; at the small-molecule workload this beat equal-edge groups
+// dispatched longest first (attn_order_kernel), which larger L = 5, 6 graphs
+// keep: there whole targets (about three 32-edge chunks each) are a coarse
+// unit for one run per compute unit without the exact refinement.
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedItems = 8;
 
@@ -1328,8 +1330,9 @@ __device__ inline int run_chunks(const RP& rp, int s, int x) {
 // Exact refinement for graphs of at most kExactTargets targets and
 // kExactRuns runs.  The fused kernel's time per run is close to
 // proportional to the run's chunk count, so the makespan is set by the
-// largest count M of the estimated runs; the whole-number rounding of
-// about 18 chunks per run costs up to a chunk there.  Since greedy maximal
+// largest count M of the estimated runs; with few chunks per run (about 18
+// at the small-molecule workload) one chunk more on one run is a few
+// percent.  Since greedy maximal
 // chunks are the fewest for any range of targets, the chunk count of a
 // range grows with the range, and the greedy partition under a cap of K
 // chunks per run (each run as long as the cap allows) uses the fewest
