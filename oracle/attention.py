@@ -87,14 +87,20 @@ def unpack_so2(w_so2, l_max: int, channels: int):
 def envelope(s, p: int = 5):
     """u(s) = 1 - (p+1)(p+2)/2 s^p + p(p+2) s^(p+1) - p(p+1)/2 s^(p+2) for
     0 <= s < 1, else 0 (the polynomial cutoff envelope; with p = 5 it reads
-    1 - 21 s^5 + 35 s^6 - 15 s^7)."""
+    1 - 21 s^5 + 35 s^6 - 15 s^7).
+
+    u(1) = u'(1) = u''(1) = 0, so (1 - s)^3 divides u, and since u = 1 +
+    O(s^p) the cofactor is the degree p-1 truncation of 1 / (1 - s)^3:
+        u(s) = (1 - s)^3 sum_{k=0}^{p-1} (k+1)(k+2)/2 s^k.
+    That form is evaluated here: every term is positive on [0, 1), so it
+    keeps its relative precision up to the cutoff, where the expanded sum
+    cancels to rounding noise."""
     s = np.asarray(s, dtype=np.float64)
-    u = (
-        1.0
-        - (p + 1) * (p + 2) / 2.0 * s**p
-        + p * (p + 2) * s ** (p + 1)
-        - p * (p + 1) / 2.0 * s ** (p + 2)
-    )
+    t = 1.0 - s
+    q = np.zeros_like(s)
+    for k in range(p - 1, -1, -1):  # Horner, highest power first
+        q = q * s + (k + 1) * (k + 2) / 2.0
+    u = t * t * t * q
     return np.where(s < 1.0, u, 0.0)
 
 
@@ -125,25 +131,27 @@ def _rotate(blocks, feat, l_max, transpose=False):
 
 
 def _so2_map(xt, w0, w1, w2, l_max):
-    """O10, the per-m map in the edge frame.
+    """O10, the per-m map in the edge frame, for a stack of edges
+    xt [E, (L+1)^2, C] (the same map for every edge; each edge's rows form
+    a row vector, so W v is written v W^T):
 
     m = 0:  yt[(l,0)]  = sum_{l'} W0[(l,.),(l',.)] xt[(l',0)]
     m >= 1: yt_+ = W1 xt_+ - W2 xt_-,  yt_- = W2 xt_+ + W1 xt_-
     with xt_{+/-} the rows (l, +/-m), l = m..L, stacked as (l - m) C + c."""
-    C = xt.shape[1]
+    n_e, _, C = xt.shape
     yt = np.zeros_like(xt)
     rows0 = [l * l + l for l in range(l_max + 1)]
-    y0 = w0 @ xt[rows0].reshape(-1)
-    yt[rows0] = y0.reshape(l_max + 1, C)
+    y0 = xt[:, rows0].reshape(n_e, -1) @ w0.T
+    yt[:, rows0] = y0.reshape(n_e, l_max + 1, C)
     for m in range(1, l_max + 1):
         rp = [l * l + l + m for l in range(m, l_max + 1)]
         rm = [l * l + l - m for l in range(m, l_max + 1)]
-        xp = xt[rp].reshape(-1)
-        xm = xt[rm].reshape(-1)
-        yp = w1[m] @ xp - w2[m] @ xm
-        ym = w2[m] @ xp + w1[m] @ xm
-        yt[rp] = yp.reshape(-1, C)
-        yt[rm] = ym.reshape(-1, C)
+        xp = xt[:, rp].reshape(n_e, -1)
+        xm = xt[:, rm].reshape(n_e, -1)
+        yp = xp @ w1[m].T - xm @ w2[m].T
+        ym = xp @ w2[m].T + xm @ w1[m].T
+        yt[:, rp] = yp.reshape(n_e, -1, C)
+        yt[:, rm] = ym.reshape(n_e, -1, C)
     return yt
 
 
@@ -212,7 +220,8 @@ def so2_attention_ref(
             continue
         z = np.empty((deg, heads))
         u = np.empty(deg)
-        v = np.empty((deg, nc, C))
+        g = np.empty((deg, C))
+        frames = np.empty((deg, 3, 3))
         for e, j in enumerate(js):
             r = _mic(pos[j] - pos[i], box)
             rho = sqrt(float(r @ r))
@@ -220,19 +229,23 @@ def so2_attention_ref(
             for h in range(heads):  # O3
                 z[e, h] = q[i, h * d : (h + 1) * d] @ k[j, h * d : (h + 1) * d] / sqrt(d)
             if flags & FLAG_NO_RADIAL:  # O6
-                g = np.ones(C)
+                g[e] = 1.0
             else:
                 phi = radial_gaussians(rho, cutoff, n_rbf)
                 if flags & FLAG_RBF_ENVELOPE:
                     phi = phi * u[e]
-                g = phi @ w_rad
-            R = frame_rotation(r / rho)  # O7
+                g[e] = phi @ w_rad
+            frames[e] = frame_rotation(r / rho)  # O7
             if gauge is not None:
-                R = rot_z(gauge(i, e)) @ R
-            blocks = wigner_d_blocks(l_max, R)  # O8
-            xt = _rotate(blocks, x[j], l_max) * g[None, :]  # O9
-            yt = _so2_map(xt, w0, w1, w2, l_max)  # O10
-            v[e] = _rotate(blocks, yt, l_max, transpose=True)  # O11
+                frames[e] = rot_z(gauge(i, e)) @ frames[e]
+        blocks = wigner_d_blocks(l_max, frames)  # O8, one [deg, 2l+1, 2l+1] stack per degree
+        xt = np.empty((deg, nc, C))
+        for e, j in enumerate(js):
+            xt[e] = _rotate([b[e] for b in blocks], x[j], l_max) * g[e][None, :]  # O9
+        yt = _so2_map(xt, w0, w1, w2, l_max)  # O10, every edge of i through the same map
+        v = np.empty((deg, nc, C))
+        for e in range(deg):
+            v[e] = _rotate([b[e] for b in blocks], yt[e], l_max, transpose=True)  # O11
         zmax = z.max(axis=0)  # O5, two-pass softmax
         ew = u[:, None] * np.exp(z - zmax[None, :])
         den = ew.sum(axis=0)
@@ -248,10 +261,11 @@ def max_rel_error(y_test, y_ref) -> float:
     """max_i max_{(l,m),c} |y_test - y_ref| / max(||y_ref,i||_inf,
     1e-6 ||y_ref||_inf): the error normalised per atom, since an
     elementwise relative error is undefined near zero."""
-    yt = np.asarray(y_test, dtype=np.float64).reshape(len(y_ref), -1)
-    yr = np.asarray(y_ref, dtype=np.float64).reshape(len(y_ref), -1)
+    yr = np.asarray(y_ref, dtype=np.float64)
     if yr.size == 0:
         return 0.0
+    yt = np.asarray(y_test, dtype=np.float64).reshape(len(yr), -1)
+    yr = yr.reshape(len(yr), -1)
     glob = np.abs(yr).max()
     per_atom = np.maximum(np.abs(yr).max(axis=1), 1e-6 * glob)
     per_atom = np.where(per_atom > 0.0, per_atom, 1.0)

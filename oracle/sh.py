@@ -16,6 +16,7 @@ on the aligned axis) is the statement Y_l(z_hat) = sqrt((2l+1)/(4 pi)) e_{m=0},
 which holds in this basis and is pinned by the tests.
 """
 
+from functools import lru_cache
 from math import factorial, pi, sqrt
 
 import numpy as np
@@ -27,16 +28,22 @@ def n_comp(l_max: int) -> int:
     return (l_max + 1) * (l_max + 1)
 
 
+@lru_cache(maxsize=None)
+def _legendre_deriv(l: int, m: int):
+    """d^m/dx^m P_l as a Legendre series (a constant of (l, m); kept once)."""
+    series = npleg.Legendre.basis(l)
+    if m:
+        series = series.deriv(m)
+    return series
+
+
 def _assoc_legendre(l: int, m: int, ct: np.ndarray, st: np.ndarray) -> np.ndarray:
     """P_l^m(cos t) without the Condon-Shortley phase, straight from its
     definition: (1-x^2)^(m/2) times the m-th derivative of the Legendre
     polynomial P_l at x = cos t (numpy's Legendre series supplies P_l and
     d/dx).  (1-x^2)^(1/2) = sin t is passed in, taken from the Cartesian
     components, so that it keeps full precision next to the poles."""
-    series = npleg.Legendre.basis(l)
-    if m:
-        series = series.deriv(m)
-    return st**m * series(ct)
+    return st**m * _legendre_deriv(l, m)(ct)
 
 
 def real_sh(l_max: int, v) -> np.ndarray:

@@ -15,12 +15,15 @@ times n_phi >= 2l+1 equally spaced azimuths (exact for trigonometric degree
 < n_phi) integrates it exactly; the result is D^l up to rounding.
 """
 
+from functools import lru_cache
+
 import numpy as np
 from numpy.polynomial import legendre as npleg
 
 from .sh import real_sh
 
 
+@lru_cache(maxsize=None)
 def _product_quadrature(l_max: int):
     """Nodes s_q [Q, 3] and weights w_q [Q] exact for degree <= 2 l_max."""
     n_t = l_max + 1
@@ -37,19 +40,37 @@ def _product_quadrature(l_max: int):
         axis=1,
     )
     weights = np.repeat(wt, n_p) * (2.0 * np.pi / n_p)
+    nodes.flags.writeable = False
+    weights.flags.writeable = False
     return nodes, weights
 
 
+@lru_cache(maxsize=None)
+def _sh_at_nodes(l_max: int):
+    """Y(s_q) at the quadrature nodes: the same for every rotation, so it is
+    evaluated once per l_max (read-only)."""
+    y = real_sh(l_max, _product_quadrature(l_max)[0])
+    y.flags.writeable = False
+    return y
+
+
 def wigner_d_blocks(l_max: int, R) -> list:
-    """[D^0(R), ..., D^L(R)], each (2l+1) x (2l+1), rows/cols m = -l..l."""
+    """[D^0(R), ..., D^L(R)], each (2l+1) x (2l+1), rows/cols m = -l..l.
+
+    R may also be a stack [E, 3, 3] of rotations; then every block is
+    [E, 2l+1, 2l+1], entry e belonging to R[e]."""
     R = np.asarray(R, dtype=np.float64)
+    single = R.ndim == 2
+    rs = R.reshape(-1, 3, 3)
     nodes, w = _product_quadrature(l_max)
-    y_s = real_sh(l_max, nodes)  # Y(s_q)
-    y_rs = real_sh(l_max, nodes @ R.T)  # Y(R s_q)
+    y_s = _sh_at_nodes(l_max)  # Y(s_q)
+    pts = np.einsum("eij,qj->eqi", rs, nodes)  # R s_q for every rotation
+    y_rs = real_sh(l_max, pts.reshape(-1, 3)).reshape(rs.shape[0], nodes.shape[0], -1)  # Y(R s_q)
     blocks = []
     for l in range(l_max + 1):
         sl = slice(l * l, (l + 1) * (l + 1))
-        blocks.append((y_rs[:, sl] * w[:, None]).T @ y_s[:, sl])
+        b = np.einsum("eqa,q,qb->eab", y_rs[:, :, sl], w, y_s[:, sl])
+        blocks.append(b[0] if single else b)
     return blocks
 
 

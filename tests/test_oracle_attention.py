@@ -17,7 +17,8 @@ mathematics fix:
 
 import json
 import os
-from math import exp
+from fractions import Fraction
+from math import comb, exp
 
 import numpy as np
 import pytest
@@ -137,6 +138,46 @@ def test_envelope_p5_published_form():
     np.testing.assert_allclose(envelope(s, 5), 1 - 21 * s**5 + 35 * s**6 - 15 * s**7, atol=1e-14)
 
 
+def _envelope_exact(s, p):
+    """The expanded polynomial 1 - (p+1)(p+2)/2 s^p + p(p+2) s^(p+1) -
+    p(p+1)/2 s^(p+2) in exact rational arithmetic at the double s."""
+    q = Fraction(s)
+    return 1 - Fraction((p + 1) * (p + 2), 2) * q**p + p * (p + 2) * q ** (p + 1) - Fraction(p * (p + 1), 2) * q ** (p + 2)
+
+
+@pytest.mark.parametrize("p", [3, 5, 6, 8])
+def test_envelope_relative_precision_up_to_the_cutoff(p):
+    # the oracle against the exact value of the same polynomial, relatively,
+    # from the middle of the range to within 1e-12 of the cutoff: the
+    # expanded form in fp64 is pure rounding noise there (a wrong cofactor or
+    # a dropped term fails at every point)
+    pts = [0.05, 0.3, 0.5, 0.9, 0.99, 1 - 1e-3, 1 - 1e-5, 1 - 1e-8, 1 - 1e-10, 1 - 1e-12]
+    for s in pts:
+        exact = _envelope_exact(s, p)
+        assert exact > 0
+        got = Fraction(float(envelope(s, p)))
+        assert abs(got - exact) <= Fraction(1, 10**13) * exact, (p, s, float(got), float(exact))
+
+
+@pytest.mark.parametrize("p", [3, 5, 6, 8])
+def test_envelope_positive_inside_and_triple_root_at_the_cutoff(p):
+    s = np.concatenate([np.linspace(0.0, 1.0, 2001)[:-1], 1.0 - np.logspace(-15, -1, 57)])
+    u = envelope(s, p)
+    assert np.all(u > 0.0)
+    # u ~ C(p+2, 3) (1 - s)^3 as s -> 1: the cofactor at s = 1 is the sum of
+    # the first p triangular numbers (the tetrahedral number)
+    t = 1e-9
+    assert abs(float(envelope(1.0 - t, p)) / t**3 - comb(p + 2, 3)) < 1e-6 * comb(p + 2, 3)
+
+
+def test_envelope_p5_factored_cofactor():
+    # at p = 5: u = (1 - s)^3 (1 + 3 s + 6 s^2 + 10 s^3 + 15 s^4), checked
+    # against the printed polynomial on exact rationals
+    for s in (0.1, 0.37, 0.8, 0.999):
+        q = Fraction(s)
+        assert (1 - q) ** 3 * (1 + 3 * q + 6 * q**2 + 10 * q**3 + 15 * q**4) == _envelope_exact(s, 5)
+
+
 def test_radial_basis_centres_and_width():
     rc, K = 5.0, 8
     sigma = rc / (K - 1)
@@ -153,6 +194,54 @@ def test_weight_count_closed_form(L):
     w0, w1, w2 = unpack_so2(np.arange(so2_weight_count(L, C)), L, C)
     assert w0.shape == ((L + 1) * C,) * 2
     assert all(w1[m].shape == ((L + 1 - m) * C,) * 2 for m in w1)
+
+
+# ---------------------------------------------------------------- the parity metric
+
+
+def test_max_rel_error_normalises_per_atom():
+    # atom 0 has entries of order 1, atom 1 of order 1e-3; an error of 1e-4
+    # on atom 1 is 10 % of that atom's scale (a global normaliser would
+    # report 1e-4)
+    ref = np.array([[[1.0, -0.5], [0.25, 0.0]], [[1e-3, 0.0], [-5e-4, 2e-4]]])
+    test = ref.copy()
+    test[1, 0, 0] += 1e-4
+    assert oracle.max_rel_error(test, ref) == pytest.approx(0.1, rel=1e-12)
+    # the same absolute error on atom 0 is 1e-4 of its scale
+    test = ref.copy()
+    test[0, 1, 1] -= 1e-4
+    assert oracle.max_rel_error(test, ref) == pytest.approx(1e-4, rel=1e-9)
+
+
+def test_max_rel_error_groups_by_the_first_axis():
+    # [T, (L+1)^2, C] with T = 3: errors are grouped per target row, whatever
+    # the trailing shape; a reshape over the wrong axis would mix the scales
+    ref = np.zeros((3, 4, 2))
+    ref[0] = 100.0
+    ref[1] = 1.0
+    ref[2, 3, 1] = -2.0
+    test = ref.copy()
+    test[1, 2, 0] += 0.5
+    assert oracle.max_rel_error(test, ref) == pytest.approx(0.5, rel=1e-12)
+    test[2, 0, 0] += 0.5
+    assert oracle.max_rel_error(test, ref) == pytest.approx(0.5, rel=1e-12)
+    test[2, 3, 1] -= 1.5
+    assert oracle.max_rel_error(test, ref) == pytest.approx(0.75, rel=1e-12)
+    assert oracle.max_rel_error(test.reshape(3, 8), ref.reshape(3, 8)) == pytest.approx(0.75, rel=1e-12)
+
+
+def test_max_rel_error_floor_and_degenerate_cases():
+    # an all-zero reference atom is measured against 1e-6 of the global scale
+    ref = np.array([[[2.0, 0.0]], [[0.0, 0.0]]])
+    test = ref.copy()
+    test[1, 0, 1] = 3e-9
+    assert oracle.max_rel_error(test, ref) == pytest.approx(3e-9 / 2e-6, rel=1e-12)
+    # an all-zero reference: absolute error
+    assert oracle.max_rel_error(np.full((2, 1, 1), 0.25), np.zeros((2, 1, 1))) == pytest.approx(0.25)
+    assert oracle.max_rel_error(np.zeros((0, 4, 2)), np.zeros((0, 4, 2))) == 0.0
+    assert oracle.max_rel_error(ref, ref) == 0.0
+    # symmetric in the sign of the error
+    assert oracle.max_rel_error(ref + 0.1, ref) == oracle.max_rel_error(ref - 0.1, ref)
 
 
 # ---------------------------------------------------------------- symmetry

@@ -106,3 +106,26 @@ def test_grid_one_node_short_is_not_equivariant():
     y = swiglu_s2_ref(x, A, B, G, O, grid=short)
     y_rot = swiglu_s2_ref(_rotate(x, blocks), A, B, G, O, grid=short)
     assert np.abs(y_rot - _rotate(y, blocks)).max() > 1e-6 * np.abs(y).max()
+
+
+def test_silu_values_and_identities():
+    # SiLU(z) = z / (1 + e^-z) (the gate of SwiGLU); literal values of the
+    # logistic function at 1 and 2 (1 / (1 + e^-1) = 0.731058578630004879...,
+    # 2 / (1 + e^-2) = 1.761594155955764888...)
+    assert silu(0.0) == 0.0
+    assert silu(1.0) == pytest.approx(0.7310585786300049, rel=1e-15)
+    assert silu(-1.0) == pytest.approx(-0.2689414213699951, rel=1e-14)
+    assert silu(2.0) == pytest.approx(1.7615941559557649, rel=1e-15)
+    z = np.linspace(-30.0, 30.0, 241)
+    # silu(z) - silu(-z) = z (sigma(z) + sigma(-z) = 1); a plain sigmoid or
+    # z sigma(-z) fails this
+    np.testing.assert_allclose(silu(z) - silu(-z), z, atol=1e-12)
+    # silu -> z for large z, -> 0 from below for very negative z, minimum
+    # near z = -1.2785 with value -0.2784645...
+    assert silu(40.0) == pytest.approx(40.0, rel=1e-15)
+    assert -1e-15 < silu(-40.0) < 0.0
+    zz = np.linspace(-2.0, -0.5, 300001)
+    assert float(silu(zz).min()) == pytest.approx(-0.27846454276107, abs=1e-10)
+    # slope 1/2 at the origin
+    h = 1e-6
+    assert (silu(h) - silu(-h)) / (2 * h) == pytest.approx(0.5, rel=1e-9)
