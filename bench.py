@@ -3,11 +3,13 @@
 equivariant graph attention forward on one MI355X.
 
 One step = the whole hot path over one batch of seeded synthetic input:
-build_neighbors (cell list, a1) + so2_attention_fwd (q/k projection and the
-fused kernel, a2-a11).  Inputs are resident in device memory before the
-timed region starts.  Prints ONE JSON line.
+build_neighbors (cell list, a1) + so2_attention_fwd (q/k projection, the
+fused kernel's prologue and the fused kernel, a2-a11).  Inputs are resident
+in device memory before the timed region starts.  Prints ONE JSON line.
+The default workload is the 100,000-atom periodic water box (L = 4,
+C = 128, bf16), the largest system of the set that runs on one GPU.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload small_molecules]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload water_100k]
     python bench.py --memory-sweep [--steps 5 --warmup 2]   (peak bytes against N)
     python bench.py --norm                                  (merged RMS layer norm, HBM roofline)
     python bench.py --swiglu                                (SwiGLU-S2 activation, vector-unit roofline)
@@ -15,8 +17,8 @@ timed region starts.  Prints ONE JSON line.
 value          messages (edges) per second of the whole step
 roofline       the fused attention kernel against the dense bf16 MFMA peak:
                algorithmic flops per launch (E * 2C^2[(L+1)^2 + 2/3 L(L+1)(2L+1)])
-               over its mean duration, timed with HIP events the library records
-               around that kernel on its own stream
+               over its mean duration, timed with torch (HIP) events on the
+               stream the library launches on, around the fused stage alone
 cpu_baseline   the fp64 oracle (never tuned) on a bounded sample of the same
                workload, on this host's cores, in worker processes forked before
                the GPU is touched
@@ -96,45 +98,71 @@ def copy_probe(mib):
 # ------------------------------------------------------------------ CPU leg
 
 
-def _oracle_worker(args):
-    name, targets, seconds = args
-    from threadpoolctl import threadpool_limits
-
+def _subsystem(w, targets, rows):
+    """The atoms the oracle needs for `targets` (the targets first, then their
+    neighbours) and the CSR of the targets' rows in that numbering: the
+    oracle's result for a target depends on nothing else."""
     import numpy as np
+
+    extra = np.setdiff1d(np.concatenate([r for r in rows] + [np.zeros(0, np.int64)]), targets)
+    atoms = np.concatenate([np.asarray(targets, dtype=np.int64), extra.astype(np.int64)])
+    index = {int(a): k for k, a in enumerate(atoms)}
+    row_ptr = np.zeros(atoms.size + 1, dtype=np.int64)
+    row_ptr[1 : len(targets) + 1] = np.cumsum([r.size for r in rows])
+    row_ptr[len(targets) + 1 :] = row_ptr[len(targets)]
+    col = np.array([index[int(j)] for r in rows for j in r], dtype=np.int64)
+    return atoms, row_ptr, col
+
+
+def _oracle_worker(args):
+    """Time the fp64 oracle on `targets` (in batches of 8, so that the time
+    budget can end it) for about `seconds`; returns (edges, targets, seconds)."""
+    targets, seconds = args
+    from threadpoolctl import threadpool_limits
 
     from oracle import neighbors_bruteforce, so2_attention_ref
 
     w = _WORKLOAD
+    done_edges, done_targets, busy = 0, 0, 0.0
     with threadpool_limits(limits=1):
-        rows = neighbors_bruteforce(w.pos, w.cutoff, w.box, w.mol_id, rows=targets)
-        row_ptr = np.zeros(w.n_atoms + 1, dtype=np.int64)
-        deg = np.zeros(w.n_atoms, dtype=np.int64)
-        for t, r in zip(targets, rows):
-            deg[t] = r.size
-        np.cumsum(deg, out=row_ptr[1:])
-        col = np.zeros(row_ptr[-1], dtype=np.int32)
-        for t, r in zip(targets, rows):
-            col[row_ptr[t] : row_ptr[t + 1]] = r
-        done_edges, done_targets = 0, 0
-        t0 = time.perf_counter()
-        for t in targets:
+        for b0 in range(0, len(targets), 8):
+            batch = targets[b0 : b0 + 8]
+            rows = neighbors_bruteforce(w.pos, w.cutoff, w.box, w.mol_id, rows=batch)
+            atoms, row_ptr, col = _subsystem(w, batch, rows)
+            t0 = time.perf_counter()
             so2_attention_ref(
-                w.pos, row_ptr, col, w.x, w.w_q, w.w_k, w.w_rad, w.w_so2, l_max=w.l_max,
-                heads=w.heads, cutoff=w.cutoff, envelope_p=w.envelope_p, box=w.box, targets=[t],
+                w.pos[atoms], row_ptr, col, w.x[atoms], w.w_q, w.w_k, w.w_rad, w.w_so2, l_max=w.l_max,
+                heads=w.heads, cutoff=w.cutoff, envelope_p=w.envelope_p, box=w.box, targets=range(len(batch)),
             )
-            done_edges += int(deg[t])
-            done_targets += 1
-            if time.perf_counter() - t0 > seconds:
+            busy += time.perf_counter() - t0
+            done_edges += int(row_ptr[len(batch)])
+            done_targets += len(batch)
+            if busy > seconds:
                 break
-        return done_edges, done_targets, time.perf_counter() - t0
+    return done_edges, done_targets, busy
 
 
 _WORKLOAD = None
 
 
-def cpu_baseline(w, seconds):
-    """Oracle messages/s on this host: fork one worker per core, each timing the
-    per-edge oracle on its own seeded share of targets for about `seconds`."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, seconds, max_workers=16):
+    """Oracle messages/s on this host, before the GPU is touched: first one
+    worker alone (the single-process rate), then one forked single-threaded
+    worker per usable core (at most max_workers, the CPU share of one GPU),
+    each timing the per-edge oracle on its own seeded share of targets for
+    about `seconds`.  The oracle runs on the sub-system of each batch's
+    targets and their neighbours, which gives the same outputs."""
     import multiprocessing as mp
 
     import numpy as np
@@ -142,16 +170,18 @@ def cpu_baseline(w, seconds):
     global _WORKLOAD
     _WORKLOAD = w
     try:
-        cores = len(os.sched_getaffinity(0))
+        avail = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
+        avail = os.cpu_count() or 1
+    workers = max(1, min(avail, max_workers))
     order = np.random.default_rng(1234).permutation(w.n_atoms)
-    shares = [order[k::cores][:400].tolist() for k in range(cores)]
     ctx = mp.get_context("fork")
+    with ctx.Pool(1) as pool:
+        e1, t1, b1 = pool.map(_oracle_worker, [(order[:400].tolist(), seconds / 3)])[0]
+    shares = [order[400 + k :: workers][:400].tolist() for k in range(workers)]
     t0 = time.perf_counter()
-    with ctx.Pool(cores) as pool:
-        res = pool.map(_oracle_worker, [(w.name, s, seconds) for s in shares])
+    with ctx.Pool(workers) as pool:
+        res = pool.map(_oracle_worker, [(s, seconds) for s in shares])
     wall = time.perf_counter() - t0
     edges = sum(r[0] for r in res)
     targets = sum(r[1] for r in res)
@@ -159,10 +189,15 @@ def cpu_baseline(w, seconds):
     return {
         "value": edges / busy,
         "unit": "messages/s",
-        "cores": cores,
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"{targets} seeded target atoms of {w.name} ({edges} edges), fp64 per-edge oracle, "
-        f"{cores} forked single-threaded workers, ~{seconds:.0f} s each (wall {wall:.1f} s incl. graph rows)",
+        "sample": f"{targets} seeded target atoms of {w.name} ({edges} edges), fp64 per-edge oracle on each "
+        f"batch's sub-system, {workers} forked single-threaded workers, ~{seconds:.0f} s each "
+        f"(wall {wall:.1f} s incl. graph rows)",
+        "single_process_value": e1 / b1,
+        "single_process_sample": f"{t1} target atoms ({e1} edges) in {b1:.1f} s, one single-threaded worker",
+        "host_cores_available": avail,
+        "cpu_model": _cpu_model(),
     }
 
 
@@ -170,6 +205,11 @@ def cpu_baseline(w, seconds):
 
 
 def run_gpu(w, steps, warmup):
+    """Warm-up, then `steps` timed steps (neighbour build + attention forward)
+    between device synchronisations; the fused kernel of every timed step is
+    bracketed by torch events on the stream the library launches on (torch's
+    current stream), by calling the prologue and the fused kernel as two
+    stages."""
     import numpy as np
     import torch
 
@@ -188,47 +228,45 @@ def run_gpu(w, steps, warmup):
     E = int(col.numel())
     nc = (w.l_max + 1) ** 2
     desc = sea.make_desc(
-        n_atoms=w.n_atoms, n_targets=w.n_atoms, n_edges=E, l_max=w.l_max, channels=w.channels,
-        heads=w.heads, n_rbf=w.n_rbf, envelope_p=w.envelope_p, cutoff=w.cutoff, flags=0,
+        n_atoms=w.n_atoms, n_targets=w.n_atoms, l_max=w.l_max, channels=w.channels, heads=w.heads,
+        n_rbf=w.n_rbf, envelope_p=w.envelope_p, cutoff=w.cutoff, flags=0,
         dtype=sea.SO2_BF16 if w.dtype == "bf16" else sea.SO2_FP32,
     )
     kind = sea.attention_kernel_kind(desc)
     attn_ws = torch.empty(sea.attention_workspace_bytes(desc), dtype=torch.uint8, device=dev)
     y = torch.empty((w.n_atoms, nc, w.channels), dtype=torch.float32, device=dev)
     cap = E
+    kw = dict(l_max=w.l_max, heads=w.heads, cutoff=w.cutoff, envelope_p=w.envelope_p, box=w.box, out=y,
+              workspace=attn_ws)
 
-    def step():
+    def step(ev=None):
         rp, cl = sea.build_neighbors(pos, w.cutoff, box=w.box, mol_id=mol, capacity=cap, workspace=nb_ws)
-        sea.so2_attention_fwd(
-            pos, rp, cl, x, w_q, w_k, w_rad, w_so2, l_max=w.l_max, heads=w.heads, cutoff=w.cutoff,
-            envelope_p=w.envelope_p, box=w.box, out=y, workspace=attn_ws,
-        )
+        sea.so2_attention_fwd(pos, rp, cl, x, w_q, w_k, w_rad, w_so2, stages=sea.STAGE_PREPARE, **kw)
+        if ev is not None:
+            ev[0].record()
+        sea.so2_attention_fwd(pos, rp, cl, x, w_q, w_k, w_rad, w_so2, stages=sea.STAGE_FUSED, **kw)
+        if ev is not None:
+            ev[1].record()
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats(dev)
-    timer = sea.KernelTimer(steps)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        timer.arm()
-        step()
+    for k in range(steps):
+        step(events[k])
     torch.cuda.synchronize()
     total = time.perf_counter() - t0
-    timer.disarm()
-    kern_ms = timer.elapsed_ms()
-    timer.close()
+    kern_ms = [a.elapsed_time(b) for a, b in events]
     peak_bytes = torch.cuda.max_memory_allocated(dev)
 
-    # attention-only rate (same kernel, no neighbour build)
+    # attention-only rate (both stages, no neighbour build)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for _ in range(steps):
-        sea.so2_attention_fwd(
-            pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, l_max=w.l_max, heads=w.heads,
-            cutoff=w.cutoff, envelope_p=w.envelope_p, box=w.box, out=y, workspace=attn_ws,
-        )
+        sea.so2_attention_fwd(pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, **kw)
     torch.cuda.synchronize()
     attn_total = time.perf_counter() - t1
     return dict(
@@ -347,17 +385,19 @@ def swiglu_bench(steps, warmup):
     for _ in range(warmup):
         sea.swiglu_s2(x, A, B, G, O, out=y, workspace=ws)
     torch.cuda.synchronize()
-    timer = sea.KernelTimer(steps)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in ev:
-        timer.arm()
+    mk_ev = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev = [mk_ev() for _ in range(steps)]
+    gev = [mk_ev() for _ in range(steps)]
+    for (a, b), (ga, gb) in zip(ev, gev):
         a.record()
-        sea.swiglu_s2(x, A, B, G, O, out=y, workspace=ws)
+        sea.swiglu_s2(x, A, B, G, O, out=y, workspace=ws, stages=sea.STAGE_SW_MAPS)
+        ga.record()
+        sea.swiglu_s2(x, A, B, G, O, out=y, workspace=ws, stages=sea.STAGE_SW_GRID)
+        gb.record()
+        sea.swiglu_s2(x, A, B, G, O, out=y, workspace=ws, stages=sea.STAGE_SW_OUT)
         b.record()
     torch.cuda.synchronize()
-    timer.disarm()
-    grid_ms = timer.elapsed_ms()
-    timer.close()
+    grid_ms = [ga.elapsed_time(gb) for ga, gb in gev]
     ms = sorted(a.elapsed_time(b) for a, b in ev)
     mean = sum(ms) / len(ms)
     gmean = sum(grid_ms) / len(grid_ms)
@@ -423,7 +463,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="small_molecules")
+    ap.add_argument("--workload", default="water_100k",
+                    help="water_100k (default, the largest single-GPU system), solvated_protein, small_molecules, "
+                    "water_l6 or tiny_fp32")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, metavar="MIB", default=0,

@@ -33,16 +33,22 @@
  *   head h owns channels [h*C/H, (h+1)*C/H)
  *   edge vector r_ij = p_j - p_i (target i, source j), minimum image when a
  *   box is given; envelope u(s) = 1 - (p+1)(p+2)/2 s^p + p(p+2) s^(p+1)
- *   - p(p+1)/2 s^(p+2) for s = |r_ij|/rc < 1, else 0.
+ *   - p(p+1)/2 s^(p+2) for s = |r_ij|/rc < 1, else 0, evaluated as
+ *   (1-s)^3 sum_{k<p} (k+1)(k+2)/2 s^k with |r_ij| and 1-s in fp64, so it
+ *   keeps its relative precision for edges just inside the cutoff.
  *
  * Conventions for every call
  *   Pointers are device pointers unless the name ends in _host.  The caller
- *   owns every buffer; the library allocates no device memory: scratch comes
- *   from the caller's `workspace` (size from the *_workspace_bytes query,
- *   256-byte alignment required).  Argument errors are detected on the host
- *   before anything is launched and leave every output untouched.  Calls on
- *   different streams may run concurrently if their buffers do not overlap.
- *   `stream` is a hipStream_t (NULL = the default stream).
+ *   owns every buffer; the library allocates no device memory and creates no
+ *   streams or events: scratch comes from the caller's `workspace` (size
+ *   from the *_workspace_bytes query, 256-byte alignment required), and
+ *   every kernel runs on the caller's `stream` (a hipStream_t, NULL = the
+ *   default stream).  Calls keep no state between them (apart from the text
+ *   behind so2_last_device_error, which is per host thread), so they are
+ *   thread-safe; calls on different streams may run concurrently if their
+ *   buffers, workspaces included, do not overlap.  Argument errors are
+ *   detected on the host before anything is launched and leave every output
+ *   untouched.
  */
 #ifndef SO2ATTN_H
 #define SO2ATTN_H
@@ -71,6 +77,19 @@ typedef enum { SO2_FP32 = 0, SO2_BF16 = 1 } so2_dtype;
 enum {
   SO2_FLAG_RBF_ENVELOPE = 1u, /* alternative reading: phi_k is also multiplied by u */
   SO2_FLAG_NO_RADIAL = 2u     /* g_ij == 1 (special-case tests)                      */
+};
+
+/* Steps of so2_attention_fwd, for so2_attention_fwd_stages. */
+enum {
+  SO2_STAGE_PREPARE = 1u, /* q/k projection and the fused kernel's prologue (workspace) */
+  SO2_STAGE_FUSED = 2u    /* the fused attention kernel: workspace -> y               */
+};
+
+/* Steps of so2_swiglu_s2, for so2_swiglu_s2_stages. */
+enum {
+  SO2_STAGE_SW_MAPS = 1u, /* per-degree maps u, v and the gate map g (workspace) */
+  SO2_STAGE_SW_GRID = 2u, /* grid product and gate (workspace -> workspace)      */
+  SO2_STAGE_SW_OUT = 4u   /* per-degree output maps (workspace -> y)             */
 };
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -122,7 +141,6 @@ so2_status build_neighbors(const float* pos, int32_t n_atoms, const int32_t* mol
 typedef struct {
   int32_t n_atoms;    /* rows of x and pos                                    */
   int32_t n_targets;  /* outputs y[0..n_targets) (targets are atoms 0..T-1)   */
-  int64_t n_edges;    /* >= row_ptr[n_targets] - row_ptr[0]; sizes workspace  */
   int32_t l_max;      /* 0..6                                                 */
   int32_t channels;   /* C >= 1                                               */
   int32_t heads;      /* H >= 1, C % H == 0                                   */
@@ -139,8 +157,8 @@ int64_t so2_weight_count(int32_t l_max, int32_t channels);
 /* Workspace so2_attention_fwd needs (0 if desc is invalid). */
 size_t so2_attention_workspace_bytes(const so2_attn_desc* desc);
 
-/* Which kernel so2_attention_fwd runs for desc: 0 = none (unsupported),
- * 1 = fp32 VALU kernel, 2 = bf16 MFMA kernel. */
+/* Which kernel so2_attention_fwd runs for desc: 0 = none (the call returns
+ * UNSUPPORTED), 1 = fp32 VALU kernel, 2 = bf16 MFMA kernel. */
 int32_t so2_attention_kernel_kind(const so2_attn_desc* desc);
 
 /*   desc      host struct above
@@ -152,11 +170,16 @@ int32_t so2_attention_kernel_kind(const so2_attn_desc* desc);
  *   y         [n_targets][(L+1)^2][C] fp32, written
  *   workspace >= so2_attention_workspace_bytes(desc) bytes
  * Kernels: bf16 with C = 128, 1 <= L <= 6, H <= 16, K <= 32 runs on the
- * MFMA kernel; every other shape (fp32 or bf16) on the VALU kernel.
- * Errors: INVALID_ARGUMENT, UNSUPPORTED (L > 6 or C > 256: no kernel), BOX,
- * WORKSPACE, DEVICE.  Asynchronous on
- * `stream`.  Device memory beyond the caller's buffers: none; activation
- * memory is O(n_atoms) (workspace), never O(E). */
+ * MFMA kernel (bf16 operands, fp32 accumulation); that kernel needs x, w_rad
+ * and w_so2 16-byte aligned (else INVALID_ARGUMENT) and addresses its
+ * repacked copy of x with 32-bit offsets, which caps n_atoms at
+ * (2^32 - 2^16) / (2 (L+1)(L+2) C) (about 559k atoms at L = 4, 299k at
+ * L = 6); beyond that the call returns UNSUPPORTED.  Every other shape
+ * (fp32, or bf16 with other C, L, H or K) runs on the fp32 VALU kernel.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (L > 6, C > 256, or the MFMA shape
+ * past its atom limit), BOX, WORKSPACE, DEVICE.  Asynchronous on `stream`.
+ * Device memory beyond the caller's buffers: none; activation memory is
+ * O(n_atoms) (workspace), never O(E). */
 so2_status so2_attention_fwd(const so2_attn_desc* desc, const float* pos,
                              const float* box_host, const int32_t* row_ptr,
                              const int32_t* col, const void* x, const void* w_q,
@@ -164,13 +187,20 @@ so2_status so2_attention_fwd(const so2_attn_desc* desc, const float* pos,
                              float* y, void* workspace, size_t workspace_bytes,
                              so2_stream_t stream);
 
-/* Benchmark hook: when both are non-NULL, every later so2_attention_fwd
- * call from this thread records `start` on its stream just before the fused
- * attention kernel and `stop` just after it, and every later so2_swiglu_s2
- * call does the same around its grid kernel (hipEvent_t handles created and
- * owned by the caller), so the kernel alone can be timed on the stream it
- * runs on.  so2_set_kernel_timing_events(NULL, NULL) switches it off. */
-void so2_set_kernel_timing_events(void* start, void* stop);
+/* so2_attention_fwd in steps: `stages` is SO2_STAGE_PREPARE, SO2_STAGE_FUSED
+ * or both (both = so2_attention_fwd).  PREPARE writes the query/key
+ * projections, the softmax statistics, the repacked operands and the run
+ * schedule into the workspace; FUSED reads them and writes y.  A FUSED call
+ * must follow a PREPARE call with the same arguments and workspace, on the
+ * same stream or ordered after it; y may be NULL for PREPARE alone.  The
+ * split lets a caller time the fused kernel by itself or overlap the
+ * prologue with other work.  Same errors as so2_attention_fwd, plus
+ * INVALID_ARGUMENT for an empty or unknown `stages`. */
+so2_status so2_attention_fwd_stages(uint32_t stages, const so2_attn_desc* desc, const float* pos,
+                                    const float* box_host, const int32_t* row_ptr, const int32_t* col,
+                                    const void* x, const void* w_q, const void* w_k, const void* w_rad,
+                                    const void* w_so2, float* y, void* workspace, size_t workspace_bytes,
+                                    so2_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * so2_merged_rms_norm - equivariant merged RMS layer norm of node features
@@ -221,6 +251,17 @@ size_t so2_swiglu_s2_workspace_bytes(int32_t n_atoms, int32_t l_max, int32_t cha
 so2_status so2_swiglu_s2(const void* x, const void* w_a, const void* w_b, const void* w_g, const void* w_o, float* y,
                          int32_t n_atoms, int32_t l_max, int32_t channels, int32_t dtype, void* workspace,
                          size_t workspace_bytes, so2_stream_t stream);
+
+/* so2_swiglu_s2 in steps: `stages` is any non-empty union of
+ * SO2_STAGE_SW_MAPS, SO2_STAGE_SW_GRID and SO2_STAGE_SW_OUT (all three =
+ * so2_swiglu_s2); the steps run in that order and pass their results
+ * through the workspace, so a step must follow the earlier ones with the same
+ * arguments and workspace, on the same stream or ordered after them.  Lets a
+ * caller time or overlap the steps.  Same errors as so2_swiglu_s2, plus
+ * INVALID_ARGUMENT for an empty or unknown `stages`. */
+so2_status so2_swiglu_s2_stages(uint32_t stages, const void* x, const void* w_a, const void* w_b, const void* w_g,
+                                const void* w_o, float* y, int32_t n_atoms, int32_t l_max, int32_t channels,
+                                int32_t dtype, void* workspace, size_t workspace_bytes, so2_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Host-side diagnostics (no device work): evaluate, on the CPU, the same

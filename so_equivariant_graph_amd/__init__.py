@@ -37,6 +37,10 @@ FLAG_NO_RADIAL = 2
 
 KERNEL_NONE, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
 
+STAGE_PREPARE = 1  # so2_attention_fwd_stages: q/k, statistics, repack, schedule
+STAGE_FUSED = 2  # the fused attention kernel
+STAGE_SW_MAPS, STAGE_SW_GRID, STAGE_SW_OUT = 1, 2, 4  # so2_swiglu_s2_stages
+
 EXPORTED_SYMBOLS = (
     "so2_status_string",
     "so2_last_device_error",
@@ -46,11 +50,12 @@ EXPORTED_SYMBOLS = (
     "so2_attention_workspace_bytes",
     "so2_attention_kernel_kind",
     "so2_attention_fwd",
+    "so2_attention_fwd_stages",
     "so2_edge_frame_host",
-    "so2_set_kernel_timing_events",
     "so2_merged_rms_norm",
     "so2_swiglu_s2_workspace_bytes",
     "so2_swiglu_s2",
+    "so2_swiglu_s2_stages",
 )
 
 
@@ -58,7 +63,6 @@ class AttnDesc(ctypes.Structure):
     _fields_ = [
         ("n_atoms", ctypes.c_int32),
         ("n_targets", ctypes.c_int32),
-        ("n_edges", ctypes.c_int64),
         ("l_max", ctypes.c_int32),
         ("channels", ctypes.c_int32),
         ("heads", ctypes.c_int32),
@@ -114,16 +118,19 @@ def load_library(path: str = LIB_PATH):
     lib.so2_attention_kernel_kind.restype = i32
     lib.so2_attention_fwd.argtypes = [ctypes.POINTER(AttnDesc)] + [vp] * 11 + [sz, vp]
     lib.so2_attention_fwd.restype = ctypes.c_int
+    lib.so2_attention_fwd_stages.argtypes = [ctypes.c_uint32, ctypes.POINTER(AttnDesc)] + [vp] * 11 + [sz, vp]
+    lib.so2_attention_fwd_stages.restype = ctypes.c_int
     lib.so2_edge_frame_host.argtypes = [i32, vp, vp, vp]
     lib.so2_edge_frame_host.restype = ctypes.c_int
-    lib.so2_set_kernel_timing_events.argtypes = [vp, vp]
-    lib.so2_set_kernel_timing_events.restype = None
     lib.so2_merged_rms_norm.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, vp]
     lib.so2_merged_rms_norm.restype = ctypes.c_int
     lib.so2_swiglu_s2_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.so2_swiglu_s2_workspace_bytes.restype = ctypes.c_size_t
     lib.so2_swiglu_s2.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, ctypes.c_size_t, vp]
     lib.so2_swiglu_s2.restype = ctypes.c_int
+    lib.so2_swiglu_s2_stages.argtypes = [ctypes.c_uint32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp,
+                                         ctypes.c_size_t, vp]
+    lib.so2_swiglu_s2_stages.restype = ctypes.c_int
     _lib_handle = lib
     return lib
 
@@ -165,11 +172,11 @@ def neighbors_workspace_bytes(n_atoms: int) -> int:
     return int(load_library().so2_neighbors_workspace_bytes(n_atoms))
 
 
-def make_desc(*, n_atoms, n_targets, n_edges, l_max, channels, heads, n_rbf, envelope_p, cutoff,
-              flags, dtype) -> AttnDesc:
+def make_desc(*, n_atoms, n_targets, l_max, channels, heads, n_rbf, envelope_p, cutoff, flags,
+              dtype) -> AttnDesc:
     return AttnDesc(
-        int(n_atoms), int(n_targets), int(n_edges), int(l_max), int(channels), int(heads),
-        int(n_rbf), int(envelope_p), float(np.float32(cutoff)), int(flags), int(dtype),
+        int(n_atoms), int(n_targets), int(l_max), int(channels), int(heads), int(n_rbf),
+        int(envelope_p), float(np.float32(cutoff)), int(flags), int(dtype),
     )
 
 
@@ -230,9 +237,12 @@ def _dtype_code(t):
 
 
 def so2_attention_fwd(pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, *, l_max, heads, cutoff,
-                      envelope_p=5, box=None, flags=0, n_targets=None, out=None, workspace=None):
+                      envelope_p=5, box=None, flags=0, n_targets=None, out=None, workspace=None,
+                      stages=STAGE_PREPARE | STAGE_FUSED):
     """Fused SO(2) attention forward.  x: [N,(L+1)^2,C] (float32 or bfloat16);
-    the weights share x's dtype.  Returns y [n_targets,(L+1)^2,C] float32."""
+    the weights share x's dtype.  Returns y [n_targets,(L+1)^2,C] float32.
+    `stages` selects the steps (so2_attention_fwd_stages): a FUSED call
+    reuses the workspace a PREPARE call with the same arguments filled."""
     import torch
 
     lib = load_library()
@@ -251,8 +261,8 @@ def so2_attention_fwd(pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, *, l_max, he
     tensors = [t.contiguous() for t in (pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2)]
     pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2 = tensors
     desc = make_desc(
-        n_atoms=n, n_targets=nt, n_edges=col.numel(), l_max=l_max, channels=C, heads=heads,
-        n_rbf=w_rad.shape[0], envelope_p=envelope_p, cutoff=cutoff, flags=flags, dtype=dt,
+        n_atoms=n, n_targets=nt, l_max=l_max, channels=C, heads=heads, n_rbf=w_rad.shape[0],
+        envelope_p=envelope_p, cutoff=cutoff, flags=flags, dtype=dt,
     )
     ws_bytes = lib.so2_attention_workspace_bytes(ctypes.byref(desc))
     if ws_bytes == 0:
@@ -263,9 +273,9 @@ def so2_attention_fwd(pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, *, l_max, he
     y = out if out is not None else torch.empty((nt, nc, C), dtype=torch.float32, device=x.device)
     keep, box_p = _host_box(box)
     col_arg = col if col.numel() > 0 else row_ptr  # any valid device pointer when E = 0
-    st = lib.so2_attention_fwd(
-        ctypes.byref(desc), _ptr(pos), box_p, _ptr(row_ptr), _ptr(col_arg), _ptr(x), _ptr(w_q),
-        _ptr(w_k), _ptr(w_rad), _ptr(w_so2), _ptr(y), _ptr(workspace), ws_bytes,
+    st = lib.so2_attention_fwd_stages(
+        int(stages), ctypes.byref(desc), _ptr(pos), box_p, _ptr(row_ptr), _ptr(col_arg), _ptr(x),
+        _ptr(w_q), _ptr(w_k), _ptr(w_rad), _ptr(w_so2), _ptr(y), _ptr(workspace), ws_bytes,
         _stream_handle(x.device),
     )
     _check(st, "so2_attention_fwd")
@@ -292,63 +302,6 @@ def merged_rms_norm(x, gamma, *, eps=1e-5, out=None):
                                  _stream_handle(x.device))
     _check(st, "so2_merged_rms_norm")
     return y
-
-
-def hip_runtime():
-    """The libamdhip64 already loaded in this process (torch's), via ctypes."""
-    import re
-
-    load_library()
-    with open("/proc/self/maps") as f:
-        paths = sorted(set(re.findall(r"\S*libamdhip64\.so\S*", f.read())))
-    if not paths:
-        raise RuntimeError("no HIP runtime loaded")
-    hip = ctypes.CDLL(paths[0])
-    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-    hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
-    return hip
-
-
-class KernelTimer:
-    """Times the fused attention kernel (so2_attention_fwd) or the grid kernel
-    (so2_swiglu_s2) alone with HIP events recorded by the library on the
-    kernel's own stream (one event pair per call)."""
-
-    def __init__(self, n_calls: int):
-        self.hip = hip_runtime()
-        self.pairs = []
-        for _ in range(n_calls):
-            a, b = ctypes.c_void_p(), ctypes.c_void_p()
-            assert self.hip.hipEventCreate(ctypes.byref(a)) == 0
-            assert self.hip.hipEventCreate(ctypes.byref(b)) == 0
-            self.pairs.append((a, b))
-        self.k = 0
-
-    def arm(self):
-        a, b = self.pairs[self.k]
-        load_library().so2_set_kernel_timing_events(a, b)
-        self.k += 1
-
-    def disarm(self):
-        load_library().so2_set_kernel_timing_events(None, None)
-
-    def elapsed_ms(self):
-        out = []
-        for a, b in self.pairs[: self.k]:
-            self.hip.hipEventSynchronize(b)
-            ms = ctypes.c_float(0.0)
-            assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
-            out.append(ms.value)
-        return out
-
-    def close(self):
-        self.disarm()
-        for a, b in self.pairs:
-            self.hip.hipEventDestroy(a)
-            self.hip.hipEventDestroy(b)
-        self.pairs = []
 
 
 def edge_frame_host(l_max: int, rhat):
@@ -384,10 +337,12 @@ __all__ = [
 ]
 
 
-def swiglu_s2(x, w_a, w_b, w_g, w_o, *, out=None, workspace=None):
+def swiglu_s2(x, w_a, w_b, w_g, w_o, *, out=None, workspace=None,
+              stages=STAGE_SW_MAPS | STAGE_SW_GRID | STAGE_SW_OUT):
     """SwiGLU-S2 activation of node features.  x: [N,(L+1)^2,C] float32 or
     bfloat16; w_a, w_b, w_o: [L+1,C,C] ([l][in][out]) and w_g: [C,C] in x's
-    dtype.  Returns y [N,(L+1)^2,C] float32."""
+    dtype.  Returns y [N,(L+1)^2,C] float32.  `stages` selects the steps
+    (so2_swiglu_s2_stages), which pass their results through `workspace`."""
     import torch
 
     lib = load_library()
@@ -409,7 +364,7 @@ def swiglu_s2(x, w_a, w_b, w_g, w_o, *, out=None, workspace=None):
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     y = out if out is not None else torch.empty((n, nc, C), dtype=torch.float32, device=x.device)
-    st = lib.so2_swiglu_s2(_ptr(x), _ptr(w_a), _ptr(w_b), _ptr(w_g), _ptr(w_o), _ptr(y), n, L, C, dt,
-                           _ptr(workspace), ws_bytes, _stream_handle(x.device))
+    st = lib.so2_swiglu_s2_stages(int(stages), _ptr(x), _ptr(w_a), _ptr(w_b), _ptr(w_g), _ptr(w_o), _ptr(y), n,
+                                  L, C, dt, _ptr(workspace), ws_bytes, _stream_handle(x.device))
     _check(st, "so2_swiglu_s2")
     return y

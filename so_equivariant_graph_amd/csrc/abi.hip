@@ -13,8 +13,6 @@
 namespace so2 {
 
 static thread_local char g_last_error[256] = "";
-static thread_local hipEvent_t g_timing_start = nullptr;
-static thread_local hipEvent_t g_timing_stop = nullptr;
 
 so2_status device_error(hipError_t err) {
   snprintf(g_last_error, sizeof(g_last_error), "%s: %s", hipGetErrorName(err),
@@ -31,7 +29,6 @@ enum Kind { kNone = 0, kValu = 1, kMfma = 2 };
 so2_status check_desc(const so2_attn_desc* d) {
   if (!d) return SO2_ERR_INVALID_ARGUMENT;
   if (d->n_atoms < 1 || d->n_targets < 0 || d->n_targets > d->n_atoms) return SO2_ERR_INVALID_ARGUMENT;
-  if (d->n_edges < 0) return SO2_ERR_INVALID_ARGUMENT;
   if (d->l_max < 0 || d->channels < 1 || d->heads < 1) return SO2_ERR_INVALID_ARGUMENT;
   if (d->channels % d->heads) return SO2_ERR_INVALID_ARGUMENT;
   if (d->n_rbf < 2 || d->envelope_p < 1 || d->envelope_p > 64) return SO2_ERR_INVALID_ARGUMENT;
@@ -42,8 +39,11 @@ so2_status check_desc(const so2_attn_desc* d) {
   return SO2_OK;
 }
 
+// bf16 shapes the MFMA kernel takes run there; past its size limit they are
+// refused (kNone) rather than moved to the untuned VALU kernel.
 Kind pick_kind(const so2_attn_desc* d) {
-  if (d->dtype == SO2_BF16 && mfma_supported(d->l_max, d->channels, d->heads, d->n_rbf, d->n_atoms)) return kMfma;
+  if (d->dtype == SO2_BF16 && mfma_shape(d->l_max, d->channels, d->heads, d->n_rbf))
+    return mfma_fits(d->l_max, d->n_atoms) ? kMfma : kNone;
   if (valu_supported(d->l_max, d->channels, d->heads)) return kValu;
   return kNone;
 }
@@ -139,19 +139,21 @@ int32_t so2_attention_kernel_kind(const so2_attn_desc* desc) {
   return (int32_t)pick_kind(desc);
 }
 
-so2_status so2_attention_fwd(const so2_attn_desc* desc, const float* pos, const float* box_host,
-                             const int32_t* row_ptr, const int32_t* col, const void* x,
-                             const void* w_q, const void* w_k, const void* w_rad,
-                             const void* w_so2, float* y, void* workspace,
-                             size_t workspace_bytes, so2_stream_t stream) {
+so2_status so2_attention_fwd_stages(uint32_t stages, const so2_attn_desc* desc, const float* pos,
+                                    const float* box_host, const int32_t* row_ptr, const int32_t* col,
+                                    const void* x, const void* w_q, const void* w_k, const void* w_rad,
+                                    const void* w_so2, float* y, void* workspace, size_t workspace_bytes,
+                                    so2_stream_t stream) {
+  if (stages == 0 || (stages & ~(uint32_t)(SO2_STAGE_PREPARE | SO2_STAGE_FUSED))) return SO2_ERR_INVALID_ARGUMENT;
   so2_status st = check_desc(desc);
   if (st != SO2_OK) return st;
   Kind kind = pick_kind(desc);
   if (kind == kNone) return SO2_ERR_UNSUPPORTED;
   st = check_box(box_host, desc->cutoff);
   if (st != SO2_OK) return st;
-  if (!pos || !row_ptr || !col || !x || !w_q || !w_k || !w_rad || !w_so2 || !y || !workspace)
+  if (!pos || !row_ptr || !col || !x || !w_q || !w_k || !w_rad || !w_so2 || !workspace)
     return SO2_ERR_INVALID_ARGUMENT;
+  if ((stages & SO2_STAGE_FUSED) && !y) return SO2_ERR_INVALID_ARGUMENT;
   const AttnLayout lay = attn_layout(desc, kind);
   if (workspace_bytes < lay.total || ((uintptr_t)workspace & 255)) return SO2_ERR_WORKSPACE;
 
@@ -172,7 +174,6 @@ so2_status so2_attention_fwd(const so2_attn_desc* desc, const float* pos, const 
   a.scratch_bytes = lay.scratch_bytes;
   a.n_atoms = desc->n_atoms;
   a.n_targets = desc->n_targets;
-  a.n_edges = desc->n_edges;
   a.L = desc->l_max;
   a.C = desc->channels;
   a.H = desc->heads;
@@ -187,22 +188,28 @@ so2_status so2_attention_fwd(const so2_attn_desc* desc, const float* pos, const 
   if (kind == kMfma && !mfma_aligned(a)) return SO2_ERR_INVALID_ARGUMENT;
 
   hipStream_t s = (hipStream_t)stream;
-  st = launch_qk_proj(a, s);
-  if (st != SO2_OK) return st;
-  if (kind == kMfma) {
-    st = launch_attention_mfma_prep(a, s);
+  if (stages & SO2_STAGE_PREPARE) {
+    st = launch_qk_proj(a, s);
+    if (st != SO2_OK) return st;
+    if (kind == kMfma) {
+      st = launch_attention_mfma_prep(a, s);
+      if (st != SO2_OK) return st;
+    }
+  }
+  if (stages & SO2_STAGE_FUSED) {
+    st = kind == kMfma ? launch_attention_mfma(a, s) : launch_attention_valu(a, s);
     if (st != SO2_OK) return st;
   }
-  if (g_timing_start && g_timing_stop) SO2_CHECK(hipEventRecord(g_timing_start, s));
-  st = kind == kMfma ? launch_attention_mfma(a, s) : launch_attention_valu(a, s);
-  if (st != SO2_OK) return st;
-  if (g_timing_start && g_timing_stop) SO2_CHECK(hipEventRecord(g_timing_stop, s));
   return SO2_OK;
 }
 
-void so2_set_kernel_timing_events(void* start, void* stop) {
-  g_timing_start = (hipEvent_t)start;
-  g_timing_stop = (hipEvent_t)stop;
+so2_status so2_attention_fwd(const so2_attn_desc* desc, const float* pos, const float* box_host,
+                             const int32_t* row_ptr, const int32_t* col, const void* x,
+                             const void* w_q, const void* w_k, const void* w_rad,
+                             const void* w_so2, float* y, void* workspace,
+                             size_t workspace_bytes, so2_stream_t stream) {
+  return so2_attention_fwd_stages(SO2_STAGE_PREPARE | SO2_STAGE_FUSED, desc, pos, box_host, row_ptr, col, x, w_q,
+                                  w_k, w_rad, w_so2, y, workspace, workspace_bytes, stream);
 }
 
 so2_status so2_merged_rms_norm(const void* x, const float* gamma, void* y, int32_t n_atoms, int32_t l_max,
@@ -220,15 +227,24 @@ size_t so2_swiglu_s2_workspace_bytes(int32_t n_atoms, int32_t l_max, int32_t cha
   return swiglu_s2_workspace_bytes(n_atoms, l_max, channels, dtype);
 }
 
-so2_status so2_swiglu_s2(const void* x, const void* w_a, const void* w_b, const void* w_g, const void* w_o, float* y,
-                         int32_t n_atoms, int32_t l_max, int32_t channels, int32_t dtype, void* workspace,
-                         size_t workspace_bytes, so2_stream_t stream) {
+so2_status so2_swiglu_s2_stages(uint32_t stages, const void* x, const void* w_a, const void* w_b, const void* w_g,
+                                const void* w_o, float* y, int32_t n_atoms, int32_t l_max, int32_t channels,
+                                int32_t dtype, void* workspace, size_t workspace_bytes, so2_stream_t stream) {
+  if (stages == 0 || (stages & ~(uint32_t)(SO2_STAGE_SW_MAPS | SO2_STAGE_SW_GRID | SO2_STAGE_SW_OUT)))
+    return SO2_ERR_INVALID_ARGUMENT;
   if (n_atoms < 0 || l_max < 0 || channels < 1) return SO2_ERR_INVALID_ARGUMENT;
   if (dtype != SO2_FP32 && dtype != SO2_BF16) return SO2_ERR_INVALID_ARGUMENT;
   if (n_atoms > 0 && (!x || !w_a || !w_b || !w_g || !w_o || !y)) return SO2_ERR_INVALID_ARGUMENT;
   if (l_max > kMaxL) return SO2_ERR_UNSUPPORTED;
-  return launch_swiglu_s2(x, w_a, w_b, w_g, w_o, y, n_atoms, l_max, channels, dtype, workspace, workspace_bytes,
-                          (hipStream_t)stream, g_timing_start, g_timing_stop);
+  return launch_swiglu_s2(stages, x, w_a, w_b, w_g, w_o, y, n_atoms, l_max, channels, dtype, workspace,
+                          workspace_bytes, (hipStream_t)stream);
+}
+
+so2_status so2_swiglu_s2(const void* x, const void* w_a, const void* w_b, const void* w_g, const void* w_o, float* y,
+                         int32_t n_atoms, int32_t l_max, int32_t channels, int32_t dtype, void* workspace,
+                         size_t workspace_bytes, so2_stream_t stream) {
+  return so2_swiglu_s2_stages(SO2_STAGE_SW_MAPS | SO2_STAGE_SW_GRID | SO2_STAGE_SW_OUT, x, w_a, w_b, w_g, w_o, y,
+                              n_atoms, l_max, channels, dtype, workspace, workspace_bytes, stream);
 }
 
 so2_status so2_edge_frame_host(int32_t l_max, const float* rhat, float* R_out, float* D_out) {

@@ -43,9 +43,10 @@
 //
 // Workgroup: 8 waves (512 lanes), two per SIMD so that one wave's memory
 // waits are covered by the other's MFMAs; wave w owns output channels
-// [16w, 16w+16).  Each workgroup takes a run of consecutive target atoms
-// holding about the same number of edges as every other workgroup (a
-// scheduling kernel orders the runs longest first); its edges are processed in
+// [16w, 16w+16).  Each workgroup (one per compute unit) takes a run of
+// consecutive target atoms holding about the same number of edge chunks as
+// every other workgroup (scheduling kernels choose the runs); its edges are
+// processed in
 // chunks of at most 64 (32) edges whose targets span at most 4 consecutive
 // indices (4 accumulator slots, slot = target mod 4); a target whose edges
 // continue into the next chunk keeps its slot, a target whose last edge is
@@ -89,7 +90,6 @@ constexpr int kNT = kC / (16 * kWaves);  // 16-column tiles per wave: wave w own
 constexpr int kGR = 1;                // generator rows per lane and K step
 constexpr int kMaxM = 64;             // largest chunk
 constexpr int kSlots = 4;             // targets live in one chunk
-constexpr int kEdgesPerGroup = 384;   // edges per workgroup for L = 5, 6 (twelve 32-edge chunks)
 constexpr int kKC = 128;              // channels per A chunk (one degree, 4 MFMA K steps)
 constexpr int kMaxHeads = 16;
 constexpr int kMaxRbf = 32;           // radial basis functions kept per edge in LDS
@@ -149,7 +149,6 @@ struct MfmaParams {
   const int32_t* row_ptr;
   const int32_t* col;
   const int32_t* gs;      // first target of every group, gs[n_groups] = n_targets
-  const int32_t* order;   // groups of each XCD's range, most chunks first
   const uint32_t* xp;     // x repacked as component pairs [n_atoms][pair_off(L+1)][C]
   const float* wrad;      // w_rad in fp32 [K][C]
   const uint16_t* wf;     // w_so2 in MFMA fragment order
@@ -211,15 +210,6 @@ template <int G>
 __device__ inline typename XVec<G>::type buffer_load_x(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   if constexpr (G == 4) return buffer_load16(r, voff, soff);
   else return buffer_load8(r, voff, soff);
-}
-
-__device__ inline void edge_vec(const MfmaParams& P, int i, int j, float* r) {
-#pragma unroll
-  for (int d = 0; d < 3; ++d) {
-    float v = P.pos[3 * (int64_t)j + d] - P.pos[3 * (int64_t)i + d];
-    if (P.periodic) v = v - P.box[d] * rintf(v / P.box[d]);
-    r[d] = v;
-  }
 }
 
 // ---------------------------------------------------------------- prologue
@@ -319,10 +309,8 @@ __global__ void __launch_bounds__(256) attn_stats_kernel(MfmaParams P, int C) {
     float ul = 0.0f;
     if (lane < nb) {
       jl = P.col[b0 + lane];
-      float r[3];
-      edge_vec(P, t, jl, r);
-      const float rho = sqrtf(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
-      ul = envelope_u(rho / P.cutoff, P.p);
+      const EdgeGeo g = edge_geometry(P.pos, t, jl, P.periodic, P.box, P.cutoff);
+      ul = envelope_u(g.s, g.t, P.p);
     }
     // one edge per half-wave: logits per head and the online softmax (both
     // halves run every iteration, so that the shuffles see all 64 lanes)
@@ -386,6 +374,7 @@ struct SmemT {
   uint16_t rowinfo[NRI];  // accumulator row R -> slot << 8 | component, 0xffff past the rows
   int row_t[kMaxM];       // target of each edge row
   f32x4 row_rv[kMaxM];    // minimum-image edge vector and its length
+  float row_u[kMaxM];     // envelope of each edge row
 };
 // the row table covers the accumulator tiles (at least 112 entries)
 template <int L>
@@ -471,16 +460,12 @@ __device__ inline int a_off(int row, int group) { return row * kKC + 8 * (group 
 __device__ inline int g_swz(int row) { return ((row & 1) << 3) | ((row >> 1) & 1); }
 __device__ inline int g_off(int row, int group) { return row * kC + 4 * (group ^ g_swz(row)); }
 
-// Edge er of the chunk: its target t (one of the slots' targets), source j
-// and minimum-image vector r_ij = p_j - p_t.
+// Edge er of the chunk: its target t (one of the slots' targets).
 template <class SM>
-__device__ inline void row_edge(const MfmaParams& P, const SM& S, int er, int t_first, int& t, int& j,
-                                float* rv) {
+__device__ inline void row_edge(const SM& S, int er, int t_first, int& t) {
   int s = 0;
   while (s + 1 < kSlots && S.rp[s + 1] <= er) ++s;
   t = t_first + s;
-  j = P.col[er];
-  edge_vec(P, t, j, rv);
 }
 
 // D^l rows of one edge as bf16 pairs: dword (l, a, p) at dpair_off(l) +
@@ -1170,91 +1155,10 @@ __device__ inline void flush_slots(const MfmaParams& P, const Smem<L>& S, int t_
 
 // ---------------------------------------------------------------- kernel
 
-// First target of group g: the smallest t with row_ptr[t] - row_ptr[0] >=
-// g E / n_groups (E = edges of all targets); group n_groups starts at
-// n_targets.  Binary search.
-__device__ inline int group_start(const int32_t* row_ptr, int n_targets, int g, int n_groups) {
-  if (g >= n_groups) return n_targets;
-  const int e0 = row_ptr[0];
-  const int64_t E = (int64_t)row_ptr[n_targets] - e0;
-  const int64_t goal = e0 + (E * g) / n_groups;
-  int lo = 0, hi = n_targets;  // answer in [lo, hi]
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if ((int64_t)row_ptr[mid] >= goal) hi = mid;
-    else lo = mid + 1;
-  }
-  return lo;
-}
-
 // Groups of XCD x: the contiguous range [xcd_first(x), xcd_first(x + 1)).
 __host__ __device__ inline int xcd_first(int x, int n_groups) {
   const int per = n_groups / 8, rem = n_groups % 8;
   return x * per + (x < rem ? x : rem);
-}
-
-// Schedule of the fused kernel, one block per XCD range of groups: the
-// group starts, then the range's groups ordered by their number of edge
-// chunks, most first (stable), so that the hardware, which hands the
-// workgroups of an XCD to its compute units in launch order, starts the
-// long groups first and the makespan stays close to the mean.  The chunk
-// count repeats the fused kernel's chunking: at most chunk_m edges and
-// kSlots consecutive targets per chunk.
-constexpr int kOrderBuckets = 32;  // chunk counts above 31 share the top bucket
-__global__ void __launch_bounds__(256) attn_order_kernel(const int32_t* __restrict__ row_ptr, int n_targets,
-                                                         int n_groups, int chunk_m, int32_t* __restrict__ gs,
-                                                         int32_t* __restrict__ bucket,
-                                                         int32_t* __restrict__ order) {
-  __shared__ int hist[kOrderBuckets][257];  // [bucket][thread]: counts, then scatter positions
-  __shared__ int base[kOrderBuckets];       // first position of every bucket
-  const int t = threadIdx.x;
-  const int r0 = xcd_first(blockIdx.x, n_groups), r1 = xcd_first(blockIdx.x + 1, n_groups);
-  // thread t owns the contiguous groups [a, b) of the range
-  const int n = r1 - r0;
-  const int a = r0 + (int)(((int64_t)n * t) / 256), b = r0 + (int)(((int64_t)n * (t + 1)) / 256);
-  for (int k = 0; k < kOrderBuckets; ++k) hist[k][t] = 0;
-  for (int g = a; g < b; ++g) {
-    const int t_begin = group_start(row_ptr, n_targets, g, n_groups);
-    const int t_end = group_start(row_ptr, n_targets, g + 1, n_groups);
-    gs[g] = t_begin;
-    if (g + 1 == n_groups) gs[n_groups] = n_targets;
-    const int e_end = row_ptr[t_end];
-    int e = row_ptr[t_begin], tc = t_begin, chunks = 0;
-    while (e < e_end) {
-      while (row_ptr[tc + 1] <= e) ++tc;
-      const int t_lim = min(tc + kSlots, t_end);
-      e = min(min(e + chunk_m, e_end), row_ptr[t_lim]);
-      ++chunks;
-    }
-    const int bk = kOrderBuckets - 1 - min(chunks, kOrderBuckets - 1);  // bucket 0: most chunks
-    bucket[g] = bk;
-    ++hist[bk][t];
-  }
-  __syncthreads();
-  // exclusive prefix in (bucket, thread) order
-  if (t < kOrderBuckets) {
-    int sum = 0;
-    for (int u = 0; u < 256; ++u) {
-      const int v = hist[t][u];
-      hist[t][u] = sum;
-      sum += v;
-    }
-    base[t] = sum;
-  }
-  __syncthreads();
-  if (t == 0) {
-    int run = 0;
-    for (int k = 0; k < kOrderBuckets; ++k) {
-      const int v = base[k];
-      base[k] = run;
-      run += v;
-    }
-  }
-  __syncthreads();
-  for (int g = a; g < b; ++g) {
-    const int bk = bucket[g];
-    order[r0 + base[bk] + hist[bk][t]++] = g;
-  }
 }
 
 // Work of target t in 1/64 of a chunk, an additive estimate of the fused
@@ -1267,8 +1171,7 @@ __device__ inline int64_t target_work(int d) {
 }
 
 // Run estimate of the fused kernel's schedule (one run of consecutive
-// targets per compute unit), one workgroup of 1024 threads; used for L <= 4,
-// and for L = 5, 6 on graphs of at most kExactTargets targets.  With W the
+// targets per compute unit), one workgroup of 1024 threads.  With W the
 // total work and wsum[t] the work of targets 0..t-1, run g of n_groups
 // starts at the first target t with wsum[t] >= goal_g = floor(g W /
 // n_groups), and run n_groups at n_targets.  Runs are written from the
@@ -1281,9 +1184,9 @@ __device__ inline int64_t target_work(int d) {
 // spans of kSchedItems per thread, walking the run index along them.  With
 // one run per compute unit all runs run at once and the makespan is that of
 // the largest; at the small-molecule workload this beat equal-edge groups
-// dispatched longest first (attn_order_kernel), which larger L = 5, 6 graphs
-// keep: there whole targets (about three 32-edge chunks each) are a coarse
-// unit for one run per compute unit without the exact refinement.
+// dispatched longest first.  Above kExactTargets targets a run holds many
+// targets, so the granularity of whole targets (about three 32-edge chunks
+// each at L = 5, 6) costs little without the exact refinement.
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedItems = 8;
 
@@ -1363,7 +1266,6 @@ template <bool EXACT, int CM>
 __global__ void __launch_bounds__(kSchedThreads) attn_groups_kernel(const int32_t* __restrict__ row_ptr,
                                                                     int n_targets, int n_groups,
                                                                     int32_t* __restrict__ gs,
-                                                                    int32_t* __restrict__ order,
                                                                     int32_t* __restrict__ sched) {
   constexpr int kSpan = kSchedThreads * kSchedItems;
   __shared__ int64_t part[kSchedThreads / 64];
@@ -1412,7 +1314,6 @@ __global__ void __launch_bounds__(kSchedThreads) attn_groups_kernel(const int32_
       gs[0] = gsl[0] = 0;
       gs[n_groups] = gsl[n_groups] = n_targets;
     }
-    if (t < n_groups) order[t] = t;  // one run per compute unit: no ordering
     int g = runs_upto(a, W, n_groups);
 #pragma unroll
     for (int j = 0; j < kExactItems; ++j) {
@@ -1448,7 +1349,6 @@ __global__ void __launch_bounds__(kSchedThreads) attn_groups_kernel(const int32_
       gs[0] = 0;
       gs[n_groups] = n_targets;
     }
-    if (t < n_groups) order[t] = t;  // one run per compute unit: no ordering
 
     // pass 2: targets i0 .. i0 + kSchedItems - 1 of each thread, their work
     // staged through LDS so that the row_ptr loads stay coalesced (the LDS
@@ -1622,12 +1522,12 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
   constexpr int CM = Geo<L>::M, GL = Geo<L>::GL, MP = Geo<L>::MP;
   typedef typename XVec<Geo<L>::GCH>::type XV;
 
-  // Workgroup -> group of consecutive targets (attn_groups_kernel or
-  // attn_order_kernel chose the group starts).  Workgroups are dispatched to
+  // Workgroup -> group of consecutive targets (attn_groups_kernel and its
+  // refinement chose the group starts).  Workgroups are dispatched to
   // the 8 XCDs round robin; XCD x takes a contiguous range of groups, since
-  // neighbouring groups share neighbours in L2, in the order P.order holds.
+  // neighbouring groups share neighbours in L2.
   const int b = blockIdx.x;
-  const int grp = P.order[xcd_first(b % 8, n_groups) + b / 8];
+  const int grp = xcd_first(b % 8, n_groups) + b / 8;
   const int t_begin = P.gs[grp];
   const int t_end = P.gs[grp + 1];
 
@@ -1686,23 +1586,33 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
       S.flush_t[tid] = (t <= t_first + sl && S.rp[t - t_first + 1] <= e_stop) ? t : -1;
     }
     {
-      // GL lanes per edge row: lane hs of row r computes the row's geometry,
-      // the radial basis functions hs, hs + GL, ... and the softmax weights
-      // of heads hs, hs + GL; lane 0 of the row stores the row metadata
+      // GL lanes per edge row: lane 0 of row r computes the row's geometry
+      // (in fp64) and stores the row metadata, then lane hs of the row
+      // computes the radial basis functions hs, hs + GL, ... and the softmax
+      // weights of heads hs, hs + GL, ... from the length and envelope it
+      // reads from lane 0
       const int r = tid / GL, hs = tid % GL;
       int jr = -1;  // source atom of row r
       if (r < nrows) {
         int t, j;
-        float rv[3];
-        row_edge(P, S, e + r, t_first, t, j, rv);
+        row_edge(S, e + r, t_first, t);
+        j = P.col[e + r];
         jr = j;
-        const float rho = sqrtf(rv[0] * rv[0] + rv[1] * rv[1] + rv[2] * rv[2]);
+        float rho = 0.0f, u = 0.0f;
         if (hs == 0) {
+          const EdgeGeo geo = edge_geometry(P.pos, t, j, P.periodic, P.box, P.cutoff);
+          rho = geo.rho;
+          u = envelope_u(geo.s, geo.t, P.p);
           S.row_j[r] = j;
           S.row_slot[r] = t % kSlots;
           S.row_t[r] = t;
-          S.row_rv[r] = f32x4{rv[0], rv[1], rv[2], rho};
+          S.row_rv[r] = f32x4{geo.r[0], geo.r[1], geo.r[2], rho};
+          S.row_u[r] = u;
         }
+        // every lane of the row is in this branch, so lane 0 of it is active
+        const int src = (tid & 63) & ~(GL - 1);
+        rho = __shfl(rho, src, 64);
+        u = __shfl(u, src, 64);
         // Gaussian radial basis of this edge (centres k rc/(K-1), width rc/(K-1))
         const float step = rc / (float)(P.K - 1);
         const float inv2s2 = 1.0f / (2.0f * step * step);
@@ -1710,7 +1620,6 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
           const float dr = rho - step * (float)kk;
           sPhi[r * kMaxRbf + kk] = kk < P.K ? expf(-dr * dr * inv2s2) : 0.0f;
         }
-        const float u = envelope_u(rho / rc, P.p);
         for (int h = hs; h < H; h += GL) {
           const f32x4* qv = (const f32x4*)(P.q + (int64_t)t * kC + h * dh);
           const f32x4* kv = (const f32x4*)(P.k + (int64_t)j * kC + h * dh);
@@ -1728,6 +1637,7 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
           S.row_slot[r] = -2;  // matches no slot
           S.row_t[r] = t_first;
           S.row_rv[r] = f32x4{0.0f, 0.0f, 1.0f, 0.0f};
+          S.row_u[r] = 0.0f;
         }
         for (int kk = hs; kk < ((P.K + 7) & ~7); kk += GL) sPhi[r * kMaxRbf + kk] = 0.0f;
         for (int h = hs; h < H; h += GL) sW[h * CM + r] = 0.0f;
@@ -1801,7 +1711,7 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
             f32x4 gi = g[i];
             if (r >= nrows) gi = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             else if (P.flags & SO2_FLAG_NO_RADIAL) gi = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
-            else if (env) gi = gi * envelope_u(S.row_rv[r].w / rc, P.p);
+            else if (env) gi = gi * S.row_u[r];
             *(f32x4*)(sG + g_off(r, cq)) = gi;
           }
         }
@@ -1852,26 +1762,10 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
   }
 }
 
-// Workgroups: for L <= 4 one per compute unit, each with an equal share of
-// the estimated work; for L = 5, 6 about kEdgesPerGroup edges each, rounded
-// up to a whole number of waves of workgroups over the compute units.
-// One run per compute unit from the run estimate (and its exact refinement)
-// for L <= 4, and for L = 5, 6 when the refinement applies.
-template <int L>
-bool one_run_per_cu(int n_targets) {
-  return L <= 4 || n_targets <= kExactTargets;
-}
-
-template <int L>
-int group_count(int n_targets, int64_t n_edges, int n_cu) {
-  if (one_run_per_cu<L>(n_targets)) {
-    return std::max(1, std::min(n_cu, n_targets));
-  } else {
-    int64_t want = (n_edges + kEdgesPerGroup - 1) / kEdgesPerGroup;
-    want = ((want + n_cu - 1) / n_cu) * n_cu;
-    return (int)std::max<int64_t>(1, std::min<int64_t>(want, n_targets));
-  }
-}
+// One workgroup per compute unit, each with a run of consecutive targets
+// holding an equal share of the estimated work (attn_groups_kernel, with the
+// exact refinement on graphs of at most kExactTargets targets).
+int group_count(int n_targets, int n_cu) { return std::max(1, std::min(n_cu, n_targets)); }
 
 so2_status device_cu_count(int* n_cu) {
   int dev = 0;
@@ -1881,52 +1775,43 @@ so2_status device_cu_count(int* n_cu) {
   return SO2_OK;
 }
 
-// The run starts (and the order of the groups) for the fused kernel.
+// The run starts of the fused kernel.
 template <int L>
-so2_status schedule_L(const MfmaParams& P, int32_t* bucket, int32_t* sched, int64_t n_edges, hipStream_t stream) {
+so2_status schedule_L(const MfmaParams& P, int32_t* next, int32_t* sched, hipStream_t stream) {
   int n_cu = 256;
   const so2_status st = device_cu_count(&n_cu);
   if (st != SO2_OK) return st;
-  const int n_groups = group_count<L>(P.n_targets, n_edges, n_cu);
-  if (one_run_per_cu<L>(P.n_targets)) {
-    const bool exact = P.n_targets <= kExactTargets && n_groups <= kExactRuns;
-    if (exact) {
-      constexpr int CM = Geo<L>::M;
-      const size_t lds1 = sizeof(int) * ((size_t)P.n_targets + 1);
-      SO2_CHECK(hipFuncSetAttribute((const void*)(attn_groups_kernel<true, CM>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)(sizeof(int) * (kExactTargets + 1))));
-      hipLaunchKernelGGL((attn_groups_kernel<true, CM>), dim3(1), dim3(kSchedThreads), lds1, stream, P.row_ptr,
-                         P.n_targets, n_groups, const_cast<int32_t*>(P.gs), const_cast<int32_t*>(P.order), sched);
-      SO2_CHECK_LAUNCH();
-      hipLaunchKernelGGL(attn_runs_next_kernel<CM>, dim3((P.n_targets + kSchedThreads) / kSchedThreads),
-                         dim3(kSchedThreads), lds1, stream, P.row_ptr, P.n_targets, (const int32_t*)sched, bucket);
-      SO2_CHECK_LAUNCH();
-      SO2_CHECK(hipFuncSetAttribute((const void*)attn_runs_chain_kernel,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)(3 * sizeof(int) * (kExactTargets + 1))));
-      hipLaunchKernelGGL(attn_runs_chain_kernel, dim3(1), dim3(kSchedThreads), 3 * lds1, stream,
-                         (const int32_t*)bucket, P.n_targets, n_groups, (const int32_t*)sched,
-                         const_cast<int32_t*>(P.gs));
-    } else {
-      hipLaunchKernelGGL((attn_groups_kernel<false, Geo<L>::M>), dim3(1), dim3(kSchedThreads), 0, stream,
-                         P.row_ptr, P.n_targets, n_groups, const_cast<int32_t*>(P.gs),
-                         const_cast<int32_t*>(P.order), sched);
-    }
+  const int n_groups = group_count(P.n_targets, n_cu);
+  constexpr int CM = Geo<L>::M;
+  const bool exact = P.n_targets <= kExactTargets && n_groups <= kExactRuns;
+  if (exact) {
+    const size_t lds1 = sizeof(int) * ((size_t)P.n_targets + 1);
+    SO2_CHECK(hipFuncSetAttribute((const void*)(attn_groups_kernel<true, CM>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)(sizeof(int) * (kExactTargets + 1))));
+    hipLaunchKernelGGL((attn_groups_kernel<true, CM>), dim3(1), dim3(kSchedThreads), lds1, stream, P.row_ptr,
+                       P.n_targets, n_groups, const_cast<int32_t*>(P.gs), sched);
+    SO2_CHECK_LAUNCH();
+    hipLaunchKernelGGL(attn_runs_next_kernel<CM>, dim3((P.n_targets + kSchedThreads) / kSchedThreads),
+                       dim3(kSchedThreads), lds1, stream, P.row_ptr, P.n_targets, (const int32_t*)sched, next);
+    SO2_CHECK_LAUNCH();
+    SO2_CHECK(hipFuncSetAttribute((const void*)attn_runs_chain_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)(3 * sizeof(int) * (kExactTargets + 1))));
+    hipLaunchKernelGGL(attn_runs_chain_kernel, dim3(1), dim3(kSchedThreads), 3 * lds1, stream, (const int32_t*)next,
+                       P.n_targets, n_groups, (const int32_t*)sched, const_cast<int32_t*>(P.gs));
   } else {
-    hipLaunchKernelGGL(attn_order_kernel, dim3(8), dim3(256), 0, stream, P.row_ptr, P.n_targets, n_groups,
-                       Geo<L>::M, const_cast<int32_t*>(P.gs), bucket, const_cast<int32_t*>(P.order));
+    hipLaunchKernelGGL((attn_groups_kernel<false, CM>), dim3(1), dim3(kSchedThreads), 0, stream, P.row_ptr,
+                       P.n_targets, n_groups, const_cast<int32_t*>(P.gs), sched);
   }
   SO2_CHECK_LAUNCH();
   return SO2_OK;
 }
 
 template <int L>
-so2_status launch_L(const MfmaParams& P, int64_t n_edges, hipStream_t stream) {
+so2_status launch_L(const MfmaParams& P, hipStream_t stream) {
   int n_cu = 256;
   const so2_status st = device_cu_count(&n_cu);
   if (st != SO2_OK) return st;
-  const int n_groups = group_count<L>(P.n_targets, n_edges, n_cu);
+  const int n_groups = group_count(P.n_targets, n_cu);
   const size_t smem = Lds<L>::kTotal;
   static_assert(Lds<L>::kTotal <= 160 * 1024, "LDS budget");
   SO2_CHECK(hipFuncSetAttribute((const void*)attn_mfma_kernel<L>,
@@ -1939,7 +1824,7 @@ so2_status launch_L(const MfmaParams& P, int64_t n_edges, hipStream_t stream) {
 // Workspace of the MFMA path: softmax statistics, the x pairs, w_rad in
 // fp32 and w_so2 in fragment order.
 struct ScratchLayout {
-  size_t stats, xp, wrad, wf, gs, bucket, order, sched, total;
+  size_t stats, xp, wrad, wf, gs, next, sched, total;
 };
 
 size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -1952,9 +1837,8 @@ ScratchLayout scratch_layout(int n_atoms, int n_targets, int L, int H, int K) {
   s.wf = s.wrad + up256(sizeof(float) * (size_t)K * kC);
   s.gs = s.wf + up256(sizeof(uint16_t) * (size_t)wf_entries(L));
   // at most n_targets groups
-  s.bucket = s.gs + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
-  s.order = s.bucket + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
-  s.sched = s.order + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
+  s.next = s.gs + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
+  s.sched = s.next + up256(sizeof(int32_t) * ((size_t)n_targets + 1));
   s.total = s.sched + 256;
   return s;
 }
@@ -1970,7 +1854,6 @@ MfmaParams make_params(const AttnArgs& a) {
   P.wrad = (const float*)(base + s.wrad);
   P.wf = (const uint16_t*)(base + s.wf);
   P.gs = (const int32_t*)(base + s.gs);
-  P.order = (const int32_t*)(base + s.order);
   P.q = a.q;
   P.k = a.k;
   float* stats = (float*)(base + s.stats);
@@ -2003,12 +1886,16 @@ so2_status launch_pack_L(const AttnArgs& a, const MfmaParams& P, hipStream_t str
 
 }  // namespace
 
-bool mfma_supported(int L, int C, int H, int K, int n_atoms) {
-  // the x pairs are addressed through a 32-bit buffer descriptor, with room
-  // past the end for the zero reads of rows without an edge
-  const uint64_t xp_bytes = (uint64_t)n_atoms * pair_off(L + 1) * C * 4;
-  return C == kC && L >= 1 && L <= 6 && H >= 1 && H <= kMaxHeads && C % H == 0 && K <= kMaxRbf &&
-         xp_bytes < 0xffff0000ull;
+bool mfma_shape(int L, int C, int H, int K) {
+  return C == kC && L >= 1 && L <= 6 && H >= 1 && H <= kMaxHeads && C % H == 0 && K <= kMaxRbf;
+}
+
+// The x pairs are addressed through a 32-bit buffer descriptor, with room
+// past the end for the zero reads of rows without an edge: 4 (L+1)(L+2)/2 C
+// bytes per atom below 2^32 - 2^16 (about 559k atoms at L = 4, 299k at L = 6).
+bool mfma_fits(int L, int n_atoms) {
+  const uint64_t xp_bytes = (uint64_t)n_atoms * pair_off(L + 1) * kC * 4;
+  return xp_bytes < 0xffff0000ull;
 }
 
 bool mfma_aligned(const AttnArgs& a) {
@@ -2023,70 +1910,35 @@ namespace {
 
 so2_status launch_schedule(const AttnArgs& a, const MfmaParams& P, hipStream_t stream) {
   const ScratchLayout s = scratch_layout(a.n_atoms, a.n_targets, a.L, a.H, a.K);
-  int32_t* bucket = (int32_t*)((char*)a.scratch + s.bucket);
+  int32_t* next = (int32_t*)((char*)a.scratch + s.next);
   int32_t* sched = (int32_t*)((char*)a.scratch + s.sched);
   switch (a.L) {
     case 1:
-      return schedule_L<1>(P, bucket, sched, a.n_edges, stream);
+      return schedule_L<1>(P, next, sched, stream);
     case 2:
-      return schedule_L<2>(P, bucket, sched, a.n_edges, stream);
+      return schedule_L<2>(P, next, sched, stream);
     case 3:
-      return schedule_L<3>(P, bucket, sched, a.n_edges, stream);
+      return schedule_L<3>(P, next, sched, stream);
     case 4:
-      return schedule_L<4>(P, bucket, sched, a.n_edges, stream);
+      return schedule_L<4>(P, next, sched, stream);
     case 5:
-      return schedule_L<5>(P, bucket, sched, a.n_edges, stream);
+      return schedule_L<5>(P, next, sched, stream);
     case 6:
-      return schedule_L<6>(P, bucket, sched, a.n_edges, stream);
+      return schedule_L<6>(P, next, sched, stream);
   }
   return SO2_ERR_UNSUPPORTED;
 }
 
-// A second stream (default priority, non-blocking) and a fork and a join
-// event, per host thread and device, created on first use and kept until the
-// process ends.  Per thread, so that calls from different host threads never
-// share an event.
-struct SideStream {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-constexpr int kMaxDevices = 64;
-
-so2_status side_stream(SideStream** out) {
-  static thread_local SideStream per_device[kMaxDevices];
-  int dev = 0;
-  SO2_CHECK(hipGetDevice(&dev));
-  if (dev < 0 || dev >= kMaxDevices) return SO2_ERR_UNSUPPORTED;
-  SideStream& ss = per_device[dev];
-  if (!ss.join) {
-    if (!ss.stream) SO2_CHECK(hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking));
-    if (!ss.fork) SO2_CHECK(hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming));
-    SO2_CHECK(hipEventCreateWithFlags(&ss.join, hipEventDisableTiming));
-  }
-  *out = &ss;
-  return SO2_OK;
-}
-
 }  // namespace
 
-// The run schedule reads only row_ptr, so it runs on a side stream beside the
-// repack and the statistics (which fill the device, while the schedule
-// kernels use one or a few workgroups); the caller's stream waits for it
-// before the fused kernel.  Without a side stream it runs in line.
+// Prologue of the fused kernel, in order on the caller's stream: the run
+// schedule (reads only row_ptr), the repack of x and the weights, and the
+// softmax statistics.
 so2_status launch_attention_mfma_prep(const AttnArgs& a, hipStream_t stream) {
   const MfmaParams P = make_params(a);
-  SideStream* side = nullptr;
   if (a.n_targets > 0) {
-    if (side_stream(&side) == SO2_OK) {
-      SO2_CHECK(hipEventRecord(side->fork, stream));
-      SO2_CHECK(hipStreamWaitEvent(side->stream, side->fork, 0));
-      const so2_status st = launch_schedule(a, P, side->stream);
-      if (st != SO2_OK) return st;
-      SO2_CHECK(hipEventRecord(side->join, side->stream));
-    } else {
-      const so2_status st = launch_schedule(a, P, stream);
-      if (st != SO2_OK) return st;
-    }
+    const so2_status st = launch_schedule(a, P, stream);
+    if (st != SO2_OK) return st;
   }
   so2_status st = SO2_OK;
   switch (a.L) {
@@ -2115,7 +1967,6 @@ so2_status launch_attention_mfma_prep(const AttnArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(attn_stats_kernel, dim3((a.n_targets + 3) / 4), dim3(256), 0, stream, P, kC);
     SO2_CHECK_LAUNCH();
   }
-  if (side) SO2_CHECK(hipStreamWaitEvent(stream, side->join, 0));
   return st;
 }
 
@@ -2124,17 +1975,17 @@ so2_status launch_attention_mfma(const AttnArgs& a, hipStream_t stream) {
   const MfmaParams P = make_params(a);
   switch (a.L) {
     case 1:
-      return launch_L<1>(P, a.n_edges, stream);
+      return launch_L<1>(P, stream);
     case 2:
-      return launch_L<2>(P, a.n_edges, stream);
+      return launch_L<2>(P, stream);
     case 3:
-      return launch_L<3>(P, a.n_edges, stream);
+      return launch_L<3>(P, stream);
     case 4:
-      return launch_L<4>(P, a.n_edges, stream);
+      return launch_L<4>(P, stream);
     case 5:
-      return launch_L<5>(P, a.n_edges, stream);
+      return launch_L<5>(P, stream);
     case 6:
-      return launch_L<6>(P, a.n_edges, stream);
+      return launch_L<6>(P, stream);
   }
   return SO2_ERR_UNSUPPORTED;
 }

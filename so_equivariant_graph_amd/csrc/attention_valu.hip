@@ -73,15 +73,6 @@ __device__ inline float block_reduce_sum(float v, float* red) {
   return r;
 }
 
-__device__ inline void edge_vector(const ValuParams& P, int i, int j, float* r) {
-#pragma unroll
-  for (int d = 0; d < 3; ++d) {
-    float v = P.pos[3 * (int64_t)j + d] - P.pos[3 * (int64_t)i + d];
-    if (P.periodic) v = v - P.box[d] * rintf(v / P.box[d]);
-    r[d] = v;
-  }
-}
-
 template <typename T>
 __global__ void __launch_bounds__(kValuThreads) attn_valu_kernel(ValuParams P) {
   const int i = blockIdx.x;
@@ -120,10 +111,8 @@ __global__ void __launch_bounds__(kValuThreads) attn_valu_kernel(ValuParams P) {
     float m = -INFINITY, s = 0.0f;
     for (int e = e0 + t; e < e1; e += kValuThreads) {
       int j = P.col[e];
-      float r[3];
-      edge_vector(P, i, j, r);
-      float rho = sqrtf(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
-      float u = envelope_u(rho / rc, P.p);
+      const EdgeGeo geo = edge_geometry(P.pos, i, j, P.periodic, P.box, rc);
+      float u = envelope_u(geo.s, geo.t, P.p);
       float z = 0.0f;
       for (int c = h * d; c < (h + 1) * d; ++c) z += s_q[c] * P.k[(int64_t)j * C + c];
       z *= inv_sqrt_d;
@@ -148,13 +137,12 @@ __global__ void __launch_bounds__(kValuThreads) attn_valu_kernel(ValuParams P) {
   for (int e = e0; e < e1; ++e) {
     const int j = P.col[e];
     if (t == 0) {
-      float r[3];
-      edge_vector(P, i, j, r);
-      float rho = sqrtf(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
+      const EdgeGeo geo = edge_geometry(P.pos, i, j, P.periodic, P.box, rc);
+      const float rho = geo.rho;
       float inv = rho > 0.0f ? 1.0f / rho : 0.0f;
       s_geo[0] = rho;
-      s_geo[1] = envelope_u(rho / rc, P.p);
-      edge_frame(r[0] * inv, r[1] * inv, r[2] * inv, s_geo + 4);
+      s_geo[1] = envelope_u(geo.s, geo.t, P.p);
+      edge_frame(geo.r[0] * inv, geo.r[1] * inv, geo.r[2] * inv, s_geo + 4);
     }
     __syncthreads();
     // Wigner-D: degree 0 and 1 directly, then one degree at a time.

@@ -69,16 +69,51 @@ __device__ inline float load_as_float<uint16_t>(const uint16_t* p, int64_t i) {
 // Envelope u(s) = 1 - (p+1)(p+2)/2 s^p + p(p+2) s^(p+1) - p(p+1)/2 s^(p+2)
 // for s < 1, else 0 (smooth radius cutoff inside attention: "EquiformerV3:
 // Scaling Efficient, Expressive, and General SE(3)-Equivariant Graph Attention
-// Transformers",
-// technical summary, section 2.B.3).
-__device__ inline float envelope_u(float s, int p) {
-  if (!(s < 1.0f)) return 0.0f;
-  float sp = 1.0f;
-  for (int k = 0; k < p; ++k) sp *= s;
-  const float a = 0.5f * (float)((p + 1) * (p + 2));
-  const float b = (float)(p * (p + 2));
-  const float c = 0.5f * (float)(p * (p + 1));
-  return 1.0f + sp * (-a + s * (b - c * s));
+// Transformers", technical summary, section 2.B.3).  u(1) = u'(1) = u''(1) =
+// 0, so u = (1 - s)^3 Q(s) with Q(s) = sum_{k<p} (k+1)(k+2)/2 s^k (the degree
+// p-1 truncation of 1/(1-s)^3), a sum of positive terms: evaluated in that
+// form from t = 1 - s it keeps its relative precision up to the cutoff,
+// where the expanded sum cancels.  Arguments: s and t = 1 - s (t computed in
+// fp64 by edge_geometry, since 1 - s formed in fp32 from an fp32 length loses
+// the digits that decide u near the cutoff).
+__host__ __device__ inline float envelope_u(float s, float t, int p) {
+  if (!(t > 0.0f)) return 0.0f;
+  float q = 0.0f;
+  for (int k = p - 1; k >= 0; --k) q = q * s + 0.5f * (float)((k + 1) * (k + 2));
+  return t * t * t * q;
+}
+
+// Geometry of edge (i -> j) from fp32 positions, in fp64: r = p_j - p_i
+// (exact in fp64), with a box the minimum image r - b rint(r / b) (the
+// operation sequence of the neighbour test, no contraction), |r| and
+// t = 1 - |r| / rc.  r and |r| are returned in fp32.
+struct EdgeGeo {
+  float r[3];
+  float rho;
+  float s;  // |r| / rc
+  float t;  // 1 - |r| / rc, from the fp64 length
+};
+
+__host__ __device__ inline EdgeGeo edge_geometry(const float* pos, int i, int j, int periodic, const float* box,
+                                                 float cutoff) {
+#pragma clang fp contract(off)
+  EdgeGeo g;
+  double r2 = 0.0;
+  for (int d = 0; d < 3; ++d) {
+    double v = (double)pos[3 * (int64_t)j + d] - (double)pos[3 * (int64_t)i + d];
+    if (periodic) {
+      const double b = (double)box[d];
+      v = v - b * rint(v / b);
+    }
+    r2 = r2 + v * v;
+    g.r[d] = (float)v;
+  }
+  const double rho = sqrt(r2);
+  const double rc = (double)cutoff;
+  g.rho = (float)rho;
+  g.s = (float)(rho / rc);
+  g.t = (float)((rc - rho) / rc);
+  return g;
 }
 
 }  // namespace so2

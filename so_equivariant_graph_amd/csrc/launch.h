@@ -43,7 +43,6 @@ struct AttnArgs {
   void* scratch;  // kernel-specific workspace area
   size_t scratch_bytes;
   int32_t n_atoms, n_targets, L, C, H, K, p;
-  int64_t n_edges;  // edges of the target rows (from the descriptor)
   float cutoff;
   uint32_t flags;
   int32_t dtype;
@@ -59,14 +58,16 @@ bool valu_supported(int L, int C, int H);
 size_t valu_scratch_bytes(int L, int C);
 so2_status launch_attention_valu(const AttnArgs& a, hipStream_t stream);
 
-// bf16 MFMA kernel (attention_mfma.hip): C = 128, 1 <= L <= 6, H <= 16, K <= 32.
-// x, w_rad and w_so2 must be 16-byte aligned.
-bool mfma_supported(int L, int C, int H, int K, int n_atoms);
+// bf16 MFMA kernel (attention_mfma.hip): C = 128, 1 <= L <= 6, H <= 16, K <= 32
+// (mfma_shape), up to the atom count its 32-bit buffer addressing covers
+// (mfma_fits).  x, w_rad and w_so2 must be 16-byte aligned.
+bool mfma_shape(int L, int C, int H, int K);
+bool mfma_fits(int L, int n_atoms);
 bool mfma_aligned(const AttnArgs& a);
 size_t mfma_scratch_bytes(int n_atoms, int n_targets, int L, int H, int K);
 // prologue (x repacked as component pairs, w_rad in fp32, w_so2 in fragment
-// order), softmax statistics and the run schedule; then the fused kernel
-// alone
+// order), softmax statistics and the run schedule, all on `stream`; then the
+// fused kernel alone
 so2_status launch_attention_mfma_prep(const AttnArgs& a, hipStream_t stream);
 so2_status launch_attention_mfma(const AttnArgs& a, hipStream_t stream);
 

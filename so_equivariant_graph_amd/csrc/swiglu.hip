@@ -429,9 +429,9 @@ size_t swiglu_s2_workspace_bytes(int n_atoms, int L, int C, int dtype) {
   return sw_layout(n_atoms, L, C).total;
 }
 
-so2_status launch_swiglu_s2(const void* x, const void* w_a, const void* w_b, const void* w_g, const void* w_o,
-                            float* y, int n_atoms, int L, int C, int dtype, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+so2_status launch_swiglu_s2(uint32_t stages, const void* x, const void* w_a, const void* w_b, const void* w_g,
+                            const void* w_o, float* y, int n_atoms, int L, int C, int dtype, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
   if (n_atoms == 0) return SO2_OK;
   const SwLayout lay = sw_layout(n_atoms, L, C);
   if (!workspace || workspace_bytes < lay.total || !aligned16(workspace)) return SO2_ERR_WORKSPACE;
@@ -444,7 +444,8 @@ so2_status launch_swiglu_s2(const void* x, const void* w_a, const void* w_b, con
   const int64_t stride = (int64_t)nc * C;
   const bool mfma = dtype == SO2_BF16 && C == 128 && aligned16(x) && aligned16(w_a) && aligned16(w_b) &&
                     aligned16(w_g) && aligned16(w_o);
-  if (mfma) {
+  if (!(stages & SO2_STAGE_SW_MAPS)) {
+  } else if (mfma) {
     const unsigned nb = (unsigned)((n_atoms + kLinNodes - 1) / kLinNodes);
     hipLaunchKernelGGL((lin_mfma_kernel<2, uint16_t>), dim3(nb, L + 1), dim3(256), 0, stream, (const uint16_t*)x,
                        stride, (const uint16_t*)w_a, (const uint16_t*)w_b, (uint16_t*)u, (uint16_t*)v, stride,
@@ -463,9 +464,8 @@ so2_status launch_swiglu_s2(const void* x, const void* w_a, const void* w_b, con
     lin_launch((const float*)x, stride, (const float*)w_g, g, (int64_t)C, n_atoms, 1, C, stream);
     SO2_CHECK_LAUNCH();
   }
-  if (ev_start && ev_stop) SO2_CHECK(hipEventRecord(ev_start, stream));
-  so2_status st = SO2_ERR_UNSUPPORTED;
-  switch (L) {
+  so2_status st = (stages & SO2_STAGE_SW_GRID) ? SO2_ERR_UNSUPPORTED : SO2_OK;
+  if (stages & SO2_STAGE_SW_GRID) switch (L) {
     case 0:
       st = launch_s2<0>(u, v, g, s, mfma, n_atoms, C, stream);
       break;
@@ -489,8 +489,8 @@ so2_status launch_swiglu_s2(const void* x, const void* w_a, const void* w_b, con
       break;
   }
   if (st != SO2_OK) return st;
-  if (ev_start && ev_stop) SO2_CHECK(hipEventRecord(ev_stop, stream));
-  if (mfma) {
+  if (!(stages & SO2_STAGE_SW_OUT)) {
+  } else if (mfma) {
     const unsigned nb = (unsigned)((n_atoms + kLinNodes - 1) / kLinNodes);
     hipLaunchKernelGGL((lin_mfma_kernel<1, float>), dim3(nb, L + 1), dim3(256), 0, stream, (const uint16_t*)s,
                        stride, (const uint16_t*)w_o, (const uint16_t*)w_o, y, y, stride, n_atoms);

@@ -90,16 +90,17 @@ def test_edge_frame_rejects_bad_input():
 
 
 def _desc(**kw):
-    base = dict(n_atoms=10, n_targets=10, n_edges=40, l_max=2, channels=16, heads=2, n_rbf=8,
+    base = dict(n_atoms=10, n_targets=10, l_max=2, channels=16, heads=2, n_rbf=8,
                 envelope_p=5, cutoff=5.0, flags=0, dtype=sea.SO2_FP32)
     base.update(kw)
     return sea.make_desc(**base)
 
 
-def _fwd(desc, box=None, ws_bytes=None, null=()):
+def _fwd(desc, box=None, ws_bytes=None, null=(), stages=None, ptr=None):
     lib = sea.load_library()
     names = ["pos", "box", "row_ptr", "col", "x", "w_q", "w_k", "w_rad", "w_so2", "y", "ws"]
     keep, box_p = sea._host_box(box)
+    ptr = ptr or {}
     args = []
     for name in names:
         if name == "box":
@@ -107,9 +108,11 @@ def _fwd(desc, box=None, ws_bytes=None, null=()):
         elif name in null:
             args.append(ctypes.c_void_p(0))
         else:
-            args.append(FAKE)
+            args.append(ptr.get(name, FAKE))
     wsb = 0 if ws_bytes is None else ws_bytes
-    return lib.so2_attention_fwd(ctypes.byref(desc), *args, wsb, ctypes.c_void_p(0))
+    if stages is None:
+        return lib.so2_attention_fwd(ctypes.byref(desc), *args, wsb, ctypes.c_void_p(0))
+    return lib.so2_attention_fwd_stages(stages, ctypes.byref(desc), *args, wsb, ctypes.c_void_p(0))
 
 
 @pytest.mark.parametrize(
@@ -149,6 +152,39 @@ def test_attention_pointer_box_and_workspace_errors():
     assert lib.so2_attention_fwd(ctypes.byref(d), *args, need, ctypes.c_void_p(0)) == sea.SO2_ERR_WORKSPACE
 
 
+def test_attention_stage_errors():
+    d = _desc()
+    need = sea.attention_workspace_bytes(d)
+    assert _fwd(d, ws_bytes=need, stages=0) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert _fwd(d, ws_bytes=need, stages=4) == sea.SO2_ERR_INVALID_ARGUMENT
+    # y is not needed by the prologue alone, but by every call with the fused stage
+    assert _fwd(d, ws_bytes=need, stages=sea.STAGE_FUSED, null=("y",)) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert _fwd(d, ws_bytes=need, stages=sea.STAGE_PREPARE, null=("x",)) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert _fwd(d, ws_bytes=need - 1, stages=sea.STAGE_PREPARE, null=("y",)) == sea.SO2_ERR_WORKSPACE
+
+
+def test_mfma_inputs_must_be_16_byte_aligned():
+    d = _desc(l_max=4, channels=128, heads=8, n_rbf=16, dtype=sea.SO2_BF16)
+    need = sea.attention_workspace_bytes(d)
+    assert need > 0
+    odd = ctypes.c_void_p((1 << 30) + 8)
+    for name in ("x", "w_rad", "w_so2"):
+        assert _fwd(d, ws_bytes=need, ptr={name: odd}) == sea.SO2_ERR_INVALID_ARGUMENT, name
+
+
+def test_mfma_shape_past_its_atom_limit_is_unsupported():
+    # 32-bit offsets into the repacked x: (2^32 - 2^16) / (2 (L+1)(L+2) C) atoms
+    for L in (4, 6):
+        limit = (2**32 - 2**16 - 1) // (2 * (L + 1) * (L + 2) * 128)
+        ok = _desc(n_atoms=limit, n_targets=16, l_max=L, channels=128, heads=8, n_rbf=16, dtype=sea.SO2_BF16)
+        assert sea.attention_kernel_kind(ok) == sea.KERNEL_MFMA
+        big = _desc(n_atoms=limit + 1, n_targets=16, l_max=L, channels=128, heads=8, n_rbf=16, dtype=sea.SO2_BF16)
+        assert sea.attention_kernel_kind(big) == sea.KERNEL_NONE
+        assert sea.attention_workspace_bytes(big) == 0
+        assert _fwd(big, ws_bytes=1 << 40) == sea.SO2_ERR_UNSUPPORTED
+    assert 559_000 < (2**32 - 2**16 - 1) // (2 * 5 * 6 * 128) < 560_000
+
+
 def test_kernel_kind_selection():
     assert sea.attention_kernel_kind(_desc()) == sea.KERNEL_VALU
     assert sea.attention_kernel_kind(_desc(l_max=7)) == sea.KERNEL_NONE
@@ -180,6 +216,10 @@ def test_swiglu_errors_before_launch():
 
     def call(n, L, C, dt, ptrs=(FAKE,) * 6, ws=None, ws_bytes=0):
         return lib.so2_swiglu_s2(*ptrs, n, L, C, dt, ws, ws_bytes, None)
+
+    for stages in (0, 8, 9):
+        assert lib.so2_swiglu_s2_stages(stages, *(FAKE,) * 6, 4, 2, 8, sea.SO2_FP32, FAKE, 1 << 30, None) == \
+            sea.SO2_ERR_INVALID_ARGUMENT
 
     for i in range(6):  # x, w_a, w_b, w_g, w_o, y
         ptrs = [FAKE] * 6

@@ -3,8 +3,11 @@ the fp64 oracle, element by element.
 
 * tiny_fp32: every atom, max relative error (normalised per atom) <= 1e-4;
 * bf16 workloads: a small batch of the same kind (several kernel tiles and a
-  ragged tail) on every atom, and the full-size workloads on seeded sampled
-  targets, at <= 2e-2 (the oracle gets the same bf16-rounded inputs);
+  ragged tail) on every atom at <= 2e-2 (the oracle gets the same
+  bf16-rounded inputs); the full-size workloads are in
+  test_gpu_x_full_parity.py;
+* edges just inside the cutoff, where the envelope is a few 1e-9 and
+  decides the softmax;
 * edge cases: empty neighbourhoods, n_targets < n_atoms, L = 0 and L = 6,
   odd channel counts, both flags;
 * GPU-side invariants: softmax weights summing to one, rotation
@@ -63,38 +66,6 @@ def test_small_molecules_batch_every_atom_bf16():
     err = max_rel_error(y, y_ref)
     say("max rel err", err)
     assert err <= TOL["bf16"]
-
-
-def _sampled(name, n_samples, seed=0):
-    import torch
-
-    import so_equivariant_graph_amd as sea
-
-    say("attention full-size sampled", name)
-    w = make_workload(name)
-    d = device_inputs(w)
-    rp_d, col_d = sea.build_neighbors(d["pos"], w.cutoff, box=w.box, mol_id=d["mol"])
-    y = gpu_attention(w, d, rp_d, col_d)
-    torch.cuda.synchronize()
-    rp, col = rp_d.cpu().numpy(), col_d.cpu().numpy()
-    # the oracle's own rows for the sampled targets decide the neighbour set
-    t = np.sort(np.random.default_rng(seed).choice(w.n_atoms, size=n_samples, replace=False))
-    t = np.unique(np.concatenate([t, [0, w.n_atoms - 1]]))
-    ref_rows = neighbors_bruteforce(w.pos, w.cutoff, w.box, w.mol_id, rows=t)
-    for i, r in zip(t, ref_rows):
-        assert np.array_equal(col[rp[i] : rp[i + 1]], r)
-    y_ref = oracle_attention(w, rp, col, targets=t)
-    err = max_rel_error(y[t].cpu().numpy(), y_ref)
-    say("max rel err", err, "targets", len(t))
-    assert np.all(np.isfinite(y.cpu().numpy()))
-    return err
-
-
-@pytest.mark.parametrize(
-    "name,n", [("small_molecules", 24), ("water_l6", 10), ("solvated_protein", 16), ("water_100k", 16)]
-)
-def test_full_size_sampled_targets_bf16(name, n):
-    assert _sampled(name, n) <= TOL["bf16"]
 
 
 def test_empty_neighbourhood_and_partial_targets():
@@ -202,10 +173,10 @@ def test_repeated_calls_are_bitwise_identical():
 # ---------------------------------------------------------------- bf16 MFMA kernel
 
 
-def _kind(w, n_edges=1000):
+def _kind(w):
     import so_equivariant_graph_amd as sea
 
-    d = sea.make_desc(n_atoms=w.n_atoms, n_targets=w.n_atoms, n_edges=n_edges, l_max=w.l_max,
+    d = sea.make_desc(n_atoms=w.n_atoms, n_targets=w.n_atoms, l_max=w.l_max,
                       channels=w.channels, heads=w.heads, n_rbf=w.n_rbf, envelope_p=w.envelope_p,
                       cutoff=w.cutoff, flags=0, dtype=sea.SO2_BF16 if w.dtype == "bf16" else sea.SO2_FP32)
     return sea.attention_kernel_kind(d)
@@ -299,26 +270,6 @@ def test_mfma_ragged_degrees_and_split_targets(L):
     assert max_rel_error(y_part.cpu().numpy(), y_ref[:nt]) <= TOL["bf16"]
 
 
-def test_mfma_every_target_row_written_small_molecules():
-    """At the full small-molecule size the runs of targets come from the
-    exact chunk-count refinement (a chunk cap one below the estimate's
-    largest run): every target row must still be written (rows start as NaN)."""
-    say("mfma run schedule covers every target, small_molecules")
-    import torch
-
-    import so_equivariant_graph_amd as sea
-
-    w = make_workload("small_molecules")
-    d = device_inputs(w)
-    rp_d, col_d = sea.build_neighbors(d["pos"], w.cutoff, box=w.box, mol_id=d["mol"])
-    y = torch.full((w.n_atoms, (w.l_max + 1) ** 2, w.x.shape[2]), float("nan"), device="cuda")
-    gpu_attention(w, d, rp_d, col_d, out=y)
-    torch.cuda.synchronize()
-    assert bool(torch.isfinite(y).all())
-    deg = torch.diff(rp_d).cpu().numpy()
-    assert np.all(y[torch.from_numpy(deg == 0).cuda()].cpu().numpy() == 0.0)
-
-
 def test_mfma_hub_target_keeps_estimated_runs():
     """One target with 250 neighbours (4 chunks of 64 edges) among
     300 targets of degree 19: the chunk cap one below the largest estimated
@@ -392,3 +343,64 @@ def test_mfma_exact_schedule_with_isolated_targets():
     err_ref = max_rel_error(y[t], oracle_attention(w, rp, col, targets=t))
     say("vs fp32 kernel", err_all, "vs oracle", err_ref)
     assert err_all <= TOL["bf16"] and err_ref <= TOL["bf16"]
+
+
+def _near_cutoff_system(L, C, H, K, dtype, seed=5):
+    """Groups far apart: in each, a target with one or two neighbours at
+    distance rc (1 - delta), delta in [1e-5, 1e-3] (the pair of neighbours on
+    opposite sides, 2 rc apart), so every atom of a group sees only edges
+    whose envelope is 1e-15..1e-7; plus a small uniform cluster of ordinary
+    atoms, so that chunks mix both kinds of edges."""
+    from synth import to_bf16_exact
+
+    w = make_workload("tiny_fp32", l_max=L, channels=C, heads=H, n_rbf=K, dtype=dtype)
+    rng = np.random.default_rng(seed)
+    rc = w.cutoff
+    pos = [w.pos[:24].astype(np.float64)]
+    deltas = np.geomspace(1e-5, 1e-3, 12)
+    for g, delta in enumerate(deltas):
+        # group centres 16 A apart (> 3 rc: atoms of different groups are more
+        # than rc apart), coordinates
+        # below 80 A so that fp32 positions move a distance by < 1e-5 A
+        c = np.array([30.0 + 16.0 * (g % 3), 16.0 * ((g // 3) % 2), 16.0 * (g // 6)])
+        u = rng.standard_normal(3)
+        u /= np.linalg.norm(u)
+        r = rc * (1.0 - delta)
+        group = [c, c + r * u]
+        if g % 2 == 0:
+            group.append(c - r * u)
+        pos.append(np.array(group))
+    w.pos = np.vstack(pos).astype(np.float32)
+    n = w.pos.shape[0]
+    w.x = rng.standard_normal((n, (L + 1) ** 2, C)).astype(np.float32)
+    if dtype == "bf16":
+        w.x = to_bf16_exact(w.x)
+    return w, deltas
+
+
+@pytest.mark.parametrize("L,C,H,K,dtype", [(2, 16, 2, 8, "fp32"), (4, 128, 8, 16, "bf16"), (6, 128, 8, 16, "bf16")])
+def test_neighbours_just_inside_the_cutoff(L, C, H, K, dtype):
+    """Atoms whose only neighbours sit within 1e-3 rc of the cutoff: the
+    envelope (about 35 (1 - s)^3 there) weighs the softmax, so an envelope
+    evaluated by cancellation, or from a length rounded to fp32, would give
+    weights of the wrong size or sign.  fp32 (VALU kernel) and bf16 (MFMA
+    kernel at L = 4 and 6) against the oracle, every atom."""
+    say("attention near-cutoff edges", L, C, dtype)
+    import so_equivariant_graph_amd as sea
+
+    w, deltas = _near_cutoff_system(L, C, H, K, dtype)
+    rp, col = neighbors_bruteforce(w.pos, w.cutoff, w.box, w.mol_id)
+    deg = np.diff(rp)
+    far = np.arange(24, w.n_atoms)
+    assert np.all(deg[far] >= 1)
+    for i in far:  # every edge of a group atom is just inside the cutoff
+        r = w.pos[col[rp[i] : rp[i + 1]]].astype(np.float64) - w.pos[i].astype(np.float64)
+        s = np.sqrt((r * r).sum(1)) / w.cutoff
+        assert np.all((s > 1 - 1.2e-3) & (s < 1.0)), (i, s)
+    assert _kind(w) == (sea.KERNEL_VALU if dtype == "fp32" else sea.KERNEL_MFMA)
+    y, y_ref = _run_pair(w)
+    err = max_rel_error(y, y_ref)
+    err_far = max_rel_error(y[far], y_ref[far])
+    say("max rel err", err, "near-cutoff atoms", err_far)
+    assert np.all(np.abs(y_ref[far]).max(axis=(1, 2)) > 0)
+    assert err <= TOL[dtype] and err_far <= TOL[dtype]
