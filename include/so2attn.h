@@ -203,6 +203,30 @@ so2_status so2_attention_fwd_stages(uint32_t stages, const so2_attn_desc* desc, 
                                     so2_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * so2_attention_fwd_noalloc - so2_attention_fwd for callers that cannot
+ * allocate device memory: code under stream (HIP graph) capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments and results
+ * as so2_attention_fwd without the workspace: the call uses a device array
+ * of SO2_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends (looked up once per device on the first call
+ * there), and it allocates nothing.  The caller still passes inputs and y.
+ *   Limit: so2_attention_workspace_bytes(desc) <= SO2_NOALLOC_SCRATCH_BYTES
+ *   (about 14,000 atoms at L = 4, C = 128, bf16; 8,500 at L = 6), else
+ *   SO2_ERR_WORKSPACE before anything is launched.
+ *   Every call rewrites all of the array it reads, so nothing carries over
+ *   from an earlier call; but calls on one GPU share the array: calls that
+ *   overlap in time on that GPU (different streams or host threads) race
+ *   and must be serialised by the caller.
+ * Errors: those of so2_attention_fwd; WORKSPACE past the limit.
+ * ---------------------------------------------------------------------- */
+#define SO2_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+so2_status so2_attention_fwd_noalloc(const so2_attn_desc* desc, const float* pos, const float* box_host,
+                                     const int32_t* row_ptr, const int32_t* col, const void* x,
+                                     const void* w_q, const void* w_k, const void* w_rad,
+                                     const void* w_so2, float* y, so2_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * so2_merged_rms_norm - equivariant merged RMS layer norm of node features
  * ("EquiformerV3: Scaling Efficient, Expressive, and General SE(3)-Equivariant
  * Graph Attention Transformers", technical summary, section 2.B.1: one RMS

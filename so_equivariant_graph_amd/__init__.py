@@ -51,6 +51,7 @@ EXPORTED_SYMBOLS = (
     "so2_attention_kernel_kind",
     "so2_attention_fwd",
     "so2_attention_fwd_stages",
+    "so2_attention_fwd_noalloc",
     "so2_edge_frame_host",
     "so2_merged_rms_norm",
     "so2_swiglu_s2_workspace_bytes",
@@ -120,6 +121,8 @@ def load_library(path: str = LIB_PATH):
     lib.so2_attention_fwd.restype = ctypes.c_int
     lib.so2_attention_fwd_stages.argtypes = [ctypes.c_uint32, ctypes.POINTER(AttnDesc)] + [vp] * 11 + [sz, vp]
     lib.so2_attention_fwd_stages.restype = ctypes.c_int
+    lib.so2_attention_fwd_noalloc.argtypes = [ctypes.POINTER(AttnDesc)] + [vp] * 11
+    lib.so2_attention_fwd_noalloc.restype = ctypes.c_int
     lib.so2_edge_frame_host.argtypes = [i32, vp, vp, vp]
     lib.so2_edge_frame_host.restype = ctypes.c_int
     lib.so2_merged_rms_norm.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, vp]

@@ -28,6 +28,7 @@ SOURCES = [
     "swiglu.hip",
     "attention_valu.hip",
     "attention_mfma.hip",
+    "noalloc.hip",
 ]
 
 HIPCC_FLAGS = [
