@@ -38,6 +38,9 @@ wigner     Wigner-D blocks by exact quadrature, edge-frame rotation
 neighbors  brute-force O(N^2) radius graph in fp64, CSR output
 attention  the per-edge loop: rotate, gate, SO(2) map, rotate back,
            two-pass softmax with the envelope, aggregate
+attention_grad  gradients of the layer (node features, positions, every
+           weight) by autograd through a PyTorch fp64 copy of the forward,
+           pinned to finite differences of the numpy forward
 norm       the merged RMS layer norm of the node features ("EquiformerV3"
            technical summary, section 2.B.1)
 swiglu     the SwiGLU-S2 activation of the node features ("EquiformerV3"
@@ -55,6 +58,7 @@ from .attention import (
     so2_weight_count,
     max_rel_error,
 )
+from .attention_grad import so2_attention_grad_ref
 from .norm import merged_rms_norm_ref
 from .swiglu import s2_grid, swiglu_s2_ref
 
@@ -66,6 +70,7 @@ __all__ = [
     "rot_z",
     "neighbors_bruteforce",
     "so2_attention_ref",
+    "so2_attention_grad_ref",
     "merged_rms_norm_ref",
     "swiglu_s2_ref",
     "s2_grid",
