@@ -203,6 +203,44 @@ so2_status so2_attention_fwd_stages(uint32_t stages, const so2_attn_desc* desc, 
                                     so2_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * so2_attention_bwd - gradients of a scalar loss L through so2_attention_fwd,
+ * for forces and training ("E2Former-V2: On-the-Fly Equivariant Attention
+ * with Linear Activation Memory", technical summary, section 4: the
+ * Conservative variant takes forces as derivatives of the energy through
+ * the layer; "DPA4: Pushing the Accuracy-Cost Frontier of Interatomic
+ * Potentials with EMFA SO(2) Convolution", technical summary, section 2.2:
+ * conservative training differentiates the energy-to-force path).  Given
+ * dy = dL/dy, returns dL/dx, dL/dpos and dL/dW for the same forward (same
+ * descriptor, graph and inputs).  Like the forward it keeps no per-edge
+ * tensor: every edge is recomputed, and only per-(atom, head) softmax
+ * statistics live between its sweeps, so memory stays O(n_atoms).
+ *   dy        [n_targets][(L+1)^2][C] fp32
+ *   dx        [n_atoms][(L+1)^2][C] fp32, written (sources and targets)
+ *   dpos      [n_atoms][3] fp32, written; minus the forces when L is an
+ *             energy.  Row sums are zero up to rounding (translation
+ *             invariance).
+ *   dw_q, dw_k [C][C], dw_rad [K][C], dw_so2 [so2_weight_count] fp32,
+ *             written; each may be NULL (not computed: the force-only path
+ *             skips the weight reductions)
+ *   workspace >= so2_attention_bwd_workspace_bytes(desc) bytes
+ * Arithmetic: fp32 on the vector ALUs for fp32 and bf16 inputs (bf16 values
+ * are widened exactly).  Contributions to dx of sources, dpos, dk and the
+ * weights are summed with fp32 atomics, so the low bits vary between runs.
+ * Shapes: any L <= 6 whose per-target working set (about 5 (L+1)^2 C
+ * floats) fits 160 KB of LDS (C <= 128 at L = 6, C <= 256 at L = 4), else
+ * UNSUPPORTED.  A target whose envelopes are all 0 (edges
+ * exactly at the cutoff only) has y = 0 and gets no gradient.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, BOX, WORKSPACE, DEVICE.
+ * Asynchronous on `stream`; no device allocation.
+ * ---------------------------------------------------------------------- */
+size_t so2_attention_bwd_workspace_bytes(const so2_attn_desc* desc);
+so2_status so2_attention_bwd(const so2_attn_desc* desc, const float* pos, const float* box_host,
+                             const int32_t* row_ptr, const int32_t* col, const void* x, const void* w_q,
+                             const void* w_k, const void* w_rad, const void* w_so2, const float* dy, float* dx,
+                             float* dpos, float* dw_q, float* dw_k, float* dw_rad, float* dw_so2, void* workspace,
+                             size_t workspace_bytes, so2_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * so2_attention_fwd_noalloc - so2_attention_fwd for callers that cannot
  * allocate device memory: code under stream (HIP graph) capture, tight
  * serving loops, harnesses that forbid hipMalloc.  Same arguments and results
@@ -297,6 +335,13 @@ so2_status so2_swiglu_s2_stages(uint32_t stages, const void* x, const void* w_a,
  * Returns INVALID_ARGUMENT for nulls, a zero vector or L outside 0..6.
  * ---------------------------------------------------------------------- */
 so2_status so2_edge_frame_host(int32_t l_max, const float* rhat, float* R_out, float* D_out);
+
+/* The rotation generators the backward uses, on the CPU by the same code:
+ * J_out[a * N + ...] (N = sum_{l<=L} (2l+1)^2, a = x, y, z) holds the blocks
+ * of d/dt D^l(exp(t [e_a]x)) at t = 0 for l = 0..L, each row-major like
+ * so2_edge_frame_host's D.  INVALID_ARGUMENT for a null pointer or L
+ * outside 0..6. */
+so2_status so2_wigner_generators_host(int32_t l_max, float* J_out);
 
 #ifdef __cplusplus
 }

@@ -52,7 +52,10 @@ EXPORTED_SYMBOLS = (
     "so2_attention_fwd",
     "so2_attention_fwd_stages",
     "so2_attention_fwd_noalloc",
+    "so2_attention_bwd_workspace_bytes",
+    "so2_attention_bwd",
     "so2_edge_frame_host",
+    "so2_wigner_generators_host",
     "so2_merged_rms_norm",
     "so2_swiglu_s2_workspace_bytes",
     "so2_swiglu_s2",
@@ -123,8 +126,14 @@ def load_library(path: str = LIB_PATH):
     lib.so2_attention_fwd_stages.restype = ctypes.c_int
     lib.so2_attention_fwd_noalloc.argtypes = [ctypes.POINTER(AttnDesc)] + [vp] * 11
     lib.so2_attention_fwd_noalloc.restype = ctypes.c_int
+    lib.so2_attention_bwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnDesc)]
+    lib.so2_attention_bwd_workspace_bytes.restype = sz
+    lib.so2_attention_bwd.argtypes = [ctypes.POINTER(AttnDesc)] + [vp] * 17 + [sz, vp]
+    lib.so2_attention_bwd.restype = ctypes.c_int
     lib.so2_edge_frame_host.argtypes = [i32, vp, vp, vp]
     lib.so2_edge_frame_host.restype = ctypes.c_int
+    lib.so2_wigner_generators_host.argtypes = [i32, vp]
+    lib.so2_wigner_generators_host.restype = ctypes.c_int
     lib.so2_merged_rms_norm.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, vp]
     lib.so2_merged_rms_norm.restype = ctypes.c_int
     lib.so2_swiglu_s2_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -285,6 +294,45 @@ def so2_attention_fwd(pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, *, l_max, he
     return y
 
 
+def so2_attention_bwd(pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, dy, *, l_max, heads, cutoff, envelope_p=5,
+                      box=None, flags=0, n_targets=None, weights=True, workspace=None):
+    """Gradients of a loss with upstream gradient dy through so2_attention_fwd
+    (same arguments).  Returns a dict of float32 tensors: dx, dpos and, with
+    weights=True, dw_q, dw_k, dw_rad, dw_so2."""
+    import torch
+
+    lib = load_library()
+    dt = _dtype_code(x)
+    n, nc, C = x.shape
+    nt = n if n_targets is None else int(n_targets)
+    if tuple(dy.shape) != (nt, nc, C) or dy.dtype != torch.float32:
+        raise ValueError("dy must be float32 [n_targets, (L+1)^2, C]")
+    tensors = [t.contiguous() for t in (pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, dy)]
+    pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, dy = tensors
+    desc = make_desc(n_atoms=n, n_targets=nt, l_max=l_max, channels=C, heads=heads, n_rbf=w_rad.shape[0],
+                     envelope_p=envelope_p, cutoff=cutoff, flags=flags, dtype=dt)
+    ws_bytes = lib.so2_attention_bwd_workspace_bytes(ctypes.byref(desc))
+    if ws_bytes == 0:
+        _check(SO2_ERR_UNSUPPORTED if l_max <= 6 else SO2_ERR_INVALID_ARGUMENT, "so2_attention_bwd")
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    f32 = dict(dtype=torch.float32, device=x.device)
+    out = {"dx": torch.empty((n, nc, C), **f32), "dpos": torch.empty((n, 3), **f32)}
+    if weights:
+        out.update(dw_q=torch.empty((C, C), **f32), dw_k=torch.empty((C, C), **f32),
+                   dw_rad=torch.empty(tuple(w_rad.shape), **f32), dw_so2=torch.empty(w_so2.numel(), **f32))
+    keep, box_p = _host_box(box)
+    col_arg = col if col.numel() > 0 else row_ptr
+    st = lib.so2_attention_bwd(
+        ctypes.byref(desc), _ptr(pos), box_p, _ptr(row_ptr), _ptr(col_arg), _ptr(x), _ptr(w_q), _ptr(w_k),
+        _ptr(w_rad), _ptr(w_so2), _ptr(dy), _ptr(out["dx"]), _ptr(out["dpos"]), _ptr(out.get("dw_q")),
+        _ptr(out.get("dw_k")), _ptr(out.get("dw_rad")), _ptr(out.get("dw_so2")), _ptr(workspace), ws_bytes,
+        _stream_handle(x.device),
+    )
+    _check(st, "so2_attention_bwd")
+    return out
+
+
 def merged_rms_norm(x, gamma, *, eps=1e-5, out=None):
     """Merged RMS layer norm: one RMS statistic per node over every degree,
     gain gamma [L+1, C] (float32) per degree and channel.  x: [N,(L+1)^2,C]
@@ -323,6 +371,23 @@ def edge_frame_host(l_max: int, rhat):
         blocks.append(D[off : off + n * n].reshape(n, n).astype(np.float64))
         off += n * n
     return R.reshape(3, 3).astype(np.float64), blocks
+
+
+def wigner_generators_host(l_max: int):
+    """The backward's rotation generators (CPU, same code): [3][l] blocks."""
+    lib = load_library()
+    total = sum((2 * l + 1) ** 2 for l in range(l_max + 1))
+    J = np.zeros(3 * total, dtype=np.float32)
+    _check(lib.so2_wigner_generators_host(l_max, J.ctypes.data), "so2_wigner_generators_host")
+    out = []
+    for a in range(3):
+        blocks, off = [], a * total
+        for l in range(l_max + 1):
+            n = 2 * l + 1
+            blocks.append(J[off : off + n * n].reshape(n, n).astype(np.float64))
+            off += n * n
+        out.append(blocks)
+    return out
 
 
 __all__ = [

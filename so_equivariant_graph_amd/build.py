@@ -28,6 +28,7 @@ SOURCES = [
     "swiglu.hip",
     "attention_valu.hip",
     "attention_mfma.hip",
+    "attention_bwd.hip",
     "noalloc.hip",
 ]
 

@@ -203,6 +203,75 @@ so2_status so2_attention_fwd_stages(uint32_t stages, const so2_attn_desc* desc, 
   return SO2_OK;
 }
 
+static so2_status bwd_layout(const so2_attn_desc* d, AttnLayout* out) {
+  so2_status st = check_desc(d);
+  if (st != SO2_OK) return st;
+  if (!bwd_supported(d->l_max, d->channels, d->heads, d->n_rbf)) return SO2_ERR_UNSUPPORTED;
+  AttnLayout L{};
+  size_t off = 0;
+  L.q = off;
+  off += align256(sizeof(float) * (size_t)d->n_atoms * d->channels);
+  L.k = off;
+  off += align256(sizeof(float) * (size_t)d->n_atoms * d->channels);
+  L.scratch = off;
+  L.scratch_bytes = bwd_scratch_bytes(d->n_atoms, d->n_targets, d->l_max, d->channels);
+  off += align256(L.scratch_bytes);
+  L.total = off;
+  *out = L;
+  return SO2_OK;
+}
+
+size_t so2_attention_bwd_workspace_bytes(const so2_attn_desc* desc) {
+  AttnLayout L{};
+  return bwd_layout(desc, &L) == SO2_OK ? L.total : 0;
+}
+
+so2_status so2_attention_bwd(const so2_attn_desc* desc, const float* pos, const float* box_host,
+                             const int32_t* row_ptr, const int32_t* col, const void* x, const void* w_q,
+                             const void* w_k, const void* w_rad, const void* w_so2, const float* dy, float* dx,
+                             float* dpos, float* dw_q, float* dw_k, float* dw_rad, float* dw_so2, void* workspace,
+                             size_t workspace_bytes, so2_stream_t stream) {
+  AttnLayout lay{};
+  so2_status st = bwd_layout(desc, &lay);
+  if (st != SO2_OK) return st;
+  st = check_box(box_host, desc->cutoff);
+  if (st != SO2_OK) return st;
+  if (!pos || !row_ptr || !col || !x || !w_q || !w_k || !w_rad || !w_so2 || !dy || !dx || !dpos || !workspace)
+    return SO2_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < lay.total || ((uintptr_t)workspace & 255)) return SO2_ERR_WORKSPACE;
+  AttnArgs a{};
+  a.pos = pos;
+  a.row_ptr = row_ptr;
+  a.col = col;
+  a.x = x;
+  a.w_q = w_q;
+  a.w_k = w_k;
+  a.w_rad = w_rad;
+  a.w_so2 = w_so2;
+  char* ws = (char*)workspace;
+  a.q = (float*)(ws + lay.q);
+  a.k = (float*)(ws + lay.k);
+  a.scratch = ws + lay.scratch;
+  a.scratch_bytes = lay.scratch_bytes;
+  a.n_atoms = desc->n_atoms;
+  a.n_targets = desc->n_atoms;  // q for every atom (the projection kernel's row count)
+  a.L = desc->l_max;
+  a.C = desc->channels;
+  a.H = desc->heads;
+  a.K = desc->n_rbf;
+  a.p = desc->envelope_p;
+  a.cutoff = desc->cutoff;
+  a.flags = desc->flags;
+  a.dtype = desc->dtype;
+  a.periodic = box_host != nullptr;
+  for (int d = 0; d < 3; ++d) a.box[d] = box_host ? box_host[d] : 0.0f;
+  hipStream_t s = (hipStream_t)stream;
+  st = launch_qk_proj(a, s);
+  if (st != SO2_OK) return st;
+  a.n_targets = desc->n_targets;
+  return launch_attention_bwd(a, dy, dx, dpos, dw_q, dw_k, dw_rad, dw_so2, s);
+}
+
 so2_status so2_attention_fwd(const so2_attn_desc* desc, const float* pos, const float* box_host,
                              const int32_t* row_ptr, const int32_t* col, const void* x,
                              const void* w_q, const void* w_k, const void* w_rad,
@@ -253,6 +322,13 @@ so2_status so2_edge_frame_host(int32_t l_max, const float* rhat, float* R_out, f
   if (!(n > 0.0f) || !isfinite(n)) return SO2_ERR_INVALID_ARGUMENT;
   edge_frame(rhat[0] / n, rhat[1] / n, rhat[2] / n, R_out);
   wigner_blocks_serial(l_max, R_out, D_out);
+  return SO2_OK;
+}
+
+so2_status so2_wigner_generators_host(int32_t l_max, float* J_out) {
+  if (!J_out || l_max < 0 || l_max > kMaxL) return SO2_ERR_INVALID_ARGUMENT;
+  float ident[wig_total(kMaxL)];
+  wigner_generators(l_max, J_out, ident);
   return SO2_OK;
 }
 

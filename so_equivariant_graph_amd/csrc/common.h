@@ -83,6 +83,18 @@ __host__ __device__ inline float envelope_u(float s, float t, int p) {
   return t * t * t * q;
 }
 
+// du/ds of envelope_u: -3 t^2 Q(s) + t^3 Q'(s), Q'(s) = sum_{1<=k<p} k (k+1)(k+2)/2 s^(k-1); 0 outside.
+__host__ __device__ inline float envelope_du(float s, float t, int p) {
+  if (!(t > 0.0f)) return 0.0f;
+  float q = 0.0f, dq = 0.0f;
+  for (int k = p - 1; k >= 0; --k) {
+    const float ck = 0.5f * (float)((k + 1) * (k + 2));
+    dq = dq * s + q;  // Horner for the derivative alongside the value
+    q = q * s + ck;
+  }
+  return t * t * (t * dq - 3.0f * q);
+}
+
 // Geometry of edge (i -> j) from fp32 positions, in fp64: r = p_j - p_i
 // (exact in fp64), with a box the minimum image r - b rint(r / b) (the
 // operation sequence of the neighbour test, no contraction), |r| and

@@ -115,6 +115,48 @@ __host__ __device__ inline void wigner_blocks_serial(int L, const float* R, floa
   }
 }
 
+// Generators of rotations in the real harmonic basis: J_a^l = d/dt
+// D^l(exp(t [e_a]x)) at t = 0 for the axes a = x, y, z ([e_a]x v = e_a x v).
+// The recursion is bilinear in (D^1, D^{l-1}) and D = I at t = 0, so
+//   J^1 = (D^1 of [e_a]x),  J^l = f(J^1, I) + f(I, J^{l-1})
+// with f the recursion step (wigner_entry).  J[a * wig_total(L) + ...]
+// holds blocks 0..L like wigner_blocks_serial; each block is antisymmetric.
+// ident must hold wig_total(L) floats of scratch.
+__host__ __device__ inline void wigner_generators(int L, float* J, float* ident) {
+  const int tot = wig_total(L);
+  for (int q = 0; q < tot; ++q) ident[q] = 0.0f;
+  for (int l = 0; l <= L; ++l)
+    for (int a = 0; a < 2 * l + 1; ++a) ident[wig_offset(l) + a * (2 * l + 1) + a] = 1.0f;
+  for (int ax = 0; ax < 3; ++ax) {
+    float* Ja = J + ax * tot;
+    Ja[0] = 0.0f;
+    if (L < 1) continue;
+    float E[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+    if (ax == 0) {
+      E[5] = -1.0f;
+      E[7] = 1.0f;
+    } else if (ax == 1) {
+      E[2] = 1.0f;
+      E[6] = -1.0f;
+    } else {
+      E[1] = -1.0f;
+      E[3] = 1.0f;
+    }
+    float* J1 = Ja + wig_offset(1);
+    wigner_l1(E, J1);
+    const float* I1 = ident + wig_offset(1);
+    for (int l = 2; l <= L; ++l) {
+      const int n = 2 * l + 1;
+      const float* Jp = Ja + wig_offset(l - 1);
+      const float* Ip = ident + wig_offset(l - 1);
+      float* Jl = Ja + wig_offset(l);
+      for (int m = 0; m < n; ++m)
+        for (int mp = 0; mp < n; ++mp)
+          Jl[m * n + mp] = wigner_entry(l, m - l, mp - l, J1, Ip) + wigner_entry(l, m - l, mp - l, I1, Jp);
+    }
+  }
+}
+
 // D^l (l >= 2) from D^1 and D^{l-1}, all in registers: with l a template
 // parameter every index, coefficient and branch of wigner_entry folds to a
 // constant, leaving a few multiply-adds per entry.

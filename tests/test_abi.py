@@ -254,3 +254,47 @@ def test_neighbor_errors_before_launch():
     assert call(FAKE, 100, box_small, 4.5, FAKE, FAKE, 10, FAKE, ws) == sea.SO2_ERR_BOX
     assert call(FAKE, 100, None, 4.5, FAKE, FAKE, 10, FAKE, ws - 1) == sea.SO2_ERR_WORKSPACE
     assert call(FAKE, 100, None, 4.5, FAKE, None, 10, FAKE, ws) == sea.SO2_ERR_INVALID_ARGUMENT
+
+
+def test_host_rotation_generators_match_the_oracle():
+    # J_a^l = d/dt D^l(exp(t [e_a]x)) at 0, against central differences of the
+    # oracle's quadrature Wigner-D
+    from scipy.spatial.transform import Rotation
+
+    L = 6
+    J = sea.wigner_generators_host(L)
+    h = 1e-5
+    for a in range(3):
+        e = np.zeros(3)
+        e[a] = 1.0
+        Dp = wigner_d_blocks(L, Rotation.from_rotvec(h * e).as_matrix())
+        Dm = wigner_d_blocks(L, Rotation.from_rotvec(-h * e).as_matrix())
+        for l in range(L + 1):
+            fd = (Dp[l] - Dm[l]) / (2 * h)
+            np.testing.assert_allclose(J[a][l], fd, atol=2e-5)
+            np.testing.assert_allclose(J[a][l], -J[a][l].T, atol=1e-5)
+    assert sea.load_library().so2_wigner_generators_host(7, None) == sea.SO2_ERR_INVALID_ARGUMENT
+
+
+def test_backward_errors_before_launch():
+    lib = sea.load_library()
+    d = _desc()
+    need = lib.so2_attention_bwd_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    keep, box_p = sea._host_box(None)
+
+    def call(desc, ws_bytes, null=(), box=None):
+        keep2, bp = sea._host_box(box)
+        names = ["pos", "row_ptr", "col", "x", "w_q", "w_k", "w_rad", "w_so2", "dy", "dx", "dpos", "dw_q", "dw_k",
+                 "dw_rad", "dw_so2", "ws"]
+        args = [ctypes.c_void_p(0) if n in null else FAKE for n in names]
+        return lib.so2_attention_bwd(ctypes.byref(desc), args[0], bp, *args[1:15], args[15], ws_bytes, None)
+
+    assert call(d, need, null=("dy",)) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(d, need, null=("dpos",)) == sea.SO2_ERR_INVALID_ARGUMENT
+    assert call(d, need - 1) == sea.SO2_ERR_WORKSPACE
+    assert call(d, need, box=[9.0, 9.0, 9.0]) == sea.SO2_ERR_BOX
+    assert call(_desc(l_max=7), need) == sea.SO2_ERR_UNSUPPORTED
+    big = _desc(l_max=6, channels=512, heads=8)
+    assert lib.so2_attention_bwd_workspace_bytes(ctypes.byref(big)) == 0
+    assert call(big, 1 << 40) == sea.SO2_ERR_UNSUPPORTED
