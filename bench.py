@@ -13,6 +13,7 @@ C = 128, bf16), the largest system of the set that runs on one GPU.
     python bench.py --memory-sweep [--steps 5 --warmup 2]   (peak bytes against N)
     python bench.py --norm                                  (merged RMS layer norm, HBM roofline)
     python bench.py --swiglu                                (SwiGLU-S2 activation, vector-unit roofline)
+    python bench.py --backward 32 --steps 3 --warmup 1      (the backward on 32 small molecules)
 
 value          messages (edges) per second of the whole step
 roofline       the fused attention kernel against the dense bf16 MFMA peak:
@@ -418,6 +419,63 @@ def swiglu_bench(steps, warmup):
     }), flush=True)
 
 
+def backward_bench(steps, warmup, n_molecules):
+    """The backward of the attention layer (so2_attention_bwd) on a batch of
+    the small-molecule workload (bf16 inputs, L = 4, C = 128, fp32 arithmetic
+    on the vector ALUs): messages/s of the force-only call (dx, dpos) and of
+    the full call (every weight gradient too), timed with torch events on the
+    stream the library launches on.  Algorithmic flops per edge: the
+    transposed per-m map (the same count as the forward map), plus the same
+    again for the SO(2) weight gradient in the full call; rooflined against
+    the fp32 vector peak."""
+    import numpy as np
+    import torch
+
+    import so_equivariant_graph_amd as sea
+    from synth import make_workload
+
+    w = make_workload("small_molecules", geometry={"n_molecules": n_molecules})
+    dev = torch.device("cuda:0")
+    t = lambda a, d=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=d)
+    pos = t(w.pos, torch.float32)
+    x, w_q, w_k, w_rad, w_so2 = (t(a) for a in (w.x, w.w_q, w.w_k, w.w_rad, w.w_so2))
+    mol = torch.from_numpy(w.mol_id.astype(np.int32)).to(dev)
+    row_ptr, col = sea.build_neighbors(pos, w.cutoff, box=w.box, mol_id=mol)
+    E = int(col.numel())
+    dy = torch.randn((w.n_atoms, (w.l_max + 1) ** 2, w.channels), generator=torch.Generator().manual_seed(0)).to(dev)
+    kw = dict(l_max=w.l_max, heads=w.heads, cutoff=w.cutoff, envelope_p=w.envelope_p, box=w.box)
+    res = {}
+    for name, weights in (("forces", False), ("full", True)):
+        for _ in range(warmup):
+            sea.so2_attention_bwd(pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, dy, weights=weights, **kw)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record()
+            g = sea.so2_attention_bwd(pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, dy, weights=weights, **kw)
+            b.record()
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in ev]
+        res[name] = (sum(ms) / len(ms), bool(all(torch.isfinite(v).all() for v in g.values())))
+    F = flops_per_edge(w.l_max, w.channels)
+    ms_f, ok_f = res["forces"]
+    ms_w, ok_w = res["full"]
+    achieved = E * 2 * F / (ms_w * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "backward neighbor-pair messages/sec (so2_attention_bwd, all gradients)",
+        "value": E / (ms_w * 1e-3), "unit": "messages/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_w, "higher_is_better": True, "dtype": "bf16 inputs, fp32 arithmetic", "data": "synthetic",
+        "config": {"workload": f"small_molecules batch of {n_molecules}", "n_atoms": w.n_atoms, "n_edges": E,
+                   "l_max": w.l_max, "channels": w.channels, "heads": w.heads},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP32_VALU_TFLOPS, "traffic": None},
+        "detail": {"forces_only_ms": ms_f, "forces_only_messages_per_s": E / (ms_f * 1e-3),
+                   "forces_only_tflops": E * F / (ms_f * 1e-3) / 1e12, "full_ms": ms_w,
+                   "flop_per_edge_full": 2 * F, "flop_per_edge_forces": F,
+                   "outputs_finite": ok_f and ok_w},
+    }), flush=True)
+
+
 SWEEP_ATOMS = (12_500, 25_000, 50_000, 100_000, 200_000)
 
 
@@ -474,6 +532,8 @@ def main():
                     help="the SwiGLU-S2 activation of the 100k-atom water box's features instead of the attention step")
     ap.add_argument("--norm", action="store_true",
                     help="only time the merged RMS layer norm on the 100k-atom water box's features")
+    ap.add_argument("--backward", type=int, metavar="N_MOLECULES", default=0,
+                    help="only time so2_attention_bwd on a batch of N small molecules")
     ap.add_argument("--memory-sweep", action="store_true",
                     help="only run the water box at 12.5k-200k atoms: peak device bytes against N")
     args = ap.parse_args()
@@ -489,6 +549,9 @@ def main():
         return
     if args.memory_sweep:
         memory_sweep(args.steps, args.warmup)
+        return
+    if args.backward:
+        backward_bench(args.steps, args.warmup, args.backward)
         return
     if args.norm:
         norm_bench(args.steps, args.warmup)
