@@ -52,20 +52,26 @@ FLAG_RBF_ENVELOPE = 1  # alternative reading: phi_k(rho) is also multiplied by u
 FLAG_NO_RADIAL = 2  # g_ij == 1 (used by special-case tests)
 
 
-def so2_weight_count(l_max: int, channels: int) -> int:
-    """C^2 [(L+1)^2 + 2 sum_{m=1..L} (L+1-m)^2]."""
+def so2_weight_count(l_max: int, channels: int, m_max=None, n_focus: int = 1) -> int:
+    """C^2 [(L+1)^2 + 2 sum_{m=1..m_max} (L+1-m)^2] for one stack over C
+    channels (m_max = L by default); with F focus streams, F stacks over C/F
+    channels each."""
+    m_max = l_max if m_max is None else m_max
+    cf = channels // n_focus
     total = (l_max + 1) ** 2
-    for m in range(1, l_max + 1):
+    for m in range(1, m_max + 1):
         total += 2 * (l_max + 1 - m) ** 2
-    return total * channels * channels
+    return n_focus * total * cf * cf
 
 
-def unpack_so2(w_so2, l_max: int, channels: int):
-    """Split the packed SO(2) weights.
+def unpack_so2(w_so2, l_max: int, channels: int, m_max=None):
+    """Split one stack of packed SO(2) weights.
 
-    Packing: W0 [(L+1)C x (L+1)C], then for m = 1..L the pair W1_m, W2_m,
-    each [(L+1-m)C x (L+1-m)C]; every block row-major [out][in] with row and
-    column index (l - m) C + c.  Returns (W0, {m: W1_m}, {m: W2_m})."""
+    Packing: W0 [(L+1)C x (L+1)C], then for m = 1..m_max (L by default) the
+    pair W1_m, W2_m, each [(L+1-m)C x (L+1-m)C]; every block row-major
+    [out][in] with row and column index (l - m) C + c.  Returns (W0,
+    {m: W1_m}, {m: W2_m})."""
+    m_max = l_max if m_max is None else m_max
     w = np.asarray(w_so2, dtype=np.float64).ravel()
     C = channels
     off = 0
@@ -73,7 +79,7 @@ def unpack_so2(w_so2, l_max: int, channels: int):
     w0 = w[off : off + k0 * k0].reshape(k0, k0)
     off += k0 * k0
     w1, w2 = {}, {}
-    for m in range(1, l_max + 1):
+    for m in range(1, m_max + 1):
         km = (l_max + 1 - m) * C
         w1[m] = w[off : off + km * km].reshape(km, km)
         off += km * km
@@ -143,7 +149,7 @@ def _so2_map(xt, w0, w1, w2, l_max):
     rows0 = [l * l + l for l in range(l_max + 1)]
     y0 = xt[:, rows0].reshape(n_e, -1) @ w0.T
     yt[:, rows0] = y0.reshape(n_e, l_max + 1, C)
-    for m in range(1, l_max + 1):
+    for m in sorted(w1):  # m = 1..m_max; rows with |m| > m_max stay 0
         rp = [l * l + l + m for l in range(m, l_max + 1)]
         rm = [l * l + l - m for l in range(m, l_max + 1)]
         xp = xt[:, rp].reshape(n_e, -1)
@@ -174,6 +180,10 @@ def so2_attention_ref(
     targets=None,
     gauge=None,
     return_weights: bool = False,
+    m_max=None,
+    w_logit=None,
+    n_focus: int = 1,
+    w_focus=None,
 ):
     """y[t] for each target t (default: all atoms), shape [T, (L+1)^2, C].
 
@@ -184,6 +194,20 @@ def so2_attention_ref(
     gauge   optional callable (target, edge_index) -> angle; the edge frame
             becomes rot_z(angle) @ R_ij (the output must not change)
     return_weights  also return {target: a [deg, H]}
+
+    Variants of the value path and the logits (readings V1-V3):
+    m_max   the per-m maps stop at |m| = m_max (default L): the rows with
+            |m| > m_max of the edge-frame message are 0, and w_so2 holds the
+            blocks for m = 0..m_max only
+    w_logit [K][H]: a radial logit bias, z_ij^h += sum_k phi_k(rho) w_logit[k][h]
+            (the same Gaussian basis as the gate, without the envelope)
+    n_focus F > 1: the channels form F contiguous streams of C/F; each
+            stream has its own stack of per-m maps (w_so2 is the F stacks
+            back to back, stack f acting on channels [f C/F, (f+1) C/F)),
+            and the streams of one edge are weighted by pi = softmax over f
+            of score_f = sum_{c in f} w_focus[c] yt[(0,0), c], the invariant
+            l = 0 part of the stream's edge-frame message (DPA4's
+            cross-focus competition); w_focus [C] is required
     """
     # fp32 positions are widened exactly; fp64 positions (symmetry tests)
     # are used as they are.
@@ -199,7 +223,19 @@ def so2_attention_ref(
     w_k = np.asarray(w_k, dtype=np.float64)
     w_rad = np.asarray(w_rad, dtype=np.float64)
     n_rbf = w_rad.shape[0]
-    w0, w1, w2 = unpack_so2(w_so2, l_max, C)
+    m_max = l_max if m_max is None else int(m_max)
+    if not 0 <= m_max <= l_max:
+        raise ValueError("m_max must lie in 0..l_max")
+    if C % n_focus or (n_focus > 1 and w_focus is None):
+        raise ValueError("n_focus must divide C, and w_focus is required with several streams")
+    cf = C // n_focus
+    w_flat = np.asarray(w_so2, dtype=np.float64).ravel()
+    per = so2_weight_count(l_max, cf, m_max)
+    if w_flat.size != n_focus * per:
+        raise ValueError(f"w_so2 has {w_flat.size} entries, expected {n_focus * per}")
+    stacks = [unpack_so2(w_flat[f * per : (f + 1) * per], l_max, cf, m_max) for f in range(n_focus)]
+    w_logit = None if w_logit is None else np.asarray(w_logit, dtype=np.float64)
+    w_focus = None if w_focus is None else np.asarray(w_focus, dtype=np.float64)
     rc = float(np.float32(cutoff))
     row_ptr = np.asarray(row_ptr, dtype=np.int64)
     col = np.asarray(col, dtype=np.int64)
@@ -228,6 +264,8 @@ def so2_attention_ref(
             u[e] = envelope(rho / rc, envelope_p)  # O4
             for h in range(heads):  # O3
                 z[e, h] = q[i, h * d : (h + 1) * d] @ k[j, h * d : (h + 1) * d] / sqrt(d)
+            if w_logit is not None:  # V2, radial logit bias
+                z[e] += radial_gaussians(rho, cutoff, n_rbf) @ w_logit
             if flags & FLAG_NO_RADIAL:  # O6
                 g[e] = 1.0
             else:
@@ -242,7 +280,14 @@ def so2_attention_ref(
         xt = np.empty((deg, nc, C))
         for e, j in enumerate(js):
             xt[e] = _rotate([b[e] for b in blocks], x[j], l_max) * g[e][None, :]  # O9
-        yt = _so2_map(xt, w0, w1, w2, l_max)  # O10, every edge of i through the same map
+        yt = np.concatenate(  # O10, every edge of i through the same map, stream by stream (V1, V3)
+            [_so2_map(xt[:, :, f * cf : (f + 1) * cf], *stacks[f], l_max) for f in range(n_focus)], axis=2
+        )
+        if n_focus > 1:  # V3, cross-focus softmax over the streams' invariant l = 0 message
+            score = (yt[:, 0, :] * w_focus[None, :]).reshape(deg, n_focus, cf).sum(-1)
+            pi = np.exp(score - score.max(axis=1, keepdims=True))
+            pi /= pi.sum(axis=1, keepdims=True)
+            yt = yt * np.repeat(pi, cf, axis=1)[:, None, :]
         v = np.empty((deg, nc, C))
         for e in range(deg):
             v[e] = _rotate([b[e] for b in blocks], yt[e], l_max, transpose=True)  # O11
