@@ -203,6 +203,45 @@ so2_status so2_attention_fwd_stages(uint32_t stages, const so2_attn_desc* desc, 
                                     so2_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * so2_attention_fwd_variant - the forward with variants of the value path
+ * and the logits.  "DPA4: Pushing the Accuracy-Cost Frontier of
+ * Interatomic Potentials with EMFA SO(2) Convolution", technical summary,
+ * section 2.1 A2: the hidden channels split into F focus streams, each with
+ * its own SO(2) stack, reweighted per edge by a softmax across streams from
+ * the invariant l = 0 section.  Per edge, in the edge frame:
+ *   m_max      the per-m maps stop at |m| = m_max (rows above give 0)
+ *   w_logit    [K][H] in dtype, or NULL: z_ij^h += sum_k phi_k(|r_ij|)
+ *              w_logit[k][h] (the gate's Gaussian basis, no envelope)
+ *   n_focus F  channels [f C/F, (f+1) C/F) form stream f; w_so2 is F stacks
+ *              back to back, stack f the packing above over C/F channels
+ *              (so2_weight_count_variant entries in all); stream f of the
+ *              edge message is scaled by pi_f = softmax_f(sum_{c in f}
+ *              w_focus[c] yt[(0,0), c])
+ *   w_focus    [C] in dtype, required when n_focus > 1
+ * The base layer (m_max = -1 or l_max, n_focus = 1) runs where
+ * so2_attention_fwd would, with or without the logit bias; truncated orders
+ * and focus streams run on the fp32 VALU kernel.  Other arguments, the
+ * workspace (so2_attention_variant_workspace_bytes) and the errors are those
+ * of so2_attention_fwd, plus INVALID_ARGUMENT for m_max outside -1..l_max,
+ * n_focus < 1 or not dividing C, or a missing w_focus.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t m_max;   /* orders |m| <= m_max; -1 = l_max (every order)      */
+  int32_t n_focus; /* F >= 1 focus streams of C / F channels (1 = one)   */
+} so2_attn_variant;
+
+/* Entries of w_so2 for a variant: F C'^2 [(L+1)^2 + 2 sum_{m=1..m_max}
+ * (L+1-m)^2], C' = C / F; -1 on bad input. */
+int64_t so2_weight_count_variant(int32_t l_max, int32_t channels, int32_t m_max, int32_t n_focus);
+size_t so2_attention_variant_workspace_bytes(const so2_attn_desc* desc, const so2_attn_variant* var);
+int32_t so2_attention_variant_kernel_kind(const so2_attn_desc* desc, const so2_attn_variant* var);
+so2_status so2_attention_fwd_variant(const so2_attn_desc* desc, const so2_attn_variant* var, const float* pos,
+                                     const float* box_host, const int32_t* row_ptr, const int32_t* col,
+                                     const void* x, const void* w_q, const void* w_k, const void* w_rad,
+                                     const void* w_so2, const void* w_logit, const void* w_focus, float* y,
+                                     void* workspace, size_t workspace_bytes, so2_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * so2_attention_bwd - gradients of a scalar loss L through so2_attention_fwd,
  * for forces and training ("E2Former-V2: On-the-Fly Equivariant Attention
  * with Linear Activation Memory", technical summary, section 4: the

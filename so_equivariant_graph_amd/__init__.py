@@ -52,6 +52,10 @@ EXPORTED_SYMBOLS = (
     "so2_attention_fwd",
     "so2_attention_fwd_stages",
     "so2_attention_fwd_noalloc",
+    "so2_weight_count_variant",
+    "so2_attention_variant_workspace_bytes",
+    "so2_attention_variant_kernel_kind",
+    "so2_attention_fwd_variant",
     "so2_attention_bwd_workspace_bytes",
     "so2_attention_bwd",
     "so2_edge_frame_host",
@@ -76,6 +80,10 @@ class AttnDesc(ctypes.Structure):
         ("flags", ctypes.c_uint32),
         ("dtype", ctypes.c_int32),
     ]
+
+
+class AttnVariant(ctypes.Structure):
+    _fields_ = [("m_max", ctypes.c_int32), ("n_focus", ctypes.c_int32)]
 
 
 class SO2Error(RuntimeError):
@@ -126,6 +134,15 @@ def load_library(path: str = LIB_PATH):
     lib.so2_attention_fwd_stages.restype = ctypes.c_int
     lib.so2_attention_fwd_noalloc.argtypes = [ctypes.POINTER(AttnDesc)] + [vp] * 11
     lib.so2_attention_fwd_noalloc.restype = ctypes.c_int
+    lib.so2_weight_count_variant.argtypes = [i32, i32, i32, i32]
+    lib.so2_weight_count_variant.restype = i64
+    lib.so2_attention_variant_workspace_bytes.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnVariant)]
+    lib.so2_attention_variant_workspace_bytes.restype = sz
+    lib.so2_attention_variant_kernel_kind.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnVariant)]
+    lib.so2_attention_variant_kernel_kind.restype = i32
+    lib.so2_attention_fwd_variant.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnVariant)] + [vp] * 13 + [
+        sz, vp]
+    lib.so2_attention_fwd_variant.restype = ctypes.c_int
     lib.so2_attention_bwd_workspace_bytes.argtypes = [ctypes.POINTER(AttnDesc)]
     lib.so2_attention_bwd_workspace_bytes.restype = sz
     lib.so2_attention_bwd.argtypes = [ctypes.POINTER(AttnDesc)] + [vp] * 17 + [sz, vp]
@@ -291,6 +308,45 @@ def so2_attention_fwd(pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, *, l_max, he
         _stream_handle(x.device),
     )
     _check(st, "so2_attention_fwd")
+    return y
+
+
+def so2_attention_fwd_variant(pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, *, l_max, heads, cutoff, envelope_p=5,
+                              box=None, flags=0, n_targets=None, m_max=-1, n_focus=1, w_logit=None, w_focus=None,
+                              out=None, workspace=None):
+    """so2_attention_fwd with the variants of so2_attention_fwd_variant:
+    truncated orders (m_max), F focus streams with w_focus [C], and a radial
+    logit bias w_logit [K, H] (each in x's dtype)."""
+    import torch
+
+    lib = load_library()
+    dt = _dtype_code(x)
+    n, nc, C = x.shape
+    nt = n if n_targets is None else int(n_targets)
+    for name, t in (("w_logit", w_logit), ("w_focus", w_focus)):
+        if t is not None and t.dtype != x.dtype:
+            raise ValueError(f"{name} must have x's dtype {x.dtype}")
+    want = lib.so2_weight_count_variant(l_max, C, m_max, n_focus)
+    if w_so2.numel() != want:
+        raise ValueError(f"w_so2 has {w_so2.numel()} entries, the variant needs {want}")
+    tensors = [None if t is None else t.contiguous()
+               for t in (pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, w_logit, w_focus)]
+    pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, w_logit, w_focus = tensors
+    desc = make_desc(n_atoms=n, n_targets=nt, l_max=l_max, channels=C, heads=heads, n_rbf=w_rad.shape[0],
+                     envelope_p=envelope_p, cutoff=cutoff, flags=flags, dtype=dt)
+    var = AttnVariant(int(m_max), int(n_focus))
+    ws_bytes = lib.so2_attention_variant_workspace_bytes(ctypes.byref(desc), ctypes.byref(var))
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    y = out if out is not None else torch.empty((nt, nc, C), dtype=torch.float32, device=x.device)
+    keep, box_p = _host_box(box)
+    col_arg = col if col.numel() > 0 else row_ptr
+    st = lib.so2_attention_fwd_variant(
+        ctypes.byref(desc), ctypes.byref(var), _ptr(pos), box_p, _ptr(row_ptr), _ptr(col_arg), _ptr(x), _ptr(w_q),
+        _ptr(w_k), _ptr(w_rad), _ptr(w_so2), _ptr(w_logit), _ptr(w_focus), _ptr(y), _ptr(workspace), ws_bytes,
+        _stream_handle(x.device),
+    )
+    _check(st, "so2_attention_fwd_variant")
     return y
 
 

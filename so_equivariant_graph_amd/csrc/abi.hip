@@ -39,10 +39,26 @@ so2_status check_desc(const so2_attn_desc* d) {
   return SO2_OK;
 }
 
+// The base layer: every order, one stream (the radial logit bias is carried
+// by both kernels).
+const so2_attn_variant kBase = {-1, 1};
+
+so2_status check_variant(const so2_attn_desc* d, const so2_attn_variant* v) {
+  if (!v) return SO2_ERR_INVALID_ARGUMENT;
+  if (v->m_max < -1 || v->m_max > d->l_max) return SO2_ERR_INVALID_ARGUMENT;
+  if (v->n_focus < 1 || d->channels % v->n_focus) return SO2_ERR_INVALID_ARGUMENT;
+  return SO2_OK;
+}
+
+bool is_base(const so2_attn_desc* d, const so2_attn_variant* v) {
+  return (v->m_max < 0 || v->m_max == d->l_max) && v->n_focus == 1;
+}
+
 // bf16 shapes the MFMA kernel takes run there; past its size limit they are
-// refused (kNone) rather than moved to the untuned VALU kernel.
-Kind pick_kind(const so2_attn_desc* d) {
-  if (d->dtype == SO2_BF16 && mfma_shape(d->l_max, d->channels, d->heads, d->n_rbf))
+// refused (kNone) rather than moved to the untuned VALU kernel.  Truncated
+// orders and focus streams run on the VALU kernel.
+Kind pick_kind(const so2_attn_desc* d, const so2_attn_variant* v = &kBase) {
+  if (is_base(d, v) && d->dtype == SO2_BF16 && mfma_shape(d->l_max, d->channels, d->heads, d->n_rbf))
     return mfma_fits(d->l_max, d->n_atoms) ? kMfma : kNone;
   if (valu_supported(d->l_max, d->channels, d->heads)) return kValu;
   return kNone;
@@ -127,6 +143,13 @@ int64_t so2_weight_count(int32_t l_max, int32_t channels) {
   return C * C * ((L + 1) * (L + 1) + L * (L + 1) * (2 * L + 1) / 3);
 }
 
+int64_t so2_weight_count_variant(int32_t l_max, int32_t channels, int32_t m_max, int32_t n_focus) {
+  if (l_max < 0 || channels < 1 || n_focus < 1 || channels % n_focus) return -1;
+  if (m_max < 0) m_max = l_max;
+  if (m_max > l_max) return -1;
+  return (int64_t)n_focus * so2_w1_offset(l_max, channels / n_focus, m_max + 1);
+}
+
 size_t so2_attention_workspace_bytes(const so2_attn_desc* desc) {
   if (check_desc(desc) != SO2_OK) return 0;
   Kind kind = pick_kind(desc);
@@ -139,15 +162,18 @@ int32_t so2_attention_kernel_kind(const so2_attn_desc* desc) {
   return (int32_t)pick_kind(desc);
 }
 
-so2_status so2_attention_fwd_stages(uint32_t stages, const so2_attn_desc* desc, const float* pos,
-                                    const float* box_host, const int32_t* row_ptr, const int32_t* col,
-                                    const void* x, const void* w_q, const void* w_k, const void* w_rad,
-                                    const void* w_so2, float* y, void* workspace, size_t workspace_bytes,
-                                    so2_stream_t stream) {
+static so2_status attention_fwd_impl(uint32_t stages, const so2_attn_desc* desc, const so2_attn_variant* var,
+                                     const float* pos, const float* box_host, const int32_t* row_ptr,
+                                     const int32_t* col, const void* x, const void* w_q, const void* w_k,
+                                     const void* w_rad, const void* w_so2, const void* w_logit, const void* w_focus,
+                                     float* y, void* workspace, size_t workspace_bytes, so2_stream_t stream) {
   if (stages == 0 || (stages & ~(uint32_t)(SO2_STAGE_PREPARE | SO2_STAGE_FUSED))) return SO2_ERR_INVALID_ARGUMENT;
   so2_status st = check_desc(desc);
   if (st != SO2_OK) return st;
-  Kind kind = pick_kind(desc);
+  st = check_variant(desc, var);
+  if (st != SO2_OK) return st;
+  if (var->n_focus > 1 && !w_focus) return SO2_ERR_INVALID_ARGUMENT;
+  Kind kind = pick_kind(desc, var);
   if (kind == kNone) return SO2_ERR_UNSUPPORTED;
   st = check_box(box_host, desc->cutoff);
   if (st != SO2_OK) return st;
@@ -184,6 +210,10 @@ so2_status so2_attention_fwd_stages(uint32_t stages, const so2_attn_desc* desc, 
   a.dtype = desc->dtype;
   a.periodic = box_host != nullptr;
   for (int d = 0; d < 3; ++d) a.box[d] = box_host ? box_host[d] : 0.0f;
+  a.m_max = var->m_max < 0 ? desc->l_max : var->m_max;
+  a.n_focus = var->n_focus;
+  a.w_logit = w_logit;
+  a.w_focus = w_focus;
 
   if (kind == kMfma && !mfma_aligned(a)) return SO2_ERR_INVALID_ARGUMENT;
 
@@ -265,11 +295,22 @@ so2_status so2_attention_bwd(const so2_attn_desc* desc, const float* pos, const 
   a.dtype = desc->dtype;
   a.periodic = box_host != nullptr;
   for (int d = 0; d < 3; ++d) a.box[d] = box_host ? box_host[d] : 0.0f;
+  a.m_max = desc->l_max;
+  a.n_focus = 1;
   hipStream_t s = (hipStream_t)stream;
   st = launch_qk_proj(a, s);
   if (st != SO2_OK) return st;
   a.n_targets = desc->n_targets;
   return launch_attention_bwd(a, dy, dx, dpos, dw_q, dw_k, dw_rad, dw_so2, s);
+}
+
+so2_status so2_attention_fwd_stages(uint32_t stages, const so2_attn_desc* desc, const float* pos,
+                                    const float* box_host, const int32_t* row_ptr, const int32_t* col,
+                                    const void* x, const void* w_q, const void* w_k, const void* w_rad,
+                                    const void* w_so2, float* y, void* workspace, size_t workspace_bytes,
+                                    so2_stream_t stream) {
+  return attention_fwd_impl(stages, desc, &kBase, pos, box_host, row_ptr, col, x, w_q, w_k, w_rad, w_so2, nullptr,
+                            nullptr, y, workspace, workspace_bytes, stream);
 }
 
 so2_status so2_attention_fwd(const so2_attn_desc* desc, const float* pos, const float* box_host,
@@ -279,6 +320,27 @@ so2_status so2_attention_fwd(const so2_attn_desc* desc, const float* pos, const 
                              size_t workspace_bytes, so2_stream_t stream) {
   return so2_attention_fwd_stages(SO2_STAGE_PREPARE | SO2_STAGE_FUSED, desc, pos, box_host, row_ptr, col, x, w_q,
                                   w_k, w_rad, w_so2, y, workspace, workspace_bytes, stream);
+}
+
+size_t so2_attention_variant_workspace_bytes(const so2_attn_desc* desc, const so2_attn_variant* var) {
+  if (check_desc(desc) != SO2_OK || check_variant(desc, var) != SO2_OK) return 0;
+  Kind kind = pick_kind(desc, var);
+  if (kind == kNone) return 0;
+  return attn_layout(desc, kind).total;
+}
+
+int32_t so2_attention_variant_kernel_kind(const so2_attn_desc* desc, const so2_attn_variant* var) {
+  if (check_desc(desc) != SO2_OK || check_variant(desc, var) != SO2_OK) return 0;
+  return (int32_t)pick_kind(desc, var);
+}
+
+so2_status so2_attention_fwd_variant(const so2_attn_desc* desc, const so2_attn_variant* var, const float* pos,
+                                     const float* box_host, const int32_t* row_ptr, const int32_t* col,
+                                     const void* x, const void* w_q, const void* w_k, const void* w_rad,
+                                     const void* w_so2, const void* w_logit, const void* w_focus, float* y,
+                                     void* workspace, size_t workspace_bytes, so2_stream_t stream) {
+  return attention_fwd_impl(SO2_STAGE_PREPARE | SO2_STAGE_FUSED, desc, var, pos, box_host, row_ptr, col, x, w_q,
+                            w_k, w_rad, w_so2, w_logit, w_focus, y, workspace, workspace_bytes, stream);
 }
 
 so2_status so2_merged_rms_norm(const void* x, const float* gamma, void* y, int32_t n_atoms, int32_t l_max,

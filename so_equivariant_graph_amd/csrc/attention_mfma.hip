@@ -157,6 +157,7 @@ struct MfmaParams {
   float* stat_max;  // [n_targets][H]
   float* stat_inv;  // [n_targets][H]
   float* y;
+  const uint16_t* w_logit;  // [K][H] bf16 radial logit bias, or null
   uint32_t xp_bytes;  // extent of xp for its buffer descriptor
   uint32_t w_bytes;   // extent of w_so2
   int32_t n_targets, H, K, p;
@@ -210,6 +211,20 @@ template <int G>
 __device__ inline typename XVec<G>::type buffer_load_x(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   if constexpr (G == 4) return buffer_load16(r, voff, soff);
   else return buffer_load8(r, voff, soff);
+}
+
+// Radial logit bias of head h for an edge of length rho: sum_k phi_k(rho)
+// w_logit[k][h] (0 without the bias).
+__device__ inline float logit_bias(const MfmaParams& P, float rho, int h) {
+  if (!P.w_logit) return 0.0f;
+  const float step = P.cutoff / (float)(P.K - 1);
+  const float inv2s2 = 1.0f / (2.0f * step * step);
+  float b = 0.0f;
+  for (int kk = 0; kk < P.K; ++kk) {
+    const float dr = rho - step * (float)kk;
+    b += expf(-dr * dr * inv2s2) * bf16_to_float(P.w_logit[kk * P.H + h]);
+  }
+  return b;
 }
 
 // ---------------------------------------------------------------- prologue
@@ -306,24 +321,26 @@ __global__ void __launch_bounds__(256) attn_stats_kernel(MfmaParams P, int C) {
     const int nb = min(64, e1 - b0);
     // one edge per lane: source and envelope
     int jl = t;
-    float ul = 0.0f;
+    float ul = 0.0f, rl = 0.0f;
     if (lane < nb) {
       jl = P.col[b0 + lane];
       const EdgeGeo g = edge_geometry(P.pos, t, jl, P.periodic, P.box, P.cutoff);
       ul = envelope_u(g.s, g.t, P.p);
+      rl = g.rho;
     }
     // one edge per half-wave: logits per head and the online softmax (both
     // halves run every iteration, so that the shuffles see all 64 lanes)
     for (int i0 = 0; i0 < nb; i0 += 2 * kStatUnroll) {
       const int i = i0 + half;
       int j[kStatUnroll];
-      float u[kStatUnroll];
+      float u[kStatUnroll], rr[kStatUnroll];
       f32x4 kv[kStatUnroll];
 #pragma unroll
       for (int v = 0; v < kStatUnroll; ++v) {
         const int src = min(i + 2 * v, 63);
         j[v] = __shfl(jl, src, 64);
         u[v] = __shfl(ul, src, 64);
+        rr[v] = __shfl(rl, src, 64);
       }
 #pragma unroll
       for (int v = 0; v < kStatUnroll; ++v) kv[v] = *(const f32x4*)(P.k + (int64_t)j[v] * kC + 4 * c4);
@@ -332,7 +349,7 @@ __global__ void __launch_bounds__(256) attn_stats_kernel(MfmaParams P, int C) {
         float z = qv.x * kv[v].x + qv.y * kv[v].y + qv.z * kv[v].z + qv.w * kv[v].w;
         for (int off = 1; off < gl; off <<= 1) z += __shfl_xor(z, off, 64);
         if (i + 2 * v < nb) {
-          z *= inv_sqrt_d;
+          z = z * inv_sqrt_d + logit_bias(P, rr[v], h);
           if (z > m) {
             ssum = ssum * expf(m - z) + u[v];
             m = z;
@@ -1628,7 +1645,7 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
             const f32x4 qa = qv[cc], kb = kv[cc];
             z += qa.x * kb.x + qa.y * kb.y + qa.z * kb.z + qa.w * kb.w;
           }
-          z *= inv_sqrt_d;
+          z = z * inv_sqrt_d + logit_bias(P, rho, h);
           sW[h * CM + r] = u * expf(z - P.stat_max[(int64_t)t * H + h]) * P.stat_inv[(int64_t)t * H + h];
         }
       } else {
@@ -1860,6 +1877,7 @@ MfmaParams make_params(const AttnArgs& a) {
   P.stat_max = stats;
   P.stat_inv = stats + (size_t)a.n_targets * a.H;
   P.y = a.y;
+  P.w_logit = (const uint16_t*)a.w_logit;
   P.xp_bytes = (uint32_t)((uint64_t)a.n_atoms * pair_off(a.L + 1) * kC * 4);
   P.w_bytes = (uint32_t)(wf_entries(a.L) * 2);
   P.n_targets = a.n_targets;

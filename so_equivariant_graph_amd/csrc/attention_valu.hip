@@ -45,7 +45,24 @@ struct ValuParams {
   uint32_t flags;
   int32_t periodic;
   float box[3];
+  int32_t m_max, n_focus;
+  const void* w_logit;  // [K][H] or null
+  const void* w_focus;  // [C] when n_focus > 1
 };
+
+// Radial logit bias of head h: sum_k phi_k(rho) w_logit[k][h] (0 without it).
+template <typename T>
+__device__ inline float logit_bias(const ValuParams& P, float rho, int h) {
+  if (!P.w_logit) return 0.0f;
+  const float step = P.cutoff / (float)(P.K - 1);
+  const float inv2s2 = 1.0f / (2.0f * step * step);
+  float b = 0.0f;
+  for (int kk = 0; kk < P.K; ++kk) {
+    const float dr = rho - step * (float)kk;
+    b += expf(-dr * dr * inv2s2) * load_as_float((const T*)P.w_logit, (int64_t)kk * P.H + h);
+  }
+  return b;
+}
 
 __device__ inline float block_reduce_max(float v, float* red) {
   int t = threadIdx.x;
@@ -115,7 +132,7 @@ __global__ void __launch_bounds__(kValuThreads) attn_valu_kernel(ValuParams P) {
       float u = envelope_u(geo.s, geo.t, P.p);
       float z = 0.0f;
       for (int c = h * d; c < (h + 1) * d; ++c) z += s_q[c] * P.k[(int64_t)j * C + c];
-      z *= inv_sqrt_d;
+      z = z * inv_sqrt_d + logit_bias<T>(P, geo.rho, h);
       if (z > m) {
         s = s * expf(m - z) + u;
         m = z;
@@ -180,7 +197,7 @@ __global__ void __launch_bounds__(kValuThreads) attn_valu_kernel(ValuParams P) {
     for (int h = t; h < H; h += kValuThreads) {
       float z = 0.0f;
       for (int c = h * d; c < (h + 1) * d; ++c) z += s_q[c] * P.k[(int64_t)j * C + c];
-      z *= inv_sqrt_d;
+      z = z * inv_sqrt_d + logit_bias<T>(P, rho, h);
       s_w[h] = u * expf(z - s_M[h]) * s_S[h];
     }
     __syncthreads();
@@ -196,30 +213,38 @@ __global__ void __launch_bounds__(kValuThreads) attn_valu_kernel(ValuParams P) {
       s_xt[a] = v * s_g[c];
     }
     __syncthreads();
-    // per-m map: one output row per wave lane group, lanes split the inputs
+    // per-m map: one output row per wave lane group, lanes split the inputs.
+    // With F focus streams, stream f = cp / Cf owns its stack of maps over
+    // its Cf channels (stack f at f * so2_w1_offset(L, Cf, m_max + 1));
+    // orders above m_max give 0.
     {
       const int lane = t & 63;
       const int wave = t >> 6;
+      const int Cf = C / P.n_focus;
+      const int64_t stack = so2_w1_offset(L, Cf, P.m_max + 1);
       for (int o = wave; o < nc * C; o += kValuThreads / 64) {
         int comp = o / C, cp = o % C;
         int l = (int)sqrtf((float)comp + 0.5f);
         int m = comp - l * l - l;
         int am = m < 0 ? -m : m;
+        const int f = cp / Cf, cpf = cp - f * Cf;
+        const T* ws = w_so2 + f * stack;
         float acc = 0.0f;
-        if (am == 0) {
-          const int64_t K0 = (int64_t)(L + 1) * C;
-          const T* row = w_so2 + ((int64_t)l * C + cp) * K0;
+        if (am > P.m_max) {
+        } else if (am == 0) {
+          const int64_t K0 = (int64_t)(L + 1) * Cf;
+          const T* row = ws + ((int64_t)l * Cf + cpf) * K0;
           for (int kk = lane; kk < K0; kk += 64) {
-            int lp = kk / C, c = kk % C;
+            int lp = kk / Cf, c = f * Cf + kk % Cf;
             acc += load_as_float(row, kk) * s_xt[(lp * lp + lp) * C + c];
           }
         } else {
-          const int64_t Km = (int64_t)(L + 1 - am) * C;
-          const int64_t off1 = so2_w1_offset(L, C, am);
-          const T* row1 = w_so2 + off1 + ((int64_t)(l - am) * C + cp) * Km;
+          const int64_t Km = (int64_t)(L + 1 - am) * Cf;
+          const int64_t off1 = so2_w1_offset(L, Cf, am);
+          const T* row1 = ws + off1 + ((int64_t)(l - am) * Cf + cpf) * Km;
           const T* row2 = row1 + Km * Km;
           for (int kk = lane; kk < Km; kk += 64) {
-            int lp = kk / C + am, c = kk % C;
+            int lp = kk / Cf + am, c = f * Cf + kk % Cf;
             float xp = s_xt[(lp * lp + lp + am) * C + c];
             float xm = s_xt[(lp * lp + lp - am) * C + c];
             float w1 = load_as_float(row1, kk), w2 = load_as_float(row2, kk);
@@ -232,6 +257,29 @@ __global__ void __launch_bounds__(kValuThreads) attn_valu_kernel(ValuParams P) {
       }
     }
     __syncthreads();
+    // cross-focus softmax: pi_f from the streams' invariant l = 0 message,
+    // score_f = sum_{c in f} w_focus[c] yt[(0,0), c]; stream f scaled by pi_f
+    if (P.n_focus > 1) {
+      const int F = P.n_focus, Cf = C / F;
+      if (t == 0) {
+        float mx = -INFINITY;
+        for (int f = 0; f < F; ++f) {
+          float sc = 0.0f;
+          for (int c = f * Cf; c < (f + 1) * Cf; ++c) sc += load_as_float((const T*)P.w_focus, c) * s_yt[c];
+          s_red[f] = sc;
+          mx = fmaxf(mx, sc);
+        }
+        float sum = 0.0f;
+        for (int f = 0; f < F; ++f) {
+          s_red[f] = expf(s_red[f] - mx);
+          sum += s_red[f];
+        }
+        for (int f = 0; f < F; ++f) s_red[f] /= sum;
+      }
+      __syncthreads();
+      for (int a = t; a < nc * C; a += kValuThreads) s_yt[a] *= s_red[(a % C) / Cf];
+      __syncthreads();
+    }
     // rotate back and accumulate: acc[(l,m'),c] += w^{h(c)} sum_m D^l[m][m'] yt[(l,m),c]
     for (int a = t; a < nc * C; a += kValuThreads) {
       int comp = a / C, c = a % C;
@@ -282,6 +330,10 @@ so2_status launch_attention_valu(const AttnArgs& a, hipStream_t stream) {
   P.flags = a.flags;
   P.periodic = a.periodic;
   for (int d = 0; d < 3; ++d) P.box[d] = a.box[d];
+  P.m_max = a.m_max;
+  P.n_focus = a.n_focus;
+  P.w_logit = a.w_logit;
+  P.w_focus = a.w_focus;
   const size_t smem = valu_smem_bytes(a.L, a.C, a.H);
   if (a.n_targets == 0) return SO2_OK;
   if (a.dtype == SO2_BF16) {

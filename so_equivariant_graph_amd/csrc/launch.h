@@ -48,6 +48,10 @@ struct AttnArgs {
   int32_t dtype;
   int32_t periodic;
   float box[3];
+  // variants (the base layer: m_max = L, n_focus = 1, no logit bias)
+  int32_t m_max, n_focus;
+  const void* w_logit;  // [K][H] or null
+  const void* w_focus;  // [C] when n_focus > 1
 };
 
 // q/k projection of the l = 0 slice (attention_prep.hip).

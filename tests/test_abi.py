@@ -298,3 +298,29 @@ def test_backward_errors_before_launch():
     big = _desc(l_max=6, channels=512, heads=8)
     assert lib.so2_attention_bwd_workspace_bytes(ctypes.byref(big)) == 0
     assert call(big, 1 << 40) == sea.SO2_ERR_UNSUPPORTED
+
+
+def test_variant_counts_and_errors():
+    lib = sea.load_library()
+    for L, C, m, F in ((4, 128, -1, 1), (4, 128, 2, 1), (3, 12, 1, 3), (6, 8, 0, 2)):
+        assert lib.so2_weight_count_variant(L, C, m, F) == so2_weight_count(L, C, None if m < 0 else m, F)
+    assert lib.so2_weight_count_variant(4, 128, 5, 1) == -1
+    assert lib.so2_weight_count_variant(4, 128, 2, 3) == -1  # 3 does not divide 128
+    d = _desc()
+    bad = [sea.AttnVariant(3, 1), sea.AttnVariant(-2, 1), sea.AttnVariant(-1, 0), sea.AttnVariant(-1, 3)]
+    for v in bad:
+        assert lib.so2_attention_variant_workspace_bytes(ctypes.byref(d), ctypes.byref(v)) == 0
+        args = [FAKE, ctypes.c_void_p(0)] + [FAKE] * 10 + [ctypes.c_void_p(1 << 30)]
+        assert lib.so2_attention_fwd_variant(ctypes.byref(d), ctypes.byref(v), *args, 1 << 40, None) == \
+            sea.SO2_ERR_INVALID_ARGUMENT
+    v = sea.AttnVariant(-1, 2)
+    args = [FAKE, ctypes.c_void_p(0)] + [FAKE] * 8 + [ctypes.c_void_p(0)] + [FAKE, ctypes.c_void_p(1 << 30)]
+    assert lib.so2_attention_fwd_variant(ctypes.byref(d), ctypes.byref(v), *args, 1 << 40, None) == \
+        sea.SO2_ERR_INVALID_ARGUMENT  # w_focus missing
+    mf = _desc(l_max=4, channels=128, heads=8, n_rbf=16, dtype=sea.SO2_BF16)
+    assert lib.so2_attention_variant_kernel_kind(ctypes.byref(mf), ctypes.byref(sea.AttnVariant(-1, 1))) == \
+        sea.KERNEL_MFMA
+    assert lib.so2_attention_variant_kernel_kind(ctypes.byref(mf), ctypes.byref(sea.AttnVariant(2, 1))) == \
+        sea.KERNEL_VALU
+    assert lib.so2_attention_variant_kernel_kind(ctypes.byref(mf), ctypes.byref(sea.AttnVariant(-1, 2))) == \
+        sea.KERNEL_VALU
