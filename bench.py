@@ -47,12 +47,12 @@ PEAK_HBM_GBS = 8000.0
 # for the kernel sources it was taken on: their digest is stored with it and a
 # mismatch reports null.
 MEASURED_TRAFFIC = {
-    # FETCH_SIZE 2588185 KiB x 2.00 (a 1 GiB copy reads as 524302 KiB), WRITE_SIZE
-    # 147800 KiB x 1.00 (the copy writes read exactly 1048576 KiB); mean of 7 launches.
-    "small_molecules": {
-        "sources_sha256": "e94fe024fc58d120beb9358742307a2e9d96a629bfedec38354fb490bc40181f",
-        "fetch_bytes": 5300458768,
-        "write_bytes": 151347200,
+    # FETCH_SIZE 115157223 KiB x 2.00 (a 1 GiB copy reads as 524305 KiB), WRITE_SIZE
+    # 2609650 KiB x 1.00 (the copy writes read exactly 1048576 KiB); mean of 5 launches.
+    "water_100k": {
+        "sources_sha256": "a7cd3845743c5a9824f0569dc43fbccdf484cdb67be309da127486ba87624d18",
+        "fetch_bytes": 235834439553,
+        "write_bytes": 2672282035,
     },
 }
 KERNEL_SOURCES = ("attention_mfma.hip", "wigner.h", "common.h", "launch.h")
