@@ -250,9 +250,10 @@ so2_status so2_attention_fwd_variant(const so2_attn_desc* desc, const so2_attn_v
  * Potentials with EMFA SO(2) Convolution", technical summary, section 2.2:
  * conservative training differentiates the energy-to-force path).  Given
  * dy = dL/dy, returns dL/dx, dL/dpos and dL/dW for the same forward (same
- * descriptor, graph and inputs).  Like the forward it keeps no per-edge
- * tensor: every edge is recomputed, and only per-(atom, head) softmax
- * statistics live between its sweeps, so memory stays O(n_atoms).
+ * descriptor, graph and inputs).  Memory stays linear in the atom count:
+ * per-edge tensors exist only for one batch of edges at a time (64 per
+ * target, between 4096 and 32768 edges, fixed by n_targets), and only the
+ * softmax statistics and head sums per (target, head) live across batches.
  *   dy        [n_targets][(L+1)^2][C] fp32
  *   dx        [n_atoms][(L+1)^2][C] fp32, written (sources and targets)
  *   dpos      [n_atoms][3] fp32, written; minus the forces when L is an
@@ -262,15 +263,19 @@ so2_status so2_attention_fwd_variant(const so2_attn_desc* desc, const so2_attn_v
  *             written; each may be NULL (not computed: the force-only path
  *             skips the weight reductions)
  *   workspace >= so2_attention_bwd_workspace_bytes(desc) bytes
- * Arithmetic: fp32 on the vector ALUs for fp32 and bf16 inputs (bf16 values
- * are widened exactly).  Contributions to dx of sources, dpos, dk and the
+ * Arithmetic: fp32 for fp32 and bf16 inputs (bf16 values are widened
+ * exactly); the three uses of the per-m map (the forward map recomputed,
+ * its transpose, the weight gradient) are fp32 GEMMs over each batch on the
+ * matrix cores.  Contributions to dx of sources, dpos, dq, dk and the
  * weights are summed with fp32 atomics, so the low bits vary between runs.
- * Shapes: any L <= 6 whose per-target working set (about 5 (L+1)^2 C
- * floats) fits 160 KB of LDS (C <= 128 at L = 6, C <= 256 at L = 4), else
- * UNSUPPORTED.  A target whose envelopes are all 0 (edges
- * exactly at the cutoff only) has y = 0 and gets no gradient.
- * Errors: INVALID_ARGUMENT, UNSUPPORTED, BOX, WORKSPACE, DEVICE.
- * Asynchronous on `stream`; no device allocation.
+ * Shapes: L <= 6, C <= 256, H <= 64, else UNSUPPORTED.  A target whose
+ * envelopes are all 0 (edges exactly at the cutoff only) has y = 0 and
+ * gets no gradient.
+ * Errors: INVALID_ARGUMENT (also row_ptr[n_targets] < row_ptr[0]),
+ * UNSUPPORTED, BOX, WORKSPACE, DEVICE.
+ * Stream: the call reads row_ptr[0] and row_ptr[n_targets] back to the host
+ * to plan its batches, which synchronises `stream` once; everything else is
+ * enqueued on `stream`.  No device allocation.
  * ---------------------------------------------------------------------- */
 size_t so2_attention_bwd_workspace_bytes(const so2_attn_desc* desc);
 so2_status so2_attention_bwd(const so2_attn_desc* desc, const float* pos, const float* box_host,

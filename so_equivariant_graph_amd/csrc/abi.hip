@@ -244,7 +244,7 @@ static so2_status bwd_layout(const so2_attn_desc* d, AttnLayout* out) {
   L.k = off;
   off += align256(sizeof(float) * (size_t)d->n_atoms * d->channels);
   L.scratch = off;
-  L.scratch_bytes = bwd_scratch_bytes(d->n_atoms, d->n_targets, d->l_max, d->channels);
+  L.scratch_bytes = bwd_scratch_bytes(d->n_atoms, d->n_targets, d->l_max, d->channels, d->heads, d->n_rbf);
   off += align256(L.scratch_bytes);
   L.total = off;
   *out = L;

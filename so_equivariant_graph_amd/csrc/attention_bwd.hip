@@ -1,4 +1,4 @@
-// Backward of the fused SO(2) attention forward, fp32 on the vector ALUs.
+// Backward of the fused SO(2) attention forward, fp32.
 //
 // For a scalar loss L with upstream gradient dy = dL/dy (one row per
 // target), the gradients of L with respect to the node features x, the
@@ -9,19 +9,31 @@
 // Accuracy-Cost Frontier of Interatomic Potentials with EMFA SO(2)
 // Convolution", technical summary, section 2.2).
 //
-// Nothing per edge is stored: like the forward, one workgroup per target
-// recomputes every edge (rotation, gate, per-m map, rotation back), and
-// only the softmax statistics per (target, head) are kept between sweeps:
-//   sweep 0   running max M and normaliser sum_j u_ij exp(z_ij - M);
-//   sweep 1   per edge v_ij and s_ij^h = <dy_i, v_ij> over the channels of
-//             head h; Sbar^h = sum_j a_ij^h s_ij^h;
-//   sweep 2   per edge, again v_ij and s_ij^h, then
+// The per-m map is the same dense map for every edge, so its three uses in
+// the backward are GEMMs over a batch of edges, on the matrix cores in fp32
+// (v_mfma_f32_16x16x4_f32):
+//   Y  = X  B_m^T      (the forward map, recomputed),
+//   dX = dY B_m        (its transpose applied to the output gradient),
+//   dB_m += dY^T X     (the weight gradient, a sum over edges),
+// where an edge's row X holds its rotated, gated input in the block layout
+// [m = 0: (l, c)], [m = 1: (sign, l, c)], ... and B_m is W0 for m = 0 and
+// [[W1, -W2], [W2, W1]] for m >= 1 (the complex product as one real matrix).
+// Everything per edge that is not a GEMM (frame, Wigner-D, gate, rotations,
+// softmax terms, the direction gradient) runs in per-edge kernels, one wave
+// per edge.  Per-edge tensors exist only for one batch of edges at a time
+// (a fixed capacity set from the target count), so memory is linear in the
+// atom count plus a constant; only the softmax statistics per (target, head)
+// and the head sums Sbar below live across batches:
+//   statistics  running max M and normaliser sum_j u_ij exp(z_ij - M);
+//   pass 1      per edge v_ij = D^T Y_ij and s_ij^h = <dy_i, v_ij> over the
+//               channels of head h; Sbar_i^h = sum_j a_ij^h s_ij^h;
+//   pass 2      per edge, again v and s, then
 //     dL/dz^h = a^h (s^h - Sbar^h),  dL/du = sum_h abar^h (s^h - Sbar^h)
 //     (abar = a / u = exp(z - M) / normaliser),
-//     dv = a (.) dy_i,  dyt = D dv,  dW_so2 += per-m outer products of dyt
-//     and xt,  dxt = W^T dyt (the transposed per-m map),
+//     dv = a (.) dy_i,  dyt = D dv,  then the GEMMs dB_m += dyt^T xt and
+//     dxt = map^T(dyt),  and per edge
 //     dg[c] = sum_(l,m) dxt xh (xh = D x_j before the gate),
-//     dx_j += D^T (dxt (.) g),  dW_rad += phi dg,
+//     dx_j += D^T (dxt (.) g),  dW_rad += phi dg (a GEMM over the batch),
 //     d|r| = sum_c dg[c] dg_c/d|r| + dL/du du/d|r|,
 //     direction: a rotation w of the edge direction r_hat -> r_hat + w x
 //     r_hat is a frame R exp(-[w]x), so D -> D (I - sum_a w_a J_a) with J_a
@@ -31,10 +43,13 @@
 //       dL/dr = (dL/dw) x r_hat / |r| + d|r| r_hat,
 //     added to dpos[j] and taken from dpos[i];
 //     dq_i += dz k_j / sqrt(d), dk_j += dz q_i / sqrt(d).
-// A second kernel takes dq and dk through the projections of the l = 0
-// slice: dx[.,0,.] += dq W_q^T + dk W_k^T, dW_q = x0^T dq, dW_k = x0^T dk.
-// Gradients that several workgroups add to (dx of sources, dpos, dk and the
-// weights) use fp32 atomics, so their summation order varies between runs.
+// When every edge fits one batch, pass 2 reuses pass 1's batch; otherwise
+// it recomputes each batch (forward map included), the last batch of pass
+// 1 first.  A last kernel takes dq and dk through the projections of the
+// l = 0 slice: dx[., 0, .] += dq W_q^T + dk W_k^T, dW_q = x0^T dq,
+// dW_k = x0^T dk.  Sums that several edges add to (dx of sources, dpos, dq,
+// dk, Sbar, the weight gradients) use fp32 atomics, so their summation
+// order varies between runs.
 #include <math.h>
 
 #include <algorithm>
@@ -47,480 +62,692 @@ namespace so2 {
 
 namespace {
 
-constexpr int kBwdThreads = 256;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kLane = 64;       // per-edge and per-target kernels: one wave per block
+constexpr int kMaxBwdHeads = 64;  // heads are held one per lane
+constexpr int kScal = 12;       // per-edge scalars (EdgeBufs::sc)
+constexpr int kGridCap = 16384; // blocks of a grid-stride per-edge launch
+
+// ---------------------------------------------------------------- layouts
+
+// Width of block m of an edge row: (L+1) C for m = 0, 2 (L+1-m) C for m >= 1.
+__host__ __device__ inline int blk_width(int L, int C, int m) { return (m == 0 ? 1 : 2) * (L + 1 - m) * C; }
+// Column of block m in an edge row.
+__host__ __device__ inline int blk_off(int L, int C, int m) {
+  int off = 0;
+  for (int q = 0; q < m; ++q) off += blk_width(L, C, q);
+  return off;
+}
+// Offset of B_m (blk_width^2 floats, row-major [out][in]) in the B array.
+__host__ __device__ inline int64_t bmat_off(int L, int C, int m) {
+  int64_t off = 0;
+  for (int q = 0; q < m; ++q) off += (int64_t)blk_width(L, C, q) * blk_width(L, C, q);
+  return off;
+}
+// Column of component (l, mm) (|mm| <= l) for channel 0: block |mm|, sign
+// half for mm < 0, degree l - |mm| inside it.
+__device__ inline int comp_col(int L, int C, int l, int mm) {
+  const int m = mm < 0 ? -mm : mm;
+  return blk_off(L, C, m) + (mm < 0 ? (L + 1 - m) * C : 0) + (l - m) * C;
+}
+
+// Per-edge tensors of one batch (capacity cap edges), fp32.
+struct EdgeBufs {
+  float* xt;   // [cap][nc C]  xt, then dxt (block layout)
+  float* yt;   // [cap][nc C]  yt, then dyt (block layout)
+  float* D;    // [cap][wig_total(L)]
+  float* g;    // [cap][C]  radial gate
+  float* gp;   // [cap][C]  d gate / d|r|
+  float* dg;   // [cap][C]  dL/d gate
+  float* phi;  // [cap][K]  radial basis (times u with the envelope flag)
+  float* a;    // [cap][H]  softmax weight u exp(z - M) / normaliser
+  float* ab;   // [cap][H]  a / u
+  float* sc;   // [cap][kScal]: |r|, u, du/d|r|, r_hat (3), dL/du, <dv, J_a v> (3)
+  int32_t* tgt;  // [cap]
+};
 
 struct BwdParams {
   const float* pos;
   const int32_t* row_ptr;
   const int32_t* col;
   const void* x;
-  const void* w_q;
-  const void* w_k;
   const void* w_rad;
-  const void* w_so2;
   const float* dy;
-  const float* q;    // [n_atoms][C]
-  const float* k;    // [n_atoms][C]
-  const float* gen;  // [3][wig_total(L)] rotation generators
-  float* dq;         // [n_targets][C]
-  float* dk;         // [n_atoms][C]
+  const float* q;     // [n_atoms][C]
+  const float* k;     // [n_atoms][C]
+  const float* gen;   // [3][wig_total(L)] rotation generators
+  float* smax;  // [n_targets][H]
+  float* sinv;  // [n_targets][H] 1 / normaliser (0 if it is 0)
+  float* sbar;        // [n_targets][H]
+  float* dq;          // [n_targets][C]
+  float* dk;          // [n_atoms][C]
   float* dx;
   float* dpos;
-  float* dw_rad;  // or null
-  float* dw_so2;  // or null
-  int32_t n_atoms, n_targets, L, C, H, K, p;
+  EdgeBufs b;
+  int64_t e0;  // first edge of the batch (CSR index)
+  int32_t nb;  // edges in the batch
+  int32_t n_targets, C, H, K, p;
   float cutoff;
   uint32_t flags;
   int32_t periodic;
   float box[3];
 };
 
-// LDS layout of the backward kernel, in floats.
-struct BwdLds {
-  int nc, C, H, K, nwig;
-  int G, XH, XT, Y, V, D, DJ, J, g, gp, dg, q, dq, phi, dwr, M, S, a, ab, s, sbar, red, total;
-  __host__ __device__ BwdLds(int L, int C_, int H_, int K_) : nc((L + 1) * (L + 1)), C(C_), H(H_), K(K_) {
-    nwig = (wig_total(L) + 3) & ~3;
-    int o = 0;
-    G = o;  // dy_i
-    o += nc * C;
-    XH = o;  // D x_j
-    o += nc * C;
-    XT = o;  // gated
-    o += nc * C;
-    Y = o;  // yt, then dyt
-    o += nc * C;
-    V = o;  // v, then dxt
-    o += nc * C;
-    D = o;
-    o += nwig;
-    DJ = o;  // D J_a
-    o += 3 * nwig;
-    J = o;  // generators
-    o += 3 * nwig;
-    g = o;
-    o += C;
-    gp = o;  // dg/d|r|
-    o += C;
-    dg = o;
-    o += C;
-    q = o;
-    o += C;
-    dq = o;
-    o += C;
-    phi = o;  // phi_k (times u with the envelope flag)
-    o += (K + 3) & ~3;
-    dwr = o;  // dW_rad of this target
-    o += K * C;
-    M = o;
-    o += H;
-    S = o;  // 1 / normaliser
-    o += H;
-    a = o;
-    o += H;
-    ab = o;
-    o += H;
-    s = o;
-    o += H;
-    sbar = o;
-    o += H;
-    red = o;  // scalars: [0] d|r| (radial part), [1..3] dir1, [4..6] dir2, [8..] geometry
-    o += 32;
-    total = o;
-  }
-};
-
-__device__ inline void atomic_add_f(float* p, float v) { atomicAdd(p, v); }
-
-// Sum v over the wave and add it to *dst from lane 0 (LDS atomics).
-__device__ inline void wave_add(float* dst, float v) {
+__device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  if ((threadIdx.x & 63) == 0) atomicAdd(dst, v);
+  return v;
 }
 
-template <typename T>
-__global__ void __launch_bounds__(kBwdThreads) attn_bwd_kernel(BwdParams P) {
-  const int i = blockIdx.x;
-  const int t = threadIdx.x;
-  const int L = P.L, C = P.C, H = P.H, K = P.K;
-  const int nc = n_comp(L);
-  const int d = C / H;
+// ---------------------------------------------------------------- statistics
+
+// One wave per target: for every head the running max of the logits and the
+// normaliser sum_j u_ij exp(z_ij - max), over the target's edges in order.
+__global__ void __launch_bounds__(kLane) bwd_stats_kernel(BwdParams P) {
+  __shared__ float zs[kMaxBwdHeads];
+  const int lane = threadIdx.x;
+  const int C = P.C, H = P.H, d = C / H;
   const float inv_sqrt_d = 1.0f / sqrtf((float)d);
-  const int e0 = P.row_ptr[i], e1 = P.row_ptr[i + 1];
-  float* dqo = P.dq + (int64_t)i * C;
-  if (e0 == e1) {
-    for (int c = t; c < C; c += kBwdThreads) dqo[c] = 0.0f;
-    return;
+  for (int i = blockIdx.x; i < P.n_targets; i += gridDim.x) {
+    float m = -INFINITY, sum = 0.0f;
+    for (int e = P.row_ptr[i]; e < P.row_ptr[i + 1]; ++e) {
+      const int j = P.col[e];
+      if (lane < H) zs[lane] = 0.0f;
+      __syncthreads();
+      for (int c = lane; c < C; c += kLane) atomicAdd(&zs[c / d], P.q[(int64_t)i * C + c] * P.k[(int64_t)j * C + c]);
+      __syncthreads();
+      if (lane < H) {
+        const EdgeGeo geo = edge_geometry(P.pos, i, j, P.periodic, P.box, P.cutoff);
+        const float u = envelope_u(geo.s, geo.t, P.p);
+        const float z = zs[lane] * inv_sqrt_d;
+        if (z > m) {
+          sum = sum * expf(m - z) + u;
+          m = z;
+        } else {
+          sum += u * expf(z - m);
+        }
+      }
+      __syncthreads();
+    }
+    if (lane < H) {
+      P.smax[(int64_t)i * H + lane] = m;
+      P.sinv[(int64_t)i * H + lane] = sum > 0.0f ? 1.0f / sum : 0.0f;
+    }
   }
-  extern __shared__ float sm[];
-  const BwdLds Ly(L, C, H, K);
-  float* sG = sm + Ly.G;
-  float* sXH = sm + Ly.XH;
-  float* sXT = sm + Ly.XT;
-  float* sY = sm + Ly.Y;
-  float* sV = sm + Ly.V;
-  float* sD = sm + Ly.D;
-  float* sDJ = sm + Ly.DJ;
-  float* sJ = sm + Ly.J;
-  float* sg = sm + Ly.g;
-  float* sgp = sm + Ly.gp;
-  float* sdg = sm + Ly.dg;
-  float* sq = sm + Ly.q;
-  float* sdq = sm + Ly.dq;
-  float* sphi = sm + Ly.phi;
-  float* sdwr = sm + Ly.dwr;
-  float* sM = sm + Ly.M;
-  float* sS = sm + Ly.S;
-  float* sa = sm + Ly.a;
-  float* sab = sm + Ly.ab;
-  float* ss = sm + Ly.s;
-  float* ssb = sm + Ly.sbar;
-  float* sred = sm + Ly.red;
-  const int nw = wig_total(L);
+}
+
+// ---------------------------------------------------------------- per-edge kernels
+
+// D^0 .. D^L of the edge into LDS (sD, wig_total(L) floats) from its frame:
+// D^1 directly, then one degree at a time over the lanes.
+template <int L>
+__device__ inline void edge_wigner(const float* rh, float* sD) {
+  const int lane = threadIdx.x;
+  float R[9], D1[9];
+  edge_frame(rh[0], rh[1], rh[2], R);
+  wigner_l1(R, D1);
+  if (lane == 0) sD[0] = 1.0f;
+  if (L >= 1 && lane < 9) sD[wig_offset(1) + lane] = D1[lane];
+  __syncthreads();
+#pragma unroll
+  for (int l = 2; l <= L; ++l) {
+    const int n = 2 * l + 1;
+    for (int q = lane; q < n * n; q += kLane)
+      sD[wig_offset(l) + q] = wigner_entry(l, q / n - l, q % n - l, sD + wig_offset(1), sD + wig_offset(l - 1));
+    __syncthreads();
+  }
+}
+
+// Largest target i with row_ptr[i] <= e (the target of CSR edge e).
+__device__ inline int edge_target(const int32_t* row_ptr, int n_targets, int64_t e) {
+  int lo = 0, hi = n_targets;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (row_ptr[mid] <= e) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Pass-1 preparation of every edge of the batch: target, geometry, frame,
+// Wigner-D, radial basis, gate and its |r| derivative, softmax weights, and
+// xt = g (.) D x_j in the block layout.
+template <int L, typename T>
+__global__ void __launch_bounds__(kLane) bwd_prep_kernel(BwdParams P) {
+  constexpr int nw = wig_total(L);
+  constexpr int nc = n_comp(L);
+  __shared__ float sD[nw];
+  __shared__ float sphi[64];
+  __shared__ float zs[kMaxBwdHeads];
+  const int lane = threadIdx.x;
+  const int C = P.C, H = P.H, K = P.K, d = C / H;
+  const float inv_sqrt_d = 1.0f / sqrtf((float)d);
   const float rc = P.cutoff;
   const bool radial = !(P.flags & SO2_FLAG_NO_RADIAL);
   const bool rbf_env = (P.flags & SO2_FLAG_RBF_ENVELOPE) != 0;
   const float mu_step = rc / (float)(K - 1);
   const float inv2s2 = 1.0f / (2.0f * mu_step * mu_step);
-
-  for (int a = t; a < nc * C; a += kBwdThreads) sG[a] = P.dy[(int64_t)i * nc * C + a];
-  for (int a = t; a < 3 * nw; a += kBwdThreads) sJ[(a / nw) * Ly.nwig + a % nw] = P.gen[a];
-  for (int c = t; c < C; c += kBwdThreads) {
-    sq[c] = P.q[(int64_t)i * C + c];
-    sdq[c] = 0.0f;
-  }
-  for (int a = t; a < K * C; a += kBwdThreads) sdwr[a] = 0.0f;
-  for (int h = t; h < H; h += kBwdThreads) ssb[h] = 0.0f;
-
-  // ---- sweep 0: softmax statistics (per head, online over the edges)
-  for (int h = t; h < H; h += kBwdThreads) {
-    float m = -INFINITY, sum = 0.0f;
-    for (int e = e0; e < e1; ++e) {
-      const int j = P.col[e];
-      const EdgeGeo geo = edge_geometry(P.pos, i, j, P.periodic, P.box, rc);
-      const float u = envelope_u(geo.s, geo.t, P.p);
-      float z = 0.0f;
-      for (int c = h * d; c < (h + 1) * d; ++c) z += P.q[(int64_t)i * C + c] * P.k[(int64_t)j * C + c];
-      z *= inv_sqrt_d;
-      if (z > m) {
-        sum = sum * expf(m - z) + u;
-        m = z;
-      } else {
-        sum += u * expf(z - m);
+  const T* x = (const T*)P.x;
+  const T* wr = (const T*)P.w_rad;
+  const EdgeBufs& B = P.b;
+  for (int e = blockIdx.x; e < P.nb; e += gridDim.x) {
+    const int64_t ge = P.e0 + e;
+    const int i = edge_target(P.row_ptr, P.n_targets, ge);
+    const int j = P.col[ge];
+    const EdgeGeo geo = edge_geometry(P.pos, i, j, P.periodic, P.box, rc);
+    const float rho = geo.rho;
+    const float u = envelope_u(geo.s, geo.t, P.p);
+    const float dudr = envelope_du(geo.s, geo.t, P.p) / rc;
+    const float inv = rho > 0.0f ? 1.0f / rho : 0.0f;
+    const float rh[3] = {geo.r[0] * inv, geo.r[1] * inv, geo.r[2] * inv};
+    edge_wigner<L>(rh, sD);
+    for (int q = lane; q < nw; q += kLane) B.D[(int64_t)e * nw + q] = sD[q];
+    for (int kk = lane; kk < K; kk += kLane) {
+      const float dr = rho - mu_step * (float)kk;
+      const float ph = expf(-dr * dr * inv2s2);
+      if (kk < 64) sphi[kk] = ph;
+      B.phi[(int64_t)e * K + kk] = rbf_env ? ph * u : ph;
+    }
+    if (lane < H) zs[lane] = 0.0f;
+    if (lane == 0) {
+      float* sc = B.sc + (int64_t)e * kScal;
+      sc[0] = rho;
+      sc[1] = u;
+      sc[2] = dudr;
+      sc[3] = rh[0];
+      sc[4] = rh[1];
+      sc[5] = rh[2];
+      B.tgt[e] = i;
+    }
+    __syncthreads();
+    float* xte = B.xt + (int64_t)e * nc * C;
+    for (int c = lane; c < C; c += kLane) {
+      float g = 1.0f, gp = 0.0f;
+      if (radial) {
+        float g0 = 0.0f, gd = 0.0f;
+        for (int kk = 0; kk < K; ++kk) {
+          const float dr = rho - mu_step * (float)kk;
+          const float ph = kk < 64 ? sphi[kk] : expf(-dr * dr * inv2s2);
+          const float w = load_as_float(wr, (int64_t)kk * C + c);
+          g0 += ph * w;
+          gd += -dr * 2.0f * inv2s2 * ph * w;
+        }
+        g = rbf_env ? g0 * u : g0;
+        gp = rbf_env ? gd * u + g0 * dudr : gd;
+      }
+      B.g[(int64_t)e * C + c] = g;
+      B.gp[(int64_t)e * C + c] = gp;
+      atomicAdd(&zs[c / d], P.q[(int64_t)i * C + c] * P.k[(int64_t)j * C + c]);
+      const T* xj = x + (int64_t)j * nc * C + c;
+#pragma unroll
+      for (int l = 0; l <= L; ++l) {
+        const int n = 2 * l + 1;
+        float xv[2 * L + 1];
+#pragma unroll
+        for (int b = 0; b < n; ++b) xv[b] = load_as_float(xj, (int64_t)(l * l + b) * C);
+        const float* Dl = sD + wig_offset(l);
+#pragma unroll
+        for (int mr = 0; mr < n; ++mr) {
+          float v = 0.0f;
+#pragma unroll
+          for (int b = 0; b < n; ++b) v += Dl[mr * n + b] * xv[b];
+          xte[comp_col(L, C, l, mr - l) + c] = g * v;
+        }
       }
     }
-    sM[h] = m;
-    sS[h] = sum > 0.0f ? 1.0f / sum : 0.0f;
-  }
-  __syncthreads();
-  bool degenerate = false;
-  for (int h = 0; h < H; ++h) degenerate |= !(sS[h] > 0.0f);
-  if (degenerate) {  // every envelope is 0: the layer output is 0 and not differentiable
-    for (int c = t; c < C; c += kBwdThreads) dqo[c] = 0.0f;
-    return;
-  }
-
-  const T* w_so2 = (const T*)P.w_so2;
-  for (int sweep = 1; sweep <= 2; ++sweep) {
-    for (int e = e0; e < e1; ++e) {
-      const int j = P.col[e];
-      // geometry, frame, envelope, softmax weights of the edge
-      if (t == 0) {
-        const EdgeGeo geo = edge_geometry(P.pos, i, j, P.periodic, P.box, rc);
-        const float inv = geo.rho > 0.0f ? 1.0f / geo.rho : 0.0f;
-        sred[8] = geo.rho;
-        sred[9] = envelope_u(geo.s, geo.t, P.p);
-        sred[10] = envelope_du(geo.s, geo.t, P.p) / rc;  // du/d|r|
-        sred[11] = geo.r[0] * inv;
-        sred[12] = geo.r[1] * inv;
-        sred[13] = geo.r[2] * inv;
-        edge_frame(sred[11], sred[12], sred[13], sred + 16);
-        for (int q = 0; q < 7; ++q) sred[q] = 0.0f;
-      }
-      for (int h = t; h < H; h += kBwdThreads) ss[h] = 0.0f;
-      __syncthreads();
-      const float rho = sred[8], u = sred[9], dudr = sred[10];
-      // Wigner-D: degree 0 and 1 directly, then one degree at a time
-      if (t == 0) sD[0] = 1.0f;
-      if (L >= 1 && t < 9) {
-        const int ax[3] = {1, 2, 0};
-        sD[wig_offset(1) + t] = sred[16 + ax[t / 3] * 3 + ax[t % 3]];
-      }
-      if (t < K) {
-        const float dr = rho - mu_step * (float)t;
-        const float ph = expf(-dr * dr * inv2s2);
-        sphi[t] = rbf_env ? ph * u : ph;
-      }
-      for (int h = t; h < H; h += kBwdThreads) {
-        float z = 0.0f;
-        for (int c = h * d; c < (h + 1) * d; ++c) z += sq[c] * P.k[(int64_t)j * C + c];
-        z *= inv_sqrt_d;
-        const float ab = expf(z - sM[h]) * sS[h];
-        sab[h] = ab;
-        sa[h] = u * ab;
-      }
-      __syncthreads();
-      for (int l = 2; l <= L; ++l) {
-        const int n = 2 * l + 1;
-        for (int q = t; q < n * n; q += kBwdThreads)
-          sD[wig_offset(l) + q] = wigner_entry(l, q / n - l, q % n - l, sD + wig_offset(1), sD + wig_offset(l - 1));
-        __syncthreads();
-      }
-      // radial gate and its derivative along |r|
-      for (int c = t; c < C; c += kBwdThreads) {
-        float g = 1.0f, gp = 0.0f;
-        if (radial) {
-          g = 0.0f;
-          float g0 = 0.0f;  // sum_k phi_k W (no envelope factor)
-          for (int kk = 0; kk < K; ++kk) {
-            const float dr = rho - mu_step * (float)kk;
-            const float ph = expf(-dr * dr * inv2s2);
-            const float w = load_as_float((const T*)P.w_rad, (int64_t)kk * C + c);
-            g0 += ph * w;
-            gp += -dr * 2.0f * inv2s2 * ph * w;
-          }
-          g = rbf_env ? g0 * u : g0;
-          if (rbf_env) gp = gp * u + g0 * dudr;
-        }
-        sg[c] = g;
-        sgp[c] = gp;
-      }
-      // D J_a (per degree) for the direction gradient
-      if (sweep == 2) {
-        for (int q = t; q < 3 * nw; q += kBwdThreads) {
-          const int ax = q / nw, r = q % nw;
-          int l = 0;
-          while (wig_offset(l + 1) <= r) ++l;
-          const int n = 2 * l + 1, o = r - wig_offset(l), m = o / n, mp = o % n;
-          const float* Dl = sD + wig_offset(l) + m * n;
-          const float* Jl = sJ + ax * Ly.nwig + wig_offset(l);
-          float acc = 0.0f;
-          for (int b = 0; b < n; ++b) acc += Dl[b] * Jl[b * n + mp];
-          sDJ[ax * Ly.nwig + r] = acc;
-        }
-      }
-      __syncthreads();
-      // xh = D x_j, xt = g xh
-      const T* xj = (const T*)P.x + (int64_t)j * nc * C;
-      for (int a = t; a < nc * C; a += kBwdThreads) {
-        const int comp = a / C, c = a % C;
-        const int l = (int)sqrtf((float)comp + 0.5f);
-        const float* Dl = sD + wig_offset(l) + (comp - l * l) * (2 * l + 1);
-        float v = 0.0f;
-        for (int b = 0; b < 2 * l + 1; ++b) v += Dl[b] * load_as_float(xj, (int64_t)(l * l + b) * C + c);
-        sXH[a] = v;
-        sXT[a] = v * sg[c];
-      }
-      __syncthreads();
-      // yt = per-m map of xt: one output row per wave, lanes split the inputs
-      {
-        const int lane = t & 63, wave = t >> 6;
-        for (int o = wave; o < nc * C; o += kBwdThreads / 64) {
-          const int comp = o / C, cp = o % C;
-          const int l = (int)sqrtf((float)comp + 0.5f);
-          const int m = comp - l * l - l, am = m < 0 ? -m : m;
-          float acc = 0.0f;
-          if (am == 0) {
-            const int64_t K0 = (int64_t)(L + 1) * C;
-            const T* row = w_so2 + ((int64_t)l * C + cp) * K0;
-            for (int kk = lane; kk < K0; kk += 64) {
-              const int lp = kk / C, c = kk % C;
-              acc += load_as_float(row, kk) * sXT[(lp * lp + lp) * C + c];
-            }
-          } else {
-            const int64_t Km = (int64_t)(L + 1 - am) * C;
-            const T* row1 = w_so2 + so2_w1_offset(L, C, am) + ((int64_t)(l - am) * C + cp) * Km;
-            const T* row2 = row1 + Km * Km;
-            for (int kk = lane; kk < Km; kk += 64) {
-              const int lp = kk / C + am, c = kk % C;
-              const float xp = sXT[(lp * lp + lp + am) * C + c], xm = sXT[(lp * lp + lp - am) * C + c];
-              const float w1 = load_as_float(row1, kk), w2 = load_as_float(row2, kk);
-              acc += m > 0 ? (w1 * xp - w2 * xm) : (w2 * xp + w1 * xm);
-            }
-          }
-#pragma unroll
-          for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-          if (lane == 0) sY[o] = acc;
-        }
-      }
-      __syncthreads();
-      // v = D^T yt; s^h = <dy_i, v> over the head's channels
-      for (int a = t; a < nc * C; a += kBwdThreads) {
-        const int comp = a / C, c = a % C;
-        const int l = (int)sqrtf((float)comp + 0.5f);
-        const int n = 2 * l + 1, mcol = comp - l * l;
-        const float* Dl = sD + wig_offset(l);
-        float v = 0.0f;
-        for (int b = 0; b < n; ++b) v += Dl[b * n + mcol] * sY[(l * l + b) * C + c];
-        sV[a] = v;
-        atomicAdd(&ss[c / d], sG[a] * v);
-      }
-      __syncthreads();
-      if (sweep == 1) {
-        for (int h = t; h < H; h += kBwdThreads) ssb[h] += sa[h] * ss[h];
-        __syncthreads();
-        continue;
-      }
-      // ---- sweep 2: gradients of this edge
-      // dir1_a = <dv, J_a v> with dv = a (.) dy_i
-      for (int a = t; a < ((nc * C + 63) & ~63); a += kBwdThreads) {
-        float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f;
-        if (a < nc * C) {
-          const int comp = a / C, c = a % C;
-          const int l = (int)sqrtf((float)comp + 0.5f);
-          const int n = 2 * l + 1, m = comp - l * l;
-          const float dv = sa[c / d] * sG[a];
-          const float* J0 = sJ + wig_offset(l) + m * n;
-          for (int b = 0; b < n; ++b) {
-            const float vb = sV[(l * l + b) * C + c];
-            p0 += J0[b] * vb;
-            p1 += J0[Ly.nwig + b] * vb;
-            p2 += J0[2 * Ly.nwig + b] * vb;
-          }
-          p0 *= dv;
-          p1 *= dv;
-          p2 *= dv;
-        }
-        wave_add(sred + 1, p0);
-        wave_add(sred + 2, p1);
-        wave_add(sred + 3, p2);
-      }
-      // dyt = D dv (into sY)
-      for (int a = t; a < nc * C; a += kBwdThreads) {
-        const int comp = a / C, c = a % C;
-        const int l = (int)sqrtf((float)comp + 0.5f);
-        const int n = 2 * l + 1;
-        const float* Dl = sD + wig_offset(l) + (comp - l * l) * n;
-        float v = 0.0f;
-        for (int b = 0; b < n; ++b) v += Dl[b] * sG[(l * l + b) * C + c];
-        sY[a] = v * sa[c / d];
-      }
-      __syncthreads();
-      // dW_so2 += per-m outer products (dyt, xt)
-      if (P.dw_so2) {
-        const int64_t k0 = (int64_t)(L + 1) * C;
-        for (int64_t q = t; q < k0 * k0; q += kBwdThreads) {
-          const int64_t r = q / k0, cc = q % k0;
-          const int l = (int)(r / C), lp = (int)(cc / C);
-          const float gv = sY[(l * l + l) * C + r % C] * sXT[(lp * lp + lp) * C + cc % C];
-          if (gv != 0.0f) atomic_add_f(P.dw_so2 + q, gv);
-        }
-        for (int m = 1; m <= L; ++m) {
-          const int64_t km = (int64_t)(L + 1 - m) * C;
-          float* d1 = P.dw_so2 + so2_w1_offset(L, C, m);
-          float* d2 = d1 + km * km;
-          for (int64_t q = t; q < km * km; q += kBwdThreads) {
-            const int64_t r = q / km, cc = q % km;
-            const int l = (int)(r / C) + m, lp = (int)(cc / C) + m;
-            const float yp = sY[(l * l + l + m) * C + r % C], ym = sY[(l * l + l - m) * C + r % C];
-            const float xp = sXT[(lp * lp + lp + m) * C + cc % C], xm = sXT[(lp * lp + lp - m) * C + cc % C];
-            atomic_add_f(d1 + q, yp * xp + ym * xm);
-            atomic_add_f(d2 + q, ym * xp - yp * xm);
-          }
-        }
-      }
-      // dxt = W^T dyt (transposed per-m map), one output per lane: the lanes
-      // of a wave read consecutive columns of a weight row
-      for (int a = t; a < nc * C; a += kBwdThreads) {
-        const int comp = a / C, c = a % C;
-        const int lp = (int)sqrtf((float)comp + 0.5f);
-        const int m = comp - lp * lp - lp, am = m < 0 ? -m : m;
-        float acc = 0.0f;
-        if (am == 0) {
-          const int64_t K0 = (int64_t)(L + 1) * C;
-          const int64_t col = (int64_t)lp * C + c;
-          for (int l = 0; l <= L; ++l)
-            for (int cp = 0; cp < C; ++cp)
-              acc += load_as_float(w_so2, ((int64_t)l * C + cp) * K0 + col) * sY[(l * l + l) * C + cp];
-        } else {
-          const int64_t Km = (int64_t)(L + 1 - am) * C;
-          const T* w1 = w_so2 + so2_w1_offset(L, C, am);
-          const T* w2 = w1 + Km * Km;
-          const int64_t col = (int64_t)(lp - am) * C + c;
-          for (int l = am; l <= L; ++l)
-            for (int cp = 0; cp < C; ++cp) {
-              const int64_t r = ((int64_t)(l - am) * C + cp) * Km + col;
-              const float yp = sY[(l * l + l + am) * C + cp], ym = sY[(l * l + l - am) * C + cp];
-              const float a1 = load_as_float(w1, r), a2 = load_as_float(w2, r);
-              // xt_+ grad: W1^T dy_+ + W2^T dy_- ; xt_- grad: -W2^T dy_+ + W1^T dy_-
-              acc += m > 0 ? (a1 * yp + a2 * ym) : (a1 * ym - a2 * yp);
-            }
-        }
-        sV[a] = acc;
-      }
-      __syncthreads();
-      // dg[c], d|r| (radial), dir2_a = <dxt g, D J_a x_j>, dx_j += D^T (dxt g)
-      for (int c = t; c < C; c += kBwdThreads) {
-        float dg = 0.0f;
-        for (int comp = 0; comp < nc; ++comp) dg += sV[comp * C + c] * sXH[comp * C + c];
-        sdg[c] = dg;
-      }
-      float* dxj = P.dx + (int64_t)j * nc * C;
-      for (int a = t; a < ((nc * C + 63) & ~63); a += kBwdThreads) {
-        float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f;
-        if (a < nc * C) {
-          const int comp = a / C, c = a % C;
-          const int l = (int)sqrtf((float)comp + 0.5f);
-          const int n = 2 * l + 1, mrow = comp - l * l;
-          const float gx = sV[a] * sg[c];
-          const float* R0 = sDJ + wig_offset(l) + mrow * n;
-          for (int b = 0; b < n; ++b) {
-            const float xb = load_as_float(xj, (int64_t)(l * l + b) * C + c);
-            p0 += R0[b] * xb;
-            p1 += R0[Ly.nwig + b] * xb;
-            p2 += R0[2 * Ly.nwig + b] * xb;
-          }
-          p0 *= gx;
-          p1 *= gx;
-          p2 *= gx;
-          // dx_j[(l, b), c] += sum_m D[m][b] dxt[(l, m), c] g[c]: column b = mrow here
-          const float* Dl = sD + wig_offset(l);
-          float dxv = 0.0f;
-          for (int mm = 0; mm < n; ++mm) dxv += Dl[mm * n + mrow] * sV[(l * l + mm) * C + c];
-          atomic_add_f(dxj + a, dxv * sg[c]);
-        }
-        wave_add(sred + 4, p0);
-        wave_add(sred + 5, p1);
-        wave_add(sred + 6, p2);
-      }
-      __syncthreads();
-      // radial parts, softmax parts, W_rad, q/k
-      for (int c = t; c < ((C + 63) & ~63); c += kBwdThreads) wave_add(sred + 0, c < C ? sdg[c] * sgp[c] : 0.0f);
-      if (radial)
-        for (int a = t; a < K * C; a += kBwdThreads) sdwr[a] += sphi[a / C] * sdg[a % C];
-      for (int c = t; c < C; c += kBwdThreads) {
-        const int h = c / d;
-        const float dz = sa[h] * (ss[h] - ssb[h]) * inv_sqrt_d;
-        sdq[c] += dz * P.k[(int64_t)j * C + c];
-        atomic_add_f(P.dk + (int64_t)j * C + c, dz * sq[c]);
-      }
-      __syncthreads();
-      if (t == 0) {
-        float du = 0.0f;
-        for (int h = 0; h < H; ++h) du += sab[h] * (ss[h] - ssb[h]);
-        const float drho = sred[0] + du * dudr;
-        const float w0 = sred[1] - sred[4], w1 = sred[2] - sred[5], w2 = sred[3] - sred[6];
-        const float rx = sred[11], ry = sred[12], rz = sred[13];
-        const float inv = rho > 0.0f ? 1.0f / rho : 0.0f;
-        // (dL/dw) x r_hat / |r| + d|r| r_hat
-        const float gx = (w1 * rz - w2 * ry) * inv + drho * rx;
-        const float gy = (w2 * rx - w0 * rz) * inv + drho * ry;
-        const float gz = (w0 * ry - w1 * rx) * inv + drho * rz;
-        atomic_add_f(P.dpos + 3 * (int64_t)j + 0, gx);
-        atomic_add_f(P.dpos + 3 * (int64_t)j + 1, gy);
-        atomic_add_f(P.dpos + 3 * (int64_t)j + 2, gz);
-        atomic_add_f(P.dpos + 3 * (int64_t)i + 0, -gx);
-        atomic_add_f(P.dpos + 3 * (int64_t)i + 1, -gy);
-        atomic_add_f(P.dpos + 3 * (int64_t)i + 2, -gz);
-      }
-      __syncthreads();
+    __syncthreads();
+    if (lane < H) {
+      const float z = zs[lane] * inv_sqrt_d;
+      const float ab = expf(z - P.smax[(int64_t)i * H + lane]) * P.sinv[(int64_t)i * H + lane];
+      B.ab[(int64_t)e * H + lane] = ab;
+      B.a[(int64_t)e * H + lane] = u * ab;
     }
     __syncthreads();
   }
-  for (int c = t; c < C; c += kBwdThreads) dqo[c] = sdq[c];
-  if (P.dw_rad && radial)
-    for (int a = t; a < K * C; a += kBwdThreads) atomic_add_f(P.dw_rad + a, sdwr[a]);
+}
+
+// v = D^T yt for degree l of one channel: yt read from the block layout.
+template <int L, int l>
+__device__ inline void rotate_back(const float* sD, const float* yte, int C, int c, float (&v)[2 * L + 1]) {
+  constexpr int n = 2 * l + 1;
+  float yv[n];
+#pragma unroll
+  for (int r = 0; r < n; ++r) yv[r] = yte[comp_col(L, C, l, r - l) + c];
+  const float* Dl = sD + wig_offset(l);
+#pragma unroll
+  for (int b = 0; b < n; ++b) {
+    float s = 0.0f;
+#pragma unroll
+    for (int r = 0; r < n; ++r) s += Dl[r * n + b] * yv[r];
+    v[b] = s;
+  }
+}
+
+// <dy_i, v> over degree l of one channel.
+template <int L, int l>
+__device__ inline float head_part(const float* sD, const float* yte, const float* dyi, int C, int c) {
+  float v[2 * L + 1];
+  rotate_back<L, l>(sD, yte, C, c, v);
+  float s = 0.0f;
+#pragma unroll
+  for (int b = 0; b < 2 * l + 1; ++b) s += dyi[(int64_t)(l * l + b) * C + c] * v[b];
+  return s;
+}
+
+template <int L, int l>
+__device__ inline float head_sum(const float* sD, const float* yte, const float* dyi, int C, int c) {
+  if constexpr (l > L) return 0.0f;
+  else return head_part<L, l>(sD, yte, dyi, C, c) + head_sum<L, l + 1>(sD, yte, dyi, C, c);
+}
+
+// Pass 1: s^h of every edge and Sbar_i^h += a^h s^h.
+template <int L>
+__global__ void __launch_bounds__(kLane) bwd_sbar_kernel(BwdParams P) {
+  constexpr int nw = wig_total(L);
+  constexpr int nc = n_comp(L);
+  __shared__ float sD[nw];
+  __shared__ float ss[kMaxBwdHeads];
+  const int lane = threadIdx.x;
+  const int C = P.C, H = P.H, d = C / H;
+  const EdgeBufs& B = P.b;
+  for (int e = blockIdx.x; e < P.nb; e += gridDim.x) {
+    const int i = B.tgt[e];
+    for (int q = lane; q < nw; q += kLane) sD[q] = B.D[(int64_t)e * nw + q];
+    if (lane < H) ss[lane] = 0.0f;
+    __syncthreads();
+    const float* yte = B.yt + (int64_t)e * nc * C;
+    const float* dyi = P.dy + (int64_t)i * nc * C;
+    for (int c = lane; c < C; c += kLane) atomicAdd(&ss[c / d], head_sum<L, 0>(sD, yte, dyi, C, c));
+    __syncthreads();
+    if (lane < H) atomicAdd(P.sbar + (int64_t)i * H + lane, B.a[(int64_t)e * H + lane] * ss[lane]);
+    __syncthreads();
+  }
+}
+
+// Degree l of one channel in pass 2: dv = a dy_i, <dv, J_a v> into dir,
+// dyt = D dv written over yt.
+template <int L, int l>
+__device__ inline void dyt_degree(const float* sD, const float* sJ, float* yte, const float* dyi, int C, int c,
+                                  float av, float (&dir)[3]) {
+  constexpr int n = 2 * l + 1;
+  constexpr int nw = wig_total(L);
+  float v[2 * L + 1];
+  rotate_back<L, l>(sD, yte, C, c, v);
+  float dv[n];
+#pragma unroll
+  for (int b = 0; b < n; ++b) dv[b] = av * dyi[(int64_t)(l * l + b) * C + c];
+#pragma unroll
+  for (int ax = 0; ax < 3; ++ax) {
+    const float* Jl = sJ + ax * nw + wig_offset(l);
+    float s = 0.0f;
+#pragma unroll
+    for (int m = 0; m < n; ++m) {
+      float jv = 0.0f;
+#pragma unroll
+      for (int b = 0; b < n; ++b) jv += Jl[m * n + b] * v[b];
+      s += dv[m] * jv;
+    }
+    dir[ax] += s;
+  }
+  const float* Dl = sD + wig_offset(l);
+#pragma unroll
+  for (int r = 0; r < n; ++r) {
+    float s = 0.0f;
+#pragma unroll
+    for (int b = 0; b < n; ++b) s += Dl[r * n + b] * dv[b];
+    yte[comp_col(L, C, l, r - l) + c] = s;
+  }
+}
+
+template <int L, int l>
+__device__ inline void dyt_all(const float* sD, const float* sJ, float* yte, const float* dyi, int C, int c, float av,
+                               float (&dir)[3]) {
+  if constexpr (l <= L) {
+    dyt_degree<L, l>(sD, sJ, yte, dyi, C, c, av, dir);
+    dyt_all<L, l + 1>(sD, sJ, yte, dyi, C, c, av, dir);
+  }
+}
+
+// Pass 2, first half: s^h again, dL/dz, dL/du, dyt (over yt), the first
+// direction term, dq and dk.
+template <int L>
+__global__ void __launch_bounds__(kLane) bwd_dyt_kernel(BwdParams P) {
+  constexpr int nw = wig_total(L);
+  constexpr int nc = n_comp(L);
+  __shared__ float sD[nw];
+  __shared__ float sJ[3 * nw];
+  __shared__ float ss[kMaxBwdHeads];
+  __shared__ float sdz[kMaxBwdHeads];
+  __shared__ float sa[kMaxBwdHeads];
+  const int lane = threadIdx.x;
+  const int C = P.C, H = P.H, d = C / H;
+  const float inv_sqrt_d = 1.0f / sqrtf((float)d);
+  const EdgeBufs& B = P.b;
+  for (int q = lane; q < 3 * nw; q += kLane) sJ[q] = P.gen[q];
+  for (int e = blockIdx.x; e < P.nb; e += gridDim.x) {
+    const int i = B.tgt[e];
+    const int j = P.col[P.e0 + e];
+    for (int q = lane; q < nw; q += kLane) sD[q] = B.D[(int64_t)e * nw + q];
+    if (lane < H) ss[lane] = 0.0f;
+    __syncthreads();
+    float* yte = B.yt + (int64_t)e * nc * C;
+    const float* dyi = P.dy + (int64_t)i * nc * C;
+    for (int c = lane; c < C; c += kLane) atomicAdd(&ss[c / d], head_sum<L, 0>(sD, yte, dyi, C, c));
+    __syncthreads();
+    float du = 0.0f;
+    if (lane < H) {
+      const float diff = ss[lane] - P.sbar[(int64_t)i * H + lane];
+      const float a = B.a[(int64_t)e * H + lane];
+      sdz[lane] = a * diff * inv_sqrt_d;
+      sa[lane] = a;
+      du = B.ab[(int64_t)e * H + lane] * diff;
+    }
+    du = wave_sum(du);
+    __syncthreads();
+    float dir[3] = {0.0f, 0.0f, 0.0f};
+    for (int c = lane; c < C; c += kLane) {
+      const int h = c / d;
+      dyt_all<L, 0>(sD, sJ, yte, dyi, C, c, sa[h], dir);
+      atomicAdd(P.dq + (int64_t)i * C + c, sdz[h] * P.k[(int64_t)j * C + c]);
+      atomicAdd(P.dk + (int64_t)j * C + c, sdz[h] * P.q[(int64_t)i * C + c]);
+    }
+#pragma unroll
+    for (int ax = 0; ax < 3; ++ax) dir[ax] = wave_sum(dir[ax]);
+    if (lane == 0) {
+      float* sc = B.sc + (int64_t)e * kScal;
+      sc[6] = du;
+      sc[7] = dir[0];
+      sc[8] = dir[1];
+      sc[9] = dir[2];
+    }
+    __syncthreads();
+  }
+}
+
+// Degree l of one channel in the last per-edge step: dg, dx_j, the second
+// direction term.
+template <int L, int l, typename T>
+__device__ inline void final_degree(const float* sD, const float* sDJ, const float* xte, const T* xj, float* dxj,
+                                    int C, int c, float g, float& dg, float (&dir)[3]) {
+  constexpr int n = 2 * l + 1;
+  constexpr int nw = wig_total(L);
+  float xv[n], gx[n];
+#pragma unroll
+  for (int b = 0; b < n; ++b) xv[b] = load_as_float(xj, (int64_t)(l * l + b) * C + c);
+  const float* Dl = sD + wig_offset(l);
+#pragma unroll
+  for (int r = 0; r < n; ++r) {
+    const float dxt = xte[comp_col(L, C, l, r - l) + c];
+    float xh = 0.0f;
+#pragma unroll
+    for (int b = 0; b < n; ++b) xh += Dl[r * n + b] * xv[b];
+    dg += dxt * xh;
+    gx[r] = dxt * g;
+  }
+#pragma unroll
+  for (int ax = 0; ax < 3; ++ax) {
+    const float* R = sDJ + ax * nw + wig_offset(l);
+    float s = 0.0f;
+#pragma unroll
+    for (int r = 0; r < n; ++r) {
+      float t = 0.0f;
+#pragma unroll
+      for (int b = 0; b < n; ++b) t += R[r * n + b] * xv[b];
+      s += gx[r] * t;
+    }
+    dir[ax] += s;
+  }
+#pragma unroll
+  for (int b = 0; b < n; ++b) {
+    float s = 0.0f;
+#pragma unroll
+    for (int r = 0; r < n; ++r) s += Dl[r * n + b] * gx[r];
+    atomicAdd(dxj + (int64_t)(l * l + b) * C + c, s);
+  }
+}
+
+template <int L, int l, typename T>
+__device__ inline void final_all(const float* sD, const float* sDJ, const float* xte, const T* xj, float* dxj, int C,
+                                 int c, float g, float& dg, float (&dir)[3]) {
+  if constexpr (l <= L) {
+    final_degree<L, l, T>(sD, sDJ, xte, xj, dxj, C, c, g, dg, dir);
+    final_all<L, l + 1, T>(sD, sDJ, xte, xj, dxj, C, c, g, dg, dir);
+  }
+}
+
+// Pass 2, second half (after dxt = map^T(dyt) is in the xt buffer): dg,
+// dx_j, the radial and direction parts of the edge vector's gradient.
+template <int L, typename T>
+__global__ void __launch_bounds__(kLane) bwd_final_kernel(BwdParams P) {
+  constexpr int nw = wig_total(L);
+  constexpr int nc = n_comp(L);
+  __shared__ float sD[nw];
+  __shared__ float sJ[3 * nw];
+  __shared__ float sDJ[3 * nw];
+  const int lane = threadIdx.x;
+  const int C = P.C;
+  const T* x = (const T*)P.x;
+  const EdgeBufs& B = P.b;
+  for (int q = lane; q < 3 * nw; q += kLane) sJ[q] = P.gen[q];
+  for (int e = blockIdx.x; e < P.nb; e += gridDim.x) {
+    const int i = B.tgt[e];
+    const int j = P.col[P.e0 + e];
+    for (int q = lane; q < nw; q += kLane) sD[q] = B.D[(int64_t)e * nw + q];
+    __syncthreads();
+    // D J_a per degree
+    for (int q = lane; q < 3 * nw; q += kLane) {
+      const int ax = q / nw, r = q % nw;
+      int l = 0;
+      while (wig_offset(l + 1) <= r) ++l;
+      const int n = 2 * l + 1, o = r - wig_offset(l), m = o / n, mp = o % n;
+      const float* Dl = sD + wig_offset(l) + m * n;
+      const float* Jl = sJ + ax * nw + wig_offset(l);
+      float acc = 0.0f;
+      for (int b = 0; b < n; ++b) acc += Dl[b] * Jl[b * n + mp];
+      sDJ[q] = acc;
+    }
+    __syncthreads();
+    const float* xte = B.xt + (int64_t)e * nc * C;
+    const T* xj = x + (int64_t)j * nc * C;
+    float* dxj = P.dx + (int64_t)j * nc * C;
+    float dir[3] = {0.0f, 0.0f, 0.0f};
+    float rad = 0.0f;
+    for (int c = lane; c < C; c += kLane) {
+      float dg = 0.0f;
+      final_all<L, 0, T>(sD, sDJ, xte, xj, dxj, C, c, B.g[(int64_t)e * C + c], dg, dir);
+      B.dg[(int64_t)e * C + c] = dg;
+      rad += dg * B.gp[(int64_t)e * C + c];
+    }
+    rad = wave_sum(rad);
+#pragma unroll
+    for (int ax = 0; ax < 3; ++ax) dir[ax] = wave_sum(dir[ax]);
+    if (lane == 0) {
+      const float* sc = B.sc + (int64_t)e * kScal;
+      const float rho = sc[0], dudr = sc[2], rx = sc[3], ry = sc[4], rz = sc[5];
+      const float drho = rad + sc[6] * dudr;
+      const float w0 = sc[7] - dir[0], w1 = sc[8] - dir[1], w2 = sc[9] - dir[2];
+      const float inv = rho > 0.0f ? 1.0f / rho : 0.0f;
+      // (dL/dw) x r_hat / |r| + d|r| r_hat
+      const float gx = (w1 * rz - w2 * ry) * inv + drho * rx;
+      const float gy = (w2 * rx - w0 * rz) * inv + drho * ry;
+      const float gz = (w0 * ry - w1 * rx) * inv + drho * rz;
+      atomicAdd(P.dpos + 3 * (int64_t)j + 0, gx);
+      atomicAdd(P.dpos + 3 * (int64_t)j + 1, gy);
+      atomicAdd(P.dpos + 3 * (int64_t)j + 2, gz);
+      atomicAdd(P.dpos + 3 * (int64_t)i + 0, -gx);
+      atomicAdd(P.dpos + 3 * (int64_t)i + 1, -gy);
+      atomicAdd(P.dpos + 3 * (int64_t)i + 2, -gz);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- fp32 GEMM
+
+// C (+)= A B on the matrix cores (v_mfma_f32_16x16x4_f32), fp32 throughout.
+//   A(m, k) = A[m lda + k]      (AT = false)  or A[k lda + m] (AT = true)
+//   B(k, n) = B[n ldb + k]      (BT = true)   or B[k ldb + n] (BT = false)
+// 64 x 64 tiles of C per workgroup (4 waves, 32 x 32 each), K in steps of
+// 16 staged through LDS; blockIdx.z splits K into ranges of kSplit.  Mode:
+// store (C = AB, one workgroup per tile) or atomic (C += AB, fp32 atomics,
+// any number of K ranges).
+struct GemmArgs {
+  const float* A;
+  const float* B;
+  float* Cm;
+  int M, N, K;
+  int64_t lda, ldb, ldc;
+  int k_split;  // K range per blockIdx.z
+  int atomic;
+};
+
+template <bool AT, bool BT>
+__global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
+  constexpr int BM = 64, BN = 64, BK = 16, LDP = BM + 16;  // row pad: the 4 k-rows of a read hit distinct banks
+  __shared__ float As[BK][LDP];
+  __shared__ float Bs[BK][LDP];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+  const int wm = (w >> 1) * 32, wn = (w & 1) * 32;
+  const int kb = blockIdx.z * g.k_split;
+  const int ke = min(g.K, kb + g.k_split);
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k0 = kb; k0 < ke; k0 += BK) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int m, k;
+      if constexpr (AT) {
+        m = t & 63;
+        k = (t >> 6) + 4 * r;
+      } else {
+        k = t & 15;
+        m = (t >> 4) + 16 * r;
+      }
+      const int gm = m0 + m, gk = k0 + k;
+      float v = 0.0f;
+      if (gm < g.M && gk < ke) v = AT ? g.A[(int64_t)gk * g.lda + gm] : g.A[(int64_t)gm * g.lda + gk];
+      As[k][m] = v;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int n, k;
+      if constexpr (BT) {
+        k = t & 15;
+        n = (t >> 4) + 16 * r;
+      } else {
+        n = t & 63;
+        k = (t >> 6) + 4 * r;
+      }
+      const int gn = n0 + n, gk = k0 + k;
+      float v = 0.0f;
+      if (gn < g.N && gk < ke) v = BT ? g.B[(int64_t)gn * g.ldb + gk] : g.B[(int64_t)gk * g.ldb + gn];
+      Bs[k][n] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 4) {
+      const int kr = kk + (lane >> 4);
+      const float a0 = As[kr][wm + (lane & 15)], a1 = As[kr][wm + 16 + (lane & 15)];
+      const float b0 = Bs[kr][wn + (lane & 15)], b1 = Bs[kr][wn + 16 + (lane & 15)];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // C layout: lane holds rows 4 (lane / 16) + r, column lane % 16 of each 16 x 16 tile
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm + 16 * a + 4 * (lane >> 4) + r;
+        const int colm = n0 + wn + 16 * b + (lane & 15);
+        if (row < g.M && colm < g.N) {
+          float* p = g.Cm + (int64_t)row * g.ldc + colm;
+          if (g.atomic) atomicAdd(p, acc[a][b][r]);
+          else *p = acc[a][b][r];
+        }
+      }
+}
+
+template <bool AT, bool BT>
+so2_status gemm(const float* A, int64_t lda, const float* B, int64_t ldb, float* Cm, int64_t ldc, int M, int N, int K,
+                bool atomic, hipStream_t stream) {
+  if (M <= 0 || N <= 0 || K <= 0) return SO2_OK;
+  GemmArgs g{A, B, Cm, M, N, K, lda, ldb, ldc, K, atomic ? 1 : 0};
+  unsigned splits = 1;
+  if (atomic) {
+    // K ranges of at least 512 so that the tile grid covers the device
+    const int64_t tiles = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
+    const int64_t want = std::max<int64_t>(1, 2048 / std::max<int64_t>(tiles, 1));
+    const int64_t by_k = std::max<int64_t>(1, K / 512);
+    splits = (unsigned)std::min(want, by_k);
+    g.k_split = (int)(((K + splits - 1) / splits + 15) / 16 * 16);
+    splits = (unsigned)((K + g.k_split - 1) / g.k_split);
+  }
+  hipLaunchKernelGGL((gemm_f32_kernel<AT, BT>), dim3((unsigned)((M + 63) / 64), (unsigned)((N + 63) / 64), splits),
+                     dim3(256), 0, stream, g);
+  SO2_CHECK_LAUNCH();
+  return SO2_OK;
+}
+
+// ---------------------------------------------------------------- weights
+
+// B_m in fp32 from w_so2: W0 for m = 0, [[W1, -W2], [W2, W1]] for m >= 1.
+template <typename T>
+__global__ void __launch_bounds__(256) bmat_build_kernel(const T* __restrict__ w, float* __restrict__ bm, int L, int C) {
+  const int m = blockIdx.y;
+  const int wd = blk_width(L, C, m);
+  const int64_t n = (int64_t)wd * wd;
+  float* out = bm + bmat_off(L, C, m);
+  for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < n; q += (int64_t)gridDim.x * blockDim.x) {
+    const int o = (int)(q / wd), in = (int)(q % wd);
+    float v;
+    if (m == 0) {
+      v = load_as_float(w, q);
+    } else {
+      const int km = wd / 2;
+      const int so = o / km, si = in / km, ro = o % km, ri = in % km;
+      const T* w1 = w + so2_w1_offset(L, C, m);
+      const T* w2 = w1 + (int64_t)km * km;
+      const int64_t r = (int64_t)ro * km + ri;
+      v = so == si ? load_as_float(w1, r) : (so == 0 ? -load_as_float(w2, r) : load_as_float(w2, r));
+    }
+    out[q] = v;
+  }
+}
+
+// dW from dB: dW0 = dB_0; dW1 = dB_m[+,+] + dB_m[-,-]; dW2 = dB_m[-,+] - dB_m[+,-].
+__global__ void __launch_bounds__(256) dw_fold_kernel(const float* __restrict__ db, float* __restrict__ dw, int L,
+                                                      int C) {
+  const int m = blockIdx.y;
+  const int wd = blk_width(L, C, m);
+  const float* src = db + bmat_off(L, C, m);
+  if (m == 0) {
+    const int64_t n = (int64_t)wd * wd;
+    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < n; q += (int64_t)gridDim.x * blockDim.x)
+      dw[q] = src[q];
+    return;
+  }
+  const int km = wd / 2;
+  const int64_t n = (int64_t)km * km;
+  float* d1 = dw + so2_w1_offset(L, C, m);
+  float* d2 = d1 + n;
+  for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < n; q += (int64_t)gridDim.x * blockDim.x) {
+    const int ro = (int)(q / km), ri = (int)(q % km);
+    const float pp = src[(int64_t)ro * wd + ri], mm = src[(int64_t)(km + ro) * wd + km + ri];
+    const float mp = src[(int64_t)(km + ro) * wd + ri], pm = src[(int64_t)ro * wd + km + ri];
+    d1[q] = pp + mm;
+    d2[q] = mp - pm;
+  }
 }
 
 // dx[a][0][c] += sum_o dq[a][o] w_q[c][o] (a < n_targets) + sum_o dk[a][o] w_k[c][o]
@@ -569,62 +796,172 @@ so2_status fill_zero(float* p, int64_t n, hipStream_t stream) {
   return SO2_OK;
 }
 
+// ---------------------------------------------------------------- workspace
+
+// Edges per batch: 64 per target, between 4096 and 32768.
+int64_t batch_edges(int n_targets) {
+  const int64_t want = ((int64_t)n_targets * 64 + 255) / 256 * 256;
+  return std::min<int64_t>(32768, std::max<int64_t>(4096, want));
+}
+
+size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Offsets (bytes) of the backward's scratch arrays.
+struct BwdScratch {
+  size_t dq, dk, gen, smax, sinv, sbar, bm, db, xt, yt, D, g, gp, dg, phi, a, ab, sc, tgt, total;
+  int64_t cap;
+  BwdScratch(int n_atoms, int n_targets, int L, int C, int H, int K) {
+    cap = batch_edges(n_targets);
+    const size_t nc = (size_t)n_comp(L), nw = (size_t)wig_total(L);
+    const size_t nb = (size_t)bmat_off(L, C, L + 1);
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+      const size_t at = o;
+      o += al256(bytes);
+      return at;
+    };
+    dq = take(4 * (size_t)n_targets * C);
+    dk = take(4 * (size_t)n_atoms * C);
+    gen = take(4 * 4 * nw);
+    smax = take(4 * (size_t)n_targets * H);
+    sinv = take(4 * (size_t)n_targets * H);
+    sbar = take(4 * (size_t)n_targets * H);
+    bm = take(4 * nb);
+    db = take(4 * nb);
+    xt = take(4 * (size_t)cap * nc * C);
+    yt = take(4 * (size_t)cap * nc * C);
+    D = take(4 * (size_t)cap * nw);
+    g = take(4 * (size_t)cap * C);
+    gp = take(4 * (size_t)cap * C);
+    dg = take(4 * (size_t)cap * C);
+    phi = take(4 * (size_t)cap * K);
+    a = take(4 * (size_t)cap * H);
+    ab = take(4 * (size_t)cap * H);
+    sc = take(4 * (size_t)cap * kScal);
+    tgt = take(4 * (size_t)cap);
+    total = o;
+  }
+};
+
+template <int L, typename T>
+so2_status launch_edges(int which, const BwdParams& P, hipStream_t stream) {
+  const unsigned grid = (unsigned)std::min<int64_t>(P.nb, kGridCap);
+  if (grid == 0) return SO2_OK;
+  switch (which) {
+    case 0: hipLaunchKernelGGL((bwd_prep_kernel<L, T>), dim3(grid), dim3(kLane), 0, stream, P); break;
+    case 1: hipLaunchKernelGGL((bwd_sbar_kernel<L>), dim3(grid), dim3(kLane), 0, stream, P); break;
+    case 2: hipLaunchKernelGGL((bwd_dyt_kernel<L>), dim3(grid), dim3(kLane), 0, stream, P); break;
+    default: hipLaunchKernelGGL((bwd_final_kernel<L, T>), dim3(grid), dim3(kLane), 0, stream, P); break;
+  }
+  SO2_CHECK_LAUNCH();
+  return SO2_OK;
+}
+
+template <typename T>
+so2_status edges_dispatch(int L, int which, const BwdParams& P, hipStream_t stream) {
+  switch (L) {
+    case 0: return launch_edges<0, T>(which, P, stream);
+    case 1: return launch_edges<1, T>(which, P, stream);
+    case 2: return launch_edges<2, T>(which, P, stream);
+    case 3: return launch_edges<3, T>(which, P, stream);
+    case 4: return launch_edges<4, T>(which, P, stream);
+    case 5: return launch_edges<5, T>(which, P, stream);
+    default: return launch_edges<6, T>(which, P, stream);
+  }
+}
+
+so2_status run_edges(int L, int dtype, int which, const BwdParams& P, hipStream_t stream) {
+  return dtype == SO2_BF16 ? edges_dispatch<uint16_t>(L, which, P, stream) : edges_dispatch<float>(L, which, P, stream);
+}
+
 }  // namespace
 
 bool bwd_supported(int L, int C, int H, int K) {
-  if (!(L >= 0 && L <= kMaxL && C >= 1 && H >= 1 && C % H == 0 && K >= 2)) return false;
-  const BwdLds Ly(L, C, H, K);
-  return sizeof(float) * (size_t)Ly.total <= 160 * 1024;
+  return L >= 0 && L <= kMaxL && C >= 1 && C <= 256 && H >= 1 && H <= kMaxBwdHeads && C % H == 0 && K >= 2;
 }
 
-size_t bwd_scratch_bytes(int n_atoms, int n_targets, int L, int C) {
-  const size_t a = (sizeof(float) * (size_t)n_targets * C + 255) & ~(size_t)255;  // dq
-  const size_t b = (sizeof(float) * (size_t)n_atoms * C + 255) & ~(size_t)255;    // dk
-  const size_t g = (sizeof(float) * 6 * (size_t)wig_total(L) + 255) & ~(size_t)255;  // generators + scratch
-  return a + b + g;
+size_t bwd_scratch_bytes(int n_atoms, int n_targets, int L, int C, int H, int K) {
+  return BwdScratch(n_atoms, n_targets, L, C, H, K).total;
 }
 
 so2_status launch_attention_bwd(const AttnArgs& a, const float* dy, float* dx, float* dpos, float* dw_q, float* dw_k,
                                 float* dw_rad, float* dw_so2, hipStream_t stream) {
-  const int nc = n_comp(a.L);
+  const int L = a.L, C = a.C;
+  const int nc = n_comp(L);
+  const BwdScratch S(a.n_atoms, a.n_targets, L, a.C, a.H, a.K);
   char* ws = (char*)a.scratch;
-  float* dq = (float*)ws;
-  float* dk = (float*)(ws + ((sizeof(float) * (size_t)a.n_targets * a.C + 255) & ~(size_t)255));
-  float* gen = (float*)((char*)dk + ((sizeof(float) * (size_t)a.n_atoms * a.C + 255) & ~(size_t)255));
+  float* dq = (float*)(ws + S.dq);
+  float* dk = (float*)(ws + S.dk);
+  float* gen = (float*)(ws + S.gen);
+  float* smax = (float*)(ws + S.smax);
+  float* sinv = (float*)(ws + S.sinv);
+  float* sbar = (float*)(ws + S.sbar);
+  float* bm = (float*)(ws + S.bm);
+  float* db = (float*)(ws + S.db);
+  const bool radial = !(a.flags & SO2_FLAG_NO_RADIAL);
   so2_status st;
-  if ((st = fill_zero(dx, (int64_t)a.n_atoms * nc * a.C, stream)) != SO2_OK) return st;
+  if ((st = fill_zero(dx, (int64_t)a.n_atoms * nc * C, stream)) != SO2_OK) return st;
   if ((st = fill_zero(dpos, (int64_t)a.n_atoms * 3, stream)) != SO2_OK) return st;
-  if ((st = fill_zero(dk, (int64_t)a.n_atoms * a.C, stream)) != SO2_OK) return st;
-  if ((st = fill_zero(dw_q, (int64_t)a.C * a.C, stream)) != SO2_OK) return st;
-  if ((st = fill_zero(dw_k, (int64_t)a.C * a.C, stream)) != SO2_OK) return st;
-  if ((st = fill_zero(dw_rad, (int64_t)a.K * a.C, stream)) != SO2_OK) return st;
-  if ((st = fill_zero(dw_so2, so2_w1_offset(a.L, a.C, a.L + 1), stream)) != SO2_OK) return st;
-  hipLaunchKernelGGL(generators_kernel, dim3(1), dim3(64), 0, stream, gen, gen + 3 * wig_total(a.L), a.L);
-  SO2_CHECK_LAUNCH();
+  if ((st = fill_zero(dq, (int64_t)a.n_targets * C, stream)) != SO2_OK) return st;
+  if ((st = fill_zero(dk, (int64_t)a.n_atoms * C, stream)) != SO2_OK) return st;
+  if ((st = fill_zero(sbar, (int64_t)a.n_targets * a.H, stream)) != SO2_OK) return st;
+  if ((st = fill_zero(dw_q, (int64_t)C * C, stream)) != SO2_OK) return st;
+  if ((st = fill_zero(dw_k, (int64_t)C * C, stream)) != SO2_OK) return st;
+  if ((st = fill_zero(dw_rad, (int64_t)a.K * C, stream)) != SO2_OK) return st;
+  if (dw_so2 && (st = fill_zero(db, bmat_off(L, C, L + 1), stream)) != SO2_OK) return st;
+
+  // edge range of the targets' rows: the batch plan needs it on the host
+  int32_t ends[2] = {0, 0};
   if (a.n_targets > 0) {
+    SO2_CHECK(hipMemcpyAsync(&ends[0], a.row_ptr, sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+    SO2_CHECK(hipMemcpyAsync(&ends[1], a.row_ptr + a.n_targets, sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+    SO2_CHECK(hipStreamSynchronize(stream));
+  }
+  const int64_t e_first = ends[0], n_edges = (int64_t)ends[1] - ends[0];
+  if (n_edges < 0) return SO2_ERR_INVALID_ARGUMENT;
+
+  if (n_edges > 0) {
+    hipLaunchKernelGGL(generators_kernel, dim3(1), dim3(64), 0, stream, gen, gen + 3 * wig_total(L), L);
+    SO2_CHECK_LAUNCH();
+    const unsigned nbw = 1024;
+    if (a.dtype == SO2_BF16)
+      hipLaunchKernelGGL(bmat_build_kernel<uint16_t>, dim3(nbw, L + 1), dim3(256), 0, stream,
+                         (const uint16_t*)a.w_so2, bm, L, C);
+    else
+      hipLaunchKernelGGL(bmat_build_kernel<float>, dim3(nbw, L + 1), dim3(256), 0, stream, (const float*)a.w_so2,
+                         bm, L, C);
+    SO2_CHECK_LAUNCH();
+
     BwdParams P{};
     P.pos = a.pos;
     P.row_ptr = a.row_ptr;
     P.col = a.col;
     P.x = a.x;
-    P.w_q = a.w_q;
-    P.w_k = a.w_k;
     P.w_rad = a.w_rad;
-    P.w_so2 = a.w_so2;
     P.dy = dy;
     P.q = a.q;
     P.k = a.k;
     P.gen = gen;
+    P.smax = smax;
+    P.sinv = sinv;
+    P.sbar = sbar;
     P.dq = dq;
     P.dk = dk;
     P.dx = dx;
     P.dpos = dpos;
-    P.dw_rad = dw_rad;
-    P.dw_so2 = dw_so2;
-    P.n_atoms = a.n_atoms;
+    P.b.xt = (float*)(ws + S.xt);
+    P.b.yt = (float*)(ws + S.yt);
+    P.b.D = (float*)(ws + S.D);
+    P.b.g = (float*)(ws + S.g);
+    P.b.gp = (float*)(ws + S.gp);
+    P.b.dg = (float*)(ws + S.dg);
+    P.b.phi = (float*)(ws + S.phi);
+    P.b.a = (float*)(ws + S.a);
+    P.b.ab = (float*)(ws + S.ab);
+    P.b.sc = (float*)(ws + S.sc);
+    P.b.tgt = (int32_t*)(ws + S.tgt);
     P.n_targets = a.n_targets;
-    P.L = a.L;
-    P.C = a.C;
+    P.C = C;
     P.H = a.H;
     P.K = a.K;
     P.p = a.p;
@@ -632,42 +969,102 @@ so2_status launch_attention_bwd(const AttnArgs& a, const float* dy, float* dx, f
     P.flags = a.flags;
     P.periodic = a.periodic;
     for (int d = 0; d < 3; ++d) P.box[d] = a.box[d];
-    const size_t smem = sizeof(float) * (size_t)BwdLds(a.L, a.C, a.H, a.K).total;
-    if (a.dtype == SO2_BF16) {
-      SO2_CHECK(hipFuncSetAttribute((const void*)attn_bwd_kernel<uint16_t>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem));
-      hipLaunchKernelGGL(attn_bwd_kernel<uint16_t>, dim3(a.n_targets), dim3(kBwdThreads), smem, stream, P);
-    } else {
-      SO2_CHECK(hipFuncSetAttribute((const void*)attn_bwd_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)smem));
-      hipLaunchKernelGGL(attn_bwd_kernel<float>, dim3(a.n_targets), dim3(kBwdThreads), smem, stream, P);
+
+    const unsigned sgrid = (unsigned)std::min(a.n_targets, kGridCap);
+    hipLaunchKernelGGL(bwd_stats_kernel, dim3(sgrid), dim3(kLane), 0, stream, P);
+    SO2_CHECK_LAUNCH();
+
+    const int64_t cap = S.cap;
+    const int64_t nbat = (n_edges + cap - 1) / cap;
+    const int64_t ld = (int64_t)nc * C;
+    auto set_batch = [&](int64_t b) {
+      P.e0 = e_first + b * cap;
+      P.nb = (int32_t)std::min<int64_t>(cap, n_edges - b * cap);
+    };
+    // forward map of the batch: Y_m = X_m B_m^T
+    auto forward_map = [&]() -> so2_status {
+      for (int m = 0; m <= L; ++m) {
+        const int wd = blk_width(L, C, m);
+        const int64_t xo = blk_off(L, C, m);
+        so2_status s2 = gemm<false, true>(P.b.xt + xo, ld, bm + bmat_off(L, C, m), wd, P.b.yt + xo, ld, P.nb, wd, wd,
+                                          false, stream);
+        if (s2 != SO2_OK) return s2;
+      }
+      return SO2_OK;
+    };
+    // pass 1: Sbar
+    for (int64_t b = 0; b < nbat; ++b) {
+      set_batch(b);
+      if ((st = run_edges(L, a.dtype, 0, P, stream)) != SO2_OK) return st;
+      if ((st = forward_map()) != SO2_OK) return st;
+      if ((st = run_edges(L, a.dtype, 1, P, stream)) != SO2_OK) return st;
     }
+    // pass 2: gradients, the batch still in the buffers first
+    for (int64_t bb = nbat - 1; bb >= 0; --bb) {
+      set_batch(bb);
+      if (bb != nbat - 1) {
+        if ((st = run_edges(L, a.dtype, 0, P, stream)) != SO2_OK) return st;
+        if ((st = forward_map()) != SO2_OK) return st;
+      }
+      if ((st = run_edges(L, a.dtype, 2, P, stream)) != SO2_OK) return st;
+      for (int m = 0; m <= L; ++m) {
+        const int wd = blk_width(L, C, m);
+        const int64_t xo = blk_off(L, C, m);
+        // dB_m += dY_m^T X_m (before dX overwrites X)
+        if (dw_so2 &&
+            (st = gemm<true, false>(P.b.yt + xo, ld, P.b.xt + xo, ld, db + bmat_off(L, C, m), wd, wd, wd, P.nb, true,
+                                    stream)) != SO2_OK)
+          return st;
+        // dX_m = dY_m B_m, over X_m
+        if ((st = gemm<false, false>(P.b.yt + xo, ld, bm + bmat_off(L, C, m), wd, P.b.xt + xo, ld, P.nb, wd, wd, false,
+                                     stream)) != SO2_OK)
+          return st;
+      }
+      if ((st = run_edges(L, a.dtype, 3, P, stream)) != SO2_OK) return st;
+      // dW_rad += phi^T dg
+      if (dw_rad && radial &&
+          (st = gemm<true, false>(P.b.phi, a.K, P.b.dg, C, dw_rad, C, a.K, C, P.nb, true, stream)) != SO2_OK)
+        return st;
+    }
+    if (dw_so2) {
+      hipLaunchKernelGGL(dw_fold_kernel, dim3(1024, L + 1), dim3(256), 0, stream, db, dw_so2, L, C);
+      SO2_CHECK_LAUNCH();
+    }
+  } else if (dw_so2) {
+    if ((st = fill_zero(dw_so2, so2_w1_offset(L, C, L + 1), stream)) != SO2_OK) return st;
+  }
+
+  // the projections of the l = 0 slice
+  const int64_t nxc = (int64_t)a.n_atoms * C;
+  const unsigned gdx = (unsigned)((nxc + 255) / 256);
+  const unsigned gw = (unsigned)(((int64_t)C * C + 255) / 256);
+  if (gdx > 0) {
+    if (a.dtype == SO2_BF16)
+      hipLaunchKernelGGL(proj_bwd_dx_kernel<uint16_t>, dim3(gdx), dim3(256), 0, stream, dq, dk, a.w_q, a.w_k, dx,
+                         a.n_atoms, a.n_targets, nc, C);
+    else
+      hipLaunchKernelGGL(proj_bwd_dx_kernel<float>, dim3(gdx), dim3(256), 0, stream, dq, dk, a.w_q, a.w_k, dx,
+                         a.n_atoms, a.n_targets, nc, C);
     SO2_CHECK_LAUNCH();
   }
-  // the projections of the l = 0 slice
-  const int64_t nxc = (int64_t)a.n_atoms * a.C;
-  const unsigned gdx = (unsigned)((nxc + 255) / 256);
-  const unsigned gw = (unsigned)(((int64_t)a.C * a.C + 255) / 256);
-  if (a.dtype == SO2_BF16) {
-    hipLaunchKernelGGL(proj_bwd_dx_kernel<uint16_t>, dim3(gdx), dim3(256), 0, stream, dq, dk, a.w_q, a.w_k, dx,
-                       a.n_atoms, a.n_targets, nc, a.C);
-    if (dw_q && a.n_targets > 0)
+  if (dw_q && a.n_targets > 0) {
+    if (a.dtype == SO2_BF16)
       hipLaunchKernelGGL(proj_bwd_dw_kernel<uint16_t>, dim3(gw, (a.n_targets + kProjAtoms - 1) / kProjAtoms),
-                         dim3(256), 0, stream, a.x, dq, dw_q, a.n_targets, nc, a.C);
-    if (dw_k)
-      hipLaunchKernelGGL(proj_bwd_dw_kernel<uint16_t>, dim3(gw, (a.n_atoms + kProjAtoms - 1) / kProjAtoms),
-                         dim3(256), 0, stream, a.x, dk, dw_k, a.n_atoms, nc, a.C);
-  } else {
-    hipLaunchKernelGGL(proj_bwd_dx_kernel<float>, dim3(gdx), dim3(256), 0, stream, dq, dk, a.w_q, a.w_k, dx,
-                       a.n_atoms, a.n_targets, nc, a.C);
-    if (dw_q && a.n_targets > 0)
+                         dim3(256), 0, stream, a.x, dq, dw_q, a.n_targets, nc, C);
+    else
       hipLaunchKernelGGL(proj_bwd_dw_kernel<float>, dim3(gw, (a.n_targets + kProjAtoms - 1) / kProjAtoms), dim3(256),
-                         0, stream, a.x, dq, dw_q, a.n_targets, nc, a.C);
-    if (dw_k)
-      hipLaunchKernelGGL(proj_bwd_dw_kernel<float>, dim3(gw, (a.n_atoms + kProjAtoms - 1) / kProjAtoms), dim3(256),
-                         0, stream, a.x, dk, dw_k, a.n_atoms, nc, a.C);
+                         0, stream, a.x, dq, dw_q, a.n_targets, nc, C);
+    SO2_CHECK_LAUNCH();
   }
-  SO2_CHECK_LAUNCH();
+  if (dw_k && a.n_atoms > 0) {
+    if (a.dtype == SO2_BF16)
+      hipLaunchKernelGGL(proj_bwd_dw_kernel<uint16_t>, dim3(gw, (a.n_atoms + kProjAtoms - 1) / kProjAtoms),
+                         dim3(256), 0, stream, a.x, dk, dw_k, a.n_atoms, nc, C);
+    else
+      hipLaunchKernelGGL(proj_bwd_dw_kernel<float>, dim3(gw, (a.n_atoms + kProjAtoms - 1) / kProjAtoms), dim3(256),
+                         0, stream, a.x, dk, dw_k, a.n_atoms, nc, C);
+    SO2_CHECK_LAUNCH();
+  }
   return SO2_OK;
 }
 

@@ -75,12 +75,14 @@ size_t mfma_scratch_bytes(int n_atoms, int n_targets, int L, int H, int K);
 so2_status launch_attention_mfma_prep(const AttnArgs& a, hipStream_t stream);
 so2_status launch_attention_mfma(const AttnArgs& a, hipStream_t stream);
 
-// Backward (attention_bwd.hip), fp32 arithmetic: shapes whose per-target
-// LDS working set fits a compute unit (about 5 (L+1)^2 C floats).  Workspace
-// beyond q, k: dq [n_targets][C], dk [n_atoms][C] and the rotation
-// generators.  dw_* may be null (not computed).
+// Backward (attention_bwd.hip), fp32 arithmetic: any L <= 6, C <= 256,
+// H <= 64.  Workspace beyond q, k: dq, dk, the softmax statistics and head
+// sums per (target, head), the per-m maps in fp32 and their gradients, and
+// the per-edge tensors of one batch of edges (batch_edges(n_targets)).
+// dw_* may be null (not computed).  Reads the targets' edge range back to
+// the host once (one stream synchronisation) to plan the batches.
 bool bwd_supported(int L, int C, int H, int K);
-size_t bwd_scratch_bytes(int n_atoms, int n_targets, int L, int C);
+size_t bwd_scratch_bytes(int n_atoms, int n_targets, int L, int C, int H, int K);
 so2_status launch_attention_bwd(const AttnArgs& a, const float* dy, float* dx, float* dpos, float* dw_q, float* dw_k,
                                 float* dw_rad, float* dw_so2, hipStream_t stream);
 
