@@ -134,6 +134,11 @@ struct BwdParams {
   float box[3];
 };
 
+// Compiler-only barrier (no instruction): LDS reads of the Wigner-D and
+// generator blocks are not moved across it, so they are re-read per degree
+// and channel instead of being hoisted into registers for the whole edge.
+__device__ inline void keep_order() { asm volatile("" ::: "memory"); }
+
 __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -214,7 +219,7 @@ __device__ inline int edge_target(const int32_t* row_ptr, int n_targets, int64_t
 // Wigner-D, radial basis, gate and its |r| derivative, softmax weights, and
 // xt = g (.) D x_j in the block layout.
 template <int L, typename T>
-__global__ void __launch_bounds__(kLane) bwd_prep_kernel(BwdParams P) {
+__global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4))) bwd_prep_kernel(BwdParams P) {
   constexpr int nw = wig_total(L);
   constexpr int nc = n_comp(L);
   __shared__ float sD[nw];
@@ -282,6 +287,7 @@ __global__ void __launch_bounds__(kLane) bwd_prep_kernel(BwdParams P) {
       const T* xj = x + (int64_t)j * nc * C + c;
 #pragma unroll
       for (int l = 0; l <= L; ++l) {
+        keep_order();
         const int n = 2 * l + 1;
         float xv[2 * L + 1];
 #pragma unroll
@@ -327,6 +333,7 @@ __device__ inline void rotate_back(const float* sD, const float* yte, int C, int
 // <dy_i, v> over degree l of one channel.
 template <int L, int l>
 __device__ inline float head_part(const float* sD, const float* yte, const float* dyi, int C, int c) {
+  keep_order();
   float v[2 * L + 1];
   rotate_back<L, l>(sD, yte, C, c, v);
   float s = 0.0f;
@@ -343,7 +350,7 @@ __device__ inline float head_sum(const float* sD, const float* yte, const float*
 
 // Pass 1: s^h of every edge and Sbar_i^h += a^h s^h.
 template <int L>
-__global__ void __launch_bounds__(kLane) bwd_sbar_kernel(BwdParams P) {
+__global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4))) bwd_sbar_kernel(BwdParams P) {
   constexpr int nw = wig_total(L);
   constexpr int nc = n_comp(L);
   __shared__ float sD[nw];
@@ -372,6 +379,7 @@ __device__ inline void dyt_degree(const float* sD, const float* sJ, float* yte, 
                                   float av, float (&dir)[3]) {
   constexpr int n = 2 * l + 1;
   constexpr int nw = wig_total(L);
+  keep_order();
   float v[2 * L + 1];
   rotate_back<L, l>(sD, yte, C, c, v);
   float dv[n];
@@ -379,6 +387,7 @@ __device__ inline void dyt_degree(const float* sD, const float* sJ, float* yte, 
   for (int b = 0; b < n; ++b) dv[b] = av * dyi[(int64_t)(l * l + b) * C + c];
 #pragma unroll
   for (int ax = 0; ax < 3; ++ax) {
+    keep_order();
     const float* Jl = sJ + ax * nw + wig_offset(l);
     float s = 0.0f;
 #pragma unroll
@@ -390,6 +399,7 @@ __device__ inline void dyt_degree(const float* sD, const float* sJ, float* yte, 
     }
     dir[ax] += s;
   }
+  keep_order();
   const float* Dl = sD + wig_offset(l);
 #pragma unroll
   for (int r = 0; r < n; ++r) {
@@ -412,7 +422,7 @@ __device__ inline void dyt_all(const float* sD, const float* sJ, float* yte, con
 // Pass 2, first half: s^h again, dL/dz, dL/du, dyt (over yt), the first
 // direction term, dq and dk.
 template <int L>
-__global__ void __launch_bounds__(kLane) bwd_dyt_kernel(BwdParams P) {
+__global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4))) bwd_dyt_kernel(BwdParams P) {
   constexpr int nw = wig_total(L);
   constexpr int nc = n_comp(L);
   __shared__ float sD[nw];
@@ -446,6 +456,7 @@ __global__ void __launch_bounds__(kLane) bwd_dyt_kernel(BwdParams P) {
     du = wave_sum(du);
     __syncthreads();
     float dir[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll 1
     for (int c = lane; c < C; c += kLane) {
       const int h = c / d;
       dyt_all<L, 0>(sD, sJ, yte, dyi, C, c, sa[h], dir);
@@ -472,6 +483,7 @@ __device__ inline void final_degree(const float* sD, const float* sDJ, const flo
                                     int C, int c, float g, float& dg, float (&dir)[3]) {
   constexpr int n = 2 * l + 1;
   constexpr int nw = wig_total(L);
+  keep_order();
   float xv[n], gx[n];
 #pragma unroll
   for (int b = 0; b < n; ++b) xv[b] = load_as_float(xj, (int64_t)(l * l + b) * C + c);
@@ -487,6 +499,7 @@ __device__ inline void final_degree(const float* sD, const float* sDJ, const flo
   }
 #pragma unroll
   for (int ax = 0; ax < 3; ++ax) {
+    keep_order();
     const float* R = sDJ + ax * nw + wig_offset(l);
     float s = 0.0f;
 #pragma unroll
@@ -498,6 +511,7 @@ __device__ inline void final_degree(const float* sD, const float* sDJ, const flo
     }
     dir[ax] += s;
   }
+  keep_order();
 #pragma unroll
   for (int b = 0; b < n; ++b) {
     float s = 0.0f;
@@ -519,7 +533,7 @@ __device__ inline void final_all(const float* sD, const float* sDJ, const float*
 // Pass 2, second half (after dxt = map^T(dyt) is in the xt buffer): dg,
 // dx_j, the radial and direction parts of the edge vector's gradient.
 template <int L, typename T>
-__global__ void __launch_bounds__(kLane) bwd_final_kernel(BwdParams P) {
+__global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4))) bwd_final_kernel(BwdParams P) {
   constexpr int nw = wig_total(L);
   constexpr int nc = n_comp(L);
   __shared__ float sD[nw];
@@ -553,6 +567,7 @@ __global__ void __launch_bounds__(kLane) bwd_final_kernel(BwdParams P) {
     float* dxj = P.dx + (int64_t)j * nc * C;
     float dir[3] = {0.0f, 0.0f, 0.0f};
     float rad = 0.0f;
+#pragma unroll 1
     for (int c = lane; c < C; c += kLane) {
       float dg = 0.0f;
       final_all<L, 0, T>(sD, sDJ, xte, xj, dxj, C, c, B.g[(int64_t)e * C + c], dg, dir);
@@ -588,10 +603,11 @@ __global__ void __launch_bounds__(kLane) bwd_final_kernel(BwdParams P) {
 // C (+)= A B on the matrix cores (v_mfma_f32_16x16x4_f32), fp32 throughout.
 //   A(m, k) = A[m lda + k]      (AT = false)  or A[k lda + m] (AT = true)
 //   B(k, n) = B[n ldb + k]      (BT = true)   or B[k ldb + n] (BT = false)
-// 64 x 64 tiles of C per workgroup (4 waves, 32 x 32 each), K in steps of
-// 16 staged through LDS; blockIdx.z splits K into ranges of kSplit.  Mode:
-// store (C = AB, one workgroup per tile) or atomic (C += AB, fp32 atomics,
-// any number of K ranges).
+// 128 x 128 tiles of C per workgroup (4 waves, 64 x 64 each: 16 MFMA tiles
+// of 16 x 16), K in steps of 16 staged through LDS; the next step's global
+// loads go to registers while the current step's MFMAs run.  blockIdx.z
+// splits K into ranges of k_split.  Mode: store (C = AB, one workgroup per
+// tile) or atomic (C += AB, fp32 atomics, any number of K ranges).
 struct GemmArgs {
   const float* A;
   const float* B;
@@ -602,70 +618,84 @@ struct GemmArgs {
   int atomic;
 };
 
+constexpr int kGemmTile = 128;
+
 template <bool AT, bool BT>
 __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
-  constexpr int BM = 64, BN = 64, BK = 16, LDP = BM + 16;  // row pad: the 4 k-rows of a read hit distinct banks
+  constexpr int BM = kGemmTile, BN = kGemmTile, BK = 16;
+  constexpr int LDP = BM + 16;  // row pad: the 4 k-rows of one MFMA operand read hit distinct banks
   __shared__ float As[BK][LDP];
   __shared__ float Bs[BK][LDP];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
-  const int wm = (w >> 1) * 32, wn = (w & 1) * 32;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
   const int kb = blockIdx.z * g.k_split;
   const int ke = min(g.K, kb + g.k_split);
-  f32x4 acc[2][2];
+  // this thread's 8 elements of the A and B tiles: coalesced along the
+  // contiguous dimension of each operand
+  int am[8], ak[8], bn[8], bk[8];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int r = 0; r < 8; ++r) {
+    if constexpr (AT) {
+      am[r] = t & 127;
+      ak[r] = (t >> 7) + 2 * r;
+    } else {
+      ak[r] = t & 15;
+      am[r] = (t >> 4) + 16 * r;
+    }
+    if constexpr (BT) {
+      bk[r] = t & 15;
+      bn[r] = (t >> 4) + 16 * r;
+    } else {
+      bn[r] = t & 127;
+      bk[r] = (t >> 7) + 2 * r;
+    }
+  }
+  float ra[8], rb[8];
+  auto load = [&](int k0) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int r = 0; r < 8; ++r) {
+      const int gm = m0 + am[r], gk = k0 + ak[r];
+      ra[r] = (gm < g.M && gk < ke) ? (AT ? g.A[(int64_t)gk * g.lda + gm] : g.A[(int64_t)gm * g.lda + gk]) : 0.0f;
+      const int gn = n0 + bn[r], gk2 = k0 + bk[r];
+      rb[r] = (gn < g.N && gk2 < ke) ? (BT ? g.B[(int64_t)gn * g.ldb + gk2] : g.B[(int64_t)gk2 * g.ldb + gn]) : 0.0f;
+    }
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (kb < ke) load(kb);
   for (int k0 = kb; k0 < ke; k0 += BK) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int m, k;
-      if constexpr (AT) {
-        m = t & 63;
-        k = (t >> 6) + 4 * r;
-      } else {
-        k = t & 15;
-        m = (t >> 4) + 16 * r;
-      }
-      const int gm = m0 + m, gk = k0 + k;
-      float v = 0.0f;
-      if (gm < g.M && gk < ke) v = AT ? g.A[(int64_t)gk * g.lda + gm] : g.A[(int64_t)gm * g.lda + gk];
-      As[k][m] = v;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int n, k;
-      if constexpr (BT) {
-        k = t & 15;
-        n = (t >> 4) + 16 * r;
-      } else {
-        n = t & 63;
-        k = (t >> 6) + 4 * r;
-      }
-      const int gn = n0 + n, gk = k0 + k;
-      float v = 0.0f;
-      if (gn < g.N && gk < ke) v = BT ? g.B[(int64_t)gn * g.ldb + gk] : g.B[(int64_t)gk * g.ldb + gn];
-      Bs[k][n] = v;
+    for (int r = 0; r < 8; ++r) {
+      As[ak[r]][am[r]] = ra[r];
+      Bs[bk[r]][bn[r]] = rb[r];
     }
     __syncthreads();
+    if (k0 + BK < ke) load(k0 + BK);
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 4) {
       const int kr = kk + (lane >> 4);
-      const float a0 = As[kr][wm + (lane & 15)], a1 = As[kr][wm + 16 + (lane & 15)];
-      const float b0 = Bs[kr][wn + (lane & 15)], b1 = Bs[kr][wn + 16 + (lane & 15)];
-      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av[i] = As[kr][wm + 16 * i + (lane & 15)];
+        bv[i] = Bs[kr][wn + 16 * i + (lane & 15)];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[j], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
   }
   // C layout: lane holds rows 4 (lane / 16) + r, column lane % 16 of each 16 x 16 tile
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + wm + 16 * a + 4 * (lane >> 4) + r;
@@ -686,14 +716,15 @@ so2_status gemm(const float* A, int64_t lda, const float* B, int64_t ldb, float*
   unsigned splits = 1;
   if (atomic) {
     // K ranges of at least 512 so that the tile grid covers the device
-    const int64_t tiles = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
+    const int64_t tiles = (int64_t)((M + kGemmTile - 1) / kGemmTile) * ((N + kGemmTile - 1) / kGemmTile);
     const int64_t want = std::max<int64_t>(1, 2048 / std::max<int64_t>(tiles, 1));
     const int64_t by_k = std::max<int64_t>(1, K / 512);
     splits = (unsigned)std::min(want, by_k);
     g.k_split = (int)(((K + splits - 1) / splits + 15) / 16 * 16);
     splits = (unsigned)((K + g.k_split - 1) / g.k_split);
   }
-  hipLaunchKernelGGL((gemm_f32_kernel<AT, BT>), dim3((unsigned)((M + 63) / 64), (unsigned)((N + 63) / 64), splits),
+  hipLaunchKernelGGL((gemm_f32_kernel<AT, BT>),
+                     dim3((unsigned)((M + kGemmTile - 1) / kGemmTile), (unsigned)((N + kGemmTile - 1) / kGemmTile), splits),
                      dim3(256), 0, stream, g);
   SO2_CHECK_LAUNCH();
   return SO2_OK;
