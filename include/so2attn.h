@@ -252,7 +252,7 @@ so2_status so2_attention_fwd_variant(const so2_attn_desc* desc, const so2_attn_v
  * dy = dL/dy, returns dL/dx, dL/dpos and dL/dW for the same forward (same
  * descriptor, graph and inputs).  Memory stays linear in the atom count:
  * per-edge tensors exist only for one batch of edges at a time (64 per
- * target, between 4096 and 32768 edges, fixed by n_targets), and only the
+ * target, between 4096 and 65536 edges, fixed by n_targets), and only the
  * softmax statistics and head sums per (target, head) live across batches.
  *   dy        [n_targets][(L+1)^2][C] fp32
  *   dx        [n_atoms][(L+1)^2][C] fp32, written (sources and targets)

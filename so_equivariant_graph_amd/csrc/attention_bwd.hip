@@ -781,19 +781,11 @@ __global__ void __launch_bounds__(256) dw_fold_kernel(const float* __restrict__ 
   }
 }
 
-// dx[a][0][c] += sum_o dq[a][o] w_q[c][o] (a < n_targets) + sum_o dk[a][o] w_k[c][o]
+// dst[i] = src[i] in fp32 (W_q and W_k for the projection GEMMs).
 template <typename T>
-__global__ void __launch_bounds__(256) proj_bwd_dx_kernel(const float* __restrict__ dq, const float* __restrict__ dk,
-                                                          const void* w_q, const void* w_k, float* __restrict__ dx,
-                                                          int n_atoms, int n_targets, int nc, int C) {
-  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)n_atoms * C) return;
-  const int a = (int)(idx / C), c = (int)(idx % C);
-  float acc = 0.0f;
-  if (a < n_targets)
-    for (int o = 0; o < C; ++o) acc += dq[(int64_t)a * C + o] * load_as_float((const T*)w_q, (int64_t)c * C + o);
-  for (int o = 0; o < C; ++o) acc += dk[(int64_t)a * C + o] * load_as_float((const T*)w_k, (int64_t)c * C + o);
-  dx[(int64_t)a * nc * C + c] += acc;
+__global__ void __launch_bounds__(256) to_f32_kernel(const void* src, float* __restrict__ dst, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = load_as_float((const T*)src, i);
 }
 
 // dw[c][o] += sum over a block of atoms of x[a][0][c] g[a][o] (g = dq or dk)
@@ -815,8 +807,50 @@ __global__ void fill_zero_kernel(float* p, int64_t n) {
     p[i] = 0.0f;
 }
 
-__global__ void generators_kernel(float* gen, float* scratch, int L) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) wigner_generators(L, gen, scratch);
+// The rotation generators J_a (wigner_generators' recursion, one degree at a
+// time): wave a takes axis a, its lanes the entries of each degree, which
+// depend on degree l - 1 of the same axis and on the identity.
+__global__ void __launch_bounds__(192) generators_kernel(float* gen, int L) {
+  constexpr int kTot = wig_total(kMaxL);
+  __shared__ float ident[kTot];
+  __shared__ float J[3][kTot];
+  const int t = threadIdx.x, ax = t / 64, lane = t % 64;
+  const int tot = wig_total(L);
+  for (int q = t; q < tot; q += 192) ident[q] = 0.0f;
+  __syncthreads();
+  for (int l = 0; l <= L; ++l)
+    for (int m = t; m < 2 * l + 1; m += 192) ident[wig_offset(l) + m * (2 * l + 1) + m] = 1.0f;
+  if (lane == 0) {
+    J[ax][0] = 0.0f;
+    if (L >= 1) {
+      // [e_a]x for a = x, y, z, row-major
+      float E[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+      if (ax == 0) {
+        E[5] = -1.0f;
+        E[7] = 1.0f;
+      } else if (ax == 1) {
+        E[2] = 1.0f;
+        E[6] = -1.0f;
+      } else {
+        E[1] = -1.0f;
+        E[3] = 1.0f;
+      }
+      wigner_l1(E, &J[ax][wig_offset(1)]);
+    }
+  }
+  __syncthreads();
+  for (int l = 2; l <= L; ++l) {
+    const int n = 2 * l + 1;
+    const float* J1 = &J[ax][wig_offset(1)];
+    const float* Jp = &J[ax][wig_offset(l - 1)];
+    const float* I1 = ident + wig_offset(1);
+    const float* Ip = ident + wig_offset(l - 1);
+    for (int q = lane; q < n * n; q += 64)
+      J[ax][wig_offset(l) + q] =
+          wigner_entry(l, q / n - l, q % n - l, J1, Ip) + wigner_entry(l, q / n - l, q % n - l, I1, Jp);
+    __syncthreads();
+  }
+  for (int q = lane; q < tot; q += 64) gen[ax * tot + q] = J[ax][q];
 }
 
 so2_status fill_zero(float* p, int64_t n, hipStream_t stream) {
@@ -829,17 +863,17 @@ so2_status fill_zero(float* p, int64_t n, hipStream_t stream) {
 
 // ---------------------------------------------------------------- workspace
 
-// Edges per batch: 64 per target, between 4096 and 32768.
+// Edges per batch: 64 per target, between 4096 and 65536.
 int64_t batch_edges(int n_targets) {
   const int64_t want = ((int64_t)n_targets * 64 + 255) / 256 * 256;
-  return std::min<int64_t>(32768, std::max<int64_t>(4096, want));
+  return std::min<int64_t>(65536, std::max<int64_t>(4096, want));
 }
 
 size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Offsets (bytes) of the backward's scratch arrays.
 struct BwdScratch {
-  size_t dq, dk, gen, smax, sinv, sbar, bm, db, xt, yt, D, g, gp, dg, phi, a, ab, sc, tgt, total;
+  size_t dq, dk, gen, wq, wk, smax, sinv, sbar, bm, db, xt, yt, D, g, gp, dg, phi, a, ab, sc, tgt, total;
   int64_t cap;
   BwdScratch(int n_atoms, int n_targets, int L, int C, int H, int K) {
     cap = batch_edges(n_targets);
@@ -853,7 +887,9 @@ struct BwdScratch {
     };
     dq = take(4 * (size_t)n_targets * C);
     dk = take(4 * (size_t)n_atoms * C);
-    gen = take(4 * 4 * nw);
+    gen = take(4 * 3 * nw);
+    wq = take(4 * (size_t)C * C);
+    wk = take(4 * (size_t)C * C);
     smax = take(4 * (size_t)n_targets * H);
     sinv = take(4 * (size_t)n_targets * H);
     sbar = take(4 * (size_t)n_targets * H);
@@ -952,7 +988,7 @@ so2_status launch_attention_bwd(const AttnArgs& a, const float* dy, float* dx, f
   if (n_edges < 0) return SO2_ERR_INVALID_ARGUMENT;
 
   if (n_edges > 0) {
-    hipLaunchKernelGGL(generators_kernel, dim3(1), dim3(64), 0, stream, gen, gen + 3 * wig_total(L), L);
+    hipLaunchKernelGGL(generators_kernel, dim3(1), dim3(192), 0, stream, gen, L);
     SO2_CHECK_LAUNCH();
     const unsigned nbw = 1024;
     if (a.dtype == SO2_BF16)
@@ -1065,19 +1101,24 @@ so2_status launch_attention_bwd(const AttnArgs& a, const float* dy, float* dx, f
     if ((st = fill_zero(dw_so2, so2_w1_offset(L, C, L + 1), stream)) != SO2_OK) return st;
   }
 
-  // the projections of the l = 0 slice
-  const int64_t nxc = (int64_t)a.n_atoms * C;
-  const unsigned gdx = (unsigned)((nxc + 255) / 256);
-  const unsigned gw = (unsigned)(((int64_t)C * C + 255) / 256);
-  if (gdx > 0) {
-    if (a.dtype == SO2_BF16)
-      hipLaunchKernelGGL(proj_bwd_dx_kernel<uint16_t>, dim3(gdx), dim3(256), 0, stream, dq, dk, a.w_q, a.w_k, dx,
-                         a.n_atoms, a.n_targets, nc, C);
-    else
-      hipLaunchKernelGGL(proj_bwd_dx_kernel<float>, dim3(gdx), dim3(256), 0, stream, dq, dk, a.w_q, a.w_k, dx,
-                         a.n_atoms, a.n_targets, nc, C);
-    SO2_CHECK_LAUNCH();
+  // the projections of the l = 0 slice: dx[., 0, .] += dq W_q^T + dk W_k^T
+  // as fp32 GEMMs (weights widened once)
+  float* wq32 = (float*)(ws + S.wq);
+  float* wk32 = (float*)(ws + S.wk);
+  const int64_t cc = (int64_t)C * C;
+  const unsigned gcc = (unsigned)std::min<int64_t>((cc + 255) / 256, 1024);
+  if (a.dtype == SO2_BF16) {
+    hipLaunchKernelGGL(to_f32_kernel<uint16_t>, dim3(gcc), dim3(256), 0, stream, a.w_q, wq32, cc);
+    hipLaunchKernelGGL(to_f32_kernel<uint16_t>, dim3(gcc), dim3(256), 0, stream, a.w_k, wk32, cc);
+  } else {
+    hipLaunchKernelGGL(to_f32_kernel<float>, dim3(gcc), dim3(256), 0, stream, a.w_q, wq32, cc);
+    hipLaunchKernelGGL(to_f32_kernel<float>, dim3(gcc), dim3(256), 0, stream, a.w_k, wk32, cc);
   }
+  SO2_CHECK_LAUNCH();
+  const int64_t ldx = (int64_t)nc * C;
+  if ((st = gemm<false, true>(dq, C, wq32, C, dx, ldx, a.n_targets, C, C, true, stream)) != SO2_OK) return st;
+  if ((st = gemm<false, true>(dk, C, wk32, C, dx, ldx, a.n_atoms, C, C, true, stream)) != SO2_OK) return st;
+  const unsigned gw = (unsigned)((cc + 255) / 256);
   if (dw_q && a.n_targets > 0) {
     if (a.dtype == SO2_BF16)
       hipLaunchKernelGGL(proj_bwd_dw_kernel<uint16_t>, dim3(gw, (a.n_targets + kProjAtoms - 1) / kProjAtoms),

@@ -7,8 +7,10 @@ fp32 bound applies: 1e-4 max relative error, normalised per atom for dx and
 dpos (the parity metric of the forward) and by the largest entry for the
 weight gradients.  Cases: the tiny fp32 workload (every atom, both flags),
 a small periodic water box, a bf16 batch at L = 4, C = 128, L = 6, empty
-neighbourhoods with n_targets < n_atoms; on the GPU's own output, forces
-that sum to zero and rotate with the system."""
+neighbourhoods with n_targets < n_atoms, targets whose edges take two and
+three batches (64 edges per target, at least 4096: the second pass then
+recomputes every batch but the last of the first); on the GPU's own output,
+forces that sum to zero and rotate with the system."""
 
 import numpy as np
 import pytest
@@ -108,6 +110,18 @@ def test_empty_rows_and_partial_targets():
     w.pos[5] = [500.0, 500.0, 500.0]
     g, r, rp, _ = _case(w, n_targets=40)
     assert np.all(g["dx"][5] == 0.0) and np.all(g["dpos"][5] == 0.0)
+    assert max(_compare(g, r).values()) <= TOL
+
+
+@pytest.mark.parametrize("cutoff,batches,L,C,dtype", [(6.0, 2, 2, 16, "fp32"), (7.5, 3, 2, 16, "fp32"),
+                                                      (6.0, 2, 4, 128, "bf16")])
+def test_edges_in_several_batches(cutoff, batches, L, C, dtype):
+    say("backward edge batches", cutoff, batches, L, C, dtype)
+    w = make_workload("water_l6", l_max=L, channels=C, heads=2, n_rbf=8, dtype=dtype, cutoff=cutoff)
+    nt = 64  # batch capacity max(4096, 64 nt) = 4096 edges
+    g, r, rp, _ = _case(w, n_targets=nt)
+    n_edges = int(rp[nt] - rp[0])
+    assert (batches - 1) * 4096 < n_edges <= batches * 4096, n_edges
     assert max(_compare(g, r).values()) <= TOL
 
 
