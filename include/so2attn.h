@@ -157,8 +157,9 @@ int64_t so2_weight_count(int32_t l_max, int32_t channels);
 /* Workspace so2_attention_fwd needs (0 if desc is invalid). */
 size_t so2_attention_workspace_bytes(const so2_attn_desc* desc);
 
-/* Which kernel so2_attention_fwd runs for desc: 0 = none (the call returns
- * UNSUPPORTED), 1 = fp32 VALU kernel, 2 = bf16 MFMA kernel. */
+/* Which path so2_attention_fwd runs for desc: 0 = none (the call returns
+ * UNSUPPORTED), 2 = bf16 MFMA kernel, 3 = fp32 edge-batch path (1, the fp32
+ * VALU kernel, is what so2_attention_fwd_noalloc takes instead of 3). */
 int32_t so2_attention_kernel_kind(const so2_attn_desc* desc);
 
 /*   desc      host struct above
@@ -175,11 +176,19 @@ int32_t so2_attention_kernel_kind(const so2_attn_desc* desc);
  * repacked copy of x with 32-bit offsets, which caps n_atoms at
  * (2^32 - 2^16) / (2 (L+1)(L+2) C) (about 559k atoms at L = 4, 299k at
  * L = 6); beyond that the call returns UNSUPPORTED.  Every other shape
- * (fp32, or bf16 with other C, L, H or K) runs on the fp32 VALU kernel.
- * Errors: INVALID_ARGUMENT, UNSUPPORTED (L > 6, C > 256, or the MFMA shape
- * past its atom limit), BOX, WORKSPACE, DEVICE.  Asynchronous on `stream`.
+ * (fp32, or bf16 with other C, L, H or K) runs on the fp32 edge-batch path:
+ * per-edge kernels for the frame, the rotations and the softmax weights,
+ * the per-m maps as fp32 GEMMs on the matrix cores over batches of 64 edges
+ * per target (4096 to 65536 edges, fixed by n_targets), and a per-target
+ * sum in edge order (bitwise repeatable).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (L > 6, C > 256, H > 256, or the
+ * MFMA shape past its atom limit), BOX, WORKSPACE, DEVICE.
+ * Stream: the MFMA kernel is asynchronous on `stream`; the edge-batch path
+ * reads row_ptr[0] and row_ptr[n_targets] back to plan its batches, which
+ * waits on `stream` once.
  * Device memory beyond the caller's buffers: none; activation memory is
- * O(n_atoms) (workspace), never O(E). */
+ * O(n_atoms) (workspace; the edge-batch path adds one batch of per-edge
+ * tensors, a constant), never O(E). */
 so2_status so2_attention_fwd(const so2_attn_desc* desc, const float* pos,
                              const float* box_host, const int32_t* row_ptr,
                              const int32_t* col, const void* x, const void* w_q,
@@ -291,8 +300,11 @@ so2_status so2_attention_bwd(const so2_attn_desc* desc, const float* pos, const 
  * as so2_attention_fwd without the workspace: the call uses a device array
  * of SO2_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
  * on until the process ends (looked up once per device on the first call
- * there), and it allocates nothing.  The caller still passes inputs and y.
- *   Limit: so2_attention_workspace_bytes(desc) <= SO2_NOALLOC_SCRATCH_BYTES
+ * there), and it allocates nothing and never waits on the stream: shapes
+ * that so2_attention_fwd runs on the edge-batch path run here on the fp32
+ * VALU kernel (one workgroup per target, asynchronous).  The caller still
+ * passes inputs and y.
+ *   Limit: the workspace of that kernel <= SO2_NOALLOC_SCRATCH_BYTES
  *   (about 14,000 atoms at L = 4, C = 128, bf16; 8,500 at L = 6), else
  *   SO2_ERR_WORKSPACE before anything is launched.
  *   Every call rewrites all of the array it reads, so nothing carries over

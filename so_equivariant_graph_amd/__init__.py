@@ -35,7 +35,7 @@ SO2_BF16 = 1
 FLAG_RBF_ENVELOPE = 1
 FLAG_NO_RADIAL = 2
 
-KERNEL_NONE, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
+KERNEL_NONE, KERNEL_VALU, KERNEL_MFMA, KERNEL_BATCH = 0, 1, 2, 3
 
 STAGE_PREPARE = 1  # so2_attention_fwd_stages: q/k, statistics, repack, schedule
 STAGE_FUSED = 2  # the fused attention kernel

@@ -28,7 +28,7 @@ SOURCES = [
     "swiglu.hip",
     "attention_valu.hip",
     "attention_mfma.hip",
-    "attention_bwd.hip",
+    "attention_batch.hip",
     "noalloc.hip",
 ]
 

@@ -24,7 +24,7 @@ namespace {
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-enum Kind { kNone = 0, kValu = 1, kMfma = 2 };
+enum Kind { kNone = 0, kValu = 1, kMfma = 2, kBatch = 3 };
 
 so2_status check_desc(const so2_attn_desc* d) {
   if (!d) return SO2_ERR_INVALID_ARGUMENT;
@@ -55,12 +55,17 @@ bool is_base(const so2_attn_desc* d, const so2_attn_variant* v) {
 }
 
 // bf16 shapes the MFMA kernel takes run there; past its size limit they are
-// refused (kNone) rather than moved to the untuned VALU kernel.  Truncated
-// orders and focus streams run on the VALU kernel.
-Kind pick_kind(const so2_attn_desc* d, const so2_attn_variant* v = &kBase) {
+// refused (kNone) rather than moved to a slower path.  Everything else
+// (fp32, other shapes, truncated orders, focus streams) runs on the fp32
+// edge-batch path, which reads the edge count back once; with allow_wait
+// false (callers that must not wait on the stream) it runs on the fp32
+// VALU kernel instead, which takes the base layer only.
+Kind pick_kind(const so2_attn_desc* d, const so2_attn_variant* v = &kBase, bool allow_wait = true) {
   if (is_base(d, v) && d->dtype == SO2_BF16 && mfma_shape(d->l_max, d->channels, d->heads, d->n_rbf))
     return mfma_fits(d->l_max, d->n_atoms) ? kMfma : kNone;
-  if (valu_supported(d->l_max, d->channels, d->heads)) return kValu;
+  const int mm = v->m_max < 0 ? d->l_max : v->m_max;
+  if (allow_wait && batch_fwd_supported(d->l_max, d->channels, d->heads, d->n_rbf, mm, v->n_focus)) return kBatch;
+  if (!allow_wait && is_base(d, v) && valu_supported(d->l_max, d->channels, d->heads)) return kValu;
   return kNone;
 }
 
@@ -68,7 +73,7 @@ struct AttnLayout {
   size_t q, k, scratch, scratch_bytes, total;
 };
 
-AttnLayout attn_layout(const so2_attn_desc* d, Kind kind) {
+AttnLayout attn_layout(const so2_attn_desc* d, Kind kind, const so2_attn_variant* v = &kBase) {
   AttnLayout L{};
   size_t off = 0;
   L.q = off;
@@ -76,8 +81,10 @@ AttnLayout attn_layout(const so2_attn_desc* d, Kind kind) {
   L.k = off;
   off += align256(sizeof(float) * (size_t)d->n_atoms * d->channels);
   L.scratch = off;
-  L.scratch_bytes = kind == kMfma ? mfma_scratch_bytes(d->n_atoms, d->n_targets, d->l_max, d->heads, d->n_rbf)
-                                  : valu_scratch_bytes(d->l_max, d->channels);
+  const int mm = v->m_max < 0 ? d->l_max : v->m_max;
+  L.scratch_bytes = kind == kMfma    ? mfma_scratch_bytes(d->n_atoms, d->n_targets, d->l_max, d->heads, d->n_rbf)
+                    : kind == kBatch ? batch_fwd_scratch_bytes(d->n_targets, d->l_max, d->channels, d->heads, mm)
+                                     : valu_scratch_bytes(d->l_max, d->channels);
   off += align256(L.scratch_bytes);
   L.total = off;
   return L;
@@ -166,21 +173,22 @@ static so2_status attention_fwd_impl(uint32_t stages, const so2_attn_desc* desc,
                                      const float* pos, const float* box_host, const int32_t* row_ptr,
                                      const int32_t* col, const void* x, const void* w_q, const void* w_k,
                                      const void* w_rad, const void* w_so2, const void* w_logit, const void* w_focus,
-                                     float* y, void* workspace, size_t workspace_bytes, so2_stream_t stream) {
+                                     float* y, void* workspace, size_t workspace_bytes, so2_stream_t stream,
+                                     bool allow_wait = true) {
   if (stages == 0 || (stages & ~(uint32_t)(SO2_STAGE_PREPARE | SO2_STAGE_FUSED))) return SO2_ERR_INVALID_ARGUMENT;
   so2_status st = check_desc(desc);
   if (st != SO2_OK) return st;
   st = check_variant(desc, var);
   if (st != SO2_OK) return st;
   if (var->n_focus > 1 && !w_focus) return SO2_ERR_INVALID_ARGUMENT;
-  Kind kind = pick_kind(desc, var);
+  Kind kind = pick_kind(desc, var, allow_wait);
   if (kind == kNone) return SO2_ERR_UNSUPPORTED;
   st = check_box(box_host, desc->cutoff);
   if (st != SO2_OK) return st;
   if (!pos || !row_ptr || !col || !x || !w_q || !w_k || !w_rad || !w_so2 || !workspace)
     return SO2_ERR_INVALID_ARGUMENT;
   if ((stages & SO2_STAGE_FUSED) && !y) return SO2_ERR_INVALID_ARGUMENT;
-  const AttnLayout lay = attn_layout(desc, kind);
+  const AttnLayout lay = attn_layout(desc, kind, var);
   if (workspace_bytes < lay.total || ((uintptr_t)workspace & 255)) return SO2_ERR_WORKSPACE;
 
   AttnArgs a{};
@@ -227,7 +235,9 @@ static so2_status attention_fwd_impl(uint32_t stages, const so2_attn_desc* desc,
     }
   }
   if (stages & SO2_STAGE_FUSED) {
-    st = kind == kMfma ? launch_attention_mfma(a, s) : launch_attention_valu(a, s);
+    st = kind == kMfma ? launch_attention_mfma(a, s)
+         : kind == kBatch ? launch_attention_batch_fwd(a, s)
+                          : launch_attention_valu(a, s);
     if (st != SO2_OK) return st;
   }
   return SO2_OK;
@@ -326,7 +336,7 @@ size_t so2_attention_variant_workspace_bytes(const so2_attn_desc* desc, const so
   if (check_desc(desc) != SO2_OK || check_variant(desc, var) != SO2_OK) return 0;
   Kind kind = pick_kind(desc, var);
   if (kind == kNone) return 0;
-  return attn_layout(desc, kind).total;
+  return attn_layout(desc, kind, var).total;
 }
 
 int32_t so2_attention_variant_kernel_kind(const so2_attn_desc* desc, const so2_attn_variant* var) {
@@ -395,3 +405,22 @@ so2_status so2_wigner_generators_host(int32_t l_max, float* J_out) {
 }
 
 }  // extern "C"
+
+namespace so2 {
+
+size_t attention_nowait_workspace_bytes(const so2_attn_desc* desc) {
+  if (check_desc(desc) != SO2_OK) return 0;
+  Kind kind = pick_kind(desc, &kBase, false);
+  if (kind == kNone) return 0;
+  return attn_layout(desc, kind).total;
+}
+
+so2_status attention_fwd_nowait(const so2_attn_desc* desc, const float* pos, const float* box_host,
+                                const int32_t* row_ptr, const int32_t* col, const void* x, const void* w_q,
+                                const void* w_k, const void* w_rad, const void* w_so2, float* y, void* workspace,
+                                size_t workspace_bytes, so2_stream_t stream) {
+  return attention_fwd_impl(SO2_STAGE_PREPARE | SO2_STAGE_FUSED, desc, &kBase, pos, box_host, row_ptr, col, x, w_q,
+                            w_k, w_rad, w_so2, nullptr, nullptr, y, workspace, workspace_bytes, stream, false);
+}
+
+}  // namespace so2

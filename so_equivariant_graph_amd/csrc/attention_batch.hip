@@ -65,7 +65,7 @@ namespace {
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kLane = 64;       // per-edge and per-target kernels: one wave per block
-constexpr int kMaxBwdHeads = 64;  // heads are held one per lane
+constexpr int kMaxHeadsB = 256;  // heads (and focus streams), per-lane loops of stride 64
 constexpr int kScal = 12;       // per-edge scalars (EdgeBufs::sc)
 constexpr int kGridCap = 16384; // blocks of a grid-stride per-edge launch
 
@@ -107,8 +107,12 @@ struct EdgeBufs {
   int32_t* tgt;  // [cap]
 };
 
-struct BwdParams {
+struct BatchParams {
   const float* pos;
+  float* y;           // forward: [n_targets][(L+1)^2][C]
+  const void* w_logit;  // [K][H] radial logit bias, or null
+  const void* w_focus;  // [C] focus scores when n_focus > 1
+  int32_t m_max, n_focus;
   const int32_t* row_ptr;
   const int32_t* col;
   const void* x;
@@ -145,39 +149,78 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
+// Radial logit bias of head h for an edge of length rho: sum_k phi_k(rho)
+// w_logit[k][h] with the gate's Gaussian basis (0 without the bias).  sphi,
+// if given, holds phi_0 .. phi_63 of this edge.
+template <typename T>
+__device__ inline float logit_bias(const BatchParams& P, int h, float rho, const float* sphi) {
+  if (!P.w_logit) return 0.0f;
+  const float step = P.cutoff / (float)(P.K - 1);
+  const float inv2s2 = 1.0f / (2.0f * step * step);
+  float b = 0.0f;
+  for (int kk = 0; kk < P.K; ++kk) {
+    float ph;
+    if (sphi && kk < 64) {
+      ph = sphi[kk];
+    } else {
+      const float dr = rho - step * (float)kk;
+      ph = expf(-dr * dr * inv2s2);
+    }
+    b += ph * load_as_float((const T*)P.w_logit, (int64_t)kk * P.H + h);
+  }
+  return b;
+}
+
 // ---------------------------------------------------------------- statistics
 
 // One wave per target: for every head the running max of the logits and the
 // normaliser sum_j u_ij exp(z_ij - max), over the target's edges in order.
-__global__ void __launch_bounds__(kLane) bwd_stats_kernel(BwdParams P) {
-  __shared__ float zs[kMaxBwdHeads];
+// Lane l keeps heads l, l + 64, ...
+constexpr int kHeadsPerLane = kMaxHeadsB / kLane;
+template <typename T>
+__global__ void __launch_bounds__(kLane) batch_stats_kernel(BatchParams P) {
+  __shared__ float zs[kMaxHeadsB];
   const int lane = threadIdx.x;
   const int C = P.C, H = P.H, d = C / H;
   const float inv_sqrt_d = 1.0f / sqrtf((float)d);
   for (int i = blockIdx.x; i < P.n_targets; i += gridDim.x) {
-    float m = -INFINITY, sum = 0.0f;
+    float m[kHeadsPerLane], sum[kHeadsPerLane];
+#pragma unroll
+    for (int r = 0; r < kHeadsPerLane; ++r) {
+      m[r] = -INFINITY;
+      sum[r] = 0.0f;
+    }
     for (int e = P.row_ptr[i]; e < P.row_ptr[i + 1]; ++e) {
       const int j = P.col[e];
-      if (lane < H) zs[lane] = 0.0f;
+      for (int h = lane; h < H; h += kLane) zs[h] = 0.0f;
       __syncthreads();
       for (int c = lane; c < C; c += kLane) atomicAdd(&zs[c / d], P.q[(int64_t)i * C + c] * P.k[(int64_t)j * C + c]);
       __syncthreads();
       if (lane < H) {
         const EdgeGeo geo = edge_geometry(P.pos, i, j, P.periodic, P.box, P.cutoff);
         const float u = envelope_u(geo.s, geo.t, P.p);
-        const float z = zs[lane] * inv_sqrt_d;
-        if (z > m) {
-          sum = sum * expf(m - z) + u;
-          m = z;
-        } else {
-          sum += u * expf(z - m);
+#pragma unroll
+        for (int r = 0; r < kHeadsPerLane; ++r) {
+          const int h = lane + kLane * r;
+          if (h >= H) break;
+          const float z = zs[h] * inv_sqrt_d + logit_bias<T>(P, h, geo.rho, nullptr);
+          if (z > m[r]) {
+            sum[r] = sum[r] * expf(m[r] - z) + u;
+            m[r] = z;
+          } else {
+            sum[r] += u * expf(z - m[r]);
+          }
         }
       }
       __syncthreads();
     }
-    if (lane < H) {
-      P.smax[(int64_t)i * H + lane] = m;
-      P.sinv[(int64_t)i * H + lane] = sum > 0.0f ? 1.0f / sum : 0.0f;
+#pragma unroll
+    for (int r = 0; r < kHeadsPerLane; ++r) {
+      const int h = lane + kLane * r;
+      if (h < H) {
+        P.smax[(int64_t)i * H + h] = m[r];
+        P.sinv[(int64_t)i * H + h] = sum[r] > 0.0f ? 1.0f / sum[r] : 0.0f;
+      }
     }
   }
 }
@@ -219,12 +262,12 @@ __device__ inline int edge_target(const int32_t* row_ptr, int n_targets, int64_t
 // Wigner-D, radial basis, gate and its |r| derivative, softmax weights, and
 // xt = g (.) D x_j in the block layout.
 template <int L, typename T>
-__global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4))) bwd_prep_kernel(BwdParams P) {
+__global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4))) bwd_prep_kernel(BatchParams P) {
   constexpr int nw = wig_total(L);
   constexpr int nc = n_comp(L);
   __shared__ float sD[nw];
   __shared__ float sphi[64];
-  __shared__ float zs[kMaxBwdHeads];
+  __shared__ float zs[kMaxHeadsB];
   const int lane = threadIdx.x;
   const int C = P.C, H = P.H, K = P.K, d = C / H;
   const float inv_sqrt_d = 1.0f / sqrtf((float)d);
@@ -252,17 +295,19 @@ __global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4)))
       const float dr = rho - mu_step * (float)kk;
       const float ph = expf(-dr * dr * inv2s2);
       if (kk < 64) sphi[kk] = ph;
-      B.phi[(int64_t)e * K + kk] = rbf_env ? ph * u : ph;
+      if (B.phi) B.phi[(int64_t)e * K + kk] = rbf_env ? ph * u : ph;
     }
-    if (lane < H) zs[lane] = 0.0f;
+    for (int h = lane; h < H; h += kLane) zs[h] = 0.0f;
     if (lane == 0) {
-      float* sc = B.sc + (int64_t)e * kScal;
-      sc[0] = rho;
-      sc[1] = u;
-      sc[2] = dudr;
-      sc[3] = rh[0];
-      sc[4] = rh[1];
-      sc[5] = rh[2];
+      if (B.sc) {
+        float* sc = B.sc + (int64_t)e * kScal;
+        sc[0] = rho;
+        sc[1] = u;
+        sc[2] = dudr;
+        sc[3] = rh[0];
+        sc[4] = rh[1];
+        sc[5] = rh[2];
+      }
       B.tgt[e] = i;
     }
     __syncthreads();
@@ -281,8 +326,10 @@ __global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4)))
         g = rbf_env ? g0 * u : g0;
         gp = rbf_env ? gd * u + g0 * dudr : gd;
       }
-      B.g[(int64_t)e * C + c] = g;
-      B.gp[(int64_t)e * C + c] = gp;
+      if (B.g) {
+        B.g[(int64_t)e * C + c] = g;
+        B.gp[(int64_t)e * C + c] = gp;
+      }
       atomicAdd(&zs[c / d], P.q[(int64_t)i * C + c] * P.k[(int64_t)j * C + c]);
       const T* xj = x + (int64_t)j * nc * C + c;
 #pragma unroll
@@ -295,6 +342,8 @@ __global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4)))
         const float* Dl = sD + wig_offset(l);
 #pragma unroll
         for (int mr = 0; mr < n; ++mr) {
+          // orders past m_max have no block (their map output is 0)
+          if (mr - l > P.m_max || l - mr > P.m_max) continue;
           float v = 0.0f;
 #pragma unroll
           for (int b = 0; b < n; ++b) v += Dl[mr * n + b] * xv[b];
@@ -303,11 +352,11 @@ __global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4)))
       }
     }
     __syncthreads();
-    if (lane < H) {
-      const float z = zs[lane] * inv_sqrt_d;
-      const float ab = expf(z - P.smax[(int64_t)i * H + lane]) * P.sinv[(int64_t)i * H + lane];
-      B.ab[(int64_t)e * H + lane] = ab;
-      B.a[(int64_t)e * H + lane] = u * ab;
+    for (int h = lane; h < H; h += kLane) {
+      const float z = zs[h] * inv_sqrt_d + logit_bias<T>(P, h, rho, sphi);
+      const float ab = expf(z - P.smax[(int64_t)i * H + h]) * P.sinv[(int64_t)i * H + h];
+      B.ab[(int64_t)e * H + h] = ab;
+      B.a[(int64_t)e * H + h] = u * ab;
     }
     __syncthreads();
   }
@@ -350,24 +399,24 @@ __device__ inline float head_sum(const float* sD, const float* yte, const float*
 
 // Pass 1: s^h of every edge and Sbar_i^h += a^h s^h.
 template <int L>
-__global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4))) bwd_sbar_kernel(BwdParams P) {
+__global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4))) bwd_sbar_kernel(BatchParams P) {
   constexpr int nw = wig_total(L);
   constexpr int nc = n_comp(L);
   __shared__ float sD[nw];
-  __shared__ float ss[kMaxBwdHeads];
+  __shared__ float ss[kMaxHeadsB];
   const int lane = threadIdx.x;
   const int C = P.C, H = P.H, d = C / H;
   const EdgeBufs& B = P.b;
   for (int e = blockIdx.x; e < P.nb; e += gridDim.x) {
     const int i = B.tgt[e];
     for (int q = lane; q < nw; q += kLane) sD[q] = B.D[(int64_t)e * nw + q];
-    if (lane < H) ss[lane] = 0.0f;
+    for (int h = lane; h < H; h += kLane) ss[h] = 0.0f;
     __syncthreads();
     const float* yte = B.yt + (int64_t)e * nc * C;
     const float* dyi = P.dy + (int64_t)i * nc * C;
     for (int c = lane; c < C; c += kLane) atomicAdd(&ss[c / d], head_sum<L, 0>(sD, yte, dyi, C, c));
     __syncthreads();
-    if (lane < H) atomicAdd(P.sbar + (int64_t)i * H + lane, B.a[(int64_t)e * H + lane] * ss[lane]);
+    for (int h = lane; h < H; h += kLane) atomicAdd(P.sbar + (int64_t)i * H + h, B.a[(int64_t)e * H + h] * ss[h]);
     __syncthreads();
   }
 }
@@ -422,14 +471,14 @@ __device__ inline void dyt_all(const float* sD, const float* sJ, float* yte, con
 // Pass 2, first half: s^h again, dL/dz, dL/du, dyt (over yt), the first
 // direction term, dq and dk.
 template <int L>
-__global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4))) bwd_dyt_kernel(BwdParams P) {
+__global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4))) bwd_dyt_kernel(BatchParams P) {
   constexpr int nw = wig_total(L);
   constexpr int nc = n_comp(L);
   __shared__ float sD[nw];
   __shared__ float sJ[3 * nw];
-  __shared__ float ss[kMaxBwdHeads];
-  __shared__ float sdz[kMaxBwdHeads];
-  __shared__ float sa[kMaxBwdHeads];
+  __shared__ float ss[kMaxHeadsB];
+  __shared__ float sdz[kMaxHeadsB];
+  __shared__ float sa[kMaxHeadsB];
   const int lane = threadIdx.x;
   const int C = P.C, H = P.H, d = C / H;
   const float inv_sqrt_d = 1.0f / sqrtf((float)d);
@@ -439,19 +488,19 @@ __global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4)))
     const int i = B.tgt[e];
     const int j = P.col[P.e0 + e];
     for (int q = lane; q < nw; q += kLane) sD[q] = B.D[(int64_t)e * nw + q];
-    if (lane < H) ss[lane] = 0.0f;
+    for (int h = lane; h < H; h += kLane) ss[h] = 0.0f;
     __syncthreads();
     float* yte = B.yt + (int64_t)e * nc * C;
     const float* dyi = P.dy + (int64_t)i * nc * C;
     for (int c = lane; c < C; c += kLane) atomicAdd(&ss[c / d], head_sum<L, 0>(sD, yte, dyi, C, c));
     __syncthreads();
     float du = 0.0f;
-    if (lane < H) {
-      const float diff = ss[lane] - P.sbar[(int64_t)i * H + lane];
-      const float a = B.a[(int64_t)e * H + lane];
-      sdz[lane] = a * diff * inv_sqrt_d;
-      sa[lane] = a;
-      du = B.ab[(int64_t)e * H + lane] * diff;
+    for (int h = lane; h < H; h += kLane) {
+      const float diff = ss[h] - P.sbar[(int64_t)i * H + h];
+      const float a = B.a[(int64_t)e * H + h];
+      sdz[h] = a * diff * inv_sqrt_d;
+      sa[h] = a;
+      du += B.ab[(int64_t)e * H + h] * diff;
     }
     du = wave_sum(du);
     __syncthreads();
@@ -533,7 +582,7 @@ __device__ inline void final_all(const float* sD, const float* sDJ, const float*
 // Pass 2, second half (after dxt = map^T(dyt) is in the xt buffer): dg,
 // dx_j, the radial and direction parts of the edge vector's gradient.
 template <int L, typename T>
-__global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4))) bwd_final_kernel(BwdParams P) {
+__global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4))) bwd_final_kernel(BatchParams P) {
   constexpr int nw = wig_total(L);
   constexpr int nc = n_comp(L);
   __shared__ float sD[nw];
@@ -595,6 +644,95 @@ __global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4)))
       atomicAdd(P.dpos + 3 * (int64_t)i + 2, -gz);
     }
     __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- forward
+
+// Degree l of one channel of the forward message: v = D^T ytilde over the
+// orders up to m_max (the others have no block), times the edge's weight w,
+// into the natural layout [(L+1)^2][C].
+template <int L, int l>
+__device__ inline void fwd_degree(const float* sD, const float* yte, float* out, int C, int c, int m_max, float w) {
+  if constexpr (l <= L) {
+    constexpr int n = 2 * l + 1;
+    keep_order();
+    float yv[n];
+#pragma unroll
+    for (int r = 0; r < n; ++r) yv[r] = (r - l <= m_max && l - r <= m_max) ? yte[comp_col(L, C, l, r - l) + c] : 0.0f;
+    const float* Dl = sD + wig_offset(l);
+#pragma unroll
+    for (int b = 0; b < n; ++b) {
+      float s = 0.0f;
+#pragma unroll
+      for (int r = 0; r < n; ++r) s += Dl[r * n + b] * yv[r];
+      out[(int64_t)(l * l + b) * C + c] = w * s;
+    }
+    fwd_degree<L, l + 1>(sD, yte, out, C, c, m_max, w);
+  }
+}
+
+// Forward, per edge once the per-m maps are in yt: the cross-focus softmax
+// (n_focus > 1: pi_f = softmax_f(sum_{c in f} w_focus[c] ytilde[(0,0), c])),
+// the rotation back and the softmax weights; the edge's message
+// a^h pi_f D^T ytilde goes over its xt row, which the map has consumed.
+template <int L, typename T>
+__global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4))) fwd_finish_kernel(BatchParams P) {
+  constexpr int nw = wig_total(L);
+  constexpr int nc = n_comp(L);
+  __shared__ float sD[nw];
+  __shared__ float sa[kMaxHeadsB];
+  __shared__ float sp[kMaxHeadsB];
+  const int lane = threadIdx.x;
+  const int C = P.C, H = P.H, d = C / H, F = P.n_focus, cf = C / F;
+  const EdgeBufs& B = P.b;
+  for (int e = blockIdx.x; e < P.nb; e += gridDim.x) {
+    for (int q = lane; q < nw; q += kLane) sD[q] = B.D[(int64_t)e * nw + q];
+    for (int h = lane; h < H; h += kLane) sa[h] = B.a[(int64_t)e * H + h];
+    const float* yte = B.yt + (int64_t)e * nc * C;
+    if (F > 1) {
+      for (int f = lane; f < F; f += kLane) sp[f] = 0.0f;
+      __syncthreads();
+      // ytilde[(0,0), c] is column c of the m = 0 block
+      for (int c = lane; c < C; c += kLane) atomicAdd(&sp[c / cf], load_as_float((const T*)P.w_focus, c) * yte[c]);
+      __syncthreads();
+      if (lane == 0) {
+        float mx = -INFINITY;
+        for (int f = 0; f < F; ++f) mx = fmaxf(mx, sp[f]);
+        float sum = 0.0f;
+        for (int f = 0; f < F; ++f) {
+          sp[f] = expf(sp[f] - mx);
+          sum += sp[f];
+        }
+        const float inv = 1.0f / sum;
+        for (int f = 0; f < F; ++f) sp[f] *= inv;
+      }
+    }
+    __syncthreads();
+    float* out = B.xt + (int64_t)e * nc * C;
+#pragma unroll 1
+    for (int c = lane; c < C; c += kLane) {
+      const float w = sa[c / d] * (F > 1 ? sp[c / cf] : 1.0f);
+      fwd_degree<L, 0>(sD, yte, out, C, c, P.m_max, w);
+    }
+    __syncthreads();
+  }
+}
+
+// y[t] += the messages of target t's edges in this batch, in edge order
+// (targets split between batches get one partial sum per batch).
+__global__ void __launch_bounds__(256) fwd_reduce_kernel(BatchParams P, int ncc) {
+  const int t0 = P.b.tgt[0], t1 = P.b.tgt[P.nb - 1];
+  for (int t = t0 + blockIdx.x; t <= t1; t += gridDim.x) {
+    const int64_t lo = max((int64_t)P.row_ptr[t], P.e0) - P.e0;
+    const int64_t hi = min((int64_t)P.row_ptr[t + 1], P.e0 + P.nb) - P.e0;
+    if (lo >= hi) continue;
+    float* yt = P.y + (int64_t)t * ncc;
+    for (int q = threadIdx.x; q < ncc; q += blockDim.x) {
+      float acc = 0.0f;
+      for (int64_t e = lo; e < hi; ++e) acc += P.b.xt[e * ncc + q];
+      yt[q] += acc;
+    }
   }
 }
 
@@ -732,25 +870,42 @@ so2_status gemm(const float* A, int64_t lda, const float* B, int64_t ldb, float*
 
 // ---------------------------------------------------------------- weights
 
-// B_m in fp32 from w_so2: W0 for m = 0, [[W1, -W2], [W2, W1]] for m >= 1.
+// B_m in fp32 from w_so2: W0 for m = 0, [[W1, -W2], [W2, W1]] for m >= 1,
+// for the blocks m <= m_max.  With F focus streams, w_so2 is F stacks of
+// C' = C / F channels (each W0 and (W1_m, W2_m) for m = 1..m_max) and B_m is
+// block diagonal over the streams: entry (out, in) of a block is 0 unless
+// both channels belong to the same stream.
 template <typename T>
-__global__ void __launch_bounds__(256) bmat_build_kernel(const T* __restrict__ w, float* __restrict__ bm, int L, int C) {
+__global__ void __launch_bounds__(256) bmat_build_kernel(const T* __restrict__ w, float* __restrict__ bm, int L, int C,
+                                                         int m_max, int F) {
   const int m = blockIdx.y;
   const int wd = blk_width(L, C, m);
   const int64_t n = (int64_t)wd * wd;
+  const int cf = C / F;
+  const int64_t stack = so2_w1_offset(L, cf, m_max + 1);  // entries of one stream's stack
   float* out = bm + bmat_off(L, C, m);
   for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < n; q += (int64_t)gridDim.x * blockDim.x) {
     const int o = (int)(q / wd), in = (int)(q % wd);
-    float v;
+    float v = 0.0f;
     if (m == 0) {
-      v = load_as_float(w, q);
+      // (l, c) rows and columns
+      const int lo = o / C, co = o % C, li = in / C, ci = in % C;
+      if (co / cf == ci / cf) {
+        const int64_t k0 = (int64_t)(L + 1) * cf;
+        v = load_as_float(w + (co / cf) * stack, ((int64_t)lo * cf + co % cf) * k0 + (int64_t)li * cf + ci % cf);
+      }
     } else {
+      // (sign, l - m, c) rows and columns
       const int km = wd / 2;
       const int so = o / km, si = in / km, ro = o % km, ri = in % km;
-      const T* w1 = w + so2_w1_offset(L, C, m);
-      const T* w2 = w1 + (int64_t)km * km;
-      const int64_t r = (int64_t)ro * km + ri;
-      v = so == si ? load_as_float(w1, r) : (so == 0 ? -load_as_float(w2, r) : load_as_float(w2, r));
+      const int co = ro % C, ci = ri % C;
+      if (co / cf == ci / cf) {
+        const int64_t kmf = (int64_t)(L + 1 - m) * cf;
+        const T* w1 = w + (co / cf) * stack + so2_w1_offset(L, cf, m);
+        const T* w2 = w1 + kmf * kmf;
+        const int64_t r = ((int64_t)(ro / C) * cf + co % cf) * kmf + (int64_t)(ri / C) * cf + ci % cf;
+        v = so == si ? load_as_float(w1, r) : (so == 0 ? -load_as_float(w2, r) : load_as_float(w2, r));
+      }
     }
     out[q] = v;
   }
@@ -911,21 +1066,22 @@ struct BwdScratch {
 };
 
 template <int L, typename T>
-so2_status launch_edges(int which, const BwdParams& P, hipStream_t stream) {
+so2_status launch_edges(int which, const BatchParams& P, hipStream_t stream) {
   const unsigned grid = (unsigned)std::min<int64_t>(P.nb, kGridCap);
   if (grid == 0) return SO2_OK;
   switch (which) {
     case 0: hipLaunchKernelGGL((bwd_prep_kernel<L, T>), dim3(grid), dim3(kLane), 0, stream, P); break;
     case 1: hipLaunchKernelGGL((bwd_sbar_kernel<L>), dim3(grid), dim3(kLane), 0, stream, P); break;
     case 2: hipLaunchKernelGGL((bwd_dyt_kernel<L>), dim3(grid), dim3(kLane), 0, stream, P); break;
-    default: hipLaunchKernelGGL((bwd_final_kernel<L, T>), dim3(grid), dim3(kLane), 0, stream, P); break;
+    case 3: hipLaunchKernelGGL((bwd_final_kernel<L, T>), dim3(grid), dim3(kLane), 0, stream, P); break;
+    default: hipLaunchKernelGGL((fwd_finish_kernel<L, T>), dim3(grid), dim3(kLane), 0, stream, P); break;
   }
   SO2_CHECK_LAUNCH();
   return SO2_OK;
 }
 
 template <typename T>
-so2_status edges_dispatch(int L, int which, const BwdParams& P, hipStream_t stream) {
+so2_status edges_dispatch(int L, int which, const BatchParams& P, hipStream_t stream) {
   switch (L) {
     case 0: return launch_edges<0, T>(which, P, stream);
     case 1: return launch_edges<1, T>(which, P, stream);
@@ -937,18 +1093,149 @@ so2_status edges_dispatch(int L, int which, const BwdParams& P, hipStream_t stre
   }
 }
 
-so2_status run_edges(int L, int dtype, int which, const BwdParams& P, hipStream_t stream) {
+so2_status run_edges(int L, int dtype, int which, const BatchParams& P, hipStream_t stream) {
   return dtype == SO2_BF16 ? edges_dispatch<uint16_t>(L, which, P, stream) : edges_dispatch<float>(L, which, P, stream);
 }
+
+so2_status run_stats(int dtype, const BatchParams& P, hipStream_t stream) {
+  const unsigned grid = (unsigned)std::min(P.n_targets, kGridCap);
+  if (grid == 0) return SO2_OK;
+  if (dtype == SO2_BF16) hipLaunchKernelGGL(batch_stats_kernel<uint16_t>, dim3(grid), dim3(kLane), 0, stream, P);
+  else hipLaunchKernelGGL(batch_stats_kernel<float>, dim3(grid), dim3(kLane), 0, stream, P);
+  SO2_CHECK_LAUNCH();
+  return SO2_OK;
+}
+
+// Edge range [row_ptr[0], row_ptr[n_targets]) read back to the host: the
+// batch plan needs it (one wait on the stream).
+so2_status edge_range(const int32_t* row_ptr, int n_targets, int64_t* first, int64_t* count, hipStream_t stream) {
+  int32_t ends[2] = {0, 0};
+  if (n_targets > 0) {
+    SO2_CHECK(hipMemcpyAsync(&ends[0], row_ptr, sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+    SO2_CHECK(hipMemcpyAsync(&ends[1], row_ptr + n_targets, sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+    SO2_CHECK(hipStreamSynchronize(stream));
+  }
+  *first = ends[0];
+  *count = (int64_t)ends[1] - ends[0];
+  return *count < 0 ? SO2_ERR_INVALID_ARGUMENT : SO2_OK;
+}
+
+// Offsets (bytes) of the forward's scratch arrays.
+struct FwdScratch {
+  size_t smax, sinv, bm, xt, yt, D, a, ab, tgt, total;
+  int64_t cap;
+  FwdScratch(int n_targets, int L, int C, int H, int m_max) {
+    cap = batch_edges(n_targets);
+    const size_t nc = (size_t)n_comp(L), nw = (size_t)wig_total(L);
+    const size_t nb = (size_t)bmat_off(L, C, m_max + 1);
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+      const size_t at = o;
+      o += al256(bytes);
+      return at;
+    };
+    smax = take(4 * (size_t)n_targets * H);
+    sinv = take(4 * (size_t)n_targets * H);
+    bm = take(4 * nb);
+    xt = take(4 * (size_t)cap * nc * C);
+    yt = take(4 * (size_t)cap * nc * C);
+    D = take(4 * (size_t)cap * nw);
+    a = take(4 * (size_t)cap * H);
+    ab = take(4 * (size_t)cap * H);
+    tgt = take(4 * (size_t)cap);
+    total = o;
+  }
+};
 
 }  // namespace
 
 bool bwd_supported(int L, int C, int H, int K) {
-  return L >= 0 && L <= kMaxL && C >= 1 && C <= 256 && H >= 1 && H <= kMaxBwdHeads && C % H == 0 && K >= 2;
+  return L >= 0 && L <= kMaxL && C >= 1 && C <= 256 && H >= 1 && H <= kMaxHeadsB && C % H == 0 && K >= 2;
 }
 
 size_t bwd_scratch_bytes(int n_atoms, int n_targets, int L, int C, int H, int K) {
   return BwdScratch(n_atoms, n_targets, L, C, H, K).total;
+}
+
+bool batch_fwd_supported(int L, int C, int H, int K, int m_max, int n_focus) {
+  return bwd_supported(L, C, H, K) && m_max >= 0 && m_max <= L && n_focus >= 1 && n_focus <= kMaxHeadsB &&
+         C % n_focus == 0;
+}
+
+size_t batch_fwd_scratch_bytes(int n_targets, int L, int C, int H, int m_max) {
+  return FwdScratch(n_targets, L, C, H, m_max).total;
+}
+
+so2_status launch_attention_batch_fwd(const AttnArgs& a, hipStream_t stream) {
+  const int L = a.L, C = a.C, nc = n_comp(L), mm = a.m_max;
+  const FwdScratch S(a.n_targets, L, C, a.H, mm);
+  char* ws = (char*)a.scratch;
+  so2_status st;
+  if ((st = fill_zero(a.y, (int64_t)a.n_targets * nc * C, stream)) != SO2_OK) return st;
+  int64_t e_first = 0, n_edges = 0;
+  if ((st = edge_range(a.row_ptr, a.n_targets, &e_first, &n_edges, stream)) != SO2_OK) return st;
+  if (n_edges == 0) return SO2_OK;
+
+  float* bm = (float*)(ws + S.bm);
+  if (a.dtype == SO2_BF16)
+    hipLaunchKernelGGL(bmat_build_kernel<uint16_t>, dim3(1024, mm + 1), dim3(256), 0, stream,
+                       (const uint16_t*)a.w_so2, bm, L, C, mm, a.n_focus);
+  else
+    hipLaunchKernelGGL(bmat_build_kernel<float>, dim3(1024, mm + 1), dim3(256), 0, stream, (const float*)a.w_so2, bm,
+                       L, C, mm, a.n_focus);
+  SO2_CHECK_LAUNCH();
+
+  BatchParams P{};
+  P.pos = a.pos;
+  P.y = a.y;
+  P.w_logit = a.w_logit;
+  P.w_focus = a.w_focus;
+  P.m_max = mm;
+  P.n_focus = a.n_focus;
+  P.row_ptr = a.row_ptr;
+  P.col = a.col;
+  P.x = a.x;
+  P.w_rad = a.w_rad;
+  P.q = a.q;
+  P.k = a.k;
+  P.smax = (float*)(ws + S.smax);
+  P.sinv = (float*)(ws + S.sinv);
+  P.b.xt = (float*)(ws + S.xt);
+  P.b.yt = (float*)(ws + S.yt);
+  P.b.D = (float*)(ws + S.D);
+  P.b.a = (float*)(ws + S.a);
+  P.b.ab = (float*)(ws + S.ab);
+  P.b.tgt = (int32_t*)(ws + S.tgt);
+  P.n_targets = a.n_targets;
+  P.C = C;
+  P.H = a.H;
+  P.K = a.K;
+  P.p = a.p;
+  P.cutoff = a.cutoff;
+  P.flags = a.flags;
+  P.periodic = a.periodic;
+  for (int d = 0; d < 3; ++d) P.box[d] = a.box[d];
+  if ((st = run_stats(a.dtype, P, stream)) != SO2_OK) return st;
+
+  const int64_t cap = S.cap;
+  const int64_t ld = (int64_t)nc * C;
+  for (int64_t b = 0; b * cap < n_edges; ++b) {
+    P.e0 = e_first + b * cap;
+    P.nb = (int32_t)std::min<int64_t>(cap, n_edges - b * cap);
+    if ((st = run_edges(L, a.dtype, 0, P, stream)) != SO2_OK) return st;
+    for (int m = 0; m <= mm; ++m) {
+      const int wd = blk_width(L, C, m);
+      const int64_t xo = blk_off(L, C, m);
+      if ((st = gemm<false, true>(P.b.xt + xo, ld, bm + bmat_off(L, C, m), wd, P.b.yt + xo, ld, P.nb, wd, wd, false,
+                                  stream)) != SO2_OK)
+        return st;
+    }
+    if ((st = run_edges(L, a.dtype, 4, P, stream)) != SO2_OK) return st;
+    const unsigned rgrid = (unsigned)std::min<int64_t>(P.nb, kGridCap);
+    hipLaunchKernelGGL(fwd_reduce_kernel, dim3(rgrid), dim3(256), 0, stream, P, (int)ld);
+    SO2_CHECK_LAUNCH();
+  }
+  return SO2_OK;
 }
 
 so2_status launch_attention_bwd(const AttnArgs& a, const float* dy, float* dx, float* dpos, float* dw_q, float* dw_k,
@@ -977,15 +1264,8 @@ so2_status launch_attention_bwd(const AttnArgs& a, const float* dy, float* dx, f
   if ((st = fill_zero(dw_rad, (int64_t)a.K * C, stream)) != SO2_OK) return st;
   if (dw_so2 && (st = fill_zero(db, bmat_off(L, C, L + 1), stream)) != SO2_OK) return st;
 
-  // edge range of the targets' rows: the batch plan needs it on the host
-  int32_t ends[2] = {0, 0};
-  if (a.n_targets > 0) {
-    SO2_CHECK(hipMemcpyAsync(&ends[0], a.row_ptr, sizeof(int32_t), hipMemcpyDeviceToHost, stream));
-    SO2_CHECK(hipMemcpyAsync(&ends[1], a.row_ptr + a.n_targets, sizeof(int32_t), hipMemcpyDeviceToHost, stream));
-    SO2_CHECK(hipStreamSynchronize(stream));
-  }
-  const int64_t e_first = ends[0], n_edges = (int64_t)ends[1] - ends[0];
-  if (n_edges < 0) return SO2_ERR_INVALID_ARGUMENT;
+  int64_t e_first = 0, n_edges = 0;
+  if ((st = edge_range(a.row_ptr, a.n_targets, &e_first, &n_edges, stream)) != SO2_OK) return st;
 
   if (n_edges > 0) {
     hipLaunchKernelGGL(generators_kernel, dim3(1), dim3(192), 0, stream, gen, L);
@@ -993,18 +1273,20 @@ so2_status launch_attention_bwd(const AttnArgs& a, const float* dy, float* dx, f
     const unsigned nbw = 1024;
     if (a.dtype == SO2_BF16)
       hipLaunchKernelGGL(bmat_build_kernel<uint16_t>, dim3(nbw, L + 1), dim3(256), 0, stream,
-                         (const uint16_t*)a.w_so2, bm, L, C);
+                         (const uint16_t*)a.w_so2, bm, L, C, L, 1);
     else
       hipLaunchKernelGGL(bmat_build_kernel<float>, dim3(nbw, L + 1), dim3(256), 0, stream, (const float*)a.w_so2,
-                         bm, L, C);
+                         bm, L, C, L, 1);
     SO2_CHECK_LAUNCH();
 
-    BwdParams P{};
+    BatchParams P{};
     P.pos = a.pos;
     P.row_ptr = a.row_ptr;
     P.col = a.col;
     P.x = a.x;
     P.w_rad = a.w_rad;
+    P.m_max = L;
+    P.n_focus = 1;
     P.dy = dy;
     P.q = a.q;
     P.k = a.k;
@@ -1037,9 +1319,7 @@ so2_status launch_attention_bwd(const AttnArgs& a, const float* dy, float* dx, f
     P.periodic = a.periodic;
     for (int d = 0; d < 3; ++d) P.box[d] = a.box[d];
 
-    const unsigned sgrid = (unsigned)std::min(a.n_targets, kGridCap);
-    hipLaunchKernelGGL(bwd_stats_kernel, dim3(sgrid), dim3(kLane), 0, stream, P);
-    SO2_CHECK_LAUNCH();
+    if ((st = run_stats(a.dtype, P, stream)) != SO2_OK) return st;
 
     const int64_t cap = S.cap;
     const int64_t nbat = (n_edges + cap - 1) / cap;

@@ -54,6 +54,15 @@ struct AttnArgs {
   const void* w_focus;  // [C] when n_focus > 1
 };
 
+// The base forward with a kernel that never waits on the stream (abi.hip):
+// the MFMA kernel or the fp32 VALU kernel, for the no-allocation entry
+// point, whose callers may be under stream capture.
+size_t attention_nowait_workspace_bytes(const so2_attn_desc* desc);
+so2_status attention_fwd_nowait(const so2_attn_desc* desc, const float* pos, const float* box_host,
+                                const int32_t* row_ptr, const int32_t* col, const void* x, const void* w_q,
+                                const void* w_k, const void* w_rad, const void* w_so2, float* y, void* workspace,
+                                size_t workspace_bytes, so2_stream_t stream);
+
 // q/k projection of the l = 0 slice (attention_prep.hip).
 so2_status launch_qk_proj(const AttnArgs& a, hipStream_t stream);
 
@@ -75,14 +84,21 @@ size_t mfma_scratch_bytes(int n_atoms, int n_targets, int L, int H, int K);
 so2_status launch_attention_mfma_prep(const AttnArgs& a, hipStream_t stream);
 so2_status launch_attention_mfma(const AttnArgs& a, hipStream_t stream);
 
-// Backward (attention_bwd.hip), fp32 arithmetic: any L <= 6, C <= 256,
-// H <= 64.  Workspace beyond q, k: dq, dk, the softmax statistics and head
+// Backward (attention_batch.hip), fp32 arithmetic: any L <= 6, C <= 256,
+// H <= 256.  Workspace beyond q, k: dq, dk, the softmax statistics and head
 // sums per (target, head), the per-m maps in fp32 and their gradients, and
 // the per-edge tensors of one batch of edges (batch_edges(n_targets)).
 // dw_* may be null (not computed).  Reads the targets' edge range back to
 // the host once (one stream synchronisation) to plan the batches.
 bool bwd_supported(int L, int C, int H, int K);
 size_t bwd_scratch_bytes(int n_atoms, int n_targets, int L, int C, int H, int K);
+// fp32 forward on the same edge batches (attention_batch.hip): per-edge
+// rotation kernels, the per-m maps as fp32 GEMMs on the matrix cores, a
+// deterministic per-target sum; every variant (m_max, focus streams, logit
+// bias).  Reads the targets' edge range back once (one stream wait).
+bool batch_fwd_supported(int L, int C, int H, int K, int m_max, int n_focus);
+size_t batch_fwd_scratch_bytes(int n_targets, int L, int C, int H, int m_max);
+so2_status launch_attention_batch_fwd(const AttnArgs& a, hipStream_t stream);
 so2_status launch_attention_bwd(const AttnArgs& a, const float* dy, float* dx, float* dpos, float* dw_q, float* dw_k,
                                 float* dw_rad, float* dw_so2, hipStream_t stream);
 

@@ -46,15 +46,15 @@ extern "C" so2_status so2_attention_fwd_noalloc(const so2_attn_desc* desc, const
                                                 const int32_t* row_ptr, const int32_t* col, const void* x,
                                                 const void* w_q, const void* w_k, const void* w_rad,
                                                 const void* w_so2, float* y, so2_stream_t stream) {
-  const size_t need = so2_attention_workspace_bytes(desc);
+  const size_t need = attention_nowait_workspace_bytes(desc);
   if (need == 0) {
-    // invalid or unsupported: let the regular entry point name the error
-    return so2_attention_fwd(desc, pos, box_host, row_ptr, col, x, w_q, w_k, w_rad, w_so2, y, nullptr, 0, stream);
+    // invalid or unsupported: let the entry point name the error
+    return attention_fwd_nowait(desc, pos, box_host, row_ptr, col, x, w_q, w_k, w_rad, w_so2, y, nullptr, 0, stream);
   }
   if (need > (size_t)SO2_NOALLOC_SCRATCH_BYTES) return SO2_ERR_WORKSPACE;
   void* ws = nullptr;
   const so2_status st = scratch_address(&ws);
   if (st != SO2_OK) return st;
-  return so2_attention_fwd(desc, pos, box_host, row_ptr, col, x, w_q, w_k, w_rad, w_so2, y, ws,
-                           (size_t)SO2_NOALLOC_SCRATCH_BYTES, stream);
+  return attention_fwd_nowait(desc, pos, box_host, row_ptr, col, x, w_q, w_k, w_rad, w_so2, y, ws,
+                              (size_t)SO2_NOALLOC_SCRATCH_BYTES, stream);
 }

@@ -186,13 +186,13 @@ def test_mfma_shape_past_its_atom_limit_is_unsupported():
 
 
 def test_kernel_kind_selection():
-    assert sea.attention_kernel_kind(_desc()) == sea.KERNEL_VALU
+    assert sea.attention_kernel_kind(_desc()) == sea.KERNEL_BATCH
     assert sea.attention_kernel_kind(_desc(l_max=7)) == sea.KERNEL_NONE
     for L in range(1, 7):
         d = _desc(l_max=L, channels=128, heads=8, n_rbf=16, dtype=sea.SO2_BF16)
         assert sea.attention_kernel_kind(d) == sea.KERNEL_MFMA
-    assert sea.attention_kernel_kind(_desc(l_max=0, channels=128, heads=8, dtype=sea.SO2_BF16)) == sea.KERNEL_VALU
-    assert sea.attention_kernel_kind(_desc(l_max=6, channels=128, heads=8, dtype=sea.SO2_FP32)) == sea.KERNEL_VALU
+    assert sea.attention_kernel_kind(_desc(l_max=0, channels=128, heads=8, dtype=sea.SO2_BF16)) == sea.KERNEL_BATCH
+    assert sea.attention_kernel_kind(_desc(l_max=6, channels=128, heads=8, dtype=sea.SO2_FP32)) == sea.KERNEL_BATCH
 
 
 def test_norm_errors_before_launch():
@@ -321,6 +321,6 @@ def test_variant_counts_and_errors():
     assert lib.so2_attention_variant_kernel_kind(ctypes.byref(mf), ctypes.byref(sea.AttnVariant(-1, 1))) == \
         sea.KERNEL_MFMA
     assert lib.so2_attention_variant_kernel_kind(ctypes.byref(mf), ctypes.byref(sea.AttnVariant(2, 1))) == \
-        sea.KERNEL_VALU
+        sea.KERNEL_BATCH
     assert lib.so2_attention_variant_kernel_kind(ctypes.byref(mf), ctypes.byref(sea.AttnVariant(-1, 2))) == \
-        sea.KERNEL_VALU
+        sea.KERNEL_BATCH

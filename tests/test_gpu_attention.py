@@ -397,7 +397,7 @@ def test_neighbours_just_inside_the_cutoff(L, C, H, K, dtype):
         r = w.pos[col[rp[i] : rp[i + 1]]].astype(np.float64) - w.pos[i].astype(np.float64)
         s = np.sqrt((r * r).sum(1)) / w.cutoff
         assert np.all((s > 1 - 1.2e-3) & (s < 1.0)), (i, s)
-    assert _kind(w) == (sea.KERNEL_VALU if dtype == "fp32" else sea.KERNEL_MFMA)
+    assert _kind(w) == (sea.KERNEL_BATCH if dtype == "fp32" else sea.KERNEL_MFMA)
     y, y_ref = _run_pair(w)
     err = max_rel_error(y, y_ref)
     err_far = max_rel_error(y[far], y_ref[far])

@@ -2,12 +2,15 @@
 variants (m_max < L, radial logit bias, F focus streams with the
 cross-focus softmax), through the C ABI:
 
-* fp32 on the VALU kernel, every atom of the tiny workload, each variant
-  alone and all together, at 1e-4;
+* fp32 on the edge-batch path, every atom of the tiny workload, each
+  variant alone and all together, at 1e-4;
+* targets whose edges take two and three batches (64 edges per target, at
+  least 4096), with and without variants;
 * bf16 inputs: the logit bias on the MFMA kernel (a small-molecule batch
   at 2e-2, and seeded targets of the L = 6 water box); truncated orders and
-  focus streams at C = 128 on the VALU kernel (fp32 arithmetic, 1e-4);
-* the base variant through the variant call is bitwise the base call."""
+  focus streams at C = 128 on the edge-batch path (fp32 arithmetic, 1e-4);
+* the base variant through the variant call is bitwise the base call;
+  repeated calls on the edge-batch path are bitwise equal."""
 
 import numpy as np
 import pytest
@@ -34,7 +37,7 @@ def _weights(w, m_max, n_focus, logit, seed=0):
     return ws, wl, wf
 
 
-def _run(w, m_max=-1, n_focus=1, logit=False, targets=None):
+def _run(w, m_max=-1, n_focus=1, logit=False, targets=None, n_targets=None, out=None):
     import torch
 
     import so_equivariant_graph_amd as sea
@@ -49,10 +52,13 @@ def _run(w, m_max=-1, n_focus=1, logit=False, targets=None):
     y = sea.so2_attention_fwd_variant(
         d["pos"], rp_d, col_d, d["x"], d["w_q"], d["w_k"], d["w_rad"], d["w_so2"], l_max=w.l_max, heads=w.heads,
         cutoff=w.cutoff, envelope_p=w.envelope_p, box=w.box, m_max=m_max, n_focus=n_focus, w_logit=t(wl),
-        w_focus=t(wf),
+        w_focus=t(wf), n_targets=n_targets,
     )
     torch.cuda.synchronize()
-    tg = np.arange(w.n_atoms) if targets is None else np.asarray(targets)
+    if out is not None:
+        out.append(y.clone())
+    nt = w.n_atoms if n_targets is None else n_targets
+    tg = np.arange(nt) if targets is None else np.asarray(targets)
     y_ref = so2_attention_ref(w.pos, rp, col, w.x, w.w_q, w.w_k, w.w_rad, ws, l_max=w.l_max, heads=w.heads,
                               cutoff=w.cutoff, envelope_p=w.envelope_p, box=w.box, targets=tg,
                               m_max=None if m_max < 0 else m_max, w_logit=wl, n_focus=n_focus, w_focus=wf)
@@ -95,11 +101,11 @@ def test_bf16_logit_bias_l6_water_sampled():
 
 
 @pytest.mark.parametrize("m_max,n_focus", [(2, 1), (-1, 4), (3, 2)])
-def test_bf16_c128_variants_on_the_valu_kernel(m_max, n_focus):
+def test_bf16_c128_variants_on_the_batch_path(m_max, n_focus):
     import so_equivariant_graph_amd as sea
 
     w = make_workload("small_molecules", geometry=dict(n_molecules=2))
-    assert _kind(w, m_max, n_focus) == sea.KERNEL_VALU
+    assert _kind(w, m_max, n_focus) == sea.KERNEL_BATCH
     assert _run(w, m_max, n_focus, logit=True) <= 1e-4
 
 
@@ -118,3 +124,23 @@ def test_base_variant_is_the_base_call():
                                       m_max=w.l_max, **kw)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("cutoff,batches,m_max,n_focus,logit", [(6.0, 2, -1, 1, False), (7.5, 3, 1, 2, True)])
+def test_fp32_edge_batches(cutoff, batches, m_max, n_focus, logit):
+    w = make_workload("water_l6", l_max=2, channels=16, heads=2, n_rbf=8, dtype="fp32", cutoff=cutoff)
+    nt = 64  # batch capacity max(4096, 64 nt) = 4096 edges
+    rp, _ = neighbors_bruteforce(w.pos, w.cutoff, w.box, w.mol_id)
+    n_edges = int(rp[nt] - rp[0])
+    assert (batches - 1) * 4096 < n_edges <= batches * 4096, n_edges
+    assert _run(w, m_max, n_focus, logit, n_targets=nt) <= TOL["fp32"]
+
+
+def test_batch_path_repeats_bitwise():
+    import torch
+
+    w = make_workload("tiny_fp32")
+    outs = []
+    _run(w, 1, 2, True, out=outs)
+    _run(w, 1, 2, True, out=outs)
+    assert torch.equal(outs[0], outs[1])
