@@ -477,6 +477,89 @@ def backward_bench(steps, warmup, n_molecules):
     }), flush=True)
 
 
+def variant_flops(L, C, m_max, n_focus):
+    """Algorithmic flops per edge of a variant's per-m maps: F streams of C/F
+    channels, orders up to m_max, 4 real products per m >= 1."""
+    cf = C // n_focus
+    return n_focus * 2 * cf * cf * ((L + 1) ** 2 + 4 * sum((L + 1 - m) ** 2 for m in range(1, m_max + 1)))
+
+
+def variant_bench(steps, warmup, spec, workload):
+    """so2_attention_fwd_variant on a workload with the radial logit bias and
+    the orders and focus streams of spec ("M_MAX:N_FOCUS", M_MAX -1 = every
+    order), seeded weights of the variant's shapes in the workload's dtype:
+    messages/s of the whole call (torch events around each call), against
+    the peak of the path it runs on (the fp32 matrix peak for the edge-batch
+    path, whose per-m maps are fp32 GEMMs; the bf16 peak for the MFMA
+    kernel), with the variant's algorithmic flops (variant_flops)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import so_equivariant_graph_amd as sea
+    from synth import make_workload, to_bf16_exact
+
+    m_max, n_focus = (int(v) for v in spec.split(":"))
+    w = make_workload(workload)
+    L, C, H, K = w.l_max, w.channels, w.heads, w.n_rbf
+    mm = L if m_max < 0 else m_max
+    rng = np.random.default_rng(11)
+    cf = C // n_focus
+    ws = (rng.standard_normal(sea.load_library().so2_weight_count_variant(L, C, m_max, n_focus)) /
+          np.sqrt(cf * (L + 1))).astype(np.float32)
+    wl = (rng.standard_normal((K, H)) * 0.5).astype(np.float32)
+    wf = (rng.standard_normal(C) / np.sqrt(cf)).astype(np.float32)
+    if w.dtype == "bf16":
+        ws, wl, wf = to_bf16_exact(ws), to_bf16_exact(wl), to_bf16_exact(wf)
+    dev = torch.device("cuda:0")
+    dt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    t = lambda a, d=dt: torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=d)
+    pos = t(w.pos, torch.float32)
+    x, w_q, w_k, w_rad = (t(a) for a in (w.x, w.w_q, w.w_k, w.w_rad))
+    w_so2, w_logit, w_focus = t(ws), t(wl), t(wf) if n_focus > 1 else None
+    mol = None if w.mol_id is None else torch.from_numpy(w.mol_id.astype(np.int32)).to(dev)
+    row_ptr, col = sea.build_neighbors(pos, w.cutoff, box=w.box, mol_id=mol)
+    E = int(col.numel())
+    desc = sea.make_desc(n_atoms=w.n_atoms, n_targets=w.n_atoms, l_max=L, channels=C, heads=H, n_rbf=K,
+                         envelope_p=w.envelope_p, cutoff=w.cutoff, flags=0,
+                         dtype=sea.SO2_BF16 if w.dtype == "bf16" else sea.SO2_FP32)
+    var = sea.AttnVariant(m_max, n_focus)
+    lib = sea.load_library()
+    kind = int(lib.so2_attention_variant_kernel_kind(ctypes.byref(desc), ctypes.byref(var)))
+    ws_t = torch.empty(lib.so2_attention_variant_workspace_bytes(ctypes.byref(desc), ctypes.byref(var)),
+                       dtype=torch.uint8, device=dev)
+    y = torch.empty((w.n_atoms, (L + 1) ** 2, C), dtype=torch.float32, device=dev)
+    kw = dict(l_max=L, heads=H, cutoff=w.cutoff, envelope_p=w.envelope_p, box=w.box, m_max=m_max, n_focus=n_focus,
+              w_logit=w_logit, w_focus=w_focus, out=y, workspace=ws_t)
+    for _ in range(warmup):
+        sea.so2_attention_fwd_variant(pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, **kw)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        sea.so2_attention_fwd_variant(pos, row_ptr, col, x, w_q, w_k, w_rad, w_so2, **kw)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    mean = sum(ms) / len(ms)
+    F = variant_flops(L, C, mm, n_focus)
+    peak = PEAK_BF16_TFLOPS if kind == 2 else PEAK_FP32_MFMA_TFLOPS
+    achieved = E * F / (mean * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "neighbor-pair messages/sec, so2_attention_fwd_variant (logit bias, m_max, focus streams)",
+        "value": E / (mean * 1e-3), "unit": "messages/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": mean, "higher_is_better": True,
+        "dtype": ("bf16" if kind == 2 else f"{w.dtype} inputs, fp32 arithmetic"), "data": "synthetic",
+        "config": {"workload": workload, "n_atoms": w.n_atoms, "n_edges": E, "l_max": L, "channels": C, "heads": H,
+                   "m_max": mm, "n_focus": n_focus, "logit_bias": True},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None},
+        "detail": {"kernel_kind": kind, "flop_per_edge": F, "ms_min": ms[0], "ms_median": ms[len(ms) // 2],
+                   "outputs_finite": bool(torch.isfinite(y).all().item())},
+    }), flush=True)
+
+
 SWEEP_ATOMS = (12_500, 25_000, 50_000, 100_000, 200_000)
 
 
@@ -535,6 +618,8 @@ def main():
                     help="only time the merged RMS layer norm on the 100k-atom water box's features")
     ap.add_argument("--backward", type=int, metavar="N_MOLECULES", default=0,
                     help="only time so2_attention_bwd on a batch of N small molecules")
+    ap.add_argument("--variant", metavar="M_MAX:N_FOCUS", default=None,
+                    help="only time so2_attention_fwd_variant (with the radial logit bias) on --workload")
     ap.add_argument("--memory-sweep", action="store_true",
                     help="only run the water box at 12.5k-200k atoms: peak device bytes against N")
     args = ap.parse_args()
@@ -553,6 +638,9 @@ def main():
         return
     if args.backward:
         backward_bench(args.steps, args.warmup, args.backward)
+        return
+    if args.variant:
+        variant_bench(args.steps, args.warmup, args.variant, args.workload)
         return
     if args.norm:
         norm_bench(args.steps, args.warmup)
@@ -574,6 +662,8 @@ def main():
     kern = sorted(g["kern_ms"])
     kern_mean = sum(kern) / len(kern)
     achieved = E * F / (kern_mean * 1e-3) / 1e12
+    # the MFMA kernel runs bf16 operands; the edge-batch path's per-m maps are fp32 GEMMs
+    peak = PEAK_BF16_TFLOPS if g["kind"] == 2 else PEAK_FP32_MFMA_TFLOPS
     traffic = measured_traffic(w.name) if g["kind"] == 2 else None
     line = {
         "metric": METRIC,
@@ -603,9 +693,9 @@ def main():
         "roofline": {
             "bound": "mfma",
             "achieved": achieved,
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS,
+            "frac": achieved / peak,
             "traffic": traffic,
         },
         "cpu_baseline": cpu,
