@@ -83,7 +83,7 @@ AttnLayout attn_layout(const so2_attn_desc* d, Kind kind, const so2_attn_variant
   L.scratch = off;
   const int mm = v->m_max < 0 ? d->l_max : v->m_max;
   L.scratch_bytes = kind == kMfma    ? mfma_scratch_bytes(d->n_atoms, d->n_targets, d->l_max, d->heads, d->n_rbf)
-                    : kind == kBatch ? batch_fwd_scratch_bytes(d->n_targets, d->l_max, d->channels, d->heads, mm)
+                    : kind == kBatch ? batch_fwd_scratch_bytes(d->n_targets, d->l_max, d->channels, d->heads, mm, v->n_focus)
                                      : valu_scratch_bytes(d->l_max, d->channels);
   off += align256(L.scratch_bytes);
   L.total = off;

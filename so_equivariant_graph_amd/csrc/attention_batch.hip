@@ -79,10 +79,11 @@ __host__ __device__ inline int blk_off(int L, int C, int m) {
   for (int q = 0; q < m; ++q) off += blk_width(L, C, q);
   return off;
 }
-// Offset of B_m (blk_width^2 floats, row-major [out][in]) in the B array.
-__host__ __device__ inline int64_t bmat_off(int L, int C, int m) {
+// Offset of B_m in the B array: F stream matrices of (blk_width / F)^2
+// floats each, row-major [out][in] (F = 1: one matrix per block).
+__host__ __device__ inline int64_t bmat_off(int L, int C, int m, int F = 1) {
   int64_t off = 0;
-  for (int q = 0; q < m; ++q) off += (int64_t)blk_width(L, C, q) * blk_width(L, C, q);
+  for (int q = 0; q < m; ++q) off += (int64_t)(blk_width(L, C, q) / F) * (blk_width(L, C, q) / F) * F;
   return off;
 }
 // Column of component (l, mm) (|mm| <= l) for channel 0: block |mm|, sign
@@ -754,7 +755,12 @@ struct GemmArgs {
   int64_t lda, ldb, ldc;
   int k_split;  // K range per blockIdx.z
   int atomic;
+  // column maps of A (AT = false) and C: index x is column (x / g) stride +
+  // x % g, groups of g contiguous columns stride apart (g = 0: column x)
+  int kg, kstride, ng, nstride;
 };
+
+__device__ inline int colmap(int x, int g, int stride) { return g ? (x / g) * stride + x % g : x; }
 
 constexpr int kGemmTile = 128;
 
@@ -794,7 +800,9 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int gm = m0 + am[r], gk = k0 + ak[r];
-      ra[r] = (gm < g.M && gk < ke) ? (AT ? g.A[(int64_t)gk * g.lda + gm] : g.A[(int64_t)gm * g.lda + gk]) : 0.0f;
+      ra[r] = (gm < g.M && gk < ke)
+                  ? (AT ? g.A[(int64_t)gk * g.lda + gm] : g.A[(int64_t)gm * g.lda + colmap(gk, g.kg, g.kstride)])
+                  : 0.0f;
       const int gn = n0 + bn[r], gk2 = k0 + bk[r];
       rb[r] = (gn < g.N && gk2 < ke) ? (BT ? g.B[(int64_t)gn * g.ldb + gk2] : g.B[(int64_t)gk2 * g.ldb + gn]) : 0.0f;
     }
@@ -839,7 +847,7 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
         const int row = m0 + wm + 16 * a + 4 * (lane >> 4) + r;
         const int colm = n0 + wn + 16 * b + (lane & 15);
         if (row < g.M && colm < g.N) {
-          float* p = g.Cm + (int64_t)row * g.ldc + colm;
+          float* p = g.Cm + (int64_t)row * g.ldc + colmap(colm, g.ng, g.nstride);
           if (g.atomic) atomicAdd(p, acc[a][b][r]);
           else *p = acc[a][b][r];
         }
@@ -848,9 +856,9 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
 
 template <bool AT, bool BT>
 so2_status gemm(const float* A, int64_t lda, const float* B, int64_t ldb, float* Cm, int64_t ldc, int M, int N, int K,
-                bool atomic, hipStream_t stream) {
+                bool atomic, hipStream_t stream, int kg = 0, int kstride = 0, int ng = 0, int nstride = 0) {
   if (M <= 0 || N <= 0 || K <= 0) return SO2_OK;
-  GemmArgs g{A, B, Cm, M, N, K, lda, ldb, ldc, K, atomic ? 1 : 0};
+  GemmArgs g{A, B, Cm, M, N, K, lda, ldb, ldc, K, atomic ? 1 : 0, kg, kstride, ng, nstride};
   unsigned splits = 1;
   if (atomic) {
     // K ranges of at least 512 so that the tile grid covers the device
@@ -872,40 +880,36 @@ so2_status gemm(const float* A, int64_t lda, const float* B, int64_t ldb, float*
 
 // B_m in fp32 from w_so2: W0 for m = 0, [[W1, -W2], [W2, W1]] for m >= 1,
 // for the blocks m <= m_max.  With F focus streams, w_so2 is F stacks of
-// C' = C / F channels (each W0 and (W1_m, W2_m) for m = 1..m_max) and B_m is
-// block diagonal over the streams: entry (out, in) of a block is 0 unless
-// both channels belong to the same stream.
+// C' = C / F channels (each W0 and (W1_m, W2_m) for m = 1..m_max), and B_m
+// is stored as F dense stream matrices: stream f's rows and columns are the
+// block's (group, c') with c' < C', a group being one (sign, l) of the block
+// (l for m = 0), i.e. the block's columns group * C + f C' + c'.
 template <typename T>
 __global__ void __launch_bounds__(256) bmat_build_kernel(const T* __restrict__ w, float* __restrict__ bm, int L, int C,
                                                          int m_max, int F) {
   const int m = blockIdx.y;
-  const int wd = blk_width(L, C, m);
-  const int64_t n = (int64_t)wd * wd;
+  const int wd = blk_width(L, C, m) / F;  // one stream matrix is wd x wd
+  const int64_t per = (int64_t)wd * wd;
+  const int64_t n = per * F;
   const int cf = C / F;
   const int64_t stack = so2_w1_offset(L, cf, m_max + 1);  // entries of one stream's stack
-  float* out = bm + bmat_off(L, C, m);
+  float* out = bm + bmat_off(L, C, m, F);
   for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < n; q += (int64_t)gridDim.x * blockDim.x) {
-    const int o = (int)(q / wd), in = (int)(q % wd);
-    float v = 0.0f;
+    const int f = (int)(q / per);
+    const int o = (int)((q % per) / wd), in = (int)(q % wd);
+    const int go = o / cf, co = o % cf, gi = in / cf, ci = in % cf;
+    float v;
     if (m == 0) {
-      // (l, c) rows and columns
-      const int lo = o / C, co = o % C, li = in / C, ci = in % C;
-      if (co / cf == ci / cf) {
-        const int64_t k0 = (int64_t)(L + 1) * cf;
-        v = load_as_float(w + (co / cf) * stack, ((int64_t)lo * cf + co % cf) * k0 + (int64_t)li * cf + ci % cf);
-      }
+      const int64_t k0 = (int64_t)(L + 1) * cf;
+      v = load_as_float(w + f * stack, ((int64_t)go * cf + co) * k0 + (int64_t)gi * cf + ci);
     } else {
-      // (sign, l - m, c) rows and columns
-      const int km = wd / 2;
-      const int so = o / km, si = in / km, ro = o % km, ri = in % km;
-      const int co = ro % C, ci = ri % C;
-      if (co / cf == ci / cf) {
-        const int64_t kmf = (int64_t)(L + 1 - m) * cf;
-        const T* w1 = w + (co / cf) * stack + so2_w1_offset(L, cf, m);
-        const T* w2 = w1 + kmf * kmf;
-        const int64_t r = ((int64_t)(ro / C) * cf + co % cf) * kmf + (int64_t)(ri / C) * cf + ci % cf;
-        v = so == si ? load_as_float(w1, r) : (so == 0 ? -load_as_float(w2, r) : load_as_float(w2, r));
-      }
+      const int kg = L + 1 - m;  // groups per sign
+      const int so = go / kg, si = gi / kg;
+      const int64_t kmf = (int64_t)kg * cf;
+      const T* w1 = w + f * stack + so2_w1_offset(L, cf, m);
+      const T* w2 = w1 + kmf * kmf;
+      const int64_t r = ((int64_t)(go % kg) * cf + co) * kmf + (int64_t)(gi % kg) * cf + ci;
+      v = so == si ? load_as_float(w1, r) : (so == 0 ? -load_as_float(w2, r) : load_as_float(w2, r));
     }
     out[q] = v;
   }
@@ -1124,10 +1128,10 @@ so2_status edge_range(const int32_t* row_ptr, int n_targets, int64_t* first, int
 struct FwdScratch {
   size_t smax, sinv, bm, xt, yt, D, a, ab, tgt, total;
   int64_t cap;
-  FwdScratch(int n_targets, int L, int C, int H, int m_max) {
+  FwdScratch(int n_targets, int L, int C, int H, int m_max, int F) {
     cap = batch_edges(n_targets);
     const size_t nc = (size_t)n_comp(L), nw = (size_t)wig_total(L);
-    const size_t nb = (size_t)bmat_off(L, C, m_max + 1);
+    const size_t nb = (size_t)bmat_off(L, C, m_max + 1, F);
     size_t o = 0;
     auto take = [&](size_t bytes) {
       const size_t at = o;
@@ -1162,13 +1166,13 @@ bool batch_fwd_supported(int L, int C, int H, int K, int m_max, int n_focus) {
          C % n_focus == 0;
 }
 
-size_t batch_fwd_scratch_bytes(int n_targets, int L, int C, int H, int m_max) {
-  return FwdScratch(n_targets, L, C, H, m_max).total;
+size_t batch_fwd_scratch_bytes(int n_targets, int L, int C, int H, int m_max, int n_focus) {
+  return FwdScratch(n_targets, L, C, H, m_max, n_focus).total;
 }
 
 so2_status launch_attention_batch_fwd(const AttnArgs& a, hipStream_t stream) {
   const int L = a.L, C = a.C, nc = n_comp(L), mm = a.m_max;
-  const FwdScratch S(a.n_targets, L, C, a.H, mm);
+  const FwdScratch S(a.n_targets, L, C, a.H, mm, a.n_focus);
   char* ws = (char*)a.scratch;
   so2_status st;
   if ((st = fill_zero(a.y, (int64_t)a.n_targets * nc * C, stream)) != SO2_OK) return st;
@@ -1223,12 +1227,19 @@ so2_status launch_attention_batch_fwd(const AttnArgs& a, hipStream_t stream) {
     P.e0 = e_first + b * cap;
     P.nb = (int32_t)std::min<int64_t>(cap, n_edges - b * cap);
     if ((st = run_edges(L, a.dtype, 0, P, stream)) != SO2_OK) return st;
+    // per stream f: Y_m[:, f cols] = X_m[:, f cols] B_m,f^T, the stream's
+    // columns taken as groups of C' (one per (sign, l)) C apart
+    const int F = a.n_focus, cf = C / F;
     for (int m = 0; m <= mm; ++m) {
-      const int wd = blk_width(L, C, m);
+      const int wd = blk_width(L, C, m) / F;
       const int64_t xo = blk_off(L, C, m);
-      if ((st = gemm<false, true>(P.b.xt + xo, ld, bm + bmat_off(L, C, m), wd, P.b.yt + xo, ld, P.nb, wd, wd, false,
-                                  stream)) != SO2_OK)
-        return st;
+      for (int f = 0; f < F; ++f) {
+        const float* bf = bm + bmat_off(L, C, m, F) + (int64_t)f * wd * wd;
+        st = F == 1 ? gemm<false, true>(P.b.xt + xo, ld, bf, wd, P.b.yt + xo, ld, P.nb, wd, wd, false, stream)
+                    : gemm<false, true>(P.b.xt + xo + f * cf, ld, bf, wd, P.b.yt + xo + f * cf, ld, P.nb, wd, wd, false,
+                                        stream, cf, C, cf, C);
+        if (st != SO2_OK) return st;
+      }
     }
     if ((st = run_edges(L, a.dtype, 4, P, stream)) != SO2_OK) return st;
     const unsigned rgrid = (unsigned)std::min<int64_t>(P.nb, kGridCap);

@@ -97,7 +97,7 @@ size_t bwd_scratch_bytes(int n_atoms, int n_targets, int L, int C, int H, int K)
 // deterministic per-target sum; every variant (m_max, focus streams, logit
 // bias).  Reads the targets' edge range back once (one stream wait).
 bool batch_fwd_supported(int L, int C, int H, int K, int m_max, int n_focus);
-size_t batch_fwd_scratch_bytes(int n_targets, int L, int C, int H, int m_max);
+size_t batch_fwd_scratch_bytes(int n_targets, int L, int C, int H, int m_max, int n_focus);
 so2_status launch_attention_batch_fwd(const AttnArgs& a, hipStream_t stream);
 so2_status launch_attention_bwd(const AttnArgs& a, const float* dy, float* dx, float* dpos, float* dw_q, float* dw_k,
                                 float* dw_rad, float* dw_so2, hipStream_t stream);
