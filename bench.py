@@ -47,15 +47,16 @@ PEAK_HBM_GBS = 8000.0
 # for the kernel sources it was taken on: their digest is stored with it and a
 # mismatch reports null.
 MEASURED_TRAFFIC = {
-    # FETCH_SIZE 115157223 KiB x 2.00 (a 1 GiB copy reads as 524305 KiB), WRITE_SIZE
-    # 2609650 KiB x 1.00 (the copy writes read exactly 1048576 KiB); mean of 5 launches.
+    # FETCH_SIZE 114728585 KiB x 2.00 (a 1 GiB copy reads as 524305 KiB), WRITE_SIZE
+    # 2609649 KiB x 1.00 (the copy writes read exactly 1048576 KiB); mean of 5 launches.
     "water_100k": {
-        "sources_sha256": "a7cd3845743c5a9824f0569dc43fbccdf484cdb67be309da127486ba87624d18",
-        "fetch_bytes": 235834439553,
-        "write_bytes": 2672282035,
+        "sources_sha256": "7887744148cff85c5cc6dac7120b910111b649cf9b2334062c4f0523e0b26044",
+        "fetch_bytes": 234956636202,
+        "write_bytes": 2672280947,
     },
 }
-KERNEL_SOURCES = ("attention_mfma.hip", "wigner.h", "common.h", "launch.h")
+# the files that hold the fused kernel's device code
+KERNEL_SOURCES = ("attention_mfma.hip", "wigner.h", "common.h")
 
 
 def flops_per_edge(L, C):
@@ -281,9 +282,9 @@ NORM_TRAFFIC = {
     # box's features: FETCH_SIZE 312574 KiB x 2.00, WRITE_SIZE 625000 KiB x 1.00 (the same
     # copy calibration as the fused kernel's figure); mean of 4 launches.
     "water_100k": {
-        "sources_sha256": "84afa7d832182174e207bd85e5d226f8156f28722616c3d8f53e7018826b4a74",
-        "fetch_bytes": 640132977,
-        "write_bytes": 640000000,
+        "sources_sha256": "0bba6f27ba07289078f31ce07f3de142738b052cd1fe948e0466e06a7fac618b",
+        "fetch_bytes": 640131645,
+        "write_bytes": 640000032,
     },
 }
 NORM_SOURCES = ("norm.hip", "norm.h", "common.h")
