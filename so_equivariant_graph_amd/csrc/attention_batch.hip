@@ -720,6 +720,88 @@ __global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4)))
   }
 }
 
+// Degree l of one channel, accumulated: acc[(l, b)] += w (D^T ytilde)[b]
+// over the orders up to m_max.
+template <int L, int l>
+__device__ inline void fwd_degree_acc(const float* sD, const float* yte, float (&acc)[n_comp(L)], int C, int c,
+                                      int m_max, float w) {
+  if constexpr (l <= L) {
+    constexpr int n = 2 * l + 1;
+    keep_order();
+    float yv[n];
+#pragma unroll
+    for (int r = 0; r < n; ++r) yv[r] = (r - l <= m_max && l - r <= m_max) ? yte[comp_col(L, C, l, r - l) + c] : 0.0f;
+    const float* Dl = sD + wig_offset(l);
+#pragma unroll
+    for (int b = 0; b < n; ++b) {
+      float s = 0.0f;
+#pragma unroll
+      for (int r = 0; r < n; ++r) s += Dl[r * n + b] * yv[r];
+      acc[l * l + b] += w * s;
+    }
+    fwd_degree_acc<L, l + 1>(sD, yte, acc, C, c, m_max, w);
+  }
+}
+
+// Forward for C <= 128, one workgroup of 128 threads per target of the
+// batch, one channel per thread: the target's edges in order (cross-focus
+// softmax, rotation back, weights), the channel's sums kept in registers,
+// then y[t] += the sums once.  Replaces the finishing kernel's per-edge
+// messages and their per-target sum, so the messages never go through
+// memory.
+constexpr int kTargetThreads = 128;
+template <int L, typename T>
+__global__ void __launch_bounds__(kTargetThreads) fwd_target_kernel(BatchParams P) {
+  constexpr int nw = wig_total(L);
+  constexpr int nc = n_comp(L);
+  __shared__ float sD[nw];
+  __shared__ float sa[kMaxHeadsB];
+  __shared__ float sp[kMaxHeadsB];
+  const int tid = threadIdx.x;
+  const int C = P.C, H = P.H, d = C / H, F = P.n_focus, cf = C / F;
+  const EdgeBufs& B = P.b;
+  const int t0 = B.tgt[0], t1 = B.tgt[P.nb - 1];
+  const int c = tid;
+  for (int t = t0 + blockIdx.x; t <= t1; t += gridDim.x) {
+    const int64_t lo = max((int64_t)P.row_ptr[t], P.e0) - P.e0;
+    const int64_t hi = min((int64_t)P.row_ptr[t + 1], P.e0 + P.nb) - P.e0;
+    if (lo >= hi) continue;
+    float acc[nc];
+#pragma unroll
+    for (int q = 0; q < nc; ++q) acc[q] = 0.0f;
+    for (int64_t e = lo; e < hi; ++e) {
+      __syncthreads();  // the previous edge's LDS reads are done
+      for (int q = tid; q < nw; q += kTargetThreads) sD[q] = B.D[e * nw + q];
+      for (int h = tid; h < H; h += kTargetThreads) sa[h] = B.a[e * H + h];
+      const float* yte = B.yt + e * nc * C;
+      if (F > 1) {
+        for (int f = tid; f < F; f += kTargetThreads) sp[f] = 0.0f;
+        __syncthreads();
+        if (c < C) atomicAdd(&sp[c / cf], load_as_float((const T*)P.w_focus, c) * yte[c]);
+        __syncthreads();
+        if (tid == 0) {
+          float mx = -INFINITY;
+          for (int f = 0; f < F; ++f) mx = fmaxf(mx, sp[f]);
+          float sum = 0.0f;
+          for (int f = 0; f < F; ++f) {
+            sp[f] = expf(sp[f] - mx);
+            sum += sp[f];
+          }
+          const float inv = 1.0f / sum;
+          for (int f = 0; f < F; ++f) sp[f] *= inv;
+        }
+      }
+      __syncthreads();
+      if (c < C) fwd_degree_acc<L, 0>(sD, yte, acc, C, c, P.m_max, sa[c / d] * (F > 1 ? sp[c / cf] : 1.0f));
+    }
+    if (c < C) {
+      float* yt = P.y + (int64_t)t * nc * C + c;
+#pragma unroll
+      for (int q = 0; q < nc; ++q) yt[(int64_t)q * C] += acc[q];
+    }
+  }
+}
+
 // y[t] += the messages of target t's edges in this batch, in edge order
 // (targets split between batches get one partial sum per batch).
 __global__ void __launch_bounds__(256) fwd_reduce_kernel(BatchParams P, int ncc) {
@@ -1078,7 +1160,8 @@ so2_status launch_edges(int which, const BatchParams& P, hipStream_t stream) {
     case 1: hipLaunchKernelGGL((bwd_sbar_kernel<L>), dim3(grid), dim3(kLane), 0, stream, P); break;
     case 2: hipLaunchKernelGGL((bwd_dyt_kernel<L>), dim3(grid), dim3(kLane), 0, stream, P); break;
     case 3: hipLaunchKernelGGL((bwd_final_kernel<L, T>), dim3(grid), dim3(kLane), 0, stream, P); break;
-    default: hipLaunchKernelGGL((fwd_finish_kernel<L, T>), dim3(grid), dim3(kLane), 0, stream, P); break;
+    case 4: hipLaunchKernelGGL((fwd_finish_kernel<L, T>), dim3(grid), dim3(kLane), 0, stream, P); break;
+    default: hipLaunchKernelGGL((fwd_target_kernel<L, T>), dim3(grid), dim3(kTargetThreads), 0, stream, P); break;
   }
   SO2_CHECK_LAUNCH();
   return SO2_OK;
@@ -1241,10 +1324,15 @@ so2_status launch_attention_batch_fwd(const AttnArgs& a, hipStream_t stream) {
         if (st != SO2_OK) return st;
       }
     }
-    if ((st = run_edges(L, a.dtype, 4, P, stream)) != SO2_OK) return st;
-    const unsigned rgrid = (unsigned)std::min<int64_t>(P.nb, kGridCap);
-    hipLaunchKernelGGL(fwd_reduce_kernel, dim3(rgrid), dim3(256), 0, stream, P, (int)ld);
-    SO2_CHECK_LAUNCH();
+    if (C <= kTargetThreads) {
+      // one workgroup per target: the messages stay in registers
+      if ((st = run_edges(L, a.dtype, 5, P, stream)) != SO2_OK) return st;
+    } else {
+      if ((st = run_edges(L, a.dtype, 4, P, stream)) != SO2_OK) return st;
+      const unsigned rgrid = (unsigned)std::min<int64_t>(P.nb, kGridCap);
+      hipLaunchKernelGGL(fwd_reduce_kernel, dim3(rgrid), dim3(256), 0, stream, P, (int)ld);
+      SO2_CHECK_LAUNCH();
+    }
   }
   return SO2_OK;
 }
