@@ -825,7 +825,7 @@ __global__ void __launch_bounds__(256) fwd_reduce_kernel(BatchParams P, int ncc)
 //   A(m, k) = A[m lda + k]      (AT = false)  or A[k lda + m] (AT = true)
 //   B(k, n) = B[n ldb + k]      (BT = true)   or B[k ldb + n] (BT = false)
 // 128 x 128 tiles of C per workgroup (4 waves, 64 x 64 each: 16 MFMA tiles
-// of 16 x 16), K in steps of 16 staged through LDS; the next step's global
+// of 16 x 16), K in steps of kGemmK staged through LDS; the next step's global
 // loads go to registers while the current step's MFMAs run.  blockIdx.z
 // splits K into ranges of k_split.  Mode: store (C = AB, one workgroup per
 // tile) or atomic (C += AB, fp32 atomics, any number of K ranges).
@@ -845,10 +845,12 @@ struct GemmArgs {
 __device__ inline int colmap(int x, int g, int stride) { return g ? (x / g) * stride + x % g : x; }
 
 constexpr int kGemmTile = 128;
+constexpr int kGemmK = 16;  // K per LDS stage (32 was measured slower: more VGPRs, 36 KB of LDS)
 
-template <bool AT, bool BT>
+template <bool AT, bool BT, bool MAP>
 __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
-  constexpr int BM = kGemmTile, BN = kGemmTile, BK = 16;
+  constexpr int BM = kGemmTile, BN = kGemmTile, BK = kGemmK;
+  constexpr int R = BM * BK / 256;  // elements of each operand tile per thread
   constexpr int LDP = BM + 16;  // row pad: the 4 k-rows of one MFMA operand read hit distinct banks
   __shared__ float As[BK][LDP];
   __shared__ float Bs[BK][LDP];
@@ -859,31 +861,32 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
   const int ke = min(g.K, kb + g.k_split);
   // this thread's 8 elements of the A and B tiles: coalesced along the
   // contiguous dimension of each operand
-  int am[8], ak[8], bn[8], bk[8];
+  int am[R], ak[R], bn[R], bk[R];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
+  for (int r = 0; r < R; ++r) {
     if constexpr (AT) {
-      am[r] = t & 127;
-      ak[r] = (t >> 7) + 2 * r;
+      am[r] = t & (BM - 1);
+      ak[r] = t / BM + (256 / BM) * r;
     } else {
-      ak[r] = t & 15;
-      am[r] = (t >> 4) + 16 * r;
+      ak[r] = t & (BK - 1);
+      am[r] = t / BK + (256 / BK) * r;
     }
     if constexpr (BT) {
-      bk[r] = t & 15;
-      bn[r] = (t >> 4) + 16 * r;
+      bk[r] = t & (BK - 1);
+      bn[r] = t / BK + (256 / BK) * r;
     } else {
-      bn[r] = t & 127;
-      bk[r] = (t >> 7) + 2 * r;
+      bn[r] = t & (BN - 1);
+      bk[r] = t / BN + (256 / BN) * r;
     }
   }
-  float ra[8], rb[8];
+  float ra[R], rb[R];
   auto load = [&](int k0) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int r = 0; r < R; ++r) {
       const int gm = m0 + am[r], gk = k0 + ak[r];
       ra[r] = (gm < g.M && gk < ke)
-                  ? (AT ? g.A[(int64_t)gk * g.lda + gm] : g.A[(int64_t)gm * g.lda + colmap(gk, g.kg, g.kstride)])
+                  ? (AT ? g.A[(int64_t)gk * g.lda + gm]
+                        : g.A[(int64_t)gm * g.lda + (MAP ? colmap(gk, g.kg, g.kstride) : gk)])
                   : 0.0f;
       const int gn = n0 + bn[r], gk2 = k0 + bk[r];
       rb[r] = (gn < g.N && gk2 < ke) ? (BT ? g.B[(int64_t)gn * g.ldb + gk2] : g.B[(int64_t)gk2 * g.ldb + gn]) : 0.0f;
@@ -897,7 +900,7 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
   if (kb < ke) load(kb);
   for (int k0 = kb; k0 < ke; k0 += BK) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int r = 0; r < R; ++r) {
       As[ak[r]][am[r]] = ra[r];
       Bs[bk[r]][bn[r]] = rb[r];
     }
@@ -929,7 +932,7 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
         const int row = m0 + wm + 16 * a + 4 * (lane >> 4) + r;
         const int colm = n0 + wn + 16 * b + (lane & 15);
         if (row < g.M && colm < g.N) {
-          float* p = g.Cm + (int64_t)row * g.ldc + colmap(colm, g.ng, g.nstride);
+          float* p = g.Cm + (int64_t)row * g.ldc + (MAP ? colmap(colm, g.ng, g.nstride) : colm);
           if (g.atomic) atomicAdd(p, acc[a][b][r]);
           else *p = acc[a][b][r];
         }
@@ -948,12 +951,19 @@ so2_status gemm(const float* A, int64_t lda, const float* B, int64_t ldb, float*
     const int64_t want = std::max<int64_t>(1, 2048 / std::max<int64_t>(tiles, 1));
     const int64_t by_k = std::max<int64_t>(1, K / 512);
     splits = (unsigned)std::min(want, by_k);
-    g.k_split = (int)(((K + splits - 1) / splits + 15) / 16 * 16);
+    g.k_split = (int)(((K + splits - 1) / splits + kGemmK - 1) / kGemmK * kGemmK);
     splits = (unsigned)((K + g.k_split - 1) / g.k_split);
   }
-  hipLaunchKernelGGL((gemm_f32_kernel<AT, BT>),
-                     dim3((unsigned)((M + kGemmTile - 1) / kGemmTile), (unsigned)((N + kGemmTile - 1) / kGemmTile), splits),
-                     dim3(256), 0, stream, g);
+  if (kg || ng)
+    hipLaunchKernelGGL((gemm_f32_kernel<AT, BT, true>),
+                       dim3((unsigned)((M + kGemmTile - 1) / kGemmTile), (unsigned)((N + kGemmTile - 1) / kGemmTile),
+                            splits),
+                       dim3(256), 0, stream, g);
+  else
+    hipLaunchKernelGGL((gemm_f32_kernel<AT, BT, false>),
+                       dim3((unsigned)((M + kGemmTile - 1) / kGemmTile), (unsigned)((N + kGemmTile - 1) / kGemmTile),
+                            splits),
+                       dim3(256), 0, stream, g);
   SO2_CHECK_LAUNCH();
   return SO2_OK;
 }
