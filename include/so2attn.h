@@ -277,7 +277,7 @@ so2_status so2_attention_fwd_variant(const so2_attn_desc* desc, const so2_attn_v
  * its transpose, the weight gradient) are fp32 GEMMs over each batch on the
  * matrix cores.  Contributions to dx of sources, dpos, dq, dk and the
  * weights are summed with fp32 atomics, so the low bits vary between runs.
- * Shapes: L <= 6, C <= 256, H <= 64, else UNSUPPORTED.  A target whose
+ * Shapes: L <= 6, C <= 256, H <= 256, else UNSUPPORTED.  A target whose
  * envelopes are all 0 (edges exactly at the cutoff only) has y = 0 and
  * gets no gradient.
  * Errors: INVALID_ARGUMENT (also row_ptr[n_targets] < row_ptr[0]),

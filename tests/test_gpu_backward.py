@@ -6,7 +6,8 @@ Tolerance: fp32 arithmetic on fp32 or bf16-exact inputs, so the forward's
 fp32 bound applies: 1e-4 max relative error, normalised per atom for dx and
 dpos (the parity metric of the forward) and by the largest entry for the
 weight gradients.  Cases: the tiny fp32 workload (every atom, both flags),
-a small periodic water box, a bf16 batch at L = 4, C = 128, L = 6, empty
+a small periodic water box, a bf16 batch at L = 4, C = 128, L = 6, 128
+heads at C = 256, empty
 neighbourhoods with n_targets < n_atoms, targets whose edges take two and
 three batches (64 edges per target, at least 4096: the second pass then
 recomputes every batch but the last of the first); on the GPU's own output,
@@ -100,6 +101,15 @@ def test_bf16_inputs_l4_c128():
 def test_l6():
     say("backward L = 6")
     w = make_workload("tiny_fp32", l_max=6, channels=8, heads=2)
+    g, r, _, _ = _case(w)
+    assert max(_compare(g, r).values()) <= TOL
+
+
+def test_many_heads_wide_channels():
+    # 128 heads of 2 channels at C = 256: the per-(target, head) statistics
+    # and head sums hold heads lane and lane + 64 of each wave
+    say("backward C = 256, H = 128")
+    w = make_workload("tiny_fp32", l_max=1, channels=256, heads=128)
     g, r, _, _ = _case(w)
     assert max(_compare(g, r).values()) <= TOL
 

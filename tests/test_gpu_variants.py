@@ -3,7 +3,8 @@ variants (m_max < L, radial logit bias, F focus streams with the
 cross-focus softmax), through the C ABI:
 
 * fp32 on the edge-batch path, every atom of the tiny workload, each
-  variant alone and all together, at 1e-4;
+  variant alone and all together, at 1e-4; 128 heads and 128 focus streams
+  at C = 256;
 * targets whose edges take two and three batches (64 edges per target, at
   least 4096), with and without variants;
 * bf16 inputs: the logit bias on the MFMA kernel (a small-molecule batch
@@ -84,6 +85,13 @@ def _kind(w, m_max, n_focus):
 def test_fp32_variants_every_atom(m_max, n_focus, logit):
     w = make_workload("tiny_fp32")
     assert _run(w, m_max, n_focus, logit) <= TOL["fp32"]
+
+
+def test_fp32_many_heads_and_focus_streams():
+    # C = 256 with 128 heads and 128 focus streams of 2 channels: the
+    # statistics and the cross-focus softmax run over more than 64 entries
+    w = make_workload("tiny_fp32", l_max=1, channels=256, heads=128)
+    assert _run(w, 1, 128, True) <= TOL["fp32"]
 
 
 def test_bf16_logit_bias_on_the_mfma_kernel():
