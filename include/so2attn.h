@@ -227,12 +227,14 @@ so2_status so2_attention_fwd_stages(uint32_t stages, const so2_attn_desc* desc, 
  *              edge message is scaled by pi_f = softmax_f(sum_{c in f}
  *              w_focus[c] yt[(0,0), c])
  *   w_focus    [C] in dtype, required when n_focus > 1
- * The base layer (m_max = -1 or l_max, n_focus = 1) runs where
- * so2_attention_fwd would, with or without the logit bias; truncated orders
- * and focus streams run on the fp32 VALU kernel.  Other arguments, the
- * workspace (so2_attention_variant_workspace_bytes) and the errors are those
- * of so2_attention_fwd, plus INVALID_ARGUMENT for m_max outside -1..l_max,
- * n_focus < 1 or not dividing C, or a missing w_focus.
+ * One stream (n_focus = 1), any m_max, with or without the logit bias, runs
+ * where so2_attention_fwd would: bf16 MFMA shapes on the MFMA kernel (its
+ * passes for |m| > m_max are not compiled into the instance of that m_max),
+ * the rest on the fp32 edge-batch path; focus streams always run on the
+ * edge-batch path (so2_attention_variant_kernel_kind says which).  Other
+ * arguments, the workspace (so2_attention_variant_workspace_bytes) and the
+ * errors are those of so2_attention_fwd, plus INVALID_ARGUMENT for m_max
+ * outside -1..l_max, n_focus < 1 or not dividing C, or a missing w_focus.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t m_max;   /* orders |m| <= m_max; -1 = l_max (every order)      */

@@ -161,6 +161,7 @@ struct MfmaParams {
   uint32_t xp_bytes;  // extent of xp for its buffer descriptor
   uint32_t w_bytes;   // extent of w_so2
   int32_t n_targets, H, K, p;
+  int32_t m_max;  // the per-m maps stop at |m| = m_max (L: every order)
   float cutoff;
   uint32_t flags;
   int32_t periodic;
@@ -233,7 +234,7 @@ __device__ inline float logit_bias(const MfmaParams& P, float rho, int h) {
 // = x[l^2 + 2p][c] | x[l^2 + 2p + 1][c] << 16 (upper half 0 for p = l),
 // four channels per thread;
 // w_rad bf16 -> fp32;
-// w_so2 -> fragment order: each matrix (W0, then W1_m, W2_m for m = 1..L,
+// w_so2 -> fragment order: each matrix (W0, then W1_m, W2_m for m = 1..m_max,
 // at the same offsets) is cut into 16-row x 32-column blocks, block (row
 // tile R, K step s) at (R (KM / 32) + s) KB, and lane (row % 16) + 16
 // ((col % 32) / 8) of a block holds its 8 consecutive columns, so one
@@ -243,12 +244,12 @@ __global__ void __launch_bounds__(256) attn_pack_kernel(const uint16_t* __restri
                                                         int n_atoms, const uint16_t* __restrict__ w_rad,
                                                         float* __restrict__ wrad, int n_rbf,
                                                         const uint16_t* __restrict__ w_so2,
-                                                        uint16_t* __restrict__ wf) {
+                                                        uint16_t* __restrict__ wf, int64_t w_entries) {
   constexpr int NC = (L + 1) * (L + 1);
   constexpr int NP = pair_off(L + 1);
   const int64_t n_x = (int64_t)n_atoms * NP * (kC / 4);
   const int64_t n_w = (int64_t)n_rbf * kC;
-  const int64_t n_f = wf_entries(L) / 8;
+  const int64_t n_f = w_entries / 8;  // the blocks m <= m_max that w_so2 holds
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_x + n_w + n_f; i += stride) {
     if (i < n_x) {
@@ -397,21 +398,23 @@ struct SmemT {
 template <int L>
 using Smem = SmemT<(16 * Cfg<L>::TT > 112 ? 16 * Cfg<L>::TT : 112)>;
 
-// Passes in execution order: blocks m = 1..L, each in groups of at most two
-// output degrees (the limit of the register and LDS budgets with two sign
-// planes and 64-edge chunks; three with the 32-edge chunks of L >= 5), then
-// m = 0 in one pass over all its L + 1 output degrees.  Every pass
-// generates, during its last A chunk, the first A chunk of the pass after
-// it; ending on m = 0 means a pass never has to produce more sign planes
-// than it has itself (an m >= 1 pass writes both planes, m = 0 reads one).
+// Passes in execution order: blocks m = 1..MM (MM = m_max, L for the base
+// layer: the blocks above m_max are not computed), each in groups of at
+// most two output degrees (the limit of the register and LDS budgets with
+// two sign planes and 64-edge chunks; three with the 32-edge chunks of
+// L >= 5), then m = 0 in one pass over all its L + 1 output degrees.  Every
+// pass generates, during its last A chunk, the first A chunk of the pass
+// after it; ending on m = 0 means a pass never has to produce more sign
+// planes than it has itself (an m >= 1 pass writes both planes, m = 0
+// reads one).
 struct PassInfo {
   int M, LO, ND;
 };
 
-__host__ __device__ constexpr PassInfo pass_info(int L, int idx) {
+__host__ __device__ constexpr PassInfo pass_info(int L, int idx, int MM) {
   int i = 0;
-  for (int mm = 1; mm <= L + 1; ++mm) {
-    const int M = mm == L + 1 ? 0 : mm;
+  for (int mm = 1; mm <= MM + 1; ++mm) {
+    const int M = mm == MM + 1 ? 0 : mm;
     const int nd = M == 0 ? L + 1 : (L <= 4 ? 2 : 3);
     for (int lo = M; lo <= L; lo += nd) {
       if (i == idx) return PassInfo{M, lo, (L + 1 - lo) < nd ? (L + 1 - lo) : nd};
@@ -426,8 +429,8 @@ __host__ __device__ constexpr int deg_tiles(int l) {
 }
 
 // A' fragments of pass idx: (degree, tile, K step) for its output degrees.
-__host__ __device__ constexpr int frag_count(int L, int idx) {
-  const PassInfo pi = pass_info(L, idx);
+__host__ __device__ constexpr int frag_count(int L, int idx, int MM) {
+  const PassInfo pi = pass_info(L, idx, MM);
   const int rt = chunk_edges(L) / 16;
   const int steps = pi.M == 0 ? rt / 2 : rt;
   int t = 0;
@@ -435,16 +438,18 @@ __host__ __device__ constexpr int frag_count(int L, int idx) {
   return t;
 }
 
+// the most A' fragments of any pass (the passes of m_max < L are a subset
+// of those of the base layer)
 __host__ __device__ constexpr int max_frags(int L) {
   int m = 0;
-  for (int i = 0; pass_info(L, i).M >= 0; ++i) m = frag_count(L, i) > m ? frag_count(L, i) : m;
+  for (int i = 0; pass_info(L, i, L).M >= 0; ++i) m = frag_count(L, i, L) > m ? frag_count(L, i, L) : m;
   return m;
 }
 
 // A chunks (one degree of one block, 128 channels) of the passes before idx.
-__host__ __device__ constexpr int chunks_before(int L, int idx) {
+__host__ __device__ constexpr int chunks_before(int L, int idx, int MM) {
   int c = 0;
-  for (int i = 0; i < idx; ++i) c += L + 1 - pass_info(L, i).M;
+  for (int i = 0; i < idx; ++i) c += L + 1 - pass_info(L, i, MM).M;
   return c;
 }
 
@@ -907,12 +912,12 @@ __device__ inline void fused_step(const uint16_t* abuf, int k, int dglp, const u
 // A' fragments of pass PI, in the order (degree, tile, K step), 64 lanes x
 // 16 bytes each.  Wave w builds fragments w, w + 4, ...; the fragment decode
 // is wave-uniform.
-template <int L, int PI>
+template <int L, int MM, int PI>
 __device__ inline void aprime_build(char* smem, u32x4* frag) {
-  constexpr PassInfo pi = pass_info(L, PI);
+  constexpr PassInfo pi = pass_info(L, PI, MM);
   constexpr int M = pi.M, LO = pi.LO;
   constexpr int STEPS = M == 0 ? Geo<L>::RT / 2 : Geo<L>::RT;
-  constexpr int TOTAL = frag_count(L, PI);
+  constexpr int TOTAL = frag_count(L, PI, MM);
   const Smem<L>& S = *(const Smem<L>*)smem;
   const uint32_t* sD = (const uint32_t*)(smem + Lds<L>::kD);
   const int lane = threadIdx.x & 63;
@@ -1019,9 +1024,9 @@ __device__ inline void rot_back_all(char* smem, const Ctx& c, const f32x4 (&acc)
 // q is multiplied): the next degree of the same block, else the first
 // chunk of the next pass; after the last pass a dummy (degree 0 of m = 0)
 // whose result nobody reads.
-template <int L, int PI>
+template <int L, int MM, int PI>
 __device__ inline void gen_target(int q, int& gm, int& glp) {
-  constexpr PassInfo pi = pass_info(L, PI), pn = pass_info(L, PI + 1);
+  constexpr PassInfo pi = pass_info(L, PI, MM), pn = pass_info(L, PI + 1, MM);
   constexpr int NCH = L + 1 - pi.M;
   if (q + 1 < NCH) {
     gm = pi.M;
@@ -1034,7 +1039,7 @@ __device__ inline void gen_target(int q, int& gm, int& glp) {
 
 // One pass: block M, output degrees LO .. LO+ND-1.  On entry the B fragments
 // of K step 0 are in flight in ring[0] and the gathers of generator unit 0
-// of chunk 0's target in xa; A chunk 0 is in LDS buffer chunks_before(PI) & 1
+// of chunk 0's target in xa; A chunk 0 is in LDS buffer chunks_before(L, PI, MM) & 1
 // once every wave has reached the first barrier.
 //
 // K step s = 4 q + k multiplies A chunk q (degree M + q, channels 32 k ..
@@ -1043,18 +1048,18 @@ __device__ inline void gen_target(int q, int& gm, int& glp) {
 // (slice k of the other buffer), uses gathers issued one step earlier and is
 // interleaved with the MFMAs.  The loop body is two K steps; one barrier
 // per A chunk.
-template <int L, int PI>
+template <int L, int MM, int PI>
 __device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams& P, char* smem, const Ctx& c,
                                                                f32x4 (&T)[Cfg<L>::TT][kNT],
-                                                               u32x4 (&ring)[2][pass_info(L, PI).ND]
-                                                                            [n_bmat(pass_info(L, PI).M)][kNT],
+                                                               u32x4 (&ring)[2][pass_info(L, PI, MM).ND]
+                                                                            [n_bmat(pass_info(L, PI, MM).M)][kNT],
                                                                typename XVec<Geo<L>::GCH>::type (&xa)[kGR * Geo<L>::MP],
                                                                typename XVec<Geo<L>::GCH>::type (&xb)[kGR * Geo<L>::MP]) {
-  constexpr PassInfo pi = pass_info(L, PI), pn = pass_info(L, PI + 1);
+  constexpr PassInfo pi = pass_info(L, PI, MM), pn = pass_info(L, PI + 1, MM);
   constexpr int M = pi.M, LO = pi.LO, ND = pi.ND, NS = M ? 2 : 1;
   constexpr int RT = Geo<L>::RT, MP = Geo<L>::MP;
   constexpr int NCH = L + 1 - M, NSTEP = 4 * NCH;
-  constexpr int PAR = chunks_before(L, PI) & 1;
+  constexpr int PAR = chunks_before(L, PI, MM) & 1;
   const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(P.wf, P.w_bytes);
   const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(P.xp, P.xp_bytes);
   const uint32_t* sD = (const uint32_t*)(smem + Lds<L>::kD);
@@ -1067,7 +1072,7 @@ __device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams&
   b_offsets<L, M, LO, ND>(boff);
 
   __syncthreads();  // chunk 0 written; every wave is done with the previous A'
-  aprime_build<L, PI>(smem, frag);
+  aprime_build<L, MM, PI>(smem, frag);
 
   f32x4 acc[ND][NS][kNT][RT];
 #pragma unroll
@@ -1087,14 +1092,14 @@ __device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams&
     const int k = s & 3;  // 0 or 2
     if (k == 0) {
       int gm;
-      gen_target<L, PI>(q, gm, glp);
+      gen_target<L, MM, PI>(q, gm, glp);
       gen_dpairs<L>(sD, c, gm, glp, dp, dm);
     }
     // degree of the chunk whose generator unit 0 is gathered in step s + 1
     int glp2 = glp;
     if (k == 2) {
       int gm2;
-      gen_target<L, PI>(q + 1 < NCH ? q + 1 : q, gm2, glp2);
+      gen_target<L, MM, PI>(q + 1 < NCH ? q + 1 : q, gm2, glp2);
     }
     const uint16_t* acur = abase + ((PAR + q) & 1) * Geo<L>::ABUF;
     uint16_t* anext = abase + ((PAR + q + 1) & 1) * Geo<L>::ABUF;
@@ -1115,10 +1120,10 @@ __device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams&
     load_b<L, pn.M, pn.LO, NDn>(wrs, nboff, 0, nring[0]);
     // gathers of generator unit 0 for the next pass's chunk 0 target
     int gm, glp0;
-    gen_target<L, PI + 1>(0, gm, glp0);
+    gen_target<L, MM, PI + 1>(0, gm, glp0);
     gen_issue<L>(xrs, c, oob, glp0, 0, xa);
     rot_back_all<L, M, LO, 0, ND>(smem, c, acc, frag, T);
-    run_pass<L, PI + 1>(P, smem, c, T, nring, xa, xb);
+    run_pass<L, MM, PI + 1>(P, smem, c, T, nring, xa, xb);
   } else {
     rot_back_all<L, M, LO, 0, ND>(smem, c, acc, frag, T);
   }
@@ -1521,7 +1526,8 @@ __global__ void __launch_bounds__(kSchedThreads) attn_runs_chain_kernel(const in
     for (int g = t; g < n_groups; g += kSchedThreads) gs[g] = pos[g];
 }
 
-template <int L>
+// MM: the per-m maps stop at |m| = MM (m_max; L for the base layer).
+template <int L, int MM>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 attn_mfma_kernel(MfmaParams P, int n_groups) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -1534,7 +1540,7 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   constexpr int NC = Cfg<L>::NC;
-  constexpr PassInfo p0 = pass_info(L, 0);
+  constexpr PassInfo p0 = pass_info(L, 0, MM);
   constexpr int NS0 = p0.M ? 2 : 1;
   constexpr int CM = Geo<L>::M, GL = Geo<L>::GL, MP = Geo<L>::MP;
   typedef typename XVec<Geo<L>::GCH>::type XV;
@@ -1758,19 +1764,19 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
     {
       uint32_t dp[kGR][MP], dm[kGR][MP];
       gen_dpairs<L>(sD, c, p0.M, p0.M, dp, dm);
-      gen_finish<L, NS0>(sG, c, 0, xa, dp, dm, abase);  // chunks_before(L, 0) = 0
+      gen_finish<L, NS0>(sG, c, 0, xa, dp, dm, abase);  // chunks_before(L, 0, MM) = 0
       gen_issue<L>(xrs, c, P.xp_bytes, p0.M, 2, xa);
       gen_finish<L, NS0>(sG, c, 1, xb, dp, dm, abase);
       gen_issue<L>(xrs, c, P.xp_bytes, p0.M, 3, xb);
       gen_finish<L, NS0>(sG, c, 2, xa, dp, dm, abase);
       // gathers of generator unit 0 for chunk 0's target
       int gm, glp;
-      gen_target<L, 0>(0, gm, glp);
+      gen_target<L, MM, 0>(0, gm, glp);
       gen_issue<L>(xrs, c, P.xp_bytes, glp, 0, xa);
       gen_finish<L, NS0>(sG, c, 3, xb, dp, dm, abase);
 
       // ---- phase B: every pass, each ending in its rotate-back GEMMs
-      run_pass<L, 0>(P, smem, c, T, ring, xa, xb);
+      run_pass<L, MM, 0>(P, smem, c, T, ring, xa, xb);
     }
 
     // ---- phase D: write out targets whose last edge is in this chunk
@@ -1823,19 +1829,29 @@ so2_status schedule_L(const MfmaParams& P, int32_t* next, int32_t* sched, hipStr
   return SO2_OK;
 }
 
+// The kernel instance of P.m_max (MM counts down from L).
+template <int L, int MM>
+so2_status launch_LM(const MfmaParams& P, int n_groups, hipStream_t stream) {
+  if constexpr (MM > 0) {
+    if (P.m_max < MM) return launch_LM<L, MM - 1>(P, n_groups, stream);
+  }
+  if (P.m_max != MM) return SO2_ERR_INVALID_ARGUMENT;
+  const size_t smem = Lds<L>::kTotal;
+  static_assert(Lds<L>::kTotal <= 160 * 1024, "LDS budget");
+  SO2_CHECK(hipFuncSetAttribute((const void*)attn_mfma_kernel<L, MM>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)smem));
+  hipLaunchKernelGGL((attn_mfma_kernel<L, MM>), dim3(n_groups), dim3(kThreads), smem, stream, P, n_groups);
+  SO2_CHECK_LAUNCH();
+  return SO2_OK;
+}
+
 template <int L>
 so2_status launch_L(const MfmaParams& P, hipStream_t stream) {
   int n_cu = 256;
   const so2_status st = device_cu_count(&n_cu);
   if (st != SO2_OK) return st;
   const int n_groups = group_count(P.n_targets, n_cu);
-  const size_t smem = Lds<L>::kTotal;
-  static_assert(Lds<L>::kTotal <= 160 * 1024, "LDS budget");
-  SO2_CHECK(hipFuncSetAttribute((const void*)attn_mfma_kernel<L>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem));
-  hipLaunchKernelGGL(attn_mfma_kernel<L>, dim3(n_groups), dim3(kThreads), smem, stream, P, n_groups);
-  SO2_CHECK_LAUNCH();
-  return SO2_OK;
+  return launch_LM<L, L>(P, n_groups, stream);
 }
 
 // Workspace of the MFMA path: softmax statistics, the x pairs, w_rad in
@@ -1879,7 +1895,8 @@ MfmaParams make_params(const AttnArgs& a) {
   P.y = a.y;
   P.w_logit = (const uint16_t*)a.w_logit;
   P.xp_bytes = (uint32_t)((uint64_t)a.n_atoms * pair_off(a.L + 1) * kC * 4);
-  P.w_bytes = (uint32_t)(wf_entries(a.L) * 2);
+  P.w_bytes = (uint32_t)(w1_offset(a.L, a.m_max + 1) * 2);  // the blocks m <= m_max
+  P.m_max = a.m_max;
   P.n_targets = a.n_targets;
   P.H = a.H;
   P.K = a.K;
@@ -1893,11 +1910,13 @@ MfmaParams make_params(const AttnArgs& a) {
 
 template <int L>
 so2_status launch_pack_L(const AttnArgs& a, const MfmaParams& P, hipStream_t stream) {
-  const int64_t work = (int64_t)a.n_atoms * pair_off(L + 1) * (kC / 4) + (int64_t)a.K * kC + wf_entries(L) / 8;
+  const int64_t w_entries = w1_offset(L, a.m_max + 1);  // w_so2 holds the blocks m <= m_max
+  const int64_t work = (int64_t)a.n_atoms * pair_off(L + 1) * (kC / 4) + (int64_t)a.K * kC + w_entries / 8;
   const int64_t blocks = std::min<int64_t>((work + 255) / 256, 8192);
   hipLaunchKernelGGL(attn_pack_kernel<L>, dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const uint16_t*)a.x, const_cast<uint32_t*>(P.xp), a.n_atoms, (const uint16_t*)a.w_rad,
-                     const_cast<float*>(P.wrad), a.K, (const uint16_t*)a.w_so2, const_cast<uint16_t*>(P.wf));
+                     const_cast<float*>(P.wrad), a.K, (const uint16_t*)a.w_so2, const_cast<uint16_t*>(P.wf),
+                     w_entries);
   SO2_CHECK_LAUNCH();
   return SO2_OK;
 }

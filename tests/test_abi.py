@@ -320,7 +320,11 @@ def test_variant_counts_and_errors():
     mf = _desc(l_max=4, channels=128, heads=8, n_rbf=16, dtype=sea.SO2_BF16)
     assert lib.so2_attention_variant_kernel_kind(ctypes.byref(mf), ctypes.byref(sea.AttnVariant(-1, 1))) == \
         sea.KERNEL_MFMA
-    assert lib.so2_attention_variant_kernel_kind(ctypes.byref(mf), ctypes.byref(sea.AttnVariant(2, 1))) == \
+    # truncated orders run on the MFMA kernel, focus streams on the edge-batch path
+    for m in (0, 2, 3):
+        assert lib.so2_attention_variant_kernel_kind(ctypes.byref(mf), ctypes.byref(sea.AttnVariant(m, 1))) == \
+            sea.KERNEL_MFMA
+    assert lib.so2_attention_variant_kernel_kind(ctypes.byref(mf), ctypes.byref(sea.AttnVariant(2, 2))) == \
         sea.KERNEL_BATCH
     assert lib.so2_attention_variant_kernel_kind(ctypes.byref(mf), ctypes.byref(sea.AttnVariant(-1, 2))) == \
         sea.KERNEL_BATCH

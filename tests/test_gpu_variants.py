@@ -7,9 +7,11 @@ cross-focus softmax), through the C ABI:
   at C = 256;
 * targets whose edges take two and three batches (64 edges per target, at
   least 4096), with and without variants;
-* bf16 inputs: the logit bias on the MFMA kernel (a small-molecule batch
-  at 2e-2, and seeded targets of the L = 6 water box); truncated orders and
-  focus streams at C = 128 on the edge-batch path (fp32 arithmetic, 1e-4);
+* bf16 inputs on the MFMA kernel at 2e-2: the logit bias (a small-molecule
+  batch, and seeded targets of the L = 6 water box) and truncated orders
+  (m_max = 0..3 at L = 4, m_max = L - 1 and 0 at every other degree, m_max =
+  2 and 4 on seeded targets of the L = 6 water box); focus streams at
+  C = 128 on the edge-batch path (fp32 arithmetic, 1e-4);
 * the base variant through the variant call is bitwise the base call;
   repeated calls on the edge-batch path are bitwise equal."""
 
@@ -108,13 +110,41 @@ def test_bf16_logit_bias_l6_water_sampled():
     assert _run(w, logit=True, targets=t) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("m_max,n_focus", [(2, 1), (-1, 4), (3, 2)])
-def test_bf16_c128_variants_on_the_batch_path(m_max, n_focus):
+@pytest.mark.parametrize("m_max,n_focus", [(-1, 4), (3, 2), (0, 2)])
+def test_bf16_c128_focus_streams_on_the_batch_path(m_max, n_focus):
     import so_equivariant_graph_amd as sea
 
     w = make_workload("small_molecules", geometry=dict(n_molecules=2))
     assert _kind(w, m_max, n_focus) == sea.KERNEL_BATCH
     assert _run(w, m_max, n_focus, logit=True) <= 1e-4
+
+
+@pytest.mark.parametrize("m_max,logit", [(0, False), (1, True), (2, False), (3, True)])
+def test_bf16_truncated_orders_on_the_mfma_kernel(m_max, logit):
+    import so_equivariant_graph_amd as sea
+
+    w = make_workload("small_molecules", geometry=dict(n_molecules=3))
+    assert _kind(w, m_max, 1) == sea.KERNEL_MFMA
+    assert _run(w, m_max, 1, logit=logit) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 5, 6])
+def test_bf16_truncated_orders_every_degree(L):
+    # m_max = L - 1 and m_max = 0 on the MFMA kernel of every degree (the
+    # 32-edge chunks of L = 5, 6 included)
+    import so_equivariant_graph_amd as sea
+
+    w = make_workload("tiny_fp32", l_max=L, channels=128, heads=8, n_rbf=16, dtype="bf16")
+    for mm in sorted({L - 1, 0}):
+        assert _kind(w, mm, 1) == sea.KERNEL_MFMA
+        assert _run(w, mm, 1, logit=mm == 0) <= TOL["bf16"]
+
+
+def test_bf16_truncated_orders_l6_water_sampled():
+    w = make_workload("water_l6")
+    t = np.sort(np.random.default_rng(2).choice(w.n_atoms, 48, replace=False))
+    for mm in (2, 4):
+        assert _run(w, mm, 1, logit=True, targets=t) <= TOL["bf16"]
 
 
 def test_base_variant_is_the_base_call():
