@@ -54,17 +54,19 @@ bool is_base(const so2_attn_desc* d, const so2_attn_variant* v) {
   return (v->m_max < 0 || v->m_max == d->l_max) && v->n_focus == 1;
 }
 
-// bf16 shapes the MFMA kernel takes run there, the base layer and truncated
-// orders (m_max < L) alike; past its size limit they are refused (kNone)
-// rather than moved to a slower path.  Everything else (fp32, other shapes,
-// focus streams) runs on the fp32 edge-batch path, which reads the edge
-// count back once; with allow_wait false (callers that must not wait on the
-// stream) it runs on the fp32 VALU kernel instead, which takes the base
-// layer only.
+// bf16 shapes the MFMA kernel takes run there: the base layer, truncated
+// orders (m_max < L), and 2, 4 or 8 focus streams at L <= 4 with every
+// order and whole heads per stream; past its size limit they are refused
+// (kNone) rather than moved to a slower path.  Everything else (fp32, other
+// shapes, other focus streams) runs on the fp32 edge-batch path, which
+// reads the edge count back once; with allow_wait false (callers that must
+// not wait on the stream) it runs on the fp32 VALU kernel instead, which
+// takes the base layer only.
 Kind pick_kind(const so2_attn_desc* d, const so2_attn_variant* v = &kBase, bool allow_wait = true) {
-  if (v->n_focus == 1 && d->dtype == SO2_BF16 && mfma_shape(d->l_max, d->channels, d->heads, d->n_rbf))
-    return mfma_fits(d->l_max, d->n_atoms) ? kMfma : kNone;
   const int mm = v->m_max < 0 ? d->l_max : v->m_max;
+  if (d->dtype == SO2_BF16 && mfma_shape(d->l_max, d->channels, d->heads, d->n_rbf) &&
+      mfma_focus(d->l_max, d->heads, mm, v->n_focus))
+    return mfma_fits(d->l_max, d->n_atoms) ? kMfma : kNone;
   if (allow_wait && batch_fwd_supported(d->l_max, d->channels, d->heads, d->n_rbf, mm, v->n_focus)) return kBatch;
   if (!allow_wait && is_base(d, v) && valu_supported(d->l_max, d->channels, d->heads)) return kValu;
   return kNone;

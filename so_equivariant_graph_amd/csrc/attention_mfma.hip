@@ -162,6 +162,8 @@ struct MfmaParams {
   uint32_t w_bytes;   // extent of w_so2
   int32_t n_targets, H, K, p;
   int32_t m_max;  // the per-m maps stop at |m| = m_max (L: every order)
+  int32_t n_focus;          // F focus streams of C / F channels (1: one)
+  const uint16_t* w_focus;  // [C] bf16 focus score weights (F > 1)
   float cutoff;
   uint32_t flags;
   int32_t periodic;
@@ -244,12 +246,14 @@ __global__ void __launch_bounds__(256) attn_pack_kernel(const uint16_t* __restri
                                                         int n_atoms, const uint16_t* __restrict__ w_rad,
                                                         float* __restrict__ wrad, int n_rbf,
                                                         const uint16_t* __restrict__ w_so2,
-                                                        uint16_t* __restrict__ wf, int64_t w_entries) {
+                                                        uint16_t* __restrict__ wf, int64_t w_entries, int F) {
   constexpr int NC = (L + 1) * (L + 1);
   constexpr int NP = pair_off(L + 1);
   const int64_t n_x = (int64_t)n_atoms * NP * (kC / 4);
   const int64_t n_w = (int64_t)n_rbf * kC;
-  const int64_t n_f = w_entries / 8;  // the blocks m <= m_max that w_so2 holds
+  // the blocks m <= m_max that w_so2 holds (one stream), or the dense
+  // block-diagonal matrices of F streams
+  const int64_t n_f = (F == 1 ? w_entries : wf_entries(L)) / 8;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_x + n_w + n_f; i += stride) {
     if (i < n_x) {
@@ -288,7 +292,29 @@ __global__ void __launch_bounds__(256) attn_pack_kernel(const uint16_t* __restri
       const int ks = (int)(f % (KM / 32));
       const int64_t row = 16 * (f / (KM / 32)) + (lane & 15);
       const int col = 32 * ks + 8 * (lane >> 4);
-      *(u32x4*)(wf + g) = *(const u32x4*)(w_so2 + base + row * KM + col);
+      if (F == 1) {
+        *(u32x4*)(wf + g) = *(const u32x4*)(w_so2 + base + row * KM + col);
+      } else {
+        // F streams: the dense matrix is block-diagonal over the streams,
+        // stream s's block being matrix mi of stack s (the same packing
+        // over C' = C / F channels, stacks back to back in w_so2)
+        const int Cs = kC / F;
+        const int co = (int)(row % kC), ci = col % kC;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (co / Cs == ci / Cs) {
+          const int st = co / Cs;
+          int64_t sbase = 0;  // matrix mi within a stack
+          int KMs = (L + 1) * Cs;
+          for (int k = 0; k < mi; ++k) {
+            sbase += (int64_t)KMs * KMs;
+            KMs = (L + 1 - (k + 2) / 2) * Cs;
+          }
+          const int64_t per = w_entries / F;
+          const int64_t rs = (row / kC) * Cs + (co - st * Cs), cs = (col / kC) * Cs + (ci - st * Cs);
+          v = *(const u32x4*)(w_so2 + st * per + sbase + rs * KMs + cs);
+        }
+        *(u32x4*)(wf + g) = v;
+      }
     }
   }
 }
@@ -1129,6 +1155,123 @@ __device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams&
   }
 }
 
+// ---------------------------------------------------------------- focus streams
+
+// Cross-focus softmax of F streams (L <= 4; F divides the head count, so
+// every head lies in one stream): per edge, score_f = sum over the
+// stream's channels c of w_focus[c] yt[(0,0), c], the stream's invariant
+// l = 0 output of the m = 0 map in the edge frame, and pi_f = softmax_f;
+// pi then scales the softmax weights of the stream's heads in LDS, so the
+// rotate-back of every pass applies it.  yt[(0,0), .] is the m = 0 map's
+// output degree 0: a GEMM over the chunk's m = 0 A chunks (degrees 0..L,
+// generated here one after another into the two A buffers) with W0's
+// degree-0 rows, on the matrix cores; the per-wave partial scores (16
+// channels each) meet in the A' fragment area, free before the first pass.
+template <int L, int F>
+__device__ inline void focus_weights(const MfmaParams& P, char* smem, const Ctx& c, int nrows) {
+  static_assert(Geo<L>::M == 64, "64-edge chunks (L <= 4)");
+  constexpr int RT = Geo<L>::RT, MP = Geo<L>::MP;
+  const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(P.wf, P.w_bytes);
+  const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(P.xp, P.xp_bytes);
+  const uint32_t* sD = (const uint32_t*)(smem + Lds<L>::kD);
+  const float* sG = (const float*)(smem + Lds<L>::kG);
+  float* sW = (float*)(smem + Lds<L>::kW);
+  uint16_t* abase = (uint16_t*)(smem + Lds<L>::kA);
+  float* sScore = (float*)(smem + Lds<L>::kF);  // [kWaves][M]
+  const uint32_t oob = P.xp_bytes;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  uint32_t boff[1][kNT];
+  b_offsets<L, 0, 0, 1>(boff);
+  f32x4 acc[kNT][RT];
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[nt][rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  typename XVec<Geo<L>::GCH>::type xa[kGR * MP], xb[kGR * MP];
+  for (int lp = 0; lp <= L; ++lp) {
+    uint16_t* ab = abase + (lp & 1) * Geo<L>::ABUF;
+    // W0's degree-0 rows for the 4 K steps of input degree lp
+    u32x4 b[4][1][1][kNT];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) load_b<L, 0, 0, 1>(wrs, boff, 4 * lp + k, b[k]);
+    // the m = 0 A chunk of degree lp (one plane), 4 generator units
+    uint32_t dp[kGR][MP], dm[kGR][MP];
+    gen_dpairs<L>(sD, c, 0, lp, dp, dm);
+    gen_issue<L>(xrs, c, oob, lp, 0, xa);
+    gen_issue<L>(xrs, c, oob, lp, 1, xb);
+    gen_finish<L, 1>(sG, c, 0, xa, dp, dm, ab);
+    gen_issue<L>(xrs, c, oob, lp, 2, xa);
+    gen_finish<L, 1>(sG, c, 1, xb, dp, dm, ab);
+    gen_issue<L>(xrs, c, oob, lp, 3, xb);
+    gen_finish<L, 1>(sG, c, 2, xa, dp, dm, ab);
+    gen_finish<L, 1>(sG, c, 3, xb, dp, dm, ab);
+    // every wave wrote its part; every wave is done with the chunk before
+    // the previous one in this buffer
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int grp = 4 * k + g4;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const u32x4 av = *(const u32x4*)(ab + a_off(16 * rt + l16, grp));
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) acc[nt][rt] = mfma(as_bf16x8(av), as_bf16x8(b[k][0][0][nt]), acc[nt][rt]);
+      }
+    }
+  }
+  // partial scores of this wave's 16 channels: lane (g4, l16) holds rows
+  // 16 rt + 4 g4 + i of column l16; sum the 16 columns of each row
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      const float wfc = bf16_to_float(P.w_focus[16 * kNT * wave + 16 * nt + l16]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += wfc * acc[nt][rt][i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) v[i] += __shfl_xor(v[i], o, 64);
+    }
+    if (l16 == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sScore[wave * Geo<L>::M + 16 * rt + 4 * g4 + i] = v[i];
+    }
+  }
+  __syncthreads();
+  // one thread per edge row: the streams' scores, their softmax, and the
+  // stream factor on the weights of the stream's heads
+  constexpr int WPS = kWaves / F;  // waves (16 channels each) per stream
+  static_assert(kWaves % F == 0, "whole waves per stream");
+  if (threadIdx.x < Geo<L>::M) {
+    const int r = threadIdx.x;
+    float sc[F];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      float t = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WPS; ++w) t += sScore[(f * WPS + w) * Geo<L>::M + r];
+      sc[f] = t;
+      mx = fmaxf(mx, t);
+    }
+    float den = 0.0f;
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      sc[f] = expf(sc[f] - mx);
+      den += sc[f];
+    }
+    const float inv = 1.0f / den;
+    const int hps = P.H / F;  // heads per stream
+    if (r < nrows)
+      for (int h = 0; h < P.H; ++h) sW[h * Geo<L>::M + r] *= sc[h / hps] * inv;
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------- flush
 
 // Accumulator row R = kSlots l^2 + slot (2l+1) + comp - l^2 as slot << 8 |
@@ -1527,7 +1670,9 @@ __global__ void __launch_bounds__(kSchedThreads) attn_runs_chain_kernel(const in
 }
 
 // MM: the per-m maps stop at |m| = MM (m_max; L for the base layer).
-template <int L, int MM>
+// F: focus streams (1: one; 2, 4, 8 at L <= 4 with the block-diagonal
+// weights and the cross-focus softmax of focus_weights).
+template <int L, int MM, int F>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 attn_mfma_kernel(MfmaParams P, int n_groups) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -1760,6 +1905,9 @@ attn_mfma_kernel(MfmaParams P, int n_groups) {
       }
     }
 
+    // ---- focus streams: the cross-focus softmax folded into the weights
+    if constexpr (F > 1) focus_weights<L, F>(P, smem, c, nrows);
+
     // ---- first A chunk (block p0.M, degree p0.M): all four generator units
     {
       uint32_t dp[kGR][MP], dm[kGR][MP];
@@ -1829,20 +1977,25 @@ so2_status schedule_L(const MfmaParams& P, int32_t* next, int32_t* sched, hipStr
   return SO2_OK;
 }
 
-// The kernel instance of P.m_max (MM counts down from L).
+template <int L, int MM, int F>
+so2_status launch_instance(const MfmaParams& P, int n_groups, hipStream_t stream) {
+  const size_t smem = Lds<L>::kTotal;
+  static_assert(Lds<L>::kTotal <= 160 * 1024, "LDS budget");
+  SO2_CHECK(hipFuncSetAttribute((const void*)attn_mfma_kernel<L, MM, F>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem));
+  hipLaunchKernelGGL((attn_mfma_kernel<L, MM, F>), dim3(n_groups), dim3(kThreads), smem, stream, P, n_groups);
+  SO2_CHECK_LAUNCH();
+  return SO2_OK;
+}
+
+// The kernel instance of P.m_max (MM counts down from L), one stream.
 template <int L, int MM>
 so2_status launch_LM(const MfmaParams& P, int n_groups, hipStream_t stream) {
   if constexpr (MM > 0) {
     if (P.m_max < MM) return launch_LM<L, MM - 1>(P, n_groups, stream);
   }
   if (P.m_max != MM) return SO2_ERR_INVALID_ARGUMENT;
-  const size_t smem = Lds<L>::kTotal;
-  static_assert(Lds<L>::kTotal <= 160 * 1024, "LDS budget");
-  SO2_CHECK(hipFuncSetAttribute((const void*)attn_mfma_kernel<L, MM>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)smem));
-  hipLaunchKernelGGL((attn_mfma_kernel<L, MM>), dim3(n_groups), dim3(kThreads), smem, stream, P, n_groups);
-  SO2_CHECK_LAUNCH();
-  return SO2_OK;
+  return launch_instance<L, MM, 1>(P, n_groups, stream);
 }
 
 template <int L>
@@ -1851,7 +2004,19 @@ so2_status launch_L(const MfmaParams& P, hipStream_t stream) {
   const so2_status st = device_cu_count(&n_cu);
   if (st != SO2_OK) return st;
   const int n_groups = group_count(P.n_targets, n_cu);
-  return launch_LM<L, L>(P, n_groups, stream);
+  if (P.n_focus == 1) return launch_LM<L, L>(P, n_groups, stream);
+  if constexpr (L <= 4) {
+    if (P.m_max != L || P.H % P.n_focus) return SO2_ERR_INVALID_ARGUMENT;
+    switch (P.n_focus) {
+      case 2:
+        return launch_instance<L, L, 2>(P, n_groups, stream);
+      case 4:
+        return launch_instance<L, L, 4>(P, n_groups, stream);
+      case 8:
+        return launch_instance<L, L, 8>(P, n_groups, stream);
+    }
+  }
+  return SO2_ERR_INVALID_ARGUMENT;
 }
 
 // Workspace of the MFMA path: softmax statistics, the x pairs, w_rad in
@@ -1895,8 +2060,10 @@ MfmaParams make_params(const AttnArgs& a) {
   P.y = a.y;
   P.w_logit = (const uint16_t*)a.w_logit;
   P.xp_bytes = (uint32_t)((uint64_t)a.n_atoms * pair_off(a.L + 1) * kC * 4);
-  P.w_bytes = (uint32_t)(w1_offset(a.L, a.m_max + 1) * 2);  // the blocks m <= m_max
+  P.w_bytes = (uint32_t)(w1_offset(a.L, a.m_max + 1) * 2);  // the blocks m <= m_max (dense over the streams)
   P.m_max = a.m_max;
+  P.n_focus = a.n_focus;
+  P.w_focus = (const uint16_t*)a.w_focus;
   P.n_targets = a.n_targets;
   P.H = a.H;
   P.K = a.K;
@@ -1910,13 +2077,19 @@ MfmaParams make_params(const AttnArgs& a) {
 
 template <int L>
 so2_status launch_pack_L(const AttnArgs& a, const MfmaParams& P, hipStream_t stream) {
-  const int64_t w_entries = w1_offset(L, a.m_max + 1);  // w_so2 holds the blocks m <= m_max
-  const int64_t work = (int64_t)a.n_atoms * pair_off(L + 1) * (kC / 4) + (int64_t)a.K * kC + w_entries / 8;
+  // w_so2 holds the blocks m <= m_max, for each of the F streams over C / F channels
+  const int F = a.n_focus;
+  const int Cs = kC / F;
+  int64_t w_entries = (int64_t)(L + 1) * Cs * (L + 1) * Cs;
+  for (int m = 1; m <= a.m_max; ++m) w_entries += 2 * (int64_t)(L + 1 - m) * Cs * (L + 1 - m) * Cs;
+  w_entries *= F;
+  const int64_t work = (int64_t)a.n_atoms * pair_off(L + 1) * (kC / 4) + (int64_t)a.K * kC +
+                       (F == 1 ? w_entries : wf_entries(L)) / 8;
   const int64_t blocks = std::min<int64_t>((work + 255) / 256, 8192);
   hipLaunchKernelGGL(attn_pack_kernel<L>, dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const uint16_t*)a.x, const_cast<uint32_t*>(P.xp), a.n_atoms, (const uint16_t*)a.w_rad,
                      const_cast<float*>(P.wrad), a.K, (const uint16_t*)a.w_so2, const_cast<uint16_t*>(P.wf),
-                     w_entries);
+                     w_entries, F);
   SO2_CHECK_LAUNCH();
   return SO2_OK;
 }
@@ -1925,6 +2098,12 @@ so2_status launch_pack_L(const AttnArgs& a, const MfmaParams& P, hipStream_t str
 
 bool mfma_shape(int L, int C, int H, int K) {
   return C == kC && L >= 1 && L <= 6 && H >= 1 && H <= kMaxHeads && C % H == 0 && K <= kMaxRbf;
+}
+
+// Focus streams on the MFMA kernel: 64-edge chunks (L <= 4), every order,
+// F of 2, 4 or 8 streams (whole waves of 16 channels each) dividing H.
+bool mfma_focus(int L, int H, int m_max, int n_focus) {
+  return n_focus == 1 || (L <= 4 && m_max == L && (n_focus == 2 || n_focus == 4 || n_focus == 8) && H % n_focus == 0);
 }
 
 // The x pairs are addressed through a 32-bit buffer descriptor, with room

@@ -75,6 +75,8 @@ so2_status launch_attention_valu(const AttnArgs& a, hipStream_t stream);
 // (mfma_shape), up to the atom count its 32-bit buffer addressing covers
 // (mfma_fits).  x, w_rad and w_so2 must be 16-byte aligned.
 bool mfma_shape(int L, int C, int H, int K);
+// focus streams the MFMA kernel takes (n_focus = 1: always)
+bool mfma_focus(int L, int H, int m_max, int n_focus);
 bool mfma_fits(int L, int n_atoms);
 bool mfma_aligned(const AttnArgs& a);
 size_t mfma_scratch_bytes(int n_atoms, int n_targets, int L, int H, int K);

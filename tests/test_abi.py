@@ -320,11 +320,17 @@ def test_variant_counts_and_errors():
     mf = _desc(l_max=4, channels=128, heads=8, n_rbf=16, dtype=sea.SO2_BF16)
     assert lib.so2_attention_variant_kernel_kind(ctypes.byref(mf), ctypes.byref(sea.AttnVariant(-1, 1))) == \
         sea.KERNEL_MFMA
-    # truncated orders run on the MFMA kernel, focus streams on the edge-batch path
+    # truncated orders run on the MFMA kernel; so do 2, 4 or 8 focus streams
+    # with every order at L <= 4 when they hold whole heads; other focus
+    # streams on the edge-batch path
+    kind = lambda d, m, f: lib.so2_attention_variant_kernel_kind(ctypes.byref(d), ctypes.byref(sea.AttnVariant(m, f)))
     for m in (0, 2, 3):
-        assert lib.so2_attention_variant_kernel_kind(ctypes.byref(mf), ctypes.byref(sea.AttnVariant(m, 1))) == \
-            sea.KERNEL_MFMA
-    assert lib.so2_attention_variant_kernel_kind(ctypes.byref(mf), ctypes.byref(sea.AttnVariant(2, 2))) == \
-        sea.KERNEL_BATCH
-    assert lib.so2_attention_variant_kernel_kind(ctypes.byref(mf), ctypes.byref(sea.AttnVariant(-1, 2))) == \
-        sea.KERNEL_BATCH
+        assert kind(mf, m, 1) == sea.KERNEL_MFMA
+    for f in (2, 4, 8):
+        assert kind(mf, -1, f) == sea.KERNEL_MFMA
+    assert kind(mf, 2, 2) == sea.KERNEL_BATCH  # focus streams with truncated orders
+    assert kind(mf, -1, 16) == sea.KERNEL_BATCH  # 8 channels per stream
+    m4 = _desc(l_max=4, channels=128, heads=4, n_rbf=16, dtype=sea.SO2_BF16)
+    assert kind(m4, -1, 8) == sea.KERNEL_BATCH  # streams that split a head
+    m6 = _desc(l_max=6, channels=128, heads=8, n_rbf=16, dtype=sea.SO2_BF16)
+    assert kind(m6, -1, 4) == sea.KERNEL_BATCH  # 32-edge chunks

@@ -10,8 +10,10 @@ cross-focus softmax), through the C ABI:
 * bf16 inputs on the MFMA kernel at 2e-2: the logit bias (a small-molecule
   batch, and seeded targets of the L = 6 water box) and truncated orders
   (m_max = 0..3 at L = 4, m_max = L - 1 and 0 at every other degree, m_max =
-  2 and 4 on seeded targets of the L = 6 water box); focus streams at
-  C = 128 on the edge-batch path (fp32 arithmetic, 1e-4);
+  2 and 4 on seeded targets of the L = 6 water box) and 2, 4, 8 focus
+  streams at L <= 4 (small molecules, every degree 1..3, seeded targets of a
+  20,000-atom water box); focus streams with truncated orders or of 8
+  channels on the edge-batch path (fp32 arithmetic, 1e-4);
 * the base variant through the variant call is bitwise the base call;
   repeated calls on the edge-batch path are bitwise equal."""
 
@@ -110,7 +112,34 @@ def test_bf16_logit_bias_l6_water_sampled():
     assert _run(w, logit=True, targets=t) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("m_max,n_focus", [(-1, 4), (3, 2), (0, 2)])
+@pytest.mark.parametrize("n_focus,logit", [(2, False), (4, True), (8, False), (8, True)])
+def test_bf16_focus_streams_on_the_mfma_kernel(n_focus, logit):
+    import so_equivariant_graph_amd as sea
+
+    w = make_workload("small_molecules", geometry=dict(n_molecules=3))
+    assert _kind(w, -1, n_focus) == sea.KERNEL_MFMA
+    assert _run(w, -1, n_focus, logit=logit) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("L", [1, 2, 3])
+def test_bf16_focus_streams_mfma_every_degree(L):
+    import so_equivariant_graph_amd as sea
+
+    w = make_workload("tiny_fp32", l_max=L, channels=128, heads=8, n_rbf=16, dtype="bf16")
+    assert _kind(w, -1, 4) == sea.KERNEL_MFMA
+    assert _run(w, -1, 4, logit=True) <= TOL["bf16"]
+
+
+def test_bf16_focus_streams_mfma_water_sampled():
+    import so_equivariant_graph_amd as sea
+
+    w = make_workload("water_100k", geometry=dict(n_atoms=20000))
+    assert _kind(w, -1, 4) == sea.KERNEL_MFMA
+    t = np.sort(np.random.default_rng(3).choice(w.n_atoms, 48, replace=False))
+    assert _run(w, -1, 4, logit=True, targets=t) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("m_max,n_focus", [(3, 2), (0, 2), (-1, 16)])
 def test_bf16_c128_focus_streams_on_the_batch_path(m_max, n_focus):
     import so_equivariant_graph_amd as sea
 
