@@ -227,11 +227,12 @@ so2_status so2_attention_fwd_stages(uint32_t stages, const so2_attn_desc* desc, 
  *              edge message is scaled by pi_f = softmax_f(sum_{c in f}
  *              w_focus[c] yt[(0,0), c])
  *   w_focus    [C] in dtype, required when n_focus > 1
- * One stream (n_focus = 1), any m_max, with or without the logit bias, runs
- * where so2_attention_fwd would: bf16 MFMA shapes on the MFMA kernel (its
- * passes for |m| > m_max are not compiled into the instance of that m_max),
- * the rest on the fp32 edge-batch path; focus streams always run on the
- * edge-batch path (so2_attention_variant_kernel_kind says which).  Other
+ * Kernels (so2_attention_variant_kernel_kind says which): bf16 MFMA shapes
+ * run on the MFMA kernel with one stream and any m_max (the instance of
+ * that m_max has no passes for |m| > m_max), and with F = 2, 4 or 8 streams
+ * at l_max <= 4, every order, F dividing heads (block-diagonal weights, the
+ * cross-focus softmax from a score pass over the m = 0 chunks); every other
+ * variant and shape runs on the fp32 edge-batch path.  Other
  * arguments, the workspace (so2_attention_variant_workspace_bytes) and the
  * errors are those of so2_attention_fwd, plus INVALID_ARGUMENT for m_max
  * outside -1..l_max, n_focus < 1 or not dividing C, or a missing w_focus.
