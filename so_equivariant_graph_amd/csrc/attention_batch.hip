@@ -851,9 +851,13 @@ template <bool AT, bool BT, bool MAP>
 __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
   constexpr int BM = kGemmTile, BN = kGemmTile, BK = kGemmK;
   constexpr int R = BM * BK / 256;  // elements of each operand tile per thread
-  constexpr int LDP = BM + 16;  // row pad: the 4 k-rows of one MFMA operand read hit distinct banks
-  __shared__ float As[BK][LDP];
-  __shared__ float Bs[BK][LDP];
+  // tiles m-major ([row][k]): a lane reads the 4 k values it feeds to the 4
+  // MFMAs of a stage with one 16-byte load; a pitch of 20 floats puts the
+  // 16 rows of an operand read (and of the stores) on distinct bank groups
+  constexpr int LDK = BK + 4;
+  static_assert(BK == 16, "one 16-byte read per lane covers the stage's 4 MFMAs");
+  __shared__ __attribute__((aligned(16))) float As[BM][LDK];
+  __shared__ __attribute__((aligned(16))) float Bs[BN][LDK];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
   const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
@@ -901,25 +905,26 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
   for (int k0 = kb; k0 < ke; k0 += BK) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      As[ak[r]][am[r]] = ra[r];
-      Bs[bk[r]][bn[r]] = rb[r];
+      As[am[r]][ak[r]] = ra[r];
+      Bs[bn[r]][bk[r]] = rb[r];
     }
     __syncthreads();
     if (k0 + BK < ke) load(k0 + BK);
+    // MFMA q of the stage takes k = 4 (lane / 16) + q from every lane, for A
+    // and B alike: the 4 MFMAs cover the stage's 16 k once each
+    f32x4 av[4], bv[4];
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 4) {
-      const int kr = kk + (lane >> 4);
-      float av[4], bv[4];
+    for (int i = 0; i < 4; ++i) {
+      av[i] = *(const f32x4*)&As[wm + 16 * i + (lane & 15)][4 * (lane >> 4)];
+      bv[i] = *(const f32x4*)&Bs[wn + 16 * i + (lane & 15)][4 * (lane >> 4)];
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        av[i] = As[kr][wm + 16 * i + (lane & 15)];
-        bv[i] = Bs[kr][wn + 16 * i + (lane & 15)];
-      }
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[j], acc[i][j], 0, 0, 0);
-    }
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][q], bv[j][q], acc[i][j], 0, 0, 0);
     __syncthreads();
   }
   // C layout: lane holds rows 4 (lane / 16) + r, column lane % 16 of each 16 x 16 tile
