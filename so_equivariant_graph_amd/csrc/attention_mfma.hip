@@ -615,10 +615,14 @@ __device__ inline void gen_issue(__amdgpu_buffer_rsrc_t xrs, const Ctx& c, uint3
 }
 
 // D pairs of the generator rows for an A chunk (gm, glp): rows glp + gm and
-// glp - gm of D^glp, pairs 0..glp; the pairs past glp are zero (their
-// gathers read zeros too) and are not read, since past the last row of a
-// degree lie the next edge's pairs or, after the last edge, other LDS data.
-template <int L>
+// glp - gm of D^glp, pairs 0..glp.  Past the last row of a degree lie the
+// next edge's pairs or, after the last edge, other LDS data, so the pairs
+// past glp are not read: with kZero they are set to zero (for gen_finish,
+// which sums every pair; their gathers read zeros too); without it they
+// repeat pair glp, for the K steps of the main loop, whose dot products
+// stop at the unit's degree.  The reads then need no select after them and
+// all go out before the first wait.
+template <int L, bool kZero = true>
 __device__ inline void gen_dpairs(const uint32_t* sD, const Ctx& c, int gm, int glp,
                                   uint32_t (&dp)[kGR][Geo<L>::MP], uint32_t (&dm)[kGR][Geo<L>::MP]) {
   constexpr int DPW = Cfg<L>::DPW;
@@ -630,8 +634,8 @@ __device__ inline void gen_dpairs(const uint32_t* sD, const Ctx& c, int gm, int 
       const int pc = p <= glp ? p : glp;
       const uint32_t vp = d[(glp + gm) * (glp + 1) + pc];
       const uint32_t vm = d[(glp - gm) * (glp + 1) + pc];
-      dp[u][p] = p <= glp ? vp : 0u;
-      dm[u][p] = p <= glp ? vm : 0u;
+      dp[u][p] = !kZero || p <= glp ? vp : 0u;
+      dm[u][p] = !kZero || p <= glp ? vm : 0u;
     }
   }
 }
@@ -1119,7 +1123,7 @@ __device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams&
     if (k == 0) {
       int gm;
       gen_target<L, MM, PI>(q, gm, glp);
-      gen_dpairs<L>(sD, c, gm, glp, dp, dm);
+      gen_dpairs<L, false>(sD, c, gm, glp, dp, dm);
     }
     // degree of the chunk whose generator unit 0 is gathered in step s + 1
     int glp2 = glp;
