@@ -359,10 +359,14 @@ so2_status so2_merged_rms_norm(const void* x, const float* gamma, void* y, int32
  *   w_g            [channels][channels] dtype, [in][out] (device)
  *   y              [n_atoms][(l_max+1)^2][channels] fp32, written (device)
  *   workspace      >= so2_swiglu_s2_workspace_bytes(...) bytes, 16-byte
- *                  aligned (device): u, v, g and the gated product
+ *                  aligned (device): u, v, g and the gated product, or the
+ *                  weights repacked for the fused kernel (under 0.6 MB)
  * bf16 with channels = 128 and 16-byte aligned x and weights runs the maps on
  * the matrix cores (bf16 operands, fp32 sums) and keeps u, v and the gated
- * product in bf16; every other shape runs in fp32 arithmetic.
+ * product in bf16; at l_max <= 4 the whole call is one fused kernel (groups
+ * of 4 nodes through maps, grid and output map in LDS), whose results are
+ * bitwise those of the three steps of so2_swiglu_s2_stages.  Every other
+ * shape runs in fp32 arithmetic.
  * Errors: INVALID_ARGUMENT (nulls with n_atoms > 0, n_atoms < 0, l_max < 0,
  * channels < 1, bad dtype), UNSUPPORTED (l_max > 6), WORKSPACE, DEVICE.
  * Asynchronous on `stream`; no device allocation.  The workspace query

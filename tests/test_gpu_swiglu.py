@@ -1,9 +1,10 @@
 """SwiGLU-S2 activation on the GPU (through the C ABI) against the fp64
 oracle, element by element: fp32 path at <= 1e-4, bf16 at <= 2e-2 (the
-oracle gets the same bf16-rounded inputs), both kernel paths (matrix cores
-for bf16 with C = 128, the plain loops otherwise), every degree 0..6, ragged
-node counts, equivariance on the GPU, and the 100k-atom water box on sampled
-nodes."""
+oracle gets the same bf16-rounded inputs), every kernel path (the fused
+kernel for bf16 with C = 128 and L <= 4, the three matrix-core kernels for
+bf16 with C = 128 in steps or at L = 5, 6, the plain loops otherwise), every
+degree 0..6, ragged node counts, equivariance on the GPU, and the 100k-atom
+water box on sampled nodes with every row checked written."""
 
 import numpy as np
 import pytest
@@ -67,6 +68,38 @@ def test_bf16_matrix_core_path_every_node(L):
     err = max_rel_error(y, y_ref)
     say("max rel err", err)
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("L,n", [(1, 203), (3, 19), (4, 203)])
+def test_bf16_fused_kernel_equals_three_kernels(L, n):
+    """bf16, C = 128, L <= 4: one call runs the fused kernel; the same call
+    in three steps (maps, grid, output) runs the three-kernel path.  Both
+    round u, v and s to bf16 at the same points and accumulate in the same
+    order, so they agree to fp32 rounding; both match the oracle.  n = 203
+    ends on a group of 3 of the fused kernel's 8-node groups."""
+    import torch
+
+    import so_equivariant_graph_amd as sea
+
+    say("swiglu fused vs three kernels", L, n)
+    x, ws = _case(n, L, 128, "bf16", seed=30 + L)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda").to(torch.bfloat16)
+    xd, (A, B, G, O) = t(x), tuple(t(a) for a in ws)
+    y_fused = torch.full((n, (L + 1) ** 2, 128), float("nan"), device="cuda")
+    sea.swiglu_s2(xd, A, B, G, O, out=y_fused)
+    y_three = torch.full_like(y_fused, float("nan"))
+    wsp = torch.empty(sea.load_library().so2_swiglu_s2_workspace_bytes(n, L, 128, sea.SO2_BF16),
+                      dtype=torch.uint8, device="cuda")
+    for st in (sea.STAGE_SW_MAPS, sea.STAGE_SW_GRID, sea.STAGE_SW_OUT):
+        sea.swiglu_s2(xd, A, B, G, O, out=y_three, workspace=wsp, stages=st)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y_fused).all()) and bool(torch.isfinite(y_three).all())
+    a, b = y_fused.cpu().numpy().astype(np.float64), y_three.cpu().numpy().astype(np.float64)
+    y_ref = swiglu_s2_ref(x, *ws)
+    e_f, e_t, e_ft = max_rel_error(a, y_ref), max_rel_error(b, y_ref), max_rel_error(a, b)
+    say("max rel err fused", e_f, "three kernels", e_t, "fused vs three", e_ft, "bitwise", bool((a == b).all()))
+    assert e_f <= TOL["bf16"] and e_t <= TOL["bf16"]
+    assert e_ft <= TOL["fp32"]
 
 
 def test_bf16_plain_path_every_node():
@@ -133,7 +166,8 @@ def test_full_size_water_box_sampled_nodes():
     rng = np.random.default_rng(5)
     ws = tuple(to_bf16_exact(a.astype(np.float32)) for a in _weights(rng, 4, 128))
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda").to(torch.bfloat16)
-    y = sea.swiglu_s2(dev(w.x), *(dev(a) for a in ws))
+    y = torch.full(w.x.shape, float("nan"), device="cuda")  # every row written
+    sea.swiglu_s2(dev(w.x), *(dev(a) for a in ws), out=y)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(y).all())
     idx = np.sort(rng.choice(w.n_atoms, size=24, replace=False))
