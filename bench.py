@@ -47,12 +47,12 @@ PEAK_HBM_GBS = 8000.0
 # for the kernel sources it was taken on: their digest is stored with it and a
 # mismatch reports null.
 MEASURED_TRAFFIC = {
-    # FETCH_SIZE 115580722 KiB x 2.00 (a 1 GiB copy reads as 524305 KiB), WRITE_SIZE
-    # 2609655 KiB x 1.00 (the copy writes read exactly 1048576 KiB); mean of 5 launches.
+    # FETCH_SIZE 115172382 KiB x 1.99994 (a 1 GiB copy reads as 524305 KiB), WRITE_SIZE
+    # 1272532 KiB x 1.00 (the copy writes read exactly 1048576 KiB); mean of 5 launches.
     "water_100k": {
-        "sources_sha256": "1830d75789b398d4be8c8e67c09ad0cead30acec7e113a2145f89be8a72e7ba3",
-        "fetch_bytes": 236701718354,
-        "write_bytes": 2672286221,
+        "sources_sha256": "35406eaaa9784c95ad6c2ec4230f665fea339553945b7f0074fa800b99033e19",
+        "fetch_bytes": 235865480513,
+        "write_bytes": 1303072379,
     },
 }
 # the files that hold the fused kernel's device code

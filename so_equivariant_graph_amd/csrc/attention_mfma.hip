@@ -1128,8 +1128,15 @@ __device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams&
     // degree of the chunk whose generator unit 0 is gathered in step s + 1
     int glp2 = glp;
     if (k == 2) {
+      // at the pass's last A chunk, step s + 2 is the next pass's first
+      // step, whose generator unit 0 belongs to that pass's chunk 1 target
       int gm2;
-      gen_target<L, MM, PI>(q + 1 < NCH ? q + 1 : q, gm2, glp2);
+      if (q + 1 < NCH) {
+        gen_target<L, MM, PI>(q + 1, gm2, glp2);
+      } else {
+        if constexpr (pn.M >= 0) gen_target<L, MM, PI + 1>(0, gm2, glp2);
+        else gen_target<L, MM, PI>(q, gm2, glp2);
+      }
     }
     const uint16_t* acur = abase + ((PAR + q) & 1) * Geo<L>::ABUF;
     uint16_t* anext = abase + ((PAR + q + 1) & 1) * Geo<L>::ABUF;
@@ -1148,10 +1155,8 @@ __device__ __attribute__((always_inline)) inline void run_pass(const MfmaParams&
     uint32_t nboff[NDn][kNT];
     b_offsets<L, pn.M, pn.LO, NDn>(nboff);
     load_b<L, pn.M, pn.LO, NDn>(wrs, nboff, 0, nring[0]);
-    // gathers of generator unit 0 for the next pass's chunk 0 target
-    int gm, glp0;
-    gen_target<L, MM, PI + 1>(0, gm, glp0);
-    gen_issue<L>(xrs, c, oob, glp0, 0, xa);
+    // the gathers of the next pass's first generator unit are in xa (issued
+    // by the last K step)
     rot_back_all<L, M, LO, 0, ND>(smem, c, acc, frag, T);
     run_pass<L, MM, PI + 1>(P, smem, c, T, nring, xa, xb);
   } else {
