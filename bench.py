@@ -440,13 +440,14 @@ def swiglu_bench(steps, warmup):
 
 def backward_bench(steps, warmup, n_molecules):
     """The backward of the attention layer (so2_attention_bwd) on a batch of
-    the small-molecule workload (bf16 inputs, L = 4, C = 128, fp32
-    arithmetic): messages/s of the force-only call (dx, dpos) and of the full
-    call (every weight gradient too), timed with torch events on the stream
-    the library launches on.  Algorithmic flops per edge: the forward per-m
-    map (recomputed) and its transpose, plus the SO(2) weight gradient in the
-    full call, each the forward map's count; the three run as fp32 GEMMs on
-    the matrix cores, so the roofline is the fp32 MFMA peak."""
+    the small-molecule workload (bf16 inputs, L = 4, C = 128): messages/s of
+    the force-only call (dx, dpos) and of the full call (every weight
+    gradient too), timed with torch events on the stream the library
+    launches on.  Algorithmic flops per edge: the forward per-m map
+    (recomputed) and its transpose, plus the SO(2) weight gradient in the
+    full call, each the forward map's count; for bf16 inputs the three run
+    as bf16-operand GEMMs on the matrix cores (fp32 operands split into two
+    bf16 parts, fp32 accumulation), so the roofline is the bf16 MFMA peak."""
     import numpy as np
     import torch
 
@@ -483,11 +484,11 @@ def backward_bench(steps, warmup, n_molecules):
     print(json.dumps({
         "metric": "backward neighbor-pair messages/sec (so2_attention_bwd, all gradients)",
         "value": E / (ms_w * 1e-3), "unit": "messages/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
-        "ms_per_step": ms_w, "higher_is_better": True, "dtype": "bf16 inputs, fp32 arithmetic", "data": "synthetic",
+        "ms_per_step": ms_w, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"small_molecules batch of {n_molecules}", "n_atoms": w.n_atoms, "n_edges": E,
                    "l_max": w.l_max, "channels": w.channels, "heads": w.heads},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
         "detail": {"forces_only_ms": ms_f, "forces_only_messages_per_s": E / (ms_f * 1e-3),
                    "forces_only_tflops": E * 2 * F / (ms_f * 1e-3) / 1e12, "full_ms": ms_w,
                    "flop_per_edge_full": 3 * F, "flop_per_edge_forces": 2 * F,

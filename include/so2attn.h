@@ -275,11 +275,16 @@ so2_status so2_attention_fwd_variant(const so2_attn_desc* desc, const so2_attn_v
  *             written; each may be NULL (not computed: the force-only path
  *             skips the weight reductions)
  *   workspace >= so2_attention_bwd_workspace_bytes(desc) bytes
- * Arithmetic: fp32 for fp32 and bf16 inputs (bf16 values are widened
- * exactly); the three uses of the per-m map (the forward map recomputed,
- * its transpose, the weight gradient) are fp32 GEMMs over each batch on the
- * matrix cores.  Contributions to dx of sources, dpos, dq, dk and the
- * weights are summed with fp32 atomics, so the low bits vary between runs.
+ * Arithmetic: fp32, except the three uses of the per-m map (the forward
+ * map recomputed, its transpose, the weight gradient), GEMMs over each
+ * batch on the matrix cores: fp32 GEMMs for fp32 inputs; for bf16 inputs
+ * bf16-operand GEMMs with fp32 accumulation, each fp32 operand split into
+ * two bf16 parts hi + lo (about 16 significant bits; the weight matrices
+ * are exact in bf16 and not split).  Measured errors against the fp64
+ * oracle: about 1e-6 (fp32 inputs), 5e-6 to 3e-4 (bf16 inputs; the bound is
+ * the bf16 one, 2e-2).  Contributions to dx of sources, dpos, dq, dk and
+ * the weights are summed with fp32 atomics, so the low bits vary between
+ * runs.
  * Shapes: L <= 6, C <= 256, H <= 256, else UNSUPPORTED.  A target whose
  * envelopes are all 0 (edges exactly at the cutoff only) has y = 0 and
  * gets no gradient.

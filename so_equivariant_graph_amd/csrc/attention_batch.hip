@@ -63,6 +63,10 @@ namespace so2 {
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr int kLane = 64;       // per-edge and per-target kernels: one wave per block
 constexpr int kMaxHeadsB = 256;  // heads (and focus streams), per-lane loops of stride 64
@@ -944,11 +948,182 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
       }
 }
 
+// C (+)= A B on v_mfma_f32_16x16x32_bf16 with fp32 accumulation, for
+// bf16 inputs: the same operand layouts, tiles (128 x 128, 4 waves of
+// 64 x 64), K ranges and store / atomic modes as gemm_f32_kernel, K in
+// stages of 32 (stages of 64, at two waves per SIMD, measured 3 % slower
+// over the backward).  The operands stay fp32 in memory and are split as they
+// are staged into LDS: x = hi + lo with hi = bf16(x) and lo = bf16(x - hi)
+// (round to nearest even), about 16 significant bits.  An operand that is
+// exact in bf16 (the weight matrices of bf16 inputs) is staged as hi only
+// (SA / SB false); the product takes A_hi B_hi + A_lo B_hi + A_hi B_lo
+// (the lo lo term is below the fp32 rounding of the sum).  Plain bf16
+// operands (hi only on both sides) are not enough here: the position
+// gradient cancels to a small fraction of its terms.  An operand tile is
+// held in LDS as [row][k] bf16 pairs (k, k + 1) in one dword, 16 pairs per
+// row and a pitch of 20 dwords (the 16 rows of a fragment read fall on
+// distinct bank groups), so a lane's fragment (8 consecutive k of one row)
+// is one 16-byte read.  Each thread stages 8 pairs per operand and stage: with k contiguous in memory (A not transposed, B transposed)
+// one 8-byte load per pair, else two 4-byte loads (row-contiguous, so the
+// threads' loads of one k are coalesced).  No column maps.
+constexpr int kGemmKB = 32;
+constexpr int kGemmKP = kGemmKB / 2;     // bf16 pairs per LDS row
+constexpr int kGemmPitch = kGemmKP + 4;  // dwords per LDS row
+constexpr int kGemmPT = kGemmTile * kGemmKP / 256;  // pairs per thread and operand
+
+template <bool KC>
+__device__ inline void bgemm_load(const float* __restrict__ X, int64_t ld, int rows, int row0, int k0, int ke,
+                                  f32x2 (&v)[kGemmPT]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int r = 0; r < kGemmPT; ++r) {
+    int row, kp;
+    if constexpr (KC) {
+      kp = t & (kGemmKP - 1);
+      row = t / kGemmKP + (256 / kGemmKP) * r;
+    } else {
+      row = t & 127;
+      kp = (t >> 7) + 2 * r;
+    }
+    const int gr = row0 + row, gk = k0 + 2 * kp;
+    f32x2 e = f32x2{0.0f, 0.0f};
+    if (gr < rows) {
+      if constexpr (KC) {
+        const float* p = X + (int64_t)gr * ld + gk;
+        if (gk + 1 < ke) e = *(const f32x2*)p;
+        else if (gk < ke) e.x = p[0];
+      } else {
+        if (gk < ke) e.x = X[(int64_t)gk * ld + gr];
+        if (gk + 1 < ke) e.y = X[(int64_t)(gk + 1) * ld + gr];
+      }
+    }
+    v[r] = e;
+  }
+}
+
+template <bool KC, bool SPLIT>
+__device__ inline void bgemm_store(uint32_t (*Sh)[kGemmPitch], uint32_t (*Sl)[kGemmPitch],
+                                   const f32x2 (&v)[kGemmPT]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int r = 0; r < kGemmPT; ++r) {
+    const int row = KC ? t / kGemmKP + (256 / kGemmKP) * r : t & 127;
+    const int kp = KC ? t & (kGemmKP - 1) : (t >> 7) + 2 * r;
+    const bf16x2 hi = __builtin_convertvector(v[r], bf16x2);
+    Sh[row][kp] = __builtin_bit_cast(uint32_t, hi);
+    if constexpr (SPLIT) {
+      const f32x2 rest = v[r] - __builtin_convertvector(hi, f32x2);
+      Sl[row][kp] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2));
+    }
+  }
+}
+
+__device__ inline f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+template <bool AT, bool BT, bool SA, bool SB>
+__global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmArgs g) {
+  constexpr int BM = kGemmTile, BN = kGemmTile, BK = kGemmKB;
+  __shared__ __attribute__((aligned(16))) uint32_t Ah[BM][kGemmPitch];
+  __shared__ __attribute__((aligned(16))) uint32_t Al[SA ? BM : 1][kGemmPitch];
+  __shared__ __attribute__((aligned(16))) uint32_t Bh[BN][kGemmPitch];
+  __shared__ __attribute__((aligned(16))) uint32_t Bl[SB ? BN : 1][kGemmPitch];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  const int kb = blockIdx.z * g.k_split;
+  const int ke = min(g.K, kb + g.k_split);
+  // A(m, k): k contiguous unless AT; B(k, n) = B[n ldb + k]: k contiguous when BT
+  f32x2 ra[kGemmPT], rb[kGemmPT];
+  auto load = [&](int k0) {
+    bgemm_load<!AT>(g.A, g.lda, g.M, m0, k0, ke, ra);
+    bgemm_load<BT>(g.B, g.ldb, g.N, n0, k0, ke, rb);
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (kb < ke) load(kb);
+  for (int k0 = kb; k0 < ke; k0 += BK) {
+    bgemm_store<!AT, SA>(Ah, Al, ra);
+    bgemm_store<BT, SB>(Bh, Bl, rb);
+    __syncthreads();
+    if (k0 + BK < ke) load(k0 + BK);
+    // fragments of MFMA K step h: row lane % 16 of the tile, k = 32 h + 8
+    // (lane / 16) .. + 7
+#pragma unroll
+    for (int h = 0; h < kGemmKB / 32; ++h) {
+      const int fo = 16 * h + 4 * (lane >> 4);
+      u32x4 ah[4], al[4], bh[4], bl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ri = wm + 16 * i + (lane & 15), rj = wn + 16 * i + (lane & 15);
+        ah[i] = *(const u32x4*)&Ah[ri][fo];
+        bh[i] = *(const u32x4*)&Bh[rj][fo];
+        if constexpr (SA) al[i] = *(const u32x4*)&Al[ri][fo];
+        if constexpr (SB) bl[i] = *(const u32x4*)&Bl[rj][fo];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = mfma_bf16(ah[i], bh[j], acc[i][j]);
+          if constexpr (SA) acc[i][j] = mfma_bf16(al[i], bh[j], acc[i][j]);
+          if constexpr (SB) acc[i][j] = mfma_bf16(ah[i], bl[j], acc[i][j]);
+        }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm + 16 * a + 4 * (lane >> 4) + r;
+        const int colm = n0 + wn + 16 * b + (lane & 15);
+        if (row < g.M && colm < g.N) {
+          float* p = g.Cm + (int64_t)row * g.ldc + colm;
+          if (g.atomic) atomicAdd(p, acc[a][b][r]);
+          else *p = acc[a][b][r];
+        }
+      }
+}
+
+// How the bf16-operand GEMM stages its operands: not at all (the fp32
+// GEMM runs), or A split into hi + lo with B exact in bf16, or both split.
+enum GemmSplit { kSplitNone = 0, kSplitA = 1, kSplitAB = 2 };
+
+// fp32 GEMM, or with split != kSplitNone the bf16-operand GEMM above (no
+// column maps; the k-contiguous operands need 8-byte aligned rows, else the
+// fp32 kernel runs)
 template <bool AT, bool BT>
 so2_status gemm(const float* A, int64_t lda, const float* B, int64_t ldb, float* Cm, int64_t ldc, int M, int N, int K,
-                bool atomic, hipStream_t stream, int kg = 0, int kstride = 0, int ng = 0, int nstride = 0) {
+                bool atomic, hipStream_t stream, int kg = 0, int kstride = 0, int ng = 0, int nstride = 0,
+                GemmSplit split = kSplitNone) {
   if (M <= 0 || N <= 0 || K <= 0) return SO2_OK;
   GemmArgs g{A, B, Cm, M, N, K, lda, ldb, ldc, K, atomic ? 1 : 0, kg, kstride, ng, nstride};
+  const bool aligned = (AT || (lda % 2 == 0 && ((uintptr_t)A & 7) == 0)) &&
+                       (!BT || (ldb % 2 == 0 && ((uintptr_t)B & 7) == 0));
+  if (split != kSplitNone && !kg && !ng && aligned) {
+    unsigned splits = 1;
+    if (atomic) {
+      const int64_t tiles = (int64_t)((M + kGemmTile - 1) / kGemmTile) * ((N + kGemmTile - 1) / kGemmTile);
+      const int64_t want = std::max<int64_t>(1, 2048 / std::max<int64_t>(tiles, 1));
+      const int64_t by_k = std::max<int64_t>(1, K / 512);
+      splits = (unsigned)std::min(want, by_k);
+      g.k_split = (int)(((K + splits - 1) / splits + kGemmKB - 1) / kGemmKB * kGemmKB);
+      splits = (unsigned)((K + g.k_split - 1) / g.k_split);
+    }
+    const dim3 grid((unsigned)((M + kGemmTile - 1) / kGemmTile), (unsigned)((N + kGemmTile - 1) / kGemmTile), splits);
+    if (split == kSplitA) hipLaunchKernelGGL((gemm_bf16_kernel<AT, BT, true, false>), grid, dim3(256), 0, stream, g);
+    else hipLaunchKernelGGL((gemm_bf16_kernel<AT, BT, true, true>), grid, dim3(256), 0, stream, g);
+    SO2_CHECK_LAUNCH();
+    return SO2_OK;
+  }
   unsigned splits = 1;
   if (atomic) {
     // K ranges of at least 512 so that the tile grid covers the device
@@ -1438,6 +1613,11 @@ so2_status launch_attention_bwd(const AttnArgs& a, const float* dy, float* dx, f
     const int64_t cap = S.cap;
     const int64_t nbat = (n_edges + cap - 1) / cap;
     const int64_t ld = (int64_t)nc * C;
+    // bf16 inputs: the per-m maps on the matrix cores' bf16 path, each fp32
+    // operand split into two bf16 parts (the weight matrices are exact in
+    // bf16); fp32 inputs: fp32 GEMMs
+    const bool bf16 = a.dtype == SO2_BF16;
+    const GemmSplit sp_a = bf16 ? kSplitA : kSplitNone, sp_ab = bf16 ? kSplitAB : kSplitNone;
     auto set_batch = [&](int64_t b) {
       P.e0 = e_first + b * cap;
       P.nb = (int32_t)std::min<int64_t>(cap, n_edges - b * cap);
@@ -1448,7 +1628,7 @@ so2_status launch_attention_bwd(const AttnArgs& a, const float* dy, float* dx, f
         const int wd = blk_width(L, C, m);
         const int64_t xo = blk_off(L, C, m);
         so2_status s2 = gemm<false, true>(P.b.xt + xo, ld, bm + bmat_off(L, C, m), wd, P.b.yt + xo, ld, P.nb, wd, wd,
-                                          false, stream);
+                                          false, stream, 0, 0, 0, 0, sp_a);
         if (s2 != SO2_OK) return s2;
       }
       return SO2_OK;
@@ -1474,11 +1654,11 @@ so2_status launch_attention_bwd(const AttnArgs& a, const float* dy, float* dx, f
         // dB_m += dY_m^T X_m (before dX overwrites X)
         if (dw_so2 &&
             (st = gemm<true, false>(P.b.yt + xo, ld, P.b.xt + xo, ld, db + bmat_off(L, C, m), wd, wd, wd, P.nb, true,
-                                    stream)) != SO2_OK)
+                                    stream, 0, 0, 0, 0, sp_ab)) != SO2_OK)
           return st;
         // dX_m = dY_m B_m, over X_m
         if ((st = gemm<false, false>(P.b.yt + xo, ld, bm + bmat_off(L, C, m), wd, P.b.xt + xo, ld, P.nb, wd, wd, false,
-                                     stream)) != SO2_OK)
+                                     stream, 0, 0, 0, 0, sp_a)) != SO2_OK)
           return st;
       }
       if ((st = run_edges(L, a.dtype, 3, P, stream)) != SO2_OK) return st;
