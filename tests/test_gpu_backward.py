@@ -10,7 +10,8 @@ operand split into two bf16 parts, fp32 accumulation) and take the bf16
 bound, 2e-2; the measured errors are 5e-6 to 3e-4 (plain bf16 operands,
 without the split, reach 0.36 on the position gradient of the multi-batch
 case).  Cases: the tiny fp32 workload (every atom, both flags),
-a small periodic water box, a bf16 batch at L = 4, C = 128, L = 6, 128
+a small periodic water box, a bf16 batch at L = 4, C = 128, bf16 inputs at
+C = 16 and 48 (partial GEMM tiles in every dimension), L = 6, 128
 heads at C = 256, empty
 neighbourhoods with n_targets < n_atoms, targets whose edges take two and
 three batches (64 edges per target, at least 4096: the second pass then
@@ -100,6 +101,17 @@ def test_bf16_inputs_l4_c128():
     w = make_workload("small_molecules", geometry=dict(n_molecules=2))
     assert w.dtype == "bf16" and w.channels == 128
     g, r, _, _ = _case(w)
+    assert max(_compare(g, r).values()) <= TOL_BF16
+
+
+@pytest.mark.parametrize("L,C,H", [(2, 16, 2), (3, 48, 4)])
+def test_bf16_inputs_ragged_gemm_tiles(L, C, H):
+    # bf16 inputs take the split-bf16 GEMMs; with these widths every per-m
+    # block (3C, 2(L+1-m)C columns) leaves partial 128-column tiles and
+    # partial 32-wide K stages, and the edge counts partial row tiles
+    say("backward bf16 ragged GEMM tiles", L, C, H)
+    w = make_workload("tiny_fp32", l_max=L, channels=C, heads=H, dtype="bf16")
+    g, r, _, _ = _case(w, seed=5)
     assert max(_compare(g, r).values()) <= TOL_BF16
 
 
