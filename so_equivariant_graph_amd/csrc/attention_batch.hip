@@ -263,7 +263,15 @@ __device__ inline int edge_target(const int32_t* row_ptr, int n_targets, int64_t
   return lo;
 }
 
-// Pass-1 preparation of every edge of the batch: target, geometry, frame,
+// The target of every edge of the batch, one thread per edge (the per-edge
+// kernels read it instead of searching row_ptr with a whole wave per edge).
+__global__ void __launch_bounds__(256) batch_targets_kernel(BatchParams P) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e < P.nb) P.b.tgt[e] = edge_target(P.row_ptr, P.n_targets, P.e0 + e);
+}
+
+// Pass-1 preparation of every edge of the batch (its target from
+// batch_targets_kernel): geometry, frame,
 // Wigner-D, radial basis, gate and its |r| derivative, softmax weights, and
 // xt = g (.) D x_j in the block layout.
 template <int L, typename T>
@@ -286,7 +294,7 @@ __global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4)))
   const EdgeBufs& B = P.b;
   for (int e = blockIdx.x; e < P.nb; e += gridDim.x) {
     const int64_t ge = P.e0 + e;
-    const int i = edge_target(P.row_ptr, P.n_targets, ge);
+    const int i = B.tgt[e];
     const int j = P.col[ge];
     const EdgeGeo geo = edge_geometry(P.pos, i, j, P.periodic, P.box, rc);
     const float rho = geo.rho;
@@ -313,7 +321,6 @@ __global__ void __launch_bounds__(kLane) __attribute__((amdgpu_waves_per_eu(4)))
         sc[4] = rh[1];
         sc[5] = rh[2];
       }
-      B.tgt[e] = i;
     }
     __syncthreads();
     float* xte = B.xt + (int64_t)e * nc * C;
@@ -1346,7 +1353,11 @@ so2_status launch_edges(int which, const BatchParams& P, hipStream_t stream) {
   const unsigned grid = (unsigned)std::min<int64_t>(P.nb, kGridCap);
   if (grid == 0) return SO2_OK;
   switch (which) {
-    case 0: hipLaunchKernelGGL((bwd_prep_kernel<L, T>), dim3(grid), dim3(kLane), 0, stream, P); break;
+    case 0:
+      hipLaunchKernelGGL(batch_targets_kernel, dim3((unsigned)((P.nb + 255) / 256)), dim3(256), 0, stream, P);
+      SO2_CHECK_LAUNCH();
+      hipLaunchKernelGGL((bwd_prep_kernel<L, T>), dim3(grid), dim3(kLane), 0, stream, P);
+      break;
     case 1: hipLaunchKernelGGL((bwd_sbar_kernel<L>), dim3(grid), dim3(kLane), 0, stream, P); break;
     case 2: hipLaunchKernelGGL((bwd_dyt_kernel<L>), dim3(grid), dim3(kLane), 0, stream, P); break;
     case 3: hipLaunchKernelGGL((bwd_final_kernel<L, T>), dim3(grid), dim3(kLane), 0, stream, P); break;
